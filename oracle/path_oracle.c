@@ -1,0 +1,159 @@
+/*
+ * path_oracle.c -- plain fp64 CPU oracle for PaTH attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code, header, table or helper with the
+ * HIP implementation.
+ *
+ * Citations name a page and a section of it:
+ *   [Notes s2.x]  the reading-notes page "PaTH Attention:通过累积 Householder
+ *                 变换编码位置" (cc.laoqi.cc, notes on arXiv 2505.16381v2),
+ *                 section 2.x;
+ *   [Explainer s3] the explainer page "PaTH Attention: Position Encoding via
+ *                 Accumulating Householder Transformations" (gist.science),
+ *                 section 3 ("Effizientes Training und Inferenz").
+ *
+ * What is computed is the plain definition, not a blockwise algorithm:
+ *   logit(i, j) = scale * k_j^T H_{j+1} ... H_i q_i  +  sum_{s=j+1..i} log f_s
+ * for j <= i, with H_t = I - beta_t w_t w_t^T            [Notes s2.1, s2.5]
+ * followed by a causal softmax over j <= i and the value sum o_i.
+ * The product is evaluated right to left as a walk: z starts at q_i, the
+ * score of key j is read off as k_j . z, and then H_j is applied to z, so
+ * that the next key (j-1) sees H_j ... H_i q_i.  This is only associativity
+ * of the matrix product in the definition; no block structure is used.
+ *
+ * The attention scale is an explicit argument (the pages leave it out of
+ * their notation [Notes s2.1]); the forget-gate bias is added after scaling
+ * and is not scaled.  Positions are 0-based here; the pages count from 1.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* z <- (I - beta w w^T) z.  One Householder-like transition [Notes s2.1, s2.2]. */
+static void apply_transition(int d, const double *w, double beta, double *z)
+{
+    double wz = 0.0;
+    for (int e = 0; e < d; ++e) wz += w[e] * z[e];
+    for (int e = 0; e < d; ++e) z[e] -= beta * wz * w[e];
+}
+
+static double dot(int d, const double *a, const double *b)
+{
+    double s = 0.0;
+    for (int e = 0; e < d; ++e) s += a[e] * b[e];
+    return s;
+}
+
+/*
+ * One query row i of one (batch, head) slice.
+ *   q, k, w : [L, d]   v : [L, dv]   beta, logf : [L]  (logf may be NULL: PaTH)
+ *   o_row : [dv]   lse : natural-log log-sum-exp of the final logits of row i.
+ *   scores : caller scratch of length >= i+1.
+ * Definition: [Notes s2.1] (logit, softmax, value sum), [Notes s2.5] (bias).
+ */
+static void walk_row(int L, int d, int dv, const double *q, const double *k,
+                     const double *v, const double *w, const double *beta,
+                     const double *logf, double scale, int i, double *z,
+                     double *scores, double *o_row, double *lse)
+{
+    (void)L;
+    memcpy(z, q + (size_t)i * d, sizeof(double) * d);
+    double bias = 0.0;                 /* sum_{s=j+1..i} log f_s */
+    for (int j = i; j >= 0; --j) {
+        scores[j] = scale * dot(d, k + (size_t)j * d, z) + bias;
+        apply_transition(d, w + (size_t)j * d, beta[j], z);   /* z <- H_j z */
+        if (logf) bias += logf[j];
+    }
+    double m = -INFINITY;
+    for (int j = 0; j <= i; ++j) if (scores[j] > m) m = scores[j];
+    double l = 0.0;
+    for (int e = 0; e < dv; ++e) o_row[e] = 0.0;
+    for (int j = 0; j <= i; ++j) {
+        double p = exp(scores[j] - m);
+        l += p;
+        const double *vj = v + (size_t)j * dv;
+        for (int e = 0; e < dv; ++e) o_row[e] += p * vj[e];
+    }
+    for (int e = 0; e < dv; ++e) o_row[e] /= l;
+    *lse = m + log(l);
+}
+
+/*
+ * Forward pass for selected rows of S independent slices.
+ *   q, k, w : [S, L, d]   v : [S, L, dv]   beta, logf : [S, L]
+ *   rows : [S, nrows] 0-based query positions (each in [0, L))
+ *   o : [S, nrows, dv]   lse : [S, nrows]
+ * Rows are independent; they are spread over OpenMP threads.
+ * Returns 0, or -1 if a row index is out of range (nothing is written then).
+ */
+int oracle_fwd_rows(int S, int L, int d, int dv,
+                    const double *q, const double *k, const double *v,
+                    const double *w, const double *beta, const double *logf,
+                    double scale, int nrows, const int *rows,
+                    double *o, double *lse)
+{
+    for (long t = 0; t < (long)S * nrows; ++t)
+        if (rows[t] < 0 || rows[t] >= L) return -1;
+    #pragma omp parallel
+    {
+        double *z = (double *)malloc(sizeof(double) * (size_t)d);
+        double *scores = (double *)malloc(sizeof(double) * (size_t)L);
+        #pragma omp for schedule(dynamic, 1)
+        for (long t = 0; t < (long)S * nrows; ++t) {
+            long s = t / nrows;
+            const size_t off = (size_t)s * L;
+            walk_row(L, d, dv, q + off * d, k + off * d, v + off * dv,
+                     w + off * d, beta + off, logf ? logf + off : NULL, scale,
+                     rows[t], z, scores, o + (size_t)t * dv, lse + t);
+        }
+        free(z);
+        free(scores);
+    }
+    return 0;
+}
+
+/*
+ * Keys as a decoding cache holds them after position t has been processed:
+ *   out_j = H_t ... H_{j+1} k_j   for j in [0, t]   (out_t = k_t)
+ * i.e. every transition after position j is applied to key j, earliest first.
+ * This is the cache rewrite of [Notes s2.8] (eq. (1) of the paper) carried
+ * out step by step, and equally the prompt-end alignment described there.
+ *   k, w : [S, L, d]  beta : [S, L]  out : [S, t+1, d]
+ * Returns 0, or -1 if t is out of range.
+ */
+int oracle_transported_keys(int S, int L, int d, const double *k,
+                            const double *w, const double *beta, int t,
+                            double *out)
+{
+    if (t < 0 || t >= L) return -1;
+    #pragma omp parallel for schedule(static)
+    for (long sj = 0; sj < (long)S * (t + 1); ++sj) {
+        long s = sj / (t + 1);
+        int j = (int)(sj % (t + 1));
+        const size_t off = (size_t)s * L;
+        double *z = out + (size_t)sj * d;
+        memcpy(z, k + (off + j) * d, sizeof(double) * d);
+        for (int u = j + 1; u <= t; ++u)
+            apply_transition(d, w + (off + u) * d, beta[off + u], z);
+    }
+    return 0;
+}
+
+/* Number of OpenMP threads a parallel region of this library would use. */
+int oracle_num_threads(void)
+{
+    int n = 1;
+    #pragma omp parallel
+    {
+        #pragma omp single
+        {
+#ifdef _OPENMP
+            extern int omp_get_num_threads(void);
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}
