@@ -1,0 +1,286 @@
+"""libpath_attn: PaTH attention prefill and decode for AMD Instinct MI355X.
+
+Thin ctypes binding over the C ABI in include/path_attn.h.  It only marshals
+arguments: torch tensors supply device memory and the current stream; every
+step of the computation runs in the library's HIP kernels.  There is no
+fallback: if libpath_attn.so is missing or a call fails, an exception is
+raised.
+
+The operation (reading-notes page "PaTH Attention:通过累积 Householder
+变换编码位置", sections 2.1 and 2.5): with H_t = I - beta_t w_t w_t^T,
+    logit(i, j) = scale * k_j^T H_{j+1}...H_i q_i + sum_{s=j+1..i} log f_s,
+for j <= i, then a causal softmax and the value sum; lse is the natural-log
+log-sum-exp of each row's logits.  Decoding (section 2.8) keeps keys already
+rewritten by every later transition, so a plain softmax over the cache gives
+the same scores.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpath_attn.so")
+
+PATH_F32, PATH_BF16 = 0, 1
+_STATUS = ["ok", "null pointer", "bad shape", "bad dtype", "unsupported",
+           "misaligned pointer", "workspace too small", "cache capacity exceeded",
+           "kernel launch failed"]
+
+
+class PathAttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        self.status = status
+        name = _STATUS[status] if 0 <= status < len(_STATUS) else str(status)
+        super().__init__(f"libpath_attn: {name} ({status}): {msg}")
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int), ("H", ctypes.c_int), ("L", ctypes.c_int),
+                ("d", ctypes.c_int), ("dtype", ctypes.c_int), ("scale", ctypes.c_float),
+                ("block", ctypes.c_int)]
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("cap", ctypes.c_int), ("k_dtype", ctypes.c_int),
+                ("kcache", ctypes.c_void_p), ("vcache", ctypes.c_void_p),
+                ("gcache", ctypes.c_void_p)]
+
+
+_lib = None
+
+EXPORTS = ["path_abi_version", "path_status_str", "path_last_error",
+           "path_attn_fwd_workspace", "path_attn_fwd", "path_kv_update",
+           "path_kv_append", "path_decode_workspace", "path_decode",
+           "path_decode_step", "path_causal_attn_fwd"]
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libpath_attn.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libpath_attn.so not built ({path}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    DP, CP = ctypes.POINTER(_Desc), ctypes.POINTER(_Cache)
+    sig = {
+        "path_abi_version": ([], I),
+        "path_status_str": ([I], ctypes.c_char_p),
+        "path_last_error": ([], ctypes.c_char_p),
+        "path_attn_fwd_workspace": ([DP, I], S),
+        "path_attn_fwd": ([DP, P, P, P, P, P, P, P, P, CP, P, S, P], I),
+        "path_kv_update": ([DP, CP, I, P, P, P], I),
+        "path_kv_append": ([DP, CP, I, P, P, P, P], I),
+        "path_decode_workspace": ([DP, I], S),
+        "path_decode": ([DP, CP, I, P, P, P, P, S, P], I),
+        "path_decode_step": ([DP, CP, I, P, P, P, P, P, P, P, P, P, S, P], I),
+        "path_causal_attn_fwd": ([DP, P, P, P, P, P, P], I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise PathAttnError(status, _lib.path_last_error().decode())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return PATH_F32
+    if t == torch.bfloat16:
+        return PATH_BF16
+    raise PathAttnError(3, f"unsupported dtype {t}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dev, shape=None, dtype=None):
+    if not t.is_cuda or t.device != dev:
+        raise ValueError(f"{name} must be on {dev}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _desc(N, H, L, d, dtype, scale, block=0):
+    return _Desc(N, H, L, d, _dtype_code(dtype), float(scale), int(block))
+
+
+def fwd_workspace_bytes(N, H, L, d, dtype, with_cache=False, block=0) -> int:
+    lib = load_library()
+    return int(lib.path_attn_fwd_workspace(ctypes.byref(_desc(N, H, L, d, dtype, 1.0, block)),
+                                           int(bool(with_cache))))
+
+
+class Cache:
+    """Decode cache: kcache/vcache [N,H,cap,d], gcache [N,H,cap] (or None).
+
+    kcache holds every key rewritten by all transitions after it; gcache holds
+    inclusive prefix sums of log f when the forget gate is used.
+    """
+
+    def __init__(self, N, H, cap, d, dtype=torch.bfloat16, k_dtype=None,
+                 gate=True, device="cuda"):
+        self.N, self.H, self.cap, self.d = N, H, cap, d
+        self.dtype = dtype
+        self.k_dtype = dtype if k_dtype is None else k_dtype
+        self.kcache = torch.zeros(N, H, cap, d, dtype=self.k_dtype, device=device)
+        self.vcache = torch.zeros(N, H, cap, d, dtype=dtype, device=device)
+        self.gcache = torch.zeros(N, H, cap, dtype=torch.float32, device=device) if gate else None
+        self.device = self.kcache.device
+
+    def _c(self):
+        return _Cache(self.cap, _dtype_code(self.k_dtype), self.kcache.data_ptr(),
+                      self.vcache.data_ptr(),
+                      self.gcache.data_ptr() if self.gcache is not None else None)
+
+
+def fwd(q, k, v, w, beta, logf=None, scale=None, cache: Cache | None = None,
+        block=0, workspace: torch.Tensor | None = None, out=None):
+    """Prefill forward.  q,k,v,w [N,H,L,d] (fp32 or bf16); beta, logf [N,H,L] fp32.
+
+    Returns (o [N,H,L,d], lse [N,H,L] fp32).  If cache is given, it is filled
+    with the prompt's keys aligned to the last position, values and log-f
+    prefix sums.
+    """
+    lib = load_library()
+    N, H, L, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("w", w)):
+        _need(t, name, dev, (N, H, L, d), q.dtype)
+    _need(beta, "beta", dev, (N, H, L), torch.float32)
+    if logf is not None:
+        _need(logf, "logf", dev, (N, H, L), torch.float32)
+    scale = d ** -0.5 if scale is None else scale
+    desc = _desc(N, H, L, d, q.dtype, scale, block)
+    nbytes = int(lib.path_attn_fwd_workspace(ctypes.byref(desc), int(cache is not None)))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty(N, H, L, dtype=torch.float32, device=dev)
+    else:
+        o, lse = out
+    cc = cache._c() if cache is not None else None
+    _check(lib.path_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w),
+                             _ptr(beta), _ptr(logf), _ptr(o), _ptr(lse),
+                             ctypes.byref(cc) if cc is not None else None,
+                             _ptr(workspace), workspace.numel(), _stream(dev)))
+    return o, lse
+
+
+def _cache_desc(cache: Cache, scale):
+    return _desc(cache.N, cache.H, 1, cache.d, cache.dtype, scale)
+
+
+def kv_update(cache: Cache, n: int, w_t, beta_t):
+    """k_j <- k_j - beta_t (w_t . k_j) w_t for slots j < n (in place)."""
+    lib = load_library()
+    _need(w_t, "w_t", cache.device, (cache.N, cache.H, cache.d), cache.dtype)
+    _need(beta_t, "beta_t", cache.device, (cache.N, cache.H), torch.float32)
+    desc = _cache_desc(cache, 1.0)
+    cc = cache._c()
+    _check(lib.path_kv_update(ctypes.byref(desc), ctypes.byref(cc), int(n), _ptr(w_t),
+                              _ptr(beta_t), _stream(cache.device)))
+
+
+def kv_append(cache: Cache, n: int, k_t, v_t, logf_t=None):
+    """Write token n: key (unrewritten), value and log-f prefix."""
+    lib = load_library()
+    for name, t in (("k_t", k_t), ("v_t", v_t)):
+        _need(t, name, cache.device, (cache.N, cache.H, cache.d), cache.dtype)
+    if logf_t is not None:
+        _need(logf_t, "logf_t", cache.device, (cache.N, cache.H), torch.float32)
+    desc = _cache_desc(cache, 1.0)
+    cc = cache._c()
+    _check(lib.path_kv_append(ctypes.byref(desc), ctypes.byref(cc), int(n), _ptr(k_t),
+                              _ptr(v_t), _ptr(logf_t), _stream(cache.device)))
+
+
+def decode_workspace_bytes(cache: Cache, n_keys: int) -> int:
+    lib = load_library()
+    return int(lib.path_decode_workspace(ctypes.byref(_cache_desc(cache, 1.0)), int(n_keys)))
+
+
+def decode(cache: Cache, n_keys: int, q_t, scale=None, workspace=None, out=None):
+    """Attend q_t [N,H,d] over cache slots [0, n_keys). Returns (o_t, lse_t)."""
+    lib = load_library()
+    _need(q_t, "q_t", cache.device, (cache.N, cache.H, cache.d), cache.dtype)
+    scale = cache.d ** -0.5 if scale is None else scale
+    desc = _cache_desc(cache, scale)
+    nbytes = decode_workspace_bytes(cache, n_keys)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=cache.device)
+    if out is None:
+        o = torch.empty_like(q_t)
+        lse = torch.empty(cache.N, cache.H, dtype=torch.float32, device=cache.device)
+    else:
+        o, lse = out
+    cc = cache._c()
+    _check(lib.path_decode(ctypes.byref(desc), ctypes.byref(cc), int(n_keys), _ptr(q_t),
+                           _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
+                           _stream(cache.device)))
+    return o, lse
+
+
+def decode_step(cache: Cache, n: int, q_t, k_t, v_t, w_t, beta_t, logf_t=None,
+                scale=None, workspace=None, out=None):
+    """Fused step at position n: rewrite slots < n, append token n, attend."""
+    lib = load_library()
+    for name, t in (("q_t", q_t), ("k_t", k_t), ("v_t", v_t), ("w_t", w_t)):
+        _need(t, name, cache.device, (cache.N, cache.H, cache.d), cache.dtype)
+    _need(beta_t, "beta_t", cache.device, (cache.N, cache.H), torch.float32)
+    if logf_t is not None:
+        _need(logf_t, "logf_t", cache.device, (cache.N, cache.H), torch.float32)
+    scale = cache.d ** -0.5 if scale is None else scale
+    desc = _cache_desc(cache, scale)
+    nbytes = decode_workspace_bytes(cache, n + 1)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=cache.device)
+    if out is None:
+        o = torch.empty_like(q_t)
+        lse = torch.empty(cache.N, cache.H, dtype=torch.float32, device=cache.device)
+    else:
+        o, lse = out
+    cc = cache._c()
+    _check(lib.path_decode_step(ctypes.byref(desc), ctypes.byref(cc), int(n), _ptr(q_t),
+                                _ptr(k_t), _ptr(v_t), _ptr(w_t), _ptr(beta_t), _ptr(logf_t),
+                                _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                _stream(cache.device)))
+    return o, lse
+
+
+def causal_attn(q, k, v, scale=None, out=None):
+    """Plain causal softmax attention (the beta = 0 baseline kernel)."""
+    lib = load_library()
+    N, H, L, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.device, (N, H, L, d), q.dtype)
+    scale = d ** -0.5 if scale is None else scale
+    desc = _desc(N, H, L, d, q.dtype, scale)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty(N, H, L, dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    _check(lib.path_causal_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                    _ptr(lse), _stream(q.device)))
+    return o, lse

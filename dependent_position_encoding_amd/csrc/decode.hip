@@ -1,0 +1,454 @@
+// decode.hip -- decoding over a rewritten key cache, and the prefill-to-cache
+// alignment.  All kernels here are bound by HBM bandwidth: each cached key
+// row is read (and, for the rewrite, written) once per call with 16-byte
+// vector accesses.
+//
+// Citations: [Notes s2.x] = reading-notes page "PaTH Attention:通过累积
+// Householder 变换编码位置" (cc.laoqi.cc), section 2.x; [Explainer s3] =
+// explainer page "PaTH Attention: Position Encoding via Accumulating
+// Householder Transformations" (gist.science), section 3.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace pa {
+
+// 16 bytes of a row: 8 bf16 or 4 float32 values.
+template <typename T> struct Vec;
+template <> struct Vec<bf16> {
+    static constexpr int n = 8;
+    uint4 raw;
+    __device__ void load(const bf16* p) { raw = *reinterpret_cast<const uint4*>(p); }
+    __device__ void store(bf16* p) const { *reinterpret_cast<uint4*>(p) = raw; }
+    __device__ float get(int i) const {
+        uint32_t wd = (&raw.x)[i >> 1];
+        union { uint32_t u; float f; } c;
+        c.u = (i & 1) ? (wd & 0xffff0000u) : (wd << 16);
+        return c.f;
+    }
+    __device__ void set(int i, float f) {
+        uint32_t b = f32_to_bf16(f).bits;
+        uint32_t& wd = (&raw.x)[i >> 1];
+        wd = (i & 1) ? ((wd & 0x0000ffffu) | (b << 16)) : ((wd & 0xffff0000u) | b);
+    }
+};
+template <> struct Vec<float> {
+    static constexpr int n = 4;
+    float4 raw;
+    __device__ void load(const float* p) { raw = *reinterpret_cast<const float4*>(p); }
+    __device__ void store(float* p) const { *reinterpret_cast<float4*>(p) = raw; }
+    __device__ float get(int i) const { return (&raw.x)[i]; }
+    __device__ void set(int i, float f) { (&raw.x)[i] = f; }
+};
+
+// Sum over the TPR consecutive lanes that share one row.
+template <int TPR>
+__device__ inline float group_sum(float x) {
+#pragma unroll
+    for (int off = TPR / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// ---------------------------------------------------------------------------
+// Cache rewrite for a new position [Notes s2.8, eq. (1)]:
+//   k_j <- k_j - beta_t (w_t . k_j) w_t  for j in [0, n).
+// Grid: (row tiles, slices).  Each group of TPR lanes owns one row.
+template <typename K, typename T, int D>
+__global__ void __launch_bounds__(256)
+kv_update_kernel(K* __restrict__ kc, int cap, int n, const T* __restrict__ w_t,
+                 const float* __restrict__ beta_t, int rows_per_block) {
+    constexpr int VN = Vec<K>::n, TPR = D / VN, GROUPS = 256 / TPR;
+    const int slice = blockIdx.y;
+    const int lane_in = threadIdx.x % TPR, grp = threadIdx.x / TPR;
+    float wv[VN];
+#pragma unroll
+    for (int e = 0; e < VN; ++e) wv[e] = to_f32(w_t[(size_t)slice * D + lane_in * VN + e]);
+    const float bt = beta_t[slice];
+    K* base = kc + (size_t)slice * cap * D;
+    const int j0 = blockIdx.x * rows_per_block;
+    const int j1 = min(n, j0 + rows_per_block);
+    for (int j = j0 + grp; j < j1; j += GROUPS) {
+        Vec<K> x;
+        x.load(base + (size_t)j * D + lane_in * VN);
+        float p = 0.f;
+#pragma unroll
+        for (int e = 0; e < VN; ++e) p += wv[e] * x.get(e);
+        const float cf = bt * group_sum<TPR>(p);
+#pragma unroll
+        for (int e = 0; e < VN; ++e) x.set(e, x.get(e) - cf * wv[e]);
+        x.store(base + (size_t)j * D + lane_in * VN);
+    }
+}
+
+// Append one token at slot n: its key unrewritten, its value, and the
+// inclusive log-f prefix.  One block per slice.
+template <typename K, typename T, int D>
+__global__ void kv_append_kernel(K* __restrict__ kc, T* __restrict__ vc,
+                                 float* __restrict__ gc, int cap, int n,
+                                 const T* __restrict__ k_t, const T* __restrict__ v_t,
+                                 const float* __restrict__ logf_t) {
+    const int slice = blockIdx.x;
+    const size_t slot = ((size_t)slice * cap + n) * D;
+    for (int x = threadIdx.x; x < D; x += blockDim.x) {
+        kc[slot + x] = from_f32<K>(to_f32(k_t[(size_t)slice * D + x]));
+        vc[slot + x] = v_t[(size_t)slice * D + x];
+    }
+    if (gc && threadIdx.x == 0) {
+        const float prev = n > 0 ? gc[(size_t)slice * cap + n - 1] : 0.f;
+        gc[(size_t)slice * cap + n] = prev + logf_t[slice];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Single-query attention over one chunk of cached keys, optionally fused with
+// the rewrite and the append of the current token [Notes s2.8].
+//   score_j = scale * q_t . k_j + (C_t - C_j),  C = inclusive log-f prefix.
+// Each group of TPR lanes walks its keys with a running (max, sum, acc) in the
+// natural-exp domain; the 256/TPR groups are merged through LDS and the
+// chunk's partial state (m, l, acc[D]) goes to part[slice][chunk].
+template <typename K, typename T, int D, bool FUSED>
+__global__ void __launch_bounds__(256)
+decode_chunk_kernel(K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ gc,
+                    int cap, int n_keys, int chunk, float scale,
+                    const T* __restrict__ q_t, const T* __restrict__ k_t,
+                    const T* __restrict__ v_t, const T* __restrict__ w_t,
+                    const float* __restrict__ beta_t, const float* __restrict__ logf_t,
+                    float* __restrict__ part) {
+    constexpr int VN = Vec<K>::n, TPR = D / VN, GROUPS = 256 / TPR;
+    const int slice = blockIdx.y, ch = blockIdx.x, nch = gridDim.x;
+    const int lane_in = threadIdx.x % TPR, grp = threadIdx.x / TPR;
+    const int t = n_keys - 1;                     // query position
+    const size_t sd = (size_t)slice * D + lane_in * VN;
+
+    float qv[VN], wv[VN], acc[VN];
+#pragma unroll
+    for (int e = 0; e < VN; ++e) {
+        qv[e] = to_f32(q_t[sd + e]);
+        wv[e] = FUSED ? to_f32(w_t[sd + e]) : 0.f;
+        acc[e] = 0.f;
+    }
+    const float bt = FUSED ? beta_t[slice] : 0.f;
+    float* gbase = gc ? gc + (size_t)slice * cap : nullptr;
+    float ct = 0.f;                               // C_t
+    if (gbase) {
+        if (FUSED) ct = (t > 0 ? gbase[t - 1] : 0.f) + logf_t[slice];
+        else ct = gbase[t];
+    }
+    K* kbase = kc + (size_t)slice * cap * D;
+    T* vbase = vc + (size_t)slice * cap * D;
+
+    float m = -INFINITY, l = 0.f;
+    const int j0 = ch * chunk, j1 = min(n_keys, j0 + chunk);
+    for (int j = j0 + grp; j < j1; j += GROUPS) {
+        float kf[VN], vf[VN], bias;
+        const size_t off = (size_t)j * D + lane_in * VN;
+        if (FUSED && j == t) {
+            // the new token: stored as given, its own transition excluded
+#pragma unroll
+            for (int e = 0; e < VN; ++e) {
+                kf[e] = to_f32(from_f32<K>(to_f32(k_t[sd + e])));
+                vf[e] = to_f32(v_t[sd + e]);
+                kbase[off + e] = from_f32<K>(kf[e]);
+                vbase[off + e] = v_t[sd + e];
+            }
+            if (gbase && lane_in == 0) gbase[t] = ct;
+            bias = 0.f;
+        } else {
+            Vec<K> x;
+            x.load(kbase + off);
+            if (FUSED) {
+                float p = 0.f;
+#pragma unroll
+                for (int e = 0; e < VN; ++e) p += wv[e] * x.get(e);
+                const float cf = bt * group_sum<TPR>(p);
+#pragma unroll
+                for (int e = 0; e < VN; ++e) x.set(e, x.get(e) - cf * wv[e]);
+                x.store(kbase + off);
+            }
+#pragma unroll
+            for (int e = 0; e < VN; ++e) {
+                kf[e] = x.get(e);
+                vf[e] = to_f32(vbase[off + e]);
+            }
+            bias = gbase ? ct - gbase[j] : 0.f;
+        }
+        float p = 0.f;
+#pragma unroll
+        for (int e = 0; e < VN; ++e) p += qv[e] * kf[e];
+        const float s = scale * group_sum<TPR>(p) + bias;
+        const float mn = fmaxf(m, s);
+        const float alpha = __expf(m - mn), pe = __expf(s - mn);
+        l = l * alpha + pe;
+#pragma unroll
+        for (int e = 0; e < VN; ++e) acc[e] = acc[e] * alpha + pe * vf[e];
+        m = mn;
+    }
+
+    // merge the groups of this block
+    __shared__ float sm[GROUPS], sl[GROUPS];
+    __shared__ float sacc[GROUPS][D + 1];
+    if (lane_in == 0) { sm[grp] = m; sl[grp] = l; }
+#pragma unroll
+    for (int e = 0; e < VN; ++e) sacc[grp][lane_in * VN + e] = acc[e];
+    __syncthreads();
+    float* out = part + ((size_t)slice * nch + ch) * (D + 2);
+    if (threadIdx.x < D) {
+        const int x = threadIdx.x;
+        float M = -INFINITY;
+        for (int g = 0; g < GROUPS; ++g) M = fmaxf(M, sm[g]);
+        float a = 0.f, ls = 0.f;
+        for (int g = 0; g < GROUPS; ++g) {
+            const float f = (sm[g] == -INFINITY) ? 0.f : __expf(sm[g] - M);
+            a += sacc[g][x] * f;
+            ls += sl[g] * f;
+        }
+        out[2 + x] = a;
+        if (x == 0) { out[0] = M; out[1] = ls; }
+    }
+}
+
+// Merge the chunk partials of one slice: o = sum acc_c e^{m_c - M} / l,
+// lse = M + log l.
+template <typename T, int D>
+__global__ void decode_combine_kernel(const float* __restrict__ part, int nch,
+                                      T* __restrict__ o_t, float* __restrict__ lse_t) {
+    const int slice = blockIdx.x;
+    const float* p = part + (size_t)slice * nch * (D + 2);
+    float M = -INFINITY;
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, p[(size_t)c * (D + 2)]);
+    const int x = threadIdx.x;
+    float a = 0.f, ls = 0.f;
+    for (int c = 0; c < nch; ++c) {
+        const float mc = p[(size_t)c * (D + 2)];
+        const float f = (mc == -INFINITY) ? 0.f : __expf(mc - M);
+        ls += p[(size_t)c * (D + 2) + 1] * f;
+        if (x < D) a += p[(size_t)c * (D + 2) + 2 + x] * f;
+    }
+    if (x < D) o_t[(size_t)slice * D + x] = from_f32<T>(a / ls);
+    if (x == 0 && lse_t) lse_t[slice] = M + logf(ls);
+}
+
+// ---------------------------------------------------------------------------
+// Prefill -> decode alignment [Notes s2.8]: the cache must hold every prompt
+// key moved to the prompt end, H_{L-1} ... H_{j+1} k_j.  Keys already sit at
+// their block's right edge (Kright); the rest of the way is the product of
+// the later blocks' transitions.  In row form, kcache_c = Kright_c S_c with
+//   S_{nb-1} = I,  S_c = F_{c+1} S_{c+1},  F_c = I - E_c.
+// suffix_kernel runs that chain (one block per slice, sequential over c);
+// the block-prefix of log f is accumulated alongside.
+template <int D>
+__global__ void __launch_bounds__(256)
+suffix_kernel(int nb, FwdWs ws) {
+    __shared__ float sS[D][D + 1], sE[D][D + 1];
+    const int slice = blockIdx.x, tid = threadIdx.x;
+    for (int e = tid; e < D * D; e += 256) sS[e / D][e % D] = (e / D == e % D) ? 1.f : 0.f;
+    const size_t b0 = (size_t)slice * nb;
+    for (int e = tid; e < D * D; e += 256) ws.suf[(b0 + nb - 1) * D * D + e] = (e / D == e % D) ? 1.f : 0.f;
+    if (tid == 0) {
+        double acc = 0.0;
+        for (int c = 0; c < nb; ++c) {
+            ws.gpre[b0 + c] = (float)acc;
+            acc += ws.tot[b0 + c];
+        }
+    }
+    for (int c = nb - 2; c >= 0; --c) {
+        __syncthreads();
+        for (int e = tid; e < D * D; e += 256) sE[e / D][e % D] = ws.e32[(b0 + c + 1) * D * D + e];
+        __syncthreads();
+        float r[D * D / 256 > 0 ? D * D / 256 : 1];
+        int cnt = 0;
+        for (int e = tid; e < D * D; e += 256, ++cnt) {
+            const int x = e / D, y = e % D;
+            float s = 0.f;
+            for (int z = 0; z < D; ++z) s += sE[x][z] * sS[z][y];
+            r[cnt] = sS[x][y] - s;
+        }
+        __syncthreads();
+        cnt = 0;
+        for (int e = tid; e < D * D; e += 256, ++cnt) {
+            sS[e / D][e % D] = r[cnt];
+            ws.suf[(b0 + c) * D * D + e] = r[cnt];
+        }
+    }
+}
+
+// kcache rows of block c = Kright_c S_c; values copied; gcache = block prefix
+// + in-block cumsum.  One block of 256 threads per (slice, c).
+template <typename K, typename T, int B, int D>
+__global__ void __launch_bounds__(256)
+align_apply_kernel(int L, int nb, FwdWs ws, const T* __restrict__ v, int has_gate,
+                   K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ gc, int cap) {
+    __shared__ float sS[D][D + 1], sK[B][D + 1];
+    const int blk = blockIdx.x, slice = blk / nb, c = blk % nb, tid = threadIdx.x;
+    for (int e = tid; e < D * D; e += 256) sS[e / D][e % D] = ws.suf[(size_t)blk * D * D + e];
+    for (int e = tid; e < B * D; e += 256) sK[e / D][e % D] = ws.k32[(size_t)blk * B * D + e];
+    __syncthreads();
+    for (int e = tid; e < B * D; e += 256) {
+        const int r = e / D, y = e % D, pos = c * B + r;
+        if (pos >= L) continue;
+        float s = 0.f;
+        for (int x = 0; x < D; ++x) s += sK[r][x] * sS[x][y];
+        const size_t dst = ((size_t)slice * cap + pos) * D + y;
+        kc[dst] = from_f32<K>(s);
+        vc[dst] = v[((size_t)slice * L + pos) * D + y];
+    }
+    if (gc && tid < B) {
+        const int pos = c * B + tid;
+        if (pos < L)
+            gc[(size_t)slice * cap + pos] =
+                has_gate ? ws.gpre[blk] + ws.gl[(size_t)blk * B + tid] : 0.f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <typename K, typename T, int D>
+static hipError_t kv_update_t(const CacheArgs& c, int n, const void* w_t,
+                              const float* beta_t, hipStream_t st) {
+    const int rows = 256;
+    dim3 grid((n + rows - 1) / rows, c.N * c.H);
+    hipLaunchKernelGGL((kv_update_kernel<K, T, D>), grid, dim3(256), 0, st,
+                       (K*)c.kcache, c.cap, n, (const T*)w_t, beta_t, rows);
+    return hipGetLastError();
+}
+
+template <typename K, typename T>
+static hipError_t kv_update_d(const CacheArgs& c, int n, const void* w_t,
+                              const float* beta_t, hipStream_t st) {
+    switch (c.d) {
+        case 16: return kv_update_t<K, T, 16>(c, n, w_t, beta_t, st);
+        case 32: return kv_update_t<K, T, 32>(c, n, w_t, beta_t, st);
+        case 64: return kv_update_t<K, T, 64>(c, n, w_t, beta_t, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_kv_update(const CacheArgs& c, int n, const void* w_t,
+                            const float* beta_t, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    if (c.k_bf16)
+        return c.v_bf16 ? kv_update_d<bf16, bf16>(c, n, w_t, beta_t, st)
+                        : kv_update_d<bf16, float>(c, n, w_t, beta_t, st);
+    return c.v_bf16 ? kv_update_d<float, bf16>(c, n, w_t, beta_t, st)
+                    : kv_update_d<float, float>(c, n, w_t, beta_t, st);
+}
+
+template <typename K, typename T, int D>
+static hipError_t kv_append_t(const CacheArgs& c, int n, const void* k_t,
+                              const void* v_t, const float* logf_t, hipStream_t st) {
+    hipLaunchKernelGGL((kv_append_kernel<K, T, D>), dim3(c.N * c.H), dim3(64), 0, st,
+                       (K*)c.kcache, (T*)c.vcache, c.gcache, c.cap, n,
+                       (const T*)k_t, (const T*)v_t, logf_t);
+    return hipGetLastError();
+}
+
+template <typename K, typename T>
+static hipError_t kv_append_d(const CacheArgs& c, int n, const void* k_t,
+                              const void* v_t, const float* logf_t, hipStream_t st) {
+    switch (c.d) {
+        case 16: return kv_append_t<K, T, 16>(c, n, k_t, v_t, logf_t, st);
+        case 32: return kv_append_t<K, T, 32>(c, n, k_t, v_t, logf_t, st);
+        case 64: return kv_append_t<K, T, 64>(c, n, k_t, v_t, logf_t, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_kv_append(const CacheArgs& c, int n, const void* k_t,
+                            const void* v_t, const float* logf_t, hipStream_t st) {
+    if (c.k_bf16)
+        return c.v_bf16 ? kv_append_d<bf16, bf16>(c, n, k_t, v_t, logf_t, st)
+                        : kv_append_d<bf16, float>(c, n, k_t, v_t, logf_t, st);
+    return c.v_bf16 ? kv_append_d<float, bf16>(c, n, k_t, v_t, logf_t, st)
+                    : kv_append_d<float, float>(c, n, k_t, v_t, logf_t, st);
+}
+
+int decode_chunk(int n_keys) {
+    // enough chunks per slice to cover the chip, each at least 256 keys
+    (void)n_keys;
+    return 256;
+}
+
+template <typename K, typename T, int D>
+static hipError_t decode_t(const CacheArgs& c, int n_keys, float scale, const void* q_t,
+                           void* o_t, float* lse_t, float* part, int chunk, bool fused,
+                           const void* k_t, const void* v_t, const void* w_t,
+                           const float* beta_t, const float* logf_t, hipStream_t st) {
+    const int nch = (n_keys + chunk - 1) / chunk;
+    dim3 grid(nch, c.N * c.H);
+    if (fused)
+        hipLaunchKernelGGL((decode_chunk_kernel<K, T, D, true>), grid, dim3(256), 0, st,
+                           (K*)c.kcache, (T*)c.vcache, c.gcache, c.cap, n_keys, chunk, scale,
+                           (const T*)q_t, (const T*)k_t, (const T*)v_t, (const T*)w_t,
+                           beta_t, logf_t, part);
+    else
+        hipLaunchKernelGGL((decode_chunk_kernel<K, T, D, false>), grid, dim3(256), 0, st,
+                           (K*)c.kcache, (T*)c.vcache, c.gcache, c.cap, n_keys, chunk, scale,
+                           (const T*)q_t, nullptr, nullptr, nullptr, nullptr, nullptr, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(c.N * c.H), dim3(64), 0, st,
+                       (const float*)part, nch, (T*)o_t, lse_t);
+    return hipGetLastError();
+}
+
+template <typename K, typename T>
+static hipError_t decode_d(const CacheArgs& c, int n_keys, float scale, const void* q_t,
+                           void* o_t, float* lse_t, float* part, int chunk, bool fused,
+                           const void* k_t, const void* v_t, const void* w_t,
+                           const float* beta_t, const float* logf_t, hipStream_t st) {
+    switch (c.d) {
+        case 16: return decode_t<K, T, 16>(c, n_keys, scale, q_t, o_t, lse_t, part, chunk, fused, k_t, v_t, w_t, beta_t, logf_t, st);
+        case 32: return decode_t<K, T, 32>(c, n_keys, scale, q_t, o_t, lse_t, part, chunk, fused, k_t, v_t, w_t, beta_t, logf_t, st);
+        case 64: return decode_t<K, T, 64>(c, n_keys, scale, q_t, o_t, lse_t, part, chunk, fused, k_t, v_t, w_t, beta_t, logf_t, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const CacheArgs& c, int n_keys, float scale, const void* q_t,
+                         void* o_t, float* lse_t, float* part, int chunk, bool fused,
+                         const void* k_t, const void* v_t, const void* w_t,
+                         const float* beta_t, const float* logf_t, hipStream_t st) {
+    if (c.k_bf16)
+        return c.v_bf16 ? decode_d<bf16, bf16>(c, n_keys, scale, q_t, o_t, lse_t, part, chunk, fused, k_t, v_t, w_t, beta_t, logf_t, st)
+                        : decode_d<bf16, float>(c, n_keys, scale, q_t, o_t, lse_t, part, chunk, fused, k_t, v_t, w_t, beta_t, logf_t, st);
+    return c.v_bf16 ? decode_d<float, bf16>(c, n_keys, scale, q_t, o_t, lse_t, part, chunk, fused, k_t, v_t, w_t, beta_t, logf_t, st)
+                    : decode_d<float, float>(c, n_keys, scale, q_t, o_t, lse_t, part, chunk, fused, k_t, v_t, w_t, beta_t, logf_t, st);
+}
+
+template <typename K, typename T, int B, int D>
+static hipError_t align_t(const FwdArgs& a, const CacheArgs& c, hipStream_t st) {
+    const int nb = (a.L + B - 1) / B;
+    hipLaunchKernelGGL((suffix_kernel<D>), dim3(a.N * a.H), dim3(256), 0, st, nb, a.ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((align_apply_kernel<K, T, B, D>), dim3(a.N * a.H * nb), dim3(256), 0, st,
+                       a.L, nb, a.ws, (const T*)a.v, a.logf ? 1 : 0, (K*)c.kcache,
+                       (T*)c.vcache, c.gcache, c.cap);
+    return hipGetLastError();
+}
+
+template <typename K, typename T, int B>
+static hipError_t align_d(const FwdArgs& a, const CacheArgs& c, hipStream_t st) {
+    switch (a.d) {
+        case 16: return align_t<K, T, B, 16>(a, c, st);
+        case 32: return align_t<K, T, B, 32>(a, c, st);
+        case 64: return align_t<K, T, B, 64>(a, c, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename K, typename T>
+static hipError_t align_b(const FwdArgs& a, const CacheArgs& c, hipStream_t st) {
+    switch (a.block) {
+        case 16: return align_d<K, T, 16>(a, c, st);
+        case 32: return align_d<K, T, 32>(a, c, st);
+        case 64: return align_d<K, T, 64>(a, c, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_kv_align(const FwdArgs& a, const CacheArgs& c, hipStream_t st) {
+    if (c.k_bf16)
+        return a.bf16 ? align_b<bf16, bf16>(a, c, st) : align_b<bf16, float>(a, c, st);
+    return a.bf16 ? align_b<float, bf16>(a, c, st) : align_b<float, float>(a, c, st);
+}
+
+}  // namespace pa

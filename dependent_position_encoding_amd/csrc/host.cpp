@@ -1,0 +1,289 @@
+// host.cpp -- the C ABI of libpath_attn (declared in include/path_attn.h):
+// argument validation, workspace sizing and carving, kernel dispatch.
+// Every argument error is detected here, before anything is enqueued.
+#include "path_attn.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+path_status fail(path_status s, const std::string& msg) {
+    g_last_error = msg;
+    return s;
+}
+
+path_status ok() {
+    g_last_error.clear();
+    return PATH_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool valid_dtype(path_dtype t) { return t == PATH_F32 || t == PATH_BF16; }
+
+size_t esize(path_dtype t) { return t == PATH_F32 ? 4 : 2; }
+
+int block_of(const path_fwd_desc* d) { return d->block == 0 ? 64 : d->block; }
+
+// Which forward kernels serve this description.
+bool use_mfma(const path_fwd_desc* d) {
+    return d->dtype == PATH_BF16 && pa::fwd_bf16_supported(d->d, block_of(d));
+}
+
+path_status check_desc(const path_fwd_desc* d, bool need_L) {
+    if (!d) return fail(PATH_E_NULL, "desc is NULL");
+    if (d->N < 1 || d->H < 1 || (need_L && d->L < 1))
+        return fail(PATH_E_SHAPE, "N, H and L must be >= 1");
+    if (!valid_dtype(d->dtype)) return fail(PATH_E_DTYPE, "unknown dtype");
+    if (d->d != 16 && d->d != 32 && d->d != 64)
+        return fail(PATH_E_UNSUPPORTED, "head dim must be 16, 32 or 64");
+    const int B = block_of(d);
+    if (B != 16 && B != 32 && B != 64)
+        return fail(PATH_E_UNSUPPORTED, "block must be 0, 16, 32 or 64");
+    if (d->dtype == PATH_BF16 && B != 64)
+        return fail(PATH_E_UNSUPPORTED, "bf16 inputs use block 64");
+    if ((size_t)d->N * d->H * (need_L ? d->L : 1) * d->d > ((size_t)1 << 40))
+        return fail(PATH_E_SHAPE, "problem too large");
+    return PATH_OK;
+}
+
+struct Layout {
+    size_t kr, vt, em, ql, dg, gl, tot, k32, e32, suf, gpre, total;
+};
+
+Layout fwd_layout(const path_fwd_desc* d, bool with_cache) {
+    const int B = block_of(d), D = d->d;
+    const size_t nb = (size_t)(d->L + B - 1) / B;
+    const size_t nblk = (size_t)d->N * d->H * nb;
+    const bool mf = use_mfma(d);
+    const size_t op = mf ? 2 : 4;       // operand element size
+    Layout l{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
+    l.kr = take(nblk * B * D * op);
+    l.vt = mf ? take(nblk * B * D * 2) : 0;
+    l.em = take(nblk * D * D * op);
+    l.ql = take(nblk * B * D * 4);
+    l.dg = take(nblk * B * B * 4);
+    l.gl = take(nblk * B * 4);
+    l.tot = take(nblk * 4);
+    if (with_cache) {
+        l.k32 = take(nblk * B * D * 4);
+        l.e32 = take(nblk * D * D * 4);
+        l.suf = take(nblk * D * D * 4);
+        l.gpre = take(nblk * 4);
+    }
+    l.total = off;
+    return l;
+}
+
+path_status check_cache(const path_fwd_desc* d, const path_cache* c) {
+    if (!c) return fail(PATH_E_NULL, "cache is NULL");
+    if (!c->kcache || !c->vcache) return fail(PATH_E_NULL, "kcache/vcache is NULL");
+    if (c->cap < 1) return fail(PATH_E_SHAPE, "cache capacity must be >= 1");
+    if (!valid_dtype(c->k_dtype)) return fail(PATH_E_DTYPE, "unknown kcache dtype");
+    if (!aligned(c->kcache, 16) || !aligned(c->vcache, 16) || !aligned(c->gcache, 4))
+        return fail(PATH_E_ALIGN, "cache pointers must be 16-byte aligned (gcache 4)");
+    (void)d;
+    return PATH_OK;
+}
+
+pa::CacheArgs cache_args(const path_fwd_desc* d, const path_cache* c) {
+    pa::CacheArgs a;
+    a.N = d->N; a.H = d->H; a.d = d->d; a.cap = c->cap;
+    a.k_bf16 = c->k_dtype == PATH_BF16;
+    a.v_bf16 = d->dtype == PATH_BF16;
+    a.kcache = c->kcache; a.vcache = c->vcache; a.gcache = c->gcache;
+    return a;
+}
+
+path_status launched(hipError_t e, const char* what) {
+    if (e != hipSuccess)
+        return fail(PATH_E_LAUNCH, std::string(what) + ": " + hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int path_abi_version(void) { return PATH_ATTN_ABI_VERSION; }
+
+const char* path_status_str(path_status s) {
+    switch (s) {
+        case PATH_OK: return "ok";
+        case PATH_E_NULL: return "null pointer";
+        case PATH_E_SHAPE: return "bad shape";
+        case PATH_E_DTYPE: return "bad dtype";
+        case PATH_E_UNSUPPORTED: return "unsupported";
+        case PATH_E_ALIGN: return "misaligned pointer";
+        case PATH_E_WORKSPACE: return "workspace too small";
+        case PATH_E_CAPACITY: return "cache capacity exceeded";
+        case PATH_E_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+const char* path_last_error(void) { return g_last_error.c_str(); }
+
+size_t path_attn_fwd_workspace(const path_fwd_desc* desc, int with_cache) {
+    if (check_desc(desc, true) != PATH_OK) return 0;
+    return fwd_layout(desc, with_cache != 0).total;
+}
+
+path_status path_attn_fwd(const path_fwd_desc* desc, const void* q, const void* k,
+                          const void* v, const void* w, const float* beta,
+                          const float* logf, void* o, float* lse,
+                          const path_cache* cache_out, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+    path_status s = check_desc(desc, true);
+    if (s != PATH_OK) return s;
+    if (!q || !k || !v || !w || !beta || !o) return fail(PATH_E_NULL, "q, k, v, w, beta and o are required");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(w, 16) || !aligned(o, 16))
+        return fail(PATH_E_ALIGN, "q, k, v, w and o must be 16-byte aligned");
+    if (!aligned(beta, 4) || !aligned(logf, 4) || !aligned(lse, 4))
+        return fail(PATH_E_ALIGN, "beta, logf and lse must be 4-byte aligned");
+    if (cache_out) {
+        s = check_cache(desc, cache_out);
+        if (s != PATH_OK) return s;
+        if (cache_out->cap < desc->L) return fail(PATH_E_CAPACITY, "cache capacity below L");
+    }
+    const Layout lay = fwd_layout(desc, cache_out != nullptr);
+    if (!ws) return fail(PATH_E_WORKSPACE, "workspace is NULL");
+    if (!aligned(ws, 256)) return fail(PATH_E_ALIGN, "workspace must be 256-byte aligned");
+    if (ws_bytes < lay.total) return fail(PATH_E_WORKSPACE, "workspace smaller than path_attn_fwd_workspace()");
+
+    char* base = static_cast<char*>(ws);
+    pa::FwdArgs a{};
+    a.N = desc->N; a.H = desc->H; a.L = desc->L; a.d = desc->d; a.block = block_of(desc);
+    a.bf16 = desc->dtype == PATH_BF16; a.scale = desc->scale;
+    a.q = q; a.k = k; a.v = v; a.w = w; a.beta = beta; a.logf = logf; a.o = o; a.lse = lse;
+    a.ws.kr = base + lay.kr;
+    a.ws.vt = lay.vt ? base + lay.vt : nullptr;
+    a.ws.em = base + lay.em;
+    a.ws.ql = reinterpret_cast<float*>(base + lay.ql);
+    a.ws.dg = reinterpret_cast<float*>(base + lay.dg);
+    a.ws.gl = reinterpret_cast<float*>(base + lay.gl);
+    a.ws.tot = reinterpret_cast<float*>(base + lay.tot);
+    if (cache_out) {
+        a.ws.k32 = reinterpret_cast<float*>(base + lay.k32);
+        a.ws.e32 = reinterpret_cast<float*>(base + lay.e32);
+        a.ws.suf = reinterpret_cast<float*>(base + lay.suf);
+        a.ws.gpre = reinterpret_cast<float*>(base + lay.gpre);
+    }
+    hipError_t e = use_mfma(desc) ? pa::launch_fwd_bf16(a, stream) : pa::launch_fwd_f32(a, stream);
+    if (e != hipSuccess) return launched(e, "path_attn_fwd");
+    if (cache_out) {
+        e = pa::launch_kv_align(a, cache_args(desc, cache_out), stream);
+        return launched(e, "path_attn_fwd (cache alignment)");
+    }
+    return ok();
+}
+
+path_status path_kv_update(const path_fwd_desc* desc, const path_cache* cache, int n,
+                           const void* w_t, const float* beta_t, hipStream_t stream) {
+    path_status s = check_desc(desc, false);
+    if (s != PATH_OK) return s;
+    if ((s = check_cache(desc, cache)) != PATH_OK) return s;
+    if (!w_t || !beta_t) return fail(PATH_E_NULL, "w_t and beta_t are required");
+    if (!aligned(w_t, 16) || !aligned(beta_t, 4)) return fail(PATH_E_ALIGN, "w_t must be 16-byte aligned");
+    if (n < 0) return fail(PATH_E_SHAPE, "n must be >= 0");
+    if (n > cache->cap) return fail(PATH_E_CAPACITY, "n exceeds cache capacity");
+    return launched(pa::launch_kv_update(cache_args(desc, cache), n, w_t, beta_t, stream),
+                    "path_kv_update");
+}
+
+path_status path_kv_append(const path_fwd_desc* desc, const path_cache* cache, int n,
+                           const void* k_t, const void* v_t, const float* logf_t,
+                           hipStream_t stream) {
+    path_status s = check_desc(desc, false);
+    if (s != PATH_OK) return s;
+    if ((s = check_cache(desc, cache)) != PATH_OK) return s;
+    if (!k_t || !v_t) return fail(PATH_E_NULL, "k_t and v_t are required");
+    if (cache->gcache && !logf_t) return fail(PATH_E_NULL, "logf_t is required when gcache is set");
+    if (!aligned(k_t, 16) || !aligned(v_t, 16) || !aligned(logf_t, 4))
+        return fail(PATH_E_ALIGN, "k_t and v_t must be 16-byte aligned");
+    if (n < 0) return fail(PATH_E_SHAPE, "n must be >= 0");
+    if (n >= cache->cap) return fail(PATH_E_CAPACITY, "slot n is beyond the cache capacity");
+    return launched(pa::launch_kv_append(cache_args(desc, cache), n, k_t, v_t, logf_t, stream),
+                    "path_kv_append");
+}
+
+size_t path_decode_workspace(const path_fwd_desc* desc, int n_keys) {
+    if (check_desc(desc, false) != PATH_OK || n_keys < 1) return 0;
+    const int chunk = pa::decode_chunk(n_keys);
+    const size_t nch = (size_t)(n_keys + chunk - 1) / chunk;
+    return up256((size_t)desc->N * desc->H * nch * (desc->d + 2) * 4);
+}
+
+static path_status decode_common(const path_fwd_desc* desc, const path_cache* cache,
+                                 int n_keys, const void* q_t, void* o_t, float* lse_t,
+                                 void* ws, size_t ws_bytes, bool fused, const void* k_t,
+                                 const void* v_t, const void* w_t, const float* beta_t,
+                                 const float* logf_t, hipStream_t stream, const char* name) {
+    path_status s = check_desc(desc, false);
+    if (s != PATH_OK) return s;
+    if ((s = check_cache(desc, cache)) != PATH_OK) return s;
+    if (!q_t || !o_t) return fail(PATH_E_NULL, "q_t and o_t are required");
+    if (!aligned(q_t, 16) || !aligned(o_t, 16) || !aligned(lse_t, 4))
+        return fail(PATH_E_ALIGN, "q_t and o_t must be 16-byte aligned");
+    if (n_keys < 1) return fail(PATH_E_SHAPE, "at least one key is required");
+    if (n_keys > cache->cap) return fail(PATH_E_CAPACITY, "keys exceed cache capacity");
+    if (!ws) return fail(PATH_E_WORKSPACE, "workspace is NULL");
+    if (!aligned(ws, 256)) return fail(PATH_E_ALIGN, "workspace must be 256-byte aligned");
+    if (ws_bytes < path_decode_workspace(desc, n_keys))
+        return fail(PATH_E_WORKSPACE, "workspace smaller than path_decode_workspace()");
+    return launched(pa::launch_decode(cache_args(desc, cache), n_keys, desc->scale, q_t, o_t,
+                                      lse_t, static_cast<float*>(ws),
+                                      pa::decode_chunk(n_keys), fused, k_t, v_t, w_t, beta_t,
+                                      logf_t, stream),
+                    name);
+}
+
+path_status path_decode(const path_fwd_desc* desc, const path_cache* cache, int n_keys,
+                        const void* q_t, void* o_t, float* lse_t, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+    return decode_common(desc, cache, n_keys, q_t, o_t, lse_t, ws, ws_bytes, false, nullptr,
+                         nullptr, nullptr, nullptr, nullptr, stream, "path_decode");
+}
+
+path_status path_decode_step(const path_fwd_desc* desc, const path_cache* cache, int n,
+                             const void* q_t, const void* k_t, const void* v_t,
+                             const void* w_t, const float* beta_t, const float* logf_t,
+                             void* o_t, float* lse_t, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+    if (!k_t || !v_t || !w_t || !beta_t) return fail(PATH_E_NULL, "k_t, v_t, w_t and beta_t are required");
+    if (!aligned(k_t, 16) || !aligned(v_t, 16) || !aligned(w_t, 16) || !aligned(beta_t, 4) ||
+        !aligned(logf_t, 4))
+        return fail(PATH_E_ALIGN, "k_t, v_t and w_t must be 16-byte aligned");
+    if (cache && cache->gcache && !logf_t) return fail(PATH_E_NULL, "logf_t is required when gcache is set");
+    if (n < 0) return fail(PATH_E_SHAPE, "n must be >= 0");
+    if (cache && n >= cache->cap) return fail(PATH_E_CAPACITY, "slot n is beyond the cache capacity");
+    return decode_common(desc, cache, n + 1, q_t, o_t, lse_t, ws, ws_bytes, true, k_t, v_t,
+                         w_t, beta_t, logf_t, stream, "path_decode_step");
+}
+
+path_status path_causal_attn_fwd(const path_fwd_desc* desc, const void* q, const void* k,
+                                 const void* v, void* o, float* lse, hipStream_t stream) {
+    path_status s = check_desc(desc, true);
+    if (s != PATH_OK) return s;
+    if (!q || !k || !v || !o) return fail(PATH_E_NULL, "q, k, v and o are required");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+        return fail(PATH_E_ALIGN, "q, k, v and o must be 16-byte aligned");
+    pa::FwdArgs a{};
+    a.N = desc->N; a.H = desc->H; a.L = desc->L; a.d = desc->d; a.block = 64;
+    a.bf16 = desc->dtype == PATH_BF16; a.scale = desc->scale;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    return launched(pa::launch_causal(a, stream), "path_causal_attn_fwd");
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// kernels.hpp -- internal interface between the C-ABI host layer and the
+// kernel translation units of libpath_attn.  Not installed; not part of the ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace pa {
+
+// Per-block products of the preconditioning step, carved from the caller's
+// workspace by the host layer.  "blk" = slice * nb + c with slice = n*H + h.
+struct FwdWs {
+    void* kr;     // keys moved to their block's right edge: [blk][B][d]
+                  //   (f32 path: float, natural order; bf16 path: bf16 in
+                  //    matrix-core operand order)
+    void* vt;     // bf16 path: values transposed per block [blk][d][B]
+    void* em;     // block transition I - E: f32 path E [blk][d][d] float;
+                  //   bf16 path -E as bf16 operand tiles
+    float* ql;    // queries moved to their block's left edge [blk][B][d]
+    float* dg;    // in-block logits lower(QK^T) - P M [blk][B][B]
+    float* gl;    // in-block inclusive cumsum of log f [blk][B]
+    float* tot;   // block sum of log f [blk]
+    // cache alignment only (NULL otherwise)
+    float* k32;   // Kright in float32 [blk][B][d]
+    float* e32;   // E in float32 [blk][d][d]
+    float* suf;   // suffix transitions S_c [blk][d][d]
+    float* gpre;  // log f sum of all blocks before c [blk]
+};
+
+struct FwdArgs {
+    int N, H, L, d, block;
+    bool bf16;
+    float scale;
+    const void *q, *k, *v, *w;
+    const float *beta, *logf;
+    void* o;
+    float* lse;
+    FwdWs ws;
+};
+
+struct CacheArgs {
+    int N, H, d, cap;
+    bool k_bf16, v_bf16;
+    void* kcache;
+    void* vcache;
+    float* gcache;
+};
+
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st);
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
+bool fwd_bf16_supported(int d, int block);
+
+// prefill -> decode alignment (uses ws.k32 / ws.e32 written by the forward)
+hipError_t launch_kv_align(const FwdArgs& a, const CacheArgs& c, hipStream_t st);
+
+hipError_t launch_kv_update(const CacheArgs& c, int n, const void* w_t,
+                            const float* beta_t, hipStream_t st);
+hipError_t launch_kv_append(const CacheArgs& c, int n, const void* k_t,
+                            const void* v_t, const float* logf_t, hipStream_t st);
+// decode: fused = 1 also rewrites slots [0, n_keys-1) with (w_t, beta_t) and
+// appends (k_t, v_t, logf_t) at slot n_keys-1 before attending.
+hipError_t launch_decode(const CacheArgs& c, int n_keys, float scale,
+                         const void* q_t, void* o_t, float* lse_t, float* part,
+                         int chunk, bool fused, const void* k_t, const void* v_t,
+                         const void* w_t, const float* beta_t,
+                         const float* logf_t, hipStream_t st);
+int decode_chunk(int n_keys);
+
+hipError_t launch_causal(const FwdArgs& a, hipStream_t st);
+
+}  // namespace pa

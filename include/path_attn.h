@@ -1,0 +1,181 @@
+/*
+ * path_attn.h -- C ABI of libpath_attn: PaTH attention prefill and decode on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Citations name a page and a section of it:
+ *   [Notes s2.x]   reading-notes page "PaTH Attention:通过累积 Householder
+ *                  变换编码位置" (cc.laoqi.cc, notes on arXiv 2505.16381v2);
+ *   [Explainer s3] explainer page "PaTH Attention: Position Encoding via
+ *                  Accumulating Householder Transformations" (gist.science),
+ *                  section 3 on efficient training and inference.
+ *
+ * The operation [Notes s2.1, s2.5]: for each (batch n, head h) and query
+ * position i, with transitions H_t = I - beta_t w_t w_t^T,
+ *   logit(i, j) = scale * k_j^T H_{j+1} ... H_i q_i + sum_{s=j+1..i} log f_s,
+ *   j <= i (causal), o_i = softmax_j(logit) . v,  lse_i = log sum_j exp(logit).
+ * The forget-gate term is present only when a log f array is given (PaTH-FoX);
+ * it is added after scaling and is not scaled.  Positions are 0-based.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All array arguments are DEVICE pointers owned by the caller.  The library
+ *   allocates nothing, frees nothing, keeps no per-call global state, and
+ *   never synchronises the host with the device.  Work is enqueued on the
+ *   caller's stream; results are visible after the caller synchronises it.
+ * - Layouts are dense and row-major:
+ *     q, k, v, w, o          [N, H, L, d]  in desc->dtype
+ *     beta, logf, lse        [N, H, L]     float32
+ *     per-token decode args  [N, H, d] (q_t, k_t, v_t, w_t, o_t) in
+ *                            desc->dtype; [N, H] float32 (beta_t, logf_t, lse_t)
+ * - Supported: dtype PATH_F32 with d in {16, 32, 64}; dtype PATH_BF16 with
+ *   d in {16, 32, 64} (d = 32 and 64 use the matrix-core kernels).
+ * - beta and log f are used as given: no clipping, no renormalisation of w.
+ *   NaN and Inf propagate.  beta in [0, 2] is the meaningful range.
+ * - Argument errors are reported synchronously, before anything is enqueued:
+ *   null pointers, sizes < 1, unsupported d or dtype, pointers that are not
+ *   16-byte aligned (4-byte for float32 arrays), a workspace smaller than the
+ *   matching *_workspace() result, or a cache index beyond its capacity.
+ *   A failed kernel launch returns PATH_E_LAUNCH.  Faults inside a kernel
+ *   surface at the caller's next synchronisation.  path_last_error() gives a
+ *   message for the last failure on the calling thread.
+ * - Outputs must not alias inputs.  Calls on different streams are
+ *   independent as long as their buffers (including workspaces and caches)
+ *   are distinct.
+ */
+#ifndef PATH_ATTN_H
+#define PATH_ATTN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PATH_ATTN_ABI_VERSION 1
+
+typedef enum {
+    PATH_OK = 0,
+    PATH_E_NULL = 1,         /* a required pointer is NULL */
+    PATH_E_SHAPE = 2,        /* N, H, L or a length argument out of range */
+    PATH_E_DTYPE = 3,        /* unknown dtype enum value */
+    PATH_E_UNSUPPORTED = 4,  /* valid but unsupported (d, block size) */
+    PATH_E_ALIGN = 5,        /* pointer not aligned as required */
+    PATH_E_WORKSPACE = 6,    /* workspace NULL or smaller than required */
+    PATH_E_CAPACITY = 7,     /* cache capacity exceeded */
+    PATH_E_LAUNCH = 8        /* a kernel launch failed */
+} path_status;
+
+typedef enum { PATH_F32 = 0, PATH_BF16 = 1 } path_dtype;
+
+/* Problem description.  L is the sequence length for the forward pass and is
+ * ignored by the decode entry points.  block = 0 selects the default block
+ * size (64); the float32 path also accepts 16 and 32, which must give the same
+ * result up to rounding (the block decomposition is exact [Notes s2.7]). */
+typedef struct {
+    int N, H, L, d;
+    path_dtype dtype;
+    float scale;
+    int block;
+} path_fwd_desc;
+
+/* Decode cache [Notes s2.8; Explainer s3].  Keys are stored already rewritten
+ * by every transition after them: after position t has been processed, slot j
+ * holds H_t ... H_{j+1} k_j, so a plain softmax decode over it gives PaTH
+ * scores.  No w or beta history is kept.
+ *   kcache [N, H, cap, d] in k_dtype (PATH_F32 or PATH_BF16)
+ *   vcache [N, H, cap, d] in desc->dtype
+ *   gcache [N, H, cap] float32: inclusive prefix sums of log f (slot j holds
+ *          sum_{s<=j} log f_s), or NULL for plain PaTH (no forget gate). */
+typedef struct {
+    int cap;
+    path_dtype k_dtype;
+    void *kcache;
+    void *vcache;
+    float *gcache;
+} path_cache;
+
+int path_abi_version(void);
+const char *path_status_str(path_status s);
+/* Message for the last failure on the calling thread ("" if none). */
+const char *path_last_error(void);
+
+/* Bytes of device workspace path_attn_fwd needs for this description
+ * (0 if the description is invalid).  with_cache != 0 sizes it for a call
+ * that also fills a decode cache (cache_out != NULL). */
+size_t path_attn_fwd_workspace(const path_fwd_desc *desc, int with_cache);
+
+/*
+ * Prefill forward pass [Notes s2.1, s2.5 (definition); s2.6-s2.7 (blockwise
+ * UT form and right-to-left scan, the algorithm used)].
+ *   q, k, v, w : [N, H, L, d] desc->dtype      beta : [N, H, L] float32
+ *   logf       : [N, H, L] float32 log forget gates, or NULL (plain PaTH)
+ *   o          : [N, H, L, d] desc->dtype (written; bf16 rounds to nearest even)
+ *   lse        : [N, H, L] float32 natural-log log-sum-exp of each row's
+ *                final logits (after scale and bias), or NULL
+ *   cache_out  : NULL, or a cache with cap >= L to fill with the prompt's keys
+ *                aligned to position L-1 (H_{L-1}...H_{j+1} k_j), its values,
+ *                and (if gcache != NULL and logf != NULL) the log f prefix.
+ *                This is the prefill-to-decode alignment of [Notes s2.8].
+ *   ws, ws_bytes : workspace of at least path_attn_fwd_workspace(desc,
+ *                cache_out != NULL) bytes,
+ *                256-byte aligned; its contents need not be initialised.
+ */
+path_status path_attn_fwd(const path_fwd_desc *desc, const void *q,
+                          const void *k, const void *v, const void *w,
+                          const float *beta, const float *logf, void *o,
+                          float *lse, const path_cache *cache_out, void *ws,
+                          size_t ws_bytes, hipStream_t stream);
+
+/* Cache rewrite for a new position [Notes s2.8, eq. (1) of the paper]:
+ *   k_j <- k_j - beta_t (w_t^T k_j) w_t   for every slot j in [0, n).
+ * w_t [N, H, d] desc->dtype; beta_t [N, H] float32.  In place on kcache. */
+path_status path_kv_update(const path_fwd_desc *desc, const path_cache *cache,
+                           int n, const void *w_t, const float *beta_t,
+                           hipStream_t stream);
+
+/* Appends one token at slot n (n < cap): kcache[n] = k_t (not rewritten: its
+ * own transition is not on its path [Notes s2.1]), vcache[n] = v_t, and, if
+ * gcache != NULL, gcache[n] = gcache[n-1] + logf_t (logf_t alone when n = 0;
+ * logf_t may be NULL only if gcache is NULL). */
+path_status path_kv_append(const path_fwd_desc *desc, const path_cache *cache,
+                           int n, const void *k_t, const void *v_t,
+                           const float *logf_t, hipStream_t stream);
+
+/* Bytes of workspace the decode entry points need for up to n_keys keys. */
+size_t path_decode_workspace(const path_fwd_desc *desc, int n_keys);
+
+/* Single-query attention over slots [0, n_keys) of a rewritten cache
+ * [Notes s2.8]: with t = n_keys - 1,
+ *   s_j = scale * q_t^T kcache[j] + (gcache[t] - gcache[j])   (bias 0 if
+ *   gcache is NULL), o_t = softmax(s) . vcache, lse_t = log sum exp s.
+ * q_t, o_t [N, H, d] desc->dtype; lse_t [N, H] float32 or NULL.
+ * Split over key chunks; ws holds the per-chunk partial softmax states. */
+path_status path_decode(const path_fwd_desc *desc, const path_cache *cache,
+                        int n_keys, const void *q_t, void *o_t, float *lse_t,
+                        void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* One fused decode step at position t = n (n keys already cached, n < cap):
+ * path_kv_update(n, w_t, beta_t), path_kv_append(n, k_t, v_t, logf_t) and
+ * path_decode(n + 1, q_t) in one pass over the cache.  Afterwards the cache
+ * holds n + 1 keys.  logf_t may be NULL only if gcache is NULL.
+ * ws: at least path_decode_workspace(desc, n + 1) bytes. */
+path_status path_decode_step(const path_fwd_desc *desc,
+                             const path_cache *cache, int n, const void *q_t,
+                             const void *k_t, const void *v_t,
+                             const void *w_t, const float *beta_t,
+                             const float *logf_t, void *o_t, float *lse_t,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Plain causal softmax attention (every beta = 0, no gate): the in-library
+ * baseline the PaTH kernels are timed against.  Same layouts as
+ * path_attn_fwd; no workspace. */
+path_status path_causal_attn_fwd(const path_fwd_desc *desc, const void *q,
+                                 const void *k, const void *v, void *o,
+                                 float *lse, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PATH_ATTN_H */

@@ -1,0 +1,114 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry
+point, and rejects bad arguments synchronously (no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "path_attn.h")).read()
+    return sorted(set(re.findall(r"\b(path_[a-z_0-9]+)\s*\(", src)))
+
+
+def _lib():
+    import dependent_position_encoding_amd as pa
+    return pa, pa.load_library()
+
+
+def test_every_declared_symbol_is_exported():
+    pa, lib = _lib()
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(pa.EXPORTS) == names
+
+
+def test_abi_version_and_status_strings():
+    pa, lib = _lib()
+    assert lib.path_abi_version() == 1
+    for s in range(9):
+        assert lib.path_status_str(s)
+    assert lib.path_status_str(99) == b"unknown status"
+
+
+def _desc(pa, **kw):
+    base = dict(N=1, H=1, L=64, d=64, dtype=pa.PATH_BF16, scale=1.0, block=0)
+    base.update(kw)
+    return pa._Desc(**base)
+
+
+FAKE = ctypes.c_void_p(1 << 20)     # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), 2), (dict(L=0), 2), (dict(d=48), 4), (dict(d=128), 4),
+    (dict(dtype=7), 3), (dict(block=8), 4), (dict(block=32), 4),
+])
+def test_fwd_rejects_bad_descriptions(kw, status):
+    pa, lib = _lib()
+    d = _desc(pa, **kw)
+    st = lib.path_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                           None, FAKE, 1 << 30, None)
+    assert st == status
+    assert lib.path_last_error()
+    assert lib.path_attn_fwd_workspace(ctypes.byref(d), 0) == 0
+
+
+def test_fwd_rejects_null_misaligned_and_small_workspace():
+    pa, lib = _lib()
+    d = _desc(pa)
+    st = lib.path_attn_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, 0, None)
+    assert st == 1
+    st = lib.path_attn_fwd(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, 0, None)
+    assert st == 1
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    st = lib.path_attn_fwd(ctypes.byref(d), odd, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, 0, None)
+    assert st == 5
+    need = lib.path_attn_fwd_workspace(ctypes.byref(d), 0)
+    assert need > 0
+    assert lib.path_attn_fwd_workspace(ctypes.byref(d), 1) > need
+    st = lib.path_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None,
+                           FAKE, need - 1, None)
+    assert st == 6
+    st = lib.path_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None,
+                           None, need, None)
+    assert st == 6
+    st = lib.path_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None,
+                           ctypes.c_void_p((1 << 20) + 16), need, None)
+    assert st == 5
+
+
+def test_fwd_cache_capacity_checked():
+    pa, lib = _lib()
+    d = _desc(pa, L=100)
+    c = pa._Cache(99, pa.PATH_BF16, 1 << 20, 1 << 21, None)
+    need = lib.path_attn_fwd_workspace(ctypes.byref(d), 1)
+    st = lib.path_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                           ctypes.byref(c), FAKE, need, None)
+    assert st == 7
+
+
+def test_decode_argument_errors():
+    pa, lib = _lib()
+    d = _desc(pa)
+    c = pa._Cache(8, pa.PATH_BF16, 1 << 20, 1 << 21, None)
+    ws = lib.path_decode_workspace(ctypes.byref(d), 8)
+    assert ws > 0
+    assert lib.path_decode(ctypes.byref(d), ctypes.byref(c), 9, FAKE, FAKE, None, FAKE, ws, None) == 7
+    assert lib.path_decode(ctypes.byref(d), ctypes.byref(c), 0, FAKE, FAKE, None, FAKE, ws, None) == 2
+    assert lib.path_decode(ctypes.byref(d), None, 4, FAKE, FAKE, None, FAKE, ws, None) == 1
+    assert lib.path_decode(ctypes.byref(d), ctypes.byref(c), 4, FAKE, FAKE, None, FAKE, 8, None) == 6
+    assert lib.path_decode_step(ctypes.byref(d), ctypes.byref(c), 8, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                None, FAKE, None, FAKE, ws, None) == 7
+    assert lib.path_kv_update(ctypes.byref(d), ctypes.byref(c), 9, FAKE, FAKE, None) == 7
+    assert lib.path_kv_update(ctypes.byref(d), ctypes.byref(c), -1, FAKE, FAKE, None) == 2
+    assert lib.path_kv_append(ctypes.byref(d), ctypes.byref(c), 8, FAKE, FAKE, None, None) == 7
+    g = pa._Cache(8, pa.PATH_BF16, 1 << 20, 1 << 21, 1 << 22)
+    assert lib.path_kv_append(ctypes.byref(d), ctypes.byref(g), 0, FAKE, FAKE, None, None) == 1
+    bad = pa._Cache(8, 5, 1 << 20, 1 << 21, None)
+    assert lib.path_kv_update(ctypes.byref(d), ctypes.byref(bad), 1, FAKE, FAKE, None) == 3

@@ -1,0 +1,123 @@
+"""GPU parity of the decode path: cache alignment after prefill, the cache
+rewrite, and single-query attention, against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.parity import check
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _pa():
+    import dependent_position_encoding_amd as pa
+    pa.load_library()
+    return pa
+
+
+def _decode_run(wl, L, steps, k_dtype, fused=True, variant=0):
+    """Prefill L tokens into a cache, then decode `steps` tokens.
+
+    Returns the GPU outputs and the fp64 oracle rows for positions
+    L .. L+steps-1 (rows of the walk on the whole sequence), and the final
+    cache keys with their oracle.
+    """
+    pa = _pa()
+    x = workloads.make_inputs(wl, device="cpu", variant=variant, L=L + steps)
+    g = {k: (v.to(DEV) if v is not None else None) for k, v in x.items()}
+    N, H, d = wl.N, wl.H, wl.d
+    gate = wl.fox
+    print(f"case {wl.name} L={L} steps={steps} k_dtype={k_dtype} fused={fused}", flush=True)
+    cache = pa.Cache(N, H, L + steps, d, dtype=wl.dtype, k_dtype=k_dtype, gate=gate, device=DEV)
+    pre = lambda n: g[n][:, :, :L].contiguous()
+    pa.fwd(pre("q"), pre("k"), pre("v"), pre("w"), pre("beta"),
+           logf=pre("logf") if gate else None, scale=wl.scale, cache=cache)
+    outs, lses = [], []
+    tok = lambda n, t: g[n][:, :, t].contiguous()
+    for t in range(L, L + steps):
+        lf = tok("logf", t) if gate else None
+        if fused:
+            o, lse = pa.decode_step(cache, t, tok("q", t), tok("k", t), tok("v", t), tok("w", t),
+                                    tok("beta", t), lf, scale=wl.scale)
+        else:
+            pa.kv_update(cache, t, tok("w", t), tok("beta", t))
+            pa.kv_append(cache, t, tok("k", t), tok("v", t), lf)
+            o, lse = pa.decode(cache, t + 1, tok("q", t), scale=wl.scale)
+        outs.append(o.clone())
+        lses.append(lse.clone())
+    torch.cuda.synchronize()
+    go = np.stack([workloads.as_slices_f64(o) for o in outs], axis=1)
+    gl = np.stack([workloads.as_slices_f64(l) for l in lses], axis=1)
+    f64 = {k: (workloads.as_slices_f64(v) if v is not None else None) for k, v in x.items()}
+    ro, rl = oracle.fwd_rows(f64["q"], f64["k"], f64["v"], f64["w"], f64["beta"],
+                             f64["logf"] if gate else None, wl.scale,
+                             rows=np.arange(L, L + steps))
+    kc = workloads.as_slices_f64(cache.kcache)
+    rk = oracle.transported_keys(f64["k"], f64["w"], f64["beta"], L + steps - 1)
+    return go, gl, ro, rl, kc, rk, cache, x
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("dtype,k_dtype", [(torch.float32, torch.float32),
+                                           (torch.bfloat16, torch.bfloat16),
+                                           (torch.bfloat16, torch.float32)])
+def test_decode_small(dtype, k_dtype, fused):
+    wl = workloads.CONFIGS["fox"].replace(N=2, H=3, L=190, dtype=dtype)
+    go, gl, ro, rl, kc, rk, _, _ = _decode_run(wl, 190, 12, k_dtype, fused)
+    bf = dtype == torch.bfloat16
+    check("decode o", go, ro, bf16=bf)
+    check("decode lse", gl, rl, bf16=bf)
+    if k_dtype == torch.float32:
+        np.testing.assert_allclose(kc, rk, atol=5e-5 if not bf else 2e-4)
+    else:
+        check("decode kcache", kc, rk, bf16=True)
+
+
+def test_decode_no_gate_and_ragged_prompt():
+    wl = workloads.CONFIGS["tiny"].replace(N=1, H=2, L=77, d=32, scale=32 ** -0.5)
+    go, gl, ro, rl, kc, rk, _, _ = _decode_run(wl, 77, 9, torch.float32, True)
+    check("decode nogate o", go, ro, bf16=False)
+    check("decode nogate lse", gl, rl, bf16=False)
+    np.testing.assert_allclose(kc, rk, atol=5e-5)
+
+
+def test_decode_from_empty_cache():
+    """Position 0 decoded alone: o_0 = v_0 and lse_0 = scale * q_0 . k_0."""
+    pa = _pa()
+    wl = workloads.CONFIGS["fox"].replace(N=1, H=4, L=4, dtype=torch.float32)
+    x = workloads.make_inputs(wl, L=4)
+    g = {k: v.to(DEV) for k, v in x.items()}
+    cache = pa.Cache(1, 4, 4, 64, dtype=torch.float32, gate=True, device=DEV)
+    tok = lambda n, t: g[n][:, :, t].contiguous()
+    o, lse = pa.decode_step(cache, 0, tok("q", 0), tok("k", 0), tok("v", 0), tok("w", 0),
+                            tok("beta", 0), tok("logf", 0), scale=0.125)
+    torch.cuda.synchronize()
+    assert torch.allclose(o, g["v"][:, :, 0], atol=1e-6)
+    ref = 0.125 * (g["q"][:, :, 0] * g["k"][:, :, 0]).sum(-1)
+    assert torch.allclose(lse, ref, atol=1e-5)
+    assert torch.allclose(cache.gcache[:, :, 0], g["logf"][:, :, 0])
+
+
+def test_fused_and_unfused_agree():
+    wl = workloads.CONFIGS["fox"].replace(N=1, H=2, L=300)
+    a = _decode_run(wl, 300, 6, torch.bfloat16, True)
+    b = _decode_run(wl, 300, 6, torch.bfloat16, False)
+    assert np.abs(a[0] - b[0]).max() < 1e-2
+    assert np.array_equal(a[4], b[4]), "the two paths must rewrite the cache identically"
+
+
+def test_cache_capacity_errors():
+    pa = _pa()
+    cache = pa.Cache(1, 1, 4, 16, dtype=torch.float32, gate=False, device=DEV)
+    z = torch.zeros(1, 1, 16, device=DEV)
+    b = torch.zeros(1, 1, device=DEV)
+    with pytest.raises(pa.PathAttnError) as e:
+        pa.decode_step(cache, 4, z, z, z, z, b, None)
+    assert e.value.status == 7
+    with pytest.raises(pa.PathAttnError) as e:
+        pa.decode(cache, 5, z)
+    assert e.value.status == 7
