@@ -1,0 +1,251 @@
+"""Benchmark of the PaTH attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic inputs that
+are already resident in HBM: the prefill forward (block UT solve and
+preconditioning, right-to-left scan with online softmax), the alignment of
+the prompt's keys into the decode cache, then `decode_steps` fused decode
+steps (rewrite every cached key with the new transition, append, attend).
+Default workload: long-context PaTH-FoX, batch 1, 32 heads, head dim 64,
+prompt 32768 tokens, 256 decode steps, bf16.
+
+Prints one JSON line.  Phase and kernel times come from HIP events recorded
+on the stream the kernels run on (the library records the prefill phase
+events itself).  The fp64 CPU oracle is timed on a bounded sample of query
+rows of the same workload as the CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("PaTH prefill TFLOP/s + tokens/s (fraction of bf16 MFMA peak); decode GB/s")
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector peak
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak
+
+WORKLOADS = {
+    "long": dict(cfg="long"),
+    "lm": dict(cfg="lm"),
+    "fox2048": dict(cfg="fox", L=2048),
+    "fox4096": dict(cfg="fox", L=4096),
+    "fox8192": dict(cfg="fox", L=8192),
+    "flipflop": dict(cfg="flipflop"),
+}
+
+
+def scan_flops(N, H, L, d, B=64):
+    """GEMM flops the scan kernel executes: per query block b, the diagonal
+    tile's P.V (its logits come from preconditioning), then for c < b the
+    Q.K^T and P.V tiles, and (for c >= 1) one d x d transition of Qwork."""
+    nb = (L + B - 1) // B
+    per_slice = (nb * 2 * B * B * d
+                 + nb * (nb - 1) // 2 * 4 * B * B * d
+                 + max(nb - 1, 0) * max(nb - 2, 0) // 2 * 2 * B * d * d)
+    return N * H * per_slice
+
+
+def precond_flops(N, H, L, d, B=64):
+    """GEMM flops of the per-block preconditioning (products of B x d and B x B
+    operands: W W^T, Q W^T, W K^T, Q K^T, P = lower(QW^T) U, P W, U M, R^T W,
+    U^T W, W^T Y, P M) and the B^3/3 triangular solve."""
+    nb = (L + B - 1) // B
+    per_block = 12 * B * B * d + 4 * B ** 3 + 2 * B * d * d
+    return N * H * nb * per_block
+
+
+def fa_eq_flops(N, H, L, d):
+    return 2.0 * N * H * L * L * d
+
+
+def decode_bytes(N, H, d, t, k_bytes, v_bytes):
+    """HBM bytes one fused step at position t must move: read and write every
+    cached key, read every cached value and log-f prefix entry."""
+    return N * H * t * (2 * d * k_bytes + d * v_bytes + 4)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="long", choices=sorted(WORKLOADS))
+    ap.add_argument("--decode-steps", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dependent_position_encoding_amd as pa
+    import workloads
+
+    pa.load_library()
+    dev = torch.device("cuda:0")
+    spec = WORKLOADS[args.workload]
+    wl = workloads.CONFIGS[spec["cfg"]]
+    if "L" in spec:
+        wl = wl.replace(L=spec["L"])
+    if args.decode_steps is not None:
+        wl = wl.replace(decode_steps=args.decode_steps)
+    N, H, L, d, T = wl.N, wl.H, wl.L, wl.d, wl.decode_steps
+    print(f"[bench] workload {args.workload}: N={N} H={H} L={L} d={d} decode={T} "
+          f"dtype={wl.dtype}", file=sys.stderr, flush=True)
+
+    x = workloads.make_inputs(wl, device=dev)
+    pre = {n: (x[n][:, :, :L].contiguous() if x[n] is not None else None) for n in x}
+    tok = {n: [x[n][:, :, t].contiguous() for t in range(L, L + T)] if x[n] is not None else None
+           for n in x}
+    cache = pa.Cache(N, H, L + T, d, dtype=wl.dtype, gate=wl.fox, device=dev) if T else None
+    ws = torch.empty(pa.fwd_workspace_bytes(N, H, L, d, wl.dtype, with_cache=T > 0),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty_like(pre["q"])
+    lse = torch.empty(N, H, L, dtype=torch.float32, device=dev)
+    dws = torch.empty(max(pa.decode_workspace_bytes(cache, L + T), 1) if T else 1,
+                      dtype=torch.uint8, device=dev)
+    ot = torch.empty(N, H, d, dtype=wl.dtype, device=dev)
+    lt = torch.empty(N, H, dtype=torch.float32, device=dev)
+
+    E = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(record):
+        evs = [E() for _ in range(4)] if record else None
+        pa.fwd(pre["q"], pre["k"], pre["v"], pre["w"], pre["beta"], logf=pre["logf"],
+               scale=wl.scale, cache=cache, workspace=ws, out=(o, lse), events=evs)
+        dev_ev = []
+        for i in range(T):
+            if record:
+                a, b = E(), E()
+                a.record()
+            pa.decode_step(cache, L + i, tok["q"][i], tok["k"][i], tok["v"][i], tok["w"][i],
+                           tok["beta"][i], tok["logf"][i] if wl.fox else None,
+                           scale=wl.scale, workspace=dws, out=(ot, lt))
+            if record:
+                b.record()
+                dev_ev.append((a, b))
+        return evs, dev_ev
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    recs = []
+    t0, t1 = E(), E()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        recs.append(step(True))
+    t1.record()
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+
+    pre_ms = np.mean([r[0][0].elapsed_time(r[0][1]) for r in recs])
+    scan_ms = np.mean([r[0][1].elapsed_time(r[0][2]) for r in recs])
+    align_ms = np.mean([r[0][2].elapsed_time(r[0][3]) for r in recs])
+    fwd_ms = pre_ms + scan_ms + align_ms
+    dec_ms = [float(np.mean([r[1][i][0].elapsed_time(r[1][i][1]) for r in recs]))
+              for i in range(T)]
+
+    f_scan = scan_flops(N, H, L, d)
+    f_pre = precond_flops(N, H, L, d)
+    f_dec = sum(8.0 * N * H * (L + i + 1) * d for i in range(T))
+    kb = 2 if cache is not None and cache.k_dtype == torch.bfloat16 else 4
+    vb = 2 if wl.dtype == torch.bfloat16 else 4
+    b_dec = sum(decode_bytes(N, H, d, L + i, kb, vb) for i in range(T))
+    dec_total_ms = float(sum(dec_ms))
+
+    value = (f_scan + f_pre + f_dec) / (ms_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == torch.bfloat16 else PEAK_F32_TFLOPS
+    scan_tf = f_scan / (scan_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded; distributions of the workload definition)",
+        "config": {"workload": args.workload, "batch": N, "heads": H, "seq_len": L,
+                   "head_dim": d, "decode_steps": T, "forget_gate": wl.fox,
+                   "block": 64, "parallelism": "single GPU"},
+        "prefill": {
+            "ms": round(fwd_ms, 4), "precond_ms": round(pre_ms, 4),
+            "scan_ms": round(scan_ms, 4), "cache_align_ms": round(align_ms, 4),
+            "executed_TFLOP_s": round((f_scan + f_pre) / ((pre_ms + scan_ms) * 1e-3) / 1e12, 3),
+            "fa_eq_TFLOP_s": round(fa_eq_flops(N, H, L, d) / ((pre_ms + scan_ms) * 1e-3) / 1e12, 3),
+            "tokens_per_s": round(N * L / ((pre_ms + scan_ms) * 1e-3), 1),
+            "frac_of_peak": round((f_scan + f_pre) / ((pre_ms + scan_ms) * 1e-3) / 1e12 / peak, 4),
+        },
+        "roofline": {
+            "kernel": "scan (right-to-left block scan with online softmax)",
+            "bound": "mfma", "achieved": round(scan_tf, 3), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(scan_tf / peak, 4), "traffic": None,
+        },
+    }
+    if T:
+        gbs = b_dec / (dec_total_ms * 1e-3) / 1e9
+        out["decode"] = {
+            "us_per_token_step": round(dec_total_ms / T * 1e3, 2),
+            "GB_s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "first_step_us": round(dec_ms[0] * 1e3, 2), "last_step_us": round(dec_ms[-1] * 1e3, 2),
+        }
+        out["roofline_decode"] = {
+            "kernel": "fused decode step (rewrite + append + split-K attention, with its combine)",
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+        }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, N * (L + T) / (ms_step * 1e-3))
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, x, seconds, gpu_tokens_per_s):
+    """Time the fp64 oracle on random query rows of 4 heads of this workload.
+    Rows are uniform over the whole sequence, so the mean cost of a sampled
+    row is the mean cost of a row of the full job; tokens/s is rows/s."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    Ltot = x["q"].shape[2]
+    heads = [0, 1, 2, 3][: wl.N * wl.H]
+    f64 = {n: (workloads.as_slices_f64(v, heads) if v is not None else None) for n, v in x.items()}
+    rng = np.random.default_rng(0)
+    # calibrate on a small batch, then size the timed sample to ~`seconds`
+    probe = rng.integers(0, Ltot, (len(heads), 8))
+    t = time.perf_counter()
+    oracle.fwd_rows(f64["q"], f64["k"], f64["v"], f64["w"], f64["beta"], f64["logf"], wl.scale, rows=probe)
+    rate = probe.size / max(time.perf_counter() - t, 1e-6)
+    nrows = int(max(8, min(200000, rate * seconds / len(heads))))
+    rows = rng.integers(0, Ltot, (len(heads), nrows))
+    t = time.perf_counter()
+    oracle.fwd_rows(f64["q"], f64["k"], f64["v"], f64["w"], f64["beta"], f64["logf"], wl.scale, rows=rows)
+    el = time.perf_counter() - t
+    tps = rows.size / el
+    return {"value": round(tps, 1), "unit": "tokens/s (query rows of the full job per second)",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{rows.size} random query rows (uniform over all {Ltot} positions) of "
+                      f"{len(heads)} heads, fp64 walk, {el:.1f} s",
+            "gpu_tokens_per_s_same_job": round(gpu_tokens_per_s, 1)}
+
+
+if __name__ == "__main__":
+    main()

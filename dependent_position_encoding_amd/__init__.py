@@ -54,7 +54,7 @@ _lib = None
 EXPORTS = ["path_abi_version", "path_status_str", "path_last_error",
            "path_attn_fwd_workspace", "path_attn_fwd", "path_kv_update",
            "path_kv_append", "path_decode_workspace", "path_decode",
-           "path_decode_step", "path_causal_attn_fwd"]
+           "path_decode_step", "path_causal_attn_fwd", "path_attn_fwd_timed"]
 
 
 def load_library(path: str = LIB_PATH):
@@ -79,6 +79,7 @@ def load_library(path: str = LIB_PATH):
         "path_decode": ([DP, CP, I, P, P, P, P, S, P], I),
         "path_decode_step": ([DP, CP, I, P, P, P, P, P, P, P, P, P, S, P], I),
         "path_causal_attn_fwd": ([DP, P, P, P, P, P, P], I),
+        "path_attn_fwd_timed": ([DP, P, P, P, P, P, P, P, P, CP, P, S, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -154,7 +155,7 @@ class Cache:
 
 
 def fwd(q, k, v, w, beta, logf=None, scale=None, cache: Cache | None = None,
-        block=0, workspace: torch.Tensor | None = None, out=None):
+        block=0, workspace: torch.Tensor | None = None, out=None, events=None):
     """Prefill forward.  q,k,v,w [N,H,L,d] (fp32 or bf16); beta, logf [N,H,L] fp32.
 
     Returns (o [N,H,L,d], lse [N,H,L] fp32).  If cache is given, it is filled
@@ -180,11 +181,24 @@ def fwd(q, k, v, w, beta, logf=None, scale=None, cache: Cache | None = None,
     else:
         o, lse = out
     cc = cache._c() if cache is not None else None
-    _check(lib.path_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w),
-                             _ptr(beta), _ptr(logf), _ptr(o), _ptr(lse),
-                             ctypes.byref(cc) if cc is not None else None,
-                             _ptr(workspace), workspace.numel(), _stream(dev)))
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf),
+            _ptr(o), _ptr(lse), ctypes.byref(cc) if cc is not None else None,
+            _ptr(workspace), workspace.numel(), _stream(dev))
+    if events is None:
+        _check(lib.path_attn_fwd(*args))
+    else:
+        # events: four torch.cuda.Event(enable_timing=True), recorded by the library
+        evs = (ctypes.c_void_p * 4)(*[e.cuda_event for e in _init_events(events, dev)])
+        _check(lib.path_attn_fwd_timed(*args, evs))
     return o, lse
+
+
+def _init_events(events, dev):
+    """torch creates the underlying hipEvent lazily; force it into existence."""
+    for e in events:
+        if e.cuda_event == 0:
+            e.record(torch.cuda.current_stream(dev))
+    return events
 
 
 def _cache_desc(cache: Cache, scale):

@@ -1,14 +1,521 @@
-// fwd_bf16.hip -- matrix-core (bf16 MFMA, fp32 accumulate) PaTH forward.
+// fwd_bf16.hip -- matrix-core PaTH forward for bf16 inputs (head dim 32, 64).
+//
+// Citations: [Notes s2.x] = reading-notes page "PaTH Attention:通过累积
+// Householder 变换编码位置" (cc.laoqi.cc), section 2.x.
+//
+// Two kernels per call:
+//   precond (one 256-thread workgroup per 64-token block): UT solve
+//     U = (I + strictLower(diag(beta) W W^T))^{-1} diag(beta)   [Notes s2.6]
+//     and the block products of [Notes s2.7]:
+//       P = lower(Q W^T) U,  Qleft = Q - P W,  M = strictLower(W K^T),
+//       Kright = K - (U M)^T W,  E = W^T U^T W (block transition I - E),
+//       Dg = lower(Q K^T) - P M  (in-block logits),
+//     on bf16 MFMA with fp32 accumulation; fp32 intermediates are split into
+//     bf16 hi + lo parts so these products keep close to fp32 accuracy.
+//   scan (one 128-thread workgroup = 2 waves per 64-query block, heaviest
+//     blocks first): the diagonal block from Dg, then for c = b-1 .. 0 the
+//     right-to-left scan of [Notes s2.7] with an online softmax.  Everything
+//     is kept transposed so that no operand needs a register transpose:
+//       S^T     = Kright_c . Qwork^T           (keys x queries)
+//       O^T    += V_c^T . P^T                  (d x queries)
+//       Qwork^T += (-E_c) . Qwork^T            (d x queries, fp32 state)
+//     Each wave owns 32 queries = one C-tile column, so a lane owns a single
+//     query: the online-softmax rescale is a per-lane scalar and the row max
+//     needs one exchange between the two lane halves.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mfma.hpp"
 
 namespace pa {
 
-bool fwd_bf16_supported(int d, int block) { (void)d; (void)block; return false; }
+namespace {
+
+constexpr int kB = 64;       // block size
+constexpr int kSB = 72;      // LDS row stride of bf16 tiles with 64 columns
+constexpr int kSF = 68;      // LDS row stride of float tiles with 64 columns
+
+// Writes a C tile through f(row, col, value).
+template <typename F>
+__device__ inline void for_tile(const f32x16& acc, int m0, int n0, int lane, F f) {
+    const int h = lane >> 5, col = n0 + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) f(m0 + crow(r, h), col, acc[r]);
+}
+
+template <int D>
+__global__ void __launch_bounds__(256)
+precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                    const __bf16* __restrict__ v, const __bf16* __restrict__ w,
+                    const float* __restrict__ beta, const float* __restrict__ logf,
+                    int L, int nb, FwdWs ws) {
+    constexpr int B = kB, SB = kSB, SF = kSF, UPR = D / 8;
+    __shared__ __attribute__((aligned(16))) __bf16 sW[B * SB], sWt[D * SB], sQ[B * SB], sK[B * SB];
+    __shared__ __attribute__((aligned(16))) float sU[B * SF], sUt[B * SF], sX[B * SF], sP[B * SF],
+        sMt[B * SF];
+    __shared__ float sBeta[B];
+
+    const int blk = blockIdx.x, slice = blk / nb, c = blk % nb;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const size_t base = (size_t)slice * L;
+    const int row0 = c * B;
+
+    // ---- 1. stage W, Q, K (and W^T) as bf16, V as float; zero U ----------
+    for (int u = tid; u < B * UPR; u += 256) {
+        const int r = u / UPR, x0 = (u % UPR) * 8, pos = row0 + r;
+        bf16x8 wv, qv, kv, vv;
+        if (pos < L) {
+            const size_t g = (base + pos) * D + x0;
+            wv = *reinterpret_cast<const bf16x8*>(w + g);
+            qv = *reinterpret_cast<const bf16x8*>(q + g);
+            kv = *reinterpret_cast<const bf16x8*>(k + g);
+            vv = *reinterpret_cast<const bf16x8*>(v + g);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wv[e] = qv[e] = kv[e] = vv[e] = (__bf16)0.f;
+        }
+        *reinterpret_cast<bf16x8*>(sW + r * SB + x0) = wv;
+        *reinterpret_cast<bf16x8*>(sQ + r * SB + x0) = qv;
+        *reinterpret_cast<bf16x8*>(sK + r * SB + x0) = kv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            sWt[(x0 + e) * SB + r] = wv[e];
+            sP[r * SF + x0 + e] = (float)vv[e];
+        }
+    }
+    for (int e = tid; e < B * B; e += 256) sU[(e / B) * SF + e % B] = 0.f;
+    if (tid < B) sBeta[tid] = row0 + tid < L ? beta[base + row0 + tid] : 0.f;
+    if (tid == 0) {
+        float acc = 0.f;
+        for (int r = 0; r < B; ++r) {
+            if (logf && row0 + r < L) acc += logf[base + row0 + r];
+            ws.gl[(size_t)blk * B + r] = acc;
+        }
+        ws.tot[blk] = acc;
+    }
+    __syncthreads();
+
+    // ---- 2. V^T with keys in operand order; G = diag(beta) strictLower(WW^T)
+    {
+        __bf16* vt = static_cast<__bf16*>(ws.vt) + (size_t)blk * D * B;
+        for (int u = tid; u < D * 8; u += 256) {
+            const int x = u / 8, s0 = (u % 8) * 8;
+            bf16x8 pk;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pk[e] = (__bf16)sP[swap23(s0 + e) * SF + x];
+            *reinterpret_cast<bf16x8*>(vt + x * B + s0) = pk;
+        }
+    }
+    if (wave < 3) {
+        const int mt = wave == 0 ? 0 : 1, nt = wave == 2 ? 1 : 0;
+        f32x16 acc = zero16();
+        tile_mm<D>(acc, sW, SB, sW, SB, 32 * mt, 32 * nt, lane);
+        for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) {
+            sX[i * SF + j] = i > j ? sBeta[i] * a : 0.f;
+        });
+    }
+    __syncthreads();
+
+    // ---- 3. T = (I + G)^{-1}, blocked over four 16 x 16 diagonal blocks ----
+    // diagonal blocks by forward substitution (wave a, one column per lane)
+    if (lane < 16) {
+        const int o = 16 * wave;
+        float t[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float s = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < i; ++kk) s += sX[(o + i) * SF + o + kk] * t[kk];
+            t[i] = i < lane ? 0.f : (i == lane ? 1.f : -s);
+            sU[(o + i) * SF + o + lane] = t[i];
+        }
+    }
+    __syncthreads();
+    // off-diagonal blocks: T_ab = -T_aa sum_{c=b}^{a-1} G_ac T_cb, by distance
+    for (int lev = 1; lev < 4; ++lev) {
+        const int njobs = 4 - lev, r = lane >> 2, c0 = (lane & 3) * 4;
+        if (wave < njobs) {
+            const int bb = wave, a = bb + lev;
+            float x[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int cb = bb; cb < a; ++cb) {
+#pragma unroll
+                for (int kk = 0; kk < 16; ++kk) {
+                    const float g = sX[(16 * a + r) * SF + 16 * cb + kk];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] += g * sU[(16 * cb + kk) * SF + 16 * bb + c0 + e];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sP[(16 * a + r) * SF + 16 * bb + c0 + e] = x[e];
+        }
+        __syncthreads();
+        if (wave < njobs) {
+            const int bb = wave, a = bb + lev;
+            float y[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk) {
+                const float t = sU[(16 * a + r) * SF + 16 * a + kk];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] -= t * sP[(16 * a + kk) * SF + 16 * bb + c0 + e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sU[(16 * a + r) * SF + 16 * bb + c0 + e] = y[e];
+        }
+        __syncthreads();
+    }
+    // U = T diag(beta), kept in both orientations
+    for (int e = tid; e < B * B; e += 256) {
+        const int i = e / B, j = e % B;
+        const float u = sU[i * SF + j] * sBeta[j];
+        sU[i * SF + j] = u;
+        sUt[j * SF + i] = u;
+    }
+    __syncthreads();
+
+    // ---- 4. X1 = lower(Q W^T) -> sX;  M^T (M = strictLower(W K^T)) -> sMt --
+    for (int job = wave; job < 8; job += 4) {
+        const int t = job & 3, mt = t >> 1, nt = t & 1;
+        f32x16 acc = zero16();
+        if (job < 4) {
+            if (!(mt == 0 && nt == 1)) tile_mm<D>(acc, sQ, SB, sW, SB, 32 * mt, 32 * nt, lane);
+            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) {
+                sX[i * SF + j] = j <= i ? a : 0.f;
+            });
+        } else {
+            // M^T[j][b] = k_j . w_b for b > j
+            if (!(mt == 1 && nt == 0)) tile_mm<D>(acc, sK, SB, sW, SB, 32 * mt, 32 * nt, lane);
+            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int j, int bcol, float a) {
+                sMt[j * SF + bcol] = bcol > j ? a : 0.f;
+            });
+        }
+    }
+    __syncthreads();
+
+    // ---- 5a. P = X1 U -> sP ------------------------------------------------
+    {
+        const int mt = wave >> 1, nt = wave & 1;
+        f32x16 acc = zero16();
+        if (!(mt == 0 && nt == 1)) tile_mm<B>(acc, sX, SF, sUt, SF, 32 * mt, 32 * nt, lane);
+        for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) { sP[i * SF + j] = a; });
+    }
+    __syncthreads();
+
+    // ---- 5b. R^T = M^T U^T -> sX;  Qleft = Q - P W;  Dg = lower(QK^T) - P M -
+    {
+        constexpr int NQ = 2 * (D / 32);
+        for (int job = wave; job < 4 + NQ + 3; job += 4) {
+            f32x16 acc = zero16();
+            if (job < 4) {
+                const int mt = job >> 1, nt = job & 1;
+                if (!(mt == 1 && nt == 0)) tile_mm<B>(acc, sMt, SF, sU, SF, 32 * mt, 32 * nt, lane);
+                for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) { sX[i * SF + j] = a; });
+            } else if (job < 4 + NQ) {
+                const int t = job - 4, mt = t / (D / 32), nt = t % (D / 32);
+                tile_mm<B>(acc, sP, SF, sWt, SB, 32 * mt, 32 * nt, lane);
+                float* ql = ws.ql + (size_t)blk * B * D;
+                for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int x, float a) {
+                    ql[i * D + x] = (float)sQ[i * SB + x] - a;
+                });
+            } else {
+                const int t = job - 4 - NQ;
+                const int mt = t == 0 ? 0 : 1, nt = t == 2 ? 1 : 0;
+                tile_mm<B>(acc, sP, SF, sMt, SF, 32 * mt, 32 * nt, lane);
+                f32x16 qk = zero16();
+                tile_mm<D>(qk, sQ, SB, sK, SB, 32 * mt, 32 * nt, lane);
+                float* dg = ws.dg + (size_t)blk * B * B;
+                const int h = lane >> 5, j = 32 * nt + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = 32 * mt + crow(r, h);
+                    dg[i * B + j] = j <= i ? qk[r] - acc[r] : 0.f;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- 6. Kright = K - R^T W (bf16, columns in operand order) -----------
+    for (int job = wave; job < 2 * (D / 32); job += 4) {
+        const int mt = job / (D / 32), nt = job % (D / 32);
+        f32x16 acc = zero16();
+        tile_mm<B>(acc, sX, SF, sWt, SB, 32 * mt, 32 * nt, lane);
+        __bf16* kr = static_cast<__bf16*>(ws.kr) + (size_t)blk * B * D;
+        float* k32 = ws.k32 ? ws.k32 + (size_t)blk * B * D : nullptr;
+        for_tile(acc, 32 * mt, 32 * nt, lane, [&](int j, int x, float a) {
+            const float val = (float)sK[j * SB + x] - a;
+            kr[j * D + swap23(x)] = (__bf16)val;
+            if (k32) k32[j * D + x] = val;
+        });
+    }
+    __syncthreads();
+
+    // ---- 7. Y^T = W^T U  (Y = U^T W) -> sX --------------------------------
+    for (int job = wave; job < 2 * (D / 32); job += 4) {
+        const int mt = job / 2, nt = job % 2;
+        f32x16 acc = zero16();
+        tile_mm<B>(acc, sWt, SB, sUt, SF, 32 * mt, 32 * nt, lane);
+        for_tile(acc, 32 * mt, 32 * nt, lane, [&](int y, int cc, float a) { sX[y * SF + cc] = a; });
+    }
+    __syncthreads();
+
+    // ---- 8. E = W^T Y; store -E with the contracted index in operand order -
+    for (int job = wave; job < (D / 32) * (D / 32); job += 4) {
+        const int mt = job / (D / 32), nt = job % (D / 32);
+        f32x16 acc = zero16();
+        tile_mm<B>(acc, sWt, SB, sX, SF, 32 * mt, 32 * nt, lane);
+        __bf16* em = static_cast<__bf16*>(ws.em) + (size_t)blk * D * D;
+        float* e32 = ws.e32 ? ws.e32 + (size_t)blk * D * D : nullptr;
+        for_tile(acc, 32 * mt, 32 * nt, lane, [&](int x, int y, float a) {
+            em[x * D + swap23(y)] = (__bf16)(-a);
+            if (e32) e32[x * D + y] = a;
+        });
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <int D>
+struct TileRegs {
+    static constexpr int KU = D / 16, VU = D / 16, EU = (D * D) / 1024 > 0 ? (D * D) / 1024 : 1;
+    uint4 k[KU], v[VU], e[EU];
+    float4 g;
+    float tot;
+};
+
+template <int D, bool FOX>
+__global__ void __launch_bounds__(128)
+scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
+                 float* __restrict__ lse) {
+    constexpr int B = kB, SK = D + 8, SV = B + 8, SE = D + 8, NT = D / 32, NKC = D / 16;
+    constexpr int EUNITS = D * D / 8;
+    __shared__ __attribute__((aligned(16))) __bf16 sK[B * SK], sV[D * SV], sE[D * SE];
+    __shared__ __attribute__((aligned(16))) float sG[B];
+
+    const int NH = gridDim.x / nb;
+    const int b = nb - 1 - (int)(blockIdx.x / NH);
+    const int slice = blockIdx.x % NH;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
+    const int col = lane & 31, qloc = 32 * wave + col;
+    const size_t blk0 = (size_t)slice * nb;
+    const __bf16* kr = static_cast<const __bf16*>(ws.kr);
+    const __bf16* vt = static_cast<const __bf16*>(ws.vt);
+    const __bf16* em = static_cast<const __bf16*>(ws.em);
+
+    auto load = [&](int c, TileRegs<D>& R) {
+        const size_t bc = blk0 + c;
+#pragma unroll
+        for (int u = 0; u < TileRegs<D>::KU; ++u) {
+            const int idx = tid + 128 * u;
+            R.k[u] = *reinterpret_cast<const uint4*>(kr + bc * B * D + (size_t)idx * 8);
+            R.v[u] = *reinterpret_cast<const uint4*>(vt + bc * D * B + (size_t)idx * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < TileRegs<D>::EU; ++u) {
+            const int idx = tid + 128 * u;
+            if (idx < EUNITS)
+                R.e[u] = *reinterpret_cast<const uint4*>(em + bc * D * D + (size_t)idx * 8);
+        }
+        if (FOX) {
+            if (tid < 16) R.g = *reinterpret_cast<const float4*>(ws.gl + bc * B + 4 * tid);
+            R.tot = ws.tot[bc];
+        }
+    };
+    auto store = [&](const TileRegs<D>& R) {
+#pragma unroll
+        for (int u = 0; u < TileRegs<D>::KU; ++u) {
+            const int idx = tid + 128 * u;
+            const int kr_row = idx / (D / 8), kx = (idx % (D / 8)) * 8;
+            *reinterpret_cast<uint4*>(sK + kr_row * SK + kx) = R.k[u];
+            const int vr = idx / 8, vs = (idx % 8) * 8;
+            *reinterpret_cast<uint4*>(sV + vr * SV + vs) = R.v[u];
+        }
+#pragma unroll
+        for (int u = 0; u < TileRegs<D>::EU; ++u) {
+            const int idx = tid + 128 * u;
+            if (idx < EUNITS) {
+                const int er = idx / (D / 8), ex = (idx % (D / 8)) * 8;
+                *reinterpret_cast<uint4*>(sE + er * SE + ex) = R.e[u];
+            }
+        }
+        if (FOX && tid < 16) *reinterpret_cast<float4*>(sG + 4 * tid) = R.g;
+    };
+
+    f32x16 Qw[NT], Ot[NT], S[2];
+    const size_t bq = blk0 + b;
+    {
+        const float* qlp = ws.ql + (bq * B + qloc) * D;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            Ot[t] = zero16();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 v4 = *reinterpret_cast<const f32x4*>(qlp + 32 * t + 8 * i + 4 * h);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Qw[t][4 * i + j] = v4[j];
+            }
+        }
+    }
+    const float gq = FOX ? ws.gl[bq * B + qloc] * kLog2e : 0.f;
+
+    TileRegs<D> R;
+    load(b, R);
+    store(R);
+    __syncthreads();
+
+    float m, l;
+    auto softmax_pv = [&](bool first) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = first ? mx : fmaxf(m, mx);
+        const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+        float rs = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(S[mt][r] - mn);
+                S[mt][r] = p;
+                rs += p;
+            }
+        rs += __shfl_xor(rs, 32, 64);
+        l = first ? rs : l * alpha + rs;
+        m = mn;
+        bf16x8 Pb[4];
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Pb[kc][e] = (__bf16)S[kc >> 1][8 * (kc & 1) + e];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (!first) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Ot[t][r] *= alpha;
+            }
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(sV + (32 * t + col) * SV + 16 * kc + 8 * h);
+                Ot[t] = mfma32(a, Pb[kc], Ot[t]);
+            }
+        }
+    };
+
+    // diagonal block: in-block logits, causal mask
+    {
+        const float* dgp = ws.dg + (bq * B + qloc) * B;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int k0 = 32 * mt + 8 * i + 4 * h;
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(dgp + k0);
+                f32x4 g4 = {0.f, 0.f, 0.f, 0.f};
+                if (FOX) g4 = *reinterpret_cast<const f32x4*>(sG + k0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    S[mt][4 * i + j] = (k0 + j <= qloc)
+                                           ? d4[j] * scale2 + (FOX ? gq - g4[j] * kLog2e : 0.f)
+                                           : -INFINITY;
+            }
+        softmax_pv(true);
+    }
+
+    float grun = 0.f;
+    if (b > 0) load(b - 1, R);
+    for (int c = b - 1; c >= 0; --c) {
+        __syncthreads();
+        store(R);
+        __syncthreads();
+        if (FOX) grun += R.tot;
+        if (c > 0) load(c - 1, R);
+
+        bf16x8 Qb[NKC];
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Qb[kc][e] = (__bf16)Qw[kc >> 1][8 * (kc & 1) + e];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            S[mt] = zero16();
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + (32 * mt + col) * SK + 16 * kc + 8 * h);
+                S[mt] = mfma32(a, Qb[kc], S[mt]);
+            }
+        }
+        const float rowb = gq + grun * kLog2e;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f32x4 g4 = {0.f, 0.f, 0.f, 0.f};
+                if (FOX) g4 = *reinterpret_cast<const f32x4*>(sG + 32 * mt + 8 * i + 4 * h);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    S[mt][4 * i + j] = FOX ? S[mt][4 * i + j] * scale2 + (rowb - g4[j] * kLog2e)
+                                           : S[mt][4 * i + j] * scale2;
+            }
+        softmax_pv(false);
+        if (c > 0) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(sE + (32 * t + col) * SE + 16 * kc + 8 * h);
+                    Qw[t] = mfma32(a, Qb[kc], Qw[t]);
+                }
+        }
+    }
+
+    const int pos = b * B + qloc;
+    if (pos < L) {
+        const float inv = 1.f / l;
+        __bf16* op = o + ((size_t)slice * L + pos) * D;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+                bf16x4 pk;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) pk[j] = (__bf16)(Ot[t][4 * i + j] * inv);
+                *reinterpret_cast<bf16x4*>(op + 32 * t + 8 * i + 4 * h) = pk;
+            }
+        if (lse && h == 0) lse[(size_t)slice * L + pos] = (m + __log2f(l)) * kLn2;
+    }
+}
+
+template <int D>
+hipError_t launch_t(const FwdArgs& a, hipStream_t st) {
+    const int nb = (a.L + kB - 1) / kB;
+    const int nblk = a.N * a.H * nb;
+    hipLaunchKernelGGL((precond_mfma_kernel<D>), dim3(nblk), dim3(256), 0, st,
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                       (const __bf16*)a.w, a.beta, a.logf, a.L, nb, a.ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.ev) hipEventRecord(a.ev[1], st);
+    const float scale2 = a.scale * kLog2e;
+    if (a.logf)
+        hipLaunchKernelGGL((scan_mfma_kernel<D, true>), dim3(nblk), dim3(128), 0, st, a.L, nb,
+                           scale2, a.ws, (__bf16*)a.o, a.lse);
+    else
+        hipLaunchKernelGGL((scan_mfma_kernel<D, false>), dim3(nblk), dim3(128), 0, st, a.L, nb,
+                           scale2, a.ws, (__bf16*)a.o, a.lse);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool fwd_bf16_supported(int d, int block) { return (d == 32 || d == 64) && block == 64; }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
-    (void)a; (void)st;
-    return hipErrorNotSupported;
+    switch (a.d) {
+        case 32: return launch_t<32>(a, st);
+        case 64: return launch_t<64>(a, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_causal(const FwdArgs& a, hipStream_t st) {

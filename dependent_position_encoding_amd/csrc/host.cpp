@@ -140,11 +140,11 @@ size_t path_attn_fwd_workspace(const path_fwd_desc* desc, int with_cache) {
     return fwd_layout(desc, with_cache != 0).total;
 }
 
-path_status path_attn_fwd(const path_fwd_desc* desc, const void* q, const void* k,
-                          const void* v, const void* w, const float* beta,
-                          const float* logf, void* o, float* lse,
-                          const path_cache* cache_out, void* ws, size_t ws_bytes,
-                          hipStream_t stream) {
+static path_status fwd_impl(const path_fwd_desc* desc, const void* q, const void* k,
+                            const void* v, const void* w, const float* beta,
+                            const float* logf, void* o, float* lse,
+                            const path_cache* cache_out, void* ws, size_t ws_bytes,
+                            hipStream_t stream, hipEvent_t* ev) {
     path_status s = check_desc(desc, true);
     if (s != PATH_OK) return s;
     if (!q || !k || !v || !w || !beta || !o) return fail(PATH_E_NULL, "q, k, v, w, beta and o are required");
@@ -180,13 +180,35 @@ path_status path_attn_fwd(const path_fwd_desc* desc, const void* q, const void* 
         a.ws.suf = reinterpret_cast<float*>(base + lay.suf);
         a.ws.gpre = reinterpret_cast<float*>(base + lay.gpre);
     }
+    a.ev = ev;
+    if (ev) hipEventRecord(ev[0], stream);
     hipError_t e = use_mfma(desc) ? pa::launch_fwd_bf16(a, stream) : pa::launch_fwd_f32(a, stream);
     if (e != hipSuccess) return launched(e, "path_attn_fwd");
+    if (ev) hipEventRecord(ev[2], stream);
     if (cache_out) {
         e = pa::launch_kv_align(a, cache_args(desc, cache_out), stream);
-        return launched(e, "path_attn_fwd (cache alignment)");
+        if (e != hipSuccess) return launched(e, "path_attn_fwd (cache alignment)");
     }
+    if (ev) hipEventRecord(ev[3], stream);
     return ok();
+}
+
+path_status path_attn_fwd(const path_fwd_desc* desc, const void* q, const void* k,
+                          const void* v, const void* w, const float* beta,
+                          const float* logf, void* o, float* lse,
+                          const path_cache* cache_out, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+    return fwd_impl(desc, q, k, v, w, beta, logf, o, lse, cache_out, ws, ws_bytes, stream,
+                    nullptr);
+}
+
+path_status path_attn_fwd_timed(const path_fwd_desc* desc, const void* q, const void* k,
+                                const void* v, const void* w, const float* beta,
+                                const float* logf, void* o, float* lse,
+                                const path_cache* cache_out, void* ws, size_t ws_bytes,
+                                hipStream_t stream, hipEvent_t ev[4]) {
+    if (!ev || !ev[0] || !ev[1] || !ev[2] || !ev[3]) return fail(PATH_E_NULL, "four events are required");
+    return fwd_impl(desc, q, k, v, w, beta, logf, o, lse, cache_out, ws, ws_bytes, stream, ev);
 }
 
 path_status path_kv_update(const path_fwd_desc* desc, const path_cache* cache, int n,

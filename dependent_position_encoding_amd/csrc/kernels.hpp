@@ -35,6 +35,7 @@ struct FwdArgs {
     void* o;
     float* lse;
     FwdWs ws;
+    hipEvent_t* ev;   // optional phase events; ev[1] is recorded before the scan
 };
 
 struct CacheArgs {

@@ -127,6 +127,17 @@ path_status path_attn_fwd(const path_fwd_desc *desc, const void *q,
                           float *lse, const path_cache *cache_out, void *ws,
                           size_t ws_bytes, hipStream_t stream);
 
+/* path_attn_fwd with phase timing, for measurement.  Identical work, plus
+ * four events recorded on `stream` (created by the caller): ev[0] before the
+ * block preconditioning, ev[1] before the right-to-left scan, ev[2] after it,
+ * ev[3] after the cache alignment (right after ev[2] when cache_out is NULL). */
+path_status path_attn_fwd_timed(const path_fwd_desc *desc, const void *q,
+                                const void *k, const void *v, const void *w,
+                                const float *beta, const float *logf, void *o,
+                                float *lse, const path_cache *cache_out,
+                                void *ws, size_t ws_bytes, hipStream_t stream,
+                                hipEvent_t ev[4]);
+
 /* Cache rewrite for a new position [Notes s2.8, eq. (1) of the paper]:
  *   k_j <- k_j - beta_t (w_t^T k_j) w_t   for every slot j in [0, n).
  * w_t [N, H, d] desc->dtype; beta_t [N, H] float32.  In place on kcache. */
