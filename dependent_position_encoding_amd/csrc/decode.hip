@@ -207,24 +207,47 @@ decode_chunk_kernel(K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ 
 }
 
 // Merge the chunk partials of one slice: o = sum acc_c e^{m_c - M} / l,
-// lse = M + log l.
+// lse = M + log l.  One 256-thread block per slice: a block-wide max, then
+// 256/D groups of D lanes each sum a strided share of the chunks.
 template <typename T, int D>
-__global__ void decode_combine_kernel(const float* __restrict__ part, int nch,
-                                      T* __restrict__ o_t, float* __restrict__ lse_t) {
-    const int slice = blockIdx.x;
+__global__ void __launch_bounds__(256)
+decode_combine_kernel(const float* __restrict__ part, int nch, T* __restrict__ o_t,
+                      float* __restrict__ lse_t) {
+    constexpr int G = 256 / D;
+    __shared__ float red[256];
+    __shared__ float sacc[G][D];
+    __shared__ float sl[G];
+    const int slice = blockIdx.x, tid = threadIdx.x;
     const float* p = part + (size_t)slice * nch * (D + 2);
-    float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, p[(size_t)c * (D + 2)]);
-    const int x = threadIdx.x;
-    float a = 0.f, ls = 0.f;
-    for (int c = 0; c < nch; ++c) {
-        const float mc = p[(size_t)c * (D + 2)];
-        const float f = (mc == -INFINITY) ? 0.f : __expf(mc - M);
-        ls += p[(size_t)c * (D + 2) + 1] * f;
-        if (x < D) a += p[(size_t)c * (D + 2) + 2 + x] * f;
+    float mloc = -INFINITY;
+    for (int c = tid; c < nch; c += 256) mloc = fmaxf(mloc, p[(size_t)c * (D + 2)]);
+    red[tid] = mloc;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+        __syncthreads();
     }
-    if (x < D) o_t[(size_t)slice * D + x] = from_f32<T>(a / ls);
-    if (x == 0 && lse_t) lse_t[slice] = M + logf(ls);
+    const float M = red[0];
+    const int g = tid / D, x = tid % D;
+    float a = 0.f, ls = 0.f;
+#pragma unroll 4
+    for (int c = g; c < nch; c += G) {
+        const float* pc = p + (size_t)c * (D + 2);
+        const float mc = pc[0];
+        const float f = (mc == -INFINITY) ? 0.f : __expf(mc - M);
+        a += f * pc[2 + x];
+        ls += f * pc[1];
+    }
+    sacc[g][x] = a;
+    if (x == 0) sl[g] = ls;
+    __syncthreads();
+    if (tid < D) {
+        float s = 0.f, lt = 0.f;
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) { s += sacc[gg][tid]; lt += sl[gg]; }
+        o_t[(size_t)slice * D + tid] = from_f32<T>(s / lt);
+        if (tid == 0 && lse_t) lse_t[slice] = M + logf(lt);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -384,7 +407,7 @@ static hipError_t decode_t(const CacheArgs& c, int n_keys, float scale, const vo
                            (const T*)q_t, nullptr, nullptr, nullptr, nullptr, nullptr, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(c.N * c.H), dim3(64), 0, st,
+    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(c.N * c.H), dim3(256), 0, st,
                        (const float*)part, nch, (T*)o_t, lse_t);
     return hipGetLastError();
 }

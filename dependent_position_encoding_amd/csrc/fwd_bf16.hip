@@ -272,20 +272,14 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 }
 
 // ---------------------------------------------------------------------------
-template <int D>
-struct TileRegs {
-    static constexpr int KU = D / 16, VU = D / 16, EU = (D * D) / 1024 > 0 ? (D * D) / 1024 : 1;
-    uint4 k[KU], v[VU], e[EU];
-    float4 g;
-    float tot;
-};
-
 template <int D, bool FOX>
 __global__ void __launch_bounds__(128)
 scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
                  float* __restrict__ lse) {
     constexpr int B = kB, SK = D + 8, SV = B + 8, SE = D + 8, NT = D / 32, NKC = D / 16;
-    constexpr int EUNITS = D * D / 8;
+    constexpr int KU = D / 16;                    // 16-byte units per thread: Kright, V^T
+    constexpr int EU = (D * D / 8 + 127) / 128;   // and -E
+    constexpr bool E_FULL = (D * D / 8) % 128 == 0;
     __shared__ __attribute__((aligned(16))) __bf16 sK[B * SK], sV[D * SV], sE[D * SE];
     __shared__ __attribute__((aligned(16))) float sG[B];
 
@@ -299,44 +293,42 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
     const __bf16* vt = static_cast<const __bf16*>(ws.vt);
     const __bf16* em = static_cast<const __bf16*>(ws.em);
 
-    auto load = [&](int c, TileRegs<D>& R) {
-        const size_t bc = blk0 + c;
-#pragma unroll
-        for (int u = 0; u < TileRegs<D>::KU; ++u) {
-            const int idx = tid + 128 * u;
-            R.k[u] = *reinterpret_cast<const uint4*>(kr + bc * B * D + (size_t)idx * 8);
-            R.v[u] = *reinterpret_cast<const uint4*>(vt + bc * D * B + (size_t)idx * 8);
-        }
-#pragma unroll
-        for (int u = 0; u < TileRegs<D>::EU; ++u) {
-            const int idx = tid + 128 * u;
-            if (idx < EUNITS)
-                R.e[u] = *reinterpret_cast<const uint4*>(em + bc * D * D + (size_t)idx * 8);
-        }
-        if (FOX) {
-            if (tid < 16) R.g = *reinterpret_cast<const float4*>(ws.gl + bc * B + 4 * tid);
-            R.tot = ws.tot[bc];
-        }
-    };
-    auto store = [&](const TileRegs<D>& R) {
-#pragma unroll
-        for (int u = 0; u < TileRegs<D>::KU; ++u) {
-            const int idx = tid + 128 * u;
-            const int kr_row = idx / (D / 8), kx = (idx % (D / 8)) * 8;
-            *reinterpret_cast<uint4*>(sK + kr_row * SK + kx) = R.k[u];
-            const int vr = idx / 8, vs = (idx % 8) * 8;
-            *reinterpret_cast<uint4*>(sV + vr * SV + vs) = R.v[u];
-        }
-#pragma unroll
-        for (int u = 0; u < TileRegs<D>::EU; ++u) {
-            const int idx = tid + 128 * u;
-            if (idx < EUNITS) {
-                const int er = idx / (D / 8), ex = (idx % (D / 8)) * 8;
-                *reinterpret_cast<uint4*>(sE + er * SE + ex) = R.e[u];
-            }
-        }
-        if (FOX && tid < 16) *reinterpret_cast<float4*>(sG + 4 * tid) = R.g;
-    };
+    // next block's tiles, in flight in registers while the current one is used
+    u32x4 rk[KU], rv[KU], re[EU];
+    f32x4 rg = {0.f, 0.f, 0.f, 0.f};
+    float rtot = 0.f;
+#define PA_LOAD_TILES(c_)                                                              \
+    do {                                                                               \
+        const size_t bc = blk0 + (c_);                                                 \
+        _Pragma("unroll") for (int u = 0; u < KU; ++u) {                              \
+            const int idx = tid + 128 * u;                                             \
+            rk[u] = *reinterpret_cast<const u32x4*>(kr + bc * B * D + (size_t)idx * 8); \
+            rv[u] = *reinterpret_cast<const u32x4*>(vt + bc * D * B + (size_t)idx * 8); \
+        }                                                                              \
+        _Pragma("unroll") for (int u = 0; u < EU; ++u) {                              \
+            const int idx = tid + 128 * u;                                             \
+            if (E_FULL || idx < D * D / 8)                                             \
+                re[u] = *reinterpret_cast<const u32x4*>(em + bc * D * D + (size_t)idx * 8); \
+        }                                                                              \
+        if (FOX) {                                                                     \
+            rg = *reinterpret_cast<const f32x4*>(ws.gl + bc * B + 4 * (tid & 15));    \
+            rtot = ws.tot[bc];                                                         \
+        }                                                                              \
+    } while (0)
+#define PA_STORE_TILES()                                                               \
+    do {                                                                               \
+        _Pragma("unroll") for (int u = 0; u < KU; ++u) {                              \
+            const int idx = tid + 128 * u;                                             \
+            *reinterpret_cast<u32x4*>(sK + (idx / (D / 8)) * SK + (idx % (D / 8)) * 8) = rk[u]; \
+            *reinterpret_cast<u32x4*>(sV + (idx / 8) * SV + (idx % 8) * 8) = rv[u];    \
+        }                                                                              \
+        _Pragma("unroll") for (int u = 0; u < EU; ++u) {                              \
+            const int idx = tid + 128 * u;                                             \
+            if (E_FULL || idx < D * D / 8)                                             \
+                *reinterpret_cast<u32x4*>(sE + (idx / (D / 8)) * SE + (idx % (D / 8)) * 8) = re[u]; \
+        }                                                                              \
+        if (FOX && tid < 16) *reinterpret_cast<f32x4*>(sG + 4 * tid) = rg;           \
+    } while (0)
 
     f32x16 Qw[NT], Ot[NT], S[2];
     const size_t bq = blk0 + b;
@@ -355,9 +347,8 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
     }
     const float gq = FOX ? ws.gl[bq * B + qloc] * kLog2e : 0.f;
 
-    TileRegs<D> R;
-    load(b, R);
-    store(R);
+    PA_LOAD_TILES(b);
+    PA_STORE_TILES();
     __syncthreads();
 
     float m, l;
@@ -422,13 +413,13 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
     }
 
     float grun = 0.f;
-    if (b > 0) load(b - 1, R);
+    if (b > 0) PA_LOAD_TILES(b - 1);
     for (int c = b - 1; c >= 0; --c) {
         __syncthreads();
-        store(R);
+        PA_STORE_TILES();
         __syncthreads();
-        if (FOX) grun += R.tot;
-        if (c > 0) load(c - 1, R);
+        if (FOX) grun += rtot;
+        if (c > 0) PA_LOAD_TILES(c - 1);
 
         bf16x8 Qb[NKC];
 #pragma unroll
@@ -484,6 +475,8 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
             }
         if (lse && h == 0) lse[(size_t)slice * L + pos] = (m + __log2f(l)) * kLn2;
     }
+#undef PA_LOAD_TILES
+#undef PA_STORE_TILES
 }
 
 template <int D>
