@@ -256,60 +256,143 @@ decode_combine_kernel(const float* __restrict__ part, int nch, T* __restrict__ o
 // their block's right edge (Kright); the rest of the way is the product of
 // the later blocks' transitions.  In row form, kcache_c = Kright_c S_c with
 //   S_{nb-1} = I,  S_c = F_{c+1} S_{c+1},  F_c = I - E_c.
-// suffix_kernel runs that chain (one block per slice, sequential over c);
-// the block-prefix of log f is accumulated alongside.
+// The chain is split into groups of kSufGroup blocks so that it runs in
+// parallel: inside group g (blocks first..last)
+//   T_last = I,  T_c = F_{c+1} T_{c+1}          (suffix_local_kernel)
+// and the group's whole transition G_g = F_first T_first; across groups
+//   Z_{ng-1} = I,  Z_g = G_{g+1} Z_{g+1}         (suffix_groups_kernel)
+// so that S_c = T_c Z_{g(c)} (align_apply_kernel).  All in fp32.
+constexpr int kSufGroup = 16;
+
+template <int D>
+__device__ inline void mat_load(float (*dst)[D + 1], const float* src, int tid) {
+    for (int e = tid; e < D * D; e += 256) dst[e / D][e % D] = src[e];
+}
+
 template <int D>
 __global__ void __launch_bounds__(256)
-suffix_kernel(int nb, FwdWs ws) {
+suffix_local_kernel(int nb, int ngroups, FwdWs ws) {
     __shared__ float sS[D][D + 1], sE[D][D + 1];
-    const int slice = blockIdx.x, tid = threadIdx.x;
-    for (int e = tid; e < D * D; e += 256) sS[e / D][e % D] = (e / D == e % D) ? 1.f : 0.f;
+    constexpr int PER = D * D / 256 > 0 ? D * D / 256 : 1;
+    const int slice = blockIdx.x / ngroups, gi = blockIdx.x % ngroups, tid = threadIdx.x;
+    const int first = gi * kSufGroup, last = min(nb - 1, first + kSufGroup - 1);
     const size_t b0 = (size_t)slice * nb;
-    for (int e = tid; e < D * D; e += 256) ws.suf[(b0 + nb - 1) * D * D + e] = (e / D == e % D) ? 1.f : 0.f;
-    if (tid == 0) {
-        double acc = 0.0;
-        for (int c = 0; c < nb; ++c) {
-            ws.gpre[b0 + c] = (float)acc;
-            acc += ws.tot[b0 + c];
-        }
+    for (int e = tid; e < D * D; e += 256) {
+        const float v = (e / D == e % D) ? 1.f : 0.f;
+        sS[e / D][e % D] = v;
+        ws.suf[(b0 + last) * D * D + e] = v;
     }
-    for (int c = nb - 2; c >= 0; --c) {
+    // c = first - 1 yields the group total F_first T_first
+    for (int c = last - 1; c >= first - 1; --c) {
         __syncthreads();
-        for (int e = tid; e < D * D; e += 256) sE[e / D][e % D] = ws.e32[(b0 + c + 1) * D * D + e];
+        mat_load<D>(sE, ws.e32 + (b0 + c + 1) * D * D, tid);
         __syncthreads();
-        float r[D * D / 256 > 0 ? D * D / 256 : 1];
+        float r[PER];
         int cnt = 0;
         for (int e = tid; e < D * D; e += 256, ++cnt) {
             const int x = e / D, y = e % D;
-            float s = 0.f;
-            for (int z = 0; z < D; ++z) s += sE[x][z] * sS[z][y];
-            r[cnt] = sS[x][y] - s;
+            float acc = 0.f;
+#pragma unroll 8
+            for (int z = 0; z < D; ++z) acc += sE[x][z] * sS[z][y];
+            r[cnt] = sS[x][y] - acc;
         }
         __syncthreads();
+        float* dst = c >= first ? ws.suf + (b0 + c) * D * D
+                                : ws.grp + ((size_t)slice * ngroups + gi) * 2 * D * D;
         cnt = 0;
         for (int e = tid; e < D * D; e += 256, ++cnt) {
             sS[e / D][e % D] = r[cnt];
-            ws.suf[(b0 + c) * D * D + e] = r[cnt];
+            dst[e] = r[cnt];
         }
     }
 }
 
-// kcache rows of block c = Kright_c S_c; values copied; gcache = block prefix
-// + in-block cumsum.  One block of 256 threads per (slice, c).
+template <int D>
+__global__ void __launch_bounds__(256)
+suffix_groups_kernel(int nb, int ngroups, FwdWs ws) {
+    __shared__ float sZ[D][D + 1], sG[D][D + 1];
+    __shared__ double sScan[256];
+    constexpr int PER = D * D / 256 > 0 ? D * D / 256 : 1;
+    const int slice = blockIdx.x, tid = threadIdx.x;
+    const size_t b0 = (size_t)slice * nb, g0 = (size_t)slice * ngroups;
+    // block prefix of log f, gpre[c] = sum_{c' < c} tot[c'], accumulated in double
+    double carry = 0.0;
+    for (int c0 = 0; c0 < nb; c0 += 256) {
+        const int c = c0 + tid;
+        const double tv = c < nb ? (double)ws.tot[b0 + c] : 0.0;
+        sScan[tid] = tv;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const double add = tid >= off ? sScan[tid - off] : 0.0;
+            __syncthreads();
+            sScan[tid] += add;
+            __syncthreads();
+        }
+        if (c < nb) ws.gpre[b0 + c] = (float)(carry + sScan[tid] - tv);
+        carry += sScan[255];
+        __syncthreads();
+    }
+    for (int e = tid; e < D * D; e += 256) {
+        const float v = (e / D == e % D) ? 1.f : 0.f;
+        sZ[e / D][e % D] = v;
+        ws.grp[((g0 + ngroups - 1) * 2 + 1) * D * D + e] = v;
+    }
+    for (int g = ngroups - 2; g >= 0; --g) {
+        __syncthreads();
+        mat_load<D>(sG, ws.grp + ((g0 + g + 1) * 2) * D * D, tid);
+        __syncthreads();
+        float r[PER];
+        int cnt = 0;
+        for (int e = tid; e < D * D; e += 256, ++cnt) {
+            const int x = e / D, y = e % D;
+            float acc = 0.f;
+#pragma unroll 8
+            for (int z = 0; z < D; ++z) acc += sG[x][z] * sZ[z][y];
+            r[cnt] = acc;
+        }
+        __syncthreads();
+        cnt = 0;
+        for (int e = tid; e < D * D; e += 256, ++cnt) {
+            sZ[e / D][e % D] = r[cnt];
+            ws.grp[((g0 + g) * 2 + 1) * D * D + e] = r[cnt];
+        }
+    }
+}
+
+// kcache rows of block c = Kright_c (T_c Z_g); values copied; gcache = block
+// prefix + in-block cumsum.  One block of 256 threads per (slice, c).
 template <typename K, typename T, int B, int D>
 __global__ void __launch_bounds__(256)
-align_apply_kernel(int L, int nb, FwdWs ws, const T* __restrict__ v, int has_gate,
-                   K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ gc, int cap) {
-    __shared__ float sS[D][D + 1], sK[B][D + 1];
+align_apply_kernel(int L, int nb, int ngroups, FwdWs ws, const T* __restrict__ v,
+                   int has_gate, K* __restrict__ kc, T* __restrict__ vc,
+                   float* __restrict__ gc, int cap) {
+    __shared__ float sA[D][D + 1], sZ[D][D + 1], sK[B][D + 1];
+    constexpr int PER = D * D / 256 > 0 ? D * D / 256 : 1;
     const int blk = blockIdx.x, slice = blk / nb, c = blk % nb, tid = threadIdx.x;
-    for (int e = tid; e < D * D; e += 256) sS[e / D][e % D] = ws.suf[(size_t)blk * D * D + e];
+    const int g = c / kSufGroup;
+    mat_load<D>(sA, ws.suf + (size_t)blk * D * D, tid);
+    mat_load<D>(sZ, ws.grp + (((size_t)slice * ngroups + g) * 2 + 1) * D * D, tid);
     for (int e = tid; e < B * D; e += 256) sK[e / D][e % D] = ws.k32[(size_t)blk * B * D + e];
     __syncthreads();
+    float r[PER];
+    int cnt = 0;
+    for (int e = tid; e < D * D; e += 256, ++cnt) {
+        const int x = e / D, y = e % D;
+        float acc = 0.f;
+#pragma unroll 8
+        for (int z = 0; z < D; ++z) acc += sA[x][z] * sZ[z][y];
+        r[cnt] = acc;
+    }
+    __syncthreads();
+    cnt = 0;
+    for (int e = tid; e < D * D; e += 256, ++cnt) sA[e / D][e % D] = r[cnt];   // S_c
+    __syncthreads();
     for (int e = tid; e < B * D; e += 256) {
-        const int r = e / D, y = e % D, pos = c * B + r;
+        const int rr = e / D, y = e % D, pos = c * B + rr;
         if (pos >= L) continue;
         float s = 0.f;
-        for (int x = 0; x < D; ++x) s += sK[r][x] * sS[x][y];
+#pragma unroll 8
+        for (int x = 0; x < D; ++x) s += sK[rr][x] * sA[x][y];
         const size_t dst = ((size_t)slice * cap + pos) * D + y;
         kc[dst] = from_f32<K>(s);
         vc[dst] = v[((size_t)slice * L + pos) * D + y];
@@ -436,14 +519,20 @@ hipError_t launch_decode(const CacheArgs& c, int n_keys, float scale, const void
                     : decode_d<float, float>(c, n_keys, scale, q_t, o_t, lse_t, part, chunk, fused, k_t, v_t, w_t, beta_t, logf_t, st);
 }
 
+int suffix_groups(int nb) { return (nb + kSufGroup - 1) / kSufGroup; }
+
 template <typename K, typename T, int B, int D>
 static hipError_t align_t(const FwdArgs& a, const CacheArgs& c, hipStream_t st) {
     const int nb = (a.L + B - 1) / B;
-    hipLaunchKernelGGL((suffix_kernel<D>), dim3(a.N * a.H), dim3(256), 0, st, nb, a.ws);
+    const int ng = suffix_groups(nb);
+    const int NH = a.N * a.H;
+    hipLaunchKernelGGL((suffix_local_kernel<D>), dim3(NH * ng), dim3(256), 0, st, nb, ng, a.ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((align_apply_kernel<K, T, B, D>), dim3(a.N * a.H * nb), dim3(256), 0, st,
-                       a.L, nb, a.ws, (const T*)a.v, a.logf ? 1 : 0, (K*)c.kcache,
+    hipLaunchKernelGGL((suffix_groups_kernel<D>), dim3(NH), dim3(256), 0, st, nb, ng, a.ws);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((align_apply_kernel<K, T, B, D>), dim3(NH * nb), dim3(256), 0, st,
+                       a.L, nb, ng, a.ws, (const T*)a.v, a.logf ? 1 : 0, (K*)c.kcache,
                        (T*)c.vcache, c.gcache, c.cap);
     return hipGetLastError();
 }

@@ -84,13 +84,16 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
     for (int e = tid; e < B * B; e += 256) sU[(e / B) * SF + e % B] = 0.f;
     if (tid < B) sBeta[tid] = row0 + tid < L ? beta[base + row0 + tid] : 0.f;
-    if (tid == 0) {
-        float acc = 0.f;
-        for (int r = 0; r < B; ++r) {
-            if (logf && row0 + r < L) acc += logf[base + row0 + r];
-            ws.gl[(size_t)blk * B + r] = acc;
+    if (wave == 0) {
+        // in-block inclusive prefix sum of log f (one lane per token)
+        float acc = (logf && row0 + lane < L) ? logf[base + row0 + lane] : 0.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float up = __shfl_up(acc, off, 64);
+            if (lane >= off) acc += up;
         }
-        ws.tot[blk] = acc;
+        ws.gl[(size_t)blk * B + lane] = acc;
+        if (lane == 63) ws.tot[blk] = acc;
     }
     __syncthreads();
 

@@ -57,7 +57,7 @@ path_status check_desc(const path_fwd_desc* d, bool need_L) {
 }
 
 struct Layout {
-    size_t kr, vt, em, ql, dg, gl, tot, k32, e32, suf, gpre, total;
+    size_t kr, vt, em, ql, dg, gl, tot, k32, e32, suf, gpre, grp, total;
 };
 
 Layout fwd_layout(const path_fwd_desc* d, bool with_cache) {
@@ -81,6 +81,7 @@ Layout fwd_layout(const path_fwd_desc* d, bool with_cache) {
         l.e32 = take(nblk * D * D * 4);
         l.suf = take(nblk * D * D * 4);
         l.gpre = take(nblk * 4);
+        l.grp = take((size_t)d->N * d->H * pa::suffix_groups((int)nb) * 2 * D * D * 4);
     }
     l.total = off;
     return l;
@@ -179,6 +180,7 @@ static path_status fwd_impl(const path_fwd_desc* desc, const void* q, const void
         a.ws.e32 = reinterpret_cast<float*>(base + lay.e32);
         a.ws.suf = reinterpret_cast<float*>(base + lay.suf);
         a.ws.gpre = reinterpret_cast<float*>(base + lay.gpre);
+        a.ws.grp = reinterpret_cast<float*>(base + lay.grp);
     }
     a.ev = ev;
     if (ev) hipEventRecord(ev[0], stream);

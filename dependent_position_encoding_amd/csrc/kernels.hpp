@@ -24,6 +24,7 @@ struct FwdWs {
     float* e32;   // E in float32 [blk][d][d]
     float* suf;   // suffix transitions S_c [blk][d][d]
     float* gpre;  // log f sum of all blocks before c [blk]
+    float* grp;   // per group of blocks: whole transition and suffix [slice][g][2][d][d]
 };
 
 struct FwdArgs {
@@ -52,6 +53,7 @@ bool fwd_bf16_supported(int d, int block);
 
 // prefill -> decode alignment (uses ws.k32 / ws.e32 written by the forward)
 hipError_t launch_kv_align(const FwdArgs& a, const CacheArgs& c, hipStream_t st);
+int suffix_groups(int nb);   // number of block groups the alignment chain uses
 
 hipError_t launch_kv_update(const CacheArgs& c, int n, const void* w_t,
                             const float* beta_t, hipStream_t st);

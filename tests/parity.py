@@ -34,3 +34,28 @@ def check(name, got, ref, bf16: bool):
     print(msg, flush=True)
     assert ok, msg
     return ma, mr
+
+
+def cache_bar(k_dtype, rewrites: int):
+    """Bar for the rewritten key cache, derived from its arithmetic (no stated
+    tolerance applies to this internal state).  Every rewrite stores the key
+    rounded to k_dtype, relative error <= u (u = 2^-9 for bf16, 2^-24 for
+    fp32), and independent roundings add up like a random walk over the
+    rewrites a key has seen; the prefill alignment contributes one more
+    rounding of a product computed in fp32 (for fp32 caches u is taken as
+    64 ulp to cover that product's accumulation).  Bars:
+    mean-rel <= 2u (1 + sqrt(r)), max-abs <= 8u (1 + sqrt(r)) max|ref|."""
+    import torch
+    u = 2.0 ** -9 if k_dtype == torch.bfloat16 else 2.0 ** -24 * 64
+    walk = 1 + rewrites ** 0.5
+    return 2 * u * walk, 8 * u * walk
+
+
+def check_cache(name, got, ref, k_dtype, rewrites):
+    mr_bar, ma_rel = cache_bar(k_dtype, rewrites)
+    ma_bar = ma_rel * float(np.abs(ref).max())
+    ma, mr = errors(got, ref)
+    msg = f"{name}: max-abs {ma:.3e} mean-rel {mr:.3e} (max-abs<={ma_bar}, mean-rel<={mr_bar:.3e})"
+    print(msg, flush=True)
+    assert ma <= ma_bar and mr <= mr_bar, msg
+    return ma, mr

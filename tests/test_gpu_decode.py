@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import workloads
-from tests.parity import check
+from tests.parity import check, check_cache
 
 pytestmark = pytest.mark.gpu
 
@@ -71,10 +71,7 @@ def test_decode_small(dtype, k_dtype, fused):
     bf = dtype == torch.bfloat16
     check("decode o", go, ro, bf16=bf)
     check("decode lse", gl, rl, bf16=bf)
-    if k_dtype == torch.float32:
-        np.testing.assert_allclose(kc, rk, atol=5e-5 if not bf else 2e-4)
-    else:
-        check("decode kcache", kc, rk, bf16=True)
+    check_cache("decode kcache", kc, rk, k_dtype, 12)
 
 
 def test_decode_no_gate_and_ragged_prompt():
@@ -121,3 +118,61 @@ def test_cache_capacity_errors():
     with pytest.raises(pa.PathAttnError) as e:
         pa.decode(cache, 5, z)
     assert e.value.status == 7
+
+
+def _long_case(wl, k_dtype, head_stride=1, steps=None, check_heads=None):
+    """Full-size long-context case in the launch configuration the benchmark
+    times: prefill with cache alignment, then fused decode steps.  Inputs are
+    drawn on the GPU (seeded); the oracle gets the sampled heads' values."""
+    pa = _pa()
+    steps = wl.decode_steps if steps is None else steps
+    L = wl.L
+    x = workloads.make_inputs(wl, device=DEV, L=L + steps)
+    N, H, d = wl.N, wl.H, wl.d
+    print(f"case {wl.name} full L={L} steps={steps} k_dtype={k_dtype}", flush=True)
+    cache = pa.Cache(N, H, L + steps, d, dtype=wl.dtype, k_dtype=k_dtype, gate=True, device=DEV)
+    pre = lambda n: x[n][:, :, :L].contiguous()
+    o, lse = pa.fwd(pre("q"), pre("k"), pre("v"), pre("w"), pre("beta"), logf=pre("logf"),
+                    scale=wl.scale, cache=cache)
+    tok = lambda n, t: x[n][:, :, t].contiguous()
+    outs, lses = [], []
+    for t in range(L, L + steps):
+        ot, lt = pa.decode_step(cache, t, tok("q", t), tok("k", t), tok("v", t), tok("w", t),
+                                tok("beta", t), tok("logf", t), scale=wl.scale)
+        outs.append(ot.clone())
+        lses.append(lt.clone())
+    torch.cuda.synchronize()
+    heads = list(range(0, N * H, head_stride)) if check_heads is None else check_heads
+    f64 = {k: workloads.as_slices_f64(v, heads) for k, v in x.items()}
+    go = np.stack([workloads.as_slices_f64(o_, heads) for o_ in outs], axis=1)
+    gl = np.stack([workloads.as_slices_f64(l_, heads) for l_ in lses], axis=1)
+    ro, rl = oracle.fwd_rows(f64["q"], f64["k"], f64["v"], f64["w"], f64["beta"], f64["logf"],
+                             wl.scale, rows=np.arange(L, L + steps))
+    check(f"{wl.name} decode o", go, ro, bf16=True)
+    check(f"{wl.name} decode lse", gl, rl, bf16=True)
+    # prefill rows of 4 heads, including the first and last rows of blocks
+    rows = np.unique(np.concatenate([[0, 63, 64, 4095, L - 64, L - 1],
+                                     np.random.default_rng(5).integers(0, L, 40)]))
+    ph = heads[:4]
+    f4 = {k: workloads.as_slices_f64(v, ph) for k, v in x.items()}
+    po, pl = oracle.fwd_rows(f4["q"], f4["k"], f4["v"], f4["w"], f4["beta"], f4["logf"],
+                             wl.scale, rows=rows)
+    check(f"{wl.name} prefill o", workloads.as_slices_f64(o, ph)[:, rows], po, bf16=True)
+    check(f"{wl.name} prefill lse", workloads.as_slices_f64(lse, ph)[:, rows], pl, bf16=True)
+    # the final cache: sampled slots of 2 heads against explicitly transported keys
+    kh = heads[:2]
+    fk = {k: workloads.as_slices_f64(v, kh) for k, v in x.items()}
+    rk = oracle.transported_keys(fk["k"], fk["w"], fk["beta"], L + steps - 1)
+    slots = np.unique(np.concatenate([[0, 1, L - 1, L, L + steps - 1],
+                                      np.random.default_rng(6).integers(0, L + steps, 250)]))
+    check_cache(f"{wl.name} kcache", workloads.as_slices_f64(cache.kcache, kh)[:, slots],
+                rk[:, slots], k_dtype, steps)
+
+
+def test_long_context_full_size():
+    _long_case(workloads.CONFIGS["long"], torch.bfloat16)
+
+
+@pytest.mark.parametrize("k_dtype", [torch.bfloat16, torch.float32])
+def test_long_context_stress_full_size(k_dtype):
+    _long_case(workloads.stress(workloads.CONFIGS["long"]), k_dtype, head_stride=4)

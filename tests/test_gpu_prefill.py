@@ -126,3 +126,21 @@ def test_bf16_ragged_and_stress():
     go, gl, ro, rl = _run(wl)
     check("bf16 ragged stress o", go, ro, bf16=True)
     check("bf16 ragged stress lse", gl, rl, bf16=True)
+
+
+@pytest.mark.parametrize("L", [4096, 8192])
+def test_fox_bf16_full_size_sampled(L):
+    """The benchmark's FoX shapes (32 x 32 heads) with inputs drawn on the GPU."""
+    pa = _pa()
+    wl = workloads.CONFIGS["fox"].replace(L=L)
+    x = workloads.make_inputs(wl, device=DEV)
+    print(f"case fox full L={L}", flush=True)
+    o, lse = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], logf=x["logf"], scale=wl.scale)
+    torch.cuda.synchronize()
+    heads = list(range(7, wl.N * wl.H, 128))
+    rows = _sample_rows(L, 32, L)
+    f64 = {k: workloads.as_slices_f64(v, heads) for k, v in x.items()}
+    ro, rl = oracle.fwd_rows(f64["q"], f64["k"], f64["v"], f64["w"], f64["beta"], f64["logf"],
+                             wl.scale, rows=rows)
+    check(f"fox full L={L} o", workloads.as_slices_f64(o, heads)[:, rows], ro, bf16=True)
+    check(f"fox full L={L} lse", workloads.as_slices_f64(lse, heads)[:, rows], rl, bf16=True)
