@@ -12,10 +12,15 @@
 //       Dg = lower(Q K^T) - P M  (in-block logits),
 //     on bf16 MFMA with fp32 accumulation; fp32 intermediates are split into
 //     bf16 hi + lo parts so these products keep close to fp32 accuracy.
-//   scan (one 128-thread workgroup = 2 waves per 64-query block, heaviest
-//     blocks first): the diagonal block from Dg, then for c = b-1 .. 0 the
-//     right-to-left scan of [Notes s2.7] with an online softmax.  Everything
-//     is kept transposed so that no operand needs a register transpose:
+//   scan (one 256-thread workgroup = 4 waves per pair of 64-query blocks,
+//     heaviest pairs first): the diagonal block from Dg, then for c = b-1 .. 0
+//     the right-to-left scan of [Notes s2.7] with an online softmax.  Each key
+//     block's operands (Kright pre-scaled by scale*log2(e), V^T, -E, the gate
+//     cumsum) are written by precond as one contiguous "tile image" that is
+//     byte-for-byte the LDS layout the scan reads (16-byte units swizzled
+//     against bank conflicts), so the scan streams it with direct
+//     global->LDS loads, double-buffered.  Everything is kept transposed so
+//     that no operand needs a register transpose:
 //       S^T     = Kright_c . Qwork^T           (keys x queries)
 //       O^T    += V_c^T . P^T                  (d x queries)
 //       Qwork^T += (-E_c) . Qwork^T            (d x queries, fp32 state)
@@ -34,6 +39,31 @@ constexpr int kB = 64;       // block size
 constexpr int kSB = 72;      // LDS row stride of bf16 tiles with 64 columns
 constexpr int kSF = 68;      // LDS row stride of float tiles with 64 columns
 
+// Tile image of one key block (bytes), identical in HBM and in LDS:
+//   [Kright: 64 rows (keys) x D bf16][V^T: D rows x 64 bf16]
+//   [-E: D rows (d_out) x D bf16 (d_in)][gate cumsum: 64 float]
+// Within a 16-column group every bf16 row stores its columns in MFMA operand
+// order (swap23).  A row's 16-byte units are XOR-swizzled by row so that the
+// 32 rows one operand read touches fall on distinct LDS banks.
+template <int D>
+struct Img {
+    static constexpr int RB_K = 2 * D, RB_V = 2 * kB, RB_E = 2 * D;
+    static constexpr int OFF_K = 0;
+    static constexpr int OFF_V = OFF_K + kB * RB_K;
+    static constexpr int OFF_E = OFF_V + D * RB_V;
+    static constexpr int OFF_G = OFF_E + D * RB_E;
+    static constexpr int BYTES = OFF_G + kB * 4;
+};
+
+// Position of 16-byte unit u of row r in a tile with rb-byte rows.
+__host__ __device__ constexpr int swz_unit(int r, int u, int rb) {
+    return u ^ ((r / (256 / rb > 1 ? 256 / rb : 1)) % (rb / 16));
+}
+// Byte offset of bf16 column e of row r.
+__host__ __device__ constexpr int img_off(int r, int e, int rb) {
+    return r * rb + swz_unit(r, e >> 3, rb) * 16 + (e & 7) * 2;
+}
+
 // Writes a C tile through f(row, col, value).
 template <typename F>
 __device__ inline void for_tile(const f32x16& acc, int m0, int n0, int lane, F f) {
@@ -47,8 +77,9 @@ __global__ void __launch_bounds__(256)
 precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                     const __bf16* __restrict__ v, const __bf16* __restrict__ w,
                     const float* __restrict__ beta, const float* __restrict__ logf,
-                    int L, int nb, FwdWs ws) {
+                    int L, int nb, float kscale, FwdWs ws) {
     constexpr int B = kB, SB = kSB, SF = kSF, UPR = D / 8;
+    using I = Img<D>;
     __shared__ __attribute__((aligned(16))) __bf16 sW[B * SB], sWt[D * SB], sQ[B * SB], sK[B * SB];
     __shared__ __attribute__((aligned(16))) float sU[B * SF], sUt[B * SF], sX[B * SF], sP[B * SF],
         sMt[B * SF];
@@ -58,6 +89,7 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const size_t base = (size_t)slice * L;
     const int row0 = c * B;
+    char* img = static_cast<char*>(ws.img) + (size_t)blk * I::BYTES;
 
     // ---- 1. stage W, Q, K (and W^T) as bf16, V as float; zero U ----------
     for (int u = tid; u < B * UPR; u += 256) {
@@ -93,20 +125,18 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             if (lane >= off) acc += up;
         }
         ws.gl[(size_t)blk * B + lane] = acc;
+        reinterpret_cast<float*>(img + I::OFF_G)[lane] = acc;
         if (lane == 63) ws.tot[blk] = acc;
     }
     __syncthreads();
 
     // ---- 2. V^T with keys in operand order; G = diag(beta) strictLower(WW^T)
-    {
-        __bf16* vt = static_cast<__bf16*>(ws.vt) + (size_t)blk * D * B;
-        for (int u = tid; u < D * 8; u += 256) {
-            const int x = u / 8, s0 = (u % 8) * 8;
-            bf16x8 pk;
+    for (int u = tid; u < D * 8; u += 256) {
+        const int x = u / 8, s0 = (u % 8) * 8;
+        bf16x8 pk;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pk[e] = (__bf16)sP[swap23(s0 + e) * SF + x];
-            *reinterpret_cast<bf16x8*>(vt + x * B + s0) = pk;
-        }
+        for (int e = 0; e < 8; ++e) pk[e] = (__bf16)sP[swap23(s0 + e) * SF + x];
+        *reinterpret_cast<bf16x8*>(img + I::OFF_V + img_off(x, s0, I::RB_V)) = pk;
     }
     if (wave < 3) {
         const int mt = wave == 0 ? 0 : 1, nt = wave == 2 ? 1 : 0;
@@ -241,11 +271,13 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const int mt = job / (D / 32), nt = job % (D / 32);
         f32x16 acc = zero16();
         tile_mm<B>(acc, sX, SF, sWt, SB, 32 * mt, 32 * nt, lane);
-        __bf16* kr = static_cast<__bf16*>(ws.kr) + (size_t)blk * B * D;
+        // staged in image layout in the (now free) P buffer, copied out below
+        char* stage = reinterpret_cast<char*>(sP);
         float* k32 = ws.k32 ? ws.k32 + (size_t)blk * B * D : nullptr;
         for_tile(acc, 32 * mt, 32 * nt, lane, [&](int j, int x, float a) {
             const float val = (float)sK[j * SB + x] - a;
-            kr[j * D + swap23(x)] = (__bf16)val;
+            *reinterpret_cast<__bf16*>(stage + I::OFF_K + img_off(j, swap23(x), I::RB_K)) =
+                (__bf16)(val * kscale);
             if (k32) k32[j * D + x] = val;
         });
     }
@@ -265,77 +297,74 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const int mt = job / (D / 32), nt = job % (D / 32);
         f32x16 acc = zero16();
         tile_mm<B>(acc, sWt, SB, sX, SF, 32 * mt, 32 * nt, lane);
-        __bf16* em = static_cast<__bf16*>(ws.em) + (size_t)blk * D * D;
+        char* stage = reinterpret_cast<char*>(sP) + (I::OFF_E - I::OFF_V);
         float* e32 = ws.e32 ? ws.e32 + (size_t)blk * D * D : nullptr;
         for_tile(acc, 32 * mt, 32 * nt, lane, [&](int x, int y, float a) {
-            em[x * D + swap23(y)] = (__bf16)(-a);
+            *reinterpret_cast<__bf16*>(stage + img_off(x, swap23(y), I::RB_E)) = (__bf16)(-a);
             if (e32) e32[x * D + y] = a;
         });
+    }
+    __syncthreads();
+    // Kright and -E images: LDS staging -> HBM with 16-byte stores
+    {
+        const char* stage = reinterpret_cast<const char*>(sP);
+        constexpr int KUN = (I::OFF_V - I::OFF_K) / 16, EUN = (I::OFF_G - I::OFF_E) / 16;
+        static_assert((I::OFF_V - I::OFF_K) + (I::OFF_G - I::OFF_E) <= kB * kSF * 4, "staging");
+        for (int u = tid; u < KUN + EUN; u += 256) {
+            const int src = u < KUN ? u * 16 : (I::OFF_V - I::OFF_K) + (u - KUN) * 16;
+            const int dst = u < KUN ? I::OFF_K + u * 16 : I::OFF_E + (u - KUN) * 16;
+            *reinterpret_cast<u32x4*>(img + dst) = *reinterpret_cast<const u32x4*>(stage + src);
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
+// Direct HBM -> LDS copy of one tile image (16 bytes per lane, the lanes of a
+// wave fill 1 KB of LDS contiguously).  The caller waits on vmcnt and
+// synchronises before reading.
+template <int BYTES>
+__device__ inline void load_image(const char* __restrict__ src, char* dst, int tid) {
+    constexpr int UNITS = BYTES / 16;
+    const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+    for (int it = 0; it < (UNITS + 255) / 256; ++it) {
+        const int u0 = (it * 4 + wave) * 64;
+        if (u0 < UNITS && u0 + lane < UNITS)
+            __builtin_amdgcn_global_load_lds(
+                src + (size_t)(u0 + lane) * 16,
+                (__attribute__((address_space(3))) void*)(dst + u0 * 16), 16, 0, 0);
+    }
+}
+
+__device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <int D, bool FOX>
-__global__ void __launch_bounds__(128)
+__global__ void __launch_bounds__(256)
 scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
                  float* __restrict__ lse) {
-    constexpr int B = kB, SK = D + 8, SV = B + 8, SE = D + 8, NT = D / 32, NKC = D / 16;
-    constexpr int KU = D / 16;                    // 16-byte units per thread: Kright, V^T
-    constexpr int EU = (D * D / 8 + 127) / 128;   // and -E
-    constexpr bool E_FULL = (D * D / 8) % 128 == 0;
-    __shared__ __attribute__((aligned(16))) __bf16 sK[B * SK], sV[D * SV], sE[D * SE];
-    __shared__ __attribute__((aligned(16))) float sG[B];
+    using I = Img<D>;
+    constexpr int B = kB, NT = D / 32, NKC = D / 16;
+    constexpr float kTau = 8.f;   // lazy rescale: keep a stale max while within 2^8
+    __shared__ __attribute__((aligned(16))) char sImg[2][I::BYTES];
 
-    const int NH = gridDim.x / nb;
-    const int b = nb - 1 - (int)(blockIdx.x / NH);
+    const int NH = gridDim.x / ((nb + 1) / 2);
+    const int pair = (int)(blockIdx.x / NH);
     const int slice = blockIdx.x % NH;
+    const int bA = nb - 1 - 2 * pair, bB = bA - 1;          // bB may be -1
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
-    const int col = lane & 31, qloc = 32 * wave + col;
+    const int col = lane & 31;
+    const int myb = wave < 2 ? bA : bB;
+    const int qloc = 32 * (wave & 1) + col;
     const size_t blk0 = (size_t)slice * nb;
-    const __bf16* kr = static_cast<const __bf16*>(ws.kr);
-    const __bf16* vt = static_cast<const __bf16*>(ws.vt);
-    const __bf16* em = static_cast<const __bf16*>(ws.em);
+    const char* img = static_cast<const char*>(ws.img);
 
-    // next block's tiles, in flight in registers while the current one is used
-    u32x4 rk[KU], rv[KU], re[EU];
-    f32x4 rg = {0.f, 0.f, 0.f, 0.f};
-    float rtot = 0.f;
-#define PA_LOAD_TILES(c_)                                                              \
-    do {                                                                               \
-        const size_t bc = blk0 + (c_);                                                 \
-        _Pragma("unroll") for (int u = 0; u < KU; ++u) {                              \
-            const int idx = tid + 128 * u;                                             \
-            rk[u] = *reinterpret_cast<const u32x4*>(kr + bc * B * D + (size_t)idx * 8); \
-            rv[u] = *reinterpret_cast<const u32x4*>(vt + bc * D * B + (size_t)idx * 8); \
-        }                                                                              \
-        _Pragma("unroll") for (int u = 0; u < EU; ++u) {                              \
-            const int idx = tid + 128 * u;                                             \
-            if (E_FULL || idx < D * D / 8)                                             \
-                re[u] = *reinterpret_cast<const u32x4*>(em + bc * D * D + (size_t)idx * 8); \
-        }                                                                              \
-        if (FOX) {                                                                     \
-            rg = *reinterpret_cast<const f32x4*>(ws.gl + bc * B + 4 * (tid & 15));    \
-            rtot = ws.tot[bc];                                                         \
-        }                                                                              \
-    } while (0)
-#define PA_STORE_TILES()                                                               \
-    do {                                                                               \
-        _Pragma("unroll") for (int u = 0; u < KU; ++u) {                              \
-            const int idx = tid + 128 * u;                                             \
-            *reinterpret_cast<u32x4*>(sK + (idx / (D / 8)) * SK + (idx % (D / 8)) * 8) = rk[u]; \
-            *reinterpret_cast<u32x4*>(sV + (idx / 8) * SV + (idx % 8) * 8) = rv[u];    \
-        }                                                                              \
-        _Pragma("unroll") for (int u = 0; u < EU; ++u) {                              \
-            const int idx = tid + 128 * u;                                             \
-            if (E_FULL || idx < D * D / 8)                                             \
-                *reinterpret_cast<u32x4*>(sE + (idx / (D / 8)) * SE + (idx % (D / 8)) * 8) = re[u]; \
-        }                                                                              \
-        if (FOX && tid < 16) *reinterpret_cast<f32x4*>(sG + 4 * tid) = rg;           \
-    } while (0)
+    load_image<I::BYTES>(img + (blk0 + bA) * I::BYTES, sImg[0], tid);
+    if (bB >= 0) load_image<I::BYTES>(img + (blk0 + bB) * I::BYTES, sImg[1], tid);
 
     f32x16 Qw[NT], Ot[NT], S[2];
-    const size_t bq = blk0 + b;
-    {
+    float m = 0.f, l = 0.f, gq = 0.f, grun = 0.f;
+    if (myb >= 0) {
+        const size_t bq = blk0 + myb;
         const float* qlp = ws.ql + (bq * B + qloc) * D;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -347,57 +376,33 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
                 for (int j = 0; j < 4; ++j) Qw[t][4 * i + j] = v4[j];
             }
         }
+        if (FOX) gq = ws.gl[bq * B + qloc] * kLog2e;
     }
-    const float gq = FOX ? ws.gl[bq * B + qloc] * kLog2e : 0.f;
 
-    PA_LOAD_TILES(b);
-    PA_STORE_TILES();
-    __syncthreads();
-
-    float m, l;
-    auto softmax_pv = [&](bool first) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mn = first ? mx : fmaxf(m, mx);
-        const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-        float rs = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(S[mt][r] - mn);
-                S[mt][r] = p;
-                rs += p;
-            }
-        rs += __shfl_xor(rs, 32, 64);
-        l = first ? rs : l * alpha + rs;
-        m = mn;
+    // P.V for the current S (already exponentiated), from the V^T image
+    auto pv = [&](const char* im) {
         bf16x8 Pb[4];
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
             for (int e = 0; e < 8; ++e) Pb[kc][e] = (__bf16)S[kc >> 1][8 * (kc & 1) + e];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            if (!first) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) Ot[t][r] *= alpha;
-            }
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(sV + (32 * t + col) * SV + 16 * kc + 8 * h);
+                const int row = 32 * t + col;
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    im + I::OFF_V + row * I::RB_V + swz_unit(row, 2 * kc + h, I::RB_V) * 16);
                 Ot[t] = mfma32(a, Pb[kc], Ot[t]);
             }
-        }
     };
 
-    // diagonal block: in-block logits, causal mask
-    {
+    // diagonal block of query block myb (image in buf), causal mask
+    auto diag = [&](const char* im) {
+        const size_t bq = blk0 + myb;
         const float* dgp = ws.dg + (bq * B + qloc) * B;
+        const float* gimg = reinterpret_cast<const float*>(im + I::OFF_G);
+        float mx = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -405,65 +410,135 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
                 const int k0 = 32 * mt + 8 * i + 4 * h;
                 const f32x4 d4 = *reinterpret_cast<const f32x4*>(dgp + k0);
                 f32x4 g4 = {0.f, 0.f, 0.f, 0.f};
-                if (FOX) g4 = *reinterpret_cast<const f32x4*>(sG + k0);
+                if (FOX) g4 = *reinterpret_cast<const f32x4*>(gimg + k0);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    S[mt][4 * i + j] = (k0 + j <= qloc)
-                                           ? d4[j] * scale2 + (FOX ? gq - g4[j] * kLog2e : 0.f)
-                                           : -INFINITY;
+                for (int j = 0; j < 4; ++j) {
+                    const float sv = (k0 + j <= qloc)
+                                         ? d4[j] * scale2 + (FOX ? gq - g4[j] * kLog2e : 0.f)
+                                         : -INFINITY;
+                    S[mt][4 * i + j] = sv;
+                    mx = fmaxf(mx, sv);
+                }
             }
-        softmax_pv(true);
-    }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        m = mx;
+        float rs = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(S[mt][r] - m);
+                S[mt][r] = p;
+                rs += p;
+            }
+        l = rs + __shfl_xor(rs, 32, 64);
+        pv(im);
+    };
 
-    float grun = 0.f;
-    if (b > 0) PA_LOAD_TILES(b - 1);
-    for (int c = b - 1; c >= 0; --c) {
-        __syncthreads();
-        PA_STORE_TILES();
-        __syncthreads();
-        if (FOX) grun += rtot;
-        if (c > 0) PA_LOAD_TILES(c - 1);
-
+    // one scan step against key block c (image in buf)
+    auto step = [&](const char* im, int c) {
+        if (FOX) grun += ws.tot[blk0 + c];
+        const float rowb = gq + grun * kLog2e;
         bf16x8 Qb[NKC];
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
             for (int e = 0; e < 8; ++e) Qb[kc][e] = (__bf16)Qw[kc >> 1][8 * (kc & 1) + e];
+        // S^T = Kright_c . Qwork^T (already in log2 units), plus the gate's
+        // per-key term -gl_c * log2(e) as one more contraction group (hi + lo)
+        const float* gimg = reinterpret_cast<const float*>(im + I::OFF_G);
+        bf16x8 ones;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ones[e] = (__bf16)((h == 0 && e < 2) ? 1.f : 0.f);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             S[mt] = zero16();
+            const int row = 32 * mt + col;
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + (32 * mt + col) * SK + 16 * kc + 8 * h);
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    im + I::OFF_K + row * I::RB_K + swz_unit(row, 2 * kc + h, I::RB_K) * 16);
                 S[mt] = mfma32(a, Qb[kc], S[mt]);
             }
+            if (FOX) {
+                const float gb = -gimg[row] * kLog2e;
+                const __bf16 hi = (__bf16)gb;
+                const __bf16 lo = (__bf16)(gb - (float)hi);
+                bf16x8 a;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[e] = (__bf16)0.f;
+                if (h == 0) { a[0] = hi; a[1] = lo; }
+                S[mt] = mfma32(a, ones, S[mt]);
+            }
         }
-        const float rowb = gq + grun * kLog2e;
+        // online softmax with a lazily updated reference max
+        float mx = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                f32x4 g4 = {0.f, 0.f, 0.f, 0.f};
-                if (FOX) g4 = *reinterpret_cast<const f32x4*>(sG + 32 * mt + 8 * i + 4 * h);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    S[mt][4 * i + j] = FOX ? S[mt][4 * i + j] * scale2 + (rowb - g4[j] * kLog2e)
-                                           : S[mt][4 * i + j] * scale2;
-            }
-        softmax_pv(false);
-        if (c > 0) {
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) + rowb;
+        if (__any(mx > m + kTau)) {
+            const float mn = fmaxf(m, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m - mn);
+            l *= alpha;
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
+                for (int r = 0; r < 16; ++r) Ot[t][r] *= alpha;
+            m = mn;
+        }
+        const float mref = m - rowb;
+        float rs = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(S[mt][r] - mref);
+                S[mt][r] = p;
+                rs += p;
+            }
+        l += rs + __shfl_xor(rs, 32, 64);
+        pv(im);
+        // Qwork^T += (-E_c) Qwork^T: carry the queries across block c
+        if (c > 0) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int row = 32 * t + col;
+#pragma unroll
                 for (int kc = 0; kc < NKC; ++kc) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(sE + (32 * t + col) * SE + 16 * kc + 8 * h);
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                        im + I::OFF_E + row * I::RB_E + swz_unit(row, 2 * kc + h, I::RB_E) * 16);
                     Qw[t] = mfma32(a, Qb[kc], Qw[t]);
                 }
+            }
+        }
+    };
+
+    wait_loads();
+    __syncthreads();
+    // phase 1: diagonal of the upper block (waves 0-1)
+    if (wave < 2) diag(sImg[0]);
+    __syncthreads();
+    if (bB >= 0) {
+        if (bB > 0) load_image<I::BYTES>(img + (blk0 + bB - 1) * I::BYTES, sImg[0], tid);
+        // phase 2: key block bB -- a scan step for the upper block, the
+        // diagonal for the lower one
+        if (wave < 2) step(sImg[1], bB);
+        else diag(sImg[1]);
+        wait_loads();
+        __syncthreads();
+        for (int c = bB - 1; c >= 0; --c) {
+            const int buf = (bA - c) & 1;
+            if (c > 0) load_image<I::BYTES>(img + (blk0 + c - 1) * I::BYTES, sImg[buf ^ 1], tid);
+            step(sImg[buf], c);
+            wait_loads();
+            __syncthreads();
         }
     }
 
-    const int pos = b * B + qloc;
-    if (pos < L) {
+    const int pos = myb * B + qloc;
+    if (myb >= 0 && pos < L) {
         const float inv = 1.f / l;
         __bf16* op = o + ((size_t)slice * L + pos) * D;
 #pragma unroll
@@ -478,26 +553,25 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
             }
         if (lse && h == 0) lse[(size_t)slice * L + pos] = (m + __log2f(l)) * kLn2;
     }
-#undef PA_LOAD_TILES
-#undef PA_STORE_TILES
 }
 
 template <int D>
 hipError_t launch_t(const FwdArgs& a, hipStream_t st) {
     const int nb = (a.L + kB - 1) / kB;
     const int nblk = a.N * a.H * nb;
+    const float scale2 = a.scale * kLog2e;
     hipLaunchKernelGGL((precond_mfma_kernel<D>), dim3(nblk), dim3(256), 0, st,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                       (const __bf16*)a.w, a.beta, a.logf, a.L, nb, a.ws);
+                       (const __bf16*)a.w, a.beta, a.logf, a.L, nb, scale2, a.ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev) hipEventRecord(a.ev[1], st);
-    const float scale2 = a.scale * kLog2e;
+    const int ngrid = a.N * a.H * ((nb + 1) / 2);
     if (a.logf)
-        hipLaunchKernelGGL((scan_mfma_kernel<D, true>), dim3(nblk), dim3(128), 0, st, a.L, nb,
+        hipLaunchKernelGGL((scan_mfma_kernel<D, true>), dim3(ngrid), dim3(256), 0, st, a.L, nb,
                            scale2, a.ws, (__bf16*)a.o, a.lse);
     else
-        hipLaunchKernelGGL((scan_mfma_kernel<D, false>), dim3(nblk), dim3(128), 0, st, a.L, nb,
+        hipLaunchKernelGGL((scan_mfma_kernel<D, false>), dim3(ngrid), dim3(256), 0, st, a.L, nb,
                            scale2, a.ws, (__bf16*)a.o, a.lse);
     return hipGetLastError();
 }
@@ -505,6 +579,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t st) {
 }  // namespace
 
 bool fwd_bf16_supported(int d, int block) { return (d == 32 || d == 64) && block == 64; }
+
+size_t fwd_bf16_image_bytes(int d) { return d == 32 ? Img<32>::BYTES : Img<64>::BYTES; }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
     switch (a.d) {

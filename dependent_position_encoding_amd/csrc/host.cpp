@@ -57,7 +57,7 @@ path_status check_desc(const path_fwd_desc* d, bool need_L) {
 }
 
 struct Layout {
-    size_t kr, vt, em, ql, dg, gl, tot, k32, e32, suf, gpre, grp, total;
+    size_t kr, em, img, ql, dg, gl, tot, k32, e32, suf, gpre, grp, total;
 };
 
 Layout fwd_layout(const path_fwd_desc* d, bool with_cache) {
@@ -69,9 +69,12 @@ Layout fwd_layout(const path_fwd_desc* d, bool with_cache) {
     Layout l{};
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
-    l.kr = take(nblk * B * D * op);
-    l.vt = mf ? take(nblk * B * D * 2) : 0;
-    l.em = take(nblk * D * D * op);
+    if (mf) {
+        l.img = take(nblk * pa::fwd_bf16_image_bytes(D));
+    } else {
+        l.kr = take(nblk * B * D * op);
+        l.em = take(nblk * D * D * op);
+    }
     l.ql = take(nblk * B * D * 4);
     l.dg = take(nblk * B * B * 4);
     l.gl = take(nblk * B * 4);
@@ -168,9 +171,10 @@ static path_status fwd_impl(const path_fwd_desc* desc, const void* q, const void
     a.N = desc->N; a.H = desc->H; a.L = desc->L; a.d = desc->d; a.block = block_of(desc);
     a.bf16 = desc->dtype == PATH_BF16; a.scale = desc->scale;
     a.q = q; a.k = k; a.v = v; a.w = w; a.beta = beta; a.logf = logf; a.o = o; a.lse = lse;
-    a.ws.kr = base + lay.kr;
-    a.ws.vt = lay.vt ? base + lay.vt : nullptr;
-    a.ws.em = base + lay.em;
+    const bool mf = use_mfma(desc);
+    a.ws.kr = mf ? nullptr : base + lay.kr;
+    a.ws.em = mf ? nullptr : base + lay.em;
+    a.ws.img = mf ? base + lay.img : nullptr;
     a.ws.ql = reinterpret_cast<float*>(base + lay.ql);
     a.ws.dg = reinterpret_cast<float*>(base + lay.dg);
     a.ws.gl = reinterpret_cast<float*>(base + lay.gl);

@@ -9,12 +9,10 @@ namespace pa {
 // Per-block products of the preconditioning step, carved from the caller's
 // workspace by the host layer.  "blk" = slice * nb + c with slice = n*H + h.
 struct FwdWs {
-    void* kr;     // keys moved to their block's right edge: [blk][B][d]
-                  //   (f32 path: float, natural order; bf16 path: bf16 in
-                  //    matrix-core operand order)
-    void* vt;     // bf16 path: values transposed per block [blk][d][B]
-    void* em;     // block transition I - E: f32 path E [blk][d][d] float;
-                  //   bf16 path -E as bf16 operand tiles
+    void* kr;     // f32 path: keys moved to their block's right edge [blk][B][d]
+    void* em;     // f32 path: block transition I - E, E as [blk][d][d]
+    void* img;    // bf16 path: per-block tile images (Kright, V^T, -E, gate
+                  //   cumsum) in the scan's LDS layout [blk][image bytes]
     float* ql;    // queries moved to their block's left edge [blk][B][d]
     float* dg;    // in-block logits lower(QK^T) - P M [blk][B][B]
     float* gl;    // in-block inclusive cumsum of log f [blk][B]
@@ -50,6 +48,7 @@ struct CacheArgs {
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
 bool fwd_bf16_supported(int d, int block);
+size_t fwd_bf16_image_bytes(int d);
 
 // prefill -> decode alignment (uses ws.k32 / ws.e32 written by the forward)
 hipError_t launch_kv_align(const FwdArgs& a, const CacheArgs& c, hipStream_t st);
