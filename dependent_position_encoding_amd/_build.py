@@ -22,6 +22,10 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 instructions stay off: the compiler only emits scalar fp32
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs: the softmax and the Qwork
+    # conversion read every accumulator, so AGPR<->VGPR copies would cost more
+    # VALU issue slots than they save registers
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wall", "-Wno-unused-result",
 ]
