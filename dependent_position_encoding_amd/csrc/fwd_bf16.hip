@@ -73,13 +73,17 @@ __device__ inline void for_tile(const f32x16& acc, int m0, int n0, int lane, F f
 }
 
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                     const __bf16* __restrict__ v, const __bf16* __restrict__ w,
                     const float* __restrict__ beta, const float* __restrict__ logf,
                     int L, int nb, float kscale, FwdWs ws) {
-    constexpr int B = kB, SB = kSB, SF = kSF, UPR = D / 8;
+    constexpr int B = kB, SB = kSB, SF = kSF, UPR = D / 8, NTH = 512;
+    constexpr int DT = D / 32;                 // 32-wide tiles along d
     using I = Img<D>;
+    // LDS roles over time (each buffer 64 x 64 float unless noted):
+    //   sX : G -> P -> image staging        sP : V (staging) -> X1 -> R^T
+    //   sMt: M^T -> Y^T                     sU : T -> U       sUt: scratch -> U^T
     __shared__ __attribute__((aligned(16))) __bf16 sW[B * SB], sWt[D * SB], sQ[B * SB], sK[B * SB];
     __shared__ __attribute__((aligned(16))) float sU[B * SF], sUt[B * SF], sX[B * SF], sP[B * SF],
         sMt[B * SF];
@@ -91,8 +95,8 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int row0 = c * B;
     char* img = static_cast<char*>(ws.img) + (size_t)blk * I::BYTES;
 
-    // ---- 1. stage W, Q, K (and W^T) as bf16, V as float; zero U ----------
-    for (int u = tid; u < B * UPR; u += 256) {
+    // ---- 1. stage W, Q, K (and W^T) as bf16, V as float; zero T ----------
+    for (int u = tid; u < B * UPR; u += NTH) {
         const int r = u / UPR, x0 = (u % UPR) * 8, pos = row0 + r;
         bf16x8 wv, qv, kv, vv;
         if (pos < L) {
@@ -114,9 +118,9 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             sP[r * SF + x0 + e] = (float)vv[e];
         }
     }
-    for (int e = tid; e < B * B; e += 256) sU[(e / B) * SF + e % B] = 0.f;
+    for (int e = tid; e < B * B; e += NTH) sU[(e / B) * SF + e % B] = 0.f;
     if (tid < B) sBeta[tid] = row0 + tid < L ? beta[base + row0 + tid] : 0.f;
-    if (wave == 0) {
+    if (wave == 7) {
         // in-block inclusive prefix sum of log f (one lane per token)
         float acc = (logf && row0 + lane < L) ? logf[base + row0 + lane] : 0.f;
 #pragma unroll
@@ -131,7 +135,7 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     __syncthreads();
 
     // ---- 2. V^T with keys in operand order; G = diag(beta) strictLower(WW^T)
-    for (int u = tid; u < D * 8; u += 256) {
+    for (int u = tid; u < D * 8; u += NTH) {
         const int x = u / 8, s0 = (u % 8) * 8;
         bf16x8 pk;
 #pragma unroll
@@ -148,19 +152,30 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
     __syncthreads();
 
-    // ---- 3. T = (I + G)^{-1}, blocked over four 16 x 16 diagonal blocks ----
-    // diagonal blocks by forward substitution (wave a, one column per lane)
-    if (lane < 16) {
-        const int o = 16 * wave;
-        float t[16];
+    // ---- 3. T = (I + G)^{-1} on waves 0-3, blocked over 16 x 16 blocks;
+    //         meanwhile waves 4-7 form X1 = lower(Q W^T) -> sP and
+    //         M^T (M = strictLower(W K^T)) -> sMt, which do not need T.
+    if (wave < 4) {
+        // diagonal blocks by forward substitution, one column per lane
+        if (lane < 16) {
+            const int o = 16 * wave;
+            float t[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float s = 0.f;
+            for (int i = 0; i < 16; ++i) {
+                float s = 0.f;
 #pragma unroll
-            for (int kk = 0; kk < i; ++kk) s += sX[(o + i) * SF + o + kk] * t[kk];
-            t[i] = i < lane ? 0.f : (i == lane ? 1.f : -s);
-            sU[(o + i) * SF + o + lane] = t[i];
+                for (int kk = 0; kk < i; ++kk) s += sX[(o + i) * SF + o + kk] * t[kk];
+                t[i] = i < lane ? 0.f : (i == lane ? 1.f : -s);
+                sU[(o + i) * SF + o + lane] = t[i];
+            }
         }
+    } else {
+        const int t = wave - 4, mt = t >> 1, nt = t & 1;
+        f32x16 acc = zero16();
+        if (!(mt == 0 && nt == 1)) tile_mm<D>(acc, sQ, SB, sW, SB, 32 * mt, 32 * nt, lane);
+        for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) {
+            sP[i * SF + j] = j <= i ? a : 0.f;
+        });
     }
     __syncthreads();
     // off-diagonal blocks: T_ab = -T_aa sum_{c=b}^{a-1} G_ac T_cb, by distance
@@ -178,7 +193,15 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 }
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sP[(16 * a + r) * SF + 16 * bb + c0 + e] = x[e];
+            for (int e = 0; e < 4; ++e) sUt[(16 * a + r) * SF + 16 * bb + c0 + e] = x[e];
+        } else if (lev == 1 && wave >= 4) {
+            const int t = wave - 4, mt = t >> 1, nt = t & 1;
+            f32x16 acc = zero16();
+            // M^T[j][b] = k_j . w_b for b > j
+            if (!(mt == 1 && nt == 0)) tile_mm<D>(acc, sK, SB, sW, SB, 32 * mt, 32 * nt, lane);
+            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int j, int bcol, float a) {
+                sMt[j * SF + bcol] = bcol > j ? a : 0.f;
+            });
         }
         __syncthreads();
         if (wave < njobs) {
@@ -188,7 +211,7 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             for (int kk = 0; kk < 16; ++kk) {
                 const float t = sU[(16 * a + r) * SF + 16 * a + kk];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] -= t * sP[(16 * a + kk) * SF + 16 * bb + c0 + e];
+                for (int e = 0; e < 4; ++e) y[e] -= t * sUt[(16 * a + kk) * SF + 16 * bb + c0 + e];
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) sU[(16 * a + r) * SF + 16 * bb + c0 + e] = y[e];
@@ -196,7 +219,7 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         __syncthreads();
     }
     // U = T diag(beta), kept in both orientations
-    for (int e = tid; e < B * B; e += 256) {
+    for (int e = tid; e < B * B; e += NTH) {
         const int i = e / B, j = e % B;
         const float u = sU[i * SF + j] * sBeta[j];
         sU[i * SF + j] = u;
@@ -204,56 +227,33 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
     __syncthreads();
 
-    // ---- 4. X1 = lower(Q W^T) -> sX;  M^T (M = strictLower(W K^T)) -> sMt --
-    for (int job = wave; job < 8; job += 4) {
-        const int t = job & 3, mt = t >> 1, nt = t & 1;
-        f32x16 acc = zero16();
-        if (job < 4) {
-            if (!(mt == 0 && nt == 1)) tile_mm<D>(acc, sQ, SB, sW, SB, 32 * mt, 32 * nt, lane);
-            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) {
-                sX[i * SF + j] = j <= i ? a : 0.f;
-            });
-        } else {
-            // M^T[j][b] = k_j . w_b for b > j
-            if (!(mt == 1 && nt == 0)) tile_mm<D>(acc, sK, SB, sW, SB, 32 * mt, 32 * nt, lane);
-            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int j, int bcol, float a) {
-                sMt[j * SF + bcol] = bcol > j ? a : 0.f;
-            });
-        }
-    }
-    __syncthreads();
-
-    // ---- 5a. P = X1 U -> sP ------------------------------------------------
-    {
+    // ---- 4. P = X1 U -> sX (waves 0-3); Q K^T tiles kept in registers by
+    //         waves 4-6 for the in-block logits
+    f32x16 qk = zero16();
+    if (wave < 4) {
         const int mt = wave >> 1, nt = wave & 1;
         f32x16 acc = zero16();
-        if (!(mt == 0 && nt == 1)) tile_mm<B>(acc, sX, SF, sUt, SF, 32 * mt, 32 * nt, lane);
-        for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) { sP[i * SF + j] = a; });
+        if (!(mt == 0 && nt == 1)) tile_mm<B>(acc, sP, SF, sUt, SF, 32 * mt, 32 * nt, lane);
+        for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) { sX[i * SF + j] = a; });
+    } else if (wave < 7) {
+        const int t = wave - 4, mt = t == 0 ? 0 : 1, nt = t == 2 ? 1 : 0;
+        tile_mm<D>(qk, sQ, SB, sK, SB, 32 * mt, 32 * nt, lane);
     }
     __syncthreads();
 
-    // ---- 5b. R^T = M^T U^T -> sX;  Qleft = Q - P W;  Dg = lower(QK^T) - P M -
+    // ---- 5. R^T = M^T U^T -> sP;  Qleft = Q - P W;  Dg = lower(QK^T) - P M
+    //         jobs: 0-3 R^T tiles, 4-6 Dg tiles (waves holding qk), then Qleft
     {
-        constexpr int NQ = 2 * (D / 32);
-        for (int job = wave; job < 4 + NQ + 3; job += 4) {
+        constexpr int NQ = 2 * DT;
+        for (int job = wave; job < 7 + NQ; job += 8) {
             f32x16 acc = zero16();
             if (job < 4) {
                 const int mt = job >> 1, nt = job & 1;
                 if (!(mt == 1 && nt == 0)) tile_mm<B>(acc, sMt, SF, sU, SF, 32 * mt, 32 * nt, lane);
-                for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) { sX[i * SF + j] = a; });
-            } else if (job < 4 + NQ) {
-                const int t = job - 4, mt = t / (D / 32), nt = t % (D / 32);
-                tile_mm<B>(acc, sP, SF, sWt, SB, 32 * mt, 32 * nt, lane);
-                float* ql = ws.ql + (size_t)blk * B * D;
-                for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int x, float a) {
-                    ql[i * D + x] = (float)sQ[i * SB + x] - a;
-                });
-            } else {
-                const int t = job - 4 - NQ;
-                const int mt = t == 0 ? 0 : 1, nt = t == 2 ? 1 : 0;
-                tile_mm<B>(acc, sP, SF, sMt, SF, 32 * mt, 32 * nt, lane);
-                f32x16 qk = zero16();
-                tile_mm<D>(qk, sQ, SB, sK, SB, 32 * mt, 32 * nt, lane);
+                for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) { sP[i * SF + j] = a; });
+            } else if (job < 7) {
+                const int t = job - 4, mt = t == 0 ? 0 : 1, nt = t == 2 ? 1 : 0;
+                tile_mm<B>(acc, sX, SF, sMt, SF, 32 * mt, 32 * nt, lane);
                 float* dg = ws.dg + (size_t)blk * B * B;
                 const int h = lane >> 5, j = 32 * nt + (lane & 31);
 #pragma unroll
@@ -261,43 +261,48 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                     const int i = 32 * mt + crow(r, h);
                     dg[i * B + j] = j <= i ? qk[r] - acc[r] : 0.f;
                 }
+            } else {
+                const int t = job - 7, mt = t / DT, nt = t % DT;
+                tile_mm<B>(acc, sX, SF, sWt, SB, 32 * mt, 32 * nt, lane);
+                float* ql = ws.ql + (size_t)blk * B * D;
+                for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int x, float a) {
+                    ql[i * D + x] = (float)sQ[i * SB + x] - a;
+                });
             }
         }
     }
     __syncthreads();
 
-    // ---- 6. Kright = K - R^T W (bf16, columns in operand order) -----------
-    for (int job = wave; job < 2 * (D / 32); job += 4) {
-        const int mt = job / (D / 32), nt = job % (D / 32);
-        f32x16 acc = zero16();
-        tile_mm<B>(acc, sX, SF, sWt, SB, 32 * mt, 32 * nt, lane);
-        // staged in image layout in the (now free) P buffer, copied out below
-        char* stage = reinterpret_cast<char*>(sP);
-        float* k32 = ws.k32 ? ws.k32 + (size_t)blk * B * D : nullptr;
-        for_tile(acc, 32 * mt, 32 * nt, lane, [&](int j, int x, float a) {
-            const float val = (float)sK[j * SB + x] - a;
-            *reinterpret_cast<__bf16*>(stage + I::OFF_K + img_off(j, swap23(x), I::RB_K)) =
-                (__bf16)(val * kscale);
-            if (k32) k32[j * D + x] = val;
-        });
+    // ---- 6. Kright = K - R^T W, staged as an image in sX (waves 0..);
+    //         Y^T = W^T U -> sMt (waves 4..)
+    {
+        char* stage = reinterpret_cast<char*>(sX);
+        if (wave < 2 * DT) {
+            const int mt = wave / DT, nt = wave % DT;
+            f32x16 acc = zero16();
+            tile_mm<B>(acc, sP, SF, sWt, SB, 32 * mt, 32 * nt, lane);
+            float* k32 = ws.k32 ? ws.k32 + (size_t)blk * B * D : nullptr;
+            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int j, int x, float a) {
+                const float val = (float)sK[j * SB + x] - a;
+                *reinterpret_cast<__bf16*>(stage + I::OFF_K + img_off(j, swap23(x), I::RB_K)) =
+                    (__bf16)(val * kscale);
+                if (k32) k32[j * D + x] = val;
+            });
+        } else if (wave >= 4 && wave < 4 + 2 * DT) {
+            const int t = wave - 4, mt = t / 2, nt = t % 2;
+            f32x16 acc = zero16();
+            tile_mm<B>(acc, sWt, SB, sUt, SF, 32 * mt, 32 * nt, lane);
+            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int y, int cc, float a) { sMt[y * SF + cc] = a; });
+        }
     }
     __syncthreads();
 
-    // ---- 7. Y^T = W^T U  (Y = U^T W) -> sX --------------------------------
-    for (int job = wave; job < 2 * (D / 32); job += 4) {
-        const int mt = job / 2, nt = job % 2;
+    // ---- 7. E = W^T Y; -E staged with the contracted index in operand order
+    if (wave < DT * DT) {
+        const int mt = wave / DT, nt = wave % DT;
         f32x16 acc = zero16();
-        tile_mm<B>(acc, sWt, SB, sUt, SF, 32 * mt, 32 * nt, lane);
-        for_tile(acc, 32 * mt, 32 * nt, lane, [&](int y, int cc, float a) { sX[y * SF + cc] = a; });
-    }
-    __syncthreads();
-
-    // ---- 8. E = W^T Y; store -E with the contracted index in operand order -
-    for (int job = wave; job < (D / 32) * (D / 32); job += 4) {
-        const int mt = job / (D / 32), nt = job % (D / 32);
-        f32x16 acc = zero16();
-        tile_mm<B>(acc, sWt, SB, sX, SF, 32 * mt, 32 * nt, lane);
-        char* stage = reinterpret_cast<char*>(sP) + (I::OFF_E - I::OFF_V);
+        tile_mm<B>(acc, sWt, SB, sMt, SF, 32 * mt, 32 * nt, lane);
+        char* stage = reinterpret_cast<char*>(sX) + (I::OFF_E - I::OFF_V);
         float* e32 = ws.e32 ? ws.e32 + (size_t)blk * D * D : nullptr;
         for_tile(acc, 32 * mt, 32 * nt, lane, [&](int x, int y, float a) {
             *reinterpret_cast<__bf16*>(stage + img_off(x, swap23(y), I::RB_E)) = (__bf16)(-a);
@@ -305,12 +310,12 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         });
     }
     __syncthreads();
-    // Kright and -E images: LDS staging -> HBM with 16-byte stores
+    // ---- 8. Kright and -E images: LDS staging -> HBM with 16-byte stores
     {
-        const char* stage = reinterpret_cast<const char*>(sP);
+        const char* stage = reinterpret_cast<const char*>(sX);
         constexpr int KUN = (I::OFF_V - I::OFF_K) / 16, EUN = (I::OFF_G - I::OFF_E) / 16;
         static_assert((I::OFF_V - I::OFF_K) + (I::OFF_G - I::OFF_E) <= kB * kSF * 4, "staging");
-        for (int u = tid; u < KUN + EUN; u += 256) {
+        for (int u = tid; u < KUN + EUN; u += NTH) {
             const int src = u < KUN ? u * 16 : (I::OFF_V - I::OFF_K) + (u - KUN) * 16;
             const int dst = u < KUN ? I::OFF_K + u * 16 : I::OFF_E + (u - KUN) * 16;
             *reinterpret_cast<u32x4*>(img + dst) = *reinterpret_cast<const u32x4*>(stage + src);
@@ -560,7 +565,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t st) {
     const int nb = (a.L + kB - 1) / kB;
     const int nblk = a.N * a.H * nb;
     const float scale2 = a.scale * kLog2e;
-    hipLaunchKernelGGL((precond_mfma_kernel<D>), dim3(nblk), dim3(256), 0, st,
+    hipLaunchKernelGGL((precond_mfma_kernel<D>), dim3(nblk), dim3(512), 0, st,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
                        (const __bf16*)a.w, a.beta, a.logf, a.L, nb, scale2, a.ws);
     hipError_t e = hipGetLastError();
