@@ -211,9 +211,36 @@ def main():
             "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
         }
+    out["beta0_baseline"] = causal_baseline(pa, pre, wl, out["prefill"])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, N * (L + T) / (ms_step * 1e-3))
     print(json.dumps(out), flush=True)
+
+
+def causal_baseline(pa, pre, wl, prefill):
+    """Time the library's plain causal attention kernel (beta = 0, no gate) at
+    the same shape: the FlashAttention-style baseline PaTH is compared with."""
+    import numpy as np
+    import torch
+    N, H, L, d = pre["q"].shape
+    o = torch.empty_like(pre["q"])
+    lse = torch.empty(N, H, L, dtype=torch.float32, device=pre["q"].device)
+    for _ in range(2):
+        pa.causal_attn(pre["q"], pre["k"], pre["v"], scale=wl.scale, out=(o, lse))
+    times = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        pa.causal_attn(pre["q"], pre["k"], pre["v"], scale=wl.scale, out=(o, lse))
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = float(np.median(times))
+    fa = fa_eq_flops(N, H, L, d)
+    return {"kernel": "path_causal_attn_fwd (plain causal softmax attention)",
+            "ms": round(ms, 4), "fa_eq_TFLOP_s": round(fa / (ms * 1e-3) / 1e12, 3),
+            "frac_of_peak": round(fa / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "path_prefill_over_baseline_time": round((prefill["precond_ms"] + prefill["scan_ms"]) / ms, 3)}
 
 
 def cpu_baseline(wl, x, seconds, gpu_tokens_per_s):

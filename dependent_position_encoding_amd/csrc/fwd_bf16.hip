@@ -560,6 +560,214 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Plain causal softmax attention (every beta = 0, no gate): the baseline the
+// PaTH kernels are measured against.  Same workgroup shape, LDS layout,
+// matrix-core formulation and online softmax as scan_mfma_kernel, minus the
+// preconditioning and the Qwork transition: key and value tiles come straight
+// from the inputs, converted to the operand layout while staged into LDS.
+template <int D>
+struct KVImg {
+    static constexpr int RB_K = 2 * D, RB_V = 2 * kB;
+    static constexpr int OFF_K = 0, OFF_V = kB * RB_K;
+    static constexpr int BYTES = OFF_V + D * RB_V;
+};
+
+template <int D>
+__global__ void __launch_bounds__(256)
+causal_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                   const __bf16* __restrict__ v, int L, int nb, float scale2,
+                   __bf16* __restrict__ o, float* __restrict__ lse) {
+    using I = KVImg<D>;
+    constexpr int B = kB, NT = D / 32, NKC = D / 16, UPR = D / 8;
+    constexpr int UN = B * UPR / 256;           // 16-byte units per thread per tensor
+    constexpr float kTau = 8.f;
+    __shared__ __attribute__((aligned(16))) char sImg[2][I::BYTES];
+
+    const int NH = gridDim.x / ((nb + 1) / 2);
+    const int pair = (int)(blockIdx.x / NH);
+    const int slice = blockIdx.x % NH;
+    const int bA = nb - 1 - 2 * pair, bB = bA - 1;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
+    const int col = lane & 31;
+    const int myb = wave < 2 ? bA : bB;
+    const int qloc = 32 * (wave & 1) + col;
+    const size_t sbase = (size_t)slice * L;
+
+    u32x4 rk[UN], rv[UN];
+    auto fetch = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < UN; ++i) {
+            const int u = tid + 256 * i, r = u / UPR, x0 = (u % UPR) * 8, pos = c * B + r;
+            const size_t g = (sbase + pos) * D + x0;
+            u32x4 z = {0u, 0u, 0u, 0u};
+            rk[i] = pos < L ? *reinterpret_cast<const u32x4*>(k + g) : z;
+            rv[i] = pos < L ? *reinterpret_cast<const u32x4*>(v + g) : z;
+        }
+    };
+    auto stage = [&](char* im) {
+#pragma unroll
+        for (int i = 0; i < UN; ++i) {
+            const int u = tid + 256 * i, r = u / UPR, x0 = (u % UPR) * 8;
+            bf16x8 kv = *reinterpret_cast<const bf16x8*>(&rk[i]);
+            bf16x8 vv = *reinterpret_cast<const bf16x8*>(&rv[i]);
+            typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+            bf16x4 lo4, hi4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                lo4[e] = (__bf16)((float)kv[e] * scale2);
+                hi4[e] = (__bf16)((float)kv[e + 4] * scale2);
+            }
+            const int g16 = x0 & ~15, off = x0 & 15;
+            *reinterpret_cast<bf16x4*>(im + I::OFF_K + img_off(r, g16 + swap23(off), I::RB_K)) = lo4;
+            *reinterpret_cast<bf16x4*>(im + I::OFF_K + img_off(r, g16 + swap23(off + 4), I::RB_K)) = hi4;
+            const int slot = swap23(r);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                *reinterpret_cast<__bf16*>(im + I::OFF_V + img_off(x0 + e, slot, I::RB_V)) = vv[e];
+        }
+    };
+
+    f32x16 Ot[NT], S[2];
+    bf16x8 Qb[NKC];
+    float m = 0.f, l = 0.f;
+    if (myb >= 0) {
+        const int pos = myb * B + qloc;
+        const __bf16* qp = q + (sbase + (pos < L ? pos : L - 1)) * D;
+        typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+            const bf16x4 a = *reinterpret_cast<const bf16x4*>(qp + 16 * kc + 4 * h);
+            const bf16x4 b = *reinterpret_cast<const bf16x4*>(qp + 16 * kc + 8 + 4 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { Qb[kc][e] = a[e]; Qb[kc][4 + e] = b[e]; }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) Ot[t] = zero16();
+    }
+
+    auto scores = [&](const char* im) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            S[mt] = zero16();
+            const int row = 32 * mt + col;
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    im + I::OFF_K + row * I::RB_K + swz_unit(row, 2 * kc + h, I::RB_K) * 16);
+                S[mt] = mfma32(a, Qb[kc], S[mt]);
+            }
+        }
+    };
+    auto pv = [&](const char* im) {
+        bf16x8 Pb[4];
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Pb[kc][e] = (__bf16)S[kc >> 1][8 * (kc & 1) + e];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) {
+                const int row = 32 * t + col;
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    im + I::OFF_V + row * I::RB_V + swz_unit(row, 2 * kc + h, I::RB_V) * 16);
+                Ot[t] = mfma32(a, Pb[kc], Ot[t]);
+            }
+    };
+    auto diag = [&](const char* im) {
+        scores(im);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = 32 * mt + crow(r, h);
+                if (key > qloc) S[mt][r] = -INFINITY;
+                mx = fmaxf(mx, S[mt][r]);
+            }
+        m = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        float rs = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(S[mt][r] - m);
+                S[mt][r] = p;
+                rs += p;
+            }
+        l = rs + __shfl_xor(rs, 32, 64);
+        pv(im);
+    };
+    auto step = [&](const char* im) {
+        scores(im);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if (__any(mx > m + kTau)) {
+            const float mn = fmaxf(m, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m - mn);
+            l *= alpha;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Ot[t][r] *= alpha;
+            m = mn;
+        }
+        float rs = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(S[mt][r] - m);
+                S[mt][r] = p;
+                rs += p;
+            }
+        l += rs + __shfl_xor(rs, 32, 64);
+        pv(im);
+    };
+
+    fetch(bA);
+    stage(sImg[0]);
+    if (bB >= 0) fetch(bB);
+    __syncthreads();
+    if (wave < 2) diag(sImg[0]);
+    if (bB >= 0) {
+        stage(sImg[1]);
+        if (bB > 0) fetch(bB - 1);
+        __syncthreads();
+        if (wave < 2) step(sImg[1]);
+        else diag(sImg[1]);
+        for (int c = bB - 1; c >= 0; --c) {
+            const int buf = (bA - c) & 1;
+            stage(sImg[buf]);
+            if (c > 0) fetch(c - 1);
+            __syncthreads();
+            step(sImg[buf]);
+        }
+    }
+
+    const int pos = myb * B + qloc;
+    if (myb >= 0 && pos < L) {
+        const float inv = 1.f / l;
+        __bf16* op = o + (sbase + pos) * D;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+                bf16x4 pk;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) pk[j] = (__bf16)(Ot[t][4 * i + j] * inv);
+                *reinterpret_cast<bf16x4*>(op + 32 * t + 8 * i + 4 * h) = pk;
+            }
+        if (lse && h == 0) lse[sbase + pos] = (m + __log2f(l)) * kLn2;
+    }
+}
+
 template <int D>
 hipError_t launch_t(const FwdArgs& a, hipStream_t st) {
     const int nb = (a.L + kB - 1) / kB;
@@ -595,9 +803,27 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+bool causal_supported(int d, bool bf16) { return bf16 && (d == 32 || d == 64); }
+
 hipError_t launch_causal(const FwdArgs& a, hipStream_t st) {
-    (void)a; (void)st;
-    return hipErrorNotSupported;
+    const int nb = (a.L + kB - 1) / kB;
+    const int ngrid = a.N * a.H * ((nb + 1) / 2);
+    const float scale2 = a.scale * kLog2e;
+    switch (a.d) {
+        case 32:
+            hipLaunchKernelGGL((causal_mfma_kernel<32>), dim3(ngrid), dim3(256), 0, st,
+                               (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.L,
+                               nb, scale2, (__bf16*)a.o, a.lse);
+            break;
+        case 64:
+            hipLaunchKernelGGL((causal_mfma_kernel<64>), dim3(ngrid), dim3(256), 0, st,
+                               (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.L,
+                               nb, scale2, (__bf16*)a.o, a.lse);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace pa

@@ -307,6 +307,8 @@ path_status path_causal_attn_fwd(const path_fwd_desc* desc, const void* q, const
     if (!q || !k || !v || !o) return fail(PATH_E_NULL, "q, k, v and o are required");
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
         return fail(PATH_E_ALIGN, "q, k, v and o must be 16-byte aligned");
+    if (!pa::causal_supported(desc->d, desc->dtype == PATH_BF16))
+        return fail(PATH_E_UNSUPPORTED, "the causal baseline takes bf16 with head dim 32 or 64");
     pa::FwdArgs a{};
     a.N = desc->N; a.H = desc->H; a.L = desc->L; a.d = desc->d; a.block = 64;
     a.bf16 = desc->dtype == PATH_BF16; a.scale = desc->scale;

@@ -67,6 +67,7 @@ hipError_t launch_decode(const CacheArgs& c, int n_keys, float scale,
                          const float* logf_t, hipStream_t st);
 int decode_chunk(int n_keys);
 
+bool causal_supported(int d, bool bf16);
 hipError_t launch_causal(const FwdArgs& a, hipStream_t st);
 
 }  // namespace pa

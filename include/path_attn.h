@@ -180,7 +180,8 @@ path_status path_decode_step(const path_fwd_desc *desc,
 
 /* Plain causal softmax attention (every beta = 0, no gate): the in-library
  * baseline the PaTH kernels are timed against.  Same layouts as
- * path_attn_fwd; no workspace. */
+ * path_attn_fwd; no workspace.  bf16 with d in {32, 64} only (other
+ * descriptions return PATH_E_UNSUPPORTED). */
 path_status path_causal_attn_fwd(const path_fwd_desc *desc, const void *q,
                                  const void *k, const void *v, void *o,
                                  float *lse, hipStream_t stream);

@@ -144,3 +144,32 @@ def test_fox_bf16_full_size_sampled(L):
                              wl.scale, rows=rows)
     check(f"fox full L={L} o", workloads.as_slices_f64(o, heads)[:, rows], ro, bf16=True)
     check(f"fox full L={L} lse", workloads.as_slices_f64(lse, heads)[:, rows], rl, bf16=True)
+
+
+@pytest.mark.parametrize("name,L,d", [("flipflop", 512, 32), ("lm", 1000, 64), ("lm", 4096, 64)])
+def test_causal_baseline_matches_oracle_at_beta_zero(name, L, d):
+    """The beta = 0 baseline kernel against the oracle with every beta = 0."""
+    pa = _pa()
+    wl = workloads.CONFIGS[name].replace(N=2, H=3, L=L, d=d)
+    x = workloads.make_inputs(wl)
+    g = {k: (v.to(DEV) if v is not None else None) for k, v in x.items()}
+    print(f"case causal {name} L={L} d={d}", flush=True)
+    o, lse = pa.causal_attn(g["q"], g["k"], g["v"], scale=wl.scale)
+    torch.cuda.synchronize()
+    f64 = {k: workloads.as_slices_f64(v) for k, v in x.items() if v is not None}
+    rows = None if L <= 1000 else _sample_rows(L, 64, 9)
+    ro, rl = oracle.fwd_rows(f64["q"], f64["k"], f64["v"], f64["w"], np.zeros_like(f64["beta"]),
+                             None, wl.scale, rows=rows)
+    go, gl = workloads.as_slices_f64(o), workloads.as_slices_f64(lse)
+    if rows is not None:
+        go, gl = go[:, rows], gl[:, rows]
+    check(f"causal {name} L={L} o", go, ro, bf16=True)
+    check(f"causal {name} L={L} lse", gl, rl, bf16=True)
+
+
+def test_causal_baseline_rejects_fp32():
+    pa = _pa()
+    z = torch.zeros(1, 1, 64, 64, device=DEV)
+    with pytest.raises(pa.PathAttnError) as e:
+        pa.causal_attn(z, z, z)
+    assert e.value.status == 4
