@@ -40,6 +40,34 @@ template <> struct Vec<float> {
     __device__ void set(int i, float f) { (&raw.x)[i] = f; }
 };
 
+// N values of type T kept as raw bits (loaded with one wide access).
+template <typename T, int N>
+struct Raw {
+    static constexpr int W = N * (int)sizeof(T) / 4;
+    uint32_t w[W];
+    __device__ void load(const T* p) {
+        if constexpr (W == 4) {
+            const uint4 x = *reinterpret_cast<const uint4*>(p);
+            w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+        } else if constexpr (W == 2) {
+            const uint2 x = *reinterpret_cast<const uint2*>(p);
+            w[0] = x.x; w[1] = x.y;
+        } else {
+#pragma unroll
+            for (int i = 0; i < W; i += 4) {
+                const uint4 x = reinterpret_cast<const uint4*>(p)[i / 4];
+                w[i] = x.x; w[i + 1] = x.y; w[i + 2] = x.z; w[i + 3] = x.w;
+            }
+        }
+    }
+    __device__ float get(int i) const {
+        union { uint32_t u; float f; } c;
+        if constexpr (sizeof(T) == 2) c.u = (i & 1) ? (w[i >> 1] & 0xffff0000u) : (w[i >> 1] << 16);
+        else c.u = w[i];
+        return c.f;
+    }
+};
+
 // Sum over the TPR consecutive lanes that share one row.
 template <int TPR>
 __device__ inline float group_sum(float x) {
@@ -102,29 +130,34 @@ __global__ void kv_append_kernel(K* __restrict__ kc, T* __restrict__ vc,
 // Single-query attention over one chunk of cached keys, optionally fused with
 // the rewrite and the append of the current token [Notes s2.8].
 //   score_j = scale * q_t . k_j + (C_t - C_j),  C = inclusive log-f prefix.
-// Each group of TPR lanes walks its keys with a running (max, sum, acc) in the
-// natural-exp domain; the 256/TPR groups are merged through LDS and the
-// chunk's partial state (m, l, acc[D]) goes to part[slice][chunk].
+// A chunk is kDecChunk keys; each group of TPR lanes owns one 16-byte slice
+// of a row and handles KPG keys spaced GROUPS apart.  All of a group's key,
+// value and prefix loads are issued before any arithmetic (KPG rows in flight
+// per group), then one max / sum / weighted value sum over its keys.  Groups
+// are merged through LDS and the chunk's partial softmax state
+// (m, l, acc[D]) goes to part[slice][chunk].
+constexpr int kDecChunk = 256;
+
 template <typename K, typename T, int D, bool FUSED>
 __global__ void __launch_bounds__(256)
 decode_chunk_kernel(K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ gc,
-                    int cap, int n_keys, int chunk, float scale,
+                    int cap, int n_keys, float scale,
                     const T* __restrict__ q_t, const T* __restrict__ k_t,
                     const T* __restrict__ v_t, const T* __restrict__ w_t,
                     const float* __restrict__ beta_t, const float* __restrict__ logf_t,
                     float* __restrict__ part) {
     constexpr int VN = Vec<K>::n, TPR = D / VN, GROUPS = 256 / TPR;
+    constexpr int KPG = kDecChunk / GROUPS;      // keys per group
     const int slice = blockIdx.y, ch = blockIdx.x, nch = gridDim.x;
     const int lane_in = threadIdx.x % TPR, grp = threadIdx.x / TPR;
     const int t = n_keys - 1;                     // query position
     const size_t sd = (size_t)slice * D + lane_in * VN;
 
-    float qv[VN], wv[VN], acc[VN];
+    float qv[VN], wv[VN];
 #pragma unroll
     for (int e = 0; e < VN; ++e) {
         qv[e] = to_f32(q_t[sd + e]);
         wv[e] = FUSED ? to_f32(w_t[sd + e]) : 0.f;
-        acc[e] = 0.f;
     }
     const float bt = FUSED ? beta_t[slice] : 0.f;
     float* gbase = gc ? gc + (size_t)slice * cap : nullptr;
@@ -135,52 +168,81 @@ decode_chunk_kernel(K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ 
     }
     K* kbase = kc + (size_t)slice * cap * D;
     T* vbase = vc + (size_t)slice * cap * D;
+    const int j0 = ch * kDecChunk;
 
-    float m = -INFINITY, l = 0.f;
-    const int j0 = ch * chunk, j1 = min(n_keys, j0 + chunk);
-    for (int j = j0 + grp; j < j1; j += GROUPS) {
-        float kf[VN], vf[VN], bias;
+    // ---- loads (every key of this group in flight at once)
+    Vec<K> kx[KPG];
+    Raw<T, VN> vr[KPG];
+    float gj[KPG];
+#pragma unroll
+    for (int i = 0; i < KPG; ++i) {
+        const int j = j0 + grp + GROUPS * i;
         const size_t off = (size_t)j * D + lane_in * VN;
+        const bool live = j < n_keys && !(FUSED && j == t);
+        if (live) {
+            kx[i].load(kbase + off);
+            vr[i].load(vbase + off);
+            gj[i] = gbase ? gbase[j] : 0.f;
+        } else {
+            // keys past the end get weight 0; their values must be finite
+#pragma unroll
+            for (int e = 0; e < Raw<T, VN>::W; ++e) vr[i].w[e] = 0u;
+            gj[i] = 0.f;
+        }
+    }
+    // ---- scores (rewriting the keys first when fused)
+    float sc[KPG];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < KPG; ++i) {
+        const int j = j0 + grp + GROUPS * i;
+        const size_t off = (size_t)j * D + lane_in * VN;
+        float kf[VN], bias = 0.f;
+        if (j >= n_keys) {
+            sc[i] = -INFINITY;
+            continue;
+        }
         if (FUSED && j == t) {
             // the new token: stored as given, its own transition excluded
 #pragma unroll
             for (int e = 0; e < VN; ++e) {
                 kf[e] = to_f32(from_f32<K>(to_f32(k_t[sd + e])));
-                vf[e] = to_f32(v_t[sd + e]);
                 kbase[off + e] = from_f32<K>(kf[e]);
                 vbase[off + e] = v_t[sd + e];
             }
+            vr[i].load(v_t + sd);
             if (gbase && lane_in == 0) gbase[t] = ct;
-            bias = 0.f;
         } else {
-            Vec<K> x;
-            x.load(kbase + off);
             if (FUSED) {
                 float p = 0.f;
 #pragma unroll
-                for (int e = 0; e < VN; ++e) p += wv[e] * x.get(e);
+                for (int e = 0; e < VN; ++e) p += wv[e] * kx[i].get(e);
                 const float cf = bt * group_sum<TPR>(p);
 #pragma unroll
-                for (int e = 0; e < VN; ++e) x.set(e, x.get(e) - cf * wv[e]);
-                x.store(kbase + off);
+                for (int e = 0; e < VN; ++e) kx[i].set(e, kx[i].get(e) - cf * wv[e]);
+                kx[i].store(kbase + off);
             }
 #pragma unroll
-            for (int e = 0; e < VN; ++e) {
-                kf[e] = x.get(e);
-                vf[e] = to_f32(vbase[off + e]);
-            }
-            bias = gbase ? ct - gbase[j] : 0.f;
+            for (int e = 0; e < VN; ++e) kf[e] = kx[i].get(e);
+            bias = gbase ? ct - gj[i] : 0.f;
         }
         float p = 0.f;
 #pragma unroll
         for (int e = 0; e < VN; ++e) p += qv[e] * kf[e];
-        const float s = scale * group_sum<TPR>(p) + bias;
-        const float mn = fmaxf(m, s);
-        const float alpha = __expf(m - mn), pe = __expf(s - mn);
-        l = l * alpha + pe;
+        sc[i] = scale * group_sum<TPR>(p) + bias;
+        m = fmaxf(m, sc[i]);
+    }
+    float l = 0.f, acc[VN];
 #pragma unroll
-        for (int e = 0; e < VN; ++e) acc[e] = acc[e] * alpha + pe * vf[e];
-        m = mn;
+    for (int e = 0; e < VN; ++e) acc[e] = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < KPG; ++i) {
+            const float pe = __expf(sc[i] - m);       // 0 for keys past the end
+            l += pe;
+#pragma unroll
+            for (int e = 0; e < VN; ++e) acc[e] += pe * vr[i].get(e);
+        }
     }
 
     // merge the groups of this block
@@ -207,45 +269,52 @@ decode_chunk_kernel(K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ 
 }
 
 // Merge the chunk partials of one slice: o = sum acc_c e^{m_c - M} / l,
-// lse = M + log l.  One 256-thread block per slice: a block-wide max, then
-// 256/D groups of D lanes each sum a strided share of the chunks.
+// lse = M + log l.  One 1024-thread block per slice: the chunk maxima and
+// sums are reduced in LDS, and 1024/D groups of D lanes each sum a strided
+// share of the chunks' accumulators (every load of a group in flight at once).
+constexpr int kCombineMaxChunks = 512;
+constexpr int kCombineThreads = 1024;
+
 template <typename T, int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kCombineThreads)
 decode_combine_kernel(const float* __restrict__ part, int nch, T* __restrict__ o_t,
                       float* __restrict__ lse_t) {
-    constexpr int G = 256 / D;
-    __shared__ float red[256];
+    constexpr int NTH = kCombineThreads, G = NTH / D;
+    __shared__ float red[NTH];
+    __shared__ float sf[kCombineMaxChunks];
     __shared__ float sacc[G][D];
-    __shared__ float sl[G];
     const int slice = blockIdx.x, tid = threadIdx.x;
     const float* p = part + (size_t)slice * nch * (D + 2);
-    float mloc = -INFINITY;
-    for (int c = tid; c < nch; c += 256) mloc = fmaxf(mloc, p[(size_t)c * (D + 2)]);
-    red[tid] = mloc;
+    const float mc = tid < nch ? p[(size_t)tid * (D + 2)] : -INFINITY;
+    const float lc = tid < nch ? p[(size_t)tid * (D + 2) + 1] : 0.f;
+    red[tid] = mc;
     __syncthreads();
-    for (int off = 128; off > 0; off >>= 1) {
+    for (int off = NTH / 2; off > 0; off >>= 1) {
         if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
         __syncthreads();
     }
     const float M = red[0];
-    const int g = tid / D, x = tid % D;
-    float a = 0.f, ls = 0.f;
-#pragma unroll 4
-    for (int c = g; c < nch; c += G) {
-        const float* pc = p + (size_t)c * (D + 2);
-        const float mc = pc[0];
-        const float f = (mc == -INFINITY) ? 0.f : __expf(mc - M);
-        a += f * pc[2 + x];
-        ls += f * pc[1];
+    __syncthreads();
+    const float f = (mc == -INFINITY) ? 0.f : __expf(mc - M);
+    if (tid < nch) sf[tid] = f;
+    red[tid] = f * lc;
+    __syncthreads();
+    for (int off = NTH / 2; off > 0; off >>= 1) {
+        if (tid < off) red[tid] += red[tid + off];
+        __syncthreads();
     }
+    const float lt = red[0];
+    const int g = tid / D, x = tid % D;
+    float a = 0.f;
+#pragma unroll 8
+    for (int c = g; c < nch; c += G) a += sf[c] * p[(size_t)c * (D + 2) + 2 + x];
     sacc[g][x] = a;
-    if (x == 0) sl[g] = ls;
     __syncthreads();
     if (tid < D) {
-        float s = 0.f, lt = 0.f;
+        float sum = 0.f;
 #pragma unroll
-        for (int gg = 0; gg < G; ++gg) { s += sacc[gg][tid]; lt += sl[gg]; }
-        o_t[(size_t)slice * D + tid] = from_f32<T>(s / lt);
+        for (int gg = 0; gg < G; ++gg) sum += sacc[gg][tid];
+        o_t[(size_t)slice * D + tid] = from_f32<T>(sum / lt);
         if (tid == 0 && lse_t) lse_t[slice] = M + logf(lt);
     }
 }
@@ -467,10 +536,11 @@ hipError_t launch_kv_append(const CacheArgs& c, int n, const void* k_t,
 }
 
 int decode_chunk(int n_keys) {
-    // enough chunks per slice to cover the chip, each at least 256 keys
     (void)n_keys;
-    return 256;
+    return kDecChunk;
 }
+
+int decode_max_keys() { return kDecChunk * kCombineMaxChunks; }
 
 template <typename K, typename T, int D>
 static hipError_t decode_t(const CacheArgs& c, int n_keys, float scale, const void* q_t,
@@ -481,16 +551,16 @@ static hipError_t decode_t(const CacheArgs& c, int n_keys, float scale, const vo
     dim3 grid(nch, c.N * c.H);
     if (fused)
         hipLaunchKernelGGL((decode_chunk_kernel<K, T, D, true>), grid, dim3(256), 0, st,
-                           (K*)c.kcache, (T*)c.vcache, c.gcache, c.cap, n_keys, chunk, scale,
+                           (K*)c.kcache, (T*)c.vcache, c.gcache, c.cap, n_keys, scale,
                            (const T*)q_t, (const T*)k_t, (const T*)v_t, (const T*)w_t,
                            beta_t, logf_t, part);
     else
         hipLaunchKernelGGL((decode_chunk_kernel<K, T, D, false>), grid, dim3(256), 0, st,
-                           (K*)c.kcache, (T*)c.vcache, c.gcache, c.cap, n_keys, chunk, scale,
+                           (K*)c.kcache, (T*)c.vcache, c.gcache, c.cap, n_keys, scale,
                            (const T*)q_t, nullptr, nullptr, nullptr, nullptr, nullptr, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(c.N * c.H), dim3(256), 0, st,
+    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(c.N * c.H), dim3(kCombineThreads), 0, st,
                        (const float*)part, nch, (T*)o_t, lse_t);
     return hipGetLastError();
 }

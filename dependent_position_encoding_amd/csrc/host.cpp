@@ -266,6 +266,8 @@ static path_status decode_common(const path_fwd_desc* desc, const path_cache* ca
         return fail(PATH_E_ALIGN, "q_t and o_t must be 16-byte aligned");
     if (n_keys < 1) return fail(PATH_E_SHAPE, "at least one key is required");
     if (n_keys > cache->cap) return fail(PATH_E_CAPACITY, "keys exceed cache capacity");
+    if (n_keys > pa::decode_max_keys())
+        return fail(PATH_E_UNSUPPORTED, "decode attends over at most 131072 keys per call");
     if (!ws) return fail(PATH_E_WORKSPACE, "workspace is NULL");
     if (!aligned(ws, 256)) return fail(PATH_E_ALIGN, "workspace must be 256-byte aligned");
     if (ws_bytes < path_decode_workspace(desc, n_keys))

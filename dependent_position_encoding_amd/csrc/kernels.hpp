@@ -66,6 +66,7 @@ hipError_t launch_decode(const CacheArgs& c, int n_keys, float scale,
                          const void* w_t, const float* beta_t,
                          const float* logf_t, hipStream_t st);
 int decode_chunk(int n_keys);
+int decode_max_keys();   // longest cache one decode call can attend over
 
 bool causal_supported(int d, bool bf16);
 hipError_t launch_causal(const FwdArgs& a, hipStream_t st);

@@ -161,7 +161,8 @@ size_t path_decode_workspace(const path_fwd_desc *desc, int n_keys);
  *   s_j = scale * q_t^T kcache[j] + (gcache[t] - gcache[j])   (bias 0 if
  *   gcache is NULL), o_t = softmax(s) . vcache, lse_t = log sum exp s.
  * q_t, o_t [N, H, d] desc->dtype; lse_t [N, H] float32 or NULL.
- * Split over key chunks; ws holds the per-chunk partial softmax states. */
+ * Split over key chunks of 256; ws holds the per-chunk partial softmax
+ * states.  At most 131072 keys per call (PATH_E_UNSUPPORTED beyond). */
 path_status path_decode(const path_fwd_desc *desc, const path_cache *cache,
                         int n_keys, const void *q_t, void *o_t, float *lse_t,
                         void *ws, size_t ws_bytes, hipStream_t stream);
