@@ -64,6 +64,75 @@ def fa_eq_flops(N, H, L, d):
     return 2.0 * N * H * L * L * d
 
 
+TRACKED_SOURCES = {
+    "scan": "dependent_position_encoding_amd/csrc/fwd_bf16.hip",
+    "decode": "dependent_position_encoding_amd/csrc/decode.hip",
+}
+KERNEL_KEYS = {"scan": "scan_mfma_kernel<64, true>",
+               "decode": "decode_chunk_kernel<pa::bf16, pa::bf16, 64, true>"}
+
+
+def _source_sha(rel):
+    import hashlib
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _pmc_by_kernel(path):
+    import csv
+    import re
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            m = re.search(r"pa::(?:\(anonymous namespace\)::)?(\w+)(<[^()]*>)?", r["Kernel_Name"])
+            name = (m.group(1) + (m.group(2) or "")) if m else r["Kernel_Name"][:40]
+            out.setdefault(name, []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize_pmc(paths, workload):
+    """HBM bytes per launch of the scan and fused decode kernels from
+    rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by what
+    the same counter reports for a device copy of known size."""
+    fetch, write, cfetch, cwrite = (_pmc_by_kernel(p) for p in paths)
+    copy_bytes = float(1 << 30)
+
+    def copy_kib(rec):
+        vals = [v for k, vs in rec.items() if "copy" in k.lower() for v in vs]
+        return sum(vals) / len(vals)
+
+    f_scale = copy_bytes / (copy_kib(cfetch) * 1024)
+    w_scale = copy_bytes / (copy_kib(cwrite) * 1024)
+    res = {"workload": workload, "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "kernels": {}}
+    for key, kname in KERNEL_KEYS.items():
+        fv, wv = fetch[kname], write[kname]
+        rb = sum(fv) / len(fv) * 1024 * f_scale
+        wb = sum(wv) / len(wv) * 1024 * w_scale
+        res["kernels"][key] = {"name": kname, "dispatches": len(fv), "read_bytes": rb,
+                               "write_bytes": wb, "bytes": rb + wb,
+                               "source": TRACKED_SOURCES[key],
+                               "source_sha256": _source_sha(TRACKED_SOURCES[key])}
+    out = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res))
+
+
+def measured_traffic(workload, key):
+    """Counter-measured HBM bytes per launch, or None if not taken for this
+    workload or if the kernel's source changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)["kernels"][key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != _source_sha(rec["source"]):
+        return None
+    return rec["bytes"]
+
+
 def decode_bytes(N, H, d, t, k_bytes, v_bytes):
     """HBM bytes one fused step at position t must move: read and write every
     cached key, read every cached value and log-f prefix entry."""
@@ -79,7 +148,16 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a bench run "
+                         "and of a --calibrate-copy run into profiles/traffic_<workload>.json")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device-to-device copy three times (the "
+                         "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
@@ -91,8 +169,17 @@ def main():
     import dependent_position_encoding_amd as pa
     import workloads
 
-    pa.load_library()
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)     # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": src.numel() * 4,
+                          "bytes_written": dst.numel() * 4, "dispatches": 3}))
+        return
+    pa.load_library()
     spec = WORKLOADS[args.workload]
     wl = workloads.CONFIGS[spec["cfg"]]
     if "L" in spec:
@@ -195,7 +282,8 @@ def main():
         "roofline": {
             "kernel": "scan (right-to-left block scan with online softmax)",
             "bound": "mfma", "achieved": round(scan_tf, 3), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(scan_tf / peak, 4), "traffic": None,
+            "frac": round(scan_tf / peak, 4), "traffic": measured_traffic(args.workload, "scan"),
+            "algorithmic_note": "flops as counted by scan_flops(); traffic = HBM bytes per launch",
         },
     }
     if T:
@@ -209,7 +297,9 @@ def main():
         out["roofline_decode"] = {
             "kernel": "fused decode step (rewrite + append + split-K attention, with its combine)",
             "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic(args.workload, "decode"),
+            "algorithmic_bytes_first_step": decode_bytes(N, H, d, L, kb, vb),
         }
     out["beta0_baseline"] = causal_baseline(pa, pre, wl, out["prefill"])
     if not args.no_cpu_baseline:
