@@ -9,6 +9,7 @@
 // Householder Transformations" (gist.science), section 3.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mfma.hpp"
 
 namespace pa {
 
@@ -333,45 +334,73 @@ decode_combine_kernel(const float* __restrict__ part, int nch, T* __restrict__ o
 // so that S_c = T_c Z_{g(c)} (align_apply_kernel).  All in fp32.
 constexpr int kSufGroup = 16;
 
+// The d x d products run on the matrix cores with fp32 operands split into
+// three bf16 parts (tile_mm_f32), on matrices padded to DP = max(d, 32).  The
+// chain is kept transposed (S^T <- S^T - S^T E^T) so that every product reads
+// both operands row-major from LDS.  Stored: suf[c] = T_c^T, grp[g][0] = G_g,
+// grp[g][1] = Z_g^T.
+constexpr int kMS = 68;   // LDS row stride (floats) of the padded matrices
+
 template <int D>
-__device__ inline void mat_load(float (*dst)[D + 1], const float* src, int tid) {
-    for (int e = tid; e < D * D; e += 256) dst[e / D][e % D] = src[e];
+struct Pad {
+    static constexpr int DP = D < 32 ? 32 : D, DT = DP / 32;
+};
+
+// dst (DP x DP, stride kMS) <- src (D x D row-major), zero padded
+template <int D>
+__device__ inline void mat_load_pad(float* dst, const float* src, int tid) {
+    constexpr int DP = Pad<D>::DP;
+    for (int e = tid; e < DP * DP; e += 256) {
+        const int x = e / DP, y = e % DP;
+        dst[x * kMS + y] = (x < D && y < D) ? src[x * D + y] : 0.f;
+    }
+}
+
+template <int D>
+__device__ inline void mat_identity(float* dst, int tid) {
+    constexpr int DP = Pad<D>::DP;
+    for (int e = tid; e < DP * DP; e += 256) dst[(e / DP) * kMS + e % DP] = (e / DP == e % DP) ? 1.f : 0.f;
 }
 
 template <int D>
 __global__ void __launch_bounds__(256)
 suffix_local_kernel(int nb, int ngroups, FwdWs ws) {
-    __shared__ float sS[D][D + 1], sE[D][D + 1];
-    constexpr int PER = D * D / 256 > 0 ? D * D / 256 : 1;
+    using P = Pad<D>;
+    __shared__ __attribute__((aligned(16))) float sSt[64 * kMS], sE[64 * kMS];
     const int slice = blockIdx.x / ngroups, gi = blockIdx.x % ngroups, tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
     const int first = gi * kSufGroup, last = min(nb - 1, first + kSufGroup - 1);
     const size_t b0 = (size_t)slice * nb;
-    for (int e = tid; e < D * D; e += 256) {
-        const float v = (e / D == e % D) ? 1.f : 0.f;
-        sS[e / D][e % D] = v;
-        ws.suf[(b0 + last) * D * D + e] = v;
-    }
-    // c = first - 1 yields the group total F_first T_first
+    mat_identity<D>(sSt, tid);
+    for (int e = tid; e < D * D; e += 256) ws.suf[(b0 + last) * D * D + e] = (e / D == e % D) ? 1.f : 0.f;
+    // c = first - 1 yields the group total: G^T = T_first^T F_first^T
     for (int c = last - 1; c >= first - 1; --c) {
         __syncthreads();
-        mat_load<D>(sE, ws.e32 + (b0 + c + 1) * D * D, tid);
+        mat_load_pad<D>(sE, ws.e32 + (b0 + c + 1) * D * D, tid);
         __syncthreads();
-        float r[PER];
-        int cnt = 0;
-        for (int e = tid; e < D * D; e += 256, ++cnt) {
-            const int x = e / D, y = e % D;
-            float acc = 0.f;
-#pragma unroll 8
-            for (int z = 0; z < D; ++z) acc += sE[x][z] * sS[z][y];
-            r[cnt] = sS[x][y] - acc;
+        f32x16 acc = zero16();
+        const int mt = wave / P::DT, nt = wave % P::DT;
+        const bool mine = wave < P::DT * P::DT;
+        if (mine) tile_mm_f32<P::DP>(acc, sSt, kMS, sE, kMS, 32 * mt, 32 * nt, lane);
+        const int h = lane >> 5, y = 32 * nt + (lane & 31);
+        float nv[16];
+        if (mine) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) nv[r] = sSt[(32 * mt + crow(r, h)) * kMS + y] - acc[r];
         }
         __syncthreads();
-        float* dst = c >= first ? ws.suf + (b0 + c) * D * D
-                                : ws.grp + ((size_t)slice * ngroups + gi) * 2 * D * D;
-        cnt = 0;
-        for (int e = tid; e < D * D; e += 256, ++cnt) {
-            sS[e / D][e % D] = r[cnt];
-            dst[e] = r[cnt];
+        if (mine) {
+            float* dst = c >= first ? ws.suf + (b0 + c) * D * D
+                                    : ws.grp + ((size_t)slice * ngroups + gi) * 2 * D * D;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int x = 32 * mt + crow(r, h);
+                sSt[x * kMS + y] = nv[r];
+                if (x < D && y < D) {
+                    if (c >= first) dst[x * D + y] = nv[r];   // T_c^T
+                    else dst[y * D + x] = nv[r];              // G (transposed back)
+                }
+            }
         }
     }
 }
@@ -379,10 +408,10 @@ suffix_local_kernel(int nb, int ngroups, FwdWs ws) {
 template <int D>
 __global__ void __launch_bounds__(256)
 suffix_groups_kernel(int nb, int ngroups, FwdWs ws) {
-    __shared__ float sZ[D][D + 1], sG[D][D + 1];
+    using P = Pad<D>;
+    __shared__ __attribute__((aligned(16))) float sZt[64 * kMS], sG[64 * kMS];
     __shared__ double sScan[256];
-    constexpr int PER = D * D / 256 > 0 ? D * D / 256 : 1;
-    const int slice = blockIdx.x, tid = threadIdx.x;
+    const int slice = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const size_t b0 = (size_t)slice * nb, g0 = (size_t)slice * ngroups;
     // block prefix of log f, gpre[c] = sum_{c' < c} tot[c'], accumulated in double
     double carry = 0.0;
@@ -401,70 +430,77 @@ suffix_groups_kernel(int nb, int ngroups, FwdWs ws) {
         carry += sScan[255];
         __syncthreads();
     }
-    for (int e = tid; e < D * D; e += 256) {
-        const float v = (e / D == e % D) ? 1.f : 0.f;
-        sZ[e / D][e % D] = v;
-        ws.grp[((g0 + ngroups - 1) * 2 + 1) * D * D + e] = v;
-    }
+    mat_identity<D>(sZt, tid);
+    for (int e = tid; e < D * D; e += 256)
+        ws.grp[((g0 + ngroups - 1) * 2 + 1) * D * D + e] = (e / D == e % D) ? 1.f : 0.f;
+    // Z_g^T = Z_{g+1}^T G_{g+1}^T
     for (int g = ngroups - 2; g >= 0; --g) {
         __syncthreads();
-        mat_load<D>(sG, ws.grp + ((g0 + g + 1) * 2) * D * D, tid);
+        mat_load_pad<D>(sG, ws.grp + ((g0 + g + 1) * 2) * D * D, tid);
         __syncthreads();
-        float r[PER];
-        int cnt = 0;
-        for (int e = tid; e < D * D; e += 256, ++cnt) {
-            const int x = e / D, y = e % D;
-            float acc = 0.f;
-#pragma unroll 8
-            for (int z = 0; z < D; ++z) acc += sG[x][z] * sZ[z][y];
-            r[cnt] = acc;
-        }
+        f32x16 acc = zero16();
+        const int mt = wave / P::DT, nt = wave % P::DT;
+        const bool mine = wave < P::DT * P::DT;
+        if (mine) tile_mm_f32<P::DP>(acc, sZt, kMS, sG, kMS, 32 * mt, 32 * nt, lane);
         __syncthreads();
-        cnt = 0;
-        for (int e = tid; e < D * D; e += 256, ++cnt) {
-            sZ[e / D][e % D] = r[cnt];
-            ws.grp[((g0 + g) * 2 + 1) * D * D + e] = r[cnt];
+        if (mine) {
+            const int h = lane >> 5, y = 32 * nt + (lane & 31);
+            float* dst = ws.grp + ((g0 + g) * 2 + 1) * D * D;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int x = 32 * mt + crow(r, h);
+                sZt[x * kMS + y] = acc[r];
+                if (x < D && y < D) dst[x * D + y] = acc[r];
+            }
         }
     }
 }
 
-// kcache rows of block c = Kright_c (T_c Z_g); values copied; gcache = block
+// kcache rows of block c = (Kright_c T_c) Z_g; values copied; gcache = block
 // prefix + in-block cumsum.  One block of 256 threads per (slice, c).
 template <typename K, typename T, int B, int D>
 __global__ void __launch_bounds__(256)
 align_apply_kernel(int L, int nb, int ngroups, FwdWs ws, const T* __restrict__ v,
                    int has_gate, K* __restrict__ kc, T* __restrict__ vc,
                    float* __restrict__ gc, int cap) {
-    __shared__ float sA[D][D + 1], sZ[D][D + 1], sK[B][D + 1];
-    constexpr int PER = D * D / 256 > 0 ? D * D / 256 : 1;
+    using P = Pad<D>;
+    __shared__ __attribute__((aligned(16))) float sK[64 * kMS], sT[64 * kMS], sZ[64 * kMS];
     const int blk = blockIdx.x, slice = blk / nb, c = blk % nb, tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, h = lane >> 5;
     const int g = c / kSufGroup;
-    mat_load<D>(sA, ws.suf + (size_t)blk * D * D, tid);
-    mat_load<D>(sZ, ws.grp + (((size_t)slice * ngroups + g) * 2 + 1) * D * D, tid);
-    for (int e = tid; e < B * D; e += 256) sK[e / D][e % D] = ws.k32[(size_t)blk * B * D + e];
-    __syncthreads();
-    float r[PER];
-    int cnt = 0;
-    for (int e = tid; e < D * D; e += 256, ++cnt) {
-        const int x = e / D, y = e % D;
-        float acc = 0.f;
-#pragma unroll 8
-        for (int z = 0; z < D; ++z) acc += sA[x][z] * sZ[z][y];
-        r[cnt] = acc;
+    mat_load_pad<D>(sT, ws.suf + (size_t)blk * D * D, tid);                                   // T^T
+    mat_load_pad<D>(sZ, ws.grp + (((size_t)slice * ngroups + g) * 2 + 1) * D * D, tid);      // Z^T
+    for (int e = tid; e < 64 * P::DP; e += 256) {
+        const int r = e / P::DP, x = e % P::DP;
+        sK[r * kMS + x] = (r < B && x < D) ? ws.k32[((size_t)blk * B + r) * D + x] : 0.f;
     }
     __syncthreads();
-    cnt = 0;
-    for (int e = tid; e < D * D; e += 256, ++cnt) sA[e / D][e % D] = r[cnt];   // S_c
+    constexpr int TILES = 2 * P::DT;                 // 64 rows x DP columns
+    f32x16 acc = zero16();
+    const int mt = wave / P::DT, nt = wave % P::DT;
+    const bool mine = wave < TILES;
+    if (mine) tile_mm_f32<P::DP>(acc, sK, kMS, sT, kMS, 32 * mt, 32 * nt, lane);   // X = K T
     __syncthreads();
+    if (mine) {
+        const int y = 32 * nt + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sK[(32 * mt + crow(r, h)) * kMS + y] = acc[r];
+    }
+    __syncthreads();
+    acc = zero16();
+    if (mine) tile_mm_f32<P::DP>(acc, sK, kMS, sZ, kMS, 32 * mt, 32 * nt, lane);   // X Z
+    if (mine) {
+        const int y = 32 * nt + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int rr = 32 * mt + crow(r, h), pos = c * B + rr;
+            if (rr < B && y < D && pos < L)
+                kc[((size_t)slice * cap + pos) * D + y] = from_f32<K>(acc[r]);
+        }
+    }
     for (int e = tid; e < B * D; e += 256) {
         const int rr = e / D, y = e % D, pos = c * B + rr;
-        if (pos >= L) continue;
-        float s = 0.f;
-#pragma unroll 8
-        for (int x = 0; x < D; ++x) s += sK[rr][x] * sA[x][y];
-        const size_t dst = ((size_t)slice * cap + pos) * D + y;
-        kc[dst] = from_f32<K>(s);
-        vc[dst] = v[((size_t)slice * L + pos) * D + y];
+        if (pos < L) vc[((size_t)slice * cap + pos) * D + y] = v[((size_t)slice * L + pos) * D + y];
     }
     if (gc && tid < B) {
         const int pos = c * B + tid;

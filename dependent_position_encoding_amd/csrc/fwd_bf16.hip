@@ -344,7 +344,7 @@ __device__ inline void load_image(const char* __restrict__ src, char* dst, int t
 __device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int D, bool FOX>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
                  float* __restrict__ lse) {
     using I = Img<D>;

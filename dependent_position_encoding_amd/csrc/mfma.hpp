@@ -71,6 +71,41 @@ __device__ inline void tile_mm(f32x16& acc, const TA* A, int lda, const TB* Bn, 
     }
 }
 
+// float32 operands split three ways (hi + mid + lo, 8 mantissa bits each):
+// acc += A * Bn^T with the six partial products that matter at fp32
+// precision, smallest first.  Used where a long chain of d x d products must
+// stay at fp32 accuracy.
+__device__ inline void ld8_3(const float* p, bf16x8& hi, bf16x8& mid, bf16x8& lo) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = e < 4 ? a[e] : b[e - 4];
+        hi[e] = (__bf16)x;
+        const float r = x - (float)hi[e];
+        mid[e] = (__bf16)r;
+        lo[e] = (__bf16)(r - (float)mid[e]);
+    }
+}
+
+template <int K>
+__device__ inline void tile_mm_f32(f32x16& acc, const float* A, int lda, const float* Bn, int ldb,
+                                   int m0, int n0, int lane) {
+    const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        bf16x8 ah, am, al, bh, bm, bl;
+        ld8_3(A + (m0 + r) * lda + k0 + 8 * h, ah, am, al);
+        ld8_3(Bn + (n0 + r) * ldb + k0 + 8 * h, bh, bm, bl);
+        acc = mfma32(am, bm, acc);
+        acc = mfma32(al, bh, acc);
+        acc = mfma32(ah, bl, acc);
+        acc = mfma32(am, bh, acc);
+        acc = mfma32(ah, bm, acc);
+        acc = mfma32(ah, bh, acc);
+    }
+}
+
 __device__ inline f32x16 zero16() {
     f32x16 z;
 #pragma unroll
