@@ -324,20 +324,24 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 }
 
 // ---------------------------------------------------------------------------
-// Direct HBM -> LDS copy of one tile image (16 bytes per lane, the lanes of a
-// wave fill 1 KB of LDS contiguously).  The caller waits on vmcnt and
+// Direct HBM -> LDS copy of one tile image through a buffer resource: the
+// lanes of a wave fill 1 KB of LDS contiguously (16 bytes each), the image
+// offset travels in a scalar register and the lane offset is one VGPR, so the
+// stream costs the scan almost no registers.  The caller waits on vmcnt and
 // synchronises before reading.
 template <int BYTES>
-__device__ inline void load_image(const char* __restrict__ src, char* dst, int tid) {
+__device__ inline void load_image(__amdgpu_buffer_rsrc_t rsrc, uint32_t src_off, char* dst,
+                                  int tid) {
     constexpr int UNITS = BYTES / 16;
-    const int wave = tid >> 6, lane = tid & 63;
+    // the wave index is uniform; saying so keeps the offsets in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 #pragma unroll
     for (int it = 0; it < (UNITS + 255) / 256; ++it) {
         const int u0 = (it * 4 + wave) * 64;
         if (u0 < UNITS && u0 + lane < UNITS)
-            __builtin_amdgcn_global_load_lds(
-                src + (size_t)(u0 + lane) * 16,
-                (__attribute__((address_space(3))) void*)(dst + u0 * 16), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void*)(dst + u0 * 16), 16,
+                (uint32_t)lane * 16, src_off + (uint32_t)u0 * 16, 0, 0);
     }
 }
 
@@ -361,10 +365,12 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
     const int myb = wave < 2 ? bA : bB;
     const int qloc = 32 * (wave & 1) + col;
     const size_t blk0 = (size_t)slice * nb;
-    const char* img = static_cast<const char*>(ws.img);
+    // this slice's images: nb * I::BYTES bytes (the host keeps that below 4 GiB)
+    const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<char*>(ws.img) + blk0 * I::BYTES, 0, nb * I::BYTES, 0x00020000);
 
-    load_image<I::BYTES>(img + (blk0 + bA) * I::BYTES, sImg[0], tid);
-    if (bB >= 0) load_image<I::BYTES>(img + (blk0 + bB) * I::BYTES, sImg[1], tid);
+    load_image<I::BYTES>(irs, (uint32_t)bA * I::BYTES, sImg[0], tid);
+    if (bB >= 0) load_image<I::BYTES>(irs, (uint32_t)bB * I::BYTES, sImg[1], tid);
 
     f32x16 Qw[NT], Ot[NT], S[2];
     float m = 0.f, l = 0.f, gq = 0.f, grun = 0.f;
@@ -455,16 +461,21 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
         bf16x8 ones;
 #pragma unroll
         for (int e = 0; e < 8; ++e) ones[e] = (__bf16)((h == 0 && e < 2) ? 1.f : 0.f);
+        bf16x8 ka[2][NKC];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) {
+                const int row = 32 * mt + col;
+                ka[mt][kc] = *reinterpret_cast<const bf16x8*>(
+                    im + I::OFF_K + row * I::RB_K + swz_unit(row, 2 * kc + h, I::RB_K) * 16);
+            }
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             S[mt] = zero16();
             const int row = 32 * mt + col;
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    im + I::OFF_K + row * I::RB_K + swz_unit(row, 2 * kc + h, I::RB_K) * 16);
-                S[mt] = mfma32(a, Qb[kc], S[mt]);
-            }
+            for (int kc = 0; kc < NKC; ++kc) S[mt] = mfma32(ka[mt][kc], Qb[kc], S[mt]);
             if (FOX) {
                 const float gb = -gimg[row] * kLog2e;
                 const __bf16 hi = (__bf16)gb;
@@ -526,7 +537,7 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
     if (wave < 2) diag(sImg[0]);
     __syncthreads();
     if (bB >= 0) {
-        if (bB > 0) load_image<I::BYTES>(img + (blk0 + bB - 1) * I::BYTES, sImg[0], tid);
+        if (bB > 0) load_image<I::BYTES>(irs, (uint32_t)(bB - 1) * I::BYTES, sImg[0], tid);
         // phase 2: key block bB -- a scan step for the upper block, the
         // diagonal for the lower one
         if (wave < 2) step(sImg[1], bB);
@@ -535,7 +546,7 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
         __syncthreads();
         for (int c = bB - 1; c >= 0; --c) {
             const int buf = (bA - c) & 1;
-            if (c > 0) load_image<I::BYTES>(img + (blk0 + c - 1) * I::BYTES, sImg[buf ^ 1], tid);
+            if (c > 0) load_image<I::BYTES>(irs, (uint32_t)(c - 1) * I::BYTES, sImg[buf ^ 1], tid);
             step(sImg[buf], c);
             wait_loads();
             __syncthreads();
