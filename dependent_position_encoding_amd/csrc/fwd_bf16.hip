@@ -398,14 +398,16 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
 #pragma unroll
             for (int e = 0; e < 8; ++e) Pb[kc][e] = (__bf16)S[kc >> 1][8 * (kc & 1) + e];
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t) {
+            const int row = 32 * t + col;
+            bf16x8 va[4];
 #pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
-                const int row = 32 * t + col;
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            for (int kc = 0; kc < 4; ++kc)
+                va[kc] = *reinterpret_cast<const bf16x8*>(
                     im + I::OFF_V + row * I::RB_V + swz_unit(row, 2 * kc + h, I::RB_V) * 16);
-                Ot[t] = mfma32(a, Pb[kc], Ot[t]);
-            }
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) Ot[t] = mfma32(va[kc], Pb[kc], Ot[t]);
+        }
     };
 
     // diagonal block of query block myb (image in buf), causal mask
@@ -487,6 +489,22 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
                 S[mt] = mfma32(a, ones, S[mt]);
             }
         }
+        // Qwork^T += (-E_c) Qwork^T: carry the queries across block c.  It
+        // needs only the bf16 Qwork already formed, so it is issued before the
+        // softmax and the matrix cores work while the vector ALUs do exp.
+        if (c > 0) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int row = 32 * t + col;
+                bf16x8 ea[NKC];
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc)
+                    ea[kc] = *reinterpret_cast<const bf16x8*>(
+                        im + I::OFF_E + row * I::RB_E + swz_unit(row, 2 * kc + h, I::RB_E) * 16);
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc) Qw[t] = mfma32(ea[kc], Qb[kc], Qw[t]);
+            }
+        }
         // online softmax with a lazily updated reference max
         float mx = -INFINITY;
 #pragma unroll
@@ -516,19 +534,6 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
             }
         l += rs + __shfl_xor(rs, 32, 64);
         pv(im);
-        // Qwork^T += (-E_c) Qwork^T: carry the queries across block c
-        if (c > 0) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int row = 32 * t + col;
-#pragma unroll
-                for (int kc = 0; kc < NKC; ++kc) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                        im + I::OFF_E + row * I::RB_E + swz_unit(row, 2 * kc + h, I::RB_E) * 16);
-                    Qw[t] = mfma32(a, Qb[kc], Qw[t]);
-                }
-            }
-        }
     };
 
     wait_loads();

@@ -176,3 +176,56 @@ def test_long_context_full_size():
 @pytest.mark.parametrize("k_dtype", [torch.bfloat16, torch.float32])
 def test_long_context_stress_full_size(k_dtype):
     _long_case(workloads.stress(workloads.CONFIGS["long"]), k_dtype, head_stride=4)
+
+
+def test_decode_steps_replayed_from_a_graph():
+    """The fused decode steps captured in a HIP graph and replayed (with eager
+    prefills in between) give exactly the eager results on every replay."""
+    pa = _pa()
+    wl = workloads.CONFIGS["fox"].replace(N=1, H=4, L=300)
+    steps = 6
+    x = workloads.make_inputs(wl, device="cpu", L=wl.L + steps)
+    g = {k: v.to(DEV) for k, v in x.items()}
+    L = wl.L
+    pre = {n: g[n][:, :, :L].contiguous() for n in g}
+    tok = {n: [g[n][:, :, t].contiguous() for t in range(L, L + steps)] for n in g}
+    cache = pa.Cache(1, 4, L + steps, wl.d, dtype=wl.dtype, gate=True, device=DEV)
+    outs = [(torch.empty(1, 4, wl.d, dtype=wl.dtype, device=DEV),
+             torch.empty(1, 4, dtype=torch.float32, device=DEV)) for _ in range(steps)]
+    dws = torch.empty(pa.decode_workspace_bytes(cache, L + steps), dtype=torch.uint8, device=DEV)
+    fws = torch.empty(pa.fwd_workspace_bytes(1, 4, L, wl.d, wl.dtype, with_cache=True),
+                      dtype=torch.uint8, device=DEV)
+
+    def prefill():
+        pa.fwd(pre["q"], pre["k"], pre["v"], pre["w"], pre["beta"], logf=pre["logf"],
+               scale=wl.scale, cache=cache, workspace=fws)
+
+    def loop():
+        for i in range(steps):
+            pa.decode_step(cache, L + i, *(tok[n][i] for n in ("q", "k", "v", "w", "beta", "logf")),
+                           scale=wl.scale, workspace=dws, out=outs[i])
+
+    print("case graph replay", flush=True)
+    prefill()
+    loop()
+    torch.cuda.synchronize()
+    ref = [(o.clone(), l.clone()) for o, l in outs]
+    ref_k = cache.kcache.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            loop()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        prefill()
+        for o, l in outs:
+            o.zero_()
+            l.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for (o, l), (ro, rl) in zip(outs, ref):
+            assert torch.equal(o, ro) and torch.equal(l, rl), f"replay {rep} differs"
+        assert torch.equal(cache.kcache, ref_k)
