@@ -82,8 +82,8 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     constexpr int DT = D / 32;                 // 32-wide tiles along d
     using I = Img<D>;
     // LDS roles over time (each buffer 64 x 64 float unless noted):
-    //   sX : G -> P -> image staging        sP : V (staging) -> X1 -> R^T
-    //   sMt: M^T -> Y^T                     sU : T -> U       sUt: scratch -> U^T
+    //   sX : G -> P                         sP : V (staging) -> X1 -> image staging
+    //   sMt: M^T                            sU : T -> Y^T     sUt: scratch -> U^T
     __shared__ __attribute__((aligned(16))) __bf16 sW[B * SB], sWt[D * SB], sQ[B * SB], sK[B * SB];
     __shared__ __attribute__((aligned(16))) float sU[B * SF], sUt[B * SF], sX[B * SF], sP[B * SF],
         sMt[B * SF];
@@ -218,101 +218,97 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         }
         __syncthreads();
     }
-    // U = T diag(beta), kept in both orientations
+    // U = T diag(beta); only U^T is kept (every product below reads U's columns)
     for (int e = tid; e < B * B; e += NTH) {
         const int i = e / B, j = e % B;
-        const float u = sU[i * SF + j] * sBeta[j];
-        sU[i * SF + j] = u;
-        sUt[j * SF + i] = u;
+        sUt[j * SF + i] = sU[i * SF + j] * sBeta[j];
     }
     __syncthreads();
 
-    // ---- 4. P = X1 U -> sX (waves 0-3); Q K^T tiles kept in registers by
-    //         waves 4-6 for the in-block logits
+    // ---- 4. P = X1 U -> sX (waves 0-3);  Y^T = W^T U (Y = U^T W) -> sU
+    //         (waves 4..);  Q K^T tiles kept in registers for the in-block
+    //         logits by the waves that will finish them
+    // Kright = K - (U M)^T W = K - M^T Y, and E = W^T Y, so Y serves both.
     f32x16 qk = zero16();
-    if (wave < 4) {
-        const int mt = wave >> 1, nt = wave & 1;
-        f32x16 acc = zero16();
-        if (!(mt == 0 && nt == 1)) tile_mm<B>(acc, sP, SF, sUt, SF, 32 * mt, 32 * nt, lane);
-        for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) { sX[i * SF + j] = a; });
-    } else if (wave < 7) {
-        const int t = wave - 4, mt = t == 0 ? 0 : 1, nt = t == 2 ? 1 : 0;
-        tile_mm<D>(qk, sQ, SB, sK, SB, 32 * mt, 32 * nt, lane);
+    {
+        if (wave < 4) {
+            const int mt = wave >> 1, nt = wave & 1;
+            f32x16 acc = zero16();
+            if (!(mt == 0 && nt == 1)) tile_mm<B>(acc, sP, SF, sUt, SF, 32 * mt, 32 * nt, lane);
+            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) { sX[i * SF + j] = a; });
+        } else if (wave < 4 + 2 * DT) {
+            const int t = wave - 4, mt = t / 2, nt = t % 2;
+            f32x16 acc = zero16();
+            tile_mm<B>(acc, sWt, SB, sUt, SF, 32 * mt, 32 * nt, lane);
+            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int y, int cc, float a) { sU[y * SF + cc] = a; });
+        }
+        // waves 5..7 (with D = 64: 5, 6, 7 hold no Y tile when D = 32) take Q K^T
+        const int qw = wave - 5;
+        if (qw >= 0 && qw < 3) {
+            const int mt = qw == 0 ? 0 : 1, nt = qw == 2 ? 1 : 0;
+            tile_mm<D>(qk, sQ, SB, sK, SB, 32 * mt, 32 * nt, lane);
+        }
     }
     __syncthreads();
 
-    // ---- 5. R^T = M^T U^T -> sP;  Qleft = Q - P W;  Dg = lower(QK^T) - P M
-    //         jobs: 0-3 R^T tiles, 4-6 Dg tiles (waves holding qk), then Qleft
+    // ---- 5. Dg = lower(QK^T) - P M (waves 5-7, holding qk); the other
+    //         jobs -- Qleft = Q - P W, Kright = K - M^T Y (staged as an image
+    //         in sP), -E = -W^T Y (staged after it) -- fill waves 0-4 first,
+    //         then all eight waves.
     {
-        constexpr int NQ = 2 * DT;
-        for (int job = wave; job < 7 + NQ; job += 8) {
+        char* stage = reinterpret_cast<char*>(sP);
+        constexpr int NQ = 2 * DT, NK = 2 * DT, NE = DT * DT, NO = NQ + NK + NE;
+        auto other = [&](int j) {
             f32x16 acc = zero16();
-            if (job < 4) {
-                const int mt = job >> 1, nt = job & 1;
-                if (!(mt == 1 && nt == 0)) tile_mm<B>(acc, sMt, SF, sU, SF, 32 * mt, 32 * nt, lane);
-                for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) { sP[i * SF + j] = a; });
-            } else if (job < 7) {
-                const int t = job - 4, mt = t == 0 ? 0 : 1, nt = t == 2 ? 1 : 0;
-                tile_mm<B>(acc, sX, SF, sMt, SF, 32 * mt, 32 * nt, lane);
-                float* dg = ws.dg + (size_t)blk * B * B;
-                const int h = lane >> 5, j = 32 * nt + (lane & 31);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = 32 * mt + crow(r, h);
-                    dg[i * B + j] = j <= i ? qk[r] - acc[r] : 0.f;
-                }
-            } else {
-                const int t = job - 7, mt = t / DT, nt = t % DT;
+            if (j < NQ) {
+                const int mt = j / DT, nt = j % DT;
                 tile_mm<B>(acc, sX, SF, sWt, SB, 32 * mt, 32 * nt, lane);
                 float* ql = ws.ql + (size_t)blk * B * D;
                 for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int x, float a) {
                     ql[i * D + x] = (float)sQ[i * SB + x] - a;
                 });
+            } else if (j < NQ + NK) {
+                // (M^T Y)[j][x] = sum_a Mt[j][a] Y[a][x];  B^T row x = Y^T row x
+                const int t = j - NQ, mt = t / DT, nt = t % DT;
+                tile_mm<B>(acc, sMt, SF, sU, SF, 32 * mt, 32 * nt, lane);
+                float* k32 = ws.k32 ? ws.k32 + (size_t)blk * B * D : nullptr;
+                for_tile(acc, 32 * mt, 32 * nt, lane, [&](int r, int x, float a) {
+                    const float val = (float)sK[r * SB + x] - a;
+                    *reinterpret_cast<__bf16*>(stage + I::OFF_K + img_off(r, swap23(x), I::RB_K)) =
+                        (__bf16)(val * kscale);
+                    if (k32) k32[r * D + x] = val;
+                });
+            } else {
+                const int t = j - NQ - NK, mt = t / DT, nt = t % DT;
+                tile_mm<B>(acc, sWt, SB, sU, SF, 32 * mt, 32 * nt, lane);
+                char* estage = stage + (I::OFF_E - I::OFF_V);
+                float* e32 = ws.e32 ? ws.e32 + (size_t)blk * D * D : nullptr;
+                for_tile(acc, 32 * mt, 32 * nt, lane, [&](int x, int y, float a) {
+                    *reinterpret_cast<__bf16*>(estage + img_off(x, swap23(y), I::RB_E)) = (__bf16)(-a);
+                    if (e32) e32[x * D + y] = a;
+                });
             }
-        }
-    }
-    __syncthreads();
-
-    // ---- 6. Kright = K - R^T W, staged as an image in sX (waves 0..);
-    //         Y^T = W^T U -> sMt (waves 4..)
-    {
-        char* stage = reinterpret_cast<char*>(sX);
-        if (wave < 2 * DT) {
-            const int mt = wave / DT, nt = wave % DT;
+        };
+        if (wave >= 5) {
+            const int t = wave - 5, mt = t == 0 ? 0 : 1, nt = t == 2 ? 1 : 0;
             f32x16 acc = zero16();
-            tile_mm<B>(acc, sP, SF, sWt, SB, 32 * mt, 32 * nt, lane);
-            float* k32 = ws.k32 ? ws.k32 + (size_t)blk * B * D : nullptr;
-            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int j, int x, float a) {
-                const float val = (float)sK[j * SB + x] - a;
-                *reinterpret_cast<__bf16*>(stage + I::OFF_K + img_off(j, swap23(x), I::RB_K)) =
-                    (__bf16)(val * kscale);
-                if (k32) k32[j * D + x] = val;
-            });
-        } else if (wave >= 4 && wave < 4 + 2 * DT) {
-            const int t = wave - 4, mt = t / 2, nt = t % 2;
-            f32x16 acc = zero16();
-            tile_mm<B>(acc, sWt, SB, sUt, SF, 32 * mt, 32 * nt, lane);
-            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int y, int cc, float a) { sMt[y * SF + cc] = a; });
+            tile_mm<B>(acc, sX, SF, sMt, SF, 32 * mt, 32 * nt, lane);
+            float* dg = ws.dg + (size_t)blk * B * B;
+            const int h = lane >> 5, j = 32 * nt + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = 32 * mt + crow(r, h);
+                dg[i * B + j] = j <= i ? qk[r] - acc[r] : 0.f;
+            }
+        } else {
+            other(wave);
         }
+        for (int j = 5 + wave; j < NO; j += 8) other(j);
     }
     __syncthreads();
-
-    // ---- 7. E = W^T Y; -E staged with the contracted index in operand order
-    if (wave < DT * DT) {
-        const int mt = wave / DT, nt = wave % DT;
-        f32x16 acc = zero16();
-        tile_mm<B>(acc, sWt, SB, sMt, SF, 32 * mt, 32 * nt, lane);
-        char* stage = reinterpret_cast<char*>(sX) + (I::OFF_E - I::OFF_V);
-        float* e32 = ws.e32 ? ws.e32 + (size_t)blk * D * D : nullptr;
-        for_tile(acc, 32 * mt, 32 * nt, lane, [&](int x, int y, float a) {
-            *reinterpret_cast<__bf16*>(stage + img_off(x, swap23(y), I::RB_E)) = (__bf16)(-a);
-            if (e32) e32[x * D + y] = a;
-        });
-    }
-    __syncthreads();
-    // ---- 8. Kright and -E images: LDS staging -> HBM with 16-byte stores
+    // ---- 6. Kright and -E images: LDS staging -> HBM with 16-byte stores
     {
-        const char* stage = reinterpret_cast<const char*>(sX);
+        const char* stage = reinterpret_cast<const char*>(sP);
         constexpr int KUN = (I::OFF_V - I::OFF_K) / 16, EUN = (I::OFF_G - I::OFF_E) / 16;
         static_assert((I::OFF_V - I::OFF_K) + (I::OFF_G - I::OFF_E) <= kB * kSF * 4, "staging");
         for (int u = tid; u < KUN + EUN; u += NTH) {
