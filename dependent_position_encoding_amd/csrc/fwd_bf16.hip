@@ -72,6 +72,41 @@ __device__ inline void for_tile(const f32x16& acc, int m0, int n0, int lane, F f
     for (int r = 0; r < 16; ++r) f(m0 + crow(r, h), col, acc[r]);
 }
 
+// A float32 matrix held in LDS as two bf16 matrices, hi = bf16(x) and
+// lo = bf16(x - hi) (about 16 significant bits together), split once by its
+// producer so that every consumer reads matrix-core operands directly.
+struct Split {
+    __bf16* hi;
+    __bf16* lo;
+};
+constexpr int kSplitBytes = 2 * kB * kSB * 2;   // one 64 x 64 split matrix
+
+__device__ inline Split split_at(char* buf) {
+    return {reinterpret_cast<__bf16*>(buf), reinterpret_cast<__bf16*>(buf + kB * kSB * 2)};
+}
+__device__ inline void put(const Split& m, int r, int c, float v) {
+    const __bf16 hi = (__bf16)v;
+    m.hi[r * kSB + c] = hi;
+    m.lo[r * kSB + c] = (__bf16)(v - (float)hi);
+}
+
+// acc += A[m0:+32, 0:K] * Bn[n0:+32, 0:K]^T over LDS bf16 operands; a split
+// operand contributes its lo part as well (lo * lo is dropped).
+template <int K, bool SA, bool SBL>
+__device__ inline void tile_mm_s(f32x16& acc, const __bf16* Ah, const __bf16* Al, const __bf16* Bh,
+                                 const __bf16* Bl, int m0, int n0, int lane) {
+    const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        const int ao = (m0 + r) * kSB + k0 + 8 * h, bo = (n0 + r) * kSB + k0 + 8 * h;
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(Ah + ao);
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(Bh + bo);
+        if constexpr (SBL) acc = mfma32(ah, *reinterpret_cast<const bf16x8*>(Bl + bo), acc);
+        if constexpr (SA) acc = mfma32(*reinterpret_cast<const bf16x8*>(Al + ao), bh, acc);
+        acc = mfma32(ah, bh, acc);
+    }
+}
+
 template <int D>
 __global__ void __launch_bounds__(512)
 precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -81,13 +116,22 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     constexpr int B = kB, SB = kSB, SF = kSF, UPR = D / 8, NTH = 512;
     constexpr int DT = D / 32;                 // 32-wide tiles along d
     using I = Img<D>;
-    // LDS roles over time (each buffer 64 x 64 float unless noted):
-    //   sX : G -> P                         sP : V (staging) -> X1 -> image staging
-    //   sMt: M^T                            sU : T -> Y^T     sUt: scratch -> U^T
+    // LDS (five 64 x 64 slots, each holding a float matrix or a split one):
+    //   bX : G (float) -> P (split)         bP : V (float staging) -> X1 (split)
+    //                                             -> image staging
+    //   bM : M^T (split)                    bU : T (float) -> Y^T (split)
+    //   bS : solve scratch (float) -> U^T (split)
     __shared__ __attribute__((aligned(16))) __bf16 sW[B * SB], sWt[D * SB], sQ[B * SB], sK[B * SB];
-    __shared__ __attribute__((aligned(16))) float sU[B * SF], sUt[B * SF], sX[B * SF], sP[B * SF],
-        sMt[B * SF];
+    __shared__ __attribute__((aligned(16))) char bX[kSplitBytes], bP[kSplitBytes], bM[kSplitBytes],
+        bU[kSplitBytes], bS[kSplitBytes];
     __shared__ float sBeta[B];
+    static_assert(kB * kSF * 4 <= kSplitBytes, "slot size");
+    float* fX = reinterpret_cast<float*>(bX);     // G
+    float* fP = reinterpret_cast<float*>(bP);     // V staging
+    float* fU = reinterpret_cast<float*>(bU);     // T
+    float* fS = reinterpret_cast<float*>(bS);     // solve scratch
+    const Split X1 = split_at(bP), P = split_at(bX), Mt = split_at(bM), Ut = split_at(bS),
+                Yt = split_at(bU);
 
     const int blk = blockIdx.x, slice = blk / nb, c = blk % nb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -115,10 +159,10 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             sWt[(x0 + e) * SB + r] = wv[e];
-            sP[r * SF + x0 + e] = (float)vv[e];
+            fP[r * SF + x0 + e] = (float)vv[e];
         }
     }
-    for (int e = tid; e < B * B; e += NTH) sU[(e / B) * SF + e % B] = 0.f;
+    for (int e = tid; e < B * B; e += NTH) fU[(e / B) * SF + e % B] = 0.f;
     if (tid < B) sBeta[tid] = row0 + tid < L ? beta[base + row0 + tid] : 0.f;
     if (wave == 7) {
         // in-block inclusive prefix sum of log f (one lane per token)
@@ -139,7 +183,7 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const int x = u / 8, s0 = (u % 8) * 8;
         bf16x8 pk;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pk[e] = (__bf16)sP[swap23(s0 + e) * SF + x];
+        for (int e = 0; e < 8; ++e) pk[e] = (__bf16)fP[swap23(s0 + e) * SF + x];
         *reinterpret_cast<bf16x8*>(img + I::OFF_V + img_off(x, s0, I::RB_V)) = pk;
     }
     if (wave < 3) {
@@ -147,14 +191,14 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         f32x16 acc = zero16();
         tile_mm<D>(acc, sW, SB, sW, SB, 32 * mt, 32 * nt, lane);
         for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) {
-            sX[i * SF + j] = i > j ? sBeta[i] * a : 0.f;
+            fX[i * SF + j] = i > j ? sBeta[i] * a : 0.f;
         });
     }
     __syncthreads();
 
     // ---- 3. T = (I + G)^{-1} on waves 0-3, blocked over 16 x 16 blocks;
-    //         meanwhile waves 4-7 form X1 = lower(Q W^T) -> sP and
-    //         M^T (M = strictLower(W K^T)) -> sMt, which do not need T.
+    //         meanwhile waves 4-7 form X1 = lower(Q W^T) and
+    //         M^T (M = strictLower(W K^T)), which do not need T.
     if (wave < 4) {
         // diagonal blocks by forward substitution, one column per lane
         if (lane < 16) {
@@ -162,11 +206,11 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             float t[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float s = 0.f;
+                float sum = 0.f;
 #pragma unroll
-                for (int kk = 0; kk < i; ++kk) s += sX[(o + i) * SF + o + kk] * t[kk];
-                t[i] = i < lane ? 0.f : (i == lane ? 1.f : -s);
-                sU[(o + i) * SF + o + lane] = t[i];
+                for (int kk = 0; kk < i; ++kk) sum += fX[(o + i) * SF + o + kk] * t[kk];
+                t[i] = i < lane ? 0.f : (i == lane ? 1.f : -sum);
+                fU[(o + i) * SF + o + lane] = t[i];
             }
         }
     } else {
@@ -174,7 +218,7 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         f32x16 acc = zero16();
         if (!(mt == 0 && nt == 1)) tile_mm<D>(acc, sQ, SB, sW, SB, 32 * mt, 32 * nt, lane);
         for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) {
-            sP[i * SF + j] = j <= i ? a : 0.f;
+            put(X1, i, j, j <= i ? a : 0.f);
         });
     }
     __syncthreads();
@@ -187,20 +231,20 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             for (int cb = bb; cb < a; ++cb) {
 #pragma unroll
                 for (int kk = 0; kk < 16; ++kk) {
-                    const float g = sX[(16 * a + r) * SF + 16 * cb + kk];
+                    const float g = fX[(16 * a + r) * SF + 16 * cb + kk];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] += g * sU[(16 * cb + kk) * SF + 16 * bb + c0 + e];
+                    for (int e = 0; e < 4; ++e) x[e] += g * fU[(16 * cb + kk) * SF + 16 * bb + c0 + e];
                 }
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sUt[(16 * a + r) * SF + 16 * bb + c0 + e] = x[e];
+            for (int e = 0; e < 4; ++e) fS[(16 * a + r) * SF + 16 * bb + c0 + e] = x[e];
         } else if (lev == 1 && wave >= 4) {
             const int t = wave - 4, mt = t >> 1, nt = t & 1;
             f32x16 acc = zero16();
             // M^T[j][b] = k_j . w_b for b > j
             if (!(mt == 1 && nt == 0)) tile_mm<D>(acc, sK, SB, sW, SB, 32 * mt, 32 * nt, lane);
             for_tile(acc, 32 * mt, 32 * nt, lane, [&](int j, int bcol, float a) {
-                sMt[j * SF + bcol] = bcol > j ? a : 0.f;
+                put(Mt, j, bcol, bcol > j ? a : 0.f);
             });
         }
         __syncthreads();
@@ -209,40 +253,39 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             float y[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 16; ++kk) {
-                const float t = sU[(16 * a + r) * SF + 16 * a + kk];
+                const float t = fU[(16 * a + r) * SF + 16 * a + kk];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] -= t * sUt[(16 * a + kk) * SF + 16 * bb + c0 + e];
+                for (int e = 0; e < 4; ++e) y[e] -= t * fS[(16 * a + kk) * SF + 16 * bb + c0 + e];
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sU[(16 * a + r) * SF + 16 * bb + c0 + e] = y[e];
+            for (int e = 0; e < 4; ++e) fU[(16 * a + r) * SF + 16 * bb + c0 + e] = y[e];
         }
         __syncthreads();
     }
-    // U = T diag(beta); only U^T is kept (every product below reads U's columns)
+    // U = T diag(beta), kept as U^T (every product below reads U's columns)
     for (int e = tid; e < B * B; e += NTH) {
         const int i = e / B, j = e % B;
-        sUt[j * SF + i] = sU[i * SF + j] * sBeta[j];
+        put(Ut, j, i, fU[i * SF + j] * sBeta[j]);
     }
     __syncthreads();
 
-    // ---- 4. P = X1 U -> sX (waves 0-3);  Y^T = W^T U (Y = U^T W) -> sU
-    //         (waves 4..);  Q K^T tiles kept in registers for the in-block
-    //         logits by the waves that will finish them
-    // Kright = K - (U M)^T W = K - M^T Y, and E = W^T Y, so Y serves both.
+    // ---- 4. P = X1 U (waves 0-3);  Y^T = W^T U, Y = U^T W (waves 4..);
+    //         Q K^T tiles kept in registers by waves 5-7 for the in-block
+    //         logits.  Kright = K - (U M)^T W = K - M^T Y and E = W^T Y.
     f32x16 qk = zero16();
     {
         if (wave < 4) {
             const int mt = wave >> 1, nt = wave & 1;
             f32x16 acc = zero16();
-            if (!(mt == 0 && nt == 1)) tile_mm<B>(acc, sP, SF, sUt, SF, 32 * mt, 32 * nt, lane);
-            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) { sX[i * SF + j] = a; });
+            if (!(mt == 0 && nt == 1))
+                tile_mm_s<B, true, true>(acc, X1.hi, X1.lo, Ut.hi, Ut.lo, 32 * mt, 32 * nt, lane);
+            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) { put(P, i, j, a); });
         } else if (wave < 4 + 2 * DT) {
             const int t = wave - 4, mt = t / 2, nt = t % 2;
             f32x16 acc = zero16();
-            tile_mm<B>(acc, sWt, SB, sUt, SF, 32 * mt, 32 * nt, lane);
-            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int y, int cc, float a) { sU[y * SF + cc] = a; });
+            tile_mm_s<B, false, true>(acc, sWt, nullptr, Ut.hi, Ut.lo, 32 * mt, 32 * nt, lane);
+            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int y, int cc, float a) { put(Yt, y, cc, a); });
         }
-        // waves 5..7 (with D = 64: 5, 6, 7 hold no Y tile when D = 32) take Q K^T
         const int qw = wave - 5;
         if (qw >= 0 && qw < 3) {
             const int mt = qw == 0 ? 0 : 1, nt = qw == 2 ? 1 : 0;
@@ -253,24 +296,25 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
     // ---- 5. Dg = lower(QK^T) - P M (waves 5-7, holding qk); the other
     //         jobs -- Qleft = Q - P W, Kright = K - M^T Y (staged as an image
-    //         in sP), -E = -W^T Y (staged after it) -- fill waves 0-4 first,
+    //         in bP), -E = -W^T Y (staged after it) -- fill waves 0-4 first,
     //         then all eight waves.
     {
-        char* stage = reinterpret_cast<char*>(sP);
+        char* stage = bP;
         constexpr int NQ = 2 * DT, NK = 2 * DT, NE = DT * DT, NO = NQ + NK + NE;
+        static_assert((I::OFF_V - I::OFF_K) + (I::OFF_G - I::OFF_E) <= kSplitBytes, "staging");
         auto other = [&](int j) {
             f32x16 acc = zero16();
             if (j < NQ) {
                 const int mt = j / DT, nt = j % DT;
-                tile_mm<B>(acc, sX, SF, sWt, SB, 32 * mt, 32 * nt, lane);
+                tile_mm_s<B, true, false>(acc, P.hi, P.lo, sWt, nullptr, 32 * mt, 32 * nt, lane);
                 float* ql = ws.ql + (size_t)blk * B * D;
                 for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int x, float a) {
                     ql[i * D + x] = (float)sQ[i * SB + x] - a;
                 });
             } else if (j < NQ + NK) {
-                // (M^T Y)[j][x] = sum_a Mt[j][a] Y[a][x];  B^T row x = Y^T row x
+                // (M^T Y)[r][x] = sum_a Mt[r][a] Y[a][x];  B^T row x = Y^T row x
                 const int t = j - NQ, mt = t / DT, nt = t % DT;
-                tile_mm<B>(acc, sMt, SF, sU, SF, 32 * mt, 32 * nt, lane);
+                tile_mm_s<B, true, true>(acc, Mt.hi, Mt.lo, Yt.hi, Yt.lo, 32 * mt, 32 * nt, lane);
                 float* k32 = ws.k32 ? ws.k32 + (size_t)blk * B * D : nullptr;
                 for_tile(acc, 32 * mt, 32 * nt, lane, [&](int r, int x, float a) {
                     const float val = (float)sK[r * SB + x] - a;
@@ -280,7 +324,7 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 });
             } else {
                 const int t = j - NQ - NK, mt = t / DT, nt = t % DT;
-                tile_mm<B>(acc, sWt, SB, sU, SF, 32 * mt, 32 * nt, lane);
+                tile_mm_s<B, false, true>(acc, sWt, nullptr, Yt.hi, Yt.lo, 32 * mt, 32 * nt, lane);
                 char* estage = stage + (I::OFF_E - I::OFF_V);
                 float* e32 = ws.e32 ? ws.e32 + (size_t)blk * D * D : nullptr;
                 for_tile(acc, 32 * mt, 32 * nt, lane, [&](int x, int y, float a) {
@@ -292,7 +336,7 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         if (wave >= 5) {
             const int t = wave - 5, mt = t == 0 ? 0 : 1, nt = t == 2 ? 1 : 0;
             f32x16 acc = zero16();
-            tile_mm<B>(acc, sX, SF, sMt, SF, 32 * mt, 32 * nt, lane);
+            tile_mm_s<B, true, true>(acc, P.hi, P.lo, Mt.hi, Mt.lo, 32 * mt, 32 * nt, lane);
             float* dg = ws.dg + (size_t)blk * B * B;
             const int h = lane >> 5, j = 32 * nt + (lane & 31);
 #pragma unroll
@@ -308,9 +352,8 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     __syncthreads();
     // ---- 6. Kright and -E images: LDS staging -> HBM with 16-byte stores
     {
-        const char* stage = reinterpret_cast<const char*>(sP);
+        const char* stage = bP;
         constexpr int KUN = (I::OFF_V - I::OFF_K) / 16, EUN = (I::OFF_G - I::OFF_E) / 16;
-        static_assert((I::OFF_V - I::OFF_K) + (I::OFF_G - I::OFF_E) <= kB * kSF * 4, "staging");
         for (int u = tid; u < KUN + EUN; u += NTH) {
             const int src = u < KUN ? u * 16 : (I::OFF_V - I::OFF_K) + (u - KUN) * 16;
             const int dst = u < KUN ? I::OFF_K + u * 16 : I::OFF_E + (u - KUN) * 16;
