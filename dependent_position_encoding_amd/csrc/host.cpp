@@ -53,8 +53,9 @@ path_status check_desc(const path_fwd_desc* d, bool need_L) {
         return fail(PATH_E_UNSUPPORTED, "bf16 inputs use block 64");
     if ((size_t)d->N * d->H * (need_L ? d->L : 1) * d->d > ((size_t)1 << 40))
         return fail(PATH_E_SHAPE, "problem too large");
-    if (need_L && d->L > (1 << 24))
-        return fail(PATH_E_SHAPE, "L must be at most 16777216");
+    // one slice's tile images must stay below 4 GiB (32-bit buffer offsets)
+    if (need_L && d->L > (1 << 23))
+        return fail(PATH_E_SHAPE, "L must be at most 8388608");
     return PATH_OK;
 }
 

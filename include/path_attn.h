@@ -32,7 +32,7 @@
  * - beta and log f are used as given: no clipping, no renormalisation of w.
  *   NaN and Inf propagate.  beta in [0, 2] is the meaningful range.
  * - Argument errors are reported synchronously, before anything is enqueued:
- *   null pointers, sizes < 1, unsupported d or dtype, pointers that are not
+ *   null pointers, sizes < 1 (or L > 8388608), unsupported d or dtype, pointers that are not
  *   16-byte aligned (4-byte for float32 arrays), a workspace smaller than the
  *   matching *_workspace() result, or a cache index beyond its capacity.
  *   A failed kernel launch returns PATH_E_LAUNCH.  Faults inside a kernel

@@ -46,7 +46,7 @@ FAKE = ctypes.c_void_p(1 << 20)     # never dereferenced: validation fails first
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(N=0), 2), (dict(L=0), 2), (dict(d=48), 4), (dict(d=128), 4),
+    (dict(N=0), 2), (dict(L=0), 2), (dict(L=(1 << 23) + 1), 2), (dict(d=48), 4), (dict(d=128), 4),
     (dict(dtype=7), 3), (dict(block=8), 4), (dict(block=32), 4),
 ])
 def test_fwd_rejects_bad_descriptions(kw, status):
