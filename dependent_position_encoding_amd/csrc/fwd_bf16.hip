@@ -496,12 +496,26 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
         for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
             for (int e = 0; e < 8; ++e) Qb[kc][e] = (__bf16)Qw[kc >> 1][8 * (kc & 1) + e];
-        // S^T = Kright_c . Qwork^T (already in log2 units), plus the gate's
-        // per-key term -gl_c * log2(e) as one more contraction group (hi + lo)
+        // S'^T = Kright_c . Qwork^T - m_ref (log2 units), where one more
+        // contraction group adds the gate's per-key term -gl_c * log2(e)
+        // (hi + lo against ones) and the per-query reference
+        // -(m - rowb) (hi + mid + lo, exact to fp32, against ones on the key
+        // side), so the softmax needs no per-score subtraction.
         const float* gimg = reinterpret_cast<const float*>(im + I::OFF_G);
-        bf16x8 ones;
+        const float nref = rowb - m;
+        bf16x8 qside;
+        {
+            const __bf16 r0 = (__bf16)nref;
+            const float t1 = nref - (float)r0;
+            const __bf16 r1 = (__bf16)t1;
+            const __bf16 r2 = (__bf16)(t1 - (float)r1);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ones[e] = (__bf16)((h == 0 && e < 2) ? 1.f : 0.f);
+            for (int e = 0; e < 8; ++e) qside[e] = (__bf16)0.f;
+            if (h == 0) {
+                qside[0] = (__bf16)1.f; qside[1] = (__bf16)1.f;
+                qside[2] = r0; qside[3] = r1; qside[4] = r2;
+            }
+        }
         bf16x8 ka[2][NKC];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -517,16 +531,19 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
             const int row = 32 * mt + col;
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) S[mt] = mfma32(ka[mt][kc], Qb[kc], S[mt]);
-            if (FOX) {
-                const float gb = -gimg[row] * kLog2e;
-                const __bf16 hi = (__bf16)gb;
-                const __bf16 lo = (__bf16)(gb - (float)hi);
-                bf16x8 a;
+            bf16x8 a;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) a[e] = (__bf16)0.f;
-                if (h == 0) { a[0] = hi; a[1] = lo; }
-                S[mt] = mfma32(a, ones, S[mt]);
+            for (int e = 0; e < 8; ++e) a[e] = (__bf16)0.f;
+            if (h == 0) {
+                if (FOX) {
+                    const float gb = -gimg[row] * kLog2e;
+                    const __bf16 hi = (__bf16)gb;
+                    a[0] = hi;
+                    a[1] = (__bf16)(gb - (float)hi);
+                }
+                a[2] = (__bf16)1.f; a[3] = (__bf16)1.f; a[4] = (__bf16)1.f;
             }
+            S[mt] = mfma32(a, qside, S[mt]);
         }
         // Qwork^T += (-E_c) Qwork^T: carry the queries across block c.  It
         // needs only the bf16 Qwork already formed, so it is issued before the
@@ -544,30 +561,34 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
                 for (int kc = 0; kc < NKC; ++kc) Qw[t] = mfma32(ea[kc], Qb[kc], Qw[t]);
             }
         }
-        // online softmax with a lazily updated reference max
+        // online softmax with a lazily updated reference max: S' is already
+        // relative to m; rescale only when a row's max exceeds it by 2^kTau
         float mx = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) + rowb;
-        if (__any(mx > m + kTau)) {
-            const float mn = fmaxf(m, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if (__any(mx > kTau)) {
+            const float up = fmaxf(mx, 0.f);
+            const float alpha = __builtin_amdgcn_exp2f(-up);
             l *= alpha;
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) Ot[t][r] *= alpha;
-            m = mn;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) S[mt][r] -= up;
+            m += up;
         }
-        const float mref = m - rowb;
         float rs = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(S[mt][r] - mref);
+                const float p = __builtin_amdgcn_exp2f(S[mt][r]);
                 S[mt][r] = p;
                 rs += p;
             }
