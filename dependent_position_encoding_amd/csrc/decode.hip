@@ -137,7 +137,7 @@ __global__ void kv_append_kernel(K* __restrict__ kc, T* __restrict__ vc,
 // per group), then one max / sum / weighted value sum over its keys.  Groups
 // are merged through LDS and the chunk's partial softmax state
 // (m, l, acc[D]) goes to part[slice][chunk].
-constexpr int kDecChunk = 256;
+constexpr int kDecChunk = 128;
 
 template <typename K, typename T, int D, bool FUSED>
 __global__ void __launch_bounds__(256)
@@ -273,7 +273,7 @@ decode_chunk_kernel(K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ 
 // lse = M + log l.  One 1024-thread block per slice: the chunk maxima and
 // sums are reduced in LDS, and 1024/D groups of D lanes each sum a strided
 // share of the chunks' accumulators (every load of a group in flight at once).
-constexpr int kCombineMaxChunks = 512;
+constexpr int kCombineMaxChunks = 1024;
 constexpr int kCombineThreads = 1024;
 
 template <typename T, int D>
