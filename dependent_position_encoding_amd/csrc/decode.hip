@@ -270,9 +270,10 @@ decode_chunk_kernel(K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ 
 }
 
 // Merge the chunk partials of one slice: o = sum acc_c e^{m_c - M} / l,
-// lse = M + log l.  One 1024-thread block per slice: the chunk maxima and
-// sums are reduced in LDS, and 1024/D groups of D lanes each sum a strided
-// share of the chunks' accumulators (every load of a group in flight at once).
+// lse = M + log l.  One 1024-thread block per slice, one chunk per thread for
+// the maxima and sums (wave shuffles, then one LDS exchange of the 16 wave
+// results), and 1024/D groups of D lanes each summing a strided share of the
+// chunks' accumulators (every load of a group in flight at once).
 constexpr int kCombineMaxChunks = 1024;
 constexpr int kCombineThreads = 1024;
 
@@ -280,31 +281,32 @@ template <typename T, int D>
 __global__ void __launch_bounds__(kCombineThreads)
 decode_combine_kernel(const float* __restrict__ part, int nch, T* __restrict__ o_t,
                       float* __restrict__ lse_t) {
-    constexpr int NTH = kCombineThreads, G = NTH / D;
-    __shared__ float red[NTH];
+    constexpr int NTH = kCombineThreads, NW = NTH / 64, G = NTH / D;
+    __shared__ float wmax[NW], wsum[NW];
     __shared__ float sf[kCombineMaxChunks];
     __shared__ float sacc[G][D];
-    const int slice = blockIdx.x, tid = threadIdx.x;
+    const int slice = blockIdx.x, tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
     const float* p = part + (size_t)slice * nch * (D + 2);
     const float mc = tid < nch ? p[(size_t)tid * (D + 2)] : -INFINITY;
     const float lc = tid < nch ? p[(size_t)tid * (D + 2) + 1] : 0.f;
-    red[tid] = mc;
+    float mx = mc;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    if (ln == 0) wmax[wv] = mx;
     __syncthreads();
-    for (int off = NTH / 2; off > 0; off >>= 1) {
-        if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
-        __syncthreads();
-    }
-    const float M = red[0];
-    __syncthreads();
+    float M = wmax[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) M = fmaxf(M, wmax[i]);
     const float f = (mc == -INFINITY) ? 0.f : __expf(mc - M);
     if (tid < nch) sf[tid] = f;
-    red[tid] = f * lc;
+    float sl = f * lc;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sl += __shfl_xor(sl, off, 64);
+    if (ln == 0) wsum[wv] = sl;
     __syncthreads();
-    for (int off = NTH / 2; off > 0; off >>= 1) {
-        if (tid < off) red[tid] += red[tid + off];
-        __syncthreads();
-    }
-    const float lt = red[0];
+    float lt = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) lt += wsum[i];
     const int g = tid / D, x = tid % D;
     float a = 0.f;
 #pragma unroll 8

@@ -363,6 +363,27 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 }
 
 // ---------------------------------------------------------------------------
+// Work order of the scan-shaped kernels: one workgroup per (slice, pair of
+// query blocks), pair p covering blocks nb-1-2p and nb-2-2p, so lower p means
+// more key blocks.  Slices are taken kSliceGroup at a time and, inside a
+// group, pairs heaviest first with the group's slices interleaved:
+//  - the workgroups resident at once share a few slices, so a key block's
+//    tile image, streamed by every pair to its left, is read from HBM about
+//    once and then hit in cache;
+//  - workgroups go to the XCDs round-robin and kSliceGroup is a multiple of 8,
+//    so all workgroups of a slice sit on one XCD and share its L2;
+//  - the long pairs start first and the short ones fill the tail.
+constexpr int kSliceGroup = 32;
+
+__device__ inline void pair_of(int nb, int& pair, int& slice) {
+    const int np = (nb + 1) / 2, nh = gridDim.x / np, span = kSliceGroup * np;
+    const int g = blockIdx.x / span, r = blockIdx.x % span;
+    const int sz = min(kSliceGroup, nh - g * kSliceGroup);
+    pair = r / sz;
+    slice = g * kSliceGroup + r % sz;
+}
+
+// ---------------------------------------------------------------------------
 // Direct HBM -> LDS copy of one tile image through a buffer resource: the
 // lanes of a wave fill 1 KB of LDS contiguously (16 bytes each), the image
 // offset travels in a scalar register and the lane offset is one VGPR, so the
@@ -371,16 +392,19 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 template <int BYTES>
 __device__ inline void load_image(__amdgpu_buffer_rsrc_t rsrc, uint32_t src_off, char* dst,
                                   int tid) {
-    constexpr int UNITS = BYTES / 16;
+    constexpr int UNITS = BYTES / 16, FULL = UNITS / 256, REM = UNITS % 256;
     // the wave index is uniform; saying so keeps the offsets in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    auto one = [&](int u0) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (__attribute__((address_space(3))) void*)(dst + u0 * 16), 16,
+            (uint32_t)lane * 16, src_off + (uint32_t)u0 * 16, 0, 0);
+    };
 #pragma unroll
-    for (int it = 0; it < (UNITS + 255) / 256; ++it) {
-        const int u0 = (it * 4 + wave) * 64;
-        if (u0 < UNITS && u0 + lane < UNITS)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc, (__attribute__((address_space(3))) void*)(dst + u0 * 16), 16,
-                (uint32_t)lane * 16, src_off + (uint32_t)u0 * 16, 0, 0);
+    for (int it = 0; it < FULL; ++it) one((it * 4 + wave) * 64);
+    if constexpr (REM > 0) {
+        const int u0 = FULL * 256 + wave * 64;
+        if (u0 + lane < UNITS) one(u0);
     }
 }
 
@@ -395,9 +419,8 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
     constexpr float kTau = 8.f;   // lazy rescale: keep a stale max while within 2^8
     __shared__ __attribute__((aligned(16))) char sImg[2][I::BYTES];
 
-    const int NH = gridDim.x / ((nb + 1) / 2);
-    const int pair = (int)(blockIdx.x / NH);
-    const int slice = blockIdx.x % NH;
+    int pair, slice;
+    pair_of(nb, pair, slice);
     const int bA = nb - 1 - 2 * pair, bB = bA - 1;          // bB may be -1
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
     const int col = lane & 31;
@@ -429,7 +452,8 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
         if (FOX) gq = ws.gl[bq * B + qloc] * kLog2e;
     }
 
-    // P.V for the current S (already exponentiated), from the V^T image
+    // P.V for the current S (already exponentiated), from the V^T image;
+    // returns this lane's share of the row sum of the bf16 P it used
     auto pv = [&](const char* im) {
         bf16x8 Pb[4];
 #pragma unroll
@@ -447,6 +471,7 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) Ot[t] = mfma32(va[kc], Pb[kc], Ot[t]);
         }
+        return sum_bf16x32(Pb);
     };
 
     // diagonal block of query block myb (image in buf), causal mask
@@ -472,19 +497,13 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
                     mx = fmaxf(mx, sv);
                 }
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = pair_max(mx);
         m = mx;
-        float rs = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(S[mt][r] - m);
-                S[mt][r] = p;
-                rs += p;
-            }
-        l = rs + __shfl_xor(rs, 32, 64);
-        pv(im);
+            for (int r = 0; r < 16; ++r) S[mt][r] = __builtin_amdgcn_exp2f(S[mt][r] - m);
+        l = pv(im);   // this half's keys only; the halves are added at the end
     };
 
     // one scan step against key block c (image in buf)
@@ -568,7 +587,7 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = pair_max(mx);
         if (__any(mx > kTau)) {
             const float up = fmaxf(mx, 0.f);
             const float alpha = __builtin_amdgcn_exp2f(-up);
@@ -583,17 +602,11 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
                 for (int r = 0; r < 16; ++r) S[mt][r] -= up;
             m += up;
         }
-        float rs = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(S[mt][r]);
-                S[mt][r] = p;
-                rs += p;
-            }
-        l += rs + __shfl_xor(rs, 32, 64);
-        pv(im);
+            for (int r = 0; r < 16; ++r) S[mt][r] = __builtin_amdgcn_exp2f(S[mt][r]);
+        l += pv(im);
     };
 
     wait_loads();
@@ -618,6 +631,7 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
         }
     }
 
+    l = pair_sum(l);   // both halves' keys (all lanes take part in the exchange)
     const int pos = myb * B + qloc;
     if (myb >= 0 && pos < L) {
         const float inv = 1.f / l;
@@ -660,9 +674,8 @@ causal_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     constexpr float kTau = 8.f;
     __shared__ __attribute__((aligned(16))) char sImg[2][I::BYTES];
 
-    const int NH = gridDim.x / ((nb + 1) / 2);
-    const int pair = (int)(blockIdx.x / NH);
-    const int slice = blockIdx.x % NH;
+    int pair, slice;
+    pair_of(nb, pair, slice);
     const int bA = nb - 1 - 2 * pair, bB = bA - 1;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
     const int col = lane & 31;
@@ -750,6 +763,7 @@ causal_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                     im + I::OFF_V + row * I::RB_V + swz_unit(row, 2 * kc + h, I::RB_V) * 16);
                 Ot[t] = mfma32(a, Pb[kc], Ot[t]);
             }
+        return sum_bf16x32(Pb);
     };
     auto diag = [&](const char* im) {
         scores(im);
@@ -762,18 +776,12 @@ causal_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 if (key > qloc) S[mt][r] = -INFINITY;
                 mx = fmaxf(mx, S[mt][r]);
             }
-        m = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        float rs = 0.f;
+        m = pair_max(mx);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(S[mt][r] - m);
-                S[mt][r] = p;
-                rs += p;
-            }
-        l = rs + __shfl_xor(rs, 32, 64);
-        pv(im);
+            for (int r = 0; r < 16; ++r) S[mt][r] = __builtin_amdgcn_exp2f(S[mt][r] - m);
+        l = pv(im);   // this half's keys only; the halves are added at the end
     };
     auto step = [&](const char* im) {
         scores(im);
@@ -782,7 +790,7 @@ causal_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = pair_max(mx);
         if (__any(mx > m + kTau)) {
             const float mn = fmaxf(m, mx);
             const float alpha = __builtin_amdgcn_exp2f(m - mn);
@@ -793,17 +801,11 @@ causal_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 for (int r = 0; r < 16; ++r) Ot[t][r] *= alpha;
             m = mn;
         }
-        float rs = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(S[mt][r] - m);
-                S[mt][r] = p;
-                rs += p;
-            }
-        l += rs + __shfl_xor(rs, 32, 64);
-        pv(im);
+            for (int r = 0; r < 16; ++r) S[mt][r] = __builtin_amdgcn_exp2f(S[mt][r] - m);
+        l += pv(im);
     };
 
     fetch(bA);
@@ -826,6 +828,7 @@ causal_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         }
     }
 
+    l = pair_sum(l);   // both halves' keys (all lanes take part in the exchange)
     const int pos = myb * B + qloc;
     if (myb >= 0 && pos < L) {
         const float inv = 1.f / l;

@@ -106,6 +106,38 @@ __device__ inline void tile_mm_f32(f32x16& acc, const float* A, int lda, const f
     }
 }
 
+// The two halves of a wave hold different key rows of the same query
+// column (C layout).  v_permlane32_swap on two copies of x leaves x[lane] in
+// one result and x[lane ^ 32] in the other, so these reduce over the pair
+// without going through LDS.
+__device__ inline float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum of the 32 bf16 probabilities a lane feeds to P.V (four bf16x8 operand
+// registers), by paired dot products against ones with fp32 accumulation:
+// the normaliser then adds exactly the weights the value product uses.
+__device__ inline float sum_bf16x32(const bf16x8 (&p)[4]) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+    float s[2] = {0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const bf16x2 two = {p[kc][e], p[kc][e + 1]};
+            s[kc & 1] = __builtin_amdgcn_fdot2_f32_bf16(two, one, s[kc & 1], false);
+        }
+    return s[0] + s[1];
+}
+
 __device__ inline f32x16 zero16() {
     f32x16 z;
 #pragma unroll
