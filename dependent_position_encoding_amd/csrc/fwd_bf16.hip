@@ -107,66 +107,95 @@ __device__ inline void tile_mm_s(f32x16& acc, const __bf16* Ah, const __bf16* Al
     }
 }
 
+// 32 rows [r0, r0 + 32) of a row-major bf16 block with D columns in global
+// memory, as the D/16 k-steps of an MFMA operand (lane: row r0 + l % 32,
+// columns 16 ks + 8h .. +7); rows at or beyond nvalid read as zero.
 template <int D>
-__global__ void __launch_bounds__(512)
+__device__ inline void ld_rows(bf16x8 (&o)[D / 16], const __bf16* base, int r0, int nvalid,
+                               int lane) {
+    const int r = r0 + (lane & 31), h = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        if (r < nvalid) {
+            o[ks] = *reinterpret_cast<const bf16x8*>(base + (size_t)r * D + 16 * ks + 8 * h);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[ks][e] = (__bf16)0.f;
+        }
+    }
+}
+
+template <int NK>
+__device__ inline void mm_regs(f32x16& acc, const bf16x8 (&a)[NK], const bf16x8 (&b)[NK]) {
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) acc = mfma32(a[ks], b[ks], acc);
+}
+
+// One 512-thread workgroup (8 waves) per 64-token block, 64.8 KB of LDS so
+// that two workgroups share a CU and one's barriers and HBM waits overlap
+// the other's work.  Products over the head dimension read Q, K and W
+// straight from HBM as matrix-core operands; products over tokens read LDS.
+template <int D>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
 precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                     const __bf16* __restrict__ v, const __bf16* __restrict__ w,
                     const float* __restrict__ beta, const float* __restrict__ logf,
                     int L, int nb, float kscale, FwdWs ws) {
-    constexpr int B = kB, SB = kSB, SF = kSF, UPR = D / 8, NTH = 512;
+    constexpr int B = kB, SB = kSB, SF = kSF, UPR = D / 8, NTH = 512, NKS = D / 16;
     constexpr int DT = D / 32;                 // 32-wide tiles along d
     using I = Img<D>;
-    // LDS (five 64 x 64 slots, each holding a float matrix or a split one):
-    //   bX : G (float) -> P (split)         bP : V (float staging) -> X1 (split)
-    //                                             -> image staging
-    //   bM : M^T (split)                    bU : T (float) -> Y^T (split)
-    //   bS : solve scratch (float) -> U^T (split)
-    __shared__ __attribute__((aligned(16))) __bf16 sW[B * SB], sWt[D * SB], sQ[B * SB], sK[B * SB];
-    __shared__ __attribute__((aligned(16))) char bX[kSplitBytes], bP[kSplitBytes], bM[kSplitBytes],
-        bU[kSplitBytes], bS[kSplitBytes];
+    // W^T and three 64 x 64 slots, each holding a float matrix or a split one:
+    //   s0 : G (float)            -> X1 (split)    -> P (split)
+    //   s1 : T (float)            -> U^T (split)   -> Y^T (split)
+    //   s2 : V (float staging)    -> solve scratch -> M^T (split)
+    __shared__ __attribute__((aligned(16))) __bf16 sWt[D * SB];
+    __shared__ __attribute__((aligned(16))) char s0[kSplitBytes], s1[kSplitBytes], s2[kSplitBytes];
     __shared__ float sBeta[B];
     static_assert(kB * kSF * 4 <= kSplitBytes, "slot size");
-    float* fX = reinterpret_cast<float*>(bX);     // G
-    float* fP = reinterpret_cast<float*>(bP);     // V staging
-    float* fU = reinterpret_cast<float*>(bU);     // T
-    float* fS = reinterpret_cast<float*>(bS);     // solve scratch
-    const Split X1 = split_at(bP), P = split_at(bX), Mt = split_at(bM), Ut = split_at(bS),
-                Yt = split_at(bU);
+    float* fG = reinterpret_cast<float*>(s0);
+    float* fT = reinterpret_cast<float*>(s1);
+    float* fV = reinterpret_cast<float*>(s2);
+    float* fS = reinterpret_cast<float*>(s2);
+    const Split X1 = split_at(s0), P = split_at(s0), Ut = split_at(s1), Yt = split_at(s1),
+                Mt = split_at(s2);
 
     const int blk = blockIdx.x, slice = blk / nb, c = blk % nb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const size_t base = (size_t)slice * L;
-    const int row0 = c * B;
+    const int row0 = c * B, nvalid = min(B, L - row0);
+    const size_t eoff = (base + row0) * D;       // the block's first element
+    const __bf16 *qb = q + eoff, *kb = k + eoff, *wb = w + eoff, *vb = v + eoff;
     char* img = static_cast<char*>(ws.img) + (size_t)blk * I::BYTES;
 
-    // ---- 1. stage W, Q, K (and W^T) as bf16, V as float; zero T ----------
+    // ---- 1. W^T and V (as float) into LDS, beta, T = 0, gate cumsum; waves
+    //         0-2 fetch their W operand rows for G meanwhile
+    const int gmt = wave == 0 ? 0 : 1, gnt = wave == 2 ? 1 : 0;   // G's lower tiles
+    bf16x8 ga[NKS], gb[NKS];
+    if (wave < 3) {
+        ld_rows<D>(ga, wb, 32 * gmt, nvalid, lane);
+        ld_rows<D>(gb, wb, 32 * gnt, nvalid, lane);
+    }
     for (int u = tid; u < B * UPR; u += NTH) {
-        const int r = u / UPR, x0 = (u % UPR) * 8, pos = row0 + r;
-        bf16x8 wv, qv, kv, vv;
-        if (pos < L) {
-            const size_t g = (base + pos) * D + x0;
-            wv = *reinterpret_cast<const bf16x8*>(w + g);
-            qv = *reinterpret_cast<const bf16x8*>(q + g);
-            kv = *reinterpret_cast<const bf16x8*>(k + g);
-            vv = *reinterpret_cast<const bf16x8*>(v + g);
+        const int r = u / UPR, x0 = (u % UPR) * 8;
+        bf16x8 wv, vv;
+        if (r < nvalid) {
+            wv = *reinterpret_cast<const bf16x8*>(wb + r * D + x0);
+            vv = *reinterpret_cast<const bf16x8*>(vb + r * D + x0);
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) wv[e] = qv[e] = kv[e] = vv[e] = (__bf16)0.f;
+            for (int e = 0; e < 8; ++e) wv[e] = vv[e] = (__bf16)0.f;
         }
-        *reinterpret_cast<bf16x8*>(sW + r * SB + x0) = wv;
-        *reinterpret_cast<bf16x8*>(sQ + r * SB + x0) = qv;
-        *reinterpret_cast<bf16x8*>(sK + r * SB + x0) = kv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             sWt[(x0 + e) * SB + r] = wv[e];
-            fP[r * SF + x0 + e] = (float)vv[e];
+            fV[r * SF + x0 + e] = (float)vv[e];
         }
     }
-    for (int e = tid; e < B * B; e += NTH) fU[(e / B) * SF + e % B] = 0.f;
-    if (tid < B) sBeta[tid] = row0 + tid < L ? beta[base + row0 + tid] : 0.f;
+    for (int e = tid; e < B * B; e += NTH) fT[(e / B) * SF + e % B] = 0.f;
+    if (tid < B) sBeta[tid] = tid < nvalid ? beta[base + row0 + tid] : 0.f;
     if (wave == 7) {
         // in-block inclusive prefix sum of log f (one lane per token)
-        float acc = (logf && row0 + lane < L) ? logf[base + row0 + lane] : 0.f;
+        float acc = (logf && lane < nvalid) ? logf[base + row0 + lane] : 0.f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float up = __shfl_up(acc, off, 64);
@@ -180,25 +209,26 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
     // ---- 2. V^T with keys in operand order; G = diag(beta) strictLower(WW^T)
     for (int u = tid; u < D * 8; u += NTH) {
-        const int x = u / 8, s0 = (u % 8) * 8;
+        const int x = u / 8, s0i = (u % 8) * 8;
         bf16x8 pk;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pk[e] = (__bf16)fP[swap23(s0 + e) * SF + x];
-        *reinterpret_cast<bf16x8*>(img + I::OFF_V + img_off(x, s0, I::RB_V)) = pk;
+        for (int e = 0; e < 8; ++e) pk[e] = (__bf16)fV[swap23(s0i + e) * SF + x];
+        *reinterpret_cast<bf16x8*>(img + I::OFF_V + img_off(x, s0i, I::RB_V)) = pk;
     }
     if (wave < 3) {
-        const int mt = wave == 0 ? 0 : 1, nt = wave == 2 ? 1 : 0;
         f32x16 acc = zero16();
-        tile_mm<D>(acc, sW, SB, sW, SB, 32 * mt, 32 * nt, lane);
-        for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) {
-            fX[i * SF + j] = i > j ? sBeta[i] * a : 0.f;
+        mm_regs(acc, ga, gb);
+        for_tile(acc, 32 * gmt, 32 * gnt, lane, [&](int i, int j, float a) {
+            fG[i * SF + j] = i > j ? sBeta[i] * a : 0.f;
         });
     }
     __syncthreads();
 
     // ---- 3. T = (I + G)^{-1} on waves 0-3, blocked over 16 x 16 blocks;
-    //         meanwhile waves 4-7 form X1 = lower(Q W^T) and
-    //         M^T (M = strictLower(W K^T)), which do not need T.
+    //         meanwhile waves 4-7 form X1 = lower(Q W^T) and M^T
+    //         (M = strictLower(W K^T)) in registers: neither needs T.
+    const int xt = wave - 4, xmt = xt >> 1, xnt = xt & 1;
+    f32x16 x1r = zero16(), mtr = zero16();
     if (wave < 4) {
         // diagonal blocks by forward substitution, one column per lane
         if (lane < 16) {
@@ -208,18 +238,16 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             for (int i = 0; i < 16; ++i) {
                 float sum = 0.f;
 #pragma unroll
-                for (int kk = 0; kk < i; ++kk) sum += fX[(o + i) * SF + o + kk] * t[kk];
+                for (int kk = 0; kk < i; ++kk) sum += fG[(o + i) * SF + o + kk] * t[kk];
                 t[i] = i < lane ? 0.f : (i == lane ? 1.f : -sum);
-                fU[(o + i) * SF + o + lane] = t[i];
+                fT[(o + i) * SF + o + lane] = t[i];
             }
         }
-    } else {
-        const int t = wave - 4, mt = t >> 1, nt = t & 1;
-        f32x16 acc = zero16();
-        if (!(mt == 0 && nt == 1)) tile_mm<D>(acc, sQ, SB, sW, SB, 32 * mt, 32 * nt, lane);
-        for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) {
-            put(X1, i, j, j <= i ? a : 0.f);
-        });
+    } else if (!(xmt == 0 && xnt == 1)) {
+        bf16x8 a[NKS], b[NKS];
+        ld_rows<D>(a, qb, 32 * xmt, nvalid, lane);
+        ld_rows<D>(b, wb, 32 * xnt, nvalid, lane);
+        mm_regs(x1r, a, b);
     }
     __syncthreads();
     // off-diagonal blocks: T_ab = -T_aa sum_{c=b}^{a-1} G_ac T_cb, by distance
@@ -231,21 +259,19 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             for (int cb = bb; cb < a; ++cb) {
 #pragma unroll
                 for (int kk = 0; kk < 16; ++kk) {
-                    const float g = fX[(16 * a + r) * SF + 16 * cb + kk];
+                    const float g = fG[(16 * a + r) * SF + 16 * cb + kk];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] += g * fU[(16 * cb + kk) * SF + 16 * bb + c0 + e];
+                    for (int e = 0; e < 4; ++e) x[e] += g * fT[(16 * cb + kk) * SF + 16 * bb + c0 + e];
                 }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) fS[(16 * a + r) * SF + 16 * bb + c0 + e] = x[e];
-        } else if (lev == 1 && wave >= 4) {
-            const int t = wave - 4, mt = t >> 1, nt = t & 1;
-            f32x16 acc = zero16();
+        } else if (lev == 1 && wave >= 4 && !(xmt == 1 && xnt == 0)) {
             // M^T[j][b] = k_j . w_b for b > j
-            if (!(mt == 1 && nt == 0)) tile_mm<D>(acc, sK, SB, sW, SB, 32 * mt, 32 * nt, lane);
-            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int j, int bcol, float a) {
-                put(Mt, j, bcol, bcol > j ? a : 0.f);
-            });
+            bf16x8 a[NKS], b[NKS];
+            ld_rows<D>(a, kb, 32 * xmt, nvalid, lane);
+            ld_rows<D>(b, wb, 32 * xnt, nvalid, lane);
+            mm_regs(mtr, a, b);
         }
         __syncthreads();
         if (wave < njobs) {
@@ -253,113 +279,114 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             float y[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 16; ++kk) {
-                const float t = fU[(16 * a + r) * SF + 16 * a + kk];
+                const float t = fT[(16 * a + r) * SF + 16 * a + kk];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) y[e] -= t * fS[(16 * a + kk) * SF + 16 * bb + c0 + e];
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) fU[(16 * a + r) * SF + 16 * bb + c0 + e] = y[e];
+            for (int e = 0; e < 4; ++e) fT[(16 * a + r) * SF + 16 * bb + c0 + e] = y[e];
         }
         __syncthreads();
     }
-    // U = T diag(beta), kept as U^T (every product below reads U's columns)
-    for (int e = tid; e < B * B; e += NTH) {
-        const int i = e / B, j = e % B;
-        put(Ut, j, i, fU[i * SF + j] * sBeta[j]);
+
+    // ---- 4. X1 and M^T to LDS (G and the scratch are dead); U = T diag(beta)
+    //         read into registers, then stored as U^T over T
+    float tv[B * B / NTH];
+#pragma unroll
+    for (int e = 0; e < B * B / NTH; ++e) {
+        const int idx = tid + NTH * e, i = idx / B, j = idx % B;
+        tv[e] = fT[i * SF + j] * sBeta[j];
+    }
+    if (wave >= 4) {
+        for_tile(x1r, 32 * xmt, 32 * xnt, lane, [&](int i, int j, float a) {
+            put(X1, i, j, j <= i ? a : 0.f);
+        });
+        for_tile(mtr, 32 * xmt, 32 * xnt, lane, [&](int j, int bcol, float a) {
+            put(Mt, j, bcol, bcol > j ? a : 0.f);
+        });
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < B * B / NTH; ++e) {
+        const int idx = tid + NTH * e, i = idx / B, j = idx % B;
+        put(Ut, j, i, tv[e]);
     }
     __syncthreads();
 
-    // ---- 4. P = X1 U (waves 0-3);  Y^T = W^T U, Y = U^T W (waves 4..);
-    //         Q K^T tiles kept in registers by waves 5-7 for the in-block
-    //         logits.  Kright = K - (U M)^T W = K - M^T Y and E = W^T Y.
-    f32x16 qk = zero16();
+    // ---- 5. P = X1 U (waves 0-3) and Y^T = W^T U (waves 4..), Y = U^T W;
+    //         Kright = K - (U M)^T W = K - M^T Y and E = W^T Y below.
     {
+        f32x16 acc = zero16();
+        const int mt = wave < 4 ? wave >> 1 : (wave - 4) / 2;
+        const int nt = wave < 4 ? wave & 1 : (wave - 4) % 2;
         if (wave < 4) {
-            const int mt = wave >> 1, nt = wave & 1;
-            f32x16 acc = zero16();
             if (!(mt == 0 && nt == 1))
                 tile_mm_s<B, true, true>(acc, X1.hi, X1.lo, Ut.hi, Ut.lo, 32 * mt, 32 * nt, lane);
-            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) { put(P, i, j, a); });
         } else if (wave < 4 + 2 * DT) {
-            const int t = wave - 4, mt = t / 2, nt = t % 2;
-            f32x16 acc = zero16();
             tile_mm_s<B, false, true>(acc, sWt, nullptr, Ut.hi, Ut.lo, 32 * mt, 32 * nt, lane);
+        }
+        __syncthreads();
+        if (wave < 4)
+            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) { put(P, i, j, a); });
+        else if (wave < 4 + 2 * DT)
             for_tile(acc, 32 * mt, 32 * nt, lane, [&](int y, int cc, float a) { put(Yt, y, cc, a); });
-        }
-        const int qw = wave - 5;
-        if (qw >= 0 && qw < 3) {
-            const int mt = qw == 0 ? 0 : 1, nt = qw == 2 ? 1 : 0;
-            tile_mm<D>(qk, sQ, SB, sK, SB, 32 * mt, 32 * nt, lane);
-        }
     }
     __syncthreads();
 
-    // ---- 5. Dg = lower(QK^T) - P M (waves 5-7, holding qk); the other
-    //         jobs -- Qleft = Q - P W, Kright = K - M^T Y (staged as an image
-    //         in bP), -E = -W^T Y (staged after it) -- fill waves 0-4 first,
-    //         then all eight waves.
-    {
-        char* stage = bP;
-        constexpr int NQ = 2 * DT, NK = 2 * DT, NE = DT * DT, NO = NQ + NK + NE;
-        static_assert((I::OFF_V - I::OFF_K) + (I::OFF_G - I::OFF_E) <= kSplitBytes, "staging");
-        auto other = [&](int j) {
-            f32x16 acc = zero16();
-            if (j < NQ) {
-                const int mt = j / DT, nt = j % DT;
-                tile_mm_s<B, true, false>(acc, P.hi, P.lo, sWt, nullptr, 32 * mt, 32 * nt, lane);
-                float* ql = ws.ql + (size_t)blk * B * D;
-                for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int x, float a) {
-                    ql[i * D + x] = (float)sQ[i * SB + x] - a;
-                });
-            } else if (j < NQ + NK) {
-                // (M^T Y)[r][x] = sum_a Mt[r][a] Y[a][x];  B^T row x = Y^T row x
-                const int t = j - NQ, mt = t / DT, nt = t % DT;
-                tile_mm_s<B, true, true>(acc, Mt.hi, Mt.lo, Yt.hi, Yt.lo, 32 * mt, 32 * nt, lane);
-                float* k32 = ws.k32 ? ws.k32 + (size_t)blk * B * D : nullptr;
-                for_tile(acc, 32 * mt, 32 * nt, lane, [&](int r, int x, float a) {
-                    const float val = (float)sK[r * SB + x] - a;
-                    *reinterpret_cast<__bf16*>(stage + I::OFF_K + img_off(r, swap23(x), I::RB_K)) =
-                        (__bf16)(val * kscale);
-                    if (k32) k32[r * D + x] = val;
-                });
-            } else {
-                const int t = j - NQ - NK, mt = t / DT, nt = t % DT;
-                tile_mm_s<B, false, true>(acc, sWt, nullptr, Yt.hi, Yt.lo, 32 * mt, 32 * nt, lane);
-                char* estage = stage + (I::OFF_E - I::OFF_V);
-                float* e32 = ws.e32 ? ws.e32 + (size_t)blk * D * D : nullptr;
-                for_tile(acc, 32 * mt, 32 * nt, lane, [&](int x, int y, float a) {
-                    *reinterpret_cast<__bf16*>(estage + img_off(x, swap23(y), I::RB_E)) = (__bf16)(-a);
-                    if (e32) e32[x * D + y] = a;
-                });
-            }
-        };
-        if (wave >= 5) {
-            const int t = wave - 5, mt = t == 0 ? 0 : 1, nt = t == 2 ? 1 : 0;
-            f32x16 acc = zero16();
+    // ---- 6. outputs, stored straight to HBM, heaviest jobs first:
+    //         Dg = lower(Q K^T) - P M (in-block logits), Kright = K - M^T Y
+    //         (image, scaled, and its fp32 copy), Qleft = Q - P W,
+    //         -E = -W^T Y (image, and E in fp32)
+    constexpr int ND = 3, NK = 2 * DT, NQ = 2 * DT, NE = DT * DT, NJ = ND + NK + NQ + NE;
+    auto job = [&](int j) {
+        f32x16 acc = zero16();
+        if (j < ND) {
+            const int mt = j == 0 ? 0 : 1, nt = j == 2 ? 1 : 0;
+            f32x16 qk = zero16();
+            bf16x8 a[NKS], b[NKS];
+            ld_rows<D>(a, qb, 32 * mt, nvalid, lane);
+            ld_rows<D>(b, kb, 32 * nt, nvalid, lane);
+            mm_regs(qk, a, b);
             tile_mm_s<B, true, true>(acc, P.hi, P.lo, Mt.hi, Mt.lo, 32 * mt, 32 * nt, lane);
             float* dg = ws.dg + (size_t)blk * B * B;
-            const int h = lane >> 5, j = 32 * nt + (lane & 31);
+            const int h = lane >> 5, jj = 32 * nt + (lane & 31);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int i = 32 * mt + crow(r, h);
-                dg[i * B + j] = j <= i ? qk[r] - acc[r] : 0.f;
+                dg[i * B + jj] = jj <= i ? qk[r] - acc[r] : 0.f;
             }
+        } else if (j < ND + NK) {
+            // (M^T Y)[r][x] = sum_a Mt[r][a] Y[a][x];  B^T row x = Y^T row x
+            const int t = j - ND, mt = t / DT, nt = t % DT;
+            tile_mm_s<B, true, true>(acc, Mt.hi, Mt.lo, Yt.hi, Yt.lo, 32 * mt, 32 * nt, lane);
+            float* k32 = ws.k32 ? ws.k32 + (size_t)blk * B * D : nullptr;
+            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int r, int x, float a) {
+                const float kv = r < nvalid ? (float)kb[r * D + x] : 0.f;
+                const float val = kv - a;
+                *reinterpret_cast<__bf16*>(img + I::OFF_K + img_off(r, swap23(x), I::RB_K)) =
+                    (__bf16)(val * kscale);
+                if (k32) k32[r * D + x] = val;
+            });
+        } else if (j < ND + NK + NQ) {
+            const int t = j - ND - NK, mt = t / DT, nt = t % DT;
+            tile_mm_s<B, true, false>(acc, P.hi, P.lo, sWt, nullptr, 32 * mt, 32 * nt, lane);
+            float* ql = ws.ql + (size_t)blk * B * D;
+            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int x, float a) {
+                const float qv = i < nvalid ? (float)qb[i * D + x] : 0.f;
+                ql[i * D + x] = qv - a;
+            });
         } else {
-            other(wave);
+            const int t = j - ND - NK - NQ, mt = t / DT, nt = t % DT;
+            tile_mm_s<B, false, true>(acc, sWt, nullptr, Yt.hi, Yt.lo, 32 * mt, 32 * nt, lane);
+            float* e32 = ws.e32 ? ws.e32 + (size_t)blk * D * D : nullptr;
+            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int x, int y, float a) {
+                *reinterpret_cast<__bf16*>(img + I::OFF_E + img_off(x, swap23(y), I::RB_E)) =
+                    (__bf16)(-a);
+                if (e32) e32[x * D + y] = a;
+            });
         }
-        for (int j = 5 + wave; j < NO; j += 8) other(j);
-    }
-    __syncthreads();
-    // ---- 6. Kright and -E images: LDS staging -> HBM with 16-byte stores
-    {
-        const char* stage = bP;
-        constexpr int KUN = (I::OFF_V - I::OFF_K) / 16, EUN = (I::OFF_G - I::OFF_E) / 16;
-        for (int u = tid; u < KUN + EUN; u += NTH) {
-            const int src = u < KUN ? u * 16 : (I::OFF_V - I::OFF_K) + (u - KUN) * 16;
-            const int dst = u < KUN ? I::OFF_K + u * 16 : I::OFF_E + (u - KUN) * 16;
-            *reinterpret_cast<u32x4*>(img + dst) = *reinterpret_cast<const u32x4*>(stage + src);
-        }
-    }
+    };
+    for (int j = wave; j < NJ; j += 8) job(j);
 }
 
 // ---------------------------------------------------------------------------
@@ -452,14 +479,21 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
         if (FOX) gq = ws.gl[bq * B + qloc] * kLog2e;
     }
 
-    // P.V for the current S (already exponentiated), from the V^T image;
-    // returns this lane's share of the row sum of the bf16 P it used
-    auto pv = [&](const char* im) {
-        bf16x8 Pb[4];
+    // p = 2^S in place, with P as bf16 operands (keys in the k-slots);
+    // returns this lane's share of the row sum of that bf16 P
+    auto probs = [&](bf16x8 (&Pb)[4]) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[mt][r] = __builtin_amdgcn_exp2f(S[mt][r]);
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
             for (int e = 0; e < 8; ++e) Pb[kc][e] = (__bf16)S[kc >> 1][8 * (kc & 1) + e];
+        return sum_bf16x32(Pb);
+    };
+    // O^T += V^T P^T from the V^T image
+    auto pv = [&](const char* im, const bf16x8 (&Pb)[4]) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int row = 32 * t + col;
@@ -471,10 +505,8 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) Ot[t] = mfma32(va[kc], Pb[kc], Ot[t]);
         }
-        return sum_bf16x32(Pb);
     };
 
-    // diagonal block of query block myb (image in buf), causal mask
     auto diag = [&](const char* im) {
         const size_t bq = blk0 + myb;
         const float* dgp = ws.dg + (bq * B + qloc) * B;
@@ -502,13 +534,18 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) S[mt][r] = __builtin_amdgcn_exp2f(S[mt][r] - m);
-        l = pv(im);   // this half's keys only; the halves are added at the end
+            for (int r = 0; r < 16; ++r) S[mt][r] -= m;
+        bf16x8 Pb[4];
+        l = probs(Pb);   // this half's keys only; the halves are added at the end
+        pv(im, Pb);
     };
 
     // one scan step against key block c (image in buf)
     auto step = [&](const char* im, int c) {
-        if (FOX) grun += ws.tot[blk0 + c];
+        (void)c;
+        const float* gimg = reinterpret_cast<const float*>(im + I::OFF_G);
+        // the block's log-f total is its last in-block cumsum entry
+        if (FOX) grun += gimg[B - 1];
         const float rowb = gq + grun * kLog2e;
         bf16x8 Qb[NKC];
 #pragma unroll
@@ -519,9 +556,13 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
         // contraction group adds the gate's per-key term -gl_c * log2(e)
         // (hi + lo against ones) and the per-query reference
         // -(m - rowb) (hi + mid + lo, exact to fp32, against ones on the key
-        // side), so the softmax needs no per-score subtraction.
-        const float* gimg = reinterpret_cast<const float*>(im + I::OFF_G);
+        // side), so the softmax needs no per-score subtraction.  Only the
+        // lower lane half carries that group (k-slots 0-7).  The last step
+        // (c = 0) also carries the queries across block 0, which is unused
+        // but cheaper than a branch.
         const float nref = rowb - m;
+        const bool lo_half = h == 0;
+        const __bf16 zb = (__bf16)0.f, ob = (__bf16)1.f;
         bf16x8 qside;
         {
             const __bf16 r0 = (__bf16)nref;
@@ -529,11 +570,12 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
             const __bf16 r1 = (__bf16)t1;
             const __bf16 r2 = (__bf16)(t1 - (float)r1);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qside[e] = (__bf16)0.f;
-            if (h == 0) {
-                qside[0] = (__bf16)1.f; qside[1] = (__bf16)1.f;
-                qside[2] = r0; qside[3] = r1; qside[4] = r2;
-            }
+            for (int e = 0; e < 8; ++e) qside[e] = zb;
+            qside[0] = lo_half ? ob : zb;
+            qside[1] = lo_half ? ob : zb;
+            qside[2] = lo_half ? r0 : zb;
+            qside[3] = lo_half ? r1 : zb;
+            qside[4] = lo_half ? r2 : zb;
         }
         bf16x8 ka[2][NKC];
 #pragma unroll
@@ -547,38 +589,34 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             S[mt] = zero16();
-            const int row = 32 * mt + col;
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) S[mt] = mfma32(ka[mt][kc], Qb[kc], S[mt]);
+            float gb = 0.f;
+            if (FOX) gb = -gimg[32 * mt + col] * kLog2e;
+            const __bf16 ghi = (__bf16)gb, glo = (__bf16)(gb - (float)ghi);
             bf16x8 a;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a[e] = (__bf16)0.f;
-            if (h == 0) {
-                if (FOX) {
-                    const float gb = -gimg[row] * kLog2e;
-                    const __bf16 hi = (__bf16)gb;
-                    a[0] = hi;
-                    a[1] = (__bf16)(gb - (float)hi);
-                }
-                a[2] = (__bf16)1.f; a[3] = (__bf16)1.f; a[4] = (__bf16)1.f;
-            }
+            for (int e = 0; e < 8; ++e) a[e] = zb;
+            a[0] = lo_half ? ghi : zb;
+            a[1] = lo_half ? glo : zb;
+            a[2] = lo_half ? ob : zb;
+            a[3] = lo_half ? ob : zb;
+            a[4] = lo_half ? ob : zb;
             S[mt] = mfma32(a, qside, S[mt]);
         }
         // Qwork^T += (-E_c) Qwork^T: carry the queries across block c.  It
         // needs only the bf16 Qwork already formed, so it is issued before the
         // softmax and the matrix cores work while the vector ALUs do exp.
-        if (c > 0) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int row = 32 * t + col;
-                bf16x8 ea[NKC];
+        for (int t = 0; t < NT; ++t) {
+            const int row = 32 * t + col;
+            bf16x8 ea[NKC];
 #pragma unroll
-                for (int kc = 0; kc < NKC; ++kc)
-                    ea[kc] = *reinterpret_cast<const bf16x8*>(
-                        im + I::OFF_E + row * I::RB_E + swz_unit(row, 2 * kc + h, I::RB_E) * 16);
+            for (int kc = 0; kc < NKC; ++kc)
+                ea[kc] = *reinterpret_cast<const bf16x8*>(
+                    im + I::OFF_E + row * I::RB_E + swz_unit(row, 2 * kc + h, I::RB_E) * 16);
 #pragma unroll
-                for (int kc = 0; kc < NKC; ++kc) Qw[t] = mfma32(ea[kc], Qb[kc], Qw[t]);
-            }
+            for (int kc = 0; kc < NKC; ++kc) Qw[t] = mfma32(ea[kc], Qb[kc], Qw[t]);
         }
         // online softmax with a lazily updated reference max: S' is already
         // relative to m; rescale only when a row's max exceeds it by 2^kTau
@@ -602,11 +640,9 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
                 for (int r = 0; r < 16; ++r) S[mt][r] -= up;
             m += up;
         }
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) S[mt][r] = __builtin_amdgcn_exp2f(S[mt][r]);
-        l += pv(im);
+        bf16x8 Pb[4];
+        l += probs(Pb);
+        pv(im, Pb);
     };
 
     wait_loads();
