@@ -348,21 +348,34 @@ struct Pad {
     static constexpr int DP = D < 32 ? 32 : D, DT = DP / 32;
 };
 
-// dst (DP x DP, stride kMS) <- src (D x D row-major), zero padded
-template <int D>
-__device__ inline void mat_load_pad(float* dst, const float* src, int tid) {
-    constexpr int DP = Pad<D>::DP;
-    for (int e = tid; e < DP * DP; e += 256) {
-        const int x = e / DP, y = e % DP;
-        dst[x * kMS + y] = (x < D && y < D) ? src[x * D + y] : 0.f;
-    }
-}
-
 template <int D>
 __device__ inline void mat_identity(float* dst, int tid) {
     constexpr int DP = Pad<D>::DP;
     for (int e = tid; e < DP * DP; e += 256) dst[(e / DP) * kMS + e % DP] = (e / DP == e % DP) ? 1.f : 0.f;
 }
+
+// A thread's share of a D x D row-major matrix (element e = tid + 256 i of
+// the padded DP x DP matrix), held in registers so that the next matrix of a
+// chain is in flight while the current product runs.
+template <int D>
+struct MatRegs {
+    static constexpr int DP = Pad<D>::DP, N = DP * DP / 256;
+    float v[N];
+    __device__ void load(const float* src, int tid) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int e = tid + 256 * i, x = e / DP, y = e % DP;
+            v[i] = (x < D && y < D) ? src[x * D + y] : 0.f;
+        }
+    }
+    __device__ void store(float* dst, int tid) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int e = tid + 256 * i;
+            dst[(e / DP) * kMS + e % DP] = v[i];
+        }
+    }
+};
 
 template <int D>
 __global__ void __launch_bounds__(256)
@@ -376,9 +389,12 @@ suffix_local_kernel(int nb, int ngroups, FwdWs ws) {
     mat_identity<D>(sSt, tid);
     for (int e = tid; e < D * D; e += 256) ws.suf[(b0 + last) * D * D + e] = (e / D == e % D) ? 1.f : 0.f;
     // c = first - 1 yields the group total: G^T = T_first^T F_first^T
+    MatRegs<D> nextE;
+    if (last - 1 >= first - 1) nextE.load(ws.e32 + (b0 + last) * D * D, tid);
     for (int c = last - 1; c >= first - 1; --c) {
         __syncthreads();
-        mat_load_pad<D>(sE, ws.e32 + (b0 + c + 1) * D * D, tid);
+        nextE.store(sE, tid);
+        if (c - 1 >= first - 1) nextE.load(ws.e32 + (b0 + c) * D * D, tid);
         __syncthreads();
         f32x16 acc = zero16();
         const int mt = wave / P::DT, nt = wave % P::DT;
@@ -436,9 +452,12 @@ suffix_groups_kernel(int nb, int ngroups, FwdWs ws) {
     for (int e = tid; e < D * D; e += 256)
         ws.grp[((g0 + ngroups - 1) * 2 + 1) * D * D + e] = (e / D == e % D) ? 1.f : 0.f;
     // Z_g^T = Z_{g+1}^T G_{g+1}^T
+    MatRegs<D> nextG;
+    if (ngroups >= 2) nextG.load(ws.grp + ((g0 + ngroups - 1) * 2) * D * D, tid);
     for (int g = ngroups - 2; g >= 0; --g) {
         __syncthreads();
-        mat_load_pad<D>(sG, ws.grp + ((g0 + g + 1) * 2) * D * D, tid);
+        nextG.store(sG, tid);
+        if (g >= 1) nextG.load(ws.grp + ((g0 + g) * 2) * D * D, tid);
         __syncthreads();
         f32x16 acc = zero16();
         const int mt = wave / P::DT, nt = wave % P::DT;
@@ -458,57 +477,133 @@ suffix_groups_kernel(int nb, int ngroups, FwdWs ws) {
     }
 }
 
+// Eight fp32 values of row `row` of a row-major matrix (stride ld) as a bf16
+// hi + lo operand pair: columns c0 + 8h .. +7, or with PERM the columns
+// c0 + swap23(8h + e) that match a C tile reused as the other operand.  Rows
+// at or beyond nr and column groups at or beyond nc read as zero.
+template <bool PERM>
+__device__ inline void ld8_split(const float* base, int ld, int row, int nr, int c0, int nc,
+                                 int h, bf16x8& hi, bf16x8& lo) {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
+    if (row < nr && c0 < nc) {
+        const float* p = base + (size_t)row * ld + c0;
+        const int o0 = PERM ? 4 * h : 8 * h, o1 = PERM ? 8 + 4 * h : 8 * h + 4;
+        a = *reinterpret_cast<const f32x4*>(p + o0);
+        b = *reinterpret_cast<const f32x4*>(p + o1);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = e < 4 ? a[e] : b[e - 4];
+        hi[e] = (__bf16)x;
+        lo[e] = (__bf16)(x - (float)hi[e]);
+    }
+}
+
+__device__ inline f32x16 mfma_split(const bf16x8& ah, const bf16x8& al, const bf16x8& bh,
+                                    const bf16x8& bl, f32x16 acc) {
+    acc = mfma32(ah, bl, acc);
+    acc = mfma32(al, bh, acc);
+    return mfma32(ah, bh, acc);
+}
+
 // kcache rows of block c = (Kright_c T_c) Z_g; values copied; gcache = block
-// prefix + in-block cumsum.  One block of 256 threads per (slice, c).
+// prefix + in-block cumsum.  Register-only: a wave owns 32 keys of one block
+// and forms X^T = T_c^T Kright_c^T (operands read from HBM as they are
+// stored), then kcache^T = Z_g^T X^T with X^T's C tiles reused directly as
+// the B operand.  Products use fp32 operands split into bf16 hi + lo (about
+// 16 significant bits), well below the bf16 or fp32 rounding of the cache.
 template <typename K, typename T, int B, int D>
 __global__ void __launch_bounds__(256)
-align_apply_kernel(int L, int nb, int ngroups, FwdWs ws, const T* __restrict__ v,
+align_apply_kernel(int L, int nb, int ngroups, int nblk, FwdWs ws, const T* __restrict__ v,
                    int has_gate, K* __restrict__ kc, T* __restrict__ vc,
                    float* __restrict__ gc, int cap) {
-    using P = Pad<D>;
-    __shared__ __attribute__((aligned(16))) float sK[64 * kMS], sT[64 * kMS], sZ[64 * kMS];
-    const int blk = blockIdx.x, slice = blk / nb, c = blk % nb, tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, h = lane >> 5;
-    const int g = c / kSufGroup;
-    mat_load_pad<D>(sT, ws.suf + (size_t)blk * D * D, tid);                                   // T^T
-    mat_load_pad<D>(sZ, ws.grp + (((size_t)slice * ngroups + g) * 2 + 1) * D * D, tid);      // Z^T
-    for (int e = tid; e < 64 * P::DP; e += 256) {
-        const int r = e / P::DP, x = e % P::DP;
-        sK[r * kMS + x] = (r < B && x < D) ? ws.k32[((size_t)blk * B + r) * D + x] : 0.f;
-    }
-    __syncthreads();
-    constexpr int TILES = 2 * P::DT;                 // 64 rows x DP columns
-    f32x16 acc = zero16();
-    const int mt = wave / P::DT, nt = wave % P::DT;
-    const bool mine = wave < TILES;
-    if (mine) tile_mm_f32<P::DP>(acc, sK, kMS, sT, kMS, 32 * mt, 32 * nt, lane);   // X = K T
-    __syncthreads();
-    if (mine) {
-        const int y = 32 * nt + (lane & 31);
+    constexpr int DP = Pad<D>::DP, XT = DP / 32, KS = DP / 16;
+    constexpr int BP = B < 32 ? 32 : B, RT = BP / 32, BPW = 4 / RT;   // blocks per workgroup
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
+    const int col = lane & 31;
+    const int blk = blockIdx.x * BPW + wave / RT, rt = wave % RT;
+    if (blk < nblk) {
+        const int slice = blk / nb, c = blk % nb, g = c / kSufGroup;
+        const float* Tt = ws.suf + (size_t)blk * D * D;
+        const float* Zt = ws.grp + (((size_t)slice * ngroups + g) * 2 + 1) * D * D;
+        const float* kr = ws.k32 + (size_t)blk * B * D;
+        const int r = 32 * rt + col;                 // this lane's key (B-operand column)
+        bf16x8 kh[KS], kl[KS];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sK[(32 * mt + crow(r, h)) * kMS + y] = acc[r];
-    }
-    __syncthreads();
-    acc = zero16();
-    if (mine) tile_mm_f32<P::DP>(acc, sK, kMS, sZ, kMS, 32 * mt, 32 * nt, lane);   // X Z
-    if (mine) {
-        const int y = 32 * nt + (lane & 31);
+        for (int ks = 0; ks < KS; ++ks) ld8_split<false>(kr, D, r, B, 16 * ks, D, h, kh[ks], kl[ks]);
+        f32x16 xt[XT];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int rr = 32 * mt + crow(r, h), pos = c * B + rr;
-            if (rr < B && y < D && pos < L)
-                kc[((size_t)slice * cap + pos) * D + y] = from_f32<K>(acc[r]);
+        for (int t = 0; t < XT; ++t) {
+            xt[t] = zero16();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8 ah, al;
+                ld8_split<false>(Tt, D, 32 * t + col, D, 16 * ks, D, h, ah, al);
+                xt[t] = mfma_split(ah, al, kh[ks], kl[ks], xt[t]);
+            }
+        }
+        // X^T's C tiles as the B operand: k-step ks holds rows 16 ks + swap23(slot)
+        bf16x8 bh[KS], bl[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = xt[ks >> 1][8 * (ks & 1) + e];
+                bh[ks][e] = (__bf16)x;
+                bl[ks][e] = (__bf16)(x - (float)bh[ks][e]);
+            }
+        const int pos = c * B + r;
+        K* krow = kc + ((size_t)slice * cap + pos) * D;
+#pragma unroll
+        for (int yt = 0; yt < XT; ++yt) {
+            f32x16 acc = zero16();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8 ah, al;
+                ld8_split<true>(Zt, D, 32 * yt + col, D, 16 * ks, D, h, ah, al);
+                acc = mfma_split(ah, al, bh[ks], bl[ks], acc);
+            }
+            if (r < B && pos < L) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int y0 = 32 * yt + 8 * i + 4 * h;
+                    if (y0 < D) {
+                        if constexpr (sizeof(K) == 2) {
+                            typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+                            bf16x4 pk;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) pk[j] = (__bf16)acc[4 * i + j];
+                            *reinterpret_cast<bf16x4*>(krow + y0) = pk;
+                        } else {
+                            f32x4 pk;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) pk[j] = acc[4 * i + j];
+                            *reinterpret_cast<f32x4*>(krow + y0) = pk;
+                        }
+                    }
+                }
+            }
         }
     }
-    for (int e = tid; e < B * D; e += 256) {
-        const int rr = e / D, y = e % D, pos = c * B + rr;
-        if (pos < L) vc[((size_t)slice * cap + pos) * D + y] = v[((size_t)slice * L + pos) * D + y];
-    }
-    if (gc && tid < B) {
-        const int pos = c * B + tid;
+    // values (16-byte units) and the gate prefix of this workgroup's blocks
+    constexpr int UPR = D * (int)sizeof(T) / 16;
+    for (int u = tid; u < BPW * B * UPR; u += 256) {
+        const int b2 = blockIdx.x * BPW + u / (B * UPR), rr = (u / UPR) % B, x = u % UPR;
+        if (b2 >= nblk) continue;
+        const int slice = b2 / nb, pos = (b2 % nb) * B + rr;
         if (pos < L)
-            gc[(size_t)slice * cap + pos] =
-                has_gate ? ws.gpre[blk] + ws.gl[(size_t)blk * B + tid] : 0.f;
+            reinterpret_cast<u32x4*>(vc + ((size_t)slice * cap + pos) * D)[x] =
+                reinterpret_cast<const u32x4*>(v + ((size_t)slice * L + pos) * D)[x];
+    }
+    if (gc) {
+        for (int u = tid; u < BPW * B; u += 256) {
+            const int b2 = blockIdx.x * BPW + u / B, rr = u % B;
+            if (b2 >= nblk) continue;
+            const int slice = b2 / nb, pos = (b2 % nb) * B + rr;
+            if (pos < L)
+                gc[(size_t)slice * cap + pos] =
+                    has_gate ? ws.gpre[b2] + ws.gl[(size_t)b2 * B + rr] : 0.f;
+        }
     }
 }
 
@@ -639,8 +734,10 @@ static hipError_t align_t(const FwdArgs& a, const CacheArgs& c, hipStream_t st) 
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((suffix_groups_kernel<D>), dim3(NH), dim3(256), 0, st, nb, ng, a.ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((align_apply_kernel<K, T, B, D>), dim3(NH * nb), dim3(256), 0, st,
-                       a.L, nb, ng, a.ws, (const T*)a.v, a.logf ? 1 : 0, (K*)c.kcache,
+    constexpr int BPW = 4 / ((B < 32 ? 32 : B) / 32);   // blocks per workgroup
+    const int nblk = NH * nb;
+    hipLaunchKernelGGL((align_apply_kernel<K, T, B, D>), dim3((nblk + BPW - 1) / BPW), dim3(256), 0,
+                       st, a.L, nb, ng, nblk, a.ws, (const T*)a.v, a.logf ? 1 : 0, (K*)c.kcache,
                        (T*)c.vcache, c.gcache, c.cap);
     return hipGetLastError();
 }
