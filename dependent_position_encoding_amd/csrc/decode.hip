@@ -499,13 +499,6 @@ __device__ inline void ld8_split(const float* base, int ld, int row, int nr, int
     }
 }
 
-__device__ inline f32x16 mfma_split(const bf16x8& ah, const bf16x8& al, const bf16x8& bh,
-                                    const bf16x8& bl, f32x16 acc) {
-    acc = mfma32(ah, bl, acc);
-    acc = mfma32(al, bh, acc);
-    return mfma32(ah, bh, acc);
-}
-
 // kcache rows of block c = (Kright_c T_c) Z_g; values copied; gcache = block
 // prefix + in-block cumsum.  Register-only: a wave owns 32 keys of one block
 // and forms X^T = T_c^T Kright_c^T (operands read from HBM as they are

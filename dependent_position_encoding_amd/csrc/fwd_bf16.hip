@@ -131,6 +131,26 @@ __device__ inline void mm_regs(f32x16& acc, const bf16x8 (&a)[NK], const bf16x8 
     for (int ks = 0; ks < NK; ++ks) acc = mfma32(a[ks], b[ks], acc);
 }
 
+// Eight floats of LDS row r (row stride kSF) as a bf16 hi + lo operand pair:
+// columns c0 + 8h .. +7, or with PERM the columns c0 + swap23(8h + e) that
+// match a C tile reused as the other operand; zero when !ok.
+template <bool PERM>
+__device__ inline void lds8_split(const float* base, int r, int c0, int h, bool ok, bf16x8& hi,
+                                  bf16x8& lo) {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
+    if (ok) {
+        const float* p = base + r * kSF + c0;
+        a = *reinterpret_cast<const f32x4*>(p + (PERM ? 4 * h : 8 * h));
+        b = *reinterpret_cast<const f32x4*>(p + (PERM ? 8 + 4 * h : 8 * h + 4));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = e < 4 ? a[e] : b[e - 4];
+        hi[e] = (__bf16)x;
+        lo[e] = (__bf16)(x - (float)hi[e]);
+    }
+}
+
 // One 512-thread workgroup (8 waves) per 64-token block, 64.8 KB of LDS so
 // that two workgroups share a CU and one's barriers and HBM waits overlap
 // the other's work.  Products over the head dimension read Q, K and W
@@ -147,7 +167,7 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     // W^T and three 64 x 64 slots, each holding a float matrix or a split one:
     //   s0 : G (float)            -> X1 (split)    -> P (split)
     //   s1 : T (float)            -> U^T (split)   -> Y^T (split)
-    //   s2 : V (float staging)    -> solve scratch -> M^T (split)
+    //   s2 : V (float staging)    -> T^T (float)   -> M^T (split)
     __shared__ __attribute__((aligned(16))) __bf16 sWt[D * SB];
     __shared__ __attribute__((aligned(16))) char s0[kSplitBytes], s1[kSplitBytes], s2[kSplitBytes];
     __shared__ float sBeta[B];
@@ -155,7 +175,7 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     float* fG = reinterpret_cast<float*>(s0);
     float* fT = reinterpret_cast<float*>(s1);
     float* fV = reinterpret_cast<float*>(s2);
-    float* fS = reinterpret_cast<float*>(s2);
+    float* fTt = reinterpret_cast<float*>(s2);
     const Split X1 = split_at(s0), P = split_at(s0), Ut = split_at(s1), Yt = split_at(s1),
                 Mt = split_at(s2);
 
@@ -224,24 +244,33 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
     __syncthreads();
 
-    // ---- 3. T = (I + G)^{-1} on waves 0-3, blocked over 16 x 16 blocks;
-    //         meanwhile waves 4-7 form X1 = lower(Q W^T) and M^T
-    //         (M = strictLower(W K^T)) in registers: neither needs T.
+    // ---- 3. T = (I + G)^{-1}.  Diagonal 16 x 16 blocks by forward
+    //         substitution (waves 0-3, one column per lane); then the
+    //         off-diagonal blocks by doubling on the matrix cores: the inverse
+    //         of a lower block-triangular [[A, 0], [C, B]] has off-diagonal
+    //         block -B^{-1} C A^{-1} (16 -> 32 on waves 0-1, 32 -> 64 on wave
+    //         0).  T is kept in both layouts (T in s1, T^T in s2) so that every
+    //         operand is read along LDS rows.  Meanwhile waves 4-7 form
+    //         X1 = lower(Q W^T) and M^T (M = strictLower(W K^T)) in registers.
     const int xt = wave - 4, xmt = xt >> 1, xnt = xt & 1;
     f32x16 x1r = zero16(), mtr = zero16();
     if (wave < 4) {
-        // diagonal blocks by forward substitution, one column per lane
         if (lane < 16) {
             const int o = 16 * wave;
             float t[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float sum = 0.f;
+            for (int i = 0; i < 16; ++i) t[i] = i == lane ? 1.f : 0.f;
 #pragma unroll
-                for (int kk = 0; kk < i; ++kk) sum += fG[(o + i) * SF + o + kk] * t[kk];
-                t[i] = i < lane ? 0.f : (i == lane ? 1.f : -sum);
-                fT[(o + i) * SF + o + lane] = t[i];
-            }
+            for (int kk = 0; kk < 15; ++kk)
+#pragma unroll
+                for (int i = kk + 1; i < 16; ++i) t[i] -= fG[(o + i) * SF + o + kk] * t[kk];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) fT[(o + i) * SF + o + lane] = t[i];
+            float* trow = fTt + (o + lane) * SF;
+            for (int c4 = 0; c4 < o; c4 += 4) *reinterpret_cast<f32x4*>(trow + c4) = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c4 = 0; c4 < 16; c4 += 4)
+                *reinterpret_cast<f32x4*>(trow + o + c4) = f32x4{t[c4], t[c4 + 1], t[c4 + 2], t[c4 + 3]};
         }
     } else if (!(xmt == 0 && xnt == 1)) {
         bf16x8 a[NKS], b[NKS];
@@ -250,44 +279,69 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         mm_regs(x1r, a, b);
     }
     __syncthreads();
-    // off-diagonal blocks: T_ab = -T_aa sum_{c=b}^{a-1} G_ac T_cb, by distance
-    for (int lev = 1; lev < 4; ++lev) {
-        const int njobs = 4 - lev, r = lane >> 2, c0 = (lane & 3) * 4;
-        if (wave < njobs) {
-            const int bb = wave, a = bb + lev;
-            float x[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int cb = bb; cb < a; ++cb) {
+    const int mrow = lane & 31, hh = lane >> 5;
+    if (wave < 2) {
+        // 16 -> 32 inside rows/columns [o2, o2 + 32): X = G_10 T_00, Y = -T_11 X
+        const int o2 = 32 * wave;
+        const bool ok = mrow < 16;
+        bf16x8 ah, al, bh, bl;
+        lds8_split<false>(fG, o2 + 16 + mrow, o2, hh, ok, ah, al);
+        lds8_split<false>(fTt, o2 + mrow, o2, hh, ok, bh, bl);
+        const f32x16 x = mfma_split(ah, al, bh, bl, zero16());
+        // X's C tile (rows 0-15 in registers 0-7) is the B operand of T_11 X
 #pragma unroll
-                for (int kk = 0; kk < 16; ++kk) {
-                    const float g = fG[(16 * a + r) * SF + 16 * cb + kk];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] += g * fT[(16 * cb + kk) * SF + 16 * bb + c0 + e];
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) fS[(16 * a + r) * SF + 16 * bb + c0 + e] = x[e];
-        } else if (lev == 1 && wave >= 4 && !(xmt == 1 && xnt == 0)) {
-            // M^T[j][b] = k_j . w_b for b > j
-            bf16x8 a[NKS], b[NKS];
-            ld_rows<D>(a, kb, 32 * xmt, nvalid, lane);
-            ld_rows<D>(b, wb, 32 * xnt, nvalid, lane);
-            mm_regs(mtr, a, b);
+        for (int e = 0; e < 8; ++e) {
+            bh[e] = (__bf16)x[e];
+            bl[e] = (__bf16)(x[e] - (float)bh[e]);
         }
-        __syncthreads();
-        if (wave < njobs) {
-            const int bb = wave, a = bb + lev;
-            float y[4] = {0.f, 0.f, 0.f, 0.f};
+        lds8_split<true>(fT, o2 + 16 + mrow, o2 + 16, hh, ok, ah, al);
+        const f32x16 y = mfma_split(ah, al, bh, bl, zero16());
+        if (ok) {
 #pragma unroll
-            for (int kk = 0; kk < 16; ++kk) {
-                const float t = fT[(16 * a + r) * SF + 16 * a + kk];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] -= t * fS[(16 * a + kk) * SF + 16 * bb + c0 + e];
+            for (int r = 0; r < 8; ++r) {
+                const int row = crow(r, hh);
+                fT[(o2 + 16 + row) * SF + o2 + mrow] = -y[r];
+                fTt[(o2 + mrow) * SF + o2 + 16 + row] = -y[r];
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) fT[(16 * a + r) * SF + 16 * bb + c0 + e] = y[e];
         }
-        __syncthreads();
+    } else if (wave >= 4 && !(xmt == 1 && xnt == 0)) {
+        // M^T[j][b] = k_j . w_b for b > j
+        bf16x8 a[NKS], b[NKS];
+        ld_rows<D>(a, kb, 32 * xmt, nvalid, lane);
+        ld_rows<D>(b, wb, 32 * xnt, nvalid, lane);
+        mm_regs(mtr, a, b);
     }
+    __syncthreads();
+    if (wave == 0) {
+        // 32 -> 64: X = G[32:64, 0:32] T[0:32, 0:32], Y = -T[32:64, 32:64] X
+        f32x16 x = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 ah, al, bh, bl;
+            lds8_split<false>(fG, 32 + mrow, 16 * ks, hh, true, ah, al);
+            lds8_split<false>(fTt, mrow, 16 * ks, hh, true, bh, bl);
+            x = mfma_split(ah, al, bh, bl, x);
+        }
+        f32x16 y = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 ah, al, bh, bl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                bh[e] = (__bf16)x[8 * ks + e];
+                bl[e] = (__bf16)(x[8 * ks + e] - (float)bh[e]);
+            }
+            lds8_split<true>(fT, 32 + mrow, 32 + 16 * ks, hh, true, ah, al);
+            y = mfma_split(ah, al, bh, bl, y);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = crow(r, hh);
+            fT[(32 + row) * SF + mrow] = -y[r];
+            fTt[mrow * SF + 32 + row] = -y[r];
+        }
+    }
+    __syncthreads();
 
     // ---- 4. X1 and M^T to LDS (G and the scratch are dead); U = T diag(beta)
     //         read into registers, then stored as U^T over T

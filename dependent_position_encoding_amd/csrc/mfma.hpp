@@ -71,6 +71,15 @@ __device__ inline void tile_mm(f32x16& acc, const TA* A, int lda, const TB* Bn, 
     }
 }
 
+// acc += A B for operands split into bf16 hi + lo parts: the three partial
+// products that matter (lo * lo dropped), smallest first.
+__device__ inline f32x16 mfma_split(const bf16x8& ah, const bf16x8& al, const bf16x8& bh,
+                                    const bf16x8& bl, f32x16 acc) {
+    acc = mfma32(ah, bl, acc);
+    acc = mfma32(al, bh, acc);
+    return mfma32(ah, bh, acc);
+}
+
 // float32 operands split three ways (hi + mid + lo, 8 mantissa bits each):
 // acc += A * Bn^T with the six partial products that matter at fp32
 // precision, smallest first.  Used where a long chain of d x d products must
