@@ -90,6 +90,29 @@ __device__ inline void put(const Split& m, int r, int c, float v) {
     m.lo[r * kSB + c] = (__bf16)(v - (float)hi);
 }
 
+// A C tile of a transposed product, read back row-wise: lane (tile column
+// c) holds row n0 + c of the wanted matrix, and registers 4i .. 4i+3 hold its
+// columns m0 + 8i + 4h .. +3, handed to f(row, col0, four values) together
+// so that they can be stored as one vector.
+template <typename F>
+__device__ inline void for_tile4(const f32x16& acc, int m0, int n0, int lane, F f) {
+    const int h = lane >> 5, row = n0 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        f(row, m0 + 8 * i + 4 * h, f32x4{acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]});
+}
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+__device__ inline void put4(const Split& m, int r, int c, f32x4 v) {
+    bf16x4 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        hi[e] = (__bf16)v[e];
+        lo[e] = (__bf16)(v[e] - (float)hi[e]);
+    }
+    *reinterpret_cast<bf16x4*>(m.hi + r * kSB + c) = hi;
+    *reinterpret_cast<bf16x4*>(m.lo + r * kSB + c) = lo;
+}
+
 // acc += A[m0:+32, 0:K] * Bn[n0:+32, 0:K]^T over LDS bf16 operands; a split
 // operand contributes its lo part as well (lo * lo is dropped).
 template <int K, bool SA, bool SBL>
@@ -237,9 +260,13 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
     if (wave < 3) {
         f32x16 acc = zero16();
-        mm_regs(acc, ga, gb);
-        for_tile(acc, 32 * gmt, 32 * gnt, lane, [&](int i, int j, float a) {
-            fG[i * SF + j] = i > j ? sBeta[i] * a : 0.f;
+        mm_regs(acc, gb, ga);   // (W W^T)^T tile: lane = row i of G
+        for_tile4(acc, 32 * gnt, 32 * gmt, lane, [&](int i, int j0, f32x4 v) {
+            const float bi = sBeta[i];
+            f32x4 g;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) g[e] = i > j0 + e ? bi * v[e] : 0.f;
+            *reinterpret_cast<f32x4*>(fG + i * SF + j0) = g;
         });
     }
     __syncthreads();
@@ -276,7 +303,7 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         bf16x8 a[NKS], b[NKS];
         ld_rows<D>(a, qb, 32 * xmt, nvalid, lane);
         ld_rows<D>(b, wb, 32 * xnt, nvalid, lane);
-        mm_regs(x1r, a, b);
+        mm_regs(x1r, b, a);     // (Q W^T)^T tile: lane = row of X1
     }
     __syncthreads();
     const int mrow = lane & 31, hh = lane >> 5;
@@ -305,11 +332,11 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             }
         }
     } else if (wave >= 4 && !(xmt == 1 && xnt == 0)) {
-        // M^T[j][b] = k_j . w_b for b > j
+        // M^T[j][b] = k_j . w_b for b > j (transposed tile: lane = row j)
         bf16x8 a[NKS], b[NKS];
         ld_rows<D>(a, kb, 32 * xmt, nvalid, lane);
         ld_rows<D>(b, wb, 32 * xnt, nvalid, lane);
-        mm_regs(mtr, a, b);
+        mm_regs(mtr, b, a);
     }
     __syncthreads();
     if (wave == 0) {
@@ -343,47 +370,50 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
     __syncthreads();
 
-    // ---- 4. X1 and M^T to LDS (G and the scratch are dead); U = T diag(beta)
-    //         read into registers, then stored as U^T over T
-    float tv[B * B / NTH];
+    // ---- 4. U^T = (T diag(beta))^T from T^T, row by row (over T); X1 to
+    //         LDS over G (waves 4-7)
+    {
+        const int j = tid / 8, c0 = (tid % 8) * 8;
+        const float bj = sBeta[j];
+        const f32x4 a = *reinterpret_cast<const f32x4*>(fTt + j * SF + c0);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(fTt + j * SF + c0 + 4);
+        put4(Ut, j, c0, a * bj);
+        put4(Ut, j, c0 + 4, b * bj);
+    }
+    if (wave >= 4)
+        for_tile4(x1r, 32 * xnt, 32 * xmt, lane, [&](int i, int j0, f32x4 v) {
 #pragma unroll
-    for (int e = 0; e < B * B / NTH; ++e) {
-        const int idx = tid + NTH * e, i = idx / B, j = idx % B;
-        tv[e] = fT[i * SF + j] * sBeta[j];
-    }
-    if (wave >= 4) {
-        for_tile(x1r, 32 * xmt, 32 * xnt, lane, [&](int i, int j, float a) {
-            put(X1, i, j, j <= i ? a : 0.f);
+            for (int e = 0; e < 4; ++e) v[e] = j0 + e <= i ? v[e] : 0.f;
+            put4(X1, i, j0, v);
         });
-        for_tile(mtr, 32 * xmt, 32 * xnt, lane, [&](int j, int bcol, float a) {
-            put(Mt, j, bcol, bcol > j ? a : 0.f);
-        });
-    }
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < B * B / NTH; ++e) {
-        const int idx = tid + NTH * e, i = idx / B, j = idx % B;
-        put(Ut, j, i, tv[e]);
-    }
     __syncthreads();
 
-    // ---- 5. P = X1 U (waves 0-3) and Y^T = W^T U (waves 4..), Y = U^T W;
+    // ---- 5. M^T to LDS over T^T (waves 4-7); P = X1 U (waves 0-3) and
+    //         Y^T = W^T U (waves 4..), Y = U^T W, both as transposed products;
     //         Kright = K - (U M)^T W = K - M^T Y and E = W^T Y below.
     {
+        if (wave >= 4)
+            for_tile4(mtr, 32 * xnt, 32 * xmt, lane, [&](int j, int b0, f32x4 v) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = b0 + e > j ? v[e] : 0.f;
+                put4(Mt, j, b0, v);
+            });
         f32x16 acc = zero16();
         const int mt = wave < 4 ? wave >> 1 : (wave - 4) / 2;
         const int nt = wave < 4 ? wave & 1 : (wave - 4) % 2;
         if (wave < 4) {
+            // P^T[a][i] = sum_k U^T[a][k] X1[i][k]
             if (!(mt == 0 && nt == 1))
-                tile_mm_s<B, true, true>(acc, X1.hi, X1.lo, Ut.hi, Ut.lo, 32 * mt, 32 * nt, lane);
+                tile_mm_s<B, true, true>(acc, Ut.hi, Ut.lo, X1.hi, X1.lo, 32 * nt, 32 * mt, lane);
         } else if (wave < 4 + 2 * DT) {
-            tile_mm_s<B, false, true>(acc, sWt, nullptr, Ut.hi, Ut.lo, 32 * mt, 32 * nt, lane);
+            // Y[cc][y] = sum_a U^T[cc][a] W^T[y][a]
+            tile_mm_s<B, true, false>(acc, Ut.hi, Ut.lo, sWt, nullptr, 32 * nt, 32 * mt, lane);
         }
         __syncthreads();
         if (wave < 4)
-            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int j, float a) { put(P, i, j, a); });
+            for_tile4(acc, 32 * nt, 32 * mt, lane, [&](int i, int a0, f32x4 v) { put4(P, i, a0, v); });
         else if (wave < 4 + 2 * DT)
-            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int y, int cc, float a) { put(Yt, y, cc, a); });
+            for_tile4(acc, 32 * nt, 32 * mt, lane, [&](int y, int c0, f32x4 v) { put4(Yt, y, c0, v); });
     }
     __syncthreads();
 
@@ -411,15 +441,24 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             }
         } else if (j < ND + NK) {
             // (M^T Y)[r][x] = sum_a Mt[r][a] Y[a][x];  B^T row x = Y^T row x
+            // transposed: (M^T Y)^T[x][r] = sum_a Y^T[x][a] M^T[r][a], lane = key r
             const int t = j - ND, mt = t / DT, nt = t % DT;
-            tile_mm_s<B, true, true>(acc, Mt.hi, Mt.lo, Yt.hi, Yt.lo, 32 * mt, 32 * nt, lane);
+            tile_mm_s<B, true, true>(acc, Yt.hi, Yt.lo, Mt.hi, Mt.lo, 32 * nt, 32 * mt, lane);
             float* k32 = ws.k32 ? ws.k32 + (size_t)blk * B * D : nullptr;
-            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int r, int x, float a) {
-                const float kv = r < nvalid ? (float)kb[r * D + x] : 0.f;
-                const float val = kv - a;
-                *reinterpret_cast<__bf16*>(img + I::OFF_K + img_off(r, swap23(x), I::RB_K)) =
-                    (__bf16)(val * kscale);
-                if (k32) k32[r * D + x] = val;
+            for_tile4(acc, 32 * nt, 32 * mt, lane, [&](int r, int x0, f32x4 a) {
+                f32x4 kv = {0.f, 0.f, 0.f, 0.f};
+                if (r < nvalid) {
+                    const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(kb + r * D + x0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) kv[e] = (float)k4[e];
+                }
+                const f32x4 val = kv - a;
+                bf16x4 ks;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ks[e] = (__bf16)(val[e] * kscale);
+                // four consecutive columns stay consecutive under swap23
+                *reinterpret_cast<bf16x4*>(img + I::OFF_K + img_off(r, swap23(x0), I::RB_K)) = ks;
+                if (k32) *reinterpret_cast<f32x4*>(k32 + r * D + x0) = val;
             });
         } else if (j < ND + NK + NQ) {
             const int t = j - ND - NK, mt = t / DT, nt = t % DT;
@@ -430,13 +469,16 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 ql[i * D + x] = qv - a;
             });
         } else {
+            // transposed: E^T[y][x] = sum_a Y^T[y][a] W^T[x][a], lane = row x of E
             const int t = j - ND - NK - NQ, mt = t / DT, nt = t % DT;
-            tile_mm_s<B, false, true>(acc, sWt, nullptr, Yt.hi, Yt.lo, 32 * mt, 32 * nt, lane);
+            tile_mm_s<B, true, false>(acc, Yt.hi, Yt.lo, sWt, nullptr, 32 * nt, 32 * mt, lane);
             float* e32 = ws.e32 ? ws.e32 + (size_t)blk * D * D : nullptr;
-            for_tile(acc, 32 * mt, 32 * nt, lane, [&](int x, int y, float a) {
-                *reinterpret_cast<__bf16*>(img + I::OFF_E + img_off(x, swap23(y), I::RB_E)) =
-                    (__bf16)(-a);
-                if (e32) e32[x * D + y] = a;
+            for_tile4(acc, 32 * nt, 32 * mt, lane, [&](int x, int y0, f32x4 a) {
+                bf16x4 es;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) es[e] = (__bf16)(-a[e]);
+                *reinterpret_cast<bf16x4*>(img + I::OFF_E + img_off(x, swap23(y0), I::RB_E)) = es;
+                if (e32) *reinterpret_cast<f32x4*>(e32 + x * D + y0) = a;
             });
         }
     };
