@@ -327,10 +327,51 @@ def main():
             "traffic": measured_traffic(args.workload, "decode"),
             "algorithmic_bytes_first_step": decode_bytes(N, H, d, L, kb, vb),
         }
+        out["unfused_decode"] = unfused_rates(pa, cache, tok, L, wl, dws, ot, lt, kb, vb)
     out["beta0_baseline"] = causal_baseline(pa, pre, wl, out["prefill"])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, N * (L + T) / (ms_step * 1e-3))
     print(json.dumps(out), flush=True)
+
+
+def unfused_rates(pa, cache, tok, n, wl, dws, ot, lt, kb, vb, reps=20):
+    """The unfused decode pieces at n cached keys, each replayed `reps` times
+    from a HIP graph: path_kv_update alone (reads and writes every cached key)
+    and path_decode alone (reads every key, value and gate prefix, then the
+    combine).  Rates use the algorithmic bytes of each call."""
+    import torch
+    N, H, d = cache.N, cache.H, cache.d
+    E = lambda: torch.cuda.Event(enable_timing=True)
+
+    def rate(fn, nbytes):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = E(), E()
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / reps * 1e3
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return {"us": round(us, 2), "GB_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                "bytes": nbytes}
+
+    g_bytes = 4 if cache.gcache is not None else 0
+    upd = rate(lambda: pa.kv_update(cache, n, tok["w"][0], tok["beta"][0]), 2 * N * H * n * d * kb)
+    dec = rate(lambda: pa.decode(cache, n, tok["q"][0], scale=wl.scale, workspace=dws, out=(ot, lt)),
+               N * H * n * (d * kb + d * vb + g_bytes))
+    return {"keys": n, "cache_update": upd, "decode_attention": dec,
+            "note": "path_kv_update over n keys; path_decode over n keys (split-K + combine)"}
 
 
 def causal_baseline(pa, pre, wl, prefill):

@@ -74,6 +74,17 @@ def test_decode_small(dtype, k_dtype, fused):
     check_cache("decode kcache", kc, rk, k_dtype, 12)
 
 
+@pytest.mark.parametrize("gate", [True, False])
+def test_decode_bf16_head_dim_32(gate):
+    """Head dim 32 on the matrix-core prefill (its own image layout and
+    alignment tiles), a ragged prompt, then fused decode steps."""
+    wl = workloads.CONFIGS["flipflop"].replace(N=2, H=2, L=203, fox=gate)
+    go, gl, ro, rl, kc, rk, _, _ = _decode_run(wl, 203, 10, torch.bfloat16, True)
+    check("d32 decode o", go, ro, bf16=True)
+    check("d32 decode lse", gl, rl, bf16=True)
+    check_cache("d32 decode kcache", kc, rk, torch.bfloat16, 10)
+
+
 def test_decode_no_gate_and_ragged_prompt():
     wl = workloads.CONFIGS["tiny"].replace(N=1, H=2, L=77, d=32, scale=32 ** -0.5)
     go, gl, ro, rl, kc, rk, _, _ = _decode_run(wl, 77, 9, torch.float32, True)
