@@ -14,6 +14,11 @@ Householder 变换编码位置", sections 2.1, 2.5 and 2.8):
 * ``transported_keys``: the keys a decoding cache holds after position t,
   H_t...H_{j+1} k_j for j <= t.
 
+* ``frontend``: the parameter branch that makes w_t (low-rank linear layer,
+  width-3 causal short convolution, per-head L2 normalisation), beta_t =
+  2 sigma(.) and log f_t = log sigma(.) from a layer input x_t (sections 2.1
+  and 2.5; the reading of the unstated details is in path_oracle.c).
+
 Decode outputs need no function of their own: the output of the decode step
 at position t is row t of ``fwd_rows`` on the prompt and decoded tokens
 concatenated, which is what the pages' cache rewrite reproduces [s2.8].
@@ -58,9 +63,38 @@ class Oracle:
         lib.oracle_transported_keys.argtypes = [ctypes.c_int] * 3 + [P] * 3 + [
             ctypes.c_int, P]
         lib.oracle_transported_keys.restype = ctypes.c_int
+        lib.oracle_frontend.argtypes = [ctypes.c_int] * 6 + [P] * 11
+        lib.oracle_frontend.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         self._lib = lib
+
+    def frontend(self, x, Wd, Wu, kc, ub, bb, uf=None, bf=None, H=None, d=None):
+        """Parameter front-end in fp64: (w [N,H,L,d], beta [N,H,L], logf [N,H,L] or None).
+
+        x [N, L, Dm]; Wd [R, Dm]; Wu [H*d, R]; kc [H*d, 3]; ub, uf [H, Dm]; bb, bf [H].
+        """
+        x, Wd, Wu, kc, ub, bb = (_f64(a) for a in (x, Wd, Wu, kc, ub, bb))
+        N, L, Dm = x.shape
+        R = Wd.shape[0]
+        H = ub.shape[0] if H is None else H
+        d = Wu.shape[0] // H if d is None else d
+        assert Wd.shape == (R, Dm) and Wu.shape == (H * d, R) and kc.shape == (H * d, 3)
+        assert ub.shape == (H, Dm) and bb.shape == (H,)
+        gate = uf is not None
+        if gate:
+            uf, bf = _f64(uf), _f64(bf)
+            assert uf.shape == (H, Dm) and bf.shape == (H,)
+        w = np.zeros((N, H, L, d))
+        beta = np.zeros((N, H, L))
+        logf = np.zeros((N, H, L)) if gate else None
+        rc = self._lib.oracle_frontend(N, L, Dm, R, H, d, _ptr(x), _ptr(Wd), _ptr(Wu), _ptr(kc),
+                                       _ptr(ub), _ptr(bb), _ptr(uf) if gate else None,
+                                       _ptr(bf) if gate else None, _ptr(w), _ptr(beta),
+                                       _ptr(logf) if gate else None)
+        if rc != 0:
+            raise RuntimeError("oracle_frontend failed")
+        return w, beta, logf
 
     def num_threads(self) -> int:
         return int(self._lib.oracle_num_threads())
@@ -136,3 +170,7 @@ def fwd_rows(*args, **kwargs):
 
 def transported_keys(*args, **kwargs):
     return default().transported_keys(*args, **kwargs)
+
+
+def frontend(*args, **kwargs):
+    return default().frontend(*args, **kwargs)

@@ -157,3 +157,79 @@ int oracle_num_threads(void)
     }
     return n;
 }
+
+/*
+ * Parameter front-end: the per-token branch that turns a layer input x_t
+ * into the transition parameters w_t, beta_t and the forget gate log f_t.
+ *   - w_t: a low-rank linear layer, then a causal short convolution of
+ *     width 3, then L2 normalisation per head        [Notes s2.1]
+ *   - beta_t = 2 sigma(u^T x_t + b), in (0, 2)        [Notes s2.1]
+ *   - f_t = sigma(u_f^T x_t + b_f), enters as log f_t [Notes s2.5]
+ * The pages fix neither the rank nor the convolution's form; the reading
+ * taken here (plainest one consistent with them):
+ *   p_t = Wd x_t                 (R outputs)
+ *   r_t = Wu p_t                 (H*d channels)
+ *   c_t = kc[:,0] r_t + kc[:,1] r_{t-1} + kc[:,2] r_{t-2}
+ *         (depthwise, causal, r_s = 0 for s < 0; no activation)
+ *   w_t^h = c_t^h / |c_t^h| over the d channels of head h (0 if c_t^h = 0)
+ *   beta_t^h = 2 / (1 + exp(-(ub_h . x_t + bb_h)))
+ *   logf_t^h = log sigma(uf_h . x_t + bf_h)
+ * Weights use the out-by-in layout of a linear layer: Wd [R, Dm],
+ * Wu [H*d, R], ub and uf [H, Dm]; kc [H*d, 3]; bb, bf [H].
+ * x is [N, L, Dm]; w is written [N, H, L, d], beta and logf [N, H, L].
+ * uf, bf and logf may all be NULL (no forget gate).
+ */
+static double log_sigmoid(double z)
+{
+    /* log(1 / (1 + e^-z)) without overflow for either sign of z */
+    return z >= 0.0 ? -log1p(exp(-z)) : z - log1p(exp(z));
+}
+
+int oracle_frontend(int N, int L, int Dm, int R, int H, int d,
+                    const double *x, const double *Wd, const double *Wu,
+                    const double *kc, const double *ub, const double *bb,
+                    const double *uf, const double *bf,
+                    double *w, double *beta, double *logf)
+{
+    if (N < 1 || L < 1 || Dm < 1 || R < 1 || H < 1 || d < 1) return 1;
+    const int C = H * d;
+    int fail = 0;
+    #pragma omp parallel for schedule(static) reduction(|:fail)
+    for (int n = 0; n < N; ++n) {
+        double *p = malloc(sizeof(double) * (size_t)L * R);
+        double *r = malloc(sizeof(double) * (size_t)L * C);
+        if (!p || !r) { free(p); free(r); fail = 1; continue; }
+        const double *xn = x + (size_t)n * L * Dm;
+        for (int t = 0; t < L; ++t) {
+            for (int j = 0; j < R; ++j)
+                p[(size_t)t * R + j] = dot(Dm, Wd + (size_t)j * Dm, xn + (size_t)t * Dm);
+            for (int ch = 0; ch < C; ++ch)
+                r[(size_t)t * C + ch] = dot(R, Wu + (size_t)ch * R, p + (size_t)t * R);
+        }
+        for (int t = 0; t < L; ++t) {
+            const double *xt = xn + (size_t)t * Dm;
+            for (int h = 0; h < H; ++h) {
+                double c[d > 0 ? d : 1];
+                double nrm2 = 0.0;
+                for (int e = 0; e < d; ++e) {
+                    const int ch = h * d + e;
+                    double s = 0.0;
+                    for (int tau = 0; tau < 3; ++tau)
+                        if (t - tau >= 0) s += kc[(size_t)ch * 3 + tau] * r[(size_t)(t - tau) * C + ch];
+                    c[e] = s;
+                    nrm2 += s * s;
+                }
+                const double inv = nrm2 > 0.0 ? 1.0 / sqrt(nrm2) : 0.0;
+                double *wo = w + (((size_t)n * H + h) * L + t) * d;
+                for (int e = 0; e < d; ++e) wo[e] = c[e] * inv;
+                const size_t o = ((size_t)n * H + h) * L + t;
+                const double zb = dot(Dm, ub + (size_t)h * Dm, xt) + bb[h];
+                beta[o] = 2.0 / (1.0 + exp(-zb));
+                if (uf && logf) logf[o] = log_sigmoid(dot(Dm, uf + (size_t)h * Dm, xt) + bf[h]);
+            }
+        }
+        free(p);
+        free(r);
+    }
+    return fail;
+}
