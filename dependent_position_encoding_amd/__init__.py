@@ -43,6 +43,12 @@ class _Desc(ctypes.Structure):
                 ("block", ctypes.c_int)]
 
 
+class _ParamDesc(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int), ("L", ctypes.c_int), ("Dm", ctypes.c_int),
+                ("R", ctypes.c_int), ("H", ctypes.c_int), ("d", ctypes.c_int),
+                ("dtype", ctypes.c_int)]
+
+
 class _Cache(ctypes.Structure):
     _fields_ = [("cap", ctypes.c_int), ("k_dtype", ctypes.c_int),
                 ("kcache", ctypes.c_void_p), ("vcache", ctypes.c_void_p),
@@ -54,7 +60,8 @@ _lib = None
 EXPORTS = ["path_abi_version", "path_status_str", "path_last_error",
            "path_attn_fwd_workspace", "path_attn_fwd", "path_kv_update",
            "path_kv_append", "path_decode_workspace", "path_decode",
-           "path_decode_step", "path_causal_attn_fwd", "path_attn_fwd_timed"]
+           "path_decode_step", "path_causal_attn_fwd", "path_attn_fwd_timed",
+           "path_param_workspace", "path_param_fwd"]
 
 
 def load_library(path: str = LIB_PATH):
@@ -80,6 +87,8 @@ def load_library(path: str = LIB_PATH):
         "path_decode_step": ([DP, CP, I, P, P, P, P, P, P, P, P, P, S, P], I),
         "path_causal_attn_fwd": ([DP, P, P, P, P, P, P], I),
         "path_attn_fwd_timed": ([DP, P, P, P, P, P, P, P, P, CP, P, S, P, P], I),
+        "path_param_workspace": ([ctypes.POINTER(_ParamDesc), I], S),
+        "path_param_fwd": ([ctypes.POINTER(_ParamDesc)] + [P] * 12 + [S, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -298,3 +307,49 @@ def causal_attn(q, k, v, scale=None, out=None):
     _check(lib.path_causal_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                     _ptr(lse), _stream(q.device)))
     return o, lse
+
+
+def param_workspace_bytes(N, L, Dm, R, H, d, dtype, gate=True) -> int:
+    lib = load_library()
+    desc = _ParamDesc(N, L, Dm, R, H, d, _dtype_code(dtype))
+    return int(lib.path_param_workspace(ctypes.byref(desc), 1 if gate else 0))
+
+
+def param_fwd(x, Wd, Wu, kc, ub, bb, uf=None, bf=None, H=None, d=None, workspace=None,
+              out=None):
+    """Parameter front-end: (w [N,H,L,d], beta [N,H,L], logf [N,H,L] or None).
+
+    x [N, L, Dm]; Wd [R, Dm]; Wu [H*d, R]; ub, uf [H, Dm] in x's dtype;
+    kc [H*d, 3], bb, bf [H] float32.  uf and bf together enable the gate.
+    """
+    lib = load_library()
+    N, L, Dm = x.shape
+    R = Wd.shape[0]
+    H = ub.shape[0] if H is None else H
+    d = Wu.shape[0] // H if d is None else d
+    dev = x.device
+    _need(x, "x", dev, (N, L, Dm), x.dtype)
+    _need(Wd, "Wd", dev, (R, Dm), x.dtype)
+    _need(Wu, "Wu", dev, (H * d, R), x.dtype)
+    _need(ub, "ub", dev, (H, Dm), x.dtype)
+    _need(kc, "kc", dev, (H * d, 3), torch.float32)
+    _need(bb, "bb", dev, (H,), torch.float32)
+    gate = uf is not None
+    if gate:
+        _need(uf, "uf", dev, (H, Dm), x.dtype)
+        _need(bf, "bf", dev, (H,), torch.float32)
+    desc = _ParamDesc(N, L, Dm, R, H, d, _dtype_code(x.dtype))
+    nbytes = int(lib.path_param_workspace(ctypes.byref(desc), 1 if gate else 0))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        w = torch.empty(N, H, L, d, dtype=x.dtype, device=dev)
+        beta = torch.empty(N, H, L, dtype=torch.float32, device=dev)
+        logf = torch.empty(N, H, L, dtype=torch.float32, device=dev) if gate else None
+    else:
+        w, beta, logf = out
+    _check(lib.path_param_fwd(ctypes.byref(desc), _ptr(x), _ptr(Wd), _ptr(Wu), _ptr(kc), _ptr(ub),
+                              _ptr(bb), _ptr(uf), _ptr(bf), _ptr(w), _ptr(beta), _ptr(logf),
+                              _ptr(workspace), workspace.numel(), _stream(dev)))
+    return w, beta, logf
+

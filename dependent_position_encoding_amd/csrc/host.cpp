@@ -119,6 +119,26 @@ path_status launched(hipError_t e, const char* what) {
     return ok();
 }
 
+path_status check_param(const path_param_desc* d) {
+    if (!d) return fail(PATH_E_NULL, "desc is NULL");
+    if (d->N < 1 || d->L < 1 || d->H < 1 || d->Dm < 1 || d->R < 1)
+        return fail(PATH_E_SHAPE, "N, L, H, Dm and R must be >= 1");
+    if (!valid_dtype(d->dtype)) return fail(PATH_E_DTYPE, "unknown dtype");
+    if (d->d != 16 && d->d != 32 && d->d != 64)
+        return fail(PATH_E_UNSUPPORTED, "head dim must be 16, 32 or 64");
+    if (d->Dm % 16 != 0) return fail(PATH_E_UNSUPPORTED, "Dm must be a multiple of 16");
+    if (d->R % 16 != 0 || d->R > 256)
+        return fail(PATH_E_UNSUPPORTED, "R must be a multiple of 16, at most 256");
+    if ((size_t)d->N * d->L > ((size_t)1 << 31) || (size_t)d->H * d->d > 65536 ||
+        (size_t)d->N * d->L * d->Dm > ((size_t)1 << 40))
+        return fail(PATH_E_SHAPE, "problem too large");
+    return PATH_OK;
+}
+
+size_t param_ws(const path_param_desc* d, bool gate) {
+    return up256((size_t)d->N * d->L * pa::param_columns(d->R, d->H, gate) * 4);
+}
+
 }  // namespace
 
 extern "C" {
@@ -319,6 +339,41 @@ path_status path_causal_attn_fwd(const path_fwd_desc* desc, const void* q, const
     a.bf16 = desc->dtype == PATH_BF16; a.scale = desc->scale;
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
     return launched(pa::launch_causal(a, stream), "path_causal_attn_fwd");
+}
+
+size_t path_param_workspace(const path_param_desc* desc, int with_gate) {
+    if (check_param(desc) != PATH_OK) return 0;
+    return param_ws(desc, with_gate != 0);
+}
+
+path_status path_param_fwd(const path_param_desc* desc, const void* x, const void* Wd,
+                           const void* Wu, const float* kc, const void* ub, const float* bb,
+                           const void* uf, const float* bf, void* w, float* beta, float* logf,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+    path_status s = check_param(desc);
+    if (s != PATH_OK) return s;
+    if (!x || !Wd || !Wu || !kc || !ub || !bb || !w || !beta || !ws)
+        return fail(PATH_E_NULL, "x, Wd, Wu, kc, ub, bb, w, beta and ws are required");
+    const bool gate = uf != nullptr;
+    if (gate != (bf != nullptr) || gate != (logf != nullptr))
+        return fail(PATH_E_NULL, "uf, bf and logf must be given together");
+    if (!aligned(x, 16) || !aligned(Wd, 16) || !aligned(Wu, 16) || !aligned(ub, 16) ||
+        !aligned(uf, 16) || !aligned(w, 16))
+        return fail(PATH_E_ALIGN, "x, Wd, Wu, ub, uf and w must be 16-byte aligned");
+    if (!aligned(kc, 4) || !aligned(bb, 4) || !aligned(bf, 4) || !aligned(beta, 4) ||
+        !aligned(logf, 4))
+        return fail(PATH_E_ALIGN, "kc, bb, bf, beta and logf must be 4-byte aligned");
+    if (!aligned(ws, 256)) return fail(PATH_E_ALIGN, "workspace must be 256-byte aligned");
+    if (ws_bytes < param_ws(desc, gate)) return fail(PATH_E_WORKSPACE, "workspace too small");
+    pa::ParamArgs a{};
+    a.N = desc->N; a.L = desc->L; a.Dm = desc->Dm; a.R = desc->R; a.H = desc->H; a.d = desc->d;
+    a.Rp = pa::param_columns(desc->R, desc->H, gate);
+    a.bf16 = desc->dtype == PATH_BF16;
+    a.x = x; a.Wd = Wd; a.Wu = Wu; a.ub = ub; a.uf = uf;
+    a.kc = kc; a.bb = bb; a.bf = bf;
+    a.w = w; a.beta = beta; a.logf = logf;
+    a.P = static_cast<float*>(ws);
+    return launched(pa::launch_param(a, stream), "path_param_fwd");
 }
 
 }  // extern "C"

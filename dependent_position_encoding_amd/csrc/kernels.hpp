@@ -71,4 +71,17 @@ int decode_max_keys();   // longest cache one decode call can attend over
 bool causal_supported(int d, bool bf16);
 hipError_t launch_causal(const FwdArgs& a, hipStream_t st);
 
+// parameter front-end (w, beta, log f from a layer input)
+struct ParamArgs {
+    int N, L, Dm, R, H, d, Rp;
+    bool bf16;
+    const void *x, *Wd, *Wu, *ub, *uf;   // uf NULL: no forget gate
+    const float *kc, *bb, *bf;
+    void* w;
+    float *beta, *logf;
+    float* P;                            // workspace [N*L, Rp]
+};
+int param_columns(int R, int H, bool gate);   // Rp
+hipError_t launch_param(const ParamArgs& a, hipStream_t st);
+
 }  // namespace pa

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define PATH_ATTN_ABI_VERSION 1
+#define PATH_ATTN_ABI_VERSION 2
 
 typedef enum {
     PATH_OK = 0,
@@ -161,7 +161,7 @@ size_t path_decode_workspace(const path_fwd_desc *desc, int n_keys);
  *   s_j = scale * q_t^T kcache[j] + (gcache[t] - gcache[j])   (bias 0 if
  *   gcache is NULL), o_t = softmax(s) . vcache, lse_t = log sum exp s.
  * q_t, o_t [N, H, d] desc->dtype; lse_t [N, H] float32 or NULL.
- * Split over key chunks of 256; ws holds the per-chunk partial softmax
+ * Split over key chunks of 128; ws holds the per-chunk partial softmax
  * states.  At most 131072 keys per call (PATH_E_UNSUPPORTED beyond). */
 path_status path_decode(const path_fwd_desc *desc, const path_cache *cache,
                         int n_keys, const void *q_t, void *o_t, float *lse_t,
@@ -186,6 +186,50 @@ path_status path_decode_step(const path_fwd_desc *desc,
 path_status path_causal_attn_fwd(const path_fwd_desc *desc, const void *q,
                                  const void *k, const void *v, void *o,
                                  float *lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Parameter front-end [Notes s2.1, s2.5]: the branch that turns a layer input
+ * x_t into the transition parameters consumed by path_attn_fwd and the decode
+ * calls.  Per sequence n and token t (0-based), with C = H * d channels:
+ *   p_t      = Wd x_t                                   (rank R)
+ *   r_t      = Wu p_t                                   (C channels)
+ *   c_t      = kc[:,0] r_t + kc[:,1] r_{t-1} + kc[:,2] r_{t-2}
+ *              (depthwise causal convolution of width 3; r_s = 0 for s < 0,
+ *              no activation)
+ *   w_t      = c_t / |c_t| per head (the head's d channels; 0 if c_t = 0)
+ *   beta_t   = 2 / (1 + exp(-(ub . x_t + bb)))          per head, in (0, 2)
+ *   logf_t   = log sigma(uf . x_t + bf)                 per head (optional)
+ * The pages give the structure (low-rank linear layer, width-3 short
+ * convolution, L2 normalisation, 2 sigma, log sigma) but not the rank or the
+ * convolution's exact form; the above is the plainest reading.
+ *
+ * Layouts (row-major, weights in the out-by-in layout of a linear layer):
+ *   x [N, L, Dm], Wd [R, Dm], Wu [C, R], ub and uf [H, Dm]  in desc->dtype;
+ *   kc [C, 3], bb and bf [H]                                  float32;
+ *   outputs w [N, H, L, d] in desc->dtype (bf16: round to nearest even),
+ *   beta and logf [N, H, L] float32.
+ * uf, bf and logf are all NULL (no forget gate) or all given.
+ * Supported: d in {16, 32, 64}, Dm a multiple of 16, R a multiple of 16 with
+ * 16 <= R <= 256; otherwise PATH_E_UNSUPPORTED.  N, L, H >= 1.
+ * ws: at least path_param_workspace(desc) bytes, 256-byte aligned; it holds
+ * the projected [N*L, R + H (+ H) rounded up to 32] float32 intermediate.
+ * Same conventions as every other entry point (device pointers, no
+ * allocation, no synchronisation, errors before launch). */
+typedef struct {
+    int N, L;          /* sequences, tokens per sequence */
+    int Dm;            /* layer input width */
+    int R;             /* rank of the low-rank layer */
+    int H, d;          /* heads, head dim */
+    path_dtype dtype;  /* of x, the weight matrices and w */
+} path_param_desc;
+
+size_t path_param_workspace(const path_param_desc *desc, int with_gate);
+
+path_status path_param_fwd(const path_param_desc *desc, const void *x,
+                           const void *Wd, const void *Wu, const float *kc,
+                           const void *ub, const float *bb, const void *uf,
+                           const float *bf, void *w, float *beta, float *logf,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

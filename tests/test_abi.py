@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     pa, lib = _lib()
-    assert lib.path_abi_version() == 1
+    assert lib.path_abi_version() == 2
     for s in range(9):
         assert lib.path_status_str(s)
     assert lib.path_status_str(99) == b"unknown status"
@@ -112,3 +112,28 @@ def test_decode_argument_errors():
     assert lib.path_kv_append(ctypes.byref(d), ctypes.byref(g), 0, FAKE, FAKE, None, None) == 1
     bad = pa._Cache(8, 5, 1 << 20, 1 << 21, None)
     assert lib.path_kv_update(ctypes.byref(d), ctypes.byref(bad), 1, FAKE, FAKE, None) == 3
+
+
+def test_param_argument_errors():
+    """The front-end rejects bad descriptions, missing or mismatched gate
+    arguments, misaligned pointers and small workspaces before any launch."""
+    pa, lib = _lib()
+    P = lambda **kw: pa._ParamDesc(**{**dict(N=1, L=64, Dm=64, R=16, H=2, d=64,
+                                               dtype=pa.PATH_BF16), **kw})
+    good = P()
+    ws = lib.path_param_workspace(ctypes.byref(good), 1)
+    assert ws >= 64 * 32 * 4 and ws % 256 == 0
+    assert lib.path_param_workspace(ctypes.byref(P(R=8)), 1) == 0
+    args = lambda d, **kw: [ctypes.byref(d)] + [kw.get(n, FAKE) for n in (
+        "x", "Wd", "Wu", "kc", "ub", "bb", "uf", "bf", "w", "beta", "logf", "ws")] + [
+        kw.get("ws_bytes", ws), None]
+    for kw, status in [(dict(N=0), 2), (dict(d=48), 4), (dict(Dm=40), 4), (dict(R=8), 4),
+                       (dict(R=272), 4), (dict(dtype=7), 3)]:
+        assert lib.path_param_fwd(*args(P(**kw))) == status, kw
+    assert lib.path_param_fwd(*args(good, x=None)) == 1
+    assert lib.path_param_fwd(*args(good, uf=None)) == 1                # gate args must match
+    assert lib.path_param_fwd(*args(good, uf=None, bf=None, logf=None, ws_bytes=8)) == 6
+    assert lib.path_param_fwd(*args(good, x=ctypes.c_void_p((1 << 20) + 8))) == 5
+    assert lib.path_param_fwd(*args(good, ws=ctypes.c_void_p((1 << 20) + 64))) == 5
+    assert lib.path_param_fwd(*args(good, ws_bytes=ws - 256)) == 6
+

@@ -123,3 +123,29 @@ def as_slices_f64(t: torch.Tensor, heads=None):
         flat = flat[torch.as_tensor(heads, dtype=torch.long, device=flat.device)]
     return flat.to("cpu", torch.float64).numpy()
 
+
+
+def make_frontend_inputs(N, L, Dm, R, H, d, dtype=torch.bfloat16, gate=True, device="cpu",
+                         seed=0):
+    """Inputs of the parameter front-end: a layer input and the branch weights.
+
+    x ~ N(0, 1) [N, L, Dm]; Wd [R, Dm] and ub, uf [H, Dm] ~ N(0, 1/Dm), so each
+    projection of x is ~N(0, 1); Wu [H*d, R] ~ N(0, 1/R); conv taps kc [H*d, 3]
+    ~ N(0, 1/3); bb = 0 and bf = 3, so beta = 2 sigma(N(0, 1)) and
+    log f = log sigma(N(3, 1)) -- the distributions the attention workloads
+    draw beta and log f from directly.  Matrices in `dtype`, kc / bb / bf fp32.
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed((0x5eed * 1000003 + seed) & ((1 << 62) - 1))
+    f32 = torch.float32
+
+    def nrm(shape, std):
+        return (torch.randn(shape, generator=g, dtype=f32, device=device) * std)
+
+    out = dict(x=nrm((N, L, Dm), 1.0).to(dtype), Wd=nrm((R, Dm), Dm ** -0.5).to(dtype),
+               Wu=nrm((H * d, R), R ** -0.5).to(dtype), kc=nrm((H * d, 3), 3 ** -0.5),
+               ub=nrm((H, Dm), Dm ** -0.5).to(dtype), bb=torch.zeros(H, dtype=f32, device=device))
+    if gate:
+        out["uf"] = nrm((H, Dm), Dm ** -0.5).to(dtype)
+        out["bf"] = torch.full((H,), 3.0, dtype=f32, device=device)
+    return out
