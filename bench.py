@@ -329,6 +329,7 @@ def main():
         }
         out["unfused_decode"] = unfused_rates(pa, cache, tok, L, wl, dws, ot, lt, kb, vb)
     out["beta0_baseline"] = causal_baseline(pa, pre, wl, out["prefill"])
+    out["front_end"] = front_end_rate(pa, wl, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, N * (L + T) / (ms_step * 1e-3))
     print(json.dumps(out), flush=True)
@@ -372,6 +373,54 @@ def unfused_rates(pa, cache, tok, n, wl, dws, ot, lt, kb, vb, reps=20):
                N * H * n * (d * kb + d * vb + g_bytes))
     return {"keys": n, "cache_update": upd, "decode_attention": dec,
             "note": "path_kv_update over n keys; path_decode over n keys (split-K + combine)"}
+
+
+def front_end_rate(pa, wl, dev, R=32, reps=10):
+    """The parameter front-end (path_param_fwd: w, beta, log f from a layer
+    input of width H*d, rank R) at the workload's token count, replayed from a
+    HIP graph.  Algorithmic bytes: the input x, the weights, and the outputs
+    w, beta, log f; the projected intermediate's round trip through the
+    workspace is reported beside them."""
+    import torch
+    import workloads
+    N, H, L, d = wl.N, wl.H, wl.L, wl.d
+    Dm = H * d
+    p = workloads.make_frontend_inputs(N, L, Dm, R, H, d, wl.dtype, gate=wl.fox, device=dev)
+    esz = 2 if wl.dtype == torch.bfloat16 else 4
+    ws = torch.empty(pa.param_workspace_bytes(N, L, Dm, R, H, d, wl.dtype, wl.fox),
+                     dtype=torch.uint8, device=dev)
+    w = torch.empty(N, H, L, d, dtype=wl.dtype, device=dev)
+    beta = torch.empty(N, H, L, dtype=torch.float32, device=dev)
+    logf = torch.empty(N, H, L, dtype=torch.float32, device=dev) if wl.fox else None
+    fn = lambda: pa.param_fwd(**p, H=H, d=d, workspace=ws, out=(w, beta, logf))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    ngate = 2 if wl.fox else 1
+    alg = (N * L * Dm * esz + (R * Dm + H * d * R + ngate * H * Dm) * esz + H * d * 12
+           + N * H * L * d * esz + ngate * N * H * L * 4)
+    rp = (R + ngate * H + 31) // 32 * 32
+    gbs = alg / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "tokens_per_s": round(N * L / (ms * 1e-3), 1),
+            "shape": {"tokens": N * L, "width": Dm, "rank": R, "heads": H, "head_dim": d,
+                      "gate": wl.fox},
+            "bound": "hbm", "GB_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": alg, "intermediate_bytes": 2 * N * L * rp * 4}
 
 
 def causal_baseline(pa, pre, wl, prefill):

@@ -66,40 +66,130 @@ __device__ inline f32x16 mfma_parts(const bf16x8 (&a)[3], const bf16x8 (&b)[3], 
     return mfma32(a[0], b[0], acc);
 }
 
-// P^T tile (32 columns of [Wd; ub; uf] x 32 tokens) per wave, contracted
-// over Dm in steps of 16.
+// The projection GEMM.  One 128-thread workgroup (2 waves) per 64 tokens and
+// up to kProjTiles column tiles.  The input width Dm is walked in chunks of
+// 64: both operands' chunks are loaded with consecutive lanes along a row
+// (rows of x and of the weights lie Dm elements apart, so a lane-per-row
+// pattern would put every lane of an instruction on the same memory channel)
+// into LDS, double-buffered, the next chunk held in registers meanwhile.
+// Each wave forms 32 tokens x (32 kProjTiles) columns of P^T, one x fragment
+// serving all its column tiles.
+constexpr int kProjTiles = 4;
+constexpr int kProjK = 64;                  // chunk of the contraction
+
 template <typename T>
-__global__ void __launch_bounds__(256)
+struct ProjLds {
+    static constexpr int RS = kProjK * (int)sizeof(T) + 16;    // row stride, bytes (padded)
+    static constexpr int XB = 64 * RS;                          // x chunk: 64 tokens
+    static constexpr int WB = 32 * kProjTiles * RS;             // weight chunk
+    static constexpr int STAGE = XB + WB;
+    static constexpr int UPR = kProjK * (int)sizeof(T) / 16;   // 16-byte units per row
+};
+
+template <typename T>
+__global__ void __launch_bounds__(128)
 param_project_kernel(const T* __restrict__ x, const T* __restrict__ Wd, const T* __restrict__ ub,
                      const T* __restrict__ uf, int M, int Dm, int R, int H, int Rp,
                      float* __restrict__ P) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, c = lane & 31;
-    const int ntn = Rp / 32, ntt = (M + 31) / 32;
-    const int tile = blockIdx.x * 4 + wave;
-    if (tile >= ntt * ntn) return;
-    const int tt = tile / ntn, jt = tile % ntn;
-    const int j = 32 * jt + c, t = 32 * tt + c;
-    const T* wrow = j < R                   ? Wd + (size_t)j * Dm
-                    : j < R + H             ? ub + (size_t)(j - R) * Dm
-                    : (uf && j < R + 2 * H) ? uf + (size_t)(j - R - H) * Dm
-                                            : nullptr;
-    const T* xrow = x + (size_t)(t < M ? t : 0) * Dm;
-    const bool wok = wrow != nullptr, xok = t < M;
-    f32x16 acc = zero16();
-#pragma unroll 4
-    for (int k0 = 0; k0 < Dm; k0 += 16) {
-        bf16x8 a[3], b[3];
-        ld8_parts(wrow + k0 + 8 * h, wok, a);
-        ld8_parts(xrow + k0 + 8 * h, xok, b);
-        acc = mfma_parts<T>(a, b, acc);
-    }
-    if (t < M) {
-        float* out = P + (size_t)t * Rp + 32 * jt + 4 * h;
+    using S = ProjLds<T>;
+    __shared__ __attribute__((aligned(16))) char lds[2][S::STAGE];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
+    const int ntn = Rp / 32, ngroups = (ntn + kProjTiles - 1) / kProjTiles;
+    const int tb = blockIdx.x / ngroups, jg = blockIdx.x % ngroups;
+    const int t0 = 64 * tb, jt0 = jg * kProjTiles, nt = min(kProjTiles, ntn - jt0);
+    const int nrows_w = 32 * nt;
+    // row pointers of the weights behind P's columns (NULL rows are padding)
+    auto wrow_of = [&](int j) -> const T* {
+        if (j < R) return Wd + (size_t)j * Dm;
+        if (j < R + H) return ub + (size_t)(j - R) * Dm;
+        if (uf && j < R + 2 * H) return uf + (size_t)(j - R - H) * Dm;
+        return nullptr;
+    };
+    // this thread's 16-byte units of a chunk: x first (64 rows), then weights
+    constexpr int UPR = S::UPR;
+    const int xunits = 64 * UPR, units = xunits + nrows_w * UPR;
+    constexpr int MAXU = (64 + 32 * kProjTiles) * UPR / 128 + 1;
+    const char* src[MAXU];
+    int dst[MAXU];
+    bool live[MAXU];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<f32x4*>(out + 8 * i) =
-                f32x4{acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]};
+    for (int i = 0; i < MAXU; ++i) {
+        const int u = tid + 128 * i;
+        live[i] = u < units;
+        const int uu = live[i] ? u : 0;
+        const bool isx = uu < xunits;
+        const int rr = isx ? uu / UPR : (uu - xunits) / UPR, ux = uu % UPR;
+        const T* base = nullptr;
+        if (isx) {
+            base = t0 + rr < M ? x + (size_t)(t0 + rr) * Dm : nullptr;
+        } else {
+            base = wrow_of(32 * jt0 + rr);
+        }
+        src[i] = base ? reinterpret_cast<const char*>(base) + 16 * ux : nullptr;
+        dst[i] = (isx ? 0 : S::XB) + rr * S::RS + 16 * ux;
     }
+    u32x4 pre[MAXU];
+    const int nchunks = Dm / kProjK + (Dm % kProjK ? 1 : 0);
+    auto fetch = [&](int kc) {
+        const int kbytes = kc * kProjK * (int)sizeof(T);
+#pragma unroll
+        for (int i = 0; i < MAXU; ++i) {
+            const bool ok = live[i] && src[i] && kbytes + (dst[i] % S::RS) < Dm * (int)sizeof(T);
+            pre[i] = ok ? *reinterpret_cast<const u32x4*>(src[i] + kbytes) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < MAXU; ++i)
+            if (live[i]) *reinterpret_cast<u32x4*>(lds[buf] + dst[i]) = pre[i];
+    };
+    f32x16 acc[kProjTiles];
+#pragma unroll
+    for (int q = 0; q < kProjTiles; ++q) acc[q] = zero16();
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int kc = 0; kc < nchunks; ++kc) {
+        const int buf = kc & 1;
+        if (kc + 1 < nchunks) fetch(kc + 1);
+        const char* xs = lds[buf] + (32 * wave + c) * S::RS;
+#pragma unroll
+        for (int ks = 0; ks < kProjK / 16; ++ks) {
+            const int kb = (16 * ks + 8 * h) * (int)sizeof(T);
+            bf16x8 b[3];
+            ld8_parts(reinterpret_cast<const T*>(xs + kb), true, b);
+#pragma unroll
+            for (int q = 0; q < kProjTiles; ++q) {
+                if (q < nt) {
+                    bf16x8 a[3];
+                    ld8_parts(reinterpret_cast<const T*>(lds[buf] + S::XB + (32 * q + c) * S::RS + kb),
+                              true, a);
+                    acc[q] = mfma_parts<T>(a, b, acc[q]);
+                }
+            }
+        }
+        if (kc + 1 < nchunks) stash(buf ^ 1);
+        __syncthreads();
+    }
+    const int t = t0 + 32 * wave + c;
+    if (t < M) {
+        // lane: token t; registers 4i..4i+3 of tile q: columns 32(jt0+q) + 8i + 4h
+#pragma unroll
+        for (int q = 0; q < kProjTiles; ++q) {
+            if (q < nt) {
+                float* out = P + (size_t)t * Rp + 32 * (jt0 + q) + 4 * h;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<f32x4*>(out + 8 * i) =
+                        f32x4{acc[q][4 * i], acc[q][4 * i + 1], acc[q][4 * i + 2], acc[q][4 * i + 3]};
+            }
+        }
+    }
+}
+
+__device__ inline float sigmoid2(float z) { return 2.f / (1.f + __expf(-z)); }
+__device__ inline float log_sigmoid(float z) {
+    return z >= 0.f ? -log1pf(__expf(-z)) : z - log1pf(__expf(z));
 }
 
 // 8 consecutive values as float (16- or 32-byte aligned loads)
@@ -117,12 +207,15 @@ __device__ inline void ld8f(const float* p, float (&v)[8]) {
     }
 }
 
-__device__ inline float sigmoid2(float z) { return 2.f / (1.f + __expf(-z)); }
-__device__ inline float log_sigmoid(float z) {
-    return z >= 0.f ? -log1pf(__expf(-z)) : z - log1pf(__expf(z));
-}
+// One workgroup per (sequence n, 32 tokens, group of kHeadsPerGroup heads):
+// the tile's rows of P (two more before it for the convolution) are split
+// once into bf16 hi + lo in LDS; the four waves then take the group's heads
+// in turn, each forming c^T (D channels x 32 tokens) = sum over taps tau and
+// rank steps of (kc[:, tau] Wu) P_{t - tau}^T.  One load of a Wu fragment
+// serves the three taps, a head's taps are loaded before its products, and
+// the next rank step's Wu fragment is in flight while the current one is used.
+constexpr int kHeadsPerGroup = 8;
 
-// One wave per (sequence n, 32 tokens, head): c^T (D channels x 32 tokens).
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 param_finish_kernel(const float* __restrict__ P, const T* __restrict__ Wu,
@@ -130,106 +223,132 @@ param_finish_kernel(const float* __restrict__ P, const T* __restrict__ Wu,
                     const float* __restrict__ bf, int N, int L, int R, int H, int Rp,
                     T* __restrict__ w, float* __restrict__ beta, float* __restrict__ logf) {
     constexpr int CT = D < 32 ? 1 : D / 32;   // 32-channel tiles per head
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, c = lane & 31;
-    const int ntt = (L + 31) / 32;
-    const int job = blockIdx.x * 4 + wave;
-    if (job >= N * ntt * H) return;
-    const int hh = job % H, tt = (job / H) % ntt, n = job / (H * ntt);
-    const int t = 32 * tt + c;                 // this lane's token (B-operand column)
-    const size_t row = (size_t)n * L + t;
-    f32x16 acc[CT];
+    constexpr int PS = 256 + 8;               // LDS row stride (bf16) for R <= 256
+    __shared__ __attribute__((aligned(16))) __bf16 sPh[34 * PS], sPl[34 * PS];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
+    const int ntt = (L + 31) / 32, nhg = (H + kHeadsPerGroup - 1) / kHeadsPerGroup;
+    const int hg = blockIdx.x % nhg, tt = (blockIdx.x / nhg) % ntt, n = blockIdx.x / (nhg * ntt);
+    const int t0 = 32 * tt;
+    const int h_end = min(H, (hg + 1) * kHeadsPerGroup);
+    // stage P rows t0-2 .. t0+31 (zero outside [0, L)), split into hi + lo
+    const int upr = R / 4;
+    for (int u = tid; u < 34 * upr; u += 256) {
+        const int rr = u / upr, c4 = (u % upr) * 4, t = t0 - 2 + rr;
+        const bool tok = t >= 0 && t < L;
+        // unconditional load (clamped row), zeroed after: static wait counts
+        f32x4 v = *reinterpret_cast<const f32x4*>(P + ((size_t)n * L + (tok ? t : 0)) * Rp + c4);
+        if (!tok) v = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) acc[ct] = zero16();
-    for (int tau = 0; tau < 3; ++tau) {
-        const bool pok = t < L && t - tau >= 0;
-        const float* prow = P + (pok ? row - tau : 0) * Rp;
-        for (int r0 = 0; r0 < R; r0 += 16) {
-            bf16x8 bh, bl;
-            {
-                f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
-                if (pok) {
-                    a = *reinterpret_cast<const f32x4*>(prow + r0 + 8 * h);
-                    b = *reinterpret_cast<const f32x4*>(prow + r0 + 8 * h + 4);
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float v = e < 4 ? a[e] : b[e - 4];
-                    bh[e] = (__bf16)v;
-                    bl[e] = (__bf16)(v - (float)bh[e]);
-                }
-            }
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                const int chl = 32 * ct + c;              // channel within the head
-                const bool cok = chl < D;
-                const int ch = hh * D + (cok ? chl : 0);
-                const float k = cok ? kc[(size_t)ch * 3 + tau] : 0.f;
-                float wv[8];
-                ld8f(Wu + (size_t)ch * R + r0 + 8 * h, wv);
-                bf16x8 ah, al;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float v = k * wv[e];
-                    ah[e] = (__bf16)v;
-                    al[e] = (__bf16)(v - (float)ah[e]);
-                }
-                acc[ct] = mfma_split(ah, al, bh, bl, acc[ct]);
-            }
+        for (int e = 0; e < 4; ++e) {
+            const __bf16 hi = (__bf16)v[e];
+            sPh[rr * PS + c4 + e] = hi;
+            sPl[rr * PS + c4 + e] = (__bf16)(v[e] - (float)hi);
         }
     }
-    // lane: token t; registers 4i..4i+3 of tile ct: channels 32ct + 8i + 4h + j
-    float ss = 0.f;
+    __syncthreads();
+    const int t = t0 + c;                      // this lane's token (B-operand column)
+    const size_t row = (size_t)n * L + t;
+    for (int hh = hg * kHeadsPerGroup + wave; hh < h_end; hh += 4) {
+        f32x16 acc[CT];
+        int ch[CT];
+        float kt[CT][3], wnext[CT][8];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+        for (int ct = 0; ct < CT; ++ct) {
+            acc[ct] = zero16();
+            const int chl = 32 * ct + c;              // channel within the head
+            const bool cok = chl < D;
+            ch[ct] = hh * D + (cok ? chl : 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ss += acc[ct][r] * acc[ct][r];
-    ss = pair_sum(ss);
-    const float inv = ss > 0.f ? rsqrtf(ss) : 0.f;
-    if (t < L) {
-        T* wo = w + (((size_t)n * H + hh) * L + t) * D;
+            for (int tau = 0; tau < 3; ++tau) {
+                const float kv = kc[(size_t)ch[ct] * 3 + tau];
+                kt[ct][tau] = cok ? kv : 0.f;
+            }
+            ld8f(Wu + (size_t)ch[ct] * R + 8 * h, wnext[ct]);
+        }
+        for (int r0 = 0; r0 < R; r0 += 16) {
+            float wcur[CT][8];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) wcur[ct][e] = wnext[ct][e];
+            {
+                // the next rank step's fragment (the last step reloads its own)
+                const int rn = r0 + 16 < R ? r0 + 16 : r0;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) ld8f(Wu + (size_t)ch[ct] * R + rn + 8 * h, wnext[ct]);
+            }
+#pragma unroll
+            for (int tau = 0; tau < 3; ++tau) {
+                const int pr = (c + 2 - tau) * PS + r0 + 8 * h;   // row t - tau
+                const bf16x8 bh = *reinterpret_cast<const bf16x8*>(sPh + pr);
+                const bf16x8 bl = *reinterpret_cast<const bf16x8*>(sPl + pr);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    bf16x8 ah, al;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float v = kt[ct][tau] * wcur[ct][e];
+                        ah[e] = (__bf16)v;
+                        al[e] = (__bf16)(v - (float)ah[e]);
+                    }
+                    acc[ct] = mfma_split(ah, al, bh, bl, acc[ct]);
+                }
+            }
+        }
+        // lane: token t; registers 4i..4i+3 of tile ct: channels 32ct + 8i + 4h + j
+        float ss = 0.f;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ch0 = 32 * ct + 8 * i + 4 * h;
-                if (ch0 < D) {
-                    if constexpr (sizeof(T) == 2) {
-                        typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-                        bf16x4 pk;
+            for (int r = 0; r < 16; ++r) ss += acc[ct][r] * acc[ct][r];
+        ss = pair_sum(ss);
+        const float inv = ss > 0.f ? rsqrtf(ss) : 0.f;
+        if (t < L) {
+            T* wo = w + (((size_t)n * H + hh) * L + t) * D;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(acc[ct][4 * i + e] * inv);
-                        *reinterpret_cast<bf16x4*>(wo + ch0) = pk;
-                    } else {
-                        f32x4 pk;
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) pk[e] = acc[ct][4 * i + e] * inv;
-                        *reinterpret_cast<f32x4*>(wo + ch0) = pk;
+                for (int i = 0; i < 4; ++i) {
+                    const int ch0 = 32 * ct + 8 * i + 4 * h;
+                    if (ch0 < D) {
+                        if constexpr (sizeof(T) == 2) {
+                            typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+                            bf16x4 pk;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(acc[ct][4 * i + e] * inv);
+                            *reinterpret_cast<bf16x4*>(wo + ch0) = pk;
+                        } else {
+                            f32x4 pk;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) pk[e] = acc[ct][4 * i + e] * inv;
+                            *reinterpret_cast<f32x4*>(wo + ch0) = pk;
+                        }
                     }
                 }
+            if (h == 0) {
+                const size_t o = ((size_t)n * H + hh) * L + t;
+                beta[o] = sigmoid2(P[row * Rp + R + hh] + bb[hh]);
+                if (logf) logf[o] = log_sigmoid(P[row * Rp + R + H + hh] + bf[hh]);
             }
-        if (h == 0) {
-            const size_t o = ((size_t)n * H + hh) * L + t;
-            beta[o] = sigmoid2(P[row * Rp + R + hh] + bb[hh]);
-            if (logf) logf[o] = log_sigmoid(P[row * Rp + R + H + hh] + bf[hh]);
         }
     }
 }
 
 template <typename T, int D>
 hipError_t finish_t(const ParamArgs& a, hipStream_t st) {
-    const int ntt = (a.L + 31) / 32;
-    const long jobs = (long)a.N * ntt * a.H;
-    hipLaunchKernelGGL((param_finish_kernel<T, D>), dim3((unsigned)((jobs + 3) / 4)), dim3(256), 0,
-                       st, a.P, (const T*)a.Wu, a.kc, a.bb, a.bf, a.N, a.L, a.R, a.H, a.Rp,
-                       (T*)a.w, a.beta, a.logf);
+    const int ntt = (a.L + 31) / 32, nhg = (a.H + kHeadsPerGroup - 1) / kHeadsPerGroup;
+    hipLaunchKernelGGL((param_finish_kernel<T, D>), dim3((unsigned)((long)a.N * ntt * nhg)),
+                       dim3(256), 0, st, a.P, (const T*)a.Wu, a.kc, a.bb, a.bf, a.N, a.L, a.R,
+                       a.H, a.Rp, (T*)a.w, a.beta, a.logf);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_param_t(const ParamArgs& a, hipStream_t st) {
     const long M = (long)a.N * a.L;
-    const long tiles = ((M + 31) / 32) * (a.Rp / 32);
-    hipLaunchKernelGGL((param_project_kernel<T>), dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0,
+    const long ngroups = (a.Rp / 32 + kProjTiles - 1) / kProjTiles;
+    hipLaunchKernelGGL((param_project_kernel<T>), dim3((unsigned)(((M + 63) / 64) * ngroups)),
+                       dim3(128), 0,
                        st, (const T*)a.x, (const T*)a.Wd, (const T*)a.ub, (const T*)a.uf,
                        (int)M, a.Dm, a.R, a.H, a.Rp, a.P);
     hipError_t e = hipGetLastError();
