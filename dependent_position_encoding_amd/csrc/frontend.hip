@@ -215,6 +215,15 @@ __device__ inline void ld8f(const float* p, float (&v)[8]) {
 // serves the three taps, a head's taps are loaded before its products, and
 // the next rank step's Wu fragment is in flight while the current one is used.
 constexpr int kHeadsPerGroup = 8;
+constexpr int kOutPad = 8;    // LDS row padding (elements) of a wave's output tile
+
+// Dynamic LDS of the finish kernel: the staged P rows (hi and lo, 34 rows of
+// R + 8 bf16) and four per-wave output tiles (32 rows of D + kOutPad).
+template <typename T, int D>
+struct FinishLds {
+    __host__ __device__ static size_t out_offset(int R) { return ((size_t)2 * 34 * (R + 8) * 2 + 15) / 16 * 16; }
+    __host__ __device__ static size_t bytes(int R) { return out_offset(R) + (size_t)4 * 32 * (D + kOutPad) * sizeof(T); }
+};
 
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
@@ -223,8 +232,12 @@ param_finish_kernel(const float* __restrict__ P, const T* __restrict__ Wu,
                     const float* __restrict__ bf, int N, int L, int R, int H, int Rp,
                     T* __restrict__ w, float* __restrict__ beta, float* __restrict__ logf) {
     constexpr int CT = D < 32 ? 1 : D / 32;   // 32-channel tiles per head
-    constexpr int PS = 256 + 8;               // LDS row stride (bf16) for R <= 256
-    __shared__ __attribute__((aligned(16))) __bf16 sPh[34 * PS], sPl[34 * PS];
+    // dynamic LDS, sized for R at launch (FinishLds)
+    extern __shared__ __attribute__((aligned(16))) char dyn[];
+    const int PS = R + 8;                      // row stride (bf16) of the staged P
+    __bf16* sPh = reinterpret_cast<__bf16*>(dyn);
+    __bf16* sPl = sPh + 34 * PS;
+    T* sOutAll = reinterpret_cast<T*>(dyn + FinishLds<T, D>::out_offset(R));
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
     const int ntt = (L + 31) / 32, nhg = (H + kHeadsPerGroup - 1) / kHeadsPerGroup;
     const int hg = blockIdx.x % nhg, tt = (blockIdx.x / nhg) % ntt, n = blockIdx.x / (nhg * ntt);
@@ -246,10 +259,73 @@ param_finish_kernel(const float* __restrict__ P, const T* __restrict__ Wu,
         }
     }
     __syncthreads();
+    // bf16 weights: the group's taps, transposed to [tau][channel], for the
+    // combination after the products
+    __shared__ __attribute__((aligned(16))) float sKc[3][kHeadsPerGroup * D];
+    if constexpr (sizeof(T) == 2) {
+        const int hg0 = hg * kHeadsPerGroup;
+        for (int e = tid; e < 3 * kHeadsPerGroup * D; e += 256) {
+            const int tau = e / (kHeadsPerGroup * D), cl = e % (kHeadsPerGroup * D);
+            const int chg = hg0 * D + cl;
+            sKc[tau][cl] = chg < H * D ? kc[(size_t)chg * 3 + tau] : 0.f;
+        }
+        __syncthreads();
+    }
     const int t = t0 + c;                      // this lane's token (B-operand column)
     const size_t row = (size_t)n * L + t;
     for (int hh = hg * kHeadsPerGroup + wave; hh < h_end; hh += 4) {
         f32x16 acc[CT];
+        if constexpr (sizeof(T) == 2) {
+            // y_tau = Wu P_{t-tau}^T with the exact bf16 Wu as the A operand
+            // (P split hi + lo), then c = sum_tau kc[:, tau] * y_tau
+            f32x16 y[3][CT];
+#pragma unroll
+            for (int tau = 0; tau < 3; ++tau)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) y[tau][ct] = zero16();
+            for (int r0 = 0; r0 < R; r0 += 16) {
+                bf16x8 wa[CT];
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const int chl = 32 * ct + c;
+                    wa[ct] = *reinterpret_cast<const bf16x8*>(
+                        Wu + (size_t)(hh * D + (chl < D ? chl : 0)) * R + r0 + 8 * h);
+                    if (chl >= D) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) wa[ct][e] = (__bf16)0.f;
+                    }
+                }
+#pragma unroll
+                for (int tau = 0; tau < 3; ++tau) {
+                    const int pr = (c + 2 - tau) * PS + r0 + 8 * h;   // row t - tau
+                    const bf16x8 bh = *reinterpret_cast<const bf16x8*>(sPh + pr);
+                    const bf16x8 bl = *reinterpret_cast<const bf16x8*>(sPl + pr);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) {
+                        y[tau][ct] = mfma32(wa[ct], bl, y[tau][ct]);
+                        y[tau][ct] = mfma32(wa[ct], bh, y[tau][ct]);
+                    }
+                }
+            }
+            const int cl0 = (hh - hg * kHeadsPerGroup) * D;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ch0 = 32 * ct + 8 * i + 4 * h;
+                    f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, k2 = k0;
+                    if (ch0 < D) {
+                        k0 = *reinterpret_cast<const f32x4*>(&sKc[0][cl0 + ch0]);
+                        k1 = *reinterpret_cast<const f32x4*>(&sKc[1][cl0 + ch0]);
+                        k2 = *reinterpret_cast<const f32x4*>(&sKc[2][cl0 + ch0]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[ct][4 * i + j] = k0[j] * y[0][ct][4 * i + j] + k1[j] * y[1][ct][4 * i + j] +
+                                             k2[j] * y[2][ct][4 * i + j];
+                }
+            }
+        } else {
         int ch[CT];
         float kt[CT][3], wnext[CT][8];
 #pragma unroll
@@ -295,6 +371,7 @@ param_finish_kernel(const float* __restrict__ P, const T* __restrict__ Wu,
                 }
             }
         }
+        }
         // lane: token t; registers 4i..4i+3 of tile ct: channels 32ct + 8i + 4h + j
         float ss = 0.f;
 #pragma unroll
@@ -303,28 +380,37 @@ param_finish_kernel(const float* __restrict__ P, const T* __restrict__ Wu,
             for (int r = 0; r < 16; ++r) ss += acc[ct][r] * acc[ct][r];
         ss = pair_sum(ss);
         const float inv = ss > 0.f ? rsqrtf(ss) : 0.f;
-        if (t < L) {
-            T* wo = w + (((size_t)n * H + hh) * L + t) * D;
+        // the 32 x D tile of w goes out through this wave's LDS tile, so that
+        // the stores write whole rows (16 bytes per lane along a row)
+        T* sOut = sOutAll + wave * 32 * (D + kOutPad);
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ch0 = 32 * ct + 8 * i + 4 * h;
-                    if (ch0 < D) {
-                        if constexpr (sizeof(T) == 2) {
-                            typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-                            bf16x4 pk;
+            for (int i = 0; i < 4; ++i) {
+                const int ch0 = 32 * ct + 8 * i + 4 * h;
+                if (ch0 < D) {
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(acc[ct][4 * i + e] * inv);
-                            *reinterpret_cast<bf16x4*>(wo + ch0) = pk;
-                        } else {
-                            f32x4 pk;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) pk[e] = acc[ct][4 * i + e] * inv;
-                            *reinterpret_cast<f32x4*>(wo + ch0) = pk;
-                        }
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        sOut[c * (D + kOutPad) + ch0 + e] = from_f32<T>(acc[ct][4 * i + e] * inv);
                 }
+            }
+        __builtin_amdgcn_wave_barrier();
+        {
+            constexpr int UPR = D * (int)sizeof(T) / 16;          // 16-byte units per row
+            const int nrows = min(32, L - t0);
+            T* wbase = w + (((size_t)n * H + hh) * L + t0) * D;
+            for (int u = lane; u < nrows * UPR; u += 64) {
+                const int rr = u / UPR, x = u % UPR;
+                const unsigned* src = reinterpret_cast<const unsigned*>(
+                    reinterpret_cast<const char*>(sOut + rr * (D + kOutPad)) + 16 * x);
+                u32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = src[e];
+                reinterpret_cast<u32x4*>(wbase + (size_t)rr * D)[x] = v;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (t < L) {
             if (h == 0) {
                 const size_t o = ((size_t)n * H + hh) * L + t;
                 beta[o] = sigmoid2(P[row * Rp + R + hh] + bb[hh]);
@@ -337,9 +423,16 @@ param_finish_kernel(const float* __restrict__ P, const T* __restrict__ Wu,
 template <typename T, int D>
 hipError_t finish_t(const ParamArgs& a, hipStream_t st) {
     const int ntt = (a.L + 31) / 32, nhg = (a.H + kHeadsPerGroup - 1) / kHeadsPerGroup;
+    const size_t lds = FinishLds<T, D>::bytes(a.R);
+    if (lds > 65536) {   // beyond the default dynamic LDS limit (fp32 with a large rank)
+        const hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&param_finish_kernel<T, D>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((param_finish_kernel<T, D>), dim3((unsigned)((long)a.N * ntt * nhg)),
-                       dim3(256), 0, st, a.P, (const T*)a.Wu, a.kc, a.bb, a.bf, a.N, a.L, a.R,
-                       a.H, a.Rp, (T*)a.w, a.beta, a.logf);
+                       dim3(256), lds, st, a.P, (const T*)a.Wu, a.kc,
+                       a.bb, a.bf, a.N, a.L, a.R, a.H, a.Rp, (T*)a.w, a.beta, a.logf);
     return hipGetLastError();
 }
 
