@@ -378,9 +378,10 @@ def unfused_rates(pa, cache, tok, n, wl, dws, ot, lt, kb, vb, reps=20):
 def front_end_rate(pa, wl, dev, R=32, reps=10):
     """The parameter front-end (path_param_fwd: w, beta, log f from a layer
     input of width H*d, rank R) at the workload's token count, replayed from a
-    HIP graph.  Algorithmic bytes: the input x, the weights, and the outputs
-    w, beta, log f; the projected intermediate's round trip through the
-    workspace is reported beside them."""
+    HIP graph (median of five replays after three warm ones).  Algorithmic
+    bytes: the input x, the weights, and the outputs w, beta, log f; the
+    projected intermediate's round trip through the workspace is reported
+    beside them."""
     import torch
     import workloads
     N, H, L, d = wl.N, wl.H, wl.L, wl.d
@@ -403,14 +404,18 @@ def front_end_rate(pa, wl, dev, R=32, reps=10):
     with torch.cuda.graph(g):
         for _ in range(reps):
             fn()
-    g.replay()
+    for _ in range(3):
+        g.replay()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    g.replay()
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
+    times = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) / reps)
+    ms = sorted(times)[len(times) // 2]
     ngate = 2 if wl.fox else 1
     alg = (N * L * Dm * esz + (R * Dm + H * d * R + ngate * H * Dm) * esz + H * d * 12
            + N * H * L * d * esz + ngate * N * H * L * 4)

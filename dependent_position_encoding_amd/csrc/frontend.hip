@@ -8,18 +8,22 @@
 // Citations: [Notes s2.x] = reading-notes page "PaTH Attention:通过累积
 // Householder 变换编码位置" (cc.laoqi.cc), section 2.x.
 //
-// Two kernels, both on the matrix cores:
+// Two kernels, both on the matrix cores, both streaming their operands
+// HBM -> LDS with direct buffer loads (no registers in between):
 //   project: P = x [Wd; ub; uf]^T, one GEMM over the input width Dm, fp32
-//            [N*L, Rp] in the workspace (Rp = R + H (+ H) rounded up to 32).
-//   finish:  per (token tile of 32, head): c^T = sum_(tau, r) A[ch][(tau, r)]
-//            P[t - tau][r] with A[ch][(tau, r)] = kc[ch][tau] Wu[ch][r] -- the
-//            convolution folded into the contraction, so the three shifted
-//            rows of P are just more k-steps -- then the norm over the head's
-//            channels (a lane owns one token: a sum over its registers and one
-//            exchange with the other lane half), beta and log f from P's gate
-//            columns.
+//            [N*L, Rp] in the workspace.  Columns: [0, R) the low-rank p,
+//            then the H beta logits and (with a gate) the H gate logits, each
+//            block padded to H8 = H rounded up to 8 columns; Rp = the total
+//            rounded up to 32.
+//   finish:  per (token tile of 32, head): y_tau = Wu P_{t - tau}^T for the
+//            three taps, c = sum_tau kc[:, tau] y_tau, the norm over the
+//            head's channels (a lane owns one token: a sum over its registers
+//            and one exchange with the other lane half), beta and log f from
+//            P's gate columns.
 // Products are formed transposed (weights as the A operand) so that a lane
-// ends up owning one token and stores four consecutive outputs at a time.
+// ends up owning one token.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma.hpp"
@@ -28,32 +32,70 @@ namespace pa {
 
 namespace {
 
-// 8 consecutive inputs as bf16 operand parts: bf16 data is exact (one part),
-// fp32 data is split three ways (hi + mid + lo) for fp32 accuracy.
-__device__ inline void ld8_parts(const bf16* p, bool ok, bf16x8 (&o)[3]) {
-    if (ok) {
-        o[0] = *reinterpret_cast<const bf16x8*>(p);
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Direct HBM -> LDS loads through buffer resources.  One instruction moves 16
+// bytes per lane and the wave's 64 lanes land contiguously from a uniform LDS
+// address; each lane's source offset is free, so a permutation or a padding
+// of the units inside that 1 KB is a matter of addressing.  A lane offset past
+// the resource's range reads zeros: kOob marks units outside the data
+// (sequence edges, the tail of a row, padding).  The host keeps every
+// resource range below 2^31 bytes, so kOob plus a chunk offset stays past it.
+constexpr uint32_t kOob = 0x80000000u;
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc_of(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ inline void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                  char* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                             voff, soff, 0, 0);
+}
+// Vector-memory waits.  The counter drains in issue order, so waiting until
+// at most N operations are pending completes everything but the last N.
+template <int N>
+__device__ inline void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ inline void wait_vm0() { wait_vm<0>(); }
+// wait for a chunk when `ahead` later chunks of IPW loads each may stay pending
+template <int IPW, int J>
+__device__ inline void wait_ahead(int ahead) {
+    if constexpr (J == 0) {
+        wait_vm<0>();
     } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[0][e] = (__bf16)0.f;
+        if (ahead >= J) wait_vm<IPW * J>();
+        else wait_ahead<IPW, J - 1>(ahead);
     }
 }
-__device__ inline void ld8_parts(const float* p, bool ok, bf16x8 (&o)[3]) {
-    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
-    if (ok) {
-        a = *reinterpret_cast<const f32x4*>(p);
-        b = *reinterpret_cast<const f32x4*>(p + 4);
-    }
+// a workgroup barrier without the memory fence of __syncthreads (which would
+// also drain every load in flight); the empty asm statements keep the
+// compiler from moving memory accesses across it
+__device__ inline void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// 8 consecutive fp32 values split into bf16 parts: two (hi + lo, ~16
+// mantissa bits) or three (hi + mid + lo, fp32 accuracy).
+template <int PARTS>
+__device__ inline void split8(const f32x4& a, const f32x4& b, bf16x8 (&o)[3]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float x = e < 4 ? a[e] : b[e - 4];
         o[0][e] = (__bf16)x;
         const float r = x - (float)o[0][e];
         o[1][e] = (__bf16)r;
-        o[2][e] = (__bf16)(r - (float)o[1][e]);
+        if constexpr (PARTS == 3) o[2][e] = (__bf16)(r - (float)o[1][e]);
     }
 }
 
+// acc += A B over bf16 operand parts: bf16 data is exact (one part); fp32
+// data is split three ways and the six partial products that matter at fp32
+// precision are taken, smallest first.
 template <typename T>
 __device__ inline f32x16 mfma_parts(const bf16x8 (&a)[3], const bf16x8 (&b)[3], f32x16 acc) {
     if constexpr (sizeof(T) == 4) {
@@ -66,122 +108,165 @@ __device__ inline f32x16 mfma_parts(const bf16x8 (&a)[3], const bf16x8 (&b)[3], 
     return mfma32(a[0], b[0], acc);
 }
 
-// The projection GEMM.  One 128-thread workgroup (2 waves) per 64 tokens and
-// up to kProjTiles column tiles.  The input width Dm is walked in chunks of
-// 64: both operands' chunks are loaded with consecutive lanes along a row
-// (rows of x and of the weights lie Dm elements apart, so a lane-per-row
-// pattern would put every lane of an instruction on the same memory channel)
-// into LDS, double-buffered, the next chunk held in registers meanwhile.
-// Each wave forms 32 tokens x (32 kProjTiles) columns of P^T, one x fragment
-// serving all its column tiles.
-constexpr int kProjTiles = 4;
-constexpr int kProjK = 64;                  // chunk of the contraction
+// ---------------------------------------------------------------------------
+// The projection GEMM.  One 256-thread workgroup (4 waves) per 128 tokens and
+// NT 32-column tiles of P.  The input width is walked in chunks of 128 bytes
+// per row; a chunk of the 128 x rows and the 32 NT weight rows fills one stage
+// of an LDS ring as deep as LDS allows, so all but one of its stages are in
+// flight while the oldest is multiplied.  The stage's 1 KB groups of 8 rows
+// are dealt to the waves, 4 + NT loads each per chunk (always that many, so
+// the waits count statically).  Each wave forms 32 tokens x 32 NT columns of
+// P^T, one x fragment serving all its column tiles.  Weight rows come in
+// groups of 8 from Wd, ub or uf (R is a multiple of 16 and the gate blocks are
+// padded to 8), so a group's load has one source; rows past the data read
+// zeros.  Workgroups start at different chunks (and wrap around), so that at
+// any moment they read different 128-byte columns of rows that lie Dm
+// elements apart.
+constexpr int kProjTM = 128;
+constexpr int kProjMaxTiles = 4;
+constexpr int kProjLds = 140 * 1024;          // LDS budget of the ring
 
-template <typename T>
-struct ProjLds {
-    static constexpr int RS = kProjK * (int)sizeof(T) + 16;    // row stride, bytes (padded)
-    static constexpr int XB = 64 * RS;                          // x chunk: 64 tokens
-    static constexpr int WB = 32 * kProjTiles * RS;             // weight chunk
-    static constexpr int STAGE = XB + WB;
-    static constexpr int UPR = kProjK * (int)sizeof(T) / 16;   // 16-byte units per row
+template <int NT>
+struct ProjGeom {
+    static constexpr int IPW = 4 + NT;                      // loads per wave per chunk
+    static constexpr int STAGE = (kProjTM + 32 * NT) * 128;
+    static constexpr int STAGES = kProjLds / STAGE < 8 ? kProjLds / STAGE : 8;
 };
 
-template <typename T>
-__global__ void __launch_bounds__(128)
+// byte offset of 16-byte unit u of row r of a stage region: 8 units per row,
+// XOR-swizzled with bits 1..3 of the row, so that 16 consecutive rows read at
+// one unit (a quarter wave) fall into 16 different bank groups
+__device__ inline int proj_off(int r, int u) { return r * 128 + 16 * (u ^ ((r >> 1) & 7)); }
+
+// the 8 values k = 16 ks + 8 h .. +7 of row r of a region as operand parts
+__device__ inline void proj_parts(const char* reg, int r, int ks, int h, const bf16* /*tag*/,
+                                  bf16x8 (&o)[3]) {
+    o[0] = *reinterpret_cast<const bf16x8*>(reg + proj_off(r, 2 * ks + h));
+}
+__device__ inline void proj_parts(const char* reg, int r, int ks, int h, const float* /*tag*/,
+                                  bf16x8 (&o)[3]) {
+    const int u = 4 * ks + 2 * h;
+    split8<3>(*reinterpret_cast<const f32x4*>(reg + proj_off(r, u)),
+              *reinterpret_cast<const f32x4*>(reg + proj_off(r, u + 1)), o);
+}
+
+template <typename T, int NT>
+__global__ void __launch_bounds__(256)
 param_project_kernel(const T* __restrict__ x, const T* __restrict__ Wd, const T* __restrict__ ub,
-                     const T* __restrict__ uf, int M, int Dm, int R, int H, int Rp,
+                     const T* __restrict__ uf, int M, int Dm, int R, int H, int H8, int Rp,
                      float* __restrict__ P) {
-    using S = ProjLds<T>;
-    __shared__ __attribute__((aligned(16))) char lds[2][S::STAGE];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
-    const int ntn = Rp / 32, ngroups = (ntn + kProjTiles - 1) / kProjTiles;
+    using G = ProjGeom<NT>;
+    constexpr int IPW = G::IPW, S = G::STAGES;
+    __shared__ __attribute__((aligned(1024))) char lds[S][G::STAGE];
+    const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, c = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ngroups = (Rp / 32 + NT - 1) / NT;
     const int tb = blockIdx.x / ngroups, jg = blockIdx.x % ngroups;
-    const int t0 = 64 * tb, jt0 = jg * kProjTiles, nt = min(kProjTiles, ntn - jt0);
-    const int nrows_w = 32 * nt;
-    // row pointers of the weights behind P's columns (NULL rows are padding)
-    auto wrow_of = [&](int j) -> const T* {
-        if (j < R) return Wd + (size_t)j * Dm;
-        if (j < R + H) return ub + (size_t)(j - R) * Dm;
-        if (uf && j < R + 2 * H) return uf + (size_t)(j - R - H) * Dm;
-        return nullptr;
-    };
-    // this thread's 16-byte units of a chunk: x first (64 rows), then weights
-    constexpr int UPR = S::UPR;
-    const int xunits = 64 * UPR, units = xunits + nrows_w * UPR;
-    constexpr int MAXU = (64 + 32 * kProjTiles) * UPR / 128 + 1;
-    const char* src[MAXU];
-    int dst[MAXU];
-    bool live[MAXU];
+    const int t0 = kProjTM * tb, jt0 = jg * NT;
+    const uint32_t rowb = (uint32_t)Dm * sizeof(T);
+    // load i of this wave fills the stage's 1 KB group gi = IPW wave + i: x rows
+    // 8 gi .. (gi < 16) or weight rows 8 (gi - 16) ..; lane -> row + lane / 8,
+    // stored unit lane % 8 (holding unit u)
+    __amdgpu_buffer_rsrc_t rs[IPW];
+    uint32_t voff[IPW];
+    int lim[IPW];   // the chunk's byte offset must not exceed this (tail of a row)
+    const int rl = lane >> 3, pu = lane & 7;
 #pragma unroll
-    for (int i = 0; i < MAXU; ++i) {
-        const int u = tid + 128 * i;
-        live[i] = u < units;
-        const int uu = live[i] ? u : 0;
-        const bool isx = uu < xunits;
-        const int rr = isx ? uu / UPR : (uu - xunits) / UPR, ux = uu % UPR;
-        const T* base = nullptr;
+    for (int i = 0; i < IPW; ++i) {
+        const int gi = IPW * wave + i;
+        const bool isx = gi < 16;
+        const int r = 8 * (isx ? gi : gi - 16) + rl, u = pu ^ ((r >> 1) & 7);
+        uint32_t row = 0;
+        lim[i] = (int)rowb - 16 * u - 16;
         if (isx) {
-            base = t0 + rr < M ? x + (size_t)(t0 + rr) * Dm : nullptr;
+            rs[i] = rsrc_of(x + (size_t)t0 * Dm, (uint32_t)min(kProjTM, M - t0) * rowb);
+            row = r;
         } else {
-            base = wrow_of(32 * jt0 + rr);
-        }
-        src[i] = base ? reinterpret_cast<const char*>(base) + 16 * ux : nullptr;
-        dst[i] = (isx ? 0 : S::XB) + rr * S::RS + 16 * ux;
-    }
-    u32x4 pre[MAXU];
-    const int nchunks = Dm / kProjK + (Dm % kProjK ? 1 : 0);
-    auto fetch = [&](int kc) {
-        const int kbytes = kc * kProjK * (int)sizeof(T);
-#pragma unroll
-        for (int i = 0; i < MAXU; ++i) {
-            const bool ok = live[i] && src[i] && kbytes + (dst[i] % S::RS) < Dm * (int)sizeof(T);
-            pre[i] = ok ? *reinterpret_cast<const u32x4*>(src[i] + kbytes) : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto stash = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < MAXU; ++i)
-            if (live[i]) *reinterpret_cast<u32x4*>(lds[buf] + dst[i]) = pre[i];
-    };
-    f32x16 acc[kProjTiles];
-#pragma unroll
-    for (int q = 0; q < kProjTiles; ++q) acc[q] = zero16();
-    fetch(0);
-    stash(0);
-    __syncthreads();
-    for (int kc = 0; kc < nchunks; ++kc) {
-        const int buf = kc & 1;
-        if (kc + 1 < nchunks) fetch(kc + 1);
-        const char* xs = lds[buf] + (32 * wave + c) * S::RS;
-#pragma unroll
-        for (int ks = 0; ks < kProjK / 16; ++ks) {
-            const int kb = (16 * ks + 8 * h) * (int)sizeof(T);
-            bf16x8 b[3];
-            ld8_parts(reinterpret_cast<const T*>(xs + kb), true, b);
-#pragma unroll
-            for (int q = 0; q < kProjTiles; ++q) {
-                if (q < nt) {
-                    bf16x8 a[3];
-                    ld8_parts(reinterpret_cast<const T*>(lds[buf] + S::XB + (32 * q + c) * S::RS + kb),
-                              true, a);
-                    acc[q] = mfma_parts<T>(a, b, acc[q]);
-                }
+            const int col0 = 32 * jt0 + 8 * (gi - 16);   // the group's first column of P
+            if (col0 < R) {
+                rs[i] = rsrc_of(Wd, (uint32_t)R * rowb);
+                row = col0 + rl;
+            } else if (col0 < R + H8) {
+                rs[i] = rsrc_of(ub, (uint32_t)H * rowb);
+                row = col0 - R + rl;
+            } else if (uf && col0 < R + 2 * H8) {
+                rs[i] = rsrc_of(uf, (uint32_t)H * rowb);
+                row = col0 - R - H8 + rl;
+            } else {
+                rs[i] = rsrc_of(Wd, 0u);             // padding columns: zeros
+                lim[i] = -1;
             }
         }
-        if (kc + 1 < nchunks) stash(buf ^ 1);
-        __syncthreads();
+        voff[i] = row * rowb + 16 * u;
     }
-    const int t = t0 + 32 * wave + c;
+    const int nch = (int)((rowb + 127) / 128), rot = tb % nch;
+    auto issue = [&](int j, int st) {
+        const int kc = j + rot < nch ? j + rot : j + rot - nch;
+        char* dst = lds[st] + IPW * wave * 1024;
+        const int off = kc * 128;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i)
+            lds_load16(rs[i], off <= lim[i] ? voff[i] : kOob, (uint32_t)off, dst + i * 1024);
+    };
+    f32x16 acc[NT];
+#pragma unroll
+    for (int q = 0; q < NT; ++q) acc[q] = zero16();
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+        if (s < nch) issue(s, s);
+    int st = 0;
+    for (int j = 0; j < nch; ++j) {
+        // chunk j has landed once at most the chunks issued after it are pending
+        wait_ahead<IPW, S - 2>(min(nch - 1, j + S - 2) - j);
+        // every wave's part of chunk j has landed, and every wave is done with
+        // the stage of chunk j - 1 (its operands were consumed by its products)
+        bare_barrier();
+        if (j + S - 1 < nch) issue(j + S - 1, st == 0 ? S - 1 : st - 1);
+        const char* xs = lds[st];
+        const char* wsr = xs + kProjTM * 128;
+        // all of the chunk's operands first, then the products
+        constexpr int KS = 128 / (16 * (int)sizeof(T));
+        bf16x8 b[KS][3], a[KS][NT][3];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            proj_parts(xs, 32 * wave + c, ks, h, (const T*)nullptr, b[ks]);
+#pragma unroll
+            for (int q = 0; q < NT; ++q) proj_parts(wsr, 32 * q + c, ks, h, (const T*)nullptr, a[ks][q]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int q = 0; q < NT; ++q) acc[q] = mfma_parts<T>(a[ks][q], b[ks], acc[q]);
+        st = st + 1 == S ? 0 : st + 1;
+    }
+    const int t = t0 + 32 * wave + c, nt = min(NT, Rp / 32 - jt0);
     if (t < M) {
-        // lane: token t; registers 4i..4i+3 of tile q: columns 32(jt0+q) + 8i + 4h
+        // lane: token t; registers 4i..4i+3 of tile q: columns 32(jt0+q) + 8i + 4h.
+        // Low-rank columns go out split: each group of 8 holds its 8 bf16 hi
+        // parts, then its 8 lo parts (the bytes of 8 floats), the operand
+        // layout of the finish; gate columns stay float.
+        char* prow = reinterpret_cast<char*>(P + (size_t)t * Rp);
 #pragma unroll
-        for (int q = 0; q < kProjTiles; ++q) {
+        for (int q = 0; q < NT; ++q) {
             if (q < nt) {
-                float* out = P + (size_t)t * Rp + 32 * (jt0 + q) + 4 * h;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<f32x4*>(out + 8 * i) =
-                        f32x4{acc[q][4 * i], acc[q][4 * i + 1], acc[q][4 * i + 2], acc[q][4 * i + 3]};
+                for (int i = 0; i < 4; ++i) {
+                    const int col = 32 * (jt0 + q) + 8 * i;
+                    const f32x4 v = {acc[q][4 * i], acc[q][4 * i + 1], acc[q][4 * i + 2],
+                                     acc[q][4 * i + 3]};
+                    if (col < R) {
+                        bf16x4 hi, lo;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            hi[e] = (__bf16)v[e];
+                            lo[e] = (__bf16)(v[e] - (float)hi[e]);
+                        }
+                        *reinterpret_cast<bf16x4*>(prow + 4 * col + 8 * h) = hi;
+                        *reinterpret_cast<bf16x4*>(prow + 4 * col + 16 + 8 * h) = lo;
+                    } else {
+                        *reinterpret_cast<f32x4*>(prow + 4 * (col + 4 * h)) = v;
+                    }
+                }
             }
         }
     }
@@ -192,187 +277,230 @@ __device__ inline float log_sigmoid(float z) {
     return z >= 0.f ? -log1pf(__expf(-z)) : z - log1pf(__expf(z));
 }
 
-// 8 consecutive values as float (16- or 32-byte aligned loads)
-__device__ inline void ld8f(const bf16* p, float (&v)[8]) {
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
-}
-__device__ inline void ld8f(const float* p, float (&v)[8]) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        v[e] = a[e];
-        v[e + 4] = b[e];
+// ---------------------------------------------------------------------------
+// The finish.  A workgroup owns a group of four heads (one per wave) and walks
+// a sequence of 32-token tiles; tiles are dealt so that the head groups of one
+// tile run on the same XCD (blockIdx % 8), which then reads the tile's rows
+// of P once into its L2.  Per tile, the 34 rows of P it needs (its tokens and
+// the two before, zeros outside the sequence) are loaded straight into an LDS
+// stage while the previous tile is computed.  A stage row holds R/4 units of
+// p, then one unit with the group's four beta logits and one with its four
+// gate logits, its unit count made odd so that consecutive rows start in
+// different bank groups.  Per head: y_tau = Wu P_{t - tau}^T (Wu the A
+// operand; bf16 Wu exact, P split into hi + lo at the read), then
+// c = sum_tau kc[:, tau] y_tau, the norm, and w written through the wave's
+// LDS tile as whole rows -- a head's 32 tokens are one contiguous block of w.
+constexpr int kFinishHeads = 4;
+constexpr int kOutPad = 8;      // row padding (elements) of a wave's output tile
+
+struct FinishGeom {
+    int U, IPW;                  // units per stage row; loads per wave per stage
+    __host__ __device__ FinishGeom(int R, bool gate) {
+        U = (R / 4 + 1 + (gate ? 1 : 0)) | 1;
+        IPW = (34 * U + 255) / 256;
     }
-}
-
-// One workgroup per (sequence n, 32 tokens, group of kHeadsPerGroup heads):
-// the tile's rows of P (two more before it for the convolution) are split
-// once into bf16 hi + lo in LDS; the four waves then take the group's heads
-// in turn, each forming c^T (D channels x 32 tokens) = sum over taps tau and
-// rank steps of (kc[:, tau] Wu) P_{t - tau}^T.  One load of a Wu fragment
-// serves the three taps, a head's taps are loaded before its products, and
-// the next rank step's Wu fragment is in flight while the current one is used.
-constexpr int kHeadsPerGroup = 8;
-constexpr int kOutPad = 8;    // LDS row padding (elements) of a wave's output tile
-
-// Dynamic LDS of the finish kernel: the staged P rows (hi and lo, 34 rows of
-// R + 8 bf16) and four per-wave output tiles (32 rows of D + kOutPad).
-template <typename T, int D>
-struct FinishLds {
-    __host__ __device__ static size_t out_offset(int R) { return ((size_t)2 * 34 * (R + 8) * 2 + 15) / 16 * 16; }
-    __host__ __device__ static size_t bytes(int R) { return out_offset(R) + (size_t)4 * 32 * (D + kOutPad) * sizeof(T); }
+    __host__ __device__ int stage_bytes() const { return IPW * 4096; }
 };
 
 template <typename T, int D>
+__host__ __device__ constexpr int finish_out_bytes() {
+    return kFinishHeads * 32 * (D + kOutPad) * (int)sizeof(T);
+}
+template <typename T, int D>
+__host__ __device__ inline int finish_lds_bytes(int R, bool gate) {
+    return 2 * FinishGeom(R, gate).stage_bytes() + finish_out_bytes<T, D>() +
+           3 * kFinishHeads * D * 4;
+}
+
+// WS > 0: the wave's Wu fragments for R <= 16 WS held in registers (bf16);
+// WS == 0: loaded per rank step (any R, any dtype).
+template <typename T, int D, int WS>
 __global__ void __launch_bounds__(256)
 param_finish_kernel(const float* __restrict__ P, const T* __restrict__ Wu,
                     const float* __restrict__ kc, const float* __restrict__ bb,
-                    const float* __restrict__ bf, int N, int L, int R, int H, int Rp,
-                    T* __restrict__ w, float* __restrict__ beta, float* __restrict__ logf) {
-    constexpr int CT = D < 32 ? 1 : D / 32;   // 32-channel tiles per head
-    // dynamic LDS, sized for R at launch (FinishLds)
-    extern __shared__ __attribute__((aligned(16))) char dyn[];
-    const int PS = R + 8;                      // row stride (bf16) of the staged P
-    __bf16* sPh = reinterpret_cast<__bf16*>(dyn);
-    __bf16* sPl = sPh + 34 * PS;
-    T* sOutAll = reinterpret_cast<T*>(dyn + FinishLds<T, D>::out_offset(R));
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, c = lane & 31;
-    const int ntt = (L + 31) / 32, nhg = (H + kHeadsPerGroup - 1) / kHeadsPerGroup;
-    const int hg = blockIdx.x % nhg, tt = (blockIdx.x / nhg) % ntt, n = blockIdx.x / (nhg * ntt);
-    const int t0 = 32 * tt;
-    const int h_end = min(H, (hg + 1) * kHeadsPerGroup);
-    // stage P rows t0-2 .. t0+31 (zero outside [0, L)), split into hi + lo
-    const int upr = R / 4;
-    for (int u = tid; u < 34 * upr; u += 256) {
-        const int rr = u / upr, c4 = (u % upr) * 4, t = t0 - 2 + rr;
-        const bool tok = t >= 0 && t < L;
-        // unconditional load (clamped row), zeroed after: static wait counts
-        f32x4 v = *reinterpret_cast<const f32x4*>(P + ((size_t)n * L + (tok ? t : 0)) * Rp + c4);
-        if (!tok) v = f32x4{0.f, 0.f, 0.f, 0.f};
+                    const float* __restrict__ bf, int N, int L, int R, int H, int H8, int Rp,
+                    int nseq, T* __restrict__ w, float* __restrict__ beta,
+                    float* __restrict__ logf) {
+    static_assert(WS == 0 || sizeof(T) == 2, "register-held Wu is the bf16 path");
+    constexpr int CT = D < 32 ? 1 : D / 32;     // 32-channel tiles per head
+    constexpr int MAXI = WS > 0 ? 3 : 9;        // loads per wave per stage, bound
+    extern __shared__ __attribute__((aligned(1024))) char dyn[];
+    const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, c = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool gate = logf != nullptr;
+    const FinishGeom geo(R, gate);
+    const int U = geo.U, IPW = geo.IPW, SB = geo.stage_bytes();
+    T* sOut = reinterpret_cast<T*>(dyn + 2 * SB) + wave * 32 * (D + kOutPad);
+    float* sKc = reinterpret_cast<float*>(dyn + 2 * SB + finish_out_bytes<T, D>());
+    const int ntt = (L + 31) / 32, ntiles = N * ntt, nhg = (H + kFinishHeads - 1) / kFinishHeads;
+    const int x8 = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int hg = j % nhg, seq = x8 + 8 * (j / nhg);
+    if (seq >= ntiles) return;
+    const int hh = kFinishHeads * hg + wave;     // this wave's head
+    const bool hok = hh < H;
+
+    // this lane's stage units: row and float column of P (-1: padding)
+    int prow[MAXI], pcol[MAXI];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const __bf16 hi = (__bf16)v[e];
-            sPh[rr * PS + c4 + e] = hi;
-            sPl[rr * PS + c4 + e] = (__bf16)(v[e] - (float)hi);
+    for (int i = 0; i < MAXI; ++i) {
+        const int slot = (wave * IPW + i) * 64 + lane, row = slot / U, u = slot - row * U;
+        int col = -1;
+        if (row < 34) {
+            if (u < R / 4) col = 4 * u;
+            else if (u == R / 4) col = R + kFinishHeads * hg;
+            else if (gate && u == R / 4 + 1) col = R + H8 + kFinishHeads * hg;
         }
+        prow[i] = row;
+        pcol[i] = col;
     }
-    __syncthreads();
-    // bf16 weights: the group's taps, transposed to [tau][channel], for the
-    // combination after the products
-    __shared__ __attribute__((aligned(16))) float sKc[3][kHeadsPerGroup * D];
-    if constexpr (sizeof(T) == 2) {
-        const int hg0 = hg * kHeadsPerGroup;
-        for (int e = tid; e < 3 * kHeadsPerGroup * D; e += 256) {
-            const int tau = e / (kHeadsPerGroup * D), cl = e % (kHeadsPerGroup * D);
-            const int chg = hg0 * D + cl;
-            sKc[tau][cl] = chg < H * D ? kc[(size_t)chg * 3 + tau] : 0.f;
+    auto issue = [&](int g, char* st) {
+        const int n = g / ntt, t0 = 32 * (g - n * ntt);
+        const auto rs = rsrc_of(P + (size_t)n * L * Rp, (uint32_t)L * Rp * 4);
+        char* dst = st + wave * IPW * 1024;
+#pragma unroll
+        for (int i = 0; i < MAXI; ++i) {
+            if (i < IPW) {
+                const int t = t0 - 2 + prow[i];
+                const bool ok = pcol[i] >= 0 && t >= 0 && t < L;
+                lds_load16(rs, ok ? (uint32_t)(t * Rp + pcol[i]) * 4u : kOob, 0u, dst + i * 1024);
+            }
         }
-        __syncthreads();
+    };
+    // the group's taps, [tau][head-local channel], read before the first
+    // stage is requested and written after, so the reads overlap it
+    constexpr int KI = (3 * kFinishHeads * D + 255) / 256;
+    float kv[KI];
+#pragma unroll
+    for (int q = 0; q < KI; ++q) {
+        const int e = tid + 256 * q, tau = e / (kFinishHeads * D), cl = e - tau * kFinishHeads * D;
+        const int ch = kFinishHeads * hg * D + cl;
+        kv[q] = e < 3 * kFinishHeads * D && ch < H * D ? kc[(size_t)(ch < H * D ? ch : 0) * 3 + tau] : 0.f;
     }
-    const int t = t0 + c;                      // this lane's token (B-operand column)
-    const size_t row = (size_t)n * L + t;
-    for (int hh = hg * kHeadsPerGroup + wave; hh < h_end; hh += 4) {
-        f32x16 acc[CT];
-        if constexpr (sizeof(T) == 2) {
-            // y_tau = Wu P_{t-tau}^T with the exact bf16 Wu as the A operand
-            // (P split hi + lo), then c = sum_tau kc[:, tau] * y_tau
-            f32x16 y[3][CT];
+    const float bbh = hok ? bb[hh] : 0.f, bfh = hok && gate ? bf[hh] : 0.f;
+    bf16x8 wreg[CT][WS > 0 ? WS : 1];
+    if constexpr (WS > 0) {
 #pragma unroll
-            for (int tau = 0; tau < 3; ++tau)
+        for (int ct = 0; ct < CT; ++ct) {
+            const int chl = 32 * ct + c;
+            const bool ok = hok && chl < D;
+            const bf16* wp = reinterpret_cast<const bf16*>(Wu) + (size_t)(ok ? hh * D + chl : 0) * R;
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) y[tau][ct] = zero16();
-            for (int r0 = 0; r0 < R; r0 += 16) {
-                bf16x8 wa[CT];
+            for (int s = 0; s < WS; ++s) {
+                const int r0 = 16 * s < R ? 16 * s : 0;
+                wreg[ct][s] = *reinterpret_cast<const bf16x8*>(wp + r0 + 8 * h);
+                if (!ok) {
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    const int chl = 32 * ct + c;
-                    wa[ct] = *reinterpret_cast<const bf16x8*>(
-                        Wu + (size_t)(hh * D + (chl < D ? chl : 0)) * R + r0 + 8 * h);
-                    if (chl >= D) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) wa[ct][e] = (__bf16)0.f;
-                    }
-                }
-#pragma unroll
-                for (int tau = 0; tau < 3; ++tau) {
-                    const int pr = (c + 2 - tau) * PS + r0 + 8 * h;   // row t - tau
-                    const bf16x8 bh = *reinterpret_cast<const bf16x8*>(sPh + pr);
-                    const bf16x8 bl = *reinterpret_cast<const bf16x8*>(sPl + pr);
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) {
-                        y[tau][ct] = mfma32(wa[ct], bl, y[tau][ct]);
-                        y[tau][ct] = mfma32(wa[ct], bh, y[tau][ct]);
-                    }
+                    for (int e = 0; e < 8; ++e) wreg[ct][s][e] = (__bf16)0.f;
                 }
             }
-            const int cl0 = (hh - hg * kHeadsPerGroup) * D;
+        }
+    }
+
+    issue(seq, dyn);
+#pragma unroll
+    for (int q = 0; q < KI; ++q)
+        if (tid + 256 * q < 3 * kFinishHeads * D) sKc[tid + 256 * q] = kv[q];
+    // per tile, a head's wave stores exactly NROW + 1 (+ 1 with a gate) times:
+    // whole rows of w, then beta (and log f); lanes past the data are dropped
+    // by the buffer ranges.  The wait for a tile's stage therefore leaves the
+    // previous tile's stores in flight.
+    constexpr int UPR = D * (int)sizeof(T) / 16;      // 16-byte units per row of w
+    constexpr int NROW = 32 * UPR / 64;
+    int k = 0;
+    for (int g = seq; g < ntiles; g += nseq, ++k) {
+        if (k == 0 || !hok) wait_vm0();
+        else if (gate) wait_vm<NROW + 2>();
+        else wait_vm<NROW + 1>();
+        // this tile's stage has landed; the other stage is free
+        if (k == 0) __syncthreads();    // also publishes the taps
+        else bare_barrier();
+        char* st = dyn + (k & 1) * SB;
+        if (g + nseq < ntiles) issue(g + nseq, dyn + ((k + 1) & 1) * SB);
+        if (!hok) continue;
+        const int n = g / ntt, t0 = 32 * (g - n * ntt);
+        // B operand of tap tau, rank step r0: P row t - tau (stage row c + 2 - tau),
+        // ranks r0 + 8h .. +7: one group of 8, its hi unit then its lo unit
+        auto bpart = [&](int tau, int r0, bf16x8 (&o)[3]) {
+            const char* rp = st + ((c + 2 - tau) * U + r0 / 4 + 2 * h) * 16;
+            o[0] = *reinterpret_cast<const bf16x8*>(rp);
+            o[1] = *reinterpret_cast<const bf16x8*>(rp + 16);
+        };
+        // c = sum_tau kc[:, tau] y_tau; lane: token t0 + c, registers 4i..4i+3
+        // of tile ct: channels 32ct + 8i + 4h + j
+        f32x16 acc[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[ct] = zero16();
+        auto fold = [&](int tau, const f32x16 (&y)[CT]) {
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int ch0 = 32 * ct + 8 * i + 4 * h;
-                    f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, k2 = k0;
-                    if (ch0 < D) {
-                        k0 = *reinterpret_cast<const f32x4*>(&sKc[0][cl0 + ch0]);
-                        k1 = *reinterpret_cast<const f32x4*>(&sKc[1][cl0 + ch0]);
-                        k2 = *reinterpret_cast<const f32x4*>(&sKc[2][cl0 + ch0]);
-                    }
+                    f32x4 kt = {0.f, 0.f, 0.f, 0.f};
+                    if (ch0 < D) kt = *reinterpret_cast<const f32x4*>(sKc + (tau * kFinishHeads + wave) * D + ch0);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[ct][4 * i + j] = k0[j] * y[0][ct][4 * i + j] + k1[j] * y[1][ct][4 * i + j] +
-                                             k2[j] * y[2][ct][4 * i + j];
+                    for (int jj = 0; jj < 4; ++jj) acc[ct][4 * i + jj] += kt[jj] * y[ct][4 * i + jj];
+                }
+            }
+        };
+        // rank step by rank step, a Wu fragment serving the three taps
+        f32x16 y[3][CT];
+#pragma unroll
+        for (int tau = 0; tau < 3; ++tau)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) y[tau][ct] = zero16();
+        auto step = [&](const bf16x8 (&a)[CT][3], int r0) {
+#pragma unroll
+            for (int tau = 0; tau < 3; ++tau) {
+                bf16x8 b[3];
+                bpart(tau, r0, b);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    if constexpr (sizeof(T) == 2) {
+                        y[tau][ct] = mfma32(a[ct][0], b[1], y[tau][ct]);
+                        y[tau][ct] = mfma32(a[ct][0], b[0], y[tau][ct]);
+                    } else {
+                        y[tau][ct] = mfma_split(a[ct][0], a[ct][1], b[0], b[1], y[tau][ct]);
+                    }
+                }
+            }
+        };
+        if constexpr (WS > 0) {
+#pragma unroll
+            for (int s = 0; s < WS; ++s) {
+                if (16 * s < R) {
+                    bf16x8 a[CT][3];
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) a[ct][0] = wreg[ct][s];
+                    step(a, 16 * s);
                 }
             }
         } else {
-        int ch[CT];
-        float kt[CT][3], wnext[CT][8];
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            acc[ct] = zero16();
-            const int chl = 32 * ct + c;              // channel within the head
-            const bool cok = chl < D;
-            ch[ct] = hh * D + (cok ? chl : 0);
-#pragma unroll
-            for (int tau = 0; tau < 3; ++tau) {
-                const float kv = kc[(size_t)ch[ct] * 3 + tau];
-                kt[ct][tau] = cok ? kv : 0.f;
-            }
-            ld8f(Wu + (size_t)ch[ct] * R + 8 * h, wnext[ct]);
-        }
-        for (int r0 = 0; r0 < R; r0 += 16) {
-            float wcur[CT][8];
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) wcur[ct][e] = wnext[ct][e];
-            {
-                // the next rank step's fragment (the last step reloads its own)
-                const int rn = r0 + 16 < R ? r0 + 16 : r0;
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) ld8f(Wu + (size_t)ch[ct] * R + rn + 8 * h, wnext[ct]);
-            }
-#pragma unroll
-            for (int tau = 0; tau < 3; ++tau) {
-                const int pr = (c + 2 - tau) * PS + r0 + 8 * h;   // row t - tau
-                const bf16x8 bh = *reinterpret_cast<const bf16x8*>(sPh + pr);
-                const bf16x8 bl = *reinterpret_cast<const bf16x8*>(sPl + pr);
+            for (int r0 = 0; r0 < R; r0 += 16) {
+                bf16x8 a[CT][3];
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
-                    bf16x8 ah, al;
+                    const int chl = 32 * ct + c;
+                    const bool ok = chl < D;
+                    const T* wp = Wu + (size_t)(hh * D + (ok ? chl : 0)) * R + r0 + 8 * h;
+                    if constexpr (sizeof(T) == 2) {
+                        a[ct][0] = *reinterpret_cast<const bf16x8*>(wp);
+                        if (!ok) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float v = kt[ct][tau] * wcur[ct][e];
-                        ah[e] = (__bf16)v;
-                        al[e] = (__bf16)(v - (float)ah[e]);
+                            for (int e = 0; e < 8; ++e) a[ct][0][e] = (__bf16)0.f;
+                        }
+                    } else {
+                        f32x4 lo = *reinterpret_cast<const f32x4*>(wp);
+                        f32x4 hi = *reinterpret_cast<const f32x4*>(wp + 4);
+                        if (!ok) lo = hi = f32x4{0.f, 0.f, 0.f, 0.f};
+                        split8<2>(lo, hi, a[ct]);
                     }
-                    acc[ct] = mfma_split(ah, al, bh, bl, acc[ct]);
                 }
+                step(a, r0);
             }
         }
-        }
-        // lane: token t; registers 4i..4i+3 of tile ct: channels 32ct + 8i + 4h + j
+#pragma unroll
+        for (int tau = 0; tau < 3; ++tau) fold(tau, y[tau]);
         float ss = 0.f;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
@@ -380,83 +508,124 @@ param_finish_kernel(const float* __restrict__ P, const T* __restrict__ Wu,
             for (int r = 0; r < 16; ++r) ss += acc[ct][r] * acc[ct][r];
         ss = pair_sum(ss);
         const float inv = ss > 0.f ? rsqrtf(ss) : 0.f;
-        // the 32 x D tile of w goes out through this wave's LDS tile, so that
-        // the stores write whole rows (16 bytes per lane along a row)
-        T* sOut = sOutAll + wave * 32 * (D + kOutPad);
+        // the wave's 32 x D tile of w through its LDS tile, out as whole rows
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
+        for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int ch0 = 32 * ct + 8 * i + 4 * h;
                 if (ch0 < D) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        sOut[c * (D + kOutPad) + ch0 + e] = from_f32<T>(acc[ct][4 * i + e] * inv);
+                    T* o = sOut + c * (D + kOutPad) + ch0;
+                    if constexpr (sizeof(T) == 2) {
+                        *reinterpret_cast<bf16x4*>(o) =
+                            bf16x4{(__bf16)(acc[ct][4 * i] * inv), (__bf16)(acc[ct][4 * i + 1] * inv),
+                                   (__bf16)(acc[ct][4 * i + 2] * inv), (__bf16)(acc[ct][4 * i + 3] * inv)};
+                    } else {
+                        *reinterpret_cast<f32x4*>(o) =
+                            f32x4{acc[ct][4 * i] * inv, acc[ct][4 * i + 1] * inv,
+                                  acc[ct][4 * i + 2] * inv, acc[ct][4 * i + 3] * inv};
+                    }
                 }
             }
+        }
         __builtin_amdgcn_wave_barrier();
-        {
-            constexpr int UPR = D * (int)sizeof(T) / 16;          // 16-byte units per row
-            const int nrows = min(32, L - t0);
-            T* wbase = w + (((size_t)n * H + hh) * L + t0) * D;
-            for (int u = lane; u < nrows * UPR; u += 64) {
-                const int rr = u / UPR, x = u % UPR;
-                const unsigned* src = reinterpret_cast<const unsigned*>(
-                    reinterpret_cast<const char*>(sOut + rr * (D + kOutPad)) + 16 * x);
-                u32x4 v;
+        const int nrows = min(32, L - t0);
+        const size_t o = ((size_t)n * H + hh) * L + t0;     // the head's first row of the tile
+        const auto wr = rsrc_of(w + o * D, (uint32_t)(nrows * D * (int)sizeof(T)));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = src[e];
-                reinterpret_cast<u32x4*>(wbase + (size_t)rr * D)[x] = v;
-            }
+        for (int q = 0; q < NROW; ++q) {
+            const int u = lane + 64 * q, rr = u / UPR, xu = u - rr * UPR;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(
+                reinterpret_cast<const char*>(sOut + rr * (D + kOutPad)) + 16 * xu);
+            __builtin_amdgcn_raw_buffer_store_b128(v, wr, 16 * u, 0, 0);
         }
         __builtin_amdgcn_wave_barrier();
-        if (t < L) {
-            if (h == 0) {
-                const size_t o = ((size_t)n * H + hh) * L + t;
-                beta[o] = sigmoid2(P[row * Rp + R + hh] + bb[hh]);
-                if (logf) logf[o] = log_sigmoid(P[row * Rp + R + H + hh] + bf[hh]);
-            }
-        }
+        const float* zr = reinterpret_cast<const float*>(st + ((c + 2) * U + R / 4) * 16);
+        const int bo = h == 0 ? 4 * c : (int)kOob;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sigmoid2(zr[wave] + bbh)),
+                                              rsrc_of(beta + o, (uint32_t)nrows * 4), bo, 0, 0);
+        if (gate)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(log_sigmoid(zr[4 + wave] + bfh)),
+                                                  rsrc_of(logf + o, (uint32_t)nrows * 4), bo, 0, 0);
     }
+    wait_vm0();
+}
+
+// finish workgroups: each head group gets 8 m tile sequences (a multiple of
+// the XCD count), about three workgroups per CU in all
+constexpr int kFinishWgs = 768;
+
+template <typename T, int D, int WS>
+hipError_t finish_t(const ParamArgs& a, int H8, hipStream_t st) {
+    const bool gate = a.logf != nullptr;
+    const long ntiles = (long)a.N * ((a.L + 31) / 32);
+    const int nhg = (a.H + kFinishHeads - 1) / kFinishHeads;
+    const long m = std::max(1L, std::min((ntiles + 7) / 8, (long)kFinishWgs / (8 * nhg)));
+    const int nseq = (int)(8 * m);
+    const int lds = finish_lds_bytes<T, D>(a.R, gate);
+    if (lds > 65536) {   // beyond the default dynamic LDS limit (large ranks)
+        const hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&param_finish_kernel<T, D, WS>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((param_finish_kernel<T, D, WS>), dim3((unsigned)(nhg * nseq)), dim3(256),
+                       (size_t)lds, st, a.P, (const T*)a.Wu, a.kc, a.bb, a.bf, a.N, a.L, a.R,
+                       a.H, H8, a.Rp, nseq, (T*)a.w, a.beta, a.logf);
+    return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t finish_t(const ParamArgs& a, hipStream_t st) {
-    const int ntt = (a.L + 31) / 32, nhg = (a.H + kHeadsPerGroup - 1) / kHeadsPerGroup;
-    const size_t lds = FinishLds<T, D>::bytes(a.R);
-    if (lds > 65536) {   // beyond the default dynamic LDS limit (fp32 with a large rank)
-        const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&param_finish_kernel<T, D>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
+hipError_t finish_d(const ParamArgs& a, int H8, hipStream_t st) {
+    if constexpr (sizeof(T) == 2) {
+        if (a.R <= 32) return finish_t<T, D, 2>(a, H8, st);
+        if (a.R <= 64) return finish_t<T, D, 4>(a, H8, st);
     }
-    hipLaunchKernelGGL((param_finish_kernel<T, D>), dim3((unsigned)((long)a.N * ntt * nhg)),
-                       dim3(256), lds, st, a.P, (const T*)a.Wu, a.kc,
-                       a.bb, a.bf, a.N, a.L, a.R, a.H, a.Rp, (T*)a.w, a.beta, a.logf);
+    return finish_t<T, D, 0>(a, H8, st);
+}
+
+// column tiles per projection workgroup: the fewest groups of at most
+// kProjMaxTiles, then as even as they go
+template <typename T, int NT>
+hipError_t project_nt(const ParamArgs& a, long M, int H8, hipStream_t st) {
+    const long ngroups = (a.Rp / 32 + NT - 1) / NT;
+    hipLaunchKernelGGL((param_project_kernel<T, NT>),
+                       dim3((unsigned)(((M + kProjTM - 1) / kProjTM) * ngroups)), dim3(256), 0,
+                       st, (const T*)a.x, (const T*)a.Wd, (const T*)a.ub, (const T*)a.uf,
+                       (int)M, a.Dm, a.R, a.H, H8, a.Rp, a.P);
     return hipGetLastError();
+}
+template <typename T>
+hipError_t project_t(const ParamArgs& a, long M, int H8, hipStream_t st) {
+    const int ntn = a.Rp / 32, ngroups = (ntn + kProjMaxTiles - 1) / kProjMaxTiles;
+    switch ((ntn + ngroups - 1) / ngroups) {
+        case 1: return project_nt<T, 1>(a, M, H8, st);
+        case 2: return project_nt<T, 2>(a, M, H8, st);
+        case 3: return project_nt<T, 3>(a, M, H8, st);
+        default: return project_nt<T, 4>(a, M, H8, st);
+    }
 }
 
 template <typename T>
 hipError_t launch_param_t(const ParamArgs& a, hipStream_t st) {
     const long M = (long)a.N * a.L;
-    const long ngroups = (a.Rp / 32 + kProjTiles - 1) / kProjTiles;
-    hipLaunchKernelGGL((param_project_kernel<T>), dim3((unsigned)(((M + 63) / 64) * ngroups)),
-                       dim3(128), 0,
-                       st, (const T*)a.x, (const T*)a.Wd, (const T*)a.ub, (const T*)a.uf,
-                       (int)M, a.Dm, a.R, a.H, a.Rp, a.P);
-    hipError_t e = hipGetLastError();
+    const int H8 = (a.H + 7) / 8 * 8;
+    hipError_t e = project_t<T>(a, M, H8, st);
     if (e != hipSuccess) return e;
     switch (a.d) {
-        case 16: return finish_t<T, 16>(a, st);
-        case 32: return finish_t<T, 32>(a, st);
-        case 64: return finish_t<T, 64>(a, st);
+        case 16: return finish_d<T, 16>(a, H8, st);
+        case 32: return finish_d<T, 32>(a, H8, st);
+        case 64: return finish_d<T, 64>(a, H8, st);
     }
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int param_columns(int R, int H, bool gate) { return (R + H * (gate ? 2 : 1) + 31) / 32 * 32; }
+int param_columns(int R, int H, bool gate) {
+    const int H8 = (H + 7) / 8 * 8;
+    return (R + H8 * (gate ? 2 : 1) + 31) / 32 * 32;
+}
 
 hipError_t launch_param(const ParamArgs& a, hipStream_t st) {
     return a.bf16 ? launch_param_t<bf16>(a, st) : launch_param_t<float>(a, st);

@@ -129,8 +129,12 @@ path_status check_param(const path_param_desc* d) {
     if (d->Dm % 16 != 0) return fail(PATH_E_UNSUPPORTED, "Dm must be a multiple of 16");
     if (d->R % 16 != 0 || d->R > 256)
         return fail(PATH_E_UNSUPPORTED, "R must be a multiple of 16, at most 256");
+    if (d->Dm > 65536) return fail(PATH_E_UNSUPPORTED, "Dm must be at most 65536");
+    // the kernels address x rows, weight matrices and a sequence's rows of the
+    // intermediate through 32-bit buffer ranges
     if ((size_t)d->N * d->L > ((size_t)1 << 31) || (size_t)d->H * d->d > 65536 ||
-        (size_t)d->N * d->L * d->Dm > ((size_t)1 << 40))
+        (size_t)d->N * d->L * d->Dm > ((size_t)1 << 40) ||
+        (size_t)d->L * pa::param_columns(d->R, d->H, true) * 4 > ((size_t)1 << 30))
         return fail(PATH_E_SHAPE, "problem too large");
     return PATH_OK;
 }

@@ -209,10 +209,14 @@ path_status path_causal_attn_fwd(const path_fwd_desc *desc, const void *q,
  *   outputs w [N, H, L, d] in desc->dtype (bf16: round to nearest even),
  *   beta and logf [N, H, L] float32.
  * uf, bf and logf are all NULL (no forget gate) or all given.
- * Supported: d in {16, 32, 64}, Dm a multiple of 16, R a multiple of 16 with
- * 16 <= R <= 256; otherwise PATH_E_UNSUPPORTED.  N, L, H >= 1.
+ * Supported: d in {16, 32, 64}, Dm a multiple of 16 and at most 65536, R a
+ * multiple of 16 with 16 <= R <= 256; otherwise PATH_E_UNSUPPORTED.
+ * N, L, H >= 1; PATH_E_SHAPE when one sequence's rows of the intermediate
+ * would pass 1 GiB (L * Rp * 4 bytes).
  * ws: at least path_param_workspace(desc) bytes, 256-byte aligned; it holds
- * the projected [N*L, R + H (+ H) rounded up to 32] float32 intermediate.
+ * the projected float32 intermediate [N*L, Rp]: R low-rank columns, then H
+ * beta and (with a gate) H gate columns, each block padded to a multiple of
+ * 8, Rp the total rounded up to 32.
  * Same conventions as every other entry point (device pointers, no
  * allocation, no synchronisation, errors before launch). */
 typedef struct {

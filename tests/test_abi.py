@@ -128,7 +128,8 @@ def test_param_argument_errors():
         "x", "Wd", "Wu", "kc", "ub", "bb", "uf", "bf", "w", "beta", "logf", "ws")] + [
         kw.get("ws_bytes", ws), None]
     for kw, status in [(dict(N=0), 2), (dict(d=48), 4), (dict(Dm=40), 4), (dict(R=8), 4),
-                       (dict(R=272), 4), (dict(dtype=7), 3)]:
+                       (dict(R=272), 4), (dict(dtype=7), 3), (dict(Dm=65552), 4),
+                       (dict(L=1 << 24), 2)]:
         assert lib.path_param_fwd(*args(P(**kw))) == status, kw
     assert lib.path_param_fwd(*args(good, x=None)) == 1
     assert lib.path_param_fwd(*args(good, uf=None)) == 1                # gate args must match

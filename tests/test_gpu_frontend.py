@@ -43,6 +43,16 @@ def test_frontend_small(dtype, d):
     _run(2, 77, 64, 16, 3, d, dtype, gate=(d != 32))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("R,Dm,H,d", [(48, 80, 5, 32), (96, 208, 9, 64)])
+def test_frontend_ranks(dtype, R, Dm, H, d):
+    # ranks past the register-held up-projection (48: four rank steps; 96:
+    # loaded per step), an input width with a partial last chunk, head counts
+    # that are not a multiple of the 4-head group or the 8-column padding, and
+    # 150 tokens: a partial 128-token projection tile and 32-token finish tile
+    _run(1, 150, Dm, R, H, d, dtype, gate=True, seed=2)
+
+
 def test_frontend_lm_shape():
     # the LM-layer shape: 4 x 4096 tokens, 24 heads of 64 (width 1536), rank 32
     _run(4, 4096, 1536, 32, 24, 64, torch.bfloat16, gate=True, seed=1)
