@@ -272,9 +272,12 @@ param_project_kernel(const T* __restrict__ x, const T* __restrict__ Wd, const T*
     }
 }
 
-__device__ inline float sigmoid2(float z) { return 2.f / (1.f + __expf(-z)); }
+// beta = 2 sigma(z) and log sigma(z) = min(z, 0) - log(1 + e^-|z|), with the
+// hardware exp, log and reciprocal (relative errors of a few ulp; the log's
+// argument lies in (1, 2], so its absolute error stays near 1e-7)
+__device__ inline float sigmoid2(float z) { return 2.f * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
 __device__ inline float log_sigmoid(float z) {
-    return z >= 0.f ? -log1pf(__expf(-z)) : z - log1pf(__expf(z));
+    return fminf(z, 0.f) - __logf(1.f + __expf(-fabsf(z)));
 }
 
 // ---------------------------------------------------------------------------
@@ -468,7 +471,7 @@ param_finish_kernel(const float* __restrict__ P, const T* __restrict__ Wu,
         if constexpr (WS > 0) {
 #pragma unroll
             for (int s = 0; s < WS; ++s) {
-                if (16 * s < R) {
+                if (s == 0 || 16 * s < R) {       // R >= 16: the first step always runs
                     bf16x8 a[CT][3];
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) a[ct][0] = wreg[ct][s];
