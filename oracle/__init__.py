@@ -19,6 +19,11 @@ Householder 变换编码位置", sections 2.1, 2.5 and 2.8):
   2 sigma(.) and log f_t = log sigma(.) from a layer input x_t (sections 2.1
   and 2.5; the reading of the unstated details is in path_oracle.c).
 
+* ``bwd``: gradients of a scalar loss sum(do * o) with respect to q, k, v,
+  w, beta and log f -- reverse-mode differentiation of the same walk (the
+  pages give no backward formulas; finite differences of ``fwd_rows`` pin
+  it).
+
 Decode outputs need no function of their own: the output of the decode step
 at position t is row t of ``fwd_rows`` on the prompt and decoded tokens
 concatenated, which is what the pages' cache rewrite reproduces [s2.8].
@@ -65,6 +70,8 @@ class Oracle:
         lib.oracle_transported_keys.restype = ctypes.c_int
         lib.oracle_frontend.argtypes = [ctypes.c_int] * 6 + [P] * 11
         lib.oracle_frontend.restype = ctypes.c_int
+        lib.oracle_bwd.argtypes = [ctypes.c_int] * 4 + [P] * 6 + [ctypes.c_double] + [P] * 7
+        lib.oracle_bwd.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         self._lib = lib
@@ -132,6 +139,31 @@ class Oracle:
             raise ValueError("row index out of range")
         return o, lse
 
+    def bwd(self, q, k, v, w, beta, logf=None, scale=1.0, do=None):
+        """Gradients of sum(do * o) through PaTH(-FoX) attention, in fp64.
+
+        Shapes as fwd_rows; do: [S, L, dv].  Returns a dict with dq, dk, dw
+        [S, L, d], dv [S, L, dv], dbeta [S, L] and dlogf [S, L] (None without
+        a gate).
+        """
+        q, k, v, w, beta, do = (_f64(x) for x in (q, k, v, w, beta, do))
+        S, L, d = q.shape
+        dv = v.shape[2]
+        assert k.shape == (S, L, d) and w.shape == (S, L, d) and do.shape == (S, L, dv)
+        assert v.shape[:2] == (S, L) and beta.shape == (S, L)
+        if logf is not None:
+            logf = _f64(logf)
+            assert logf.shape == (S, L)
+        out = dict(dq=np.empty((S, L, d)), dk=np.empty((S, L, d)), dv=np.empty((S, L, dv)),
+                   dw=np.empty((S, L, d)), dbeta=np.empty((S, L)),
+                   dlogf=np.empty((S, L)) if logf is not None else None)
+        self._lib.oracle_bwd(
+            S, L, d, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta),
+            _ptr(logf) if logf is not None else None, float(scale), _ptr(do),
+            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dw"]),
+            _ptr(out["dbeta"]), _ptr(out["dlogf"]) if logf is not None else None)
+        return out
+
     def transported_keys(self, k, w, beta, t):
         """Keys after position t is processed: H_t...H_{j+1} k_j, j in [0, t].
 
@@ -174,3 +206,7 @@ def transported_keys(*args, **kwargs):
 
 def frontend(*args, **kwargs):
     return default().frontend(*args, **kwargs)
+
+
+def bwd(*args, **kwargs):
+    return default().bwd(*args, **kwargs)

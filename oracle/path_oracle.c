@@ -141,6 +141,115 @@ int oracle_transported_keys(int S, int L, int d, const double *k,
     return 0;
 }
 
+/*
+ * Gradients of a scalar loss through the forward pass above, given dL/do_i
+ * for every row (the loss does not read lse).  The pages give no backward
+ * formulas; this is reverse-mode differentiation of the definition as the
+ * walk evaluates it, row by row, and its results are checked against finite
+ * differences of oracle_fwd_rows.  For one row i:
+ *   softmax:  D = do_i . o_i;  ds_j = p_j (do_i . v_j - D);  dv_j += p_j do_i.
+ *   walk:     z_j = H_{j+1} ... H_i q_i is the vector key j was scored with
+ *             (z_i = q_i, z_{j-1} = H_j z_j).  Going back up from j = 0, with
+ *             g the gradient reaching z_{j-1} from the keys below j (zero at
+ *             j = 0: z_{-1} is never used):
+ *               dk_j    += scale ds_j z_j
+ *               dbeta_j += -(w_j . z_j)(w_j . g)
+ *               dw_j    += -beta_j ((w_j . g) z_j + (w_j . z_j) g)
+ *               g       <- scale ds_j k_j + H_j g      (H_j is symmetric)
+ *             and dq_i += g after the last key (j = i).
+ *   bias:     the logit of key j carries sum_{s=j+1..i} log f_s, so
+ *             dlogf_s += sum_{j<s} ds_j  for 1 <= s <= i.
+ * Consequences the tests pin: w_0, beta_0 and log f_0 get no gradient.
+ *   q, k, w : [S, L, d]   v, dout : [S, L, dv]   beta, logf : [S, L] (logf may be NULL)
+ *   outputs dq, dk, dw : [S, L, d]   dvv : [S, L, dv]   dbeta, dlogf : [S, L]
+ *   (dlogf is not written when logf is NULL).  Slices run in parallel.
+ */
+int oracle_bwd(int S, int L, int d, int dv, const double *q, const double *k,
+               const double *v, const double *w, const double *beta,
+               const double *logf, double scale, const double *dout,
+               double *dq, double *dk, double *dvv, double *dw, double *dbeta,
+               double *dlogf)
+{
+    memset(dq, 0, sizeof(double) * (size_t)S * L * d);
+    memset(dk, 0, sizeof(double) * (size_t)S * L * d);
+    memset(dw, 0, sizeof(double) * (size_t)S * L * d);
+    memset(dvv, 0, sizeof(double) * (size_t)S * L * dv);
+    memset(dbeta, 0, sizeof(double) * (size_t)S * L);
+    if (logf) memset(dlogf, 0, sizeof(double) * (size_t)S * L);
+    #pragma omp parallel
+    {
+        double *Z = (double *)malloc(sizeof(double) * (size_t)L * d);
+        double *sc = (double *)malloc(sizeof(double) * (size_t)L);
+        double *ds = (double *)malloc(sizeof(double) * (size_t)L);
+        double *o = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *g = (double *)malloc(sizeof(double) * (size_t)d);
+        double *gn = (double *)malloc(sizeof(double) * (size_t)d);
+        #pragma omp for schedule(dynamic, 1)
+        for (int s = 0; s < S; ++s) {
+            const size_t off = (size_t)s * L;
+            const double *qs = q + off * d, *ks = k + off * d, *ws = w + off * d;
+            const double *vs = v + off * dv, *bs = beta + off, *fs = logf ? logf + off : NULL;
+            double *dqs = dq + off * d, *dks = dk + off * d, *dws = dw + off * d;
+            double *dvs = dvv + off * dv, *dbs = dbeta + off, *dfs = logf ? dlogf + off : NULL;
+            for (int i = 0; i < L; ++i) {
+                const double *doi = dout + (off + i) * dv;
+                /* forward walk, keeping the vector each key is scored with */
+                memcpy(Z + (size_t)i * d, qs + (size_t)i * d, sizeof(double) * d);
+                double bias = 0.0;
+                for (int j = i; j >= 0; --j) {
+                    double *zj = Z + (size_t)j * d;
+                    sc[j] = scale * dot(d, ks + (size_t)j * d, zj) + bias;
+                    if (j > 0) {
+                        memcpy(zj - d, zj, sizeof(double) * d);
+                        apply_transition(d, ws + (size_t)j * d, bs[j], zj - d);
+                    }
+                    if (fs) bias += fs[j];
+                }
+                double m = -INFINITY, l = 0.0;
+                for (int j = 0; j <= i; ++j) if (sc[j] > m) m = sc[j];
+                for (int e = 0; e < dv; ++e) o[e] = 0.0;
+                for (int j = 0; j <= i; ++j) {
+                    sc[j] = exp(sc[j] - m);      /* unnormalised p_j */
+                    l += sc[j];
+                    for (int e = 0; e < dv; ++e) o[e] += sc[j] * vs[(size_t)j * dv + e];
+                }
+                for (int e = 0; e < dv; ++e) o[e] /= l;
+                /* softmax backward */
+                const double D = dot(dv, doi, o);
+                for (int j = 0; j <= i; ++j) {
+                    const double p = sc[j] / l;
+                    const double *vj = vs + (size_t)j * dv;
+                    ds[j] = p * (dot(dv, doi, vj) - D);
+                    for (int e = 0; e < dv; ++e) dvs[(size_t)j * dv + e] += p * doi[e];
+                }
+                /* walk backward, from the farthest key up to the query */
+                for (int e = 0; e < d; ++e) g[e] = 0.0;
+                for (int j = 0; j <= i; ++j) {
+                    const double *zj = Z + (size_t)j * d, *kj = ks + (size_t)j * d;
+                    const double *wj = ws + (size_t)j * d;
+                    for (int e = 0; e < d; ++e) dks[(size_t)j * d + e] += scale * ds[j] * zj[e];
+                    const double a = dot(d, wj, zj), b = dot(d, wj, g);
+                    dbs[j] += -a * b;
+                    for (int e = 0; e < d; ++e)
+                        dws[(size_t)j * d + e] += -bs[j] * (b * zj[e] + a * g[e]);
+                    for (int e = 0; e < d; ++e) gn[e] = scale * ds[j] * kj[e] + g[e] - bs[j] * b * wj[e];
+                    memcpy(g, gn, sizeof(double) * d);
+                }
+                for (int e = 0; e < d; ++e) dqs[(size_t)i * d + e] += g[e];
+                if (dfs) {
+                    double cum = 0.0;
+                    for (int j = 0; j < i; ++j) {
+                        cum += ds[j];
+                        dfs[j + 1] += cum;
+                    }
+                }
+            }
+        }
+        free(Z); free(sc); free(ds); free(o); free(g); free(gn);
+    }
+    return 0;
+}
+
 /* Number of OpenMP threads a parallel region of this library would use. */
 int oracle_num_threads(void)
 {
