@@ -61,7 +61,8 @@ EXPORTS = ["path_abi_version", "path_status_str", "path_last_error",
            "path_attn_fwd_workspace", "path_attn_fwd", "path_kv_update",
            "path_kv_append", "path_decode_workspace", "path_decode",
            "path_decode_step", "path_causal_attn_fwd", "path_attn_fwd_timed",
-           "path_param_workspace", "path_param_fwd"]
+           "path_param_workspace", "path_param_fwd", "path_attn_bwd_workspace",
+           "path_attn_bwd"]
 
 
 def load_library(path: str = LIB_PATH):
@@ -89,6 +90,8 @@ def load_library(path: str = LIB_PATH):
         "path_attn_fwd_timed": ([DP, P, P, P, P, P, P, P, P, CP, P, S, P, P], I),
         "path_param_workspace": ([ctypes.POINTER(_ParamDesc), I], S),
         "path_param_fwd": ([ctypes.POINTER(_ParamDesc)] + [P] * 12 + [S, P], I),
+        "path_attn_bwd_workspace": ([DP], S),
+        "path_attn_bwd": ([DP] + [P] * 16 + [S, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -200,6 +203,45 @@ def fwd(q, k, v, w, beta, logf=None, scale=None, cache: Cache | None = None,
         evs = (ctypes.c_void_p * 4)(*[e.cuda_event for e in _init_events(events, dev)])
         _check(lib.path_attn_fwd_timed(*args, evs))
     return o, lse
+
+
+def bwd_workspace_bytes(N, H, L, d, dtype, block=0) -> int:
+    lib = load_library()
+    return int(lib.path_attn_bwd_workspace(ctypes.byref(_desc(N, H, L, d, dtype, 1.0, block))))
+
+
+def bwd(q, k, v, w, beta, logf, o, lse, do, scale=None, workspace=None, out=None):
+    """Backward pass: gradients of a loss through fwd(), given do = dL/do.
+
+    q, k, v, w, o, do [N,H,L,d] (fp32 or bf16); beta, logf, lse [N,H,L] fp32
+    (logf None: plain PaTH).  Returns (dq, dk, dv, dw, dbeta, dlogf) with
+    dlogf None without a gate.
+    """
+    lib = load_library()
+    N, H, L, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("w", w), ("o", o), ("do", do)):
+        _need(t, name, dev, (N, H, L, d), q.dtype)
+    for name, t in (("beta", beta), ("lse", lse)):
+        _need(t, name, dev, (N, H, L), torch.float32)
+    if logf is not None:
+        _need(logf, "logf", dev, (N, H, L), torch.float32)
+    scale = d ** -0.5 if scale is None else scale
+    desc = _desc(N, H, L, d, q.dtype, scale)
+    nbytes = int(lib.path_attn_bwd_workspace(ctypes.byref(desc)))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        dq, dk, dv, dw = (torch.empty_like(q) for _ in range(4))
+        dbeta = torch.empty(N, H, L, dtype=torch.float32, device=dev)
+        dlogf = torch.empty(N, H, L, dtype=torch.float32, device=dev) if logf is not None else None
+    else:
+        dq, dk, dv, dw, dbeta, dlogf = out
+    _check(lib.path_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta),
+                             _ptr(logf), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                             _ptr(dv), _ptr(dw), _ptr(dbeta), _ptr(dlogf), _ptr(workspace),
+                             workspace.numel(), _stream(dev)))
+    return dq, dk, dv, dw, dbeta, dlogf
 
 
 def _init_events(events, dev):

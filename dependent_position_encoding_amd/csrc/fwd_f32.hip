@@ -318,6 +318,29 @@ static hipError_t launch_fwd_f32_b(const FwdArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+// The preconditioning step alone (block 64), for the backward pass, which
+// differentiates through these per-block products.
+template <typename T, int D>
+static hipError_t launch_precond_t(const FwdArgs& a, hipStream_t st) {
+    const int nb = (a.L + 63) / 64;
+    hipLaunchKernelGGL((precond_f32_kernel<T, 64, D>), dim3(a.N * a.H * nb), dim3(256), 0, st,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.w, a.beta, a.logf, a.L, nb,
+                       a.ws);
+    return hipGetLastError();
+}
+template <typename T>
+static hipError_t launch_precond_d(const FwdArgs& a, hipStream_t st) {
+    switch (a.d) {
+        case 16: return launch_precond_t<T, 16>(a, st);
+        case 32: return launch_precond_t<T, 32>(a, st);
+        case 64: return launch_precond_t<T, 64>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+hipError_t launch_precond_f32(const FwdArgs& a, hipStream_t st) {
+    return a.bf16 ? launch_precond_d<bf16>(a, st) : launch_precond_d<float>(a, st);
+}
+
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st) {
     return a.bf16 ? launch_fwd_f32_b<bf16>(a, st) : launch_fwd_f32_b<float>(a, st);
 }

@@ -119,6 +119,46 @@ path_status launched(hipError_t e, const char* what) {
     return ok();
 }
 
+// Backward workspace: the recomputed preconditioning, per-block gradients,
+// per-position sums, then the pair buffers and scratch for `chunk` slices at a
+// time (chunk chosen so those stay within kBwdChunkBytes).
+constexpr size_t kBwdChunkBytes = (size_t)4 << 30;
+
+struct BwdLayout {
+    size_t ql, kr, em, dg, gl, tot, dQl, dKr, dEm, dDg, rowsum, colsum, delta, X, Z, scr, total;
+    int chunk;
+};
+
+BwdLayout bwd_layout(const path_fwd_desc* d) {
+    const int B = pa::bwd_block(), D = d->d;
+    const size_t nb = (size_t)(d->L + B - 1) / B, ns = (size_t)d->N * d->H, nblk = ns * nb;
+    const size_t per_slice = 4 * (2 * pa::bwd_pair_floats(d->L, D, 1) + pa::bwd_scratch_floats(d->L, 1));
+    size_t chunk = per_slice ? kBwdChunkBytes / per_slice : ns;
+    chunk = chunk < 1 ? 1 : (chunk > ns ? ns : chunk);
+    BwdLayout l{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
+    l.ql = take(nblk * B * D * 4);
+    l.kr = take(nblk * B * D * 4);
+    l.em = take(nblk * D * D * 4);
+    l.dg = take(nblk * B * B * 4);
+    l.gl = take(nblk * B * 4);
+    l.tot = take(nblk * 4);
+    l.dQl = take(nblk * B * D * 4);
+    l.dKr = take(nblk * B * D * 4);
+    l.dEm = take(nblk * D * D * 4);
+    l.dDg = take(nblk * B * B * 4);
+    l.rowsum = take(nblk * B * 4);
+    l.colsum = take(nblk * B * 4);
+    l.delta = take(nblk * B * 4);
+    l.X = take(4 * pa::bwd_pair_floats(d->L, D, (int)chunk));
+    l.Z = take(4 * pa::bwd_pair_floats(d->L, D, (int)chunk));
+    l.scr = take(4 * pa::bwd_scratch_floats(d->L, (int)chunk));
+    l.total = off;
+    l.chunk = (int)chunk;
+    return l;
+}
+
 path_status check_param(const path_param_desc* d) {
     if (!d) return fail(PATH_E_NULL, "desc is NULL");
     if (d->N < 1 || d->L < 1 || d->H < 1 || d->Dm < 1 || d->R < 1)
@@ -343,6 +383,54 @@ path_status path_causal_attn_fwd(const path_fwd_desc* desc, const void* q, const
     a.bf16 = desc->dtype == PATH_BF16; a.scale = desc->scale;
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
     return launched(pa::launch_causal(a, stream), "path_causal_attn_fwd");
+}
+
+size_t path_attn_bwd_workspace(const path_fwd_desc* desc) {
+    if (check_desc(desc, true) != PATH_OK || block_of(desc) != pa::bwd_block()) return 0;
+    return bwd_layout(desc).total;
+}
+
+path_status path_attn_bwd(const path_fwd_desc* desc, const void* q, const void* k,
+                          const void* v, const void* w, const float* beta, const float* logf,
+                          const void* o, const float* lse, const void* dout, void* dq,
+                          void* dk, void* dv, void* dw, float* dbeta, float* dlogf, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+    path_status s = check_desc(desc, true);
+    if (s != PATH_OK) return s;
+    if (block_of(desc) != pa::bwd_block())
+        return fail(PATH_E_UNSUPPORTED, "the backward pass uses block 64");
+    if (!q || !k || !v || !w || !beta || !o || !lse || !dout || !dq || !dk || !dv || !dw ||
+        !dbeta)
+        return fail(PATH_E_NULL, "q, k, v, w, beta, o, lse, dout, dq, dk, dv, dw and dbeta are required");
+    if ((logf != nullptr) != (dlogf != nullptr))
+        return fail(PATH_E_NULL, "logf and dlogf must be given together");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(w, 16) ||
+        !aligned(o, 16) || !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) ||
+        !aligned(dv, 16) || !aligned(dw, 16))
+        return fail(PATH_E_ALIGN, "tensors of [N,H,L,d] must be 16-byte aligned");
+    if (!aligned(beta, 4) || !aligned(logf, 4) || !aligned(lse, 4) || !aligned(dbeta, 4) ||
+        !aligned(dlogf, 4))
+        return fail(PATH_E_ALIGN, "beta, logf, lse, dbeta and dlogf must be 4-byte aligned");
+    const BwdLayout lay = bwd_layout(desc);
+    if (!ws) return fail(PATH_E_WORKSPACE, "workspace is NULL");
+    if (!aligned(ws, 256)) return fail(PATH_E_ALIGN, "workspace must be 256-byte aligned");
+    if (ws_bytes < lay.total) return fail(PATH_E_WORKSPACE, "workspace smaller than path_attn_bwd_workspace()");
+    char* base = static_cast<char*>(ws);
+    auto at = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
+    pa::BwdArgs a{};
+    a.N = desc->N; a.H = desc->H; a.L = desc->L; a.d = desc->d;
+    a.bf16 = desc->dtype == PATH_BF16; a.scale = desc->scale;
+    a.q = q; a.k = k; a.v = v; a.w = w; a.o = o; a.dout = dout;
+    a.beta = beta; a.logf = logf; a.lse = lse;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dw = dw; a.dbeta = dbeta; a.dlogf = dlogf;
+    a.fw.ql = at(lay.ql); a.fw.kr = at(lay.kr); a.fw.em = at(lay.em); a.fw.dg = at(lay.dg);
+    a.fw.gl = at(lay.gl); a.fw.tot = at(lay.tot);
+    a.X = at(lay.X); a.Z = at(lay.Z);
+    a.dQl = at(lay.dQl); a.dKr = at(lay.dKr); a.dEm = at(lay.dEm); a.dDg = at(lay.dDg);
+    a.rowsum = at(lay.rowsum); a.colsum = at(lay.colsum); a.delta = at(lay.delta);
+    a.scr = at(lay.scr);
+    a.chunk = lay.chunk;
+    return launched(pa::launch_bwd(a, stream), "path_attn_bwd");
 }
 
 size_t path_param_workspace(const path_param_desc* desc, int with_gate) {

@@ -71,6 +71,30 @@ int decode_max_keys();   // longest cache one decode call can attend over
 bool causal_supported(int d, bool bf16);
 hipError_t launch_causal(const FwdArgs& a, hipStream_t st);
 
+// the preconditioning step alone (block 64, fp32 products in ws.ql/kr/em/dg/gl/tot)
+hipError_t launch_precond_f32(const FwdArgs& a, hipStream_t st);
+
+// backward pass (block 64)
+struct BwdArgs {
+    int N, H, L, d;
+    bool bf16;
+    float scale;
+    const void *q, *k, *v, *w, *o, *dout;
+    const float *beta, *logf, *lse;
+    void *dq, *dk, *dv, *dw;
+    float *dbeta, *dlogf;
+    FwdWs fw;            // recomputed preconditioning (ql, kr, em, dg, gl, tot; fp32)
+    float *X, *Z;        // per block pair of a chunk of slices [slice][pair][B][d]
+    float *dQl, *dKr, *dEm, *dDg;   // per block: gradients of the preconditioned products
+    float *rowsum, *colsum, *delta; // per position [blk][B]
+    float* scr;          // per block of a chunk: scratch of the preconditioning's backward
+    int chunk;           // slices per pass over the pair buffers
+};
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t st);
+size_t bwd_pair_floats(int L, int d, int chunk);     // X (and Z) for a chunk
+size_t bwd_scratch_floats(int L, int chunk);         // scr for a chunk
+int bwd_block();
+
 // parameter front-end (w, beta, log f from a layer input)
 struct ParamArgs {
     int N, L, Dm, R, H, d, Rp;

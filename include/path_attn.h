@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define PATH_ATTN_ABI_VERSION 2
+#define PATH_ATTN_ABI_VERSION 3
 
 typedef enum {
     PATH_OK = 0,
@@ -137,6 +137,42 @@ path_status path_attn_fwd_timed(const path_fwd_desc *desc, const void *q,
                                 float *lse, const path_cache *cache_out,
                                 void *ws, size_t ws_bytes, hipStream_t stream,
                                 hipEvent_t ev[4]);
+
+/* Bytes of device workspace path_attn_bwd needs (0 if the description is
+ * invalid or its block is not 64).  It holds the recomputed preconditioning,
+ * per-block gradients, and per block pair of a bounded group of slices (the
+ * call walks the slices in groups so this part stays within 4 GiB) the
+ * queries carried to each key block and the gradient chain. */
+size_t path_attn_bwd_workspace(const path_fwd_desc *desc);
+
+/*
+ * Backward pass (training): gradients of a scalar loss with respect to q, k,
+ * v, w, beta and log f, given dL/do.  The pages give no backward formulas;
+ * this differentiates the forward's block algorithm [Notes s2.6-s2.7], the
+ * same function as the definition [Notes s2.1, s2.5], so the gradients are
+ * those of the definition.  The loss is taken not to depend on lse.
+ *   desc       : as for path_attn_fwd; block must be 0 or 64.
+ *   q, k, v, w, beta, logf : the forward's inputs (logf NULL: plain PaTH)
+ *   o, lse     : the forward's outputs for these inputs (lse required)
+ *   dout       : [N, H, L, d] desc->dtype, dL/do
+ *   dq, dk, dv, dw : [N, H, L, d] desc->dtype (written)
+ *   dbeta      : [N, H, L] float32 (written)
+ *   dlogf      : [N, H, L] float32 (written; dlogf[.., 0] = 0, since log f at
+ *                the first position never reaches an output), given exactly
+ *                when logf is given
+ *   ws, ws_bytes : at least path_attn_bwd_workspace(desc) bytes, 256-byte
+ *                aligned; contents need not be initialised.
+ * Same conventions as path_attn_fwd (device pointers, no allocation, no
+ * synchronisation, argument errors before launch).  Products run on the
+ * matrix cores from fp32 operands split into bf16 parts (two for bf16 data,
+ * three for fp32 data).
+ */
+path_status path_attn_bwd(const path_fwd_desc *desc, const void *q,
+                          const void *k, const void *v, const void *w,
+                          const float *beta, const float *logf, const void *o,
+                          const float *lse, const void *dout, void *dq, void *dk,
+                          void *dv, void *dw, float *dbeta, float *dlogf,
+                          void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Cache rewrite for a new position [Notes s2.8, eq. (1) of the paper]:
  *   k_j <- k_j - beta_t (w_t^T k_j) w_t   for every slot j in [0, n).

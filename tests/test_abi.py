@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     pa, lib = _lib()
-    assert lib.path_abi_version() == 2
+    assert lib.path_abi_version() == 3
     for s in range(9):
         assert lib.path_status_str(s)
     assert lib.path_status_str(99) == b"unknown status"

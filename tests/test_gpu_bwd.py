@@ -1,0 +1,110 @@
+"""GPU parity of the backward pass (path_attn_bwd, through the C ABI) against
+the fp64 oracle's gradients (oracle.bwd), on the same inputs: the forward's
+inputs, dL/do, and the forward's own o and lse.
+
+Bars, relative to each gradient's largest reference magnitude g_max (the
+gradients are sums of many terms whose scale depends on the tensor; g_max is
+taken as at least 1, so gradients smaller than that get an absolute bar):
+  float32 inputs: max |err| <= 1e-4 g_max;
+  bf16 inputs:    max |err| <= 2e-2 g_max and sum |err| / sum |ref| <= 1e-2.
+The bf16 bar follows from the arithmetic: the rows' Delta_i = do_i . o_i
+uses the forward's bf16-rounded o (relative error 2^-9 per element), which
+enters every dS_ij, and every gradient is itself rounded to bf16 (2^-9); the
+products carry ~16 mantissa bits (hi + lo operand parts).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+NAMES = ("dq", "dk", "dv", "dw", "dbeta", "dlogf")
+
+
+def _pa():
+    import dependent_position_encoding_amd as pa
+    pa.load_library()
+    return pa
+
+
+def _errs(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), "non-finite gradient"
+    gmax = max(float(np.abs(ref).max()), 1.0)   # an absolute bar for small gradients
+    err = np.abs(got - ref)
+    return float(err.max()) / gmax, float(err.sum() / max(np.abs(ref).sum(), 1e-300)), gmax
+
+
+def _run(wl, L, seed=0):
+    pa = _pa()
+    x = workloads.make_inputs(wl, device="cpu", variant=seed, L=L)
+    g = {k: (v.to(DEV) if v is not None else None) for k, v in x.items()}
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(1234 + seed)
+    do = torch.randn(g["q"].shape, generator=gen).to(wl.dtype).to(DEV)
+    print(f"case bwd {wl.name} N={wl.N} H={wl.H} L={L} d={wl.d} {wl.dtype} fox={wl.fox}",
+          flush=True)
+    o, lse = pa.fwd(g["q"], g["k"], g["v"], g["w"], g["beta"], logf=g["logf"], scale=wl.scale)
+    grads = pa.bwd(g["q"], g["k"], g["v"], g["w"], g["beta"], g["logf"], o, lse, do,
+                   scale=wl.scale)
+    torch.cuda.synchronize()
+    f64 = {k: (workloads.as_slices_f64(v) if v is not None else None) for k, v in x.items()}
+    ref = oracle.bwd(f64["q"], f64["k"], f64["v"], f64["w"], f64["beta"], f64["logf"],
+                     wl.scale, workloads.as_slices_f64(do))
+    bf16 = wl.dtype == torch.bfloat16
+    out = {}
+    for name, got in zip(NAMES, grads):
+        if ref[name] is None:
+            assert got is None
+            continue
+        gm = workloads.as_slices_f64(got)
+        ma, mr, gmax = _errs(gm, ref[name])
+        ok = ma <= 2e-2 and mr <= 1e-2 if bf16 else ma <= 1e-4
+        msg = f"  {name}: max-err/g_max {ma:.2e} mean-rel {mr:.2e} (g_max {gmax:.3g})"
+        print(msg, flush=True)
+        out[name] = (ok, msg)
+    bad = [m for ok, m in out.values() if not ok]
+    assert not bad, bad
+    return grads, ref
+
+
+@pytest.mark.parametrize("d", [16, 32, 64])
+@pytest.mark.parametrize("fox", [False, True])
+def test_bwd_fp32(d, fox):
+    # three blocks, the last one ragged
+    wl = workloads.CONFIGS["tiny"].replace(H=2, d=d, fox=fox, scale=d ** -0.5)
+    _run(wl, L=150)
+
+
+def test_bwd_fp32_one_block_and_single_token():
+    wl = workloads.CONFIGS["tiny"].replace(H=2, fox=True)
+    _run(wl, L=64)
+    grads, ref = _run(wl, L=1)
+    # one key per row: P = 1 and dS = 0 (up to the rounding of do . o against
+    # do . v), so only v gets gradient, and dv = do
+    for t in (grads[0], grads[1], grads[3], grads[4]):
+        assert t.abs().max().item() < 1e-5
+
+
+def test_bwd_fp32_near_reflections():
+    wl = workloads.stress(workloads.CONFIGS["tiny"].replace(H=2, d=32, fox=True,
+                                                            scale=32 ** -0.5))
+    _run(wl, L=200, seed=1)
+
+
+@pytest.mark.parametrize("fox", [False, True])
+def test_bwd_bf16(fox):
+    wl = workloads.CONFIGS["lm"].replace(N=1, H=2, fox=fox)
+    _run(wl, L=150)
+
+
+def test_bwd_bf16_many_blocks():
+    # 16 blocks: long transition chains through the scan's backward
+    wl = workloads.CONFIGS["fox"].replace(N=1, H=2)
+    _run(wl, L=1024, seed=2)
