@@ -46,35 +46,80 @@ struct Dims {
     static constexpr int LD = DP + 4;            // LDS row stride of a B x DP / DP x DP tile
 };
 
-// 8 fp32 values as bf16 operand parts: hi + lo (2) or hi + mid + lo (3)
+// 8 fp32 values as bf16 operand parts: hi (1: exact for bf16 data), hi + lo
+// (2) or hi + mid + lo (3)
 template <int PARTS>
 __device__ inline void parts8(const float (&v)[8], bf16x8 (&o)[3]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         o[0][e] = (__bf16)v[e];
-        const float r = v[e] - (float)o[0][e];
-        o[1][e] = (__bf16)r;
-        if constexpr (PARTS == 3) o[2][e] = (__bf16)(r - (float)o[1][e]);
+        if constexpr (PARTS >= 2) {
+            const float r = v[e] - (float)o[0][e];
+            o[1][e] = (__bf16)r;
+            if constexpr (PARTS == 3) o[2][e] = (__bf16)(r - (float)o[1][e]);
+        }
     }
 }
-// acc += A B over the partial products that matter, smallest first
-template <int PARTS>
+// acc += A B over the partial products that matter (a part of order i times
+// one of order j kept when i + j < the larger part count), smallest first
+template <int PA, int PB>
 __device__ inline f32x16 mma(const bf16x8 (&a)[3], const bf16x8 (&b)[3], f32x16 c) {
-    if constexpr (PARTS == 3) {
-        c = mfma32(a[1], b[1], c);
-        c = mfma32(a[2], b[0], c);
-        c = mfma32(a[0], b[2], c);
+    constexpr int P = PA > PB ? PA : PB;
+    if constexpr (P == 3) {
+        if constexpr (PA >= 2 && PB >= 2) c = mfma32(a[1], b[1], c);
+        if constexpr (PA == 3) c = mfma32(a[2], b[0], c);
+        if constexpr (PB == 3) c = mfma32(a[0], b[2], c);
     }
-    c = mfma32(a[1], b[0], c);
-    c = mfma32(a[0], b[1], c);
+    if constexpr (PA >= 2) c = mfma32(a[1], b[0], c);
+    if constexpr (PB >= 2) c = mfma32(a[0], b[1], c);
     return mfma32(a[0], b[0], c);
 }
 
-// C (M x N) = sum_k A(m, k) B(k, n) on the matrix cores; the 32 x 32 output
-// tiles are dealt to the workgroup's waves and out(m, n, value) receives each
-// element (exactly one lane per element).  M, N multiples of 32, K of 16.
-template <int PARTS, typename FA, typename FB, typename FO>
-__device__ inline void gemm(int M, int N, int K, FA A, FB Bm, FO out) {
+// Operand views over fp32 tiles, read 8 values along the contraction at once.
+// Rows (index i) past imax and contraction indices past kmax read zero; kmax
+// is a multiple of 8.
+struct Cont {           // value (i, k) = p[i * ld + k]: contiguous along k, vector loads
+    const float* p;
+    int ld, imax, kmax;
+    __device__ void ld8(int i, int k0, float (&v)[8]) const {
+        if (i < imax && k0 < kmax) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(p + (size_t)i * ld + k0);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(p + (size_t)i * ld + k0 + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = a[e];
+                v[e + 4] = b[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        }
+    }
+};
+struct Strd {           // value (i, k) = p[k * ld + i]: strided along k
+    const float* p;
+    int ld, imax, kmax;
+    __device__ void ld8(int i, int k0, float (&v)[8]) const {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            v[e] = i < imax && k0 < kmax ? p[(size_t)(k0 + e) * ld + i] : 0.f;
+    }
+};
+__device__ inline Cont cont(const float* p, int ld, int imax = 1 << 30, int kmax = 1 << 30) {
+    return Cont{p, ld, imax, kmax};
+}
+__device__ inline Strd strd(const float* p, int ld, int imax = 1 << 30, int kmax = 1 << 30) {
+    return Strd{p, ld, imax, kmax};
+}
+
+// C (M x N) = sum_k A(m, k) B(k, n) on the matrix cores, A and B given as
+// views indexed (row of the product's operand, contraction index): A by m, B
+// by n.  The 32 x 32 output tiles are dealt to the workgroup's waves and
+// out(m, n, value) receives each element (one lane per element; gemms of the
+// same M x N deal their tiles identically, so a lane may accumulate into an
+// element across such gemms without a barrier).  M, N multiples of 32, K of 16.
+template <int PA, int PB, typename VA, typename VB, typename FO>
+__device__ inline void gemm(int M, int N, int K, const VA& A, const VB& Bv, FO out) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int r = lane & 31, h = lane >> 5;
     const int tn = N / 32, nt = (M / 32) * tn;
@@ -83,15 +128,12 @@ __device__ inline void gemm(int M, int N, int K, FA A, FB Bm, FO out) {
         f32x16 c = zero16();
         for (int k0 = 0; k0 < K; k0 += 16) {
             float av[8], bv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                av[e] = A(m0 + r, k0 + 8 * h + e);
-                bv[e] = Bm(k0 + 8 * h + e, n0 + r);
-            }
+            A.ld8(m0 + r, k0 + 8 * h, av);
+            Bv.ld8(n0 + r, k0 + 8 * h, bv);
             bf16x8 ap[3], bp[3];
-            parts8<PARTS>(av, ap);
-            parts8<PARTS>(bv, bp);
-            c = mma<PARTS>(ap, bp, c);
+            parts8<PA>(av, ap);
+            parts8<PB>(bv, bp);
+            c = mma<PA, PB>(ap, bp, c);
         }
         // C layout: lane -> column n0 + r, register 4i + j -> row m0 + 8i + 4h + j
 #pragma unroll
@@ -101,21 +143,104 @@ __device__ inline void gemm(int M, int N, int K, FA A, FB Bm, FO out) {
     }
 }
 
+// The wave's own 32 x 32 tile (tile index = wave) of C = sum_k A(m, k) B(k, n),
+// accumulated into acc; waves past the tile count do nothing.  Its elements
+// are visited with for_acc.  Callers use it where M x N has at most one tile
+// per wave.
+template <int PA, int PB, typename VA, typename VB>
+__device__ inline void gemm_acc(int M, int N, int K, const VA& A, const VB& Bv, f32x16& acc) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 31, h = lane >> 5;
+    const int tn = N / 32;
+    if (wave >= (M / 32) * tn) return;
+    const int m0 = (wave / tn) * 32, n0 = (wave % tn) * 32;
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        float av[8], bv[8];
+        A.ld8(m0 + r, k0 + 8 * h, av);
+        Bv.ld8(n0 + r, k0 + 8 * h, bv);
+        bf16x8 ap[3], bp[3];
+        parts8<PA>(av, ap);
+        parts8<PB>(bv, bp);
+        acc = mma<PA, PB>(ap, bp, acc);
+    }
+}
+template <typename FO>
+__device__ inline void for_acc(int M, int N, const f32x16& acc, FO f) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 31, h = lane >> 5;
+    const int tn = N / 32;
+    if (wave >= (M / 32) * tn) return;
+    const int m0 = (wave / tn) * 32, n0 = (wave % tn) * 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f(m0 + 8 * i + 4 * h + j, n0 + r, acc[4 * i + j]);
+}
+
 __device__ inline size_t pair_index(int b, int c) { return (size_t)b * (b - 1) / 2 + c; }
+
+// F: operand parts of fp32 intermediates (2 for bf16 data, 3 for fp32 data);
+// X: parts of the caller's own data (v, do): 1 for bf16 (exact), else F.
+template <typename T, int PARTS>
+struct Parts {
+    static constexpr int F = PARTS;
+    static constexpr int X = sizeof(T) == 2 ? 1 : PARTS;
+};
+
+// Register prefetch of an [R][D] row-major tile (element type S) from global
+// memory, in 16-byte units, later written into an fp32 LDS tile of row stride
+// ld (columns past D are left alone: the caller zeroes them once).
+template <typename S, int R, int D>
+struct TilePf {
+    static constexpr int EPU = 16 / (int)sizeof(S);     // elements per unit
+    static constexpr int UPR = D / EPU;                 // units per row
+    static constexpr int NU = (R * UPR + 255) / 256;
+    u32x4 u[NU];
+    __device__ void load(const S* src, int rows_valid) {
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int e = threadIdx.x + 256 * i, r = e / UPR, x = e % UPR;
+            u[i] = u32x4{0u, 0u, 0u, 0u};
+            if (e < R * UPR && r < rows_valid)
+                u[i] = *reinterpret_cast<const u32x4*>(src + (size_t)r * D + x * EPU);
+        }
+    }
+    __device__ void store(float* dst, int ld) const {
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int e = threadIdx.x + 256 * i, r = e / UPR, x = e % UPR;
+            if (e >= R * UPR) continue;
+            if constexpr (sizeof(S) == 4) {
+                *reinterpret_cast<u32x4*>(dst + r * ld + 4 * x) = u[i];
+            } else {   // 8 bf16 -> 8 floats (exact)
+                f32x4 a, b;
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    a[2 * q] = __uint_as_float(u[i][q] << 16);
+                    a[2 * q + 1] = __uint_as_float(u[i][q] & 0xffff0000u);
+                    b[2 * q] = __uint_as_float(u[i][q + 2] << 16);
+                    b[2 * q + 1] = __uint_as_float(u[i][q + 2] & 0xffff0000u);
+                }
+                *reinterpret_cast<f32x4*>(dst + r * ld + 8 * x) = a;
+                *reinterpret_cast<f32x4*>(dst + r * ld + 8 * x + 4) = b;
+            }
+        }
+    }
+};
 
 // ---------------------------------------------------------------------------
 // chain: for query block b >= 1 of a slice, the queries Qw_c used against every
 // key block c < b, carried right to left as in the forward scan; stored per
-// block pair in X [slice][pair][B][d].
+// block pair in X [slice][pair][B][d].  Longest chains first.
 template <int D, int PARTS>
 __global__ void __launch_bounds__(256)
-bwd_chain_kernel(int nb, int slice0, const float* __restrict__ ql,
+bwd_chain_kernel(int nb, int nsc, int slice0, const float* __restrict__ ql,
                  const float* __restrict__ em, float* __restrict__ X) {
     using Dm = Dims<D>;
     constexpr int DP = Dm::DP, LD = Dm::LD;
-    __shared__ float sQ[kB * LD], sT[kB * LD], sE[DP * LD];
+    __shared__ __attribute__((aligned(16))) float sQ[kB * LD], sT[kB * LD], sE[DP * LD];
     const int tid = threadIdx.x;
-    const int b = 1 + (int)(blockIdx.x % (nb - 1)), sl = (int)(blockIdx.x / (nb - 1));
+    const int b = nb - 1 - (int)(blockIdx.x / nsc), sl = (int)(blockIdx.x % nsc);
     const size_t slice = (size_t)slice0 + sl, npairs = (size_t)nb * (nb - 1) / 2;
     float* Xs = X + (size_t)sl * npairs * kB * D;
     const float* qlb = ql + (slice * nb + b) * kB * D;
@@ -132,10 +257,9 @@ bwd_chain_kernel(int nb, int slice0, const float* __restrict__ ql,
         const float* ec = em + (slice * nb + c) * D * D;
         for (int e = tid; e < D * D; e += 256) sE[(e / D) * LD + e % D] = ec[e];
         __syncthreads();
-        // Qw_{c-1} = Qw_c - Qw_c E_c^T
-        gemm<PARTS>(kB, DP, DP, [&](int m, int k) { return sQ[m * LD + k]; },
-                    [&](int k, int n) { return sE[n * LD + k]; },
-                    [&](int m, int n, float v) { sT[m * LD + n] = v; });
+        // Qw_{c-1} = Qw_c - Qw_c E_c^T:  B(k, n) = E[n][k]
+        gemm<PARTS, PARTS>(kB, DP, DP, cont(sQ, LD), cont(sE, LD),
+                           [&](int m, int n, float v) { sT[m * LD + n] = v; });
         __syncthreads();
         for (int e = tid; e < kB * DP; e += 256) {
             const int r = e / DP, x = e % DP;
@@ -148,22 +272,23 @@ bwd_chain_kernel(int nb, int slice0, const float* __restrict__ ql,
 // query: for query block b of a slice, left to right over the key blocks:
 // the diagonal tile's dS (-> dDg_b), then for c = 0 .. b-1 the pair's dS and
 // the chain A_c (A_{c-1} kept in Z for the transitions' gradients); dQl_b,
-// the rows' dS sums and Delta.
+// the rows' dS sums and Delta.  Longest rows of pairs first.
 template <typename T, int D, int PARTS>
 __global__ void __launch_bounds__(256)
-bwd_query_kernel(int L, int nb, int slice0, float scale, int fox, const T* __restrict__ v,
-                 const T* __restrict__ o, const T* __restrict__ dout,
+bwd_query_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
+                 const T* __restrict__ v, const T* __restrict__ o, const T* __restrict__ dout,
                  const float* __restrict__ lse, FwdWs fw, const float* __restrict__ X,
                  float* __restrict__ Z, float* __restrict__ dQl, float* __restrict__ dDg,
                  float* __restrict__ rowsum, float* __restrict__ delta) {
     using Dm = Dims<D>;
+    using Pt = Parts<T, PARTS>;
     constexpr int DP = Dm::DP, LD = Dm::LD;
-    __shared__ float sdO[kB * LD], sV[kB * LD], sA[kB * LD], sG[kB * LD];
-    __shared__ float sS[kB * kLdB], sP[kB * kLdB];
+    __shared__ __attribute__((aligned(16))) float sdO[kB * LD], sV[kB * LD], sA[kB * LD],
+        sK[kB * LD], sX[kB * LD], sE[DP * LD], sS[kB * kLdB], sP[kB * kLdB];
     __shared__ float sLse[kB], sDel[kB], sGb[kB], sGc[kB], sRow[kB];
     __shared__ float sTb;
     const int tid = threadIdx.x;
-    const int b = (int)(blockIdx.x % nb), sl = (int)(blockIdx.x / nb);
+    const int b = nb - 1 - (int)(blockIdx.x / nsc), sl = (int)(blockIdx.x % nsc);
     const size_t slice = (size_t)slice0 + sl, blk_b = slice * nb + b, base = slice * L;
     const size_t npairs = (size_t)nb * (nb - 1) / 2;
     const float* Xs = X + (size_t)sl * npairs * kB * D;
@@ -199,82 +324,105 @@ bwd_query_kernel(int L, int nb, int slice0, float scale, int fox, const T* __res
             sV[r * LD + x] = x < D && pos < L ? to_f32(v[(base + pos) * D + x]) : 0.f;
         }
     };
-    // sS holds logits -> P; then dP -> sP and dS = P (dP - Delta) -> sS, rows summed
-    auto backprop_softmax = [&]() {
-        for (int e = tid; e < kB * kB; e += 256) {
-            const int i = e / kB, j = e % kB;
-            const float s = sS[i * kLdB + j];
-            sS[i * kLdB + j] = b * kB + i < L ? __expf(s - sLse[i]) : 0.f;
-        }
-        gemm<PARTS>(kB, kB, DP, [&](int m, int k) { return sdO[m * LD + k]; },
-                    [&](int k, int n) { return sV[n * LD + k]; },
-                    [&](int m, int n, float val) { sP[m * kLdB + n] = val; });
-        __syncthreads();
-        for (int e = tid; e < kB * kB; e += 256) {
-            const int i = e / kB, j = e % kB;
-            sS[i * kLdB + j] *= sP[i * kLdB + j] - sDel[i];
-        }
-        __syncthreads();
-        if (tid < kB) {
-            float s = 0.f;
-            for (int j = 0; j < kB; ++j) s += sS[tid * kLdB + j];
-            sRow[tid] += s;
-        }
+    auto row_sums = [&]() {   // four lanes per row, 16 columns each
+        const int i = tid >> 2, q = tid & 3;
+        float s = 0.f;
+        for (int j = 16 * q; j < 16 * q + 16; ++j) s += sS[i * kLdB + j];
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        if (q == 0) sRow[i] += s;
     };
+    // the next key block's V, Kr, X_bc and E, in flight in registers while the
+    // current one is processed
+    TilePf<T, kB, D> pfV;
+    TilePf<float, kB, D> pfK, pfX;
+    TilePf<float, D, D> pfE;
+    float pGc = 0.f;
+    for (int e = tid; e < kB * LD; e += 256) sK[e] = sX[e] = 0.f;   // pad columns
+    for (int e = tid; e < DP * LD; e += 256) sE[e] = 0.f;
+    auto prefetch = [&](int c) {
+        const size_t blk_c = slice * nb + c;
+        pfV.load(v + (base + (size_t)c * kB) * D, min(kB, L - c * kB));
+        pfK.load(kr + blk_c * kB * D, kB);
+        pfX.load(Xs + pair_index(b, c) * kB * D, kB);
+        if (c >= 1) pfE.load(em + blk_c * D * D, D);
+        if (tid < kB) pGc = fox ? fw.gl[blk_c * kB + tid] : 0.f;
+    };
+    if (b > 0) prefetch(0);
 
-    // diagonal tile
+    // diagonal tile: P from the in-block logits, then dS = P (dP - Delta)
     load_v(b);
     __syncthreads();
     for (int e = tid; e < kB * kB; e += 256) {
         const int i = e / kB, j = e % kB;
-        sS[i * kLdB + j] = j <= i ? scale * fw.dg[blk_b * kB * kB + e] + (sGb[i] - sGb[j])
-                                  : -INFINITY;
+        sS[i * kLdB + j] = j <= i && b * kB + i < L
+            ? __expf(scale * fw.dg[blk_b * kB * kB + e] + (sGb[i] - sGb[j]) - sLse[i]) : 0.f;
     }
     __syncthreads();
-    backprop_softmax();
-    for (int e = tid; e < kB * kB; e += 256)
-        dDg[blk_b * kB * kB + e] = scale * sS[(e / kB) * kLdB + e % kB];
+    gemm<Pt::X, Pt::X>(kB, kB, DP, cont(sdO, LD), cont(sV, LD), [&](int m, int n, float val) {
+        sP[m * kLdB + n] = val;
+    });
+    __syncthreads();
+    for (int e = tid; e < kB * kB; e += 256) {
+        const int i = e / kB, j = e % kB;
+        const float ds = sS[i * kLdB + j] * (sP[i * kLdB + j] - sDel[i]);
+        sS[i * kLdB + j] = ds;
+        dDg[blk_b * kB * kB + e] = scale * ds;
+    }
     for (int e = tid; e < kB * DP; e += 256) sA[(e / DP) * LD + e % DP] = 0.f;
+    __syncthreads();
+    row_sums();
 
     float Tc = 0.f;                 // sum of the gate totals of blocks before c
     for (int c = 0; c < b; ++c) {
         const size_t blk_c = slice * nb + c;
         __syncthreads();
-        if (tid < kB) sGc[tid] = fox ? fw.gl[blk_c * kB + tid] : 0.f;
-        load_v(c);
+        pfV.store(sV, LD);
+        pfK.store(sK, LD);
+        pfX.store(sX, LD);
+        if (c >= 1) pfE.store(sE, LD);
+        if (tid < kB) sGc[tid] = pGc;
         __syncthreads();
+        if (c + 1 < b) prefetch(c + 1);
         const float shift = fox ? sTb - Tc : 0.f;   // sum of the totals of blocks c .. b-1
-        const float* xbc = Xs + pair_index(b, c) * kB * D;
-        const float* krc = kr + blk_c * kB * D;
-        const float* ec = em + blk_c * D * D;
-        gemm<PARTS>(kB, kB, DP, [&](int m, int k) { return k < D ? xbc[m * D + k] : 0.f; },
-                    [&](int k, int n) { return k < D ? krc[n * D + k] : 0.f; },
-                    [&](int m, int n, float val) {
-                        sS[m * kLdB + n] = scale * val + (sGb[m] + shift - sGc[n]);
-                    });
+        // P = exp(scale X Kr^T + bias - lse), then dS = P (dO V^T - Delta) in place
+        // (the two products deal their tiles alike: each lane finishes its own P)
+        gemm<Pt::F, Pt::F>(kB, kB, DP, cont(sX, LD), cont(sK, LD), [&](int m, int n, float val) {
+            sS[m * kLdB + n] = b * kB + m < L
+                ? __expf(scale * val + (sGb[m] + shift - sGc[n]) - sLse[m]) : 0.f;
+        });
+        gemm<Pt::X, Pt::X>(kB, kB, DP, cont(sdO, LD), cont(sV, LD), [&](int m, int n, float val) {
+            sS[m * kLdB + n] *= val - sDel[m];
+        });
         __syncthreads();
-        backprop_softmax();
-        // G = scale dS Kr_c
-        gemm<PARTS>(kB, DP, kB, [&](int m, int k) { return sS[m * kLdB + k]; },
-                    [&](int k, int n) { return n < D ? krc[k * D + n] : 0.f; },
-                    [&](int m, int n, float val) { sG[m * LD + n] = scale * val; });
+        row_sums();
+        // G = scale dS Kr_c and (c >= 1) A_{c-1} E_c, in registers
+        f32x16 gt = zero16(), ae = zero16();
+        gemm_acc<Pt::F, Pt::F>(kB, DP, kB, cont(sS, kLdB), strd(sK, LD), gt);
         if (c >= 1) {
             float* zo = Zs + pair_index(b, c) * kB * D;
-            for (int e = tid; e < kB * D; e += 256) zo[e] = sA[(e / D) * LD + e % D];
-            // A_c = G + A_{c-1} - A_{c-1} E_c  (A E_c into sP)
-            gemm<PARTS>(kB, DP, DP, [&](int m, int k) { return sA[m * LD + k]; },
-                        [&](int k, int n) { return k < D && n < D ? ec[k * D + n] : 0.f; },
-                        [&](int m, int n, float val) { sP[m * LD + n] = val; });
-            __syncthreads();
-            for (int e = tid; e < kB * DP; e += 256) {
-                const int r = e / DP, x = e % DP;
-                sA[r * LD + x] += sG[r * LD + x] - sP[r * LD + x];
+            for (int e = tid; e < kB * (D / 4); e += 256) {
+                const int r = e / (D / 4), x = 4 * (e % (D / 4));
+                *reinterpret_cast<f32x4*>(zo + (size_t)r * D + x) =
+                    *reinterpret_cast<const f32x4*>(sA + r * LD + x);
             }
-        } else {
-            __syncthreads();
-            for (int e = tid; e < kB * DP; e += 256) {
-                const int r = e / DP, x = e % DP;
-                sA[r * LD + x] = sG[r * LD + x];
+            gemm_acc<Pt::F, Pt::F>(kB, DP, DP, cont(sA, LD), strd(sE, LD, D, D), ae);
+        }
+        __syncthreads();   // every read of A_{c-1} is done
+        // A_c = scale dS Kr_c + A_{c-1} - A_{c-1} E_c
+        const bool first = c == 0;
+        {
+            const int lane = tid & 63, wave = tid >> 6, r = lane & 31, h = lane >> 5;
+            const int tn = DP / 32;
+            if (wave < 2 * tn) {
+                const int m0 = (wave / tn) * 32, n0 = (wave % tn) * 32;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float* a = sA + (m0 + 8 * i + 4 * h + j) * LD + n0 + r;
+                        *a = scale * gt[4 * i + j] + (first ? 0.f : *a - ae[4 * i + j]);
+                    }
             }
         }
         if (fox) Tc += fw.tot[blk_c];
@@ -286,38 +434,65 @@ bwd_query_kernel(int L, int nb, int slice0, float scale, int fox, const T* __res
 
 // ---------------------------------------------------------------------------
 // key: for key block c of a slice, over the query blocks b >= c: dV_c, dKr_c,
-// dE_c and the keys' dS column sums, accumulated in LDS.
+// dE_c (matrix-core accumulators held in registers across the loop, a wave per
+// output tile) and the keys' dS column sums.  Longest first.
 template <typename T, int D, int PARTS>
 __global__ void __launch_bounds__(256)
-bwd_key_kernel(int L, int nb, int slice0, float scale, int fox, const T* __restrict__ v,
-               const T* __restrict__ dout, const float* __restrict__ lse,
-               const float* __restrict__ delta, FwdWs fw, const float* __restrict__ X,
-               const float* __restrict__ Z, float* __restrict__ dKr, float* __restrict__ dEm,
-               T* __restrict__ dv, float* __restrict__ colsum) {
+bwd_key_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
+               const T* __restrict__ v, const T* __restrict__ dout,
+               const float* __restrict__ lse, const float* __restrict__ delta, FwdWs fw,
+               const float* __restrict__ X, const float* __restrict__ Z,
+               float* __restrict__ dKr, float* __restrict__ dEm, T* __restrict__ dv,
+               float* __restrict__ colsum) {
     using Dm = Dims<D>;
+    using Pt = Parts<T, PARTS>;
     constexpr int DP = Dm::DP, LD = Dm::LD;
-    __shared__ float sV[kB * LD], sK[kB * LD], sdV[kB * LD], sdK[kB * LD], sdE[DP * LD];
-    __shared__ float sdO[kB * LD], sS[kB * kLdB], sP[kB * kLdB];
-    __shared__ float sLse[kB], sDel[kB], sGb[kB], sGc[kB], sCol[kB];
+    __shared__ __attribute__((aligned(16))) float sV[kB * LD], sK[kB * LD], sdO[kB * LD],
+        sX[kB * LD], sZ[kB * LD], sS[kB * kLdB], sP[kB * kLdB];
+    __shared__ float sLse[kB], sDel[kB], sGb[kB], sGc[kB], sCol[kB], sCp[4][kB];
     const int tid = threadIdx.x;
-    const int c = (int)(blockIdx.x % nb), sl = (int)(blockIdx.x / nb);
+    const int c = (int)(blockIdx.x / nsc), sl = (int)(blockIdx.x % nsc);
     const size_t slice = (size_t)slice0 + sl, blk_c = slice * nb + c, base = slice * L;
     const size_t npairs = (size_t)nb * (nb - 1) / 2;
     const float* Xs = X + (size_t)sl * npairs * kB * D;
     const float* Zs = Z + (size_t)sl * npairs * kB * D;
-    const float* krc = static_cast<const float*>(fw.kr) + blk_c * kB * D;
+    auto stage = [&](float* dst, const float* src) {
+        for (int e = tid; e < kB * (DP / 4); e += 256) {
+            const int r = e / (DP / 4), x = 4 * (e % (DP / 4));
+            *reinterpret_cast<f32x4*>(dst + r * LD + x) =
+                x < D ? *reinterpret_cast<const f32x4*>(src + (size_t)r * D + x)
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
 
     for (int e = tid; e < kB * DP; e += 256) {
         const int r = e / DP, x = e % DP, pos = c * kB + r;
         sV[r * LD + x] = x < D && pos < L ? to_f32(v[(base + pos) * D + x]) : 0.f;
-        sK[r * LD + x] = x < D ? krc[r * D + x] : 0.f;
-        sdK[r * LD + x] = 0.f;
     }
-    for (int e = tid; e < DP * LD; e += 256) sdE[e] = 0.f;
+    stage(sK, static_cast<const float*>(fw.kr) + blk_c * kB * D);
     if (tid < kB) {
         sGc[tid] = fox ? fw.gl[blk_c * kB + tid] : 0.f;
         sCol[tid] = 0.f;
     }
+    f32x16 accV = zero16(), accK = zero16(), accE = zero16();
+    // the next query block's dO, X_bc, Z_bc and row terms, in flight in
+    // registers while the current block is processed
+    TilePf<T, kB, D> pfO;
+    TilePf<float, kB, D> pfX, pfZ;
+    float pLse = 0.f, pDel = 0.f, pGb = 0.f;
+    for (int e = tid; e < kB * LD; e += 256) sX[e] = sZ[e] = 0.f;   // pad columns
+    auto prefetch = [&](int b) {
+        const size_t blk_b = slice * nb + b;
+        pfO.load(dout + (base + (size_t)b * kB) * D, min(kB, L - b * kB));
+        pfX.load(Xs + pair_index(b, c) * kB * D, kB);
+        if (c >= 1) pfZ.load(Zs + pair_index(b, c) * kB * D, kB);
+        if (tid < kB) {
+            const int pos = b * kB + tid;
+            pLse = pos < L ? lse[base + pos] : 0.f;
+            pDel = delta[blk_b * kB + tid];
+            pGb = fox ? fw.gl[blk_b * kB + tid] : 0.f;
+        }
+    };
     // per query block b: its dO, lse, Delta and gate cumsum
     auto load_rows = [&](int b) {
         const size_t blk_b = slice * nb + b;
@@ -332,34 +507,24 @@ bwd_key_kernel(int L, int nb, int slice0, float scale, int fox, const T* __restr
             sGb[tid] = fox ? fw.gl[blk_b * kB + tid] : 0.f;
         }
     };
-    // sS: logits -> P; dV += P^T dO; dP -> sP; dS -> sS; columns summed
-    auto backprop = [&](int b, bool first) {
-        __syncthreads();   // the logits tile is complete
+    // sS holds P: dV += P^T dO; dP -> sP; dS -> sS; columns summed
+    auto backprop = [&]() {
+        __syncthreads();   // P is complete
+        gemm_acc<Pt::F, Pt::X>(kB, DP, kB, strd(sS, kLdB), strd(sdO, LD), accV);
+        gemm<Pt::X, Pt::X>(kB, kB, DP, cont(sdO, LD), cont(sV, LD),
+                           [&](int m, int n, float val) { sP[m * kLdB + n] = val; });
+        __syncthreads();
+        // a thread keeps one column (tid % 64) and every fourth row
+        float cs = 0.f;
         for (int e = tid; e < kB * kB; e += 256) {
             const int i = e / kB, j = e % kB;
-            const float s = sS[i * kLdB + j];
-            sS[i * kLdB + j] = b * kB + i < L ? __expf(s - sLse[i]) : 0.f;
+            const float ds = sS[i * kLdB + j] * (sP[i * kLdB + j] - sDel[i]);
+            sS[i * kLdB + j] = ds;
+            cs += ds;
         }
+        sCp[tid >> 6][tid & 63] = cs;
         __syncthreads();
-        gemm<PARTS>(kB, DP, kB, [&](int m, int k) { return sS[k * kLdB + m]; },
-                    [&](int k, int n) { return sdO[k * LD + n]; },
-                    [&](int m, int n, float val) {
-                        sdV[m * LD + n] = first ? val : sdV[m * LD + n] + val;
-                    });
-        gemm<PARTS>(kB, kB, DP, [&](int m, int k) { return sdO[m * LD + k]; },
-                    [&](int k, int n) { return sV[n * LD + k]; },
-                    [&](int m, int n, float val) { sP[m * kLdB + n] = val; });
-        __syncthreads();
-        for (int e = tid; e < kB * kB; e += 256) {
-            const int i = e / kB, j = e % kB;
-            sS[i * kLdB + j] *= sP[i * kLdB + j] - sDel[i];
-        }
-        __syncthreads();
-        if (tid < kB) {
-            float s = 0.f;
-            for (int i = 0; i < kB; ++i) s += sS[i * kLdB + tid];
-            sCol[tid] += s;
-        }
+        if (tid < kB) sCol[tid] += sCp[0][tid] + sCp[1][tid] + sCp[2][tid] + sCp[3][tid];
     };
 
     // diagonal tile (b = c)
@@ -367,42 +532,46 @@ bwd_key_kernel(int L, int nb, int slice0, float scale, int fox, const T* __restr
     __syncthreads();
     for (int e = tid; e < kB * kB; e += 256) {
         const int i = e / kB, j = e % kB;
-        sS[i * kLdB + j] = j <= i ? scale * fw.dg[blk_c * kB * kB + e] + (sGc[i] - sGc[j])
-                                  : -INFINITY;
+        sS[i * kLdB + j] = j <= i && c * kB + i < L
+            ? __expf(scale * fw.dg[blk_c * kB * kB + e] + (sGc[i] - sGc[j]) - sLse[i]) : 0.f;
     }
-    backprop(c, true);
+    if (c + 1 < nb) prefetch(c + 1);
+    backprop();
 
     float shift = 0.f;              // sum of the gate totals of blocks c .. b-1
     for (int b = c + 1; b < nb; ++b) {
         if (fox) shift += fw.tot[slice * nb + b - 1];
         __syncthreads();
-        load_rows(b);
-        __syncthreads();
-        const float* xbc = Xs + pair_index(b, c) * kB * D;
-        gemm<PARTS>(kB, kB, DP, [&](int m, int k) { return k < D ? xbc[m * D + k] : 0.f; },
-                    [&](int k, int n) { return sK[n * LD + k]; },
-                    [&](int m, int n, float val) {
-                        sS[m * kLdB + n] = scale * val + (sGb[m] + shift - sGc[n]);
-                    });
-        backprop(b, false);
-        // dKr += scale dS^T Qw_c;  dE -= A_{c-1}^T Qw_c
-        gemm<PARTS>(kB, DP, kB, [&](int m, int k) { return sS[k * kLdB + m]; },
-                    [&](int k, int n) { return n < D ? xbc[k * D + n] : 0.f; },
-                    [&](int m, int n, float val) { sdK[m * LD + n] += scale * val; });
-        if (c >= 1) {
-            const float* zbc = Zs + pair_index(b, c) * kB * D;
-            gemm<PARTS>(DP, DP, kB, [&](int m, int k) { return m < D ? zbc[k * D + m] : 0.f; },
-                        [&](int k, int n) { return n < D ? xbc[k * D + n] : 0.f; },
-                        [&](int m, int n, float val) { sdE[m * LD + n] -= val; });
+        pfO.store(sdO, LD);
+        pfX.store(sX, LD);
+        if (c >= 1) pfZ.store(sZ, LD);
+        if (tid < kB) {
+            sLse[tid] = pLse;
+            sDel[tid] = pDel;
+            sGb[tid] = pGb;
         }
+        __syncthreads();
+        if (b + 1 < nb) prefetch(b + 1);
+        // P = exp(scale X Kr^T + bias - lse)
+        gemm<Pt::F, Pt::F>(kB, kB, DP, cont(sX, LD), cont(sK, LD), [&](int m, int n, float val) {
+            sS[m * kLdB + n] = b * kB + m < L
+                ? __expf(scale * val + (sGb[m] + shift - sGc[n]) - sLse[m]) : 0.f;
+        });
+        backprop();
+        // dKr += dS^T X (scaled at the end);  dE -= A_{c-1}^T X
+        gemm_acc<Pt::F, Pt::F>(kB, DP, kB, strd(sS, kLdB), strd(sX, LD), accK);
+        if (c >= 1) gemm_acc<Pt::F, Pt::F>(DP, DP, kB, strd(sZ, LD), strd(sX, LD), accE);
     }
+    for_acc(kB, DP, accK, [&](int m, int n, float val) {
+        if (n < D) dKr[blk_c * kB * D + m * D + n] = scale * val;
+    });
+    for_acc(kB, DP, accV, [&](int m, int n, float val) {
+        if (n < D && c * kB + m < L) dv[(base + c * kB + m) * D + n] = from_f32<T>(val);
+    });
+    for_acc(DP, DP, accE, [&](int m, int n, float val) {
+        if (m < D && n < D) dEm[blk_c * D * D + m * D + n] = -val;
+    });
     __syncthreads();
-    for (int e = tid; e < kB * D; e += 256) {
-        const int r = e / D, x = e % D, pos = c * kB + r;
-        dKr[blk_c * kB * D + e] = sdK[r * LD + x];
-        if (pos < L) dv[(base + pos) * D + x] = from_f32<T>(sdV[r * LD + x]);
-    }
-    for (int e = tid; e < D * D; e += 256) dEm[blk_c * D * D + e] = sdE[(e / D) * LD + e % D];
     if (tid < kB) colsum[blk_c * kB + tid] = sCol[tid];
 }
 
@@ -412,9 +581,10 @@ bwd_key_kernel(int L, int nb, int slice0, float scale, int fox, const T* __restr
 //   X = lower(Q W^T), P = X U, Ql = Q - P W, M = strictLower(W K^T), R = U M,
 //   Kr = K - R^T W, Y = U^T W, E = W^T Y, Dg = lower(Q K^T) - P M
 // [Notes s2.6, s2.7]; intermediate B x B and B x d products live in a per-block
-// scratch area of the workspace (kScr tiles of 64 x 64 floats).
-constexpr int kScr = 15;
-enum { sU_, sX_, sM_, sY_, sP_, sR_, sdP_, sdR_, sdY_, sdM_, sdU_, sdX_, sTmp_, sdG_, sWW_ };
+// scratch area of the workspace (kScr tiles of 64 x 64 floats, row stride 64).
+constexpr int kScr = 17;
+enum { sU_, sX_, sM_, sY_, sP_, sR_, sdP_, sdR_, sdY_, sdM_, sdU_, sdX_, sTmp_, sdG_, sWW_,
+       sdT_, sAA_ };
 
 template <typename T, int D, int PARTS>
 __global__ void __launch_bounds__(256)
@@ -425,15 +595,18 @@ bwd_precond_kernel(int L, int nb, int slice0, const T* __restrict__ q, const T* 
                    float* __restrict__ scr, T* __restrict__ dq, T* __restrict__ dk,
                    T* __restrict__ dw, float* __restrict__ dbeta) {
     using Dm = Dims<D>;
-    constexpr int DP = Dm::DP, LD = Dm::LD;
-    __shared__ float sQ[kB * LD], sK[kB * LD], sW[kB * LD];
-    __shared__ float sT[kB * kLdB], sG[kB * kLdB], oQ[kB * LD], oK[kB * LD];
+    using Pt = Parts<T, PARTS>;
+    constexpr int DP = Dm::DP, LD = Dm::LD, F = Pt::F, XP = Pt::X;
+    __shared__ __attribute__((aligned(16))) float sQ[kB * LD], sK[kB * LD], sW[kB * LD],
+        sT[kB * kLdB], sG[kB * kLdB], oQ[kB * LD], oK[kB * LD];
     __shared__ float sBeta[kB], sdB[kB];
     const int tid = threadIdx.x;
     const int c = (int)(blockIdx.x % nb), sl = (int)(blockIdx.x / nb);
     const size_t slice = (size_t)slice0 + sl, blk = slice * nb + c, base = slice * L;
     float* S = scr + (size_t)blockIdx.x * kScr * kB * kB;
-    auto g = [&](int t) { return S + (size_t)t * kB * kB; };   // 64 x 64, row stride 64
+    auto g = [&](int t) { return S + (size_t)t * kB * kB; };
+    auto gc = [&](int t) { return cont(g(t), kB); };    // (i, k) = tile[i][k]
+    auto gs = [&](int t) { return strd(g(t), kB); };    // (i, k) = tile[k][i]
     const float* dql = dQl + blk * kB * D;
     const float* dkr = dKr + blk * kB * D;
     const float* dem = dEm + blk * D * D;
@@ -453,11 +626,8 @@ bwd_precond_kernel(int L, int nb, int slice0, const T* __restrict__ q, const T* 
         sdB[tid] = 0.f;
     }
     __syncthreads();
-    auto Wm = [&](int m, int kk) { return sW[m * LD + kk]; };        // W (m, k)
-    auto WT = [&](int kk, int n) { return sW[n * LD + kk]; };        // W^T as the right operand
-    auto Um = [&](int a, int j) { return sT[a * kLdB + j] * sBeta[j]; };
-    // G and W W^T
-    gemm<PARTS>(kB, kB, DP, Wm, WT, [&](int m, int n, float val) {
+    // G and W W^T (inputs are exact in their dtype)
+    gemm<XP, XP>(kB, kB, DP, cont(sW, LD), cont(sW, LD), [&](int m, int n, float val) {
         sG[m * kLdB + n] = n < m ? sBeta[m] * val : 0.f;
         g(sWW_)[m * kB + n] = val;
     });
@@ -473,119 +643,98 @@ bwd_precond_kernel(int L, int nb, int slice0, const T* __restrict__ q, const T* 
         }
     }
     __syncthreads();
-    // forward products: X, M, Y, U; then P, R
-    gemm<PARTS>(kB, kB, DP, [&](int m, int kk) { return sQ[m * LD + kk]; }, WT,
-                [&](int m, int n, float val) { g(sX_)[m * kB + n] = n <= m ? val : 0.f; });
-    gemm<PARTS>(kB, kB, DP, Wm, [&](int kk, int n) { return sK[n * LD + kk]; },
-                [&](int m, int n, float val) { g(sM_)[m * kB + n] = n < m ? val : 0.f; });
-    gemm<PARTS>(kB, DP, kB, [&](int m, int kk) { return Um(kk, m); },
-                [&](int kk, int n) { return sW[kk * LD + n]; },
-                [&](int m, int n, float val) { g(sY_)[m * kB + n] = val; });
-    for (int e = tid; e < kB * kB; e += 256) g(sU_)[e] = Um(e / kB, e % kB);
+    for (int e = tid; e < kB * kB; e += 256) g(sU_)[e] = sT[(e / kB) * kLdB + e % kB] * sBeta[e % kB];
+    // forward products X, M (exact inputs), then Y = U^T W
+    gemm<XP, XP>(kB, kB, DP, cont(sQ, LD), cont(sW, LD),
+                 [&](int m, int n, float val) { g(sX_)[m * kB + n] = n <= m ? val : 0.f; });
+    gemm<XP, XP>(kB, kB, DP, cont(sW, LD), cont(sK, LD),
+                 [&](int m, int n, float val) { g(sM_)[m * kB + n] = n < m ? val : 0.f; });
     __syncthreads();
-    gemm<PARTS>(kB, kB, kB, [&](int m, int kk) { return g(sX_)[m * kB + kk]; }, Um,
-                [&](int m, int n, float val) { g(sP_)[m * kB + n] = val; });
-    gemm<PARTS>(kB, kB, kB, Um, [&](int kk, int n) { return g(sM_)[kk * kB + n]; },
-                [&](int m, int n, float val) { g(sR_)[m * kB + n] = val; });
+    gemm<F, XP>(kB, DP, kB, gs(sU_), strd(sW, LD),
+                [&](int m, int n, float val) { g(sY_)[m * kB + n] = val; });
+    // P = X U, R = U M
+    gemm<F, F>(kB, kB, kB, gc(sX_), gs(sU_),
+               [&](int m, int n, float val) { g(sP_)[m * kB + n] = val; });
+    gemm<F, F>(kB, kB, kB, gc(sU_), gs(sM_),
+               [&](int m, int n, float val) { g(sR_)[m * kB + n] = val; });
     __syncthreads();
     // dP = -dDg M^T - dQl W^T;  dR = -W dKr^T;  dY = W dE
-    gemm<PARTS>(kB, kB, kB, [&](int m, int kk) { return ddg[m * kB + kk]; },
-                [&](int kk, int n) { return g(sM_)[n * kB + kk]; },
-                [&](int m, int n, float val) { g(sdP_)[m * kB + n] = -val; });
-    gemm<PARTS>(kB, kB, DP, Wm, [&](int kk, int n) { return kk < D ? dkr[n * D + kk] : 0.f; },
+    gemm<F, F>(kB, kB, kB, cont(ddg, kB), gc(sM_),
+               [&](int m, int n, float val) { g(sdP_)[m * kB + n] = -val; });
+    gemm<F, XP>(kB, kB, DP, cont(dql, D, kB, D), cont(sW, LD),
+                [&](int m, int n, float val) { g(sdP_)[m * kB + n] -= val; });
+    gemm<XP, F>(kB, kB, DP, cont(sW, LD), cont(dkr, D, kB, D),
                 [&](int m, int n, float val) { g(sdR_)[m * kB + n] = -val; });
-    gemm<PARTS>(kB, DP, DP, Wm,
-                [&](int kk, int n) { return kk < D && n < D ? dem[kk * D + n] : 0.f; },
+    gemm<XP, F>(kB, DP, DP, cont(sW, LD), strd(dem, D, D, D),
                 [&](int m, int n, float val) { g(sdY_)[m * kB + n] = val; });
     __syncthreads();
-    gemm<PARTS>(kB, kB, DP, [&](int m, int kk) { return kk < D ? dql[m * D + kk] : 0.f; }, WT,
-                [&](int m, int n, float val) { g(sdP_)[m * kB + n] -= val; });
-    // dM = strictLower(-P^T dDg + U^T dR)
-    gemm<PARTS>(kB, kB, kB, [&](int m, int kk) { return g(sP_)[kk * kB + m]; },
-                [&](int kk, int n) { return ddg[kk * kB + n]; },
-                [&](int m, int n, float val) { g(sdM_)[m * kB + n] = -val; });
-    // dU = lower(X^T dP + dR M^T + W dY^T), first term after dP is complete
-    gemm<PARTS>(kB, kB, kB, [&](int m, int kk) { return g(sdR_)[m * kB + kk]; },
-                [&](int kk, int n) { return g(sM_)[n * kB + kk]; },
-                [&](int m, int n, float val) { g(sdU_)[m * kB + n] = val; });
-    __syncthreads();
-    gemm<PARTS>(kB, kB, kB, [&](int m, int kk) { return Um(kk, m); },
-                [&](int kk, int n) { return g(sdR_)[kk * kB + n]; },
-                [&](int m, int n, float val) {
-                    g(sdM_)[m * kB + n] = n < m ? g(sdM_)[m * kB + n] + val : 0.f;
-                });
-    gemm<PARTS>(kB, kB, DP, Wm, [&](int kk, int n) { return g(sdY_)[n * kB + kk]; },
+    // dM = strictLower(-P^T dDg + U^T dR);  dU = lower(X^T dP + dR M^T + W dY^T)
+    gemm<F, F>(kB, kB, kB, gs(sP_), strd(ddg, kB),
+               [&](int m, int n, float val) { g(sdM_)[m * kB + n] = -val; });
+    gemm<F, F>(kB, kB, kB, gs(sU_), gs(sdR_), [&](int m, int n, float val) {
+        g(sdM_)[m * kB + n] = n < m ? g(sdM_)[m * kB + n] + val : 0.f;
+    });
+    gemm<F, F>(kB, kB, kB, gc(sdR_), gc(sM_),
+               [&](int m, int n, float val) { g(sdU_)[m * kB + n] = val; });
+    gemm<XP, F>(kB, kB, DP, cont(sW, LD), gc(sdY_),
                 [&](int m, int n, float val) { g(sdU_)[m * kB + n] += val; });
+    gemm<F, F>(kB, kB, kB, gs(sX_), gs(sdP_), [&](int m, int n, float val) {
+        g(sdU_)[m * kB + n] = n <= m ? g(sdU_)[m * kB + n] + val : 0.f;
+    });
     // dX = lower(dP U^T)
-    gemm<PARTS>(kB, kB, kB, [&](int m, int kk) { return g(sdP_)[m * kB + kk]; },
-                [&](int kk, int n) { return Um(n, kk); },
-                [&](int m, int n, float val) { g(sdX_)[m * kB + n] = n <= m ? val : 0.f; });
-    __syncthreads();
-    gemm<PARTS>(kB, kB, kB, [&](int m, int kk) { return g(sX_)[kk * kB + m]; },
-                [&](int kk, int n) { return g(sdP_)[kk * kB + n]; },
-                [&](int m, int n, float val) {
-                    g(sdU_)[m * kB + n] = n <= m ? g(sdU_)[m * kB + n] + val : 0.f;
-                });
+    gemm<F, F>(kB, kB, kB, gc(sdP_), gc(sU_),
+               [&](int m, int n, float val) { g(sdX_)[m * kB + n] = n <= m ? val : 0.f; });
     __syncthreads();
     // U = T diag(beta): dbeta_j += sum_a T_aj dU_aj;  dT = dU diag(beta)
-    // dG = strictLower(-T^T dT T^T): Tmp = dT T^T, then -T^T Tmp
     if (tid < kB) {
         float s = 0.f;
         for (int a = tid; a < kB; ++a) s += sT[a * kLdB + tid] * g(sdU_)[a * kB + tid];
         sdB[tid] += s;
     }
-    gemm<PARTS>(kB, kB, kB, [&](int m, int kk) { return g(sdU_)[m * kB + kk] * sBeta[kk]; },
-                [&](int kk, int n) { return sT[n * kLdB + kk]; },
-                [&](int m, int n, float val) { g(sTmp_)[m * kB + n] = val; });
+    for (int e = tid; e < kB * kB; e += 256) g(sdT_)[e] = g(sdU_)[e] * sBeta[e % kB];
     __syncthreads();
-    gemm<PARTS>(kB, kB, kB, [&](int m, int kk) { return sT[kk * kLdB + m]; },
-                [&](int kk, int n) { return g(sTmp_)[kk * kB + n]; },
-                [&](int m, int n, float val) { g(sdG_)[m * kB + n] = n < m ? -val : 0.f; });
+    // dG = strictLower(-T^T dT T^T): Tmp = dT T^T, then -T^T Tmp
+    gemm<F, F>(kB, kB, kB, gc(sdT_), cont(sT, kLdB),
+               [&](int m, int n, float val) { g(sTmp_)[m * kB + n] = val; });
     __syncthreads();
-    // G_ij = beta_i (w_i . w_j), i > j: dbeta_i += sum_j dG_ij (W W^T)_ij
+    gemm<F, F>(kB, kB, kB, strd(sT, kLdB), gs(sTmp_),
+               [&](int m, int n, float val) { g(sdG_)[m * kB + n] = n < m ? -val : 0.f; });
+    __syncthreads();
+    // G_ij = beta_i (w_i . w_j), i > j: dbeta_i += sum_j dG_ij (W W^T)_ij; and the
+    // symmetric weight A + A^T, A = diag(beta) dG, for dW
     if (tid < kB) {
         float s = 0.f;
         for (int j = 0; j < tid; ++j) s += g(sdG_)[tid * kB + j] * g(sWW_)[tid * kB + j];
         sdB[tid] += s;
     }
+    for (int e = tid; e < kB * kB; e += 256) {
+        const int m = e / kB, n = e % kB;
+        g(sAA_)[e] = sBeta[m] * g(sdG_)[m * kB + n] + sBeta[n] * g(sdG_)[n * kB + m];
+    }
     // dW = -P^T dQl - R dKr + dX^T Q + dM K + Y dE^T + U dY + (A + A^T) W,
-    // A = diag(beta) dG; accumulated in sG (free now)
-    auto acc = [&](int m, int n, float val) { sG[m * kLdB + n] += val; };
+    // accumulated in sG (free now); dQ = dQl + dDg K + dX W; dK = dKr + dDg^T Q + dM^T W
     for (int e = tid; e < kB * kLdB; e += 256) sG[e] = 0.f;
-    __syncthreads();
-    gemm<PARTS>(kB, DP, kB, [&](int m, int kk) { return -g(sP_)[kk * kB + m]; },
-                [&](int kk, int n) { return n < D ? dql[kk * D + n] : 0.f; }, acc);
-    gemm<PARTS>(kB, DP, kB, [&](int m, int kk) { return -g(sR_)[m * kB + kk]; },
-                [&](int kk, int n) { return n < D ? dkr[kk * D + n] : 0.f; }, acc);
-    gemm<PARTS>(kB, DP, kB, [&](int m, int kk) { return g(sdX_)[kk * kB + m]; },
-                [&](int kk, int n) { return sQ[kk * LD + n]; }, acc);
-    gemm<PARTS>(kB, DP, kB, [&](int m, int kk) { return g(sdM_)[m * kB + kk]; },
-                [&](int kk, int n) { return sK[kk * LD + n]; }, acc);
-    gemm<PARTS>(kB, DP, DP, [&](int m, int kk) { return g(sY_)[m * kB + kk]; },
-                [&](int kk, int n) { return kk < D && n < D ? dem[n * D + kk] : 0.f; }, acc);
-    gemm<PARTS>(kB, DP, kB, Um, [&](int kk, int n) { return g(sdY_)[kk * kB + n]; }, acc);
-    gemm<PARTS>(kB, DP, kB,
-                [&](int m, int kk) {
-                    return sBeta[m] * g(sdG_)[m * kB + kk] + sBeta[kk] * g(sdG_)[kk * kB + m];
-                },
-                [&](int kk, int n) { return sW[kk * LD + n]; }, acc);
-    // dQ = dQl + dDg K + dX W;  dK = dKr + dDg^T Q + dM^T W
     for (int e = tid; e < kB * DP; e += 256) {
         const int r = e / DP, x = e % DP;
         oQ[r * LD + x] = x < D ? dql[r * D + x] : 0.f;
         oK[r * LD + x] = x < D ? dkr[r * D + x] : 0.f;
     }
     __syncthreads();
+    auto accW = [&](int m, int n, float val) { sG[m * kLdB + n] += val; };
+    auto subW = [&](int m, int n, float val) { sG[m * kLdB + n] -= val; };
     auto accQ = [&](int m, int n, float val) { oQ[m * LD + n] += val; };
     auto accK = [&](int m, int n, float val) { oK[m * LD + n] += val; };
-    gemm<PARTS>(kB, DP, kB, [&](int m, int kk) { return ddg[m * kB + kk]; },
-                [&](int kk, int n) { return sK[kk * LD + n]; }, accQ);
-    gemm<PARTS>(kB, DP, kB, [&](int m, int kk) { return g(sdX_)[m * kB + kk]; },
-                [&](int kk, int n) { return sW[kk * LD + n]; }, accQ);
-    gemm<PARTS>(kB, DP, kB, [&](int m, int kk) { return ddg[kk * kB + m]; },
-                [&](int kk, int n) { return sQ[kk * LD + n]; }, accK);
-    gemm<PARTS>(kB, DP, kB, [&](int m, int kk) { return g(sdM_)[kk * kB + m]; },
-                [&](int kk, int n) { return sW[kk * LD + n]; }, accK);
+    gemm<F, F>(kB, DP, kB, gs(sP_), strd(dql, D, D, kB), subW);
+    gemm<F, F>(kB, DP, kB, gc(sR_), strd(dkr, D, D, kB), subW);
+    gemm<F, XP>(kB, DP, kB, gs(sdX_), strd(sQ, LD), accW);
+    gemm<F, XP>(kB, DP, kB, gc(sdM_), strd(sK, LD), accW);
+    gemm<F, F>(kB, DP, DP, gc(sY_), cont(dem, D, D, D), accW);
+    gemm<F, F>(kB, DP, kB, gc(sU_), gs(sdY_), accW);
+    gemm<F, XP>(kB, DP, kB, gc(sAA_), strd(sW, LD), accW);
+    gemm<F, XP>(kB, DP, kB, cont(ddg, kB), strd(sK, LD), accQ);
+    gemm<F, XP>(kB, DP, kB, gc(sdX_), strd(sW, LD), accQ);
+    gemm<F, XP>(kB, DP, kB, strd(ddg, kB), strd(sQ, LD), accK);
+    gemm<F, XP>(kB, DP, kB, gs(sdM_), strd(sW, LD), accK);
     __syncthreads();
     for (int e = tid; e < kB * D; e += 256) {
         const int r = e / D, x = e % D, pos = c * kB + r;
@@ -637,22 +786,32 @@ hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
     f.N = a.N; f.H = a.H; f.L = a.L; f.d = a.d; f.block = kB; f.bf16 = sizeof(T) == 2;
     f.q = a.q; f.k = a.k; f.w = a.w; f.beta = a.beta; f.logf = a.logf;
     f.ws = a.fw;
-    hipError_t e = launch_precond_f32(f, st);
+    f.v = a.v;
+    f.scale = a.scale;
+    hipError_t e;
+    if (a.img) {   // bf16, d in {32, 64}: the matrix-core preconditioning
+        f.ws.img = a.img;
+        f.ws.k32 = static_cast<float*>(a.fw.kr);
+        f.ws.e32 = static_cast<float*>(a.fw.em);
+        e = launch_precond_bf16(f, st);
+    } else {
+        e = launch_precond_f32(f, st);
+    }
     if (e != hipSuccess) return e;
     for (int s0 = 0; s0 < ns; s0 += a.chunk) {
         const int nsc = std::min(a.chunk, ns - s0);
         if (nb > 1) {
             hipLaunchKernelGGL((bwd_chain_kernel<D, PARTS>), dim3(nsc * (nb - 1)), dim3(256), 0,
-                               st, nb, s0, a.fw.ql, (const float*)a.fw.em, a.X);
+                               st, nb, nsc, s0, a.fw.ql, (const float*)a.fw.em, a.X);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         hipLaunchKernelGGL((bwd_query_kernel<T, D, PARTS>), dim3(nsc * nb), dim3(256), 0, st,
-                           a.L, nb, s0, a.scale, fox, (const T*)a.v, (const T*)a.o,
+                           a.L, nb, nsc, s0, a.scale, fox, (const T*)a.v, (const T*)a.o,
                            (const T*)a.dout, a.lse, a.fw, a.X, a.Z, a.dQl, a.dDg, a.rowsum,
                            a.delta);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL((bwd_key_kernel<T, D, PARTS>), dim3(nsc * nb), dim3(256), 0, st,
-                           a.L, nb, s0, a.scale, fox, (const T*)a.v, (const T*)a.dout, a.lse,
+                           a.L, nb, nsc, s0, a.scale, fox, (const T*)a.v, (const T*)a.dout, a.lse,
                            a.delta, a.fw, a.X, a.Z, a.dKr, a.dEm, (T*)a.dv, a.colsum);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL((bwd_precond_kernel<T, D, PARTS>), dim3(nsc * nb), dim3(256), 0, st,

@@ -1014,6 +1014,28 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+// The preconditioning alone, for the backward pass: besides the images it
+// writes ql, dg, gl, tot and, with ws.k32 / ws.e32 set, Kright and E in fp32.
+hipError_t launch_precond_bf16(const FwdArgs& a, hipStream_t st) {
+    const int nb = (a.L + kB - 1) / kB, nblk = a.N * a.H * nb;
+    const float scale2 = a.scale * kLog2e;
+    switch (a.d) {
+        case 32:
+            hipLaunchKernelGGL((precond_mfma_kernel<32>), dim3(nblk), dim3(512), 0, st,
+                               (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                               (const __bf16*)a.w, a.beta, a.logf, a.L, nb, scale2, a.ws);
+            break;
+        case 64:
+            hipLaunchKernelGGL((precond_mfma_kernel<64>), dim3(nblk), dim3(512), 0, st,
+                               (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                               (const __bf16*)a.w, a.beta, a.logf, a.L, nb, scale2, a.ws);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 bool causal_supported(int d, bool bf16) { return bf16 && (d == 32 || d == 64); }
 
 hipError_t launch_causal(const FwdArgs& a, hipStream_t st) {

@@ -125,7 +125,8 @@ path_status launched(hipError_t e, const char* what) {
 constexpr size_t kBwdChunkBytes = (size_t)4 << 30;
 
 struct BwdLayout {
-    size_t ql, kr, em, dg, gl, tot, dQl, dKr, dEm, dDg, rowsum, colsum, delta, X, Z, scr, total;
+    size_t ql, kr, em, dg, gl, tot, dQl, dKr, dEm, dDg, rowsum, colsum, delta, X, Z, scr, img, total;
+    bool mfma_precond;
     int chunk;
 };
 
@@ -154,6 +155,8 @@ BwdLayout bwd_layout(const path_fwd_desc* d) {
     l.X = take(4 * pa::bwd_pair_floats(d->L, D, (int)chunk));
     l.Z = take(4 * pa::bwd_pair_floats(d->L, D, (int)chunk));
     l.scr = take(4 * pa::bwd_scratch_floats(d->L, (int)chunk));
+    l.mfma_precond = d->dtype == PATH_BF16 && pa::fwd_bf16_supported(D, B);
+    if (l.mfma_precond) l.img = take(nblk * pa::fwd_bf16_image_bytes(D));
     l.total = off;
     l.chunk = (int)chunk;
     return l;
@@ -429,6 +432,7 @@ path_status path_attn_bwd(const path_fwd_desc* desc, const void* q, const void* 
     a.dQl = at(lay.dQl); a.dKr = at(lay.dKr); a.dEm = at(lay.dEm); a.dDg = at(lay.dDg);
     a.rowsum = at(lay.rowsum); a.colsum = at(lay.colsum); a.delta = at(lay.delta);
     a.scr = at(lay.scr);
+    a.img = lay.mfma_precond ? base + lay.img : nullptr;
     a.chunk = lay.chunk;
     return launched(pa::launch_bwd(a, stream), "path_attn_bwd");
 }

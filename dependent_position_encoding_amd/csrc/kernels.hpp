@@ -73,6 +73,9 @@ hipError_t launch_causal(const FwdArgs& a, hipStream_t st);
 
 // the preconditioning step alone (block 64, fp32 products in ws.ql/kr/em/dg/gl/tot)
 hipError_t launch_precond_f32(const FwdArgs& a, hipStream_t st);
+// same on the matrix cores for bf16 d in {32, 64}: Kright and E in fp32 go to
+// ws.k32 / ws.e32 (ws.img receives the scan's tile images)
+hipError_t launch_precond_bf16(const FwdArgs& a, hipStream_t st);
 
 // backward pass (block 64)
 struct BwdArgs {
@@ -88,6 +91,7 @@ struct BwdArgs {
     float *dQl, *dKr, *dEm, *dDg;   // per block: gradients of the preconditioned products
     float *rowsum, *colsum, *delta; // per position [blk][B]
     float* scr;          // per block of a chunk: scratch of the preconditioning's backward
+    void* img;           // bf16 d in {32, 64}: tile images of the matrix-core preconditioning
     int chunk;           // slices per pass over the pair buffers
 };
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t st);
