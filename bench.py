@@ -60,6 +60,20 @@ def precond_flops(N, H, L, d, B=64):
     return N * H * nb * per_block
 
 
+def bwd_flops(N, H, L, d, B=64):
+    """Matrix-core flops the backward kernels execute, for B = d: per block
+    pair c < b, eight B x B x d products (the logits and dO V^T, each formed
+    by both the query-major and the key-major pass; dS Kr; P^T dO; dS^T Qw)
+    and three B x d x d ones (the carried queries' transition, the gradient
+    chain's, dE); per block, 32 products of B x B x d size (29 in the
+    backward of the preconditioning with its recomputed forward products,
+    three for the diagonal tile); plus the recomputed preconditioning."""
+    nb = (L + B - 1) // B
+    pairs = nb * (nb - 1) // 2
+    per_slice = pairs * (8 * 2 * B * B * d + 3 * 2 * B * d * d) + nb * 32 * 2 * B * B * d
+    return N * H * per_slice + precond_flops(N, H, L, d, B)
+
+
 def fa_eq_flops(N, H, L, d):
     return 2.0 * N * H * L * L * d
 
@@ -330,6 +344,7 @@ def main():
         out["unfused_decode"] = unfused_rates(pa, cache, tok, L, wl, dws, ot, lt, kb, vb)
     out["beta0_baseline"] = causal_baseline(pa, pre, wl, out["prefill"])
     out["front_end"] = front_end_rate(pa, wl, dev)
+    out["backward"] = backward_rate(pa, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, N * (L + T) / (ms_step * 1e-3))
     print(json.dumps(out), flush=True)
@@ -426,6 +441,52 @@ def front_end_rate(pa, wl, dev, R=32, reps=10):
                       "gate": wl.fox},
             "bound": "hbm", "GB_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
             "algorithmic_bytes": alg, "intermediate_bytes": 2 * N * L * rp * 4}
+
+
+def backward_rate(pa, dev, reps=3):
+    """The backward pass (path_attn_bwd) at the LM-layer training shape (batch
+    4, 24 heads, 4096 tokens, d = 64, bf16, scale 1, synthetic inputs of that
+    workload), on the forward's own o and lse and a random dL/do: median of
+    `reps` timed calls after a warm one; the forward timed alike beside it."""
+    import torch
+    import workloads
+    wl = workloads.CONFIGS["lm"]
+    x = workloads.make_inputs(wl, device=dev)
+    N, H, L, d = x["q"].shape
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    do = torch.randn(x["q"].shape, generator=g, device=dev).to(wl.dtype)
+    fwd = lambda: pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], logf=x["logf"],
+                         scale=wl.scale)
+    o, lse = fwd()
+    ws = torch.empty(pa.bwd_workspace_bytes(N, H, L, d, wl.dtype), dtype=torch.uint8,
+                     device=dev)
+    bwd = lambda: pa.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], o, lse, do,
+                         scale=wl.scale, workspace=ws)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)[len(ts) // 2]
+
+    ms, fwd_ms = timed(bwd), timed(fwd)
+    fl = bwd_flops(N, H, L, d)
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"shape": {"batch": N, "heads": H, "seq_len": L, "head_dim": d, "dtype": "bf16",
+                      "forget_gate": wl.fox},
+            "ms": round(ms, 3), "executed_TFLOP_s": round(tf, 2),
+            "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "executed_flops": fl,
+            "fwd_ms": round(fwd_ms, 3), "bwd_over_fwd": round(ms / fwd_ms, 2),
+            "tokens_per_s": round(N * L / (ms * 1e-3), 1),
+            "workspace_GB": round(ws.numel() / 1e9, 3)}
 
 
 def causal_baseline(pa, pre, wl, prefill):

@@ -118,14 +118,15 @@ __device__ inline Strd strd(const float* p, int ld, int imax = 1 << 30, int kmax
 // out(m, n, value) receives each element (one lane per element; gemms of the
 // same M x N deal their tiles identically, so a lane may accumulate into an
 // element across such gemms without a barrier).  M, N multiples of 32, K of 16.
-template <int PA, int PB, typename VA, typename VB, typename FO>
-__device__ inline void gemm(int M, int N, int K, const VA& A, const VB& Bv, FO out) {
+template <int PA, int PB, int K, typename VA, typename VB, typename FO>
+__device__ inline void gemm(int M, int N, const VA& A, const VB& Bv, FO out) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int r = lane & 31, h = lane >> 5;
     const int tn = N / 32, nt = (M / 32) * tn;
     for (int t = wave; t < nt; t += nw) {
         const int m0 = (t / tn) * 32, n0 = (t % tn) * 32;
         f32x16 c = zero16();
+#pragma unroll
         for (int k0 = 0; k0 < K; k0 += 16) {
             float av[8], bv[8];
             A.ld8(m0 + r, k0 + 8 * h, av);
@@ -147,13 +148,14 @@ __device__ inline void gemm(int M, int N, int K, const VA& A, const VB& Bv, FO o
 // accumulated into acc; waves past the tile count do nothing.  Its elements
 // are visited with for_acc.  Callers use it where M x N has at most one tile
 // per wave.
-template <int PA, int PB, typename VA, typename VB>
-__device__ inline void gemm_acc(int M, int N, int K, const VA& A, const VB& Bv, f32x16& acc) {
+template <int PA, int PB, int K, typename VA, typename VB>
+__device__ inline void gemm_acc(int M, int N, const VA& A, const VB& Bv, f32x16& acc) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 31, h = lane >> 5;
     const int tn = N / 32;
     if (wave >= (M / 32) * tn) return;
     const int m0 = (wave / tn) * 32, n0 = (wave % tn) * 32;
+#pragma unroll
     for (int k0 = 0; k0 < K; k0 += 16) {
         float av[8], bv[8];
         A.ld8(m0 + r, k0 + 8 * h, av);
@@ -249,16 +251,22 @@ bwd_chain_kernel(int nb, int nsc, int slice0, const float* __restrict__ ql,
         sQ[r * LD + x] = x < D ? qlb[r * D + x] : 0.f;
     }
     for (int e = tid; e < DP * LD; e += 256) sE[e] = 0.f;   // the padding stays zero
+    TilePf<float, D, D> pfE;                                 // the next step's E, in flight
+    if (b - 1 >= 1) pfE.load(em + (slice * nb + b - 1) * D * D, D);
     for (int c = b - 1; c >= 0; --c) {
         __syncthreads();
         float* xo = Xs + pair_index(b, c) * kB * D;
-        for (int e = tid; e < kB * D; e += 256) xo[e] = sQ[(e / D) * LD + e % D];
+        for (int e = tid; e < kB * (D / 4); e += 256) {
+            const int r = e / (D / 4), x = 4 * (e % (D / 4));
+            *reinterpret_cast<f32x4*>(xo + (size_t)r * D + x) =
+                *reinterpret_cast<const f32x4*>(sQ + r * LD + x);
+        }
         if (c == 0) break;
-        const float* ec = em + (slice * nb + c) * D * D;
-        for (int e = tid; e < D * D; e += 256) sE[(e / D) * LD + e % D] = ec[e];
+        pfE.store(sE, LD);
         __syncthreads();
+        if (c - 1 >= 1) pfE.load(em + (slice * nb + c - 1) * D * D, D);
         // Qw_{c-1} = Qw_c - Qw_c E_c^T:  B(k, n) = E[n][k]
-        gemm<PARTS, PARTS>(kB, DP, DP, cont(sQ, LD), cont(sE, LD),
+        gemm<PARTS, PARTS, DP>(kB, DP, cont(sQ, LD), cont(sE, LD),
                            [&](int m, int n, float v) { sT[m * LD + n] = v; });
         __syncthreads();
         for (int e = tid; e < kB * DP; e += 256) {
@@ -359,7 +367,7 @@ bwd_query_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
             ? __expf(scale * fw.dg[blk_b * kB * kB + e] + (sGb[i] - sGb[j]) - sLse[i]) : 0.f;
     }
     __syncthreads();
-    gemm<Pt::X, Pt::X>(kB, kB, DP, cont(sdO, LD), cont(sV, LD), [&](int m, int n, float val) {
+    gemm<Pt::X, Pt::X, DP>(kB, kB, cont(sdO, LD), cont(sV, LD), [&](int m, int n, float val) {
         sP[m * kLdB + n] = val;
     });
     __syncthreads();
@@ -387,18 +395,18 @@ bwd_query_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         const float shift = fox ? sTb - Tc : 0.f;   // sum of the totals of blocks c .. b-1
         // P = exp(scale X Kr^T + bias - lse), then dS = P (dO V^T - Delta) in place
         // (the two products deal their tiles alike: each lane finishes its own P)
-        gemm<Pt::F, Pt::F>(kB, kB, DP, cont(sX, LD), cont(sK, LD), [&](int m, int n, float val) {
+        gemm<Pt::F, Pt::F, DP>(kB, kB, cont(sX, LD), cont(sK, LD), [&](int m, int n, float val) {
             sS[m * kLdB + n] = b * kB + m < L
                 ? __expf(scale * val + (sGb[m] + shift - sGc[n]) - sLse[m]) : 0.f;
         });
-        gemm<Pt::X, Pt::X>(kB, kB, DP, cont(sdO, LD), cont(sV, LD), [&](int m, int n, float val) {
+        gemm<Pt::X, Pt::X, DP>(kB, kB, cont(sdO, LD), cont(sV, LD), [&](int m, int n, float val) {
             sS[m * kLdB + n] *= val - sDel[m];
         });
         __syncthreads();
         row_sums();
         // G = scale dS Kr_c and (c >= 1) A_{c-1} E_c, in registers
         f32x16 gt = zero16(), ae = zero16();
-        gemm_acc<Pt::F, Pt::F>(kB, DP, kB, cont(sS, kLdB), strd(sK, LD), gt);
+        gemm_acc<Pt::F, Pt::F, kB>(kB, DP, cont(sS, kLdB), strd(sK, LD), gt);
         if (c >= 1) {
             float* zo = Zs + pair_index(b, c) * kB * D;
             for (int e = tid; e < kB * (D / 4); e += 256) {
@@ -406,7 +414,7 @@ bwd_query_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
                 *reinterpret_cast<f32x4*>(zo + (size_t)r * D + x) =
                     *reinterpret_cast<const f32x4*>(sA + r * LD + x);
             }
-            gemm_acc<Pt::F, Pt::F>(kB, DP, DP, cont(sA, LD), strd(sE, LD, D, D), ae);
+            gemm_acc<Pt::F, Pt::F, DP>(kB, DP, cont(sA, LD), strd(sE, LD, D, D), ae);
         }
         __syncthreads();   // every read of A_{c-1} is done
         // A_c = scale dS Kr_c + A_{c-1} - A_{c-1} E_c
@@ -510,8 +518,8 @@ bwd_key_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     // sS holds P: dV += P^T dO; dP -> sP; dS -> sS; columns summed
     auto backprop = [&]() {
         __syncthreads();   // P is complete
-        gemm_acc<Pt::F, Pt::X>(kB, DP, kB, strd(sS, kLdB), strd(sdO, LD), accV);
-        gemm<Pt::X, Pt::X>(kB, kB, DP, cont(sdO, LD), cont(sV, LD),
+        gemm_acc<Pt::F, Pt::X, kB>(kB, DP, strd(sS, kLdB), strd(sdO, LD), accV);
+        gemm<Pt::X, Pt::X, DP>(kB, kB, cont(sdO, LD), cont(sV, LD),
                            [&](int m, int n, float val) { sP[m * kLdB + n] = val; });
         __syncthreads();
         // a thread keeps one column (tid % 64) and every fourth row
@@ -553,14 +561,14 @@ bwd_key_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         __syncthreads();
         if (b + 1 < nb) prefetch(b + 1);
         // P = exp(scale X Kr^T + bias - lse)
-        gemm<Pt::F, Pt::F>(kB, kB, DP, cont(sX, LD), cont(sK, LD), [&](int m, int n, float val) {
+        gemm<Pt::F, Pt::F, DP>(kB, kB, cont(sX, LD), cont(sK, LD), [&](int m, int n, float val) {
             sS[m * kLdB + n] = b * kB + m < L
                 ? __expf(scale * val + (sGb[m] + shift - sGc[n]) - sLse[m]) : 0.f;
         });
         backprop();
         // dKr += dS^T X (scaled at the end);  dE -= A_{c-1}^T X
-        gemm_acc<Pt::F, Pt::F>(kB, DP, kB, strd(sS, kLdB), strd(sX, LD), accK);
-        if (c >= 1) gemm_acc<Pt::F, Pt::F>(DP, DP, kB, strd(sZ, LD), strd(sX, LD), accE);
+        gemm_acc<Pt::F, Pt::F, kB>(kB, DP, strd(sS, kLdB), strd(sX, LD), accK);
+        if (c >= 1) gemm_acc<Pt::F, Pt::F, kB>(DP, DP, strd(sZ, LD), strd(sX, LD), accE);
     }
     for_acc(kB, DP, accK, [&](int m, int n, float val) {
         if (n < D) dKr[blk_c * kB * D + m * D + n] = scale * val;
@@ -627,7 +635,7 @@ bwd_precond_kernel(int L, int nb, int slice0, const T* __restrict__ q, const T* 
     }
     __syncthreads();
     // G and W W^T (inputs are exact in their dtype)
-    gemm<XP, XP>(kB, kB, DP, cont(sW, LD), cont(sW, LD), [&](int m, int n, float val) {
+    gemm<XP, XP, DP>(kB, kB, cont(sW, LD), cont(sW, LD), [&](int m, int n, float val) {
         sG[m * kLdB + n] = n < m ? sBeta[m] * val : 0.f;
         g(sWW_)[m * kB + n] = val;
     });
@@ -645,68 +653,64 @@ bwd_precond_kernel(int L, int nb, int slice0, const T* __restrict__ q, const T* 
     __syncthreads();
     for (int e = tid; e < kB * kB; e += 256) g(sU_)[e] = sT[(e / kB) * kLdB + e % kB] * sBeta[e % kB];
     // forward products X, M (exact inputs), then Y = U^T W
-    gemm<XP, XP>(kB, kB, DP, cont(sQ, LD), cont(sW, LD),
+    gemm<XP, XP, DP>(kB, kB, cont(sQ, LD), cont(sW, LD),
                  [&](int m, int n, float val) { g(sX_)[m * kB + n] = n <= m ? val : 0.f; });
-    gemm<XP, XP>(kB, kB, DP, cont(sW, LD), cont(sK, LD),
+    gemm<XP, XP, DP>(kB, kB, cont(sW, LD), cont(sK, LD),
                  [&](int m, int n, float val) { g(sM_)[m * kB + n] = n < m ? val : 0.f; });
     __syncthreads();
-    gemm<F, XP>(kB, DP, kB, gs(sU_), strd(sW, LD),
+    gemm<F, XP, kB>(kB, DP, gs(sU_), strd(sW, LD),
                 [&](int m, int n, float val) { g(sY_)[m * kB + n] = val; });
     // P = X U, R = U M
-    gemm<F, F>(kB, kB, kB, gc(sX_), gs(sU_),
+    gemm<F, F, kB>(kB, kB, gc(sX_), gs(sU_),
                [&](int m, int n, float val) { g(sP_)[m * kB + n] = val; });
-    gemm<F, F>(kB, kB, kB, gc(sU_), gs(sM_),
+    gemm<F, F, kB>(kB, kB, gc(sU_), gs(sM_),
                [&](int m, int n, float val) { g(sR_)[m * kB + n] = val; });
     __syncthreads();
     // dP = -dDg M^T - dQl W^T;  dR = -W dKr^T;  dY = W dE
-    gemm<F, F>(kB, kB, kB, cont(ddg, kB), gc(sM_),
+    gemm<F, F, kB>(kB, kB, cont(ddg, kB), gc(sM_),
                [&](int m, int n, float val) { g(sdP_)[m * kB + n] = -val; });
-    gemm<F, XP>(kB, kB, DP, cont(dql, D, kB, D), cont(sW, LD),
+    gemm<F, XP, DP>(kB, kB, cont(dql, D, kB, D), cont(sW, LD),
                 [&](int m, int n, float val) { g(sdP_)[m * kB + n] -= val; });
-    gemm<XP, F>(kB, kB, DP, cont(sW, LD), cont(dkr, D, kB, D),
+    gemm<XP, F, DP>(kB, kB, cont(sW, LD), cont(dkr, D, kB, D),
                 [&](int m, int n, float val) { g(sdR_)[m * kB + n] = -val; });
-    gemm<XP, F>(kB, DP, DP, cont(sW, LD), strd(dem, D, D, D),
+    gemm<XP, F, DP>(kB, DP, cont(sW, LD), strd(dem, D, D, D),
                 [&](int m, int n, float val) { g(sdY_)[m * kB + n] = val; });
     __syncthreads();
     // dM = strictLower(-P^T dDg + U^T dR);  dU = lower(X^T dP + dR M^T + W dY^T)
-    gemm<F, F>(kB, kB, kB, gs(sP_), strd(ddg, kB),
+    gemm<F, F, kB>(kB, kB, gs(sP_), strd(ddg, kB),
                [&](int m, int n, float val) { g(sdM_)[m * kB + n] = -val; });
-    gemm<F, F>(kB, kB, kB, gs(sU_), gs(sdR_), [&](int m, int n, float val) {
+    gemm<F, F, kB>(kB, kB, gs(sU_), gs(sdR_), [&](int m, int n, float val) {
         g(sdM_)[m * kB + n] = n < m ? g(sdM_)[m * kB + n] + val : 0.f;
     });
-    gemm<F, F>(kB, kB, kB, gc(sdR_), gc(sM_),
+    gemm<F, F, kB>(kB, kB, gc(sdR_), gc(sM_),
                [&](int m, int n, float val) { g(sdU_)[m * kB + n] = val; });
-    gemm<XP, F>(kB, kB, DP, cont(sW, LD), gc(sdY_),
+    gemm<XP, F, DP>(kB, kB, cont(sW, LD), gc(sdY_),
                 [&](int m, int n, float val) { g(sdU_)[m * kB + n] += val; });
-    gemm<F, F>(kB, kB, kB, gs(sX_), gs(sdP_), [&](int m, int n, float val) {
-        g(sdU_)[m * kB + n] = n <= m ? g(sdU_)[m * kB + n] + val : 0.f;
+    // (the last term also takes U = T diag(beta) into dbeta: dbeta_j += sum_a T_aj dU_aj)
+    gemm<F, F, kB>(kB, kB, gs(sX_), gs(sdP_), [&](int m, int n, float val) {
+        const float du = n <= m ? g(sdU_)[m * kB + n] + val : 0.f;
+        g(sdU_)[m * kB + n] = du;
+        if (n <= m) atomicAdd(&sdB[n], sT[m * kLdB + n] * du);
     });
     // dX = lower(dP U^T)
-    gemm<F, F>(kB, kB, kB, gc(sdP_), gc(sU_),
+    gemm<F, F, kB>(kB, kB, gc(sdP_), gc(sU_),
                [&](int m, int n, float val) { g(sdX_)[m * kB + n] = n <= m ? val : 0.f; });
     __syncthreads();
-    // U = T diag(beta): dbeta_j += sum_a T_aj dU_aj;  dT = dU diag(beta)
-    if (tid < kB) {
-        float s = 0.f;
-        for (int a = tid; a < kB; ++a) s += sT[a * kLdB + tid] * g(sdU_)[a * kB + tid];
-        sdB[tid] += s;
-    }
+    // dT = dU diag(beta)
     for (int e = tid; e < kB * kB; e += 256) g(sdT_)[e] = g(sdU_)[e] * sBeta[e % kB];
     __syncthreads();
     // dG = strictLower(-T^T dT T^T): Tmp = dT T^T, then -T^T Tmp
-    gemm<F, F>(kB, kB, kB, gc(sdT_), cont(sT, kLdB),
+    gemm<F, F, kB>(kB, kB, gc(sdT_), cont(sT, kLdB),
                [&](int m, int n, float val) { g(sTmp_)[m * kB + n] = val; });
     __syncthreads();
-    gemm<F, F>(kB, kB, kB, strd(sT, kLdB), gs(sTmp_),
-               [&](int m, int n, float val) { g(sdG_)[m * kB + n] = n < m ? -val : 0.f; });
+    // (G_ij = beta_i (w_i . w_j), i > j: dbeta_i += sum_j dG_ij (W W^T)_ij)
+    gemm<F, F, kB>(kB, kB, strd(sT, kLdB), gs(sTmp_), [&](int m, int n, float val) {
+        const float dg = n < m ? -val : 0.f;
+        g(sdG_)[m * kB + n] = dg;
+        if (n < m) atomicAdd(&sdB[m], dg * g(sWW_)[m * kB + n]);
+    });
     __syncthreads();
-    // G_ij = beta_i (w_i . w_j), i > j: dbeta_i += sum_j dG_ij (W W^T)_ij; and the
-    // symmetric weight A + A^T, A = diag(beta) dG, for dW
-    if (tid < kB) {
-        float s = 0.f;
-        for (int j = 0; j < tid; ++j) s += g(sdG_)[tid * kB + j] * g(sWW_)[tid * kB + j];
-        sdB[tid] += s;
-    }
+    // the symmetric weight A + A^T, A = diag(beta) dG, for dW
     for (int e = tid; e < kB * kB; e += 256) {
         const int m = e / kB, n = e % kB;
         g(sAA_)[e] = sBeta[m] * g(sdG_)[m * kB + n] + sBeta[n] * g(sdG_)[n * kB + m];
@@ -724,17 +728,17 @@ bwd_precond_kernel(int L, int nb, int slice0, const T* __restrict__ q, const T* 
     auto subW = [&](int m, int n, float val) { sG[m * kLdB + n] -= val; };
     auto accQ = [&](int m, int n, float val) { oQ[m * LD + n] += val; };
     auto accK = [&](int m, int n, float val) { oK[m * LD + n] += val; };
-    gemm<F, F>(kB, DP, kB, gs(sP_), strd(dql, D, D, kB), subW);
-    gemm<F, F>(kB, DP, kB, gc(sR_), strd(dkr, D, D, kB), subW);
-    gemm<F, XP>(kB, DP, kB, gs(sdX_), strd(sQ, LD), accW);
-    gemm<F, XP>(kB, DP, kB, gc(sdM_), strd(sK, LD), accW);
-    gemm<F, F>(kB, DP, DP, gc(sY_), cont(dem, D, D, D), accW);
-    gemm<F, F>(kB, DP, kB, gc(sU_), gs(sdY_), accW);
-    gemm<F, XP>(kB, DP, kB, gc(sAA_), strd(sW, LD), accW);
-    gemm<F, XP>(kB, DP, kB, cont(ddg, kB), strd(sK, LD), accQ);
-    gemm<F, XP>(kB, DP, kB, gc(sdX_), strd(sW, LD), accQ);
-    gemm<F, XP>(kB, DP, kB, strd(ddg, kB), strd(sQ, LD), accK);
-    gemm<F, XP>(kB, DP, kB, gs(sdM_), strd(sW, LD), accK);
+    gemm<F, F, kB>(kB, DP, gs(sP_), strd(dql, D, D, kB), subW);
+    gemm<F, F, kB>(kB, DP, gc(sR_), strd(dkr, D, D, kB), subW);
+    gemm<F, XP, kB>(kB, DP, gs(sdX_), strd(sQ, LD), accW);
+    gemm<F, XP, kB>(kB, DP, gc(sdM_), strd(sK, LD), accW);
+    gemm<F, F, DP>(kB, DP, gc(sY_), cont(dem, D, D, D), accW);
+    gemm<F, F, kB>(kB, DP, gc(sU_), gs(sdY_), accW);
+    gemm<F, XP, kB>(kB, DP, gc(sAA_), strd(sW, LD), accW);
+    gemm<F, XP, kB>(kB, DP, cont(ddg, kB), strd(sK, LD), accQ);
+    gemm<F, XP, kB>(kB, DP, gc(sdX_), strd(sW, LD), accQ);
+    gemm<F, XP, kB>(kB, DP, strd(ddg, kB), strd(sQ, LD), accK);
+    gemm<F, XP, kB>(kB, DP, gs(sdM_), strd(sW, LD), accK);
     __syncthreads();
     for (int e = tid; e < kB * D; e += 256) {
         const int r = e / D, x = e % D, pos = c * kB + r;
