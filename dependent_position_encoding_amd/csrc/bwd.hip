@@ -782,6 +782,524 @@ bwd_gate_kernel(int L, int nb, const float* __restrict__ rowsum,
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 pair kernels (d in {32, 64}).  Every operand tile is held in LDS as
+// bf16 parts -- one for the caller's exact bf16 data (V, dO), hi + lo for fp32
+// intermediates -- in the orientation its products read it, so a fragment is
+// one or two 16-byte loads and nothing is converted inside a product.
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// An R x C fp32 matrix as P bf16 parts, rows padded to C + 8 elements (16-byte
+// multiples; consecutive rows start in different bank groups).
+template <int R, int C, int P>
+struct BTile {
+    static constexpr int LDE = C + 8;
+    __bf16 v[P][R * LDE];
+    __device__ void put(int r, int c, float x) {
+        const __bf16 h = (__bf16)x;
+        v[0][r * LDE + c] = h;
+        if constexpr (P == 2) v[1][r * LDE + c] = (__bf16)(x - (float)h);
+    }
+    __device__ void put4(int r, int c0, const f32x4& x) {
+        bf16x4_t h, l;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h[e] = (__bf16)x[e];
+            l[e] = (__bf16)(x[e] - (float)h[e]);
+        }
+        *reinterpret_cast<bf16x4_t*>(&v[0][r * LDE + c0]) = h;
+        if constexpr (P == 2) *reinterpret_cast<bf16x4_t*>(&v[1][r * LDE + c0]) = l;
+    }
+    __device__ float get(int r, int c) const {
+        float x = (float)v[0][r * LDE + c];
+        if constexpr (P == 2) x += (float)v[1][r * LDE + c];
+        return x;
+    }
+    __device__ f32x4 get4(int r, int c0) const {
+        const bf16x4_t h = *reinterpret_cast<const bf16x4_t*>(&v[0][r * LDE + c0]);
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (float)h[e];
+        if constexpr (P == 2) {
+            const bf16x4_t l = *reinterpret_cast<const bf16x4_t*>(&v[1][r * LDE + c0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] += (float)l[e];
+        }
+        return x;
+    }
+};
+// operand view of a tile: (i, k) = row i, column k
+struct BV {
+    const __bf16* p0;
+    const __bf16* p1;
+    int ld;
+};
+template <typename Tile>
+__device__ inline BV bview(const Tile& t) {
+    return BV{t.v[0], t.v[sizeof(t.v) / sizeof(t.v[0]) - 1], Tile::LDE};
+}
+template <int P>
+__device__ inline void bparts(const BV& a, int i, int k0, bf16x8 (&o)[3]) {
+    o[0] = *reinterpret_cast<const bf16x8*>(a.p0 + i * a.ld + k0);
+    if constexpr (P == 2) o[1] = *reinterpret_cast<const bf16x8*>(a.p1 + i * a.ld + k0);
+}
+// One 32 x 32 tile of sum_k A(m0 + ., k) B(n0 + ., k).
+template <int PA, int PB, int K>
+__device__ inline f32x16 tile_b(const BV& A, const BV& Bv, int m0, int n0, int r, int h) {
+    f32x16 c = zero16();
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        bf16x8 ap[3], bp[3];
+        bparts<PA>(A, m0 + r, k0 + 8 * h, ap);
+        bparts<PB>(Bv, n0 + r, k0 + 8 * h, bp);
+        c = mma<PA, PB>(ap, bp, c);
+    }
+    return c;
+}
+template <int PA, int PB, int K, typename FO>
+__device__ inline void gemm_b(int M, int N, const BV& A, const BV& Bv, FO out) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int r = lane & 31, h = lane >> 5;
+    const int tn = N / 32, nt = (M / 32) * tn;
+    for (int t = wave; t < nt; t += nw) {
+        const int m0 = (t / tn) * 32, n0 = (t % tn) * 32;
+        const f32x16 c = tile_b<PA, PB, K>(A, Bv, m0, n0, r, h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) out(m0 + 8 * i + 4 * h + j, n0 + r, c[4 * i + j], 4 * i + j);
+    }
+}
+// as gemm_b, with the epilogue called once per group of four consecutive
+// product rows of a lane: out4(n, m, v) receives rows m .. m+3 of column n
+template <int PA, int PB, int K, typename FO>
+__device__ inline void gemm_b4(int M, int N, const BV& A, const BV& Bv, FO out4) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int r = lane & 31, h = lane >> 5;
+    const int tn = N / 32, nt = (M / 32) * tn;
+    for (int t = wave; t < nt; t += nw) {
+        const int m0 = (t / tn) * 32, n0 = (t % tn) * 32;
+        const f32x16 c = tile_b<PA, PB, K>(A, Bv, m0, n0, r, h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            out4(n0 + r, m0 + 8 * i + 4 * h, f32x4{c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]});
+    }
+}
+template <int PA, int PB, int K>
+__device__ inline void gemm_b_acc(int M, int N, const BV& A, const BV& Bv, f32x16& acc) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 31, h = lane >> 5;
+    const int tn = N / 32;
+    if (wave >= (M / 32) * tn) return;
+    const int m0 = (wave / tn) * 32, n0 = (wave % tn) * 32;
+    const f32x16 c = tile_b<PA, PB, K>(A, Bv, m0, n0, r, h);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] += c[e];
+}
+
+// key, bf16: for key block c, over the query blocks b >= c.  The logits are
+// formed query-major (S = X Kr^T) and written transposed, four queries of a
+// key at a time, so P^T and dS^T are key-major operands of dV = P^T dO and
+// dKr = dS^T X; X, Z and dO are staged in 4 x 4 (4 x 8) register blocks and
+// written both ways, for the products that contract over the queries.
+template <int D>
+__global__ void __launch_bounds__(256)
+bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
+                   const bf16* __restrict__ v, const bf16* __restrict__ dout,
+                   const float* __restrict__ lse, const float* __restrict__ delta, FwdWs fw,
+                   const float* __restrict__ X, const float* __restrict__ Z,
+                   float* __restrict__ dKr, float* __restrict__ dEm, bf16* __restrict__ dv,
+                   float* __restrict__ colsum) {
+    __shared__ __attribute__((aligned(16))) BTile<kB, D, 2> sK;     // Kr_c [key][d]
+    __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sV;     // V_c [key][d]
+    __shared__ __attribute__((aligned(16))) BTile<kB, D, 2> sX;     // X_bc [query][d]
+    __shared__ __attribute__((aligned(16))) BTile<D, kB, 2> sXT;    // X_bc^T
+    __shared__ __attribute__((aligned(16))) BTile<D, kB, 2> sZT;    // A_{c-1}^T
+    __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sdO;    // dO_b [query][d]
+    __shared__ __attribute__((aligned(16))) BTile<D, kB, 1> sdOT;   // dO_b^T
+    __shared__ __attribute__((aligned(16))) BTile<kB, kB, 1> sPT;   // P^T, then dS^T [key][query] (bf16)
+    __shared__ float sLse[kB], sDel[kB], sGb[kB], sGc[kB], sCol[kB];
+    const int tid = threadIdx.x;
+    const int c = (int)(blockIdx.x / nsc), sl = (int)(blockIdx.x % nsc);
+    const size_t slice = (size_t)slice0 + sl, blk_c = slice * nb + c, base = slice * L;
+    const size_t npairs = (size_t)nb * (nb - 1) / 2;
+    const float* Xs = X + (size_t)sl * npairs * kB * D;
+    const float* Zs = Z + (size_t)sl * npairs * kB * D;
+    constexpr int NB4 = kB * D / 16;   // 4 x 4 blocks of a [kB][D] fp32 tile
+    constexpr int NB8 = kB * D / 32;   // 4 x 8 blocks of a [kB][D] bf16 tile
+    const int rb4 = tid / (D / 4), cb4 = tid % (D / 4);   // this thread's 4 x 4 block
+    const int rb8 = tid / (D / 8), cb8 = tid % (D / 8);   // and 4 x 8 block
+
+    {   // resident: Kr_c, V_c
+        const float* krc = static_cast<const float*>(fw.kr) + blk_c * kB * D;
+        for (int e = tid; e < kB * D / 4; e += 256) {
+            const int r = e / (D / 4), c0 = 4 * (e % (D / 4));
+            sK.put4(r, c0, *reinterpret_cast<const f32x4*>(krc + (size_t)r * D + c0));
+        }
+        for (int e = tid; e < kB * D / 8; e += 256) {
+            const int r = e / (D / 8), c0 = 8 * (e % (D / 8)), pos = c * kB + r;
+            u32x4 u = {0u, 0u, 0u, 0u};
+            if (pos < L) u = *reinterpret_cast<const u32x4*>(v + (base + pos) * D + c0);
+            *reinterpret_cast<u32x4*>(&sV.v[0][r * sV.LDE + c0]) = u;
+        }
+    }
+    if (tid < kB) {
+        sGc[tid] = fox ? fw.gl[blk_c * kB + tid] : 0.f;
+        sCol[tid] = 0.f;
+    }
+    // prefetch of query block b's X_bc, Z_bc, dO and row terms
+    f32x4 pX[4], pZ[4];
+    u32x4 pO[4];
+    float pLse = 0.f, pDel = 0.f, pGb = 0.f;
+    auto prefetch = [&](int b) {
+        const size_t blk_b = slice * nb + b;
+        if (b > c && tid < NB4) {
+            const float* xb = Xs + pair_index(b, c) * kB * D + (size_t)(4 * rb4) * D + 4 * cb4;
+            const float* zb = Zs + pair_index(b, c) * kB * D + (size_t)(4 * rb4) * D + 4 * cb4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                pX[q] = *reinterpret_cast<const f32x4*>(xb + (size_t)q * D);
+                if (c >= 1) pZ[q] = *reinterpret_cast<const f32x4*>(zb + (size_t)q * D);
+            }
+        }
+        if (tid < NB8) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int pos = b * kB + 4 * rb8 + q;
+                pO[q] = u32x4{0u, 0u, 0u, 0u};
+                if (pos < L)
+                    pO[q] = *reinterpret_cast<const u32x4*>(dout + (base + pos) * D + 8 * cb8);
+            }
+        }
+        if (tid < kB) {
+            const int pos = b * kB + tid;
+            pLse = pos < L ? lse[base + pos] : 0.f;
+            pDel = delta[blk_b * kB + tid];
+            pGb = fox ? fw.gl[blk_b * kB + tid] : 0.f;
+        }
+    };
+    auto commit = [&](int b) {
+        if (b > c && tid < NB4) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                sX.put4(4 * rb4 + q, 4 * cb4, pX[q]);
+                sXT.put4(4 * cb4 + q, 4 * rb4, f32x4{pX[0][q], pX[1][q], pX[2][q], pX[3][q]});
+                if (c >= 1)
+                    sZT.put4(4 * cb4 + q, 4 * rb4, f32x4{pZ[0][q], pZ[1][q], pZ[2][q], pZ[3][q]});
+            }
+        }
+        if (tid < NB8) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<u32x4*>(&sdO.v[0][(4 * rb8 + q) * sdO.LDE + 8 * cb8]) = pO[q];
+            const bf16x8 o0 = *reinterpret_cast<const bf16x8*>(&pO[0]);
+            const bf16x8 o1 = *reinterpret_cast<const bf16x8*>(&pO[1]);
+            const bf16x8 o2 = *reinterpret_cast<const bf16x8*>(&pO[2]);
+            const bf16x8 o3 = *reinterpret_cast<const bf16x8*>(&pO[3]);
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                *reinterpret_cast<bf16x4_t*>(&sdOT.v[0][(8 * cb8 + q) * sdOT.LDE + 4 * rb8]) =
+                    bf16x4_t{o0[q], o1[q], o2[q], o3[q]};
+        }
+        if (tid < kB) {
+            sLse[tid] = pLse;
+            sDel[tid] = pDel;
+            sGb[tid] = pGb;
+        }
+    };
+    f32x16 accV = zero16(), accK = zero16(), accE = zero16();
+    float colAcc = 0.f;   // the lane's key column (fixed by the tiling): dS summed over queries
+    // dV += P^T dO;  then dS = P (dO V^T - Delta), written back transposed
+    auto backprop = [&]() {
+        __syncthreads();   // P^T complete
+        gemm_b_acc<1, 1, kB>(kB, D, bview(sPT), bview(sdOT), accV);
+        __syncthreads();   // every read of P^T done
+        gemm_b4<1, 1, D>(kB, kB, bview(sdO), bview(sV), [&](int n, int m, f32x4 dp) {
+            // queries m .. m+3, key n
+            const f32x4 p = sPT.get4(n, m);
+            f32x4 ds;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ds[e] = p[e] * (dp[e] - sDel[m + e]);
+                colAcc += ds[e];
+            }
+            sPT.put4(n, m, ds);
+        });
+        __syncthreads();   // dS^T complete
+    };
+
+    // diagonal tile (b = c): P^T[j][i] = exp(scale Dg[i][j] + bias - lse_i), j <= i
+    prefetch(c);
+    commit(c);
+    __syncthreads();
+    for (int e = tid; e < kB * kB / 4; e += 256) {
+        const int j = e / (kB / 4), i0 = 4 * (e % (kB / 4));   // key j, queries i0 .. i0+3
+        f32x4 p;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = i0 + q;
+            p[q] = j <= i && c * kB + i < L
+                ? __expf(scale * fw.dg[blk_c * kB * kB + i * kB + j] + (sGc[i] - sGc[j]) - sLse[i])
+                : 0.f;
+        }
+        sPT.put4(j, i0, p);
+    }
+    if (c + 1 < nb) prefetch(c + 1);
+    backprop();
+
+    float shift = 0.f;              // sum of the gate totals of blocks c .. b-1
+    for (int b = c + 1; b < nb; ++b) {
+        if (fox) shift += fw.tot[slice * nb + b - 1];
+        commit(b);
+        __syncthreads();
+        if (b + 1 < nb) prefetch(b + 1);
+        // P = exp(scale X Kr^T + bias - lse), queries m .. m+3 of key n, into P^T
+        gemm_b4<2, 2, D>(kB, kB, bview(sX), bview(sK), [&](int n, int m, f32x4 sv) {
+            f32x4 p;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                p[e] = b * kB + m + e < L
+                    ? __expf(scale * sv[e] + (sGb[m + e] + shift - sGc[n]) - sLse[m + e]) : 0.f;
+            sPT.put4(n, m, p);
+        });
+        backprop();
+        // dKr += dS^T X (scaled at the end);  dE -= A_{c-1}^T X
+        gemm_b_acc<1, 2, kB>(kB, D, bview(sPT), bview(sXT), accK);
+        if (c >= 1) gemm_b_acc<2, 2, kB>(D, D, bview(sZT), bview(sXT), accE);
+        __syncthreads();   // the pair's tiles may be replaced
+    }
+    for_acc(kB, D, accK, [&](int m, int n, float val) {
+        dKr[blk_c * kB * D + m * D + n] = scale * val;
+    });
+    for_acc(kB, D, accV, [&](int m, int n, float val) {
+        if (c * kB + m < L) dv[(base + c * kB + m) * D + n] = from_f32<bf16>(val);
+    });
+    for_acc(D, D, accE, [&](int m, int n, float val) { dEm[blk_c * D * D + m * D + n] = -val; });
+    {   // the lane's key column of the (query x key) dS tiles
+        const int lane = tid & 63, wave = tid >> 6;
+        atomicAdd(&sCol[(wave % 2) * 32 + (lane & 31)], colAcc);
+    }
+    __syncthreads();
+    if (tid < kB) colsum[blk_c * kB + tid] = sCol[tid];
+}
+
+// query, bf16: for query block b, left to right over the key blocks c < b.
+// The logits are formed key-major (S^T = Kr X^T) and written back query-major,
+// four keys of a query at a time; the chain is carried transposed
+// (A^T = scale Kr^T dS^T + A^T - E^T A^T), a lane owning one query's four
+// consecutive d values per register group, so the operand copy of A in LDS
+// and the stores of A go out as vectors.
+template <int D>
+__global__ void __launch_bounds__(256)
+bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
+                     const bf16* __restrict__ v, const bf16* __restrict__ o,
+                     const bf16* __restrict__ dout, const float* __restrict__ lse, FwdWs fw,
+                     const float* __restrict__ X, float* __restrict__ Z,
+                     float* __restrict__ dQl, float* __restrict__ dDg,
+                     float* __restrict__ rowsum, float* __restrict__ delta) {
+    __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sdO;    // dO_b [query][d]
+    __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sV;     // V_c [key][d]
+    __shared__ __attribute__((aligned(16))) BTile<kB, D, 2> sX;     // X_bc [query][d]
+    __shared__ __attribute__((aligned(16))) BTile<kB, D, 2> sK;     // Kr_c [key][d]
+    __shared__ __attribute__((aligned(16))) BTile<D, kB, 2> sKT;    // Kr_c^T [d][key]
+    __shared__ __attribute__((aligned(16))) BTile<D, D, 2> sET;     // E_c^T
+    __shared__ __attribute__((aligned(16))) BTile<kB, D, 2> sA;     // A_{c-1} [query][d]
+    __shared__ __attribute__((aligned(16))) BTile<kB, kB, 1> sS;    // P, then dS [query][key] (bf16)
+    __shared__ float sLse[kB], sDel[kB], sGb[kB], sGc[kB], sRow[kB];
+    __shared__ float sTb;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = nb - 1 - (int)(blockIdx.x / nsc), sl = (int)(blockIdx.x % nsc);
+    const size_t slice = (size_t)slice0 + sl, blk_b = slice * nb + b, base = slice * L;
+    const size_t npairs = (size_t)nb * (nb - 1) / 2;
+    const float* Xs = X + (size_t)sl * npairs * kB * D;
+    float* Zs = Z + (size_t)sl * npairs * kB * D;
+    const float* kr = static_cast<const float*>(fw.kr);
+    const float* em = static_cast<const float*>(fw.em);
+    constexpr int UF = kB * D / 4 / 256, UB = kB * D / 8 / 256;
+    constexpr int NB4 = kB * D / 16, NE4 = D * D / 16;
+    const int rb4 = tid / (D / 4), cb4 = tid % (D / 4);
+
+    // resident: dO_b; Delta = dO . o per row
+#pragma unroll
+    for (int i = 0; i < UB; ++i) {
+        const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+        const int pos = b * kB + r;
+        u32x4 u = {0u, 0u, 0u, 0u};
+        if (pos < L) u = *reinterpret_cast<const u32x4*>(dout + (base + pos) * D + c0);
+        *reinterpret_cast<u32x4*>(&sdO.v[0][r * sdO.LDE + c0]) = u;
+    }
+    if (tid < kB) {
+        const int pos = b * kB + tid;
+        float dl = 0.f;
+        if (pos < L)
+            for (int x = 0; x < D; ++x)
+                dl += to_f32(dout[(base + pos) * D + x]) * to_f32(o[(base + pos) * D + x]);
+        sDel[tid] = dl;
+        sLse[tid] = pos < L ? lse[base + pos] : 0.f;
+        sGb[tid] = fox ? fw.gl[blk_b * kB + tid] : 0.f;
+        sRow[tid] = 0.f;
+        delta[blk_b * kB + tid] = dl;
+    }
+    if (tid == 0) {
+        float s = 0.f;
+        if (fox)
+            for (int c = 0; c < b; ++c) s += fw.tot[slice * nb + c];
+        sTb = s;
+    }
+    // prefetch of key block c's V, Kr (4 x 4 blocks), X_bc, E (4 x 4 blocks)
+    u32x4 pV[UB];
+    f32x4 pK[4], pX[UF], pE[4];
+    float pGc = 0.f;
+    auto prefetch = [&](int c) {
+        const size_t blk_c = slice * nb + c;
+#pragma unroll
+        for (int i = 0; i < UB; ++i) {
+            const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            const int pos = c * kB + r;
+            pV[i] = u32x4{0u, 0u, 0u, 0u};
+            if (pos < L) pV[i] = *reinterpret_cast<const u32x4*>(v + (base + pos) * D + c0);
+        }
+        if (tid < NB4)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                pK[q] = *reinterpret_cast<const f32x4*>(kr + blk_c * kB * D +
+                                                         (size_t)(4 * rb4 + q) * D + 4 * cb4);
+        if (c < b)
+#pragma unroll
+            for (int i = 0; i < UF; ++i) {
+                const int e = tid + 256 * i, r = e / (D / 4), c0 = 4 * (e % (D / 4));
+                pX[i] = *reinterpret_cast<const f32x4*>(Xs + pair_index(b, c) * kB * D +
+                                                         (size_t)r * D + c0);
+            }
+        if (c >= 1 && tid < NE4)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                pE[q] = *reinterpret_cast<const f32x4*>(em + blk_c * D * D +
+                                                         (size_t)(4 * rb4 + q) * D + 4 * cb4);
+        if (tid < kB) pGc = fox ? fw.gl[blk_c * kB + tid] : 0.f;
+    };
+    auto commit = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < UB; ++i) {
+            const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            *reinterpret_cast<u32x4*>(&sV.v[0][r * sV.LDE + c0]) = pV[i];
+        }
+        if (tid < NB4)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                sK.put4(4 * rb4 + q, 4 * cb4, pK[q]);
+                sKT.put4(4 * cb4 + q, 4 * rb4, f32x4{pK[0][q], pK[1][q], pK[2][q], pK[3][q]});
+            }
+        if (c < b)
+#pragma unroll
+            for (int i = 0; i < UF; ++i) {
+                const int e = tid + 256 * i, r = e / (D / 4), c0 = 4 * (e % (D / 4));
+                sX.put4(r, c0, pX[i]);
+            }
+        if (c >= 1 && tid < NE4)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                sET.put4(4 * cb4 + q, 4 * rb4, f32x4{pE[0][q], pE[1][q], pE[2][q], pE[3][q]});
+        if (tid < kB) sGc[tid] = pGc;
+    };
+    float rowAcc = 0.f;   // the lane's query column (fixed by the tiling): dS summed over keys
+    // dS = P (dO V^T - Delta), formed key-major (dP^T = V dO^T) and written back
+    auto backprop = [&](bool diag) {
+        gemm_b4<1, 1, D>(kB, kB, bview(sV), bview(sdO), [&](int n, int m, f32x4 dp) {
+            // keys m .. m+3, query n
+            const f32x4 p = sS.get4(n, m);
+            f32x4 ds;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ds[e] = p[e] * (dp[e] - sDel[n]);
+                rowAcc += ds[e];
+            }
+            sS.put4(n, m, ds);
+            if (diag)
+                *reinterpret_cast<f32x4*>(dDg + blk_b * kB * kB + n * kB + m) =
+                    f32x4{scale * ds[0], scale * ds[1], scale * ds[2], scale * ds[3]};
+        });
+        __syncthreads();   // dS complete
+    };
+
+    // diagonal tile: P from the in-block logits
+    prefetch(b);   // V_b only is used here
+    commit(b);
+    __syncthreads();
+    for (int e = tid; e < kB * kB / 4; e += 256) {
+        const int i = e / (kB / 4), j0 = 4 * (e % (kB / 4));   // query i, keys j0 .. j0+3
+        f32x4 p;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int j = j0 + q;
+            p[q] = j <= i && b * kB + i < L
+                ? __expf(scale * fw.dg[blk_b * kB * kB + i * kB + j] + (sGb[i] - sGb[j]) - sLse[i])
+                : 0.f;
+        }
+        sS.put4(i, j0, p);
+    }
+    if (b > 0) prefetch(0);
+    __syncthreads();
+    backprop(true);
+
+    // the chain, transposed: a wave owns a (32 d) x (32 queries) tile of A^T
+    f32x16 At = zero16();
+    float Tc = 0.f;                 // sum of the gate totals of blocks before c
+    const int tq = kB / 32, mA = (wave / tq) * 32, nA = (wave % tq) * 32, h = lane >> 5;
+    const bool owner = wave < (D / 32) * tq;
+    const int qcol = nA + (lane & 31);   // the lane's query
+    for (int c = 0; c < b; ++c) {
+        const size_t blk_c = slice * nb + c;
+        commit(c);
+        __syncthreads();
+        if (c + 1 < b) prefetch(c + 1);
+        const float shift = fox ? sTb - Tc : 0.f;   // sum of the totals of blocks c .. b-1
+        // S^T = Kr X^T: keys m .. m+3 of query n, written to the query-major P
+        gemm_b4<2, 2, D>(kB, kB, bview(sK), bview(sX), [&](int n, int m, f32x4 sv) {
+            f32x4 p;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                p[e] = b * kB + n < L
+                    ? __expf(scale * sv[e] + (sGb[n] + shift - sGc[m + e]) - sLse[n]) : 0.f;
+            sS.put4(n, m, p);
+        });
+        backprop(false);
+        // G^T = Kr^T dS^T;  (A E)^T = E^T A^T;  A^T <- scale G^T + A^T - (A E)^T
+        f32x16 gt = zero16(), ae = zero16();
+        gemm_b_acc<2, 1, kB>(D, kB, bview(sKT), bview(sS), gt);
+        if (c >= 1) {
+            gemm_b_acc<2, 2, D>(D, kB, bview(sET), bview(sA), ae);
+            if (owner) {   // Z = A_{c-1}: four consecutive d of the lane's query per group
+                float* zo = Zs + pair_index(b, c) * kB * D + (size_t)qcol * D;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<f32x4*>(zo + mA + 8 * i + 4 * h) =
+                        f32x4{At[4 * i], At[4 * i + 1], At[4 * i + 2], At[4 * i + 3]};
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) At[q] = scale * gt[q] + (c >= 1 ? At[q] - ae[q] : 0.f);
+        __syncthreads();   // every read of A_{c-1} and of the pair's tiles is done
+        if (owner)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sA.put4(qcol, mA + 8 * i + 4 * h,
+                        f32x4{At[4 * i], At[4 * i + 1], At[4 * i + 2], At[4 * i + 3]});
+        if (fox) Tc += fw.tot[blk_c];
+    }
+    if (owner) {
+        float* qo = dQl + blk_b * kB * D + (size_t)qcol * D;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<f32x4*>(qo + mA + 8 * i + 4 * h) =
+                f32x4{At[4 * i], At[4 * i + 1], At[4 * i + 2], At[4 * i + 3]};
+    }
+    atomicAdd(&sRow[(wave % 2) * 32 + (lane & 31)], rowAcc);   // the lane's query column
+    __syncthreads();
+    if (tid < kB) rowsum[blk_b * kB + tid] = sRow[tid];
+}
+
 template <typename T, int D, int PARTS>
 hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
     const int nb = (a.L + kB - 1) / kB, ns = a.N * a.H;
@@ -809,15 +1327,28 @@ hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
                                st, nb, nsc, s0, a.fw.ql, (const float*)a.fw.em, a.X);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        hipLaunchKernelGGL((bwd_query_kernel<T, D, PARTS>), dim3(nsc * nb), dim3(256), 0, st,
-                           a.L, nb, nsc, s0, a.scale, fox, (const T*)a.v, (const T*)a.o,
-                           (const T*)a.dout, a.lse, a.fw, a.X, a.Z, a.dQl, a.dDg, a.rowsum,
-                           a.delta);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_key_kernel<T, D, PARTS>), dim3(nsc * nb), dim3(256), 0, st,
-                           a.L, nb, nsc, s0, a.scale, fox, (const T*)a.v, (const T*)a.dout, a.lse,
-                           a.delta, a.fw, a.X, a.Z, a.dKr, a.dEm, (T*)a.dv, a.colsum);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if constexpr (sizeof(T) == 2 && D >= 32) {
+            hipLaunchKernelGGL((bwd_query_b16_kernel<D>), dim3(nsc * nb), dim3(256), 0, st, a.L,
+                               nb, nsc, s0, a.scale, fox, (const bf16*)a.v, (const bf16*)a.o,
+                               (const bf16*)a.dout, a.lse, a.fw, a.X, a.Z, a.dQl, a.dDg,
+                               a.rowsum, a.delta);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL((bwd_key_b16_kernel<D>), dim3(nsc * nb), dim3(256), 0, st, a.L, nb,
+                               nsc, s0, a.scale, fox, (const bf16*)a.v, (const bf16*)a.dout,
+                               a.lse, a.delta, a.fw, a.X, a.Z, a.dKr, a.dEm, (bf16*)a.dv,
+                               a.colsum);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        } else {
+            hipLaunchKernelGGL((bwd_query_kernel<T, D, PARTS>), dim3(nsc * nb), dim3(256), 0, st,
+                               a.L, nb, nsc, s0, a.scale, fox, (const T*)a.v, (const T*)a.o,
+                               (const T*)a.dout, a.lse, a.fw, a.X, a.Z, a.dQl, a.dDg, a.rowsum,
+                               a.delta);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL((bwd_key_kernel<T, D, PARTS>), dim3(nsc * nb), dim3(256), 0, st,
+                               a.L, nb, nsc, s0, a.scale, fox, (const T*)a.v, (const T*)a.dout,
+                               a.lse, a.delta, a.fw, a.X, a.Z, a.dKr, a.dEm, (T*)a.dv, a.colsum);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
         hipLaunchKernelGGL((bwd_precond_kernel<T, D, PARTS>), dim3(nsc * nb), dim3(256), 0, st,
                            a.L, nb, s0, (const T*)a.q, (const T*)a.k, (const T*)a.w, a.beta,
                            a.dQl, a.dKr, a.dEm, a.dDg, a.scr, (T*)a.dq, (T*)a.dk, (T*)a.dw,

@@ -9,8 +9,9 @@ taken as at least 1, so gradients smaller than that get an absolute bar):
   bf16 inputs:    max |err| <= 2e-2 g_max and sum |err| / sum |ref| <= 1e-2.
 The bf16 bar follows from the arithmetic: the rows' Delta_i = do_i . o_i
 uses the forward's bf16-rounded o (relative error 2^-9 per element), which
-enters every dS_ij, and every gradient is itself rounded to bf16 (2^-9); the
-products carry ~16 mantissa bits (hi + lo operand parts).
+enters every dS_ij; P and dS enter their products rounded to bf16 (2^-9),
+the other fp32 operands as hi + lo parts (~16 mantissa bits); and every
+gradient is itself rounded to bf16 (2^-9).
 """
 import numpy as np
 import pytest
