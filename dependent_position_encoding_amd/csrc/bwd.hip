@@ -28,6 +28,7 @@
 // (per block), `gate_bwd` (per slice).  All products run on the matrix cores
 // from fp32 tiles split into bf16 parts (two for bf16 data, three for fp32).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -105,6 +106,29 @@ struct Strd {           // value (i, k) = p[k * ld + i]: strided along k
             v[e] = i < imax && k0 < kmax ? p[(size_t)(k0 + e) * ld + i] : 0.f;
     }
 };
+// the same over bf16 storage (the caller's exact bf16 data in LDS)
+struct ContH {
+    const __bf16* p;
+    int ld;
+    __device__ void ld8(int i, int k0, float (&v)[8]) const {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(p + i * ld + k0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
+    }
+};
+struct StrdH {
+    const __bf16* p;
+    int ld;
+    __device__ void ld8(int i, int k0, float (&v)[8]) const {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (float)p[(k0 + e) * ld + i];
+    }
+};
+// views of an LDS tile of element type E (float or bf16) with row stride ld
+__device__ inline Cont contv(const float* p, int ld) { return Cont{p, ld, 1 << 30, 1 << 30}; }
+__device__ inline Strd strdv(const float* p, int ld) { return Strd{p, ld, 1 << 30, 1 << 30}; }
+__device__ inline ContH contv(const __bf16* p, int ld) { return ContH{p, ld}; }
+__device__ inline StrdH strdv(const __bf16* p, int ld) { return StrdH{p, ld}; }
 __device__ inline Cont cont(const float* p, int ld, int imax = 1 << 30, int kmax = 1 << 30) {
     return Cont{p, ld, imax, kmax};
 }
@@ -604,9 +628,13 @@ bwd_precond_kernel(int L, int nb, int slice0, const T* __restrict__ q, const T* 
                    T* __restrict__ dw, float* __restrict__ dbeta) {
     using Dm = Dims<D>;
     using Pt = Parts<T, PARTS>;
-    constexpr int DP = Dm::DP, LD = Dm::LD, F = Pt::F, XP = Pt::X;
-    __shared__ __attribute__((aligned(16))) float sQ[kB * LD], sK[kB * LD], sW[kB * LD],
-        sT[kB * kLdB], sG[kB * kLdB], oQ[kB * LD], oK[kB * LD];
+    // q, k, w tiles in their own (exact) element type: bf16 data halves the
+    // LDS, which lets two workgroups share a CU
+    using E = typename std::conditional<sizeof(T) == 2, __bf16, float>::type;
+    constexpr int DP = Dm::DP, F = Pt::F, XP = Pt::X;
+    constexpr int LD = sizeof(T) == 2 ? DP + 8 : Dm::LD;
+    __shared__ __attribute__((aligned(16))) E sQ[kB * LD], sK[kB * LD], sW[kB * LD];
+    __shared__ __attribute__((aligned(16))) float sT[kB * kLdB], sG[kB * kLdB];
     __shared__ float sBeta[kB], sdB[kB];
     const int tid = threadIdx.x;
     const int c = (int)(blockIdx.x % nb), sl = (int)(blockIdx.x / nb);
@@ -624,9 +652,9 @@ bwd_precond_kernel(int L, int nb, int slice0, const T* __restrict__ q, const T* 
         const int r = e / DP, x = e % DP, pos = c * kB + r;
         const bool in = x < D && pos < L;
         const size_t gi = (base + pos) * D + x;
-        sQ[r * LD + x] = in ? to_f32(q[gi]) : 0.f;
-        sK[r * LD + x] = in ? to_f32(k[gi]) : 0.f;
-        sW[r * LD + x] = in ? to_f32(w[gi]) : 0.f;
+        sQ[r * LD + x] = (E)(in ? to_f32(q[gi]) : 0.f);
+        sK[r * LD + x] = (E)(in ? to_f32(k[gi]) : 0.f);
+        sW[r * LD + x] = (E)(in ? to_f32(w[gi]) : 0.f);
     }
     if (tid < kB) {
         const int pos = c * kB + tid;
@@ -635,7 +663,7 @@ bwd_precond_kernel(int L, int nb, int slice0, const T* __restrict__ q, const T* 
     }
     __syncthreads();
     // G and W W^T (inputs are exact in their dtype)
-    gemm<XP, XP, DP>(kB, kB, cont(sW, LD), cont(sW, LD), [&](int m, int n, float val) {
+    gemm<XP, XP, DP>(kB, kB, contv(sW, LD), contv(sW, LD), [&](int m, int n, float val) {
         sG[m * kLdB + n] = n < m ? sBeta[m] * val : 0.f;
         g(sWW_)[m * kB + n] = val;
     });
@@ -653,12 +681,12 @@ bwd_precond_kernel(int L, int nb, int slice0, const T* __restrict__ q, const T* 
     __syncthreads();
     for (int e = tid; e < kB * kB; e += 256) g(sU_)[e] = sT[(e / kB) * kLdB + e % kB] * sBeta[e % kB];
     // forward products X, M (exact inputs), then Y = U^T W
-    gemm<XP, XP, DP>(kB, kB, cont(sQ, LD), cont(sW, LD),
+    gemm<XP, XP, DP>(kB, kB, contv(sQ, LD), contv(sW, LD),
                  [&](int m, int n, float val) { g(sX_)[m * kB + n] = n <= m ? val : 0.f; });
-    gemm<XP, XP, DP>(kB, kB, cont(sW, LD), cont(sK, LD),
+    gemm<XP, XP, DP>(kB, kB, contv(sW, LD), contv(sK, LD),
                  [&](int m, int n, float val) { g(sM_)[m * kB + n] = n < m ? val : 0.f; });
     __syncthreads();
-    gemm<F, XP, kB>(kB, DP, gs(sU_), strd(sW, LD),
+    gemm<F, XP, kB>(kB, DP, gs(sU_), strdv(sW, LD),
                 [&](int m, int n, float val) { g(sY_)[m * kB + n] = val; });
     // P = X U, R = U M
     gemm<F, F, kB>(kB, kB, gc(sX_), gs(sU_),
@@ -669,11 +697,11 @@ bwd_precond_kernel(int L, int nb, int slice0, const T* __restrict__ q, const T* 
     // dP = -dDg M^T - dQl W^T;  dR = -W dKr^T;  dY = W dE
     gemm<F, F, kB>(kB, kB, cont(ddg, kB), gc(sM_),
                [&](int m, int n, float val) { g(sdP_)[m * kB + n] = -val; });
-    gemm<F, XP, DP>(kB, kB, cont(dql, D, kB, D), cont(sW, LD),
+    gemm<F, XP, DP>(kB, kB, cont(dql, D, kB, D), contv(sW, LD),
                 [&](int m, int n, float val) { g(sdP_)[m * kB + n] -= val; });
-    gemm<XP, F, DP>(kB, kB, cont(sW, LD), cont(dkr, D, kB, D),
+    gemm<XP, F, DP>(kB, kB, contv(sW, LD), cont(dkr, D, kB, D),
                 [&](int m, int n, float val) { g(sdR_)[m * kB + n] = -val; });
-    gemm<XP, F, DP>(kB, DP, cont(sW, LD), strd(dem, D, D, D),
+    gemm<XP, F, DP>(kB, DP, contv(sW, LD), strd(dem, D, D, D),
                 [&](int m, int n, float val) { g(sdY_)[m * kB + n] = val; });
     __syncthreads();
     // dM = strictLower(-P^T dDg + U^T dR);  dU = lower(X^T dP + dR M^T + W dY^T)
@@ -684,7 +712,7 @@ bwd_precond_kernel(int L, int nb, int slice0, const T* __restrict__ q, const T* 
     });
     gemm<F, F, kB>(kB, kB, gc(sdR_), gc(sM_),
                [&](int m, int n, float val) { g(sdU_)[m * kB + n] = val; });
-    gemm<XP, F, DP>(kB, kB, cont(sW, LD), gc(sdY_),
+    gemm<XP, F, DP>(kB, kB, contv(sW, LD), gc(sdY_),
                 [&](int m, int n, float val) { g(sdU_)[m * kB + n] += val; });
     // (the last term also takes U = T diag(beta) into dbeta: dbeta_j += sum_a T_aj dU_aj)
     gemm<F, F, kB>(kB, kB, gs(sX_), gs(sdP_), [&](int m, int n, float val) {
@@ -715,40 +743,40 @@ bwd_precond_kernel(int L, int nb, int slice0, const T* __restrict__ q, const T* 
         const int m = e / kB, n = e % kB;
         g(sAA_)[e] = sBeta[m] * g(sdG_)[m * kB + n] + sBeta[n] * g(sdG_)[n * kB + m];
     }
-    // dW = -P^T dQl - R dKr + dX^T Q + dM K + Y dE^T + U dY + (A + A^T) W,
-    // accumulated in sG (free now); dQ = dQl + dDg K + dX W; dK = dKr + dDg^T Q + dM^T W
-    for (int e = tid; e < kB * kLdB; e += 256) sG[e] = 0.f;
-    for (int e = tid; e < kB * DP; e += 256) {
-        const int r = e / DP, x = e % DP;
-        oQ[r * LD + x] = x < D ? dql[r * D + x] : 0.f;
-        oK[r * LD + x] = x < D ? dkr[r * D + x] : 0.f;
-    }
+    // dW = -P^T dQl - R dKr + dX^T Q + dM K + Y dE^T + U dY + (A + A^T) W;
+    // dQ = dQl + dDg K + dX W;  dK = dKr + dDg^T Q + dM^T W -- matrix-core
+    // accumulators in registers (a wave per output tile)
     __syncthreads();
-    auto accW = [&](int m, int n, float val) { sG[m * kLdB + n] += val; };
-    auto subW = [&](int m, int n, float val) { sG[m * kLdB + n] -= val; };
-    auto accQ = [&](int m, int n, float val) { oQ[m * LD + n] += val; };
-    auto accK = [&](int m, int n, float val) { oK[m * LD + n] += val; };
-    gemm<F, F, kB>(kB, DP, gs(sP_), strd(dql, D, D, kB), subW);
-    gemm<F, F, kB>(kB, DP, gc(sR_), strd(dkr, D, D, kB), subW);
-    gemm<F, XP, kB>(kB, DP, gs(sdX_), strd(sQ, LD), accW);
-    gemm<F, XP, kB>(kB, DP, gc(sdM_), strd(sK, LD), accW);
-    gemm<F, F, DP>(kB, DP, gc(sY_), cont(dem, D, D, D), accW);
-    gemm<F, F, kB>(kB, DP, gc(sU_), gs(sdY_), accW);
-    gemm<F, XP, kB>(kB, DP, gc(sAA_), strd(sW, LD), accW);
-    gemm<F, XP, kB>(kB, DP, cont(ddg, kB), strd(sK, LD), accQ);
-    gemm<F, XP, kB>(kB, DP, gc(sdX_), strd(sW, LD), accQ);
-    gemm<F, XP, kB>(kB, DP, strd(ddg, kB), strd(sQ, LD), accK);
-    gemm<F, XP, kB>(kB, DP, gs(sdM_), strd(sW, LD), accK);
-    __syncthreads();
-    for (int e = tid; e < kB * D; e += 256) {
-        const int r = e / D, x = e % D, pos = c * kB + r;
-        if (pos < L) {
-            const size_t gi = (base + pos) * D + x;
-            dq[gi] = from_f32<T>(oQ[r * LD + x]);
-            dk[gi] = from_f32<T>(oK[r * LD + x]);
-            dw[gi] = from_f32<T>(sG[r * kLdB + x]);
-        }
+    f32x16 aW = zero16(), aQ = zero16(), aK = zero16();
+    gemm_acc<F, F, kB>(kB, DP, gs(sP_), strd(dql, D, D, kB), aW);
+    for (int e = 0; e < 16; ++e) aW[e] = -aW[e];
+    {
+        f32x16 t = zero16();
+        gemm_acc<F, F, kB>(kB, DP, gc(sR_), strd(dkr, D, D, kB), t);
+        for (int e = 0; e < 16; ++e) aW[e] -= t[e];
     }
+    gemm_acc<F, XP, kB>(kB, DP, gs(sdX_), strdv(sQ, LD), aW);
+    gemm_acc<F, XP, kB>(kB, DP, gc(sdM_), strdv(sK, LD), aW);
+    gemm_acc<F, F, DP>(kB, DP, gc(sY_), cont(dem, D, D, D), aW);
+    gemm_acc<F, F, kB>(kB, DP, gc(sU_), gs(sdY_), aW);
+    gemm_acc<F, XP, kB>(kB, DP, gc(sAA_), strdv(sW, LD), aW);
+    gemm_acc<F, XP, kB>(kB, DP, cont(ddg, kB), strdv(sK, LD), aQ);
+    gemm_acc<F, XP, kB>(kB, DP, gc(sdX_), strdv(sW, LD), aQ);
+    gemm_acc<F, XP, kB>(kB, DP, strd(ddg, kB), strdv(sQ, LD), aK);
+    gemm_acc<F, XP, kB>(kB, DP, gs(sdM_), strdv(sW, LD), aK);
+    for_acc(kB, DP, aW, [&](int m, int n, float val) {
+        const int pos = c * kB + m;
+        if (n < D && pos < L) dw[(base + pos) * D + n] = from_f32<T>(val);
+    });
+    for_acc(kB, DP, aQ, [&](int m, int n, float val) {
+        const int pos = c * kB + m;
+        if (n < D && pos < L) dq[(base + pos) * D + n] = from_f32<T>(val + dql[m * D + n]);
+    });
+    for_acc(kB, DP, aK, [&](int m, int n, float val) {
+        const int pos = c * kB + m;
+        if (n < D && pos < L) dk[(base + pos) * D + n] = from_f32<T>(val + dkr[m * D + n]);
+    });
+    __syncthreads();
     if (tid < kB && c * kB + tid < L) dbeta[base + c * kB + tid] = sdB[tid];
 }
 
