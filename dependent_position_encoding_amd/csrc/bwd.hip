@@ -939,11 +939,11 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
                    const float* __restrict__ X, const float* __restrict__ Z,
                    float* __restrict__ dKr, float* __restrict__ dEm, bf16* __restrict__ dv,
                    float* __restrict__ colsum) {
-    __shared__ __attribute__((aligned(16))) BTile<kB, D, 2> sK;     // Kr_c [key][d]
+    __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sK;     // Kr_c [key][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sV;     // V_c [key][d]
-    __shared__ __attribute__((aligned(16))) BTile<kB, D, 2> sX;     // X_bc [query][d]
-    __shared__ __attribute__((aligned(16))) BTile<D, kB, 2> sXT;    // X_bc^T
-    __shared__ __attribute__((aligned(16))) BTile<D, kB, 2> sZT;    // A_{c-1}^T
+    __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sX;     // X_bc [query][d]
+    __shared__ __attribute__((aligned(16))) BTile<D, kB, 1> sXT;    // X_bc^T
+    __shared__ __attribute__((aligned(16))) BTile<D, kB, 1> sZT;    // A_{c-1}^T
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sdO;    // dO_b [query][d]
     __shared__ __attribute__((aligned(16))) BTile<D, kB, 1> sdOT;   // dO_b^T
     __shared__ __attribute__((aligned(16))) BTile<kB, kB, 1> sPT;   // P^T, then dS^T [key][query] (bf16)
@@ -1083,7 +1083,7 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         __syncthreads();
         if (b + 1 < nb) prefetch(b + 1);
         // P = exp(scale X Kr^T + bias - lse), queries m .. m+3 of key n, into P^T
-        gemm_b4<2, 2, D>(kB, kB, bview(sX), bview(sK), [&](int n, int m, f32x4 sv) {
+        gemm_b4<1, 1, D>(kB, kB, bview(sX), bview(sK), [&](int n, int m, f32x4 sv) {
             f32x4 p;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -1093,8 +1093,8 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         });
         backprop();
         // dKr += dS^T X (scaled at the end);  dE -= A_{c-1}^T X
-        gemm_b_acc<1, 2, kB>(kB, D, bview(sPT), bview(sXT), accK);
-        if (c >= 1) gemm_b_acc<2, 2, kB>(D, D, bview(sZT), bview(sXT), accE);
+        gemm_b_acc<1, 1, kB>(kB, D, bview(sPT), bview(sXT), accK);
+        if (c >= 1) gemm_b_acc<1, 1, kB>(D, D, bview(sZT), bview(sXT), accE);
         __syncthreads();   // the pair's tiles may be replaced
     }
     for_acc(kB, D, accK, [&](int m, int n, float val) {
@@ -1128,11 +1128,11 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
                      float* __restrict__ rowsum, float* __restrict__ delta) {
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sdO;    // dO_b [query][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sV;     // V_c [key][d]
-    __shared__ __attribute__((aligned(16))) BTile<kB, D, 2> sX;     // X_bc [query][d]
-    __shared__ __attribute__((aligned(16))) BTile<kB, D, 2> sK;     // Kr_c [key][d]
-    __shared__ __attribute__((aligned(16))) BTile<D, kB, 2> sKT;    // Kr_c^T [d][key]
-    __shared__ __attribute__((aligned(16))) BTile<D, D, 2> sET;     // E_c^T
-    __shared__ __attribute__((aligned(16))) BTile<kB, D, 2> sA;     // A_{c-1} [query][d]
+    __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sX;     // X_bc [query][d]
+    __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sK;     // Kr_c [key][d]
+    __shared__ __attribute__((aligned(16))) BTile<D, kB, 1> sKT;    // Kr_c^T [d][key]
+    __shared__ __attribute__((aligned(16))) BTile<D, D, 1> sET;     // E_c^T
+    __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sA;     // A_{c-1} [query][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, kB, 1> sS;    // P, then dS [query][key] (bf16)
     __shared__ float sLse[kB], sDel[kB], sGb[kB], sGc[kB], sRow[kB];
     __shared__ float sTb;
@@ -1284,7 +1284,7 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         if (c + 1 < b) prefetch(c + 1);
         const float shift = fox ? sTb - Tc : 0.f;   // sum of the totals of blocks c .. b-1
         // S^T = Kr X^T: keys m .. m+3 of query n, written to the query-major P
-        gemm_b4<2, 2, D>(kB, kB, bview(sK), bview(sX), [&](int n, int m, f32x4 sv) {
+        gemm_b4<1, 1, D>(kB, kB, bview(sK), bview(sX), [&](int n, int m, f32x4 sv) {
             f32x4 p;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -1295,9 +1295,9 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         backprop(false);
         // G^T = Kr^T dS^T;  (A E)^T = E^T A^T;  A^T <- scale G^T + A^T - (A E)^T
         f32x16 gt = zero16(), ae = zero16();
-        gemm_b_acc<2, 1, kB>(D, kB, bview(sKT), bview(sS), gt);
+        gemm_b_acc<1, 1, kB>(D, kB, bview(sKT), bview(sS), gt);
         if (c >= 1) {
-            gemm_b_acc<2, 2, D>(D, kB, bview(sET), bview(sA), ae);
+            gemm_b_acc<1, 1, D>(D, kB, bview(sET), bview(sA), ae);
             if (owner) {   // Z = A_{c-1}: four consecutive d of the lane's query per group
                 float* zo = Zs + pair_index(b, c) * kB * D + (size_t)qcol * D;
 #pragma unroll
