@@ -38,6 +38,8 @@ namespace pa {
 
 namespace {
 
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
 constexpr int kB = 64;          // block size
 constexpr int kLdB = kB + 4;    // LDS row stride of a B x B tile (floats)
 
@@ -258,7 +260,9 @@ struct TilePf {
 // chain: for query block b >= 1 of a slice, the queries Qw_c used against every
 // key block c < b, carried right to left as in the forward scan; stored per
 // block pair in X [slice][pair][B][d].  Longest chains first.
-template <int D, int PARTS>
+// OUTB: the carried queries are stored as bf16 (the bf16 path reads them in
+// one part), the transition taken as bf16(Qw) bf16(E) like the forward scan.
+template <int D, int PARTS, bool OUTB>
 __global__ void __launch_bounds__(256)
 bwd_chain_kernel(int nb, int nsc, int slice0, const float* __restrict__ ql,
                  const float* __restrict__ em, float* __restrict__ X) {
@@ -279,19 +283,26 @@ bwd_chain_kernel(int nb, int nsc, int slice0, const float* __restrict__ ql,
     if (b - 1 >= 1) pfE.load(em + (slice * nb + b - 1) * D * D, D);
     for (int c = b - 1; c >= 0; --c) {
         __syncthreads();
-        float* xo = Xs + pair_index(b, c) * kB * D;
         for (int e = tid; e < kB * (D / 4); e += 256) {
             const int r = e / (D / 4), x = 4 * (e % (D / 4));
-            *reinterpret_cast<f32x4*>(xo + (size_t)r * D + x) =
-                *reinterpret_cast<const f32x4*>(sQ + r * LD + x);
+            const f32x4 q4 = *reinterpret_cast<const f32x4*>(sQ + r * LD + x);
+            if constexpr (OUTB) {
+                __bf16* xo = reinterpret_cast<__bf16*>(X) + ((size_t)sl * npairs + pair_index(b, c)) * kB * D;
+                *reinterpret_cast<bf16x4_t*>(xo + (size_t)r * D + x) =
+                    bf16x4_t{(__bf16)q4[0], (__bf16)q4[1], (__bf16)q4[2], (__bf16)q4[3]};
+            } else {
+                float* xo = Xs + pair_index(b, c) * kB * D;
+                *reinterpret_cast<f32x4*>(xo + (size_t)r * D + x) = q4;
+            }
         }
         if (c == 0) break;
         pfE.store(sE, LD);
         __syncthreads();
         if (c - 1 >= 1) pfE.load(em + (slice * nb + c - 1) * D * D, D);
         // Qw_{c-1} = Qw_c - Qw_c E_c^T:  B(k, n) = E[n][k]
-        gemm<PARTS, PARTS, DP>(kB, DP, cont(sQ, LD), cont(sE, LD),
-                           [&](int m, int n, float v) { sT[m * LD + n] = v; });
+        constexpr int PC = OUTB ? 1 : PARTS;
+        gemm<PC, PC, DP>(kB, DP, cont(sQ, LD), cont(sE, LD),
+                         [&](int m, int n, float v) { sT[m * LD + n] = v; });
         __syncthreads();
         for (int e = tid; e < kB * DP; e += 256) {
             const int r = e / DP, x = e % DP;
@@ -816,8 +827,6 @@ bwd_gate_kernel(int L, int nb, const float* __restrict__ rowsum,
 // intermediates -- in the orientation its products read it, so a fragment is
 // one or two 16-byte loads and nothing is converted inside a product.
 
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-
 // An R x C fp32 matrix as P bf16 parts, rows padded to C + 8 elements (16-byte
 // multiples; consecutive rows start in different bank groups).
 template <int R, int C, int P>
@@ -952,9 +961,10 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     const int c = (int)(blockIdx.x / nsc), sl = (int)(blockIdx.x % nsc);
     const size_t slice = (size_t)slice0 + sl, blk_c = slice * nb + c, base = slice * L;
     const size_t npairs = (size_t)nb * (nb - 1) / 2;
-    const float* Xs = X + (size_t)sl * npairs * kB * D;
-    const float* Zs = Z + (size_t)sl * npairs * kB * D;
-    constexpr int NB4 = kB * D / 16;   // 4 x 4 blocks of a [kB][D] fp32 tile
+    // the carried queries and the gradient chain, bf16 [pair][kB][D]
+    const __bf16* Xs = reinterpret_cast<const __bf16*>(X) + (size_t)sl * npairs * kB * D;
+    const __bf16* Zs = reinterpret_cast<const __bf16*>(Z) + (size_t)sl * npairs * kB * D;
+    constexpr int NB4 = kB * D / 16;   // 4 x 4 blocks of a [kB][D] tile
     constexpr int NB8 = kB * D / 32;   // 4 x 8 blocks of a [kB][D] bf16 tile
     const int rb4 = tid / (D / 4), cb4 = tid % (D / 4);   // this thread's 4 x 4 block
     const int rb8 = tid / (D / 8), cb8 = tid % (D / 8);   // and 4 x 8 block
@@ -976,19 +986,19 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         sGc[tid] = fox ? fw.gl[blk_c * kB + tid] : 0.f;
         sCol[tid] = 0.f;
     }
-    // prefetch of query block b's X_bc, Z_bc, dO and row terms
-    f32x4 pX[4], pZ[4];
+    // prefetch of query block b's X_bc, Z_bc (4 x 4 bf16 blocks), dO and row terms
+    bf16x4_t pX[4], pZ[4];
     u32x4 pO[4];
     float pLse = 0.f, pDel = 0.f, pGb = 0.f;
     auto prefetch = [&](int b) {
         const size_t blk_b = slice * nb + b;
         if (b > c && tid < NB4) {
-            const float* xb = Xs + pair_index(b, c) * kB * D + (size_t)(4 * rb4) * D + 4 * cb4;
-            const float* zb = Zs + pair_index(b, c) * kB * D + (size_t)(4 * rb4) * D + 4 * cb4;
+            const __bf16* xb = Xs + pair_index(b, c) * kB * D + (size_t)(4 * rb4) * D + 4 * cb4;
+            const __bf16* zb = Zs + pair_index(b, c) * kB * D + (size_t)(4 * rb4) * D + 4 * cb4;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                pX[q] = *reinterpret_cast<const f32x4*>(xb + (size_t)q * D);
-                if (c >= 1) pZ[q] = *reinterpret_cast<const f32x4*>(zb + (size_t)q * D);
+                pX[q] = *reinterpret_cast<const bf16x4_t*>(xb + (size_t)q * D);
+                if (c >= 1) pZ[q] = *reinterpret_cast<const bf16x4_t*>(zb + (size_t)q * D);
             }
         }
         if (tid < NB8) {
@@ -1011,10 +1021,12 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         if (b > c && tid < NB4) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                sX.put4(4 * rb4 + q, 4 * cb4, pX[q]);
-                sXT.put4(4 * cb4 + q, 4 * rb4, f32x4{pX[0][q], pX[1][q], pX[2][q], pX[3][q]});
+                *reinterpret_cast<bf16x4_t*>(&sX.v[0][(4 * rb4 + q) * sX.LDE + 4 * cb4]) = pX[q];
+                *reinterpret_cast<bf16x4_t*>(&sXT.v[0][(4 * cb4 + q) * sXT.LDE + 4 * rb4]) =
+                    bf16x4_t{pX[0][q], pX[1][q], pX[2][q], pX[3][q]};
                 if (c >= 1)
-                    sZT.put4(4 * cb4 + q, 4 * rb4, f32x4{pZ[0][q], pZ[1][q], pZ[2][q], pZ[3][q]});
+                    *reinterpret_cast<bf16x4_t*>(&sZT.v[0][(4 * cb4 + q) * sZT.LDE + 4 * rb4]) =
+                        bf16x4_t{pZ[0][q], pZ[1][q], pZ[2][q], pZ[3][q]};
             }
         }
         if (tid < NB8) {
@@ -1140,11 +1152,12 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     const int b = nb - 1 - (int)(blockIdx.x / nsc), sl = (int)(blockIdx.x % nsc);
     const size_t slice = (size_t)slice0 + sl, blk_b = slice * nb + b, base = slice * L;
     const size_t npairs = (size_t)nb * (nb - 1) / 2;
-    const float* Xs = X + (size_t)sl * npairs * kB * D;
-    float* Zs = Z + (size_t)sl * npairs * kB * D;
+    // the carried queries and the gradient chain, bf16 [pair][kB][D]
+    const __bf16* Xs = reinterpret_cast<const __bf16*>(X) + (size_t)sl * npairs * kB * D;
+    __bf16* Zs = reinterpret_cast<__bf16*>(Z) + (size_t)sl * npairs * kB * D;
     const float* kr = static_cast<const float*>(fw.kr);
     const float* em = static_cast<const float*>(fw.em);
-    constexpr int UF = kB * D / 4 / 256, UB = kB * D / 8 / 256;
+    constexpr int UB = kB * D / 8 / 256;
     constexpr int NB4 = kB * D / 16, NE4 = D * D / 16;
     const int rb4 = tid / (D / 4), cb4 = tid % (D / 4);
 
@@ -1176,8 +1189,8 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         sTb = s;
     }
     // prefetch of key block c's V, Kr (4 x 4 blocks), X_bc, E (4 x 4 blocks)
-    u32x4 pV[UB];
-    f32x4 pK[4], pX[UF], pE[4];
+    u32x4 pV[UB], pX[UB];
+    f32x4 pK[4], pE[4];
     float pGc = 0.f;
     auto prefetch = [&](int c) {
         const size_t blk_c = slice * nb + c;
@@ -1195,9 +1208,9 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
                                                          (size_t)(4 * rb4 + q) * D + 4 * cb4);
         if (c < b)
 #pragma unroll
-            for (int i = 0; i < UF; ++i) {
-                const int e = tid + 256 * i, r = e / (D / 4), c0 = 4 * (e % (D / 4));
-                pX[i] = *reinterpret_cast<const f32x4*>(Xs + pair_index(b, c) * kB * D +
+            for (int i = 0; i < UB; ++i) {
+                const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+                pX[i] = *reinterpret_cast<const u32x4*>(Xs + pair_index(b, c) * kB * D +
                                                          (size_t)r * D + c0);
             }
         if (c >= 1 && tid < NE4)
@@ -1221,9 +1234,9 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
             }
         if (c < b)
 #pragma unroll
-            for (int i = 0; i < UF; ++i) {
-                const int e = tid + 256 * i, r = e / (D / 4), c0 = 4 * (e % (D / 4));
-                sX.put4(r, c0, pX[i]);
+            for (int i = 0; i < UB; ++i) {
+                const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+                *reinterpret_cast<u32x4*>(&sX.v[0][r * sX.LDE + c0]) = pX[i];
             }
         if (c >= 1 && tid < NE4)
 #pragma unroll
@@ -1299,11 +1312,12 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         if (c >= 1) {
             gemm_b_acc<1, 1, D>(D, kB, bview(sET), bview(sA), ae);
             if (owner) {   // Z = A_{c-1}: four consecutive d of the lane's query per group
-                float* zo = Zs + pair_index(b, c) * kB * D + (size_t)qcol * D;
+                __bf16* zo = Zs + pair_index(b, c) * kB * D + (size_t)qcol * D;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<f32x4*>(zo + mA + 8 * i + 4 * h) =
-                        f32x4{At[4 * i], At[4 * i + 1], At[4 * i + 2], At[4 * i + 3]};
+                    *reinterpret_cast<bf16x4_t*>(zo + mA + 8 * i + 4 * h) =
+                        bf16x4_t{(__bf16)At[4 * i], (__bf16)At[4 * i + 1], (__bf16)At[4 * i + 2],
+                                 (__bf16)At[4 * i + 3]};
             }
         }
 #pragma unroll
@@ -1351,8 +1365,9 @@ hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
     for (int s0 = 0; s0 < ns; s0 += a.chunk) {
         const int nsc = std::min(a.chunk, ns - s0);
         if (nb > 1) {
-            hipLaunchKernelGGL((bwd_chain_kernel<D, PARTS>), dim3(nsc * (nb - 1)), dim3(256), 0,
-                               st, nb, nsc, s0, a.fw.ql, (const float*)a.fw.em, a.X);
+            constexpr bool OUTB = sizeof(T) == 2 && D >= 32;
+            hipLaunchKernelGGL((bwd_chain_kernel<D, PARTS, OUTB>), dim3(nsc * (nb - 1)), dim3(256),
+                               0, st, nb, nsc, s0, a.fw.ql, (const float*)a.fw.em, a.X);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         if constexpr (sizeof(T) == 2 && D >= 32) {
