@@ -679,15 +679,22 @@ bwd_precond_kernel(int L, int nb, int slice0, const T* __restrict__ q, const T* 
         g(sWW_)[m * kB + n] = val;
     });
     __syncthreads();
-    // T = (I + G)^{-1}: T_jj = 1, T_ij = -sum_{k=j}^{i-1} G_ik T_kj, a column per thread
+    // T = (I + G)^{-1}: T_jj = 1, T_ij = -sum_{k=j}^{i-1} G_ik T_kj.  A lane of the
+    // first wave per column, the column in registers; the sum runs over all
+    // k < i for every lane (T_kj = 0 for k < j), so the loops are uniform and
+    // unrolled, and every lane reads the same G entries (LDS broadcasts).
     if (tid < kB) {
         const int j = tid;
+        float t[kB];
+#pragma unroll
         for (int i = 0; i < kB; ++i) {
-            float t = i == j ? 1.f : 0.f;
-            if (i > j)
-                for (int kk = j; kk < i; ++kk) t -= sG[i * kLdB + kk] * sT[kk * kLdB + j];
-            sT[i * kLdB + j] = t;
+            float acc = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < i; ++kk) acc -= sG[i * kLdB + kk] * t[kk];
+            t[i] = i == j ? 1.f : (i < j ? 0.f : acc);
         }
+#pragma unroll
+        for (int i = 0; i < kB; ++i) sT[i * kLdB + j] = t[i];
     }
     __syncthreads();
     for (int e = tid; e < kB * kB; e += 256) g(sU_)[e] = sT[(e / kB) * kLdB + e % kB] * sBeta[e % kB];
