@@ -55,6 +55,12 @@ class _Cache(ctypes.Structure):
                 ("gcache", ctypes.c_void_p)]
 
 
+class _PagedCache(ctypes.Structure):
+    _fields_ = [("num_pages", ctypes.c_int), ("page_size", ctypes.c_int),
+                ("k_dtype", ctypes.c_int), ("kpages", ctypes.c_void_p),
+                ("vpages", ctypes.c_void_p), ("gpages", ctypes.c_void_p)]
+
+
 _lib = None
 
 EXPORTS = ["path_abi_version", "path_status_str", "path_last_error",
@@ -62,7 +68,8 @@ EXPORTS = ["path_abi_version", "path_status_str", "path_last_error",
            "path_kv_append", "path_decode_workspace", "path_decode",
            "path_decode_step", "path_causal_attn_fwd", "path_attn_fwd_timed",
            "path_param_workspace", "path_param_fwd", "path_attn_bwd_workspace",
-           "path_attn_bwd"]
+           "path_attn_bwd", "path_paged_decode_workspace", "path_paged_decode_step",
+           "path_paged_import"]
 
 
 def load_library(path: str = LIB_PATH):
@@ -92,6 +99,10 @@ def load_library(path: str = LIB_PATH):
         "path_param_fwd": ([ctypes.POINTER(_ParamDesc)] + [P] * 12 + [S, P], I),
         "path_attn_bwd_workspace": ([DP], S),
         "path_attn_bwd": ([DP] + [P] * 16 + [S, P], I),
+        "path_paged_decode_workspace": ([DP, I], S),
+        "path_paged_decode_step": ([DP, ctypes.POINTER(_PagedCache), P, I, P, I] + [P] * 9
+                                   + [S, P], I),
+        "path_paged_import": ([DP, CP, ctypes.POINTER(_PagedCache), P, I, P, I, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -331,6 +342,93 @@ def decode_step(cache: Cache, n: int, q_t, k_t, v_t, w_t, beta_t, logf_t=None,
                                 _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
                                 _stream(cache.device)))
     return o, lse
+
+
+class PagedCache:
+    """Paged decode cache for a batch of sequences: kpages/vpages
+    [num_pages, H, page_size, d], gpages [num_pages, H, page_size] (or None).
+
+    A sequence's slots [i*page_size, (i+1)*page_size) live in the page its
+    table row names at entry i; slots hold rewritten keys as in Cache.
+    """
+
+    def __init__(self, num_pages, page_size, H, d, dtype=torch.bfloat16, k_dtype=None,
+                 gate=True, device="cuda"):
+        self.num_pages, self.page_size, self.H, self.d = num_pages, page_size, H, d
+        self.dtype = dtype
+        self.k_dtype = dtype if k_dtype is None else k_dtype
+        self.kpages = torch.zeros(num_pages, H, page_size, d, dtype=self.k_dtype, device=device)
+        self.vpages = torch.zeros(num_pages, H, page_size, d, dtype=dtype, device=device)
+        self.gpages = (torch.zeros(num_pages, H, page_size, dtype=torch.float32, device=device)
+                       if gate else None)
+        self.device = self.kpages.device
+
+    def _c(self):
+        return _PagedCache(self.num_pages, self.page_size, _dtype_code(self.k_dtype),
+                           self.kpages.data_ptr(), self.vpages.data_ptr(),
+                           self.gpages.data_ptr() if self.gpages is not None else None)
+
+
+def _paged_tables(cache: PagedCache, page_table, seq_lens, max_keys):
+    S = seq_lens.shape[0]
+    _need(seq_lens, "seq_lens", cache.device, (S,), torch.int32)
+    if page_table.dim() != 2 or page_table.shape[0] != S:
+        raise ValueError(f"page_table must be [S, table_stride], got {tuple(page_table.shape)}")
+    _need(page_table, "page_table", cache.device, None, torch.int32)
+    return S, page_table.shape[1]
+
+
+def paged_decode_workspace_bytes(S, H, d, dtype, max_keys) -> int:
+    lib = load_library()
+    return int(lib.path_paged_decode_workspace(ctypes.byref(_desc(S, H, 1, d, dtype, 1.0)),
+                                               int(max_keys)))
+
+
+def paged_decode_step(cache: PagedCache, page_table, seq_lens, max_keys, q_t, k_t, v_t, w_t,
+                      beta_t, logf_t=None, scale=None, workspace=None, out=None):
+    """Fused step for a batch of S sequences at positions seq_lens (int32 [S],
+    advanced by one): rewrite each sequence's cached keys, append its token,
+    attend.  q_t, k_t, v_t, w_t [S,H,d]; beta_t, logf_t [S,H] fp32; page_table
+    int32 [S, table_stride].  Returns (o_t [S,H,d], lse_t [S,H])."""
+    lib = load_library()
+    S, stride = _paged_tables(cache, page_table, seq_lens, max_keys)
+    H, d = cache.H, cache.d
+    for name, t in (("q_t", q_t), ("k_t", k_t), ("v_t", v_t), ("w_t", w_t)):
+        _need(t, name, cache.device, (S, H, d), cache.dtype)
+    _need(beta_t, "beta_t", cache.device, (S, H), torch.float32)
+    if logf_t is not None:
+        _need(logf_t, "logf_t", cache.device, (S, H), torch.float32)
+    scale = d ** -0.5 if scale is None else scale
+    desc = _desc(S, H, 1, d, cache.dtype, scale)
+    nbytes = paged_decode_workspace_bytes(S, H, d, cache.dtype, max_keys)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=cache.device)
+    if out is None:
+        o = torch.empty_like(q_t)
+        lse = torch.empty(S, H, dtype=torch.float32, device=cache.device)
+    else:
+        o, lse = out
+    pc = cache._c()
+    _check(lib.path_paged_decode_step(ctypes.byref(desc), ctypes.byref(pc), _ptr(page_table),
+                                      int(stride), _ptr(seq_lens), int(max_keys), _ptr(q_t),
+                                      _ptr(k_t), _ptr(v_t), _ptr(w_t), _ptr(beta_t),
+                                      _ptr(logf_t), _ptr(o), _ptr(lse), _ptr(workspace),
+                                      workspace.numel(), _stream(cache.device)))
+    return o, lse
+
+
+def paged_import(src: Cache, dst: PagedCache, page_table, seq_lens, max_keys):
+    """Copy slots [0, seq_lens[s]) of each sequence of a contiguous cache into
+    its pages (src.N = S sequences)."""
+    lib = load_library()
+    S, stride = _paged_tables(dst, page_table, seq_lens, max_keys)
+    if src.N != S or src.H != dst.H or src.d != dst.d:
+        raise ValueError("source cache and paged cache shapes differ")
+    desc = _desc(S, dst.H, 1, dst.d, dst.dtype, 1.0)
+    sc, pc = src._c(), dst._c()
+    _check(lib.path_paged_import(ctypes.byref(desc), ctypes.byref(sc), ctypes.byref(pc),
+                                 _ptr(page_table), int(stride), _ptr(seq_lens), int(max_keys),
+                                 _stream(dst.device)))
 
 
 def causal_attn(q, k, v, scale=None, out=None):

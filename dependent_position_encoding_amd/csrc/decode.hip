@@ -136,20 +136,49 @@ __global__ void kv_append_kernel(K* __restrict__ kc, T* __restrict__ vc,
 // value and prefix loads are issued before any arithmetic (KPG rows in flight
 // per group), then one max / sum / weighted value sum over its keys.  Groups
 // are merged through LDS and the chunk's partial softmax state
-// (m, l, acc[D]) goes to part[slice][chunk].
+// (m, l, acc[D]) goes to `out`.
+//
+// Where slot j of a slice lives is a policy: its key row starts at element
+// Rows::off(j) of Rows::k0 and its value row at the same offset of Rows::v0;
+// Rows::g(j) points at its log-f prefix entry (Rows::gate() false: no gate).
 constexpr int kDecChunk = 128;
 
-template <typename K, typename T, int D, bool FUSED>
-__global__ void __launch_bounds__(256)
-decode_chunk_kernel(K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ gc,
-                    int cap, int n_keys, float scale,
-                    const T* __restrict__ q_t, const T* __restrict__ k_t,
-                    const T* __restrict__ v_t, const T* __restrict__ w_t,
-                    const float* __restrict__ beta_t, const float* __restrict__ logf_t,
-                    float* __restrict__ part) {
+// one slice of a contiguous cache [slice][cap][D]
+template <typename K, typename T, int D>
+struct ContigRows {
+    K* k0;            // the slice's slot 0
+    T* v0;
+    float* g0;        // its log-f prefix (NULL: no gate)
+    __device__ size_t off(int j) const { return (size_t)j * D; }
+    __device__ float* g(int j) const { return g0 + j; }
+    __device__ bool gate() const { return g0 != nullptr; }
+};
+
+// one (sequence, head) of a paged cache [page][H][P][D]: slot j is in page
+// table[j >> lp] at position j & (P - 1)
+template <typename K, typename T, int D>
+struct PagedRows {
+    K* k0;             // the page pool
+    T* v0;
+    float* gp;         // log-f pages [page][H][P] (NULL: no gate)
+    const int* table;  // the sequence's page table row
+    int lp, H, h;
+    __device__ size_t slab(int j) const {
+        return ((size_t)table[j >> lp] * H + h) << lp | (size_t)(j & ((1 << lp) - 1));
+    }
+    __device__ size_t off(int j) const { return slab(j) * D; }
+    __device__ float* g(int j) const { return gp + slab(j); }
+    __device__ bool gate() const { return gp != nullptr; }
+};
+
+template <typename K, typename T, int D, bool FUSED, typename Rows>
+__device__ inline void chunk_attend(const Rows& rows, int slice, int ch, int n_keys, float scale,
+                                    const T* __restrict__ q_t, const T* __restrict__ k_t,
+                                    const T* __restrict__ v_t, const T* __restrict__ w_t,
+                                    const float* __restrict__ beta_t,
+                                    const float* __restrict__ logf_t, float* __restrict__ out) {
     constexpr int VN = Vec<K>::n, TPR = D / VN, GROUPS = 256 / TPR;
     constexpr int KPG = kDecChunk / GROUPS;      // keys per group
-    const int slice = blockIdx.y, ch = blockIdx.x, nch = gridDim.x;
     const int lane_in = threadIdx.x % TPR, grp = threadIdx.x / TPR;
     const int t = n_keys - 1;                     // query position
     const size_t sd = (size_t)slice * D + lane_in * VN;
@@ -161,14 +190,12 @@ decode_chunk_kernel(K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ 
         wv[e] = FUSED ? to_f32(w_t[sd + e]) : 0.f;
     }
     const float bt = FUSED ? beta_t[slice] : 0.f;
-    float* gbase = gc ? gc + (size_t)slice * cap : nullptr;
+    const bool gate = rows.gate();
     float ct = 0.f;                               // C_t
-    if (gbase) {
-        if (FUSED) ct = (t > 0 ? gbase[t - 1] : 0.f) + logf_t[slice];
-        else ct = gbase[t];
+    if (gate) {
+        if (FUSED) ct = (t > 0 ? *rows.g(t - 1) : 0.f) + logf_t[slice];
+        else ct = *rows.g(t);
     }
-    K* kbase = kc + (size_t)slice * cap * D;
-    T* vbase = vc + (size_t)slice * cap * D;
     const int j0 = ch * kDecChunk;
 
     // ---- loads (every key of this group in flight at once)
@@ -178,12 +205,12 @@ decode_chunk_kernel(K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ 
 #pragma unroll
     for (int i = 0; i < KPG; ++i) {
         const int j = j0 + grp + GROUPS * i;
-        const size_t off = (size_t)j * D + lane_in * VN;
         const bool live = j < n_keys && !(FUSED && j == t);
         if (live) {
-            kx[i].load(kbase + off);
-            vr[i].load(vbase + off);
-            gj[i] = gbase ? gbase[j] : 0.f;
+            const size_t off = rows.off(j) + lane_in * VN;
+            kx[i].load(rows.k0 + off);
+            vr[i].load(rows.v0 + off);
+            gj[i] = gate ? *rows.g(j) : 0.f;
         } else {
             // keys past the end get weight 0; their values must be finite
 #pragma unroll
@@ -197,22 +224,22 @@ decode_chunk_kernel(K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ 
 #pragma unroll
     for (int i = 0; i < KPG; ++i) {
         const int j = j0 + grp + GROUPS * i;
-        const size_t off = (size_t)j * D + lane_in * VN;
         float kf[VN], bias = 0.f;
         if (j >= n_keys) {
             sc[i] = -INFINITY;
             continue;
         }
+        const size_t off = rows.off(j) + lane_in * VN;
         if (FUSED && j == t) {
             // the new token: stored as given, its own transition excluded
 #pragma unroll
             for (int e = 0; e < VN; ++e) {
                 kf[e] = to_f32(from_f32<K>(to_f32(k_t[sd + e])));
-                kbase[off + e] = from_f32<K>(kf[e]);
-                vbase[off + e] = v_t[sd + e];
+                rows.k0[off + e] = from_f32<K>(kf[e]);
+                rows.v0[off + e] = v_t[sd + e];
             }
             vr[i].load(v_t + sd);
-            if (gbase && lane_in == 0) gbase[t] = ct;
+            if (gate && lane_in == 0) *rows.g(t) = ct;
         } else {
             if (FUSED) {
                 float p = 0.f;
@@ -221,11 +248,11 @@ decode_chunk_kernel(K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ 
                 const float cf = bt * group_sum<TPR>(p);
 #pragma unroll
                 for (int e = 0; e < VN; ++e) kx[i].set(e, kx[i].get(e) - cf * wv[e]);
-                kx[i].store(kbase + off);
+                kx[i].store(rows.k0 + off);
             }
 #pragma unroll
             for (int e = 0; e < VN; ++e) kf[e] = kx[i].get(e);
-            bias = gbase ? ct - gj[i] : 0.f;
+            bias = gate ? ct - gj[i] : 0.f;
         }
         float p = 0.f;
 #pragma unroll
@@ -253,7 +280,6 @@ decode_chunk_kernel(K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ 
 #pragma unroll
     for (int e = 0; e < VN; ++e) sacc[grp][lane_in * VN + e] = acc[e];
     __syncthreads();
-    float* out = part + ((size_t)slice * nch + ch) * (D + 2);
     if (threadIdx.x < D) {
         const int x = threadIdx.x;
         float M = -INFINITY;
@@ -269,24 +295,94 @@ decode_chunk_kernel(K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ 
     }
 }
 
+// Contiguous cache: grid (chunks, slices); partials part[slice][chunk].
+template <typename K, typename T, int D, bool FUSED>
+__global__ void __launch_bounds__(256)
+decode_chunk_kernel(K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ gc,
+                    int cap, int n_keys, float scale,
+                    const T* __restrict__ q_t, const T* __restrict__ k_t,
+                    const T* __restrict__ v_t, const T* __restrict__ w_t,
+                    const float* __restrict__ beta_t, const float* __restrict__ logf_t,
+                    float* __restrict__ part) {
+    const int slice = blockIdx.y, ch = blockIdx.x, nch = gridDim.x;
+    const ContigRows<K, T, D> rows{kc + (size_t)slice * cap * D, vc + (size_t)slice * cap * D,
+                                   gc ? gc + (size_t)slice * cap : nullptr};
+    chunk_attend<K, T, D, FUSED>(rows, slice, ch, n_keys, scale, q_t, k_t, v_t, w_t, beta_t,
+                                 logf_t, part + ((size_t)slice * nch + ch) * (D + 2));
+}
+
+// Paged cache, one fused step for a batch of sequences of their own lengths
+// [Notes s2.8]: grid (chunks of the longest sequence, S * H); slice = s*H + h.
+// Sequence s has n_keys = seq_lens[s] + 1 keys (the new token at slot
+// seq_lens[s]); chunks past its end exit at once.  The chunk-0 workgroup
+// records n_keys (or -1 when seq_lens[s] is out of [0, max_keys)) in nk[slice]
+// for the combine.  A chunk whose page-table entries fall outside
+// [0, num_pages) touches no cache memory and leaves m = +inf, which makes the
+// combine's result NaN for that (sequence, head).
+template <typename K, typename T, int D>
+__global__ void __launch_bounds__(256)
+paged_chunk_kernel(K* __restrict__ kp, T* __restrict__ vp, float* __restrict__ gp,
+                   int num_pages, int lp, int H, const int* __restrict__ tables,
+                   int table_stride, const int* __restrict__ seq_lens, int max_keys,
+                   float scale, const T* __restrict__ q_t, const T* __restrict__ k_t,
+                   const T* __restrict__ v_t, const T* __restrict__ w_t,
+                   const float* __restrict__ beta_t, const float* __restrict__ logf_t,
+                   float* __restrict__ part, int* __restrict__ nk) {
+    const int slice = blockIdx.y, ch = blockIdx.x, nch = gridDim.x;
+    const int s = slice / H, h = slice % H;
+    const int len = seq_lens[s];
+    const bool ok = len >= 0 && len < max_keys;
+    const int n_keys = len + 1;
+    if (ch == 0 && threadIdx.x == 0) nk[slice] = ok ? n_keys : -1;
+    if (!ok || ch * kDecChunk >= n_keys) return;
+    const int* table = tables + (size_t)s * table_stride;
+    float* out = part + ((size_t)slice * nch + ch) * (D + 2);
+    // every page this chunk reaches must exist
+    const int p0 = (ch * kDecChunk) >> lp, p1 = (min(n_keys, (ch + 1) * kDecChunk) - 1) >> lp;
+    bool pages_ok = true;
+    for (int p = p0; p <= p1; ++p) pages_ok = pages_ok && (unsigned)table[p] < (unsigned)num_pages;
+    if (!pages_ok) {
+        if (threadIdx.x < D + 2) out[threadIdx.x] = threadIdx.x == 0 ? INFINITY : 0.f;
+        return;
+    }
+    const PagedRows<K, T, D> rows{kp, vp, gp, table, lp, H, h};
+    chunk_attend<K, T, D, true>(rows, slice, ch, n_keys, scale, q_t, k_t, v_t, w_t, beta_t,
+                                logf_t, out);
+}
+
 // Merge the chunk partials of one slice: o = sum acc_c e^{m_c - M} / l,
 // lse = M + log l.  One 1024-thread block per slice, one chunk per thread for
 // the maxima and sums (wave shuffles, then one LDS exchange of the 16 wave
 // results), and 1024/D groups of D lanes each summing a strided share of the
 // chunks' accumulators (every load of a group in flight at once).
+// Contiguous cache: every slice has nch chunks (nk NULL).  Paged cache: slice
+// s*H + h has ceil(nk[slice] / kDecChunk) of the pstride chunk rows (nk < 0:
+// the output is NaN), and the head-0 block of a sequence then advances
+// seq_lens[s] to nk (the chunk kernel, which reads it, has finished).
 constexpr int kCombineMaxChunks = 1024;
 constexpr int kCombineThreads = 1024;
 
 template <typename T, int D>
 __global__ void __launch_bounds__(kCombineThreads)
-decode_combine_kernel(const float* __restrict__ part, int nch, T* __restrict__ o_t,
-                      float* __restrict__ lse_t) {
+decode_combine_kernel(const float* __restrict__ part, int nch, int pstride,
+                      const int* __restrict__ nk, int H, int* __restrict__ seq_lens,
+                      T* __restrict__ o_t, float* __restrict__ lse_t) {
     constexpr int NTH = kCombineThreads, NW = NTH / 64, G = NTH / D;
     __shared__ float wmax[NW], wsum[NW];
     __shared__ float sf[kCombineMaxChunks];
     __shared__ float sacc[G][D];
     const int slice = blockIdx.x, tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
-    const float* p = part + (size_t)slice * nch * (D + 2);
+    if (nk) {
+        const int n = nk[slice];
+        if (n < 1) {
+            if (tid < D) o_t[(size_t)slice * D + tid] = from_f32<T>(NAN);
+            if (tid == 0 && lse_t) lse_t[slice] = NAN;
+            return;
+        }
+        nch = (n + kDecChunk - 1) / kDecChunk;
+        if (tid == 0 && seq_lens && slice % H == 0) seq_lens[slice / H] = n;
+    }
+    const float* p = part + (size_t)slice * pstride * (D + 2);
     const float mc = tid < nch ? p[(size_t)tid * (D + 2)] : -INFINITY;
     const float lc = tid < nch ? p[(size_t)tid * (D + 2) + 1] : 0.f;
     float mx = mc;
@@ -687,7 +783,7 @@ static hipError_t decode_t(const CacheArgs& c, int n_keys, float scale, const vo
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(c.N * c.H), dim3(kCombineThreads), 0, st,
-                       (const float*)part, nch, (T*)o_t, lse_t);
+                       (const float*)part, nch, nch, nullptr, c.H, nullptr, (T*)o_t, lse_t);
     return hipGetLastError();
 }
 
@@ -713,6 +809,109 @@ hipError_t launch_decode(const CacheArgs& c, int n_keys, float scale, const void
                         : decode_d<bf16, float>(c, n_keys, scale, q_t, o_t, lse_t, part, chunk, fused, k_t, v_t, w_t, beta_t, logf_t, st);
     return c.v_bf16 ? decode_d<float, bf16>(c, n_keys, scale, q_t, o_t, lse_t, part, chunk, fused, k_t, v_t, w_t, beta_t, logf_t, st)
                     : decode_d<float, float>(c, n_keys, scale, q_t, o_t, lse_t, part, chunk, fused, k_t, v_t, w_t, beta_t, logf_t, st);
+}
+
+// ---------------------------------------------------------------------------
+// Paged cache: one fused step for a batch of sequences, and the import of a
+// contiguous (prefill-aligned) cache into pages.
+
+// Slots [0, n) of sequence s (n = seq_lens[s], at most min(max_keys, cap)) of a
+// contiguous cache [S][H][cap][D] copied into the sequence's pages.  Grid
+// (pages of the longest sequence, S * H).  Pages whose table entry is outside
+// [0, num_pages), and sequences whose length is out of range, are skipped.
+template <typename K, typename T, int D>
+__global__ void __launch_bounds__(256)
+paged_import_kernel(const K* __restrict__ kc, const T* __restrict__ vc,
+                    const float* __restrict__ gc, int cap, K* __restrict__ kp,
+                    T* __restrict__ vp, float* __restrict__ gp, int num_pages, int lp, int H,
+                    const int* __restrict__ tables, int table_stride,
+                    const int* __restrict__ seq_lens, int max_keys) {
+    constexpr int KU = 16 / (int)sizeof(K), VU = 16 / (int)sizeof(T);   // elements per 16 B
+    const int slice = blockIdx.y, pg = blockIdx.x, s = slice / H, h = slice % H;
+    const int P = 1 << lp;
+    const int n = seq_lens[s];
+    if (n < 0 || n > max_keys || n > cap || pg * P >= n) return;
+    const int page = tables[(size_t)s * table_stride + pg];
+    if ((unsigned)page >= (unsigned)num_pages) return;
+    const int rows = min(P, n - pg * P);
+    const size_t src = ((size_t)slice * cap + (size_t)pg * P) * D;
+    const size_t dst = ((size_t)page * H + h) * P * D;
+    for (int e = threadIdx.x; e < rows * (D / KU); e += blockDim.x)
+        *reinterpret_cast<uint4*>(kp + dst + (size_t)e * KU) =
+            *reinterpret_cast<const uint4*>(kc + src + (size_t)e * KU);
+    for (int e = threadIdx.x; e < rows * (D / VU); e += blockDim.x)
+        *reinterpret_cast<uint4*>(vp + dst + (size_t)e * VU) =
+            *reinterpret_cast<const uint4*>(vc + src + (size_t)e * VU);
+    if (gc && gp)
+        for (int r = threadIdx.x; r < rows; r += blockDim.x)
+            gp[((size_t)page * H + h) * P + r] = gc[(size_t)slice * cap + pg * P + r];
+}
+
+template <typename K, typename T, int D>
+static hipError_t paged_step_t(const PagedArgs& a, hipStream_t st) {
+    const int mch = (a.max_keys + kDecChunk - 1) / kDecChunk;
+    const int S = a.S * a.H;
+    float* part = a.ws;
+    int* nk = reinterpret_cast<int*>(a.ws + (size_t)S * mch * (D + 2));
+    hipLaunchKernelGGL((paged_chunk_kernel<K, T, D>), dim3(mch, S), dim3(256), 0, st,
+                       (K*)a.kpages, (T*)a.vpages, a.gpages, a.num_pages, a.lp, a.H, a.tables,
+                       a.table_stride, (const int*)a.seq_lens, a.max_keys, a.scale,
+                       (const T*)a.q_t, (const T*)a.k_t, (const T*)a.v_t, (const T*)a.w_t,
+                       a.beta_t, a.logf_t, part, nk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(S), dim3(kCombineThreads), 0, st,
+                       (const float*)part, mch, mch, (const int*)nk, a.H, a.seq_lens,
+                       (T*)a.o_t, a.lse_t);
+    return hipGetLastError();
+}
+
+template <typename K, typename T, int D>
+static hipError_t paged_import_t(const PagedArgs& a, const CacheArgs& c, hipStream_t st) {
+    const int mp = (a.max_keys + (1 << a.lp) - 1) >> a.lp;
+    hipLaunchKernelGGL((paged_import_kernel<K, T, D>), dim3(mp, a.S * a.H), dim3(256), 0, st,
+                       (const K*)c.kcache, (const T*)c.vcache, (const float*)c.gcache, c.cap,
+                       (K*)a.kpages, (T*)a.vpages, a.gpages, a.num_pages, a.lp, a.H, a.tables,
+                       a.table_stride, (const int*)a.seq_lens, a.max_keys);
+    return hipGetLastError();
+}
+
+// dispatch over (key type, value type, d)
+template <template <typename, typename, int> class F, typename... Args>
+static hipError_t paged_dispatch(const PagedArgs& a, Args&&... args) {
+    auto by_d = [&](auto kt, auto vt) -> hipError_t {
+        using K = decltype(kt);
+        using T = decltype(vt);
+        switch (a.d) {
+            case 16: return F<K, T, 16>::run(a, args...);
+            case 32: return F<K, T, 32>::run(a, args...);
+            case 64: return F<K, T, 64>::run(a, args...);
+        }
+        return hipErrorInvalidValue;
+    };
+    if (a.k_bf16) return a.v_bf16 ? by_d(bf16{}, bf16{}) : by_d(bf16{}, float{});
+    return a.v_bf16 ? by_d(float{}, bf16{}) : by_d(float{}, float{});
+}
+template <typename K, typename T, int D>
+struct PagedStep {
+    static hipError_t run(const PagedArgs& a, hipStream_t st) { return paged_step_t<K, T, D>(a, st); }
+};
+template <typename K, typename T, int D>
+struct PagedImport {
+    static hipError_t run(const PagedArgs& a, const CacheArgs& c, hipStream_t st) {
+        return paged_import_t<K, T, D>(a, c, st);
+    }
+};
+
+hipError_t launch_paged_step(const PagedArgs& a, hipStream_t st) {
+    return paged_dispatch<PagedStep>(a, st);
+}
+hipError_t launch_paged_import(const PagedArgs& a, const CacheArgs& c, hipStream_t st) {
+    return paged_dispatch<PagedImport>(a, c, st);
+}
+size_t paged_workspace_bytes(int S, int H, int d, int max_keys) {
+    const size_t mch = (size_t)(max_keys + kDecChunk - 1) / kDecChunk;
+    return (size_t)S * H * (mch * (d + 2) * 4 + 4);
 }
 
 int suffix_groups(int nb) { return (nb + kSufGroup - 1) / kSufGroup; }

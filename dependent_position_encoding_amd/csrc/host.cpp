@@ -372,6 +372,99 @@ path_status path_decode_step(const path_fwd_desc* desc, const path_cache* cache,
                          w_t, beta_t, logf_t, stream, "path_decode_step");
 }
 
+// ---- paged cache
+
+static path_status check_paged(const path_fwd_desc* d, const path_paged_cache* c,
+                               const int* table, int table_stride, const int* seq_lens,
+                               int max_keys, int* lp) {
+    if (!c) return fail(PATH_E_NULL, "paged cache is NULL");
+    if (!c->kpages || !c->vpages) return fail(PATH_E_NULL, "kpages/vpages is NULL");
+    if (!table || !seq_lens) return fail(PATH_E_NULL, "page_table and seq_lens are required");
+    if (!valid_dtype(c->k_dtype)) return fail(PATH_E_DTYPE, "unknown kpages dtype");
+    int l = 0;
+    while (l < 8 && (1 << l) != c->page_size) ++l;
+    if (l < 4 || l > 7) return fail(PATH_E_UNSUPPORTED, "page_size must be 16, 32, 64 or 128");
+    if (c->num_pages < 1) return fail(PATH_E_SHAPE, "num_pages must be >= 1");
+    if ((size_t)c->num_pages * d->H * c->page_size * d->d > ((size_t)1 << 40))
+        return fail(PATH_E_SHAPE, "paged cache too large");
+    if (max_keys < 1) return fail(PATH_E_SHAPE, "max_keys must be >= 1");
+    if (max_keys > pa::decode_max_keys())
+        return fail(PATH_E_UNSUPPORTED, "decode attends over at most 131072 keys per sequence");
+    if (table_stride < (max_keys + c->page_size - 1) / c->page_size)
+        return fail(PATH_E_SHAPE, "table_stride below ceil(max_keys / page_size)");
+    if (!aligned(c->kpages, 16) || !aligned(c->vpages, 16) || !aligned(c->gpages, 4) ||
+        !aligned(table, 4) || !aligned(seq_lens, 4))
+        return fail(PATH_E_ALIGN, "page pointers must be 16-byte aligned (gpages, tables 4)");
+    *lp = l;
+    return PATH_OK;
+}
+
+static pa::PagedArgs paged_args(const path_fwd_desc* d, const path_paged_cache* c,
+                                const int* table, int table_stride, int* seq_lens,
+                                int max_keys, int lp) {
+    pa::PagedArgs a{};
+    a.S = d->N; a.H = d->H; a.d = d->d; a.num_pages = c->num_pages; a.lp = lp;
+    a.table_stride = table_stride; a.max_keys = max_keys;
+    a.k_bf16 = c->k_dtype == PATH_BF16; a.v_bf16 = d->dtype == PATH_BF16;
+    a.scale = d->scale;
+    a.kpages = c->kpages; a.vpages = c->vpages; a.gpages = c->gpages;
+    a.tables = table; a.seq_lens = seq_lens;
+    return a;
+}
+
+size_t path_paged_decode_workspace(const path_fwd_desc* desc, int max_keys) {
+    if (check_desc(desc, false) != PATH_OK || max_keys < 1 || max_keys > pa::decode_max_keys())
+        return 0;
+    return up256(pa::paged_workspace_bytes(desc->N, desc->H, desc->d, max_keys));
+}
+
+path_status path_paged_decode_step(const path_fwd_desc* desc, const path_paged_cache* cache,
+                                   const int* page_table, int table_stride, int* seq_lens,
+                                   int max_keys, const void* q_t, const void* k_t,
+                                   const void* v_t, const void* w_t, const float* beta_t,
+                                   const float* logf_t, void* o_t, float* lse_t, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+    path_status s = check_desc(desc, false);
+    if (s != PATH_OK) return s;
+    int lp = 0;
+    if ((s = check_paged(desc, cache, page_table, table_stride, seq_lens, max_keys, &lp)) != PATH_OK)
+        return s;
+    if (!q_t || !k_t || !v_t || !w_t || !beta_t || !o_t)
+        return fail(PATH_E_NULL, "q_t, k_t, v_t, w_t, beta_t and o_t are required");
+    if (cache->gpages && !logf_t) return fail(PATH_E_NULL, "logf_t is required when gpages is set");
+    if (!aligned(q_t, 16) || !aligned(k_t, 16) || !aligned(v_t, 16) || !aligned(w_t, 16) ||
+        !aligned(o_t, 16) || !aligned(beta_t, 4) || !aligned(logf_t, 4) || !aligned(lse_t, 4))
+        return fail(PATH_E_ALIGN, "q_t, k_t, v_t, w_t and o_t must be 16-byte aligned");
+    if (!ws) return fail(PATH_E_WORKSPACE, "workspace is NULL");
+    if (!aligned(ws, 256)) return fail(PATH_E_ALIGN, "workspace must be 256-byte aligned");
+    if (ws_bytes < path_paged_decode_workspace(desc, max_keys))
+        return fail(PATH_E_WORKSPACE, "workspace smaller than path_paged_decode_workspace()");
+    pa::PagedArgs a = paged_args(desc, cache, page_table, table_stride, seq_lens, max_keys, lp);
+    a.q_t = q_t; a.k_t = k_t; a.v_t = v_t; a.w_t = w_t; a.beta_t = beta_t;
+    a.logf_t = cache->gpages ? logf_t : nullptr;
+    a.o_t = o_t; a.lse_t = lse_t;
+    a.ws = static_cast<float*>(ws);
+    return launched(pa::launch_paged_step(a, stream), "path_paged_decode_step");
+}
+
+path_status path_paged_import(const path_fwd_desc* desc, const path_cache* src,
+                              const path_paged_cache* dst, const int* page_table,
+                              int table_stride, const int* seq_lens, int max_keys,
+                              hipStream_t stream) {
+    path_status s = check_desc(desc, false);
+    if (s != PATH_OK) return s;
+    if ((s = check_cache(desc, src)) != PATH_OK) return s;
+    int lp = 0;
+    if ((s = check_paged(desc, dst, page_table, table_stride, seq_lens, max_keys, &lp)) != PATH_OK)
+        return s;
+    if (src->k_dtype != dst->k_dtype) return fail(PATH_E_DTYPE, "kcache and kpages dtypes differ");
+    if ((src->gcache == nullptr) != (dst->gpages == nullptr))
+        return fail(PATH_E_NULL, "gcache and gpages must be given together");
+    pa::PagedArgs a = paged_args(desc, dst, page_table, table_stride,
+                                 const_cast<int*>(seq_lens), max_keys, lp);
+    return launched(pa::launch_paged_import(a, cache_args(desc, src), stream), "path_paged_import");
+}
+
 path_status path_causal_attn_fwd(const path_fwd_desc* desc, const void* q, const void* k,
                                  const void* v, void* o, float* lse, hipStream_t stream) {
     path_status s = check_desc(desc, true);

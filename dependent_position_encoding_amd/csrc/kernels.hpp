@@ -68,6 +68,25 @@ hipError_t launch_decode(const CacheArgs& c, int n_keys, float scale,
 int decode_chunk(int n_keys);
 int decode_max_keys();   // longest cache one decode call can attend over
 
+// paged cache [page][H][P][d] (P = 1 << lp) for a batch of S sequences
+struct PagedArgs {
+    int S, H, d, num_pages, lp, table_stride, max_keys;
+    bool k_bf16, v_bf16;
+    float scale;
+    void *kpages, *vpages;
+    float* gpages;
+    const int* tables;    // [S][table_stride] page of each P-slot range
+    int* seq_lens;        // [S] keys cached (advanced by one by the step)
+    const void *q_t, *k_t, *v_t, *w_t;
+    const float *beta_t, *logf_t;
+    void* o_t;
+    float* lse_t;
+    float* ws;            // partials [S*H][chunks][d+2], then n_keys [S*H] (int)
+};
+hipError_t launch_paged_step(const PagedArgs& a, hipStream_t st);
+hipError_t launch_paged_import(const PagedArgs& a, const CacheArgs& src, hipStream_t st);
+size_t paged_workspace_bytes(int S, int H, int d, int max_keys);
+
 bool causal_supported(int d, bool bf16);
 hipError_t launch_causal(const FwdArgs& a, hipStream_t st);
 

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define PATH_ATTN_ABI_VERSION 3
+#define PATH_ATTN_ABI_VERSION 4
 
 typedef enum {
     PATH_OK = 0,
@@ -214,6 +214,77 @@ path_status path_decode_step(const path_fwd_desc *desc,
                              const void *w_t, const float *beta_t,
                              const float *logf_t, void *o_t, float *lse_t,
                              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Paged decode cache for a batch of sequences of different lengths
+ * [Notes s2.8; Explainer s3: the in-place key rewrite keeps decoding
+ * compatible with paged caches and FlashDecoding-style split-K kernels].
+ * Keys, values and log-f prefixes of a sequence live in fixed-size pages
+ * taken from one pool; a per-sequence page table maps the slot range
+ * [i*page_size, (i+1)*page_size) to a page.  Within a page the H heads are
+ * separate contiguous [page_size, d] slabs:
+ *   kpages [num_pages, H, page_size, d] in k_dtype (PATH_F32 or PATH_BF16)
+ *   vpages [num_pages, H, page_size, d] in desc->dtype
+ *   gpages [num_pages, H, page_size] float32 inclusive log-f prefixes of the
+ *          sequence (as gcache of path_cache), or NULL (no forget gate).
+ * Slots hold rewritten keys exactly as path_cache does. */
+typedef struct {
+    int num_pages;
+    int page_size;      /* 16, 32, 64 or 128 */
+    path_dtype k_dtype;
+    void *kpages;
+    void *vpages;
+    float *gpages;
+} path_paged_cache;
+
+/* Bytes of workspace path_paged_decode_step needs for desc->N sequences of up
+ * to max_keys keys each (0 if the arguments are invalid). */
+size_t path_paged_decode_workspace(const path_fwd_desc *desc, int max_keys);
+
+/*
+ * One fused decode step for a batch of S = desc->N sequences at their own
+ * positions [Notes s2.8]: for each sequence s with n = seq_lens[s] keys
+ * cached, path_decode_step's work at position t = n (every cached key
+ * rewritten in place by H_t, the token appended at slot n, single-query
+ * attention over slots [0, n]), with the page indirection.
+ *   page_table   : [S, table_stride] int32, device; entry i of row s is the
+ *                  page holding slots [i*page_size, (i+1)*page_size) of s.
+ *   seq_lens     : [S] int32, device; keys cached per sequence on entry,
+ *                  advanced by one on exit (so the same call, or a captured
+ *                  graph of it, serves the next position).
+ *   max_keys     : bound on seq_lens[s] + 1 over the batch (sets the grid);
+ *                  table_stride >= ceil(max_keys / page_size); at most 131072.
+ *   q_t, k_t, v_t, w_t : [S, H, d] desc->dtype; beta_t, logf_t : [S, H]
+ *                  float32 (logf_t may be NULL only if gpages is NULL).
+ *   o_t [S, H, d] desc->dtype, lse_t [S, H] float32 or NULL (written).
+ *   ws           : at least path_paged_decode_workspace(desc, max_keys)
+ *                  bytes, 256-byte aligned; contents need not be initialised.
+ * Split over chunks of 128 keys per (sequence, head), then a combine.
+ * Device-side values are checked where they are read: a sequence whose
+ * seq_lens entry is outside [0, max_keys) is left untouched (seq_lens too)
+ * and gets NaN outputs; a chunk whose page-table entries fall outside
+ * [0, num_pages) touches no cache memory, and its (sequence, head) gets NaN
+ * outputs.  Same conventions as path_decode_step otherwise.
+ */
+path_status path_paged_decode_step(const path_fwd_desc *desc,
+                                   const path_paged_cache *cache,
+                                   const int *page_table, int table_stride,
+                                   int *seq_lens, int max_keys, const void *q_t,
+                                   const void *k_t, const void *v_t,
+                                   const void *w_t, const float *beta_t,
+                                   const float *logf_t, void *o_t, float *lse_t,
+                                   void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Copies slots [0, seq_lens[s]) of each sequence s of a contiguous cache (for
+ * example the one path_attn_fwd aligns a prefill into, desc->N = S
+ * sequences) into its pages, so that paged decoding can continue from a
+ * prefill.  Key dtypes must match, and gcache / gpages be given together.
+ * seq_lens and page_table as for path_paged_decode_step (seq_lens is only
+ * read); sequences with seq_lens[s] outside [0, min(max_keys, src->cap)] and
+ * table entries outside [0, num_pages) are skipped. */
+path_status path_paged_import(const path_fwd_desc *desc, const path_cache *src,
+                              const path_paged_cache *dst, const int *page_table,
+                              int table_stride, const int *seq_lens, int max_keys,
+                              hipStream_t stream);
 
 /* Plain causal softmax attention (every beta = 0, no gate): the in-library
  * baseline the PaTH kernels are timed against.  Same layouts as

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     pa, lib = _lib()
-    assert lib.path_abi_version() == 3
+    assert lib.path_abi_version() == 4
     for s in range(9):
         assert lib.path_status_str(s)
     assert lib.path_status_str(99) == b"unknown status"
@@ -138,3 +138,51 @@ def test_param_argument_errors():
     assert lib.path_param_fwd(*args(good, ws=ctypes.c_void_p((1 << 20) + 64))) == 5
     assert lib.path_param_fwd(*args(good, ws_bytes=ws - 256)) == 6
 
+
+
+def _paged(pa, **kw):
+    base = dict(num_pages=8, page_size=64, k_dtype=pa.PATH_BF16, kpages=FAKE.value,
+                vpages=FAKE.value, gpages=None)
+    base.update(kw)
+    return pa._PagedCache(**base)
+
+
+def _paged_step(pa, lib, d, pc, stride=4, max_keys=256, ws_bytes=1 << 30, ws=FAKE, q=FAKE,
+                logf=None):
+    return lib.path_paged_decode_step(ctypes.byref(d), ctypes.byref(pc) if pc else None, FAKE,
+                                      stride, FAKE, max_keys, q, FAKE, FAKE, FAKE, FAKE, logf,
+                                      FAKE, None, ws, ws_bytes, None)
+
+
+def test_paged_argument_errors():
+    pa, lib = _lib()
+    d = _desc(pa, N=3, H=2)
+    assert _paged_step(pa, lib, d, None) == 1
+    assert _paged_step(pa, lib, d, _paged(pa), q=None) == 1
+    assert _paged_step(pa, lib, d, _paged(pa, gpages=FAKE.value)) == 1     # logf_t missing
+    for ps in (8, 48, 256):
+        assert _paged_step(pa, lib, d, _paged(pa, page_size=ps)) == 4
+    assert _paged_step(pa, lib, d, _paged(pa, num_pages=0)) == 2
+    assert _paged_step(pa, lib, d, _paged(pa, k_dtype=5)) == 3
+    assert _paged_step(pa, lib, d, _paged(pa), max_keys=0) == 2
+    assert _paged_step(pa, lib, d, _paged(pa), max_keys=131073, stride=4096) == 4
+    assert _paged_step(pa, lib, d, _paged(pa), max_keys=257, stride=4) == 2   # 5 pages needed
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert _paged_step(pa, lib, d, _paged(pa, kpages=odd.value)) == 5
+    need = lib.path_paged_decode_workspace(ctypes.byref(d), 256)
+    assert need > 0 and lib.path_paged_decode_workspace(ctypes.byref(d), 0) == 0
+    assert _paged_step(pa, lib, d, _paged(pa), ws_bytes=need - 1) == 6
+    assert _paged_step(pa, lib, d, _paged(pa), ws=None, ws_bytes=need) == 6
+    assert _paged_step(pa, lib, _desc(pa, N=3, H=2, d=48), _paged(pa)) == 4
+    # import: dtype and gate consistency are checked before any launch
+    src = pa._Cache(512, pa.PATH_F32, FAKE.value, FAKE.value, None)
+    st = lib.path_paged_import(ctypes.byref(d), ctypes.byref(src), ctypes.byref(_paged(pa)),
+                               FAKE, 4, FAKE, 256, None)
+    assert st == 3
+    src = pa._Cache(512, pa.PATH_BF16, FAKE.value, FAKE.value, FAKE.value)
+    st = lib.path_paged_import(ctypes.byref(d), ctypes.byref(src), ctypes.byref(_paged(pa)),
+                               FAKE, 4, FAKE, 256, None)
+    assert st == 1
+    st = lib.path_paged_import(ctypes.byref(d), ctypes.byref(src), ctypes.byref(_paged(pa)),
+                               None, 4, FAKE, 256, None)
+    assert st == 1
