@@ -345,6 +345,7 @@ def main():
     out["beta0_baseline"] = causal_baseline(pa, pre, wl, out["prefill"])
     out["front_end"] = front_end_rate(pa, wl, dev)
     out["backward"] = backward_rate(pa, dev)
+    out["paged_decode"] = paged_decode_rate(pa, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, N * (L + T) / (ms_step * 1e-3))
     print(json.dumps(out), flush=True)
@@ -441,6 +442,82 @@ def front_end_rate(pa, wl, dev, R=32, reps=10):
                       "gate": wl.fox},
             "bound": "hbm", "GB_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
             "algorithmic_bytes": alg, "intermediate_bytes": 2 * N * L * rp * 4}
+
+
+def paged_decode_rate(pa, dev, S=32, H=32, d=64, page=64, steps=16, seed=7):
+    """Fused decode steps over a paged cache for a batch of S sequences of
+    mixed lengths (seeded, uniform in [1024, 8192] cached keys), bf16 with the
+    forget gate, pages assigned in a shuffled order.  One captured step
+    (path_paged_decode_step advances the device lengths itself) is replayed
+    `steps` times; the rate uses the algorithmic bytes of every step (read and
+    write each cached key, read each value and gate prefix)."""
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1024, 8193, size=S)
+    max_keys = int(lens.max()) + steps + 1        # one warm step, then `steps`
+    need = (lens + 1 + steps + page - 1) // page  # pages of each final length
+    stride = int(need.max())
+    num_pages = int(need.sum())
+    perm = rng.permutation(num_pages)
+    table = np.zeros((S, stride), dtype=np.int32)
+    at = 0
+    for s in range(S):
+        table[s, :need[s]] = perm[at:at + need[s]]
+        at += need[s]
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    cache = pa.PagedCache(num_pages, page, H, d, dtype=torch.bfloat16, gate=True, device=dev)
+    cache.kpages.copy_(torch.randn(cache.kpages.shape, generator=g, device=dev) * d ** -0.25)
+    cache.vpages.copy_(torch.randn(cache.vpages.shape, generator=g, device=dev))
+    cache.gpages.copy_(-torch.rand(cache.gpages.shape, generator=g, device=dev).cumsum(2) * 0.05)
+    tab = torch.from_numpy(table).to(dev)
+    seq = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    q = torch.randn(S, H, d, generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn(S, H, d, generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn(S, H, d, generator=g, device=dev).to(torch.bfloat16)
+    w = torch.nn.functional.normalize(torch.randn(S, H, d, generator=g, device=dev), dim=-1)
+    w = w.to(torch.bfloat16)
+    beta = 2 * torch.sigmoid(torch.randn(S, H, generator=g, device=dev))
+    logf = torch.nn.functional.logsigmoid(3 + torch.randn(S, H, generator=g, device=dev))
+    o = torch.empty_like(q)
+    lse = torch.empty(S, H, dtype=torch.float32, device=dev)
+    ws = torch.empty(pa.paged_decode_workspace_bytes(S, H, d, torch.bfloat16, max_keys),
+                     dtype=torch.uint8, device=dev)
+
+    def launch():
+        pa.paged_decode_step(cache, tab, seq, max_keys, q, k, v, w, beta, logf,
+                             workspace=ws, out=(o, lse))
+
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        launch()                                  # warm the binding (one real step)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        launch()
+    torch.cuda.synchronize()
+    start = lens + 1                              # cached keys at the first timed step
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    assert seq.cpu().numpy().tolist() == (lens + 1 + steps).tolist()
+    assert torch.isfinite(o.float()).all()
+    per_key = 2 * d * 2 + d * 2 + 4
+    total = sum(float(H * (start + i).sum() * per_key) for i in range(steps))
+    gbs = total / (ms * 1e-3) / 1e9
+    return {"shape": {"sequences": S, "heads": H, "head_dim": d, "page_size": page,
+                      "lengths": "uniform [1024, 8192] (seeded)",
+                      "mean_cached_keys": round(float(start.mean()), 1)},
+            "us_per_step": round(ms / steps * 1e3, 2), "GB_s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "loop": "HIP graph of one step, replayed (device lengths advance)"}
 
 
 def backward_rate(pa, dev, reps=3):

@@ -142,6 +142,9 @@ __global__ void kv_append_kernel(K* __restrict__ kc, T* __restrict__ vc,
 // Rows::off(j) of Rows::k0 and its value row at the same offset of Rows::v0;
 // Rows::g(j) points at its log-f prefix entry (Rows::gate() false: no gate).
 constexpr int kDecChunk = 128;
+// keys per workgroup of the paged step (256, with its doubled registers, is
+// slower at every page size)
+constexpr int kPagedChunk = 128;
 
 // one slice of a contiguous cache [slice][cap][D]
 template <typename K, typename T, int D>
@@ -151,34 +154,38 @@ struct ContigRows {
     float* g0;        // its log-f prefix (NULL: no gate)
     __device__ size_t off(int j) const { return (size_t)j * D; }
     __device__ float* g(int j) const { return g0 + j; }
+    __device__ float prev_prefix(int t) const { return g0[t - 1]; }
     __device__ bool gate() const { return g0 != nullptr; }
 };
 
-// one (sequence, head) of a paged cache [page][H][P][D]: slot j is in page
-// table[j >> lp] at position j & (P - 1)
+// one (sequence, head) of a paged cache [page][H][P][D], seen from one chunk:
+// slot j is in page pages[(j >> lp) - p0] (the chunk's page-table entries,
+// staged in LDS) at position j & (P - 1)
 template <typename K, typename T, int D>
 struct PagedRows {
     K* k0;             // the page pool
     T* v0;
     float* gp;         // log-f pages [page][H][P] (NULL: no gate)
-    const int* table;  // the sequence's page table row
-    int lp, H, h;
+    const int* pages;  // page-table entries p0, p0 + 1, ... of the sequence
+    const float* gprev;  // log-f prefix of slot t - 1, wherever its page is
+    int p0, lp, H, h;
     __device__ size_t slab(int j) const {
-        return ((size_t)table[j >> lp] * H + h) << lp | (size_t)(j & ((1 << lp) - 1));
+        return ((size_t)pages[(j >> lp) - p0] * H + h) << lp | (size_t)(j & ((1 << lp) - 1));
     }
     __device__ size_t off(int j) const { return slab(j) * D; }
     __device__ float* g(int j) const { return gp + slab(j); }
+    __device__ float prev_prefix(int) const { return *gprev; }
     __device__ bool gate() const { return gp != nullptr; }
 };
 
-template <typename K, typename T, int D, bool FUSED, typename Rows>
+template <typename K, typename T, int D, bool FUSED, int CH, typename Rows>
 __device__ inline void chunk_attend(const Rows& rows, int slice, int ch, int n_keys, float scale,
                                     const T* __restrict__ q_t, const T* __restrict__ k_t,
                                     const T* __restrict__ v_t, const T* __restrict__ w_t,
                                     const float* __restrict__ beta_t,
                                     const float* __restrict__ logf_t, float* __restrict__ out) {
     constexpr int VN = Vec<K>::n, TPR = D / VN, GROUPS = 256 / TPR;
-    constexpr int KPG = kDecChunk / GROUPS;      // keys per group
+    constexpr int KPG = CH / GROUPS;             // keys per group
     const int lane_in = threadIdx.x % TPR, grp = threadIdx.x / TPR;
     const int t = n_keys - 1;                     // query position
     const size_t sd = (size_t)slice * D + lane_in * VN;
@@ -193,10 +200,10 @@ __device__ inline void chunk_attend(const Rows& rows, int slice, int ch, int n_k
     const bool gate = rows.gate();
     float ct = 0.f;                               // C_t
     if (gate) {
-        if (FUSED) ct = (t > 0 ? *rows.g(t - 1) : 0.f) + logf_t[slice];
+        if (FUSED) ct = (t > 0 ? rows.prev_prefix(t) : 0.f) + logf_t[slice];
         else ct = *rows.g(t);
     }
-    const int j0 = ch * kDecChunk;
+    const int j0 = ch * CH;
 
     // ---- loads (every key of this group in flight at once)
     Vec<K> kx[KPG];
@@ -307,8 +314,9 @@ decode_chunk_kernel(K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ 
     const int slice = blockIdx.y, ch = blockIdx.x, nch = gridDim.x;
     const ContigRows<K, T, D> rows{kc + (size_t)slice * cap * D, vc + (size_t)slice * cap * D,
                                    gc ? gc + (size_t)slice * cap : nullptr};
-    chunk_attend<K, T, D, FUSED>(rows, slice, ch, n_keys, scale, q_t, k_t, v_t, w_t, beta_t,
-                                 logf_t, part + ((size_t)slice * nch + ch) * (D + 2));
+    chunk_attend<K, T, D, FUSED, kDecChunk>(rows, slice, ch, n_keys, scale, q_t, k_t, v_t, w_t,
+                                            beta_t, logf_t,
+                                            part + ((size_t)slice * nch + ch) * (D + 2));
 }
 
 // Paged cache, one fused step for a batch of sequences of their own lengths
@@ -316,9 +324,10 @@ decode_chunk_kernel(K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ 
 // Sequence s has n_keys = seq_lens[s] + 1 keys (the new token at slot
 // seq_lens[s]); chunks past its end exit at once.  The chunk-0 workgroup
 // records n_keys (or -1 when seq_lens[s] is out of [0, max_keys)) in nk[slice]
-// for the combine.  A chunk whose page-table entries fall outside
-// [0, num_pages) touches no cache memory and leaves m = +inf, which makes the
-// combine's result NaN for that (sequence, head).
+// for the combine.  A chunk that reaches a page-table entry outside
+// [0, num_pages) (its own pages, or with the gate the page of slot t - 1)
+// touches no cache memory and leaves m = +inf, which makes the combine's
+// result NaN for that (sequence, head).
 template <typename K, typename T, int D>
 __global__ void __launch_bounds__(256)
 paged_chunk_kernel(K* __restrict__ kp, T* __restrict__ vp, float* __restrict__ gp,
@@ -334,20 +343,40 @@ paged_chunk_kernel(K* __restrict__ kp, T* __restrict__ vp, float* __restrict__ g
     const bool ok = len >= 0 && len < max_keys;
     const int n_keys = len + 1;
     if (ch == 0 && threadIdx.x == 0) nk[slice] = ok ? n_keys : -1;
-    if (!ok || ch * kDecChunk >= n_keys) return;
+    if (!ok || ch * kPagedChunk >= n_keys) return;
     const int* table = tables + (size_t)s * table_stride;
     float* out = part + ((size_t)slice * nch + ch) * (D + 2);
-    // every page this chunk reaches must exist
-    const int p0 = (ch * kDecChunk) >> lp, p1 = (min(n_keys, (ch + 1) * kDecChunk) - 1) >> lp;
-    bool pages_ok = true;
-    for (int p = p0; p <= p1; ++p) pages_ok = pages_ok && (unsigned)table[p] < (unsigned)num_pages;
-    if (!pages_ok) {
+    // The chunk's page-table entries into LDS, each checked against the pool
+    // (one lane per page); the key rows then read their page from LDS.  With
+    // the gate, every chunk also reads the log-f prefix of slot t - 1 (the
+    // new token's prefix continues it), whose page is loaded and checked on
+    // its own: it need not be one of this chunk's pages.
+    __shared__ int sPage[kPagedChunk / 16];
+    __shared__ int sBad, sPrev;
+    const int p0 = (ch * kPagedChunk) >> lp, p1 = (min(n_keys, (ch + 1) * kPagedChunk) - 1) >> lp;
+    const int tp = n_keys - 2;                    // slot t - 1
+    if (threadIdx.x == 0) {
+        int prev = 0;
+        if (gp && tp >= 0) prev = table[tp >> lp];
+        sPrev = prev;
+        sBad = (unsigned)prev >= (unsigned)num_pages;
+    }
+    __syncthreads();
+    if (threadIdx.x <= p1 - p0) {
+        const int pg = table[p0 + threadIdx.x];
+        sPage[threadIdx.x] = pg;
+        if ((unsigned)pg >= (unsigned)num_pages) sBad = 1;
+    }
+    __syncthreads();
+    if (sBad) {
         if (threadIdx.x < D + 2) out[threadIdx.x] = threadIdx.x == 0 ? INFINITY : 0.f;
         return;
     }
-    const PagedRows<K, T, D> rows{kp, vp, gp, table, lp, H, h};
-    chunk_attend<K, T, D, true>(rows, slice, ch, n_keys, scale, q_t, k_t, v_t, w_t, beta_t,
-                                logf_t, out);
+    const float* gprev = gp && tp >= 0
+        ? gp + ((((size_t)sPrev * H + h) << lp) | (size_t)(tp & ((1 << lp) - 1))) : nullptr;
+    const PagedRows<K, T, D> rows{kp, vp, gp, sPage, gprev, p0, lp, H, h};
+    chunk_attend<K, T, D, true, kPagedChunk>(rows, slice, ch, n_keys, scale, q_t, k_t, v_t,
+                                             w_t, beta_t, logf_t, out);
 }
 
 // Merge the chunk partials of one slice: o = sum acc_c e^{m_c - M} / l,
@@ -364,7 +393,7 @@ constexpr int kCombineThreads = 1024;
 
 template <typename T, int D>
 __global__ void __launch_bounds__(kCombineThreads)
-decode_combine_kernel(const float* __restrict__ part, int nch, int pstride,
+decode_combine_kernel(const float* __restrict__ part, int nch, int pstride, int chunk,
                       const int* __restrict__ nk, int H, int* __restrict__ seq_lens,
                       T* __restrict__ o_t, float* __restrict__ lse_t) {
     constexpr int NTH = kCombineThreads, NW = NTH / 64, G = NTH / D;
@@ -379,7 +408,7 @@ decode_combine_kernel(const float* __restrict__ part, int nch, int pstride,
             if (tid == 0 && lse_t) lse_t[slice] = NAN;
             return;
         }
-        nch = (n + kDecChunk - 1) / kDecChunk;
+        nch = (n + chunk - 1) / chunk;
         if (tid == 0 && seq_lens && slice % H == 0) seq_lens[slice / H] = n;
     }
     const float* p = part + (size_t)slice * pstride * (D + 2);
@@ -783,7 +812,8 @@ static hipError_t decode_t(const CacheArgs& c, int n_keys, float scale, const vo
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(c.N * c.H), dim3(kCombineThreads), 0, st,
-                       (const float*)part, nch, nch, nullptr, c.H, nullptr, (T*)o_t, lse_t);
+                       (const float*)part, nch, nch, kDecChunk, nullptr, c.H, nullptr, (T*)o_t,
+                       lse_t);
     return hipGetLastError();
 }
 
@@ -849,7 +879,7 @@ paged_import_kernel(const K* __restrict__ kc, const T* __restrict__ vc,
 
 template <typename K, typename T, int D>
 static hipError_t paged_step_t(const PagedArgs& a, hipStream_t st) {
-    const int mch = (a.max_keys + kDecChunk - 1) / kDecChunk;
+    const int mch = (a.max_keys + kPagedChunk - 1) / kPagedChunk;
     const int S = a.S * a.H;
     float* part = a.ws;
     int* nk = reinterpret_cast<int*>(a.ws + (size_t)S * mch * (D + 2));
@@ -861,7 +891,7 @@ static hipError_t paged_step_t(const PagedArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(S), dim3(kCombineThreads), 0, st,
-                       (const float*)part, mch, mch, (const int*)nk, a.H, a.seq_lens,
+                       (const float*)part, mch, mch, kPagedChunk, (const int*)nk, a.H, a.seq_lens,
                        (T*)a.o_t, a.lse_t);
     return hipGetLastError();
 }
@@ -910,7 +940,7 @@ hipError_t launch_paged_import(const PagedArgs& a, const CacheArgs& c, hipStream
     return paged_dispatch<PagedImport>(a, c, st);
 }
 size_t paged_workspace_bytes(int S, int H, int d, int max_keys) {
-    const size_t mch = (size_t)(max_keys + kDecChunk - 1) / kDecChunk;
+    const size_t mch = (size_t)(max_keys + kPagedChunk - 1) / kPagedChunk;
     return (size_t)S * H * (mch * (d + 2) * 4 + 4);
 }
 

@@ -261,9 +261,11 @@ size_t path_paged_decode_workspace(const path_fwd_desc *desc, int max_keys);
  * Split over chunks of 128 keys per (sequence, head), then a combine.
  * Device-side values are checked where they are read: a sequence whose
  * seq_lens entry is outside [0, max_keys) is left untouched (seq_lens too)
- * and gets NaN outputs; a chunk whose page-table entries fall outside
- * [0, num_pages) touches no cache memory, and its (sequence, head) gets NaN
- * outputs.  Same conventions as path_decode_step otherwise.
+ * and gets NaN outputs; a chunk of 128 keys that reaches a page-table entry
+ * outside [0, num_pages) (one of its own pages or, with the gate, the page of
+ * slot n - 1) touches no cache memory, and its (sequence, head) gets NaN
+ * outputs while seq_lens still advances.  Same conventions as
+ * path_decode_step otherwise.
  */
 path_status path_paged_decode_step(const path_fwd_desc *desc,
                                    const path_paged_cache *cache,

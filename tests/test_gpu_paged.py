@@ -176,22 +176,26 @@ def test_paged_matches_contiguous_step_bitwise():
 def test_paged_bad_entries_give_nan_without_touching_others():
     pa = _pa()
     wl = workloads.CONFIGS["fox"].replace(H=2)
-    b = Batch(wl, [100, 200, 50], steps=1, page_size=64, k_dtype=torch.bfloat16, seed=9)
+    b = Batch(wl, [100, 200, 50, 128], steps=1, page_size=64, k_dtype=torch.bfloat16, seed=9)
     keys_before = b.cache.kpages.clone()
     # sequence 1: its second page entry points past the pool; sequence 2: a
-    # length beyond max_keys
+    # length beyond max_keys; sequence 3: the page of slot t - 1 (whose gate
+    # prefix every chunk reads; the new token at t = 128 opens the next page)
+    # is negative
     b.table[1, 1] = b.cache.num_pages + 3
     b.seq_lens[2] = b.max_keys
+    b.table[3, 1] = -2
     o, lse = b.step(0)
     torch.cuda.synchronize()
-    assert torch.isnan(o[1]).all() and torch.isnan(lse[1]).all()
-    assert torch.isnan(o[2]).all() and torch.isnan(lse[2]).all()
+    for s in (1, 2, 3):
+        assert torch.isnan(o[s]).all() and torch.isnan(lse[s]).all(), s
     assert torch.isfinite(o[0]).all() and torch.isfinite(lse[0]).all()
-    assert b.seq_lens.cpu().tolist() == [101, 201, b.max_keys]
-    # sequence 2 wrote nothing; sequence 0 is right
-    t2 = b.table_np[2]
-    for p in t2[t2 >= 0]:
-        assert torch.equal(b.cache.kpages[int(p)], keys_before[int(p)])
+    assert b.seq_lens.cpu().tolist() == [101, 201, b.max_keys, 129]
+    # sequences 2 and 3 wrote nothing; sequence 0 is right
+    for s in (2, 3):
+        ts = b.table_np[s]
+        for p in ts[ts >= 0]:
+            assert torch.equal(b.cache.kpages[int(p)], keys_before[int(p)]), s
     f64 = {k: (workloads.as_slices_f64(v) if v is not None else None) for k, v in b.x[0].items()}
     ro, rl = oracle.fwd_rows(f64["q"], f64["k"], f64["v"], f64["w"], f64["beta"], f64["logf"],
                              wl.scale, rows=[100])
