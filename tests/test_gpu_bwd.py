@@ -109,3 +109,33 @@ def test_bwd_bf16_many_blocks():
     # 16 blocks: long transition chains through the scan's backward
     wl = workloads.CONFIGS["fox"].replace(N=1, H=2)
     _run(wl, L=1024, seed=2)
+
+
+def test_bwd_bf16_full_lm_shape_sampled_slices():
+    """The LM-layer training shape the benchmark times (4 x 24 heads, L =
+    4096, d = 64, bf16), in its launch configuration (the slices split into
+    two groups over the pair buffers); the gradients of slices in both groups
+    and at the edges against the oracle, slice by slice."""
+    pa = _pa()
+    wl = workloads.CONFIGS["lm"]
+    x = workloads.make_inputs(wl, device=DEV, variant=3)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(77)
+    do = torch.randn(x["q"].shape, generator=gen, device=DEV).to(wl.dtype)
+    print(f"case bwd full lm {tuple(x['q'].shape)}", flush=True)
+    o, lse = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], logf=None, scale=wl.scale)
+    grads = pa.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], None, o, lse, do, scale=wl.scale)
+    torch.cuda.synchronize()
+    nsl = wl.N * wl.H
+    for s in (0, nsl // 2, nsl - 1):
+        f64 = {k: (workloads.as_slices_f64(v, heads=[s]) if v is not None else None)
+               for k, v in x.items()}
+        ref = oracle.bwd(f64["q"], f64["k"], f64["v"], f64["w"], f64["beta"], None, wl.scale,
+                         workloads.as_slices_f64(do, heads=[s]))
+        for name, got in zip(NAMES, grads):
+            if ref[name] is None:
+                continue
+            ma, mr, gmax = _errs(workloads.as_slices_f64(got, heads=[s]), ref[name])
+            msg = f"  slice {s} {name}: max-err/g_max {ma:.2e} mean-rel {mr:.2e} (g_max {gmax:.3g})"
+            print(msg, flush=True)
+            assert ma <= 2e-2 and mr <= 1e-2, msg
