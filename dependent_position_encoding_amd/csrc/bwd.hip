@@ -1349,6 +1349,294 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     if (tid < kB) rowsum[blk_b * kB + tid] = sRow[tid];
 }
 
+// ---------------------------------------------------------------------------
+// precond_bwd for bf16 inputs at d in {32, 64}: the same products as
+// bwd_precond_kernel, every operand and intermediate held in LDS as one bf16
+// part (the precision the pair kernels work in), so no product waits on a
+// round trip to global memory.  One 512-thread workgroup per block; its two
+// four-wave halves run independent products side by side.  Seventeen tile
+// slots of 64 x 72 bf16 hold the live matrices; a slot is reused once its
+// matrix is dead, and the fp32 G of the UT solve and the fp32 dG for the
+// symmetric weight each take two adjacent free slots.
+constexpr int kLT = 72;                        // row stride of a slot (bf16)
+constexpr int kSlot = kB * kLT;                // elements per slot
+constexpr int kSlots = 17;
+
+// fragment of a slot-resident bf16 matrix: 8 consecutive contraction indices
+// of operand row i, read along a row (C) or down a column (S)
+__device__ inline bf16x8 fragC(const __bf16* t, int i, int k0) {
+    return *reinterpret_cast<const bf16x8*>(t + i * kLT + k0);
+}
+__device__ inline bf16x8 fragS(const __bf16* t, int i, int k0) {
+    bf16x8 x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = t[(k0 + e) * kLT + i];
+    return x;
+}
+// One 32 x 32 tile of sum_k A(m0 + ., k) B(n0 + ., k); SA / SB: the operand is
+// read down the stored matrix's columns (the product contracts its rows).
+template <bool SA, bool SB, int K>
+__device__ inline f32x16 tprod(const __bf16* A, const __bf16* B, int m0, int n0, f32x16 c) {
+    const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        const bf16x8 a = SA ? fragS(A, m0 + r, k0 + 8 * h) : fragC(A, m0 + r, k0 + 8 * h);
+        const bf16x8 b = SB ? fragS(B, n0 + r, k0 + 8 * h) : fragC(B, n0 + r, k0 + 8 * h);
+        c = mfma32(a, b, c);
+    }
+    return c;
+}
+// The output tiles of an M x N product dealt to the four waves of half g
+// (waves 4g .. 4g+3); the wave's own tile index, or -1
+__device__ inline int half_tile(int g, int M, int N, int k) {
+    const int wave = threadIdx.x >> 6;
+    if ((wave >> 2) != g) return -1;
+    const int t = (wave & 3) + 4 * k;
+    return t < (M / 32) * (N / 32) ? t : -1;
+}
+// element visitor of a tile in the matrix-core C layout
+template <typename F>
+__device__ inline void for_tile(int t, int N, const f32x16& c, F f) {
+    const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+    const int m0 = (t / (N / 32)) * 32, n0 = (t % (N / 32)) * 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f(m0 + 8 * i + 4 * h + j, n0 + r, c[4 * i + j]);
+}
+// C = A B (as tprod) over all output tiles, on half g, written through f
+template <bool SA, bool SB, int K, typename F>
+__device__ inline void hprod(int g, int M, int N, const __bf16* A, const __bf16* B, F f) {
+    for (int k = 0;; ++k) {
+        const int t = half_tile(g, M, N, k);
+        if (t < 0) return;
+        const int m0 = (t / (N / 32)) * 32, n0 = (t % (N / 32)) * 32;
+        for_tile(t, N, tprod<SA, SB, K>(A, B, m0, n0, zero16()), f);
+    }
+}
+__device__ inline void put_bf(__bf16* t, int m, int n, float v) { t[m * kLT + n] = (__bf16)v; }
+
+template <int D>
+__global__ void __launch_bounds__(512)
+bwd_precond_b16_kernel(int L, int nb, int slice0, const bf16* __restrict__ q,
+                       const bf16* __restrict__ k, const bf16* __restrict__ w,
+                       const float* __restrict__ beta, const float* __restrict__ dQl,
+                       const float* __restrict__ dKr, const float* __restrict__ dEm,
+                       const float* __restrict__ dDg, bf16* __restrict__ dq,
+                       bf16* __restrict__ dk, bf16* __restrict__ dw,
+                       float* __restrict__ dbeta) {
+    static_assert(D == 32 || D == 64, "bf16 tiles");
+    __shared__ __attribute__((aligned(16))) __bf16 sl[kSlots * kSlot];
+    __shared__ float sBeta[kB], sdB[kB];
+    const int tid = threadIdx.x;
+    const int c = (int)(blockIdx.x % nb), sli = (int)(blockIdx.x / nb);
+    const size_t slice = (size_t)slice0 + sli, blk = slice * nb + c, base = slice * L;
+    auto S = [&](int i) { return sl + i * kSlot; };
+    // slot map (a slot is reused once its matrix is dead)
+    __bf16 *sW = S(0), *sQ = S(1), *sK = S(2), *sDg = S(3), *sDq = S(4), *sDk = S(5),
+           *sDe = S(6), *sX = S(7), *sM = S(8), *sDr = S(9), *sT = S(10), *sU = S(11),
+           *sDy = S(12), *sDp = S(13), *sDm = S(14), *sP = S(15), *sR = S(16);
+    __bf16 *sY = S(15), *sDx = S(16), *sDt = S(4), *sTmp = S(5), *sAA = S(6);
+    float* fG = reinterpret_cast<float*>(S(15));   // slots 15-16, phases 1-3
+    float* fdG = reinterpret_cast<float*>(S(7));   // slots 7-8, phases 9-10
+    static_assert(kB * kLdB * 4 <= 2 * kSlot * 2, "fp32 matrix in two slots");
+    const float* dql = dQl + blk * kB * D;
+    const float* dkr = dKr + blk * kB * D;
+    const float* dem = dEm + blk * D * D;
+    const float* ddg = dDg + blk * kB * kB;
+
+    // ---- 0. inputs: q, k, w (exact), the incoming gradients rounded to bf16
+    for (int e = tid; e < kB * D / 8; e += 512) {
+        const int r = e / (D / 8), x0 = 8 * (e % (D / 8)), pos = c * kB + r;
+        u32x4 uq = {0u, 0u, 0u, 0u}, uk = uq, uw = uq;
+        if (pos < L) {
+            const size_t gi = (base + pos) * D + x0;
+            uq = *reinterpret_cast<const u32x4*>(q + gi);
+            uk = *reinterpret_cast<const u32x4*>(k + gi);
+            uw = *reinterpret_cast<const u32x4*>(w + gi);
+        }
+        *reinterpret_cast<u32x4*>(sQ + r * kLT + x0) = uq;
+        *reinterpret_cast<u32x4*>(sK + r * kLT + x0) = uk;
+        *reinterpret_cast<u32x4*>(sW + r * kLT + x0) = uw;
+    }
+    auto stage = [&](__bf16* dst, const float* src, int rows, int cols) {
+        for (int e = tid; e < rows * cols / 4; e += 512) {
+            const int r = e / (cols / 4), x0 = 4 * (e % (cols / 4));
+            const f32x4 v = *reinterpret_cast<const f32x4*>(src + (size_t)r * cols + x0);
+            *reinterpret_cast<bf16x4_t*>(dst + r * kLT + x0) =
+                bf16x4_t{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        }
+    };
+    stage(sDq, dql, kB, D);
+    stage(sDk, dkr, kB, D);
+    stage(sDe, dem, D, D);
+    stage(sDg, ddg, kB, kB);
+    if (tid < kB) {
+        const int pos = c * kB + tid;
+        sBeta[tid] = pos < L ? beta[base + pos] : 0.f;
+        sdB[tid] = 0.f;
+    }
+    __syncthreads();
+
+    // ---- 1. G = diag(beta) strictLower(W W^T) (fp32, for the solve) | X = lower(Q W^T)
+    hprod<false, false, D>(0, kB, kB, sW, sW, [&](int m, int n, float v) {
+        fG[m * kLdB + n] = n < m ? sBeta[m] * v : 0.f;
+    });
+    hprod<false, false, D>(1, kB, kB, sQ, sW,
+                           [&](int m, int n, float v) { put_bf(sX, m, n, n <= m ? v : 0.f); });
+    __syncthreads();
+    // ---- 2. M = strictLower(W K^T) | dR = -W dKr^T
+    hprod<false, false, D>(0, kB, kB, sW, sK,
+                           [&](int m, int n, float v) { put_bf(sM, m, n, n < m ? v : 0.f); });
+    hprod<false, false, D>(1, kB, kB, sW, sDk, [&](int m, int n, float v) { put_bf(sDr, m, n, -v); });
+    __syncthreads();
+    // ---- 3. T = (I + G)^{-1} and U = T diag(beta), a column per lane of wave 0
+    //         (uniform unrolled substitution, G read as LDS broadcasts) |
+    //         dY = W dE, dP = -dQl W^T - dDg M^T
+    if (tid < kB) {
+        const int j = tid;
+        float t[kB];
+#pragma unroll
+        for (int i = 0; i < kB; ++i) {
+            float acc = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < i; ++kk) acc -= fG[i * kLdB + kk] * t[kk];
+            t[i] = i == j ? 1.f : (i < j ? 0.f : acc);
+        }
+        const float bj = sBeta[j];
+#pragma unroll
+        for (int i = 0; i < kB; ++i) {
+            put_bf(sT, i, j, t[i]);
+            put_bf(sU, i, j, t[i] * bj);
+        }
+    }
+    hprod<false, true, D>(1, kB, D, sW, sDe, [&](int m, int n, float v) { put_bf(sDy, m, n, v); });
+    for (int kq = 0;; ++kq) {
+        const int t = half_tile(1, kB, kB, kq);
+        if (t < 0) break;
+        const int m0 = (t / 2) * 32, n0 = (t % 2) * 32;
+        f32x16 acc = tprod<false, false, D>(sDq, sW, m0, n0, zero16());
+        acc = tprod<false, false, kB>(sDg, sM, m0, n0, acc);
+        for_tile(t, kB, acc, [&](int m, int n, float v) { put_bf(sDp, m, n, -v); });
+    }
+    __syncthreads();
+    // ---- 4. P = X U | R = U M
+    hprod<false, true, kB>(0, kB, kB, sX, sU, [&](int m, int n, float v) { put_bf(sP, m, n, v); });
+    hprod<false, true, kB>(1, kB, kB, sU, sM, [&](int m, int n, float v) { put_bf(sR, m, n, v); });
+    __syncthreads();
+    // ---- 5. dW accumulators (half 0, a tile per wave): -P^T dQl - R dKr |
+    //         dM = strictLower(-P^T dDg + U^T dR)
+    const int wt = half_tile(0, kB, D, 0);          // this wave's dW tile (half 0)
+    const int wm0 = wt >= 0 ? (wt / (D / 32)) * 32 : 0, wn0 = wt >= 0 ? (wt % (D / 32)) * 32 : 0;
+    f32x16 aW = zero16();
+    if (wt >= 0) {
+        aW = tprod<true, true, kB>(sP, sDq, wm0, wn0, aW);
+        aW = tprod<false, true, kB>(sR, sDk, wm0, wn0, aW);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) aW[e] = -aW[e];
+    }
+    for (int kq = 0;; ++kq) {
+        const int t = half_tile(1, kB, kB, kq);
+        if (t < 0) break;
+        const int m0 = (t / 2) * 32, n0 = (t % 2) * 32;
+        f32x16 acc = tprod<true, true, kB>(sP, sDg, m0, n0, zero16());
+        f32x16 acc2 = tprod<true, true, kB>(sU, sDr, m0, n0, zero16());
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = acc2[e] - acc[e];
+        for_tile(t, kB, acc, [&](int m, int n, float v) { put_bf(sDm, m, n, n < m ? v : 0.f); });
+    }
+    __syncthreads();
+    // ---- 6. Y = U^T W | dX = lower(dP U^T)
+    hprod<true, true, kB>(0, kB, D, sU, sW, [&](int m, int n, float v) { put_bf(sY, m, n, v); });
+    hprod<false, false, kB>(1, kB, kB, sDp, sU,
+                            [&](int m, int n, float v) { put_bf(sDx, m, n, n <= m ? v : 0.f); });
+    __syncthreads();
+    // ---- 7. dW += Y dE^T + U dY |
+    //         dU = lower(X^T dP + dR M^T + W dY^T) -> dT = dU diag(beta), and
+    //         U = T diag(beta) gives dbeta_n += sum_m T_mn dU_mn
+    if (wt >= 0) {
+        aW = tprod<false, false, D>(sY, sDe, wm0, wn0, aW);
+        aW = tprod<false, true, kB>(sU, sDy, wm0, wn0, aW);
+    }
+    for (int kq = 0;; ++kq) {
+        const int t = half_tile(1, kB, kB, kq);
+        if (t < 0) break;
+        const int m0 = (t / 2) * 32, n0 = (t % 2) * 32;
+        f32x16 acc = tprod<true, true, kB>(sX, sDp, m0, n0, zero16());
+        acc = tprod<false, false, kB>(sDr, sM, m0, n0, acc);
+        acc = tprod<false, false, D>(sW, sDy, m0, n0, acc);
+        for_tile(t, kB, acc, [&](int m, int n, float v) {
+            const float du = n <= m ? v : 0.f;
+            put_bf(sDt, m, n, du * sBeta[n]);
+            if (n <= m) atomicAdd(&sdB[n], (float)sT[m * kLT + n] * du);
+        });
+    }
+    __syncthreads();
+    // ---- 8. Tmp = dT T^T | dQ, dK accumulators (half 1, a tile of each per
+    //         wave): dDg K, dDg^T Q
+    const int qt = half_tile(1, kB, D, 0);
+    const int qm0 = qt >= 0 ? (qt / (D / 32)) * 32 : 0, qn0 = qt >= 0 ? (qt % (D / 32)) * 32 : 0;
+    f32x16 aQ = zero16(), aK = zero16();
+    hprod<false, false, kB>(0, kB, kB, sDt, sT, [&](int m, int n, float v) { put_bf(sTmp, m, n, v); });
+    if (qt >= 0) {
+        aQ = tprod<false, true, kB>(sDg, sK, qm0, qn0, aQ);
+        aK = tprod<true, true, kB>(sDg, sQ, qm0, qn0, aK);
+    }
+    __syncthreads();
+    // ---- 9. dG = strictLower(-T^T Tmp) (fp32), with G_mn = beta_m (W W^T)_mn
+    //         giving dbeta_m += sum_n dG_mn (W W^T)_mn | dQ += dX W, dK += dM^T W
+    for (int kq = 0;; ++kq) {
+        const int t = half_tile(0, kB, kB, kq);
+        if (t < 0) break;
+        const int m0 = (t / 2) * 32, n0 = (t % 2) * 32;
+        const f32x16 g = tprod<true, true, kB>(sT, sTmp, m0, n0, zero16());
+        const f32x16 ww = tprod<false, false, D>(sW, sW, m0, n0, zero16());
+        f32x16 dgv;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dgv[e] = -g[e];
+        int e = 0;
+        for_tile(t, kB, dgv, [&](int m, int n, float v) {
+            const float dg = n < m ? v : 0.f;
+            fdG[m * kLdB + n] = dg;
+            if (n < m) atomicAdd(&sdB[m], dg * ww[e]);
+            ++e;
+        });
+    }
+    if (qt >= 0) {
+        aQ = tprod<false, true, kB>(sDx, sW, qm0, qn0, aQ);
+        aK = tprod<true, true, kB>(sDm, sW, qm0, qn0, aK);
+    }
+    __syncthreads();
+    // ---- 10. the symmetric weight A + A^T, A = diag(beta) dG, of dW's last term
+    for (int e = tid; e < kB * kB; e += 512) {
+        const int m = e / kB, n = e % kB;
+        put_bf(sAA, m, n, sBeta[m] * fdG[m * kLdB + n] + sBeta[n] * fdG[n * kLdB + m]);
+    }
+    __syncthreads();
+    // ---- 11. dW += dX^T Q + dM K + (A + A^T) W; then every output
+    if (wt >= 0) {
+        aW = tprod<true, true, kB>(sDx, sQ, wm0, wn0, aW);
+        aW = tprod<false, true, kB>(sDm, sK, wm0, wn0, aW);
+        aW = tprod<false, true, kB>(sAA, sW, wm0, wn0, aW);
+        for_tile(wt, D, aW, [&](int m, int n, float v) {
+            const int pos = c * kB + m;
+            if (pos < L) dw[(base + pos) * D + n] = from_f32<bf16>(v);
+        });
+    }
+    if (qt >= 0) {
+        for_tile(qt, D, aQ, [&](int m, int n, float v) {
+            const int pos = c * kB + m;
+            if (pos < L) dq[(base + pos) * D + n] = from_f32<bf16>(v + dql[m * D + n]);
+        });
+        for_tile(qt, D, aK, [&](int m, int n, float v) {
+            const int pos = c * kB + m;
+            if (pos < L) dk[(base + pos) * D + n] = from_f32<bf16>(v + dkr[m * D + n]);
+        });
+    }
+    __syncthreads();
+    if (tid < kB && c * kB + tid < L) dbeta[base + c * kB + tid] = sdB[tid];
+}
+
 template <typename T, int D, int PARTS>
 hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
     const int nb = (a.L + kB - 1) / kB, ns = a.N * a.H;
@@ -1399,10 +1687,17 @@ hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
                                a.lse, a.delta, a.fw, a.X, a.Z, a.dKr, a.dEm, (T*)a.dv, a.colsum);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        hipLaunchKernelGGL((bwd_precond_kernel<T, D, PARTS>), dim3(nsc * nb), dim3(256), 0, st,
-                           a.L, nb, s0, (const T*)a.q, (const T*)a.k, (const T*)a.w, a.beta,
-                           a.dQl, a.dKr, a.dEm, a.dDg, a.scr, (T*)a.dq, (T*)a.dk, (T*)a.dw,
-                           a.dbeta);
+        if constexpr (sizeof(T) == 2 && D >= 32) {
+            hipLaunchKernelGGL((bwd_precond_b16_kernel<D>), dim3(nsc * nb), dim3(512), 0, st,
+                               a.L, nb, s0, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.w,
+                               a.beta, a.dQl, a.dKr, a.dEm, a.dDg, (bf16*)a.dq, (bf16*)a.dk,
+                               (bf16*)a.dw, a.dbeta);
+        } else {
+            hipLaunchKernelGGL((bwd_precond_kernel<T, D, PARTS>), dim3(nsc * nb), dim3(256), 0,
+                               st, a.L, nb, s0, (const T*)a.q, (const T*)a.k, (const T*)a.w,
+                               a.beta, a.dQl, a.dKr, a.dEm, a.dDg, a.scr, (T*)a.dq, (T*)a.dk,
+                               (T*)a.dw, a.dbeta);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (fox) {
