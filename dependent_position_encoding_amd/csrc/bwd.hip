@@ -1492,7 +1492,7 @@ bwd_precond_b16_kernel(int L, int nb, int slice0, const bf16* __restrict__ q,
     __syncthreads();
     // ---- 3. T = (I + G)^{-1} and U = T diag(beta), a column per lane of wave 0
     //         (uniform unrolled substitution, G read as LDS broadcasts) |
-    //         dY = W dE, dP = -dQl W^T - dDg M^T
+    //         dY = W dE, dP = -dQl W^T - dDg M^T, dQ += dDg K, dK += dDg^T Q
     if (tid < kB) {
         const int j = tid;
         float t[kB];
@@ -1518,6 +1518,15 @@ bwd_precond_b16_kernel(int L, int nb, int slice0, const bf16* __restrict__ q,
         f32x16 acc = tprod<false, false, D>(sDq, sW, m0, n0, zero16());
         acc = tprod<false, false, kB>(sDg, sM, m0, n0, acc);
         for_tile(t, kB, acc, [&](int m, int n, float v) { put_bf(sDp, m, n, -v); });
+    }
+    // dQ, dK accumulators (half 1, a tile of each per wave), their input-only
+    // terms while the solve runs: dDg K, dDg^T Q
+    const int qt = half_tile(1, kB, D, 0);
+    const int qm0 = qt >= 0 ? (qt / (D / 32)) * 32 : 0, qn0 = qt >= 0 ? (qt % (D / 32)) * 32 : 0;
+    f32x16 aQ = zero16(), aK = zero16();
+    if (qt >= 0) {
+        aQ = tprod<false, true, kB>(sDg, sK, qm0, qn0, aQ);
+        aK = tprod<true, true, kB>(sDg, sQ, qm0, qn0, aK);
     }
     __syncthreads();
     // ---- 4. P = X U | R = U M
@@ -1572,16 +1581,8 @@ bwd_precond_b16_kernel(int L, int nb, int slice0, const bf16* __restrict__ q,
         });
     }
     __syncthreads();
-    // ---- 8. Tmp = dT T^T | dQ, dK accumulators (half 1, a tile of each per
-    //         wave): dDg K, dDg^T Q
-    const int qt = half_tile(1, kB, D, 0);
-    const int qm0 = qt >= 0 ? (qt / (D / 32)) * 32 : 0, qn0 = qt >= 0 ? (qt % (D / 32)) * 32 : 0;
-    f32x16 aQ = zero16(), aK = zero16();
+    // ---- 8. Tmp = dT T^T
     hprod<false, false, kB>(0, kB, kB, sDt, sT, [&](int m, int n, float v) { put_bf(sTmp, m, n, v); });
-    if (qt >= 0) {
-        aQ = tprod<false, true, kB>(sDg, sK, qm0, qn0, aQ);
-        aK = tprod<true, true, kB>(sDg, sQ, qm0, qn0, aK);
-    }
     __syncthreads();
     // ---- 9. dG = strictLower(-T^T Tmp) (fp32), with G_mn = beta_m (W W^T)_mn
     //         giving dbeta_m += sum_n dG_mn (W W^T)_mn | dQ += dX W, dK += dM^T W
