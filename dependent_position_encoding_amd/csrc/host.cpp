@@ -133,7 +133,13 @@ struct BwdLayout {
 BwdLayout bwd_layout(const path_fwd_desc* d) {
     const int B = pa::bwd_block(), D = d->d;
     const size_t nb = (size_t)(d->L + B - 1) / B, ns = (size_t)d->N * d->H, nblk = ns * nb;
-    const size_t per_slice = 4 * (2 * pa::bwd_pair_floats(d->L, D, 1) + pa::bwd_scratch_floats(d->L, 1));
+    // bf16 at d >= 32: the pair buffers hold bf16 and the preconditioning's
+    // backward keeps its intermediates in LDS (no scratch area)
+    const bool b16 = d->dtype == PATH_BF16 && D >= 32;
+    const size_t pair_el = b16 ? 2 : 4;
+    const size_t scr_el = b16 ? 0 : 4;
+    const size_t per_slice = 2 * pair_el * pa::bwd_pair_floats(d->L, D, 1) +
+                             scr_el * pa::bwd_scratch_floats(d->L, 1);
     size_t chunk = per_slice ? kBwdChunkBytes / per_slice : ns;
     chunk = chunk < 1 ? 1 : (chunk > ns ? ns : chunk);
     BwdLayout l{};
@@ -152,9 +158,9 @@ BwdLayout bwd_layout(const path_fwd_desc* d) {
     l.rowsum = take(nblk * B * 4);
     l.colsum = take(nblk * B * 4);
     l.delta = take(nblk * B * 4);
-    l.X = take(4 * pa::bwd_pair_floats(d->L, D, (int)chunk));
-    l.Z = take(4 * pa::bwd_pair_floats(d->L, D, (int)chunk));
-    l.scr = take(4 * pa::bwd_scratch_floats(d->L, (int)chunk));
+    l.X = take(pair_el * pa::bwd_pair_floats(d->L, D, (int)chunk));
+    l.Z = take(pair_el * pa::bwd_pair_floats(d->L, D, (int)chunk));
+    l.scr = take(scr_el * pa::bwd_scratch_floats(d->L, (int)chunk));
     l.mfma_precond = d->dtype == PATH_BF16 && pa::fwd_bf16_supported(D, B);
     if (l.mfma_precond) l.img = take(nblk * pa::fwd_bf16_image_bytes(D));
     l.total = off;

@@ -106,7 +106,8 @@ struct BwdArgs {
     void *dq, *dk, *dv, *dw;
     float *dbeta, *dlogf;
     FwdWs fw;            // recomputed preconditioning (ql, kr, em, dg, gl, tot; fp32)
-    float *X, *Z;        // per block pair of a chunk of slices [slice][pair][B][d]
+    float *X, *Z;        // per block pair of a chunk of slices [slice][pair][B][d] (bf16
+                         // elements for bf16 inputs at d >= 32)
     float *dQl, *dKr, *dEm, *dDg;   // per block: gradients of the preconditioned products
     float *rowsum, *colsum, *delta; // per position [blk][B]
     float* scr;          // per block of a chunk: scratch of the preconditioning's backward
