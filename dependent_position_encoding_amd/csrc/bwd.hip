@@ -1367,10 +1367,25 @@ constexpr int kSlots = 17;
 __device__ inline bf16x8 fragC(const __bf16* t, int i, int k0) {
     return *reinterpret_cast<const bf16x8*>(t + i * kLT + k0);
 }
+// The column read uses gfx950's transposing LDS load: in each group of 16
+// lanes, lane j names 4 consecutive elements of row k0 + j/4 starting at
+// column c0 + 4 (j mod 4), and lane i receives column c0 + i of those 4
+// rows; two such loads give a lane its 8 consecutive rows.  (i runs over 16
+// consecutive columns in each group of 16 lanes, as the fragment layout has
+// it.)
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 __device__ inline bf16x8 fragS(const __bf16* t, int i, int k0) {
+    const int j = threadIdx.x & 15;
+    const __bf16* p = t + (k0 + (j >> 2)) * kLT + (i - j) + 4 * (j & 3);
+    typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4;
+    const bf16x4v a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+    const bf16x4v b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * kLT));
     bf16x8 x;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = t[(k0 + e) * kLT + i];
+    for (int e = 0; e < 4; ++e) {
+        x[e] = a[e];
+        x[e + 4] = b[e];
+    }
     return x;
 }
 // One 32 x 32 tile of sum_k A(m0 + ., k) B(n0 + ., k); SA / SB: the operand is
