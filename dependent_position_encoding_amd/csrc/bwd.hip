@@ -942,6 +942,46 @@ __device__ inline void gemm_b_acc(int M, int N, const BV& A, const BV& Bv, f32x1
     for (int e = 0; e < 16; ++e) acc[e] += c[e];
 }
 
+// A fragment read down the columns of a bf16 LDS matrix of row stride ld:
+// the 8 consecutive rows k0 .. k0+7 of column i, through gfx950's transposing
+// LDS load.  In each group of 16 lanes (16 consecutive columns i, one k0),
+// lane j names 4 consecutive elements of row k0 + j/4 starting at column
+// c0 + 4 (j mod 4), and lane i receives column c0 + i of those 4 rows; a
+// second load covers rows k0+4 .. k0+7.  Every lane of the wave must take part.
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+__device__ inline bf16x8 frag_col(const __bf16* t, int ld, int i, int k0) {
+    const int j = threadIdx.x & 15;
+    const __bf16* p = t + (k0 + (j >> 2)) * ld + (i - j) + 4 * (j & 3);
+    typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4;
+    const bf16x4v a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+    const bf16x4v b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * ld));
+    bf16x8 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[e] = a[e];
+        x[e + 4] = b[e];
+    }
+    return x;
+}
+// as gemm_b_acc (one part each), CA / CB: the operand is read down the columns
+// of its stored matrix (the product contracts the matrix's rows)
+template <bool CA, bool CB, int K>
+__device__ inline void gemm_bc_acc(int M, int N, const BV& A, const BV& Bv, f32x16& acc) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 31, h = lane >> 5;
+    const int tn = N / 32;
+    if (wave >= (M / 32) * tn) return;
+    const int m0 = (wave / tn) * 32, n0 = (wave % tn) * 32;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        const bf16x8 a = CA ? frag_col(A.p0, A.ld, m0 + r, k0 + 8 * h)
+                            : *reinterpret_cast<const bf16x8*>(A.p0 + (m0 + r) * A.ld + k0 + 8 * h);
+        const bf16x8 b = CB ? frag_col(Bv.p0, Bv.ld, n0 + r, k0 + 8 * h)
+                            : *reinterpret_cast<const bf16x8*>(Bv.p0 + (n0 + r) * Bv.ld + k0 + 8 * h);
+        acc = mfma32(a, b, acc);
+    }
+}
+
 // key, bf16: for key block c, over the query blocks b >= c.  The logits are
 // formed query-major (S = X Kr^T) and written transposed, four queries of a
 // key at a time, so P^T and dS^T are key-major operands of dV = P^T dO and
@@ -958,10 +998,8 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sK;     // Kr_c [key][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sV;     // V_c [key][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sX;     // X_bc [query][d]
-    __shared__ __attribute__((aligned(16))) BTile<D, kB, 1> sXT;    // X_bc^T
-    __shared__ __attribute__((aligned(16))) BTile<D, kB, 1> sZT;    // A_{c-1}^T
+    __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sZ;     // A_{c-1} [query][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sdO;    // dO_b [query][d]
-    __shared__ __attribute__((aligned(16))) BTile<D, kB, 1> sdOT;   // dO_b^T
     __shared__ __attribute__((aligned(16))) BTile<kB, kB, 1> sPT;   // P^T, then dS^T [key][query] (bf16)
     __shared__ float sLse[kB], sDel[kB], sGb[kB], sGc[kB], sCol[kB];
     const int tid = threadIdx.x;
@@ -1029,25 +1067,14 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 *reinterpret_cast<bf16x4_t*>(&sX.v[0][(4 * rb4 + q) * sX.LDE + 4 * cb4]) = pX[q];
-                *reinterpret_cast<bf16x4_t*>(&sXT.v[0][(4 * cb4 + q) * sXT.LDE + 4 * rb4]) =
-                    bf16x4_t{pX[0][q], pX[1][q], pX[2][q], pX[3][q]};
                 if (c >= 1)
-                    *reinterpret_cast<bf16x4_t*>(&sZT.v[0][(4 * cb4 + q) * sZT.LDE + 4 * rb4]) =
-                        bf16x4_t{pZ[0][q], pZ[1][q], pZ[2][q], pZ[3][q]};
+                    *reinterpret_cast<bf16x4_t*>(&sZ.v[0][(4 * rb4 + q) * sZ.LDE + 4 * cb4]) = pZ[q];
             }
         }
         if (tid < NB8) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 *reinterpret_cast<u32x4*>(&sdO.v[0][(4 * rb8 + q) * sdO.LDE + 8 * cb8]) = pO[q];
-            const bf16x8 o0 = *reinterpret_cast<const bf16x8*>(&pO[0]);
-            const bf16x8 o1 = *reinterpret_cast<const bf16x8*>(&pO[1]);
-            const bf16x8 o2 = *reinterpret_cast<const bf16x8*>(&pO[2]);
-            const bf16x8 o3 = *reinterpret_cast<const bf16x8*>(&pO[3]);
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                *reinterpret_cast<bf16x4_t*>(&sdOT.v[0][(8 * cb8 + q) * sdOT.LDE + 4 * rb8]) =
-                    bf16x4_t{o0[q], o1[q], o2[q], o3[q]};
         }
         if (tid < kB) {
             sLse[tid] = pLse;
@@ -1060,7 +1087,7 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     // dV += P^T dO;  then dS = P (dO V^T - Delta), written back transposed
     auto backprop = [&]() {
         __syncthreads();   // P^T complete
-        gemm_b_acc<1, 1, kB>(kB, D, bview(sPT), bview(sdOT), accV);
+        gemm_bc_acc<false, true, kB>(kB, D, bview(sPT), bview(sdO), accV);
         __syncthreads();   // every read of P^T done
         gemm_b4<1, 1, D>(kB, kB, bview(sdO), bview(sV), [&](int n, int m, f32x4 dp) {
             // queries m .. m+3, key n
@@ -1112,8 +1139,8 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         });
         backprop();
         // dKr += dS^T X (scaled at the end);  dE -= A_{c-1}^T X
-        gemm_b_acc<1, 1, kB>(kB, D, bview(sPT), bview(sXT), accK);
-        if (c >= 1) gemm_b_acc<1, 1, kB>(D, D, bview(sZT), bview(sXT), accE);
+        gemm_bc_acc<false, true, kB>(kB, D, bview(sPT), bview(sX), accK);
+        if (c >= 1) gemm_bc_acc<true, true, kB>(D, D, bview(sZ), bview(sX), accE);
         __syncthreads();   // the pair's tiles may be replaced
     }
     for_acc(kB, D, accK, [&](int m, int n, float val) {
@@ -1149,8 +1176,7 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sV;     // V_c [key][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sX;     // X_bc [query][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sK;     // Kr_c [key][d]
-    __shared__ __attribute__((aligned(16))) BTile<D, kB, 1> sKT;    // Kr_c^T [d][key]
-    __shared__ __attribute__((aligned(16))) BTile<D, D, 1> sET;     // E_c^T
+    __shared__ __attribute__((aligned(16))) BTile<D, D, 1> sE;      // E_c [d][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sA;     // A_{c-1} [query][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, kB, 1> sS;    // P, then dS [query][key] (bf16)
     __shared__ float sLse[kB], sDel[kB], sGb[kB], sGc[kB], sRow[kB];
@@ -1237,7 +1263,6 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 sK.put4(4 * rb4 + q, 4 * cb4, pK[q]);
-                sKT.put4(4 * cb4 + q, 4 * rb4, f32x4{pK[0][q], pK[1][q], pK[2][q], pK[3][q]});
             }
         if (c < b)
 #pragma unroll
@@ -1248,7 +1273,7 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         if (c >= 1 && tid < NE4)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                sET.put4(4 * cb4 + q, 4 * rb4, f32x4{pE[0][q], pE[1][q], pE[2][q], pE[3][q]});
+                sE.put4(4 * rb4 + q, 4 * cb4, pE[q]);
         if (tid < kB) sGc[tid] = pGc;
     };
     float rowAcc = 0.f;   // the lane's query column (fixed by the tiling): dS summed over keys
@@ -1315,9 +1340,9 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         backprop(false);
         // G^T = Kr^T dS^T;  (A E)^T = E^T A^T;  A^T <- scale G^T + A^T - (A E)^T
         f32x16 gt = zero16(), ae = zero16();
-        gemm_b_acc<1, 1, kB>(D, kB, bview(sKT), bview(sS), gt);
+        gemm_bc_acc<true, false, kB>(D, kB, bview(sK), bview(sS), gt);
         if (c >= 1) {
-            gemm_b_acc<1, 1, D>(D, kB, bview(sET), bview(sA), ae);
+            gemm_bc_acc<true, false, D>(D, kB, bview(sE), bview(sA), ae);
             if (owner) {   // Z = A_{c-1}: four consecutive d of the lane's query per group
                 __bf16* zo = Zs + pair_index(b, c) * kB * D + (size_t)qcol * D;
 #pragma unroll
@@ -1367,27 +1392,7 @@ constexpr int kSlots = 17;
 __device__ inline bf16x8 fragC(const __bf16* t, int i, int k0) {
     return *reinterpret_cast<const bf16x8*>(t + i * kLT + k0);
 }
-// The column read uses gfx950's transposing LDS load: in each group of 16
-// lanes, lane j names 4 consecutive elements of row k0 + j/4 starting at
-// column c0 + 4 (j mod 4), and lane i receives column c0 + i of those 4
-// rows; two such loads give a lane its 8 consecutive rows.  (i runs over 16
-// consecutive columns in each group of 16 lanes, as the fragment layout has
-// it.)
-typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
-__device__ inline bf16x8 fragS(const __bf16* t, int i, int k0) {
-    const int j = threadIdx.x & 15;
-    const __bf16* p = t + (k0 + (j >> 2)) * kLT + (i - j) + 4 * (j & 3);
-    typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4;
-    const bf16x4v a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
-    const bf16x4v b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * kLT));
-    bf16x8 x;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        x[e] = a[e];
-        x[e + 4] = b[e];
-    }
-    return x;
-}
+__device__ inline bf16x8 fragS(const __bf16* t, int i, int k0) { return frag_col(t, kLT, i, k0); }
 // One 32 x 32 tile of sum_k A(m0 + ., k) B(n0 + ., k); SA / SB: the operand is
 // read down the stored matrix's columns (the product contracts its rows).
 template <bool SA, bool SB, int K>
