@@ -259,10 +259,9 @@ struct TilePf {
 // ---------------------------------------------------------------------------
 // chain: for query block b >= 1 of a slice, the queries Qw_c used against every
 // key block c < b, carried right to left as in the forward scan; stored per
-// block pair in X [slice][pair][B][d].  Longest chains first.
-// OUTB: the carried queries are stored as bf16 (the bf16 path reads them in
-// one part), the transition taken as bf16(Qw) bf16(E) like the forward scan.
-template <int D, int PARTS, bool OUTB>
+// block pair in X [slice][pair][B][d].  Longest chains first.  (fp32 inputs
+// and d = 16; bf16 at d 32/64 takes bwd_chain_b16_kernel.)
+template <int D, int PARTS>
 __global__ void __launch_bounds__(256)
 bwd_chain_kernel(int nb, int nsc, int slice0, const float* __restrict__ ql,
                  const float* __restrict__ em, float* __restrict__ X) {
@@ -286,22 +285,15 @@ bwd_chain_kernel(int nb, int nsc, int slice0, const float* __restrict__ ql,
         for (int e = tid; e < kB * (D / 4); e += 256) {
             const int r = e / (D / 4), x = 4 * (e % (D / 4));
             const f32x4 q4 = *reinterpret_cast<const f32x4*>(sQ + r * LD + x);
-            if constexpr (OUTB) {
-                __bf16* xo = reinterpret_cast<__bf16*>(X) + ((size_t)sl * npairs + pair_index(b, c)) * kB * D;
-                *reinterpret_cast<bf16x4_t*>(xo + (size_t)r * D + x) =
-                    bf16x4_t{(__bf16)q4[0], (__bf16)q4[1], (__bf16)q4[2], (__bf16)q4[3]};
-            } else {
-                float* xo = Xs + pair_index(b, c) * kB * D;
-                *reinterpret_cast<f32x4*>(xo + (size_t)r * D + x) = q4;
-            }
+            float* xo = Xs + pair_index(b, c) * kB * D;
+            *reinterpret_cast<f32x4*>(xo + (size_t)r * D + x) = q4;
         }
         if (c == 0) break;
         pfE.store(sE, LD);
         __syncthreads();
         if (c - 1 >= 1) pfE.load(em + (slice * nb + c - 1) * D * D, D);
         // Qw_{c-1} = Qw_c - Qw_c E_c^T:  B(k, n) = E[n][k]
-        constexpr int PC = OUTB ? 1 : PARTS;
-        gemm<PC, PC, DP>(kB, DP, cont(sQ, LD), cont(sE, LD),
+        gemm<PARTS, PARTS, DP>(kB, DP, cont(sQ, LD), cont(sE, LD),
                          [&](int m, int n, float v) { sT[m * LD + n] = v; });
         __syncthreads();
         for (int e = tid; e < kB * DP; e += 256) {
@@ -901,22 +893,9 @@ __device__ inline f32x16 tile_b(const BV& A, const BV& Bv, int m0, int n0, int r
     }
     return c;
 }
-template <int PA, int PB, int K, typename FO>
-__device__ inline void gemm_b(int M, int N, const BV& A, const BV& Bv, FO out) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    const int r = lane & 31, h = lane >> 5;
-    const int tn = N / 32, nt = (M / 32) * tn;
-    for (int t = wave; t < nt; t += nw) {
-        const int m0 = (t / tn) * 32, n0 = (t % tn) * 32;
-        const f32x16 c = tile_b<PA, PB, K>(A, Bv, m0, n0, r, h);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) out(m0 + 8 * i + 4 * h + j, n0 + r, c[4 * i + j], 4 * i + j);
-    }
-}
-// as gemm_b, with the epilogue called once per group of four consecutive
-// product rows of a lane: out4(n, m, v) receives rows m .. m+3 of column n
+// All 32 x 32 tiles of an M x N product dealt to the workgroup's waves, the
+// epilogue called once per group of four consecutive product rows of a lane:
+// out4(n, m, v) receives rows m .. m+3 of column n
 template <int PA, int PB, int K, typename FO>
 __device__ inline void gemm_b4(int M, int N, const BV& A, const BV& Bv, FO out4) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -1375,6 +1354,92 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
 }
 
 // ---------------------------------------------------------------------------
+// chain for bf16 inputs at d in {32, 64}: the carried queries stay in
+// registers, a 32 x 32 tile of Qw per wave in the matrix-core C layout (lane:
+// column d, registers: rows q), as the forward's scan keeps them.  Each step
+// writes the tile to LDS once as bf16 Qw^T; from there the pair's X_bc rows
+// go to memory as 16-byte chunks (read down Qw^T's columns by the transposing
+// load) and the transition Qw <- Qw - Qw E_c^T takes its Qw operand the same
+// way, with -E_c (bf16) from LDS, accumulating into the registers.
+template <int D>
+__global__ void __launch_bounds__(256)
+bwd_chain_b16_kernel(int nb, int nsc, int slice0, const float* __restrict__ ql,
+                     const float* __restrict__ em, float* __restrict__ X) {
+    constexpr int TN = D / 32, NT = (kB / 32) * TN;        // Qw tiles
+    constexpr int LQ = kB + 8, LE = D + 8;                  // LDS row strides (bf16)
+    constexpr int EU = (D * D / 4 + 255) / 256;             // E float4 units per thread
+    __shared__ __attribute__((aligned(16))) __bf16 sQt[D * LQ];   // Qw^T [d][q]
+    __shared__ __attribute__((aligned(16))) __bf16 sE[D * LE];    // -E_c [d_out][d_in]
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, h = lane >> 5;
+    const int b = nb - 1 - (int)(blockIdx.x / nsc), sl = (int)(blockIdx.x % nsc);
+    const size_t slice = (size_t)slice0 + sl, npairs = (size_t)nb * (nb - 1) / 2;
+    __bf16* Xs = reinterpret_cast<__bf16*>(X) + (size_t)sl * npairs * kB * D;
+    const bool owner = wave < NT;
+    const int m0 = (wave / TN) * 32, n0 = (wave % TN) * 32;   // q rows, d columns of the tile
+    f32x16 qw = zero16();
+    if (owner) {
+        const float* qlb = ql + (slice * nb + b) * kB * D;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qw[4 * i + j] = qlb[(m0 + 8 * i + 4 * h + j) * D + n0 + r];
+    }
+    f32x4 pe[EU];
+    auto loadE = [&](int c) {
+        const float* e = em + (slice * nb + c) * D * D;
+#pragma unroll
+        for (int u = 0; u < EU; ++u) {
+            const int idx = tid + 256 * u;
+            if (idx < D * D / 4) pe[u] = *reinterpret_cast<const f32x4*>(e + 4 * idx);
+        }
+    };
+    if (b - 1 >= 1) loadE(b - 1);
+    // the X_bc chunk a lane stores: 16 consecutive q per group of 16 lanes, 8 d
+    constexpr int XP = (kB * D / 8) / 256;                    // fragment passes per wave
+    for (int c = b - 1; c >= 0; --c) {
+        if (owner)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<bf16x4_t*>(sQt + (n0 + r) * LQ + m0 + 8 * i + 4 * h) =
+                    bf16x4_t{(__bf16)qw[4 * i], (__bf16)qw[4 * i + 1], (__bf16)qw[4 * i + 2],
+                             (__bf16)qw[4 * i + 3]};
+        if (c > 0)
+#pragma unroll
+            for (int u = 0; u < EU; ++u) {
+                const int idx = tid + 256 * u;
+                if (idx < D * D / 4) {
+                    const int row = (4 * idx) / D, col = (4 * idx) % D;
+                    *reinterpret_cast<bf16x4_t*>(sE + row * LE + col) =
+                        bf16x4_t{(__bf16)-pe[u][0], (__bf16)-pe[u][1], (__bf16)-pe[u][2],
+                                 (__bf16)-pe[u][3]};
+                }
+            }
+        __syncthreads();   // Qw^T and -E_c in LDS
+        if (c - 1 >= 1) loadE(c - 1);
+        {   // X_bc = Qw as bf16 rows [q][d]
+            __bf16* xo = Xs + pair_index(b, c) * kB * D;
+#pragma unroll
+            for (int u = 0; u < XP; ++u) {
+                const int G = (u * 4 + wave) * 4 + (lane >> 4);   // (16-q block, 8-d chunk)
+                const int q = 16 * (G % (kB / 16)) + (lane & 15), d0 = 8 * (G / (kB / 16));
+                const bf16x8 x = frag_col(sQt, LQ, q, d0);
+                *reinterpret_cast<bf16x8*>(xo + (size_t)q * D + d0) = x;
+            }
+        }
+        if (c > 0 && owner) {
+            // Qw(q, d) += sum_k Qw(q, k) (-E_c(d, k))
+#pragma unroll
+            for (int k0 = 0; k0 < D; k0 += 16) {
+                const bf16x8 a = frag_col(sQt, LQ, m0 + r, k0 + 8 * h);
+                const bf16x8 e = *reinterpret_cast<const bf16x8*>(sE + (n0 + r) * LE + k0 + 8 * h);
+                qw = mfma32(a, e, qw);
+            }
+        }
+        __syncthreads();   // every read of this step's LDS done
+    }
+}
+
+// ---------------------------------------------------------------------------
 // precond_bwd for bf16 inputs at d in {32, 64}: the same products as
 // bwd_precond_kernel, every operand and intermediate held in LDS as one bf16
 // part (the precision the pair kernels work in), so no product waits on a
@@ -1681,9 +1746,13 @@ hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
     for (int s0 = 0; s0 < ns; s0 += a.chunk) {
         const int nsc = std::min(a.chunk, ns - s0);
         if (nb > 1) {
-            constexpr bool OUTB = sizeof(T) == 2 && D >= 32;
-            hipLaunchKernelGGL((bwd_chain_kernel<D, PARTS, OUTB>), dim3(nsc * (nb - 1)), dim3(256),
-                               0, st, nb, nsc, s0, a.fw.ql, (const float*)a.fw.em, a.X);
+            if constexpr (sizeof(T) == 2 && D >= 32)
+                hipLaunchKernelGGL((bwd_chain_b16_kernel<D>), dim3(nsc * (nb - 1)), dim3(256), 0,
+                                   st, nb, nsc, s0, a.fw.ql, (const float*)a.fw.em, a.X);
+            else
+                hipLaunchKernelGGL((bwd_chain_kernel<D, PARTS>), dim3(nsc * (nb - 1)),
+                                   dim3(256), 0, st, nb, nsc, s0, a.fw.ql, (const float*)a.fw.em,
+                                   a.X);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         if constexpr (sizeof(T) == 2 && D >= 32) {
