@@ -37,7 +37,7 @@ class Batch:
     """S sequences with their own token streams, prefilled to lens[s] tokens
     into a shared paged cache."""
 
-    def __init__(self, wl, lens, steps, page_size, k_dtype, seed, spare_pages=7):
+    def __init__(self, wl, lens, steps, page_size, k_dtype, seed, spare_pages=7, device="cpu"):
         pa = _pa()
         self.pa, self.wl, self.lens, self.steps = pa, wl, list(lens), steps
         S, H, d = len(lens), wl.H, wl.d
@@ -56,7 +56,7 @@ class Batch:
         self.table = torch.from_numpy(table).to(DEV)
         self.cache = pa.PagedCache(num_pages, page_size, H, d, dtype=wl.dtype, k_dtype=k_dtype,
                                    gate=wl.fox, device=DEV)
-        self.x = [workloads.make_inputs(wl.replace(N=1), device="cpu", variant=seed * 31 + s,
+        self.x = [workloads.make_inputs(wl.replace(N=1), device=device, variant=seed * 31 + s,
                                         L=lens[s] + steps) for s in range(S)]
         for s in range(S):
             n = lens[s]
@@ -252,3 +252,31 @@ def test_paged_step_graph_replay():
         gl = np.stack([workloads.as_slices_f64(x[s:s + 1]) for x in got_l], axis=1)
         check(f"graph paged o (seq {s})", go, ro, bf16=True)
         check(f"graph paged lse (seq {s})", gl, rl, bf16=True)
+
+
+def test_paged_serving_shape_sampled():
+    """The paged step at the shape the benchmark times: 32 sequences x 32
+    heads, d = 64, bf16 with the gate, cached lengths uniform in [1024, 8192]
+    (the benchmark's seed), page size 64; every sequence prefilled and
+    imported, two fused steps, and the outputs of sampled (sequence, head)
+    slices against the oracle's rows."""
+    import numpy as np
+    rng = np.random.default_rng(7)
+    lens = [int(n) for n in rng.integers(1024, 8193, size=32)]
+    wl = workloads.CONFIGS["fox"].replace(H=32)
+    print(f"case paged serving shape, lengths {min(lens)}..{max(lens)}", flush=True)
+    b = Batch(wl, lens, steps=2, page_size=64, k_dtype=torch.bfloat16, seed=13, device=DEV)
+    outs = [b.step(i) for i in range(2)]
+    torch.cuda.synchronize()
+    assert b.seq_lens.cpu().tolist() == [n + 2 for n in lens]
+    for s in (0, 13, 31):
+        n = lens[s]
+        for h in (0, 17):
+            f64 = {k: (workloads.as_slices_f64(v, heads=[h]) if v is not None else None)
+                   for k, v in b.x[s].items()}
+            ro, rl = oracle.fwd_rows(f64["q"], f64["k"], f64["v"], f64["w"], f64["beta"],
+                                     f64["logf"], wl.scale, rows=np.arange(n, n + 2))
+            go = np.stack([workloads.as_slices_f64(o[s:s + 1, h:h + 1]) for o, _ in outs], axis=1)
+            gl = np.stack([workloads.as_slices_f64(l[s:s + 1, h:h + 1]) for _, l in outs], axis=1)
+            check(f"paged o (seq {s}, {n} keys, head {h})", go, ro, bf16=True)
+            check(f"paged lse (seq {s}, head {h})", gl, rl, bf16=True)
