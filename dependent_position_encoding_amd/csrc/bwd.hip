@@ -981,6 +981,12 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sdO;    // dO_b [query][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, kB, 1> sPT;   // P^T, then dS^T [key][query] (bf16)
     __shared__ float sLse[kB], sDel[kB], sGb[kB], sGc[kB], sCol[kB];
+    // log2-unit logit terms of the off-diagonal steps: per query row
+    // (gate, shift, -lse; -inf past the sequence end) and per key (-gate)
+    __shared__ __attribute__((aligned(16))) float sRow2[kB];
+    __shared__ float sCol2[kB];
+    const float scale2 = scale * kLog2e;
+    float shift = 0.f;              // sum of the gate totals of blocks c .. b-1
     const int tid = threadIdx.x;
     const int c = (int)(blockIdx.x / nsc), sl = (int)(blockIdx.x % nsc);
     const size_t slice = (size_t)slice0 + sl, blk_c = slice * nb + c, base = slice * L;
@@ -1008,6 +1014,7 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     }
     if (tid < kB) {
         sGc[tid] = fox ? fw.gl[blk_c * kB + tid] : 0.f;
+        sCol2[tid] = -sGc[tid] * kLog2e;
         sCol[tid] = 0.f;
     }
     // prefetch of query block b's X_bc, Z_bc (4 x 4 bf16 blocks), dO and row terms
@@ -1059,6 +1066,7 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
             sLse[tid] = pLse;
             sDel[tid] = pDel;
             sGb[tid] = pGb;
+            sRow2[tid] = b * kB + tid < L ? (pGb + shift - pLse) * kLog2e : -INFINITY;
         }
     };
     f32x16 accV = zero16(), accK = zero16(), accE = zero16();
@@ -1101,7 +1109,6 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     if (c + 1 < nb) prefetch(c + 1);
     backprop();
 
-    float shift = 0.f;              // sum of the gate totals of blocks c .. b-1
     for (int b = c + 1; b < nb; ++b) {
         if (fox) shift += fw.tot[slice * nb + b - 1];
         commit(b);
@@ -1109,11 +1116,12 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         if (b + 1 < nb) prefetch(b + 1);
         // P = exp(scale X Kr^T + bias - lse), queries m .. m+3 of key n, into P^T
         gemm_b4<1, 1, D>(kB, kB, bview(sX), bview(sK), [&](int n, int m, f32x4 sv) {
+            const f32x4 rw = *reinterpret_cast<const f32x4*>(sRow2 + m);
+            const float cl = sCol2[n];
             f32x4 p;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                p[e] = b * kB + m + e < L
-                    ? __expf(scale * sv[e] + (sGb[m + e] + shift - sGc[n]) - sLse[m + e]) : 0.f;
+                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(scale2, sv[e], rw[e] + cl));
             sPT.put4(n, m, p);
         });
         backprop();
@@ -1159,6 +1167,11 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sA;     // A_{c-1} [query][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, kB, 1> sS;    // P, then dS [query][key] (bf16)
     __shared__ float sLse[kB], sDel[kB], sGb[kB], sGc[kB], sRow[kB];
+    // log2-unit logit terms of the off-diagonal steps: per query row (gate,
+    // -lse; -inf past the sequence end) and per key of the current block (-gate)
+    __shared__ float sRowB[kB];
+    __shared__ __attribute__((aligned(16))) float sCol2[kB];
+    const float scale2 = scale * kLog2e;
     __shared__ float sTb;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = nb - 1 - (int)(blockIdx.x / nsc), sl = (int)(blockIdx.x % nsc);
@@ -1191,6 +1204,7 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         sDel[tid] = dl;
         sLse[tid] = pos < L ? lse[base + pos] : 0.f;
         sGb[tid] = fox ? fw.gl[blk_b * kB + tid] : 0.f;
+        sRowB[tid] = pos < L ? (sGb[tid] - sLse[tid]) * kLog2e : -INFINITY;
         sRow[tid] = 0.f;
         delta[blk_b * kB + tid] = dl;
     }
@@ -1253,7 +1267,10 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 sE.put4(4 * rb4 + q, 4 * cb4, pE[q]);
-        if (tid < kB) sGc[tid] = pGc;
+        if (tid < kB) {
+            sGc[tid] = pGc;
+            sCol2[tid] = -pGc * kLog2e;
+        }
     };
     float rowAcc = 0.f;   // the lane's query column (fixed by the tiling): dS summed over keys
     // dS = P (dO V^T - Delta), formed key-major (dP^T = V dO^T) and written back
@@ -1308,12 +1325,14 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         if (c + 1 < b) prefetch(c + 1);
         const float shift = fox ? sTb - Tc : 0.f;   // sum of the totals of blocks c .. b-1
         // S^T = Kr X^T: keys m .. m+3 of query n, written to the query-major P
+        const float shift2 = shift * kLog2e;
         gemm_b4<1, 1, D>(kB, kB, bview(sK), bview(sX), [&](int n, int m, f32x4 sv) {
+            const float rw = sRowB[n] + shift2;
+            const f32x4 cl = *reinterpret_cast<const f32x4*>(sCol2 + m);
             f32x4 p;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                p[e] = b * kB + n < L
-                    ? __expf(scale * sv[e] + (sGb[n] + shift - sGc[m + e]) - sLse[n]) : 0.f;
+                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(scale2, sv[e], rw + cl[e]));
             sS.put4(n, m, p);
         });
         backprop(false);
