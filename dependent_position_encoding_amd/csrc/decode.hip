@@ -390,6 +390,7 @@ paged_chunk_kernel(K* __restrict__ kp, T* __restrict__ vp, float* __restrict__ g
 // seq_lens[s] to nk (the chunk kernel, which reads it, has finished).
 constexpr int kCombineMaxChunks = 1024;
 constexpr int kCombineThreads = 1024;
+constexpr int kCombinePre = 24;  // chunks per thread whose accumulators are loaded up front
 
 template <typename T, int D>
 __global__ void __launch_bounds__(kCombineThreads)
@@ -412,6 +413,15 @@ decode_combine_kernel(const float* __restrict__ part, int nch, int pstride, int 
         if (tid == 0 && seq_lens && slice % H == 0) seq_lens[slice / H] = n;
     }
     const float* p = part + (size_t)slice * pstride * (D + 2);
+    const int g = tid / D, x = tid % D;
+    // this thread's share of the accumulators, loaded beside the maxima and
+    // sums (they do not depend on them), for up to kCombinePre chunks
+    float pre[kCombinePre];
+#pragma unroll
+    for (int i = 0; i < kCombinePre; ++i) {
+        const int c = g + G * i;
+        pre[i] = c < nch ? p[(size_t)c * (D + 2) + 2 + x] : 0.f;
+    }
     const float mc = tid < nch ? p[(size_t)tid * (D + 2)] : -INFINITY;
     const float lc = tid < nch ? p[(size_t)tid * (D + 2) + 1] : 0.f;
     float mx = mc;
@@ -432,10 +442,14 @@ decode_combine_kernel(const float* __restrict__ part, int nch, int pstride, int 
     float lt = 0.f;
 #pragma unroll
     for (int i = 0; i < NW; ++i) lt += wsum[i];
-    const int g = tid / D, x = tid % D;
     float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < kCombinePre; ++i) {
+        const int c = g + G * i;
+        if (c < nch) a += sf[c] * pre[i];
+    }
 #pragma unroll 8
-    for (int c = g; c < nch; c += G) a += sf[c] * p[(size_t)c * (D + 2) + 2 + x];
+    for (int c = g + G * kCombinePre; c < nch; c += G) a += sf[c] * p[(size_t)c * (D + 2) + 2 + x];
     sacc[g][x] = a;
     __syncthreads();
     if (tid < D) {
