@@ -961,6 +961,23 @@ __device__ inline void gemm_bc_acc(int M, int N, const BV& A, const BV& Bv, f32x
     }
 }
 
+// Work order of the bf16 pair kernels: workgroup = (slice, rank), rank 0 the
+// block with the most partner blocks.  Slices are taken kPairGroup at a time
+// and, inside a group, ranks in order with the group's slices interleaved, so
+// the workgroups resident at once cover a few slices and the key-block tiles
+// (query kernel) and dO tiles (key kernel) they all stream are hit in L2.  The
+// grid goes to the XCDs round-robin and kPairGroup is a multiple of 8, so all
+// workgroups of a slice share one XCD's L2.  At the LM-layer shape this cuts
+// the query kernel's HBM reads from ~29 to ~13 KB per block pair.
+constexpr int kPairGroup = 16;
+
+__device__ inline void pair_order(int nb, int nsc, int& rank, int& sl) {
+    const int span = kPairGroup * nb, g = (int)blockIdx.x / span, r = (int)blockIdx.x % span;
+    const int sz = min(kPairGroup, nsc - g * kPairGroup);
+    rank = r / sz;
+    sl = g * kPairGroup + r % sz;
+}
+
 // key, bf16: for key block c, over the query blocks b >= c.  The logits are
 // formed query-major (S = X Kr^T) and written transposed, four queries of a
 // key at a time, so P^T and dS^T are key-major operands of dV = P^T dO and
@@ -988,7 +1005,8 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     const float scale2 = scale * kLog2e;
     float shift = 0.f;              // sum of the gate totals of blocks c .. b-1
     const int tid = threadIdx.x;
-    const int c = (int)(blockIdx.x / nsc), sl = (int)(blockIdx.x % nsc);
+    int c, sl;
+    pair_order(nb, nsc, c, sl);
     const size_t slice = (size_t)slice0 + sl, blk_c = slice * nb + c, base = slice * L;
     const size_t npairs = (size_t)nb * (nb - 1) / 2;
     // the carried queries and the gradient chain, bf16 [pair][kB][D]
@@ -1174,7 +1192,9 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     const float scale2 = scale * kLog2e;
     __shared__ float sTb;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int b = nb - 1 - (int)(blockIdx.x / nsc), sl = (int)(blockIdx.x % nsc);
+    int b, sl;
+    pair_order(nb, nsc, b, sl);
+    b = nb - 1 - b;
     const size_t slice = (size_t)slice0 + sl, blk_b = slice * nb + b, base = slice * L;
     const size_t npairs = (size_t)nb * (nb - 1) / 2;
     // the carried queries and the gradient chain, bf16 [pair][kB][D]
