@@ -342,6 +342,9 @@ def main():
             "algorithmic_bytes_first_step": decode_bytes(N, H, d, L, kb, vb),
         }
         out["unfused_decode"] = unfused_rates(pa, cache, tok, L, wl, dws, ot, lt, kb, vb)
+        out["decode_cache_cold"] = cold_decode_rate(pa, pre, cache, tok, L, wl, ws, dws, ot, lt,
+                                                    kb, vb)
+    out["prefill_reps"] = prefill_reps(pa, pre, wl, cache, ws, o, lse)
     out["beta0_baseline"] = causal_baseline(pa, pre, wl, out["prefill"])
     out["front_end"] = front_end_rate(pa, wl, dev)
     out["backward"] = backward_rate(pa, dev)
@@ -349,6 +352,70 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, N * (L + T) / (ms_step * 1e-3))
     print(json.dumps(out), flush=True)
+
+
+def prefill_reps(pa, pre, wl, cache, ws, o, lse, reps=20):
+    """Whole-prefill time (preconditioning, scan and, with a cache, its
+    alignment) over `reps` back-to-back calls after three warm ones, each
+    bracketed by its own events: median and minimum."""
+    import numpy as np
+    import torch
+    run = lambda: pa.fwd(pre["q"], pre["k"], pre["v"], pre["w"], pre["beta"], logf=pre["logf"],
+                         scale=wl.scale, cache=cache, workspace=ws, out=(o, lse))
+    for _ in range(3):
+        run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) for a, b in evs]
+    return {"reps": reps, "median_ms": round(float(np.median(t)), 4),
+            "min_ms": round(float(np.min(t)), 4), "includes_cache_alignment": cache is not None}
+
+
+def cold_decode_rate(pa, pre, cache, tok, L, wl, ws, dws, ot, lt, kb, vb, steps=32,
+                     scratch_bytes=512 << 20):
+    """Fused decode steps with the caches cold: before each step a 512 MiB
+    scratch buffer (twice the size of the Infinity Cache) is either written
+    (fill) or read (sum), so no cached key or value is left in any cache.  The
+    written variant also leaves the Infinity Cache full of dirty scratch lines
+    that the step's own traffic must write back to HBM; the read variant leaves
+    clean lines only.  The cache is re-aligned from the prompt before each
+    variant; each step is bracketed by its own events (the flush is outside
+    them); eager launches, mean over `steps` steps."""
+    import torch
+    N, H, d = cache.N, cache.H, cache.d
+    scratch = torch.empty(scratch_bytes // 4, dtype=torch.float32, device=cache.device)
+    scratch.fill_(1.0)
+    acc = torch.empty((), dtype=torch.float32, device=cache.device)
+    by = sum(decode_bytes(N, H, d, L + i, kb, vb) for i in range(steps))
+    res = {"scratch_bytes_between_steps": scratch_bytes, "steps": steps}
+    for mode in ("after_write", "after_read"):
+        pa.fwd(pre["q"], pre["k"], pre["v"], pre["w"], pre["beta"], logf=pre["logf"],
+               scale=wl.scale, cache=cache, workspace=ws)
+        evs = []
+        for i in range(steps):
+            if mode == "after_write":
+                scratch.fill_(float(i + 2))
+            else:
+                torch.sum(scratch, dim=0, out=acc)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            pa.decode_step(cache, L + i, tok["q"][i], tok["k"][i], tok["v"][i], tok["w"][i],
+                           tok["beta"][i], tok["logf"][i] if wl.fox else None,
+                           scale=wl.scale, workspace=dws, out=(ot, lt))
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in evs)
+        gbs = by / (ms * 1e-3) / 1e9
+        res[mode] = {"us_per_token_step": round(ms / steps * 1e3, 2), "GB_s": round(gbs, 1),
+                     "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    del scratch
+    return res
 
 
 def unfused_rates(pa, cache, tok, n, wl, dws, ot, lt, kb, vb, reps=20):
@@ -616,11 +683,41 @@ def cpu_baseline(wl, x, seconds, gpu_tokens_per_s):
     oracle.fwd_rows(f64["q"], f64["k"], f64["v"], f64["w"], f64["beta"], f64["logf"], wl.scale, rows=rows)
     el = time.perf_counter() - t
     tps = rows.size / el
+    cores = oracle.num_threads()
+    # the same walk on one thread, sized to about a tenth of the timed sample's time
+    rows1 = rng.integers(0, Ltot, (len(heads), max(4, nrows // (10 * max(cores, 1)))))
+    oracle.set_num_threads(1)
+    try:
+        t = time.perf_counter()
+        oracle.fwd_rows(f64["q"], f64["k"], f64["v"], f64["w"], f64["beta"], f64["logf"],
+                        wl.scale, rows=rows1)
+        el1 = time.perf_counter() - t
+    finally:
+        oracle.set_num_threads(cores)
+    job_rows = wl.N * wl.H * Ltot
     return {"value": round(tps, 1), "unit": "tokens/s (query rows of the full job per second)",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": cores, "kind": "oracle",
             "sample": f"{rows.size} random query rows (uniform over all {Ltot} positions) of "
                       f"{len(heads)} heads, fp64 walk, {el:.1f} s",
+            "single_thread_tokens_per_s": round(rows1.size / el1, 1),
+            "single_thread_sample": f"{rows1.size} rows, {el1:.1f} s",
+            "extrapolated_full_job_s": round(job_rows / tps, 1),
+            "extrapolated_note": f"all {job_rows} rows of the job at the sampled rate "
+                                 "(sampled rows are uniform over positions, so their mean "
+                                 "cost is a full-job row's)",
+            "cpu_model": _cpu_model(),
             "gpu_tokens_per_s_same_job": round(gpu_tokens_per_s, 1)}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":

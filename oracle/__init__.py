@@ -74,6 +74,8 @@ class Oracle:
         lib.oracle_bwd.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
         self._lib = lib
 
     def frontend(self, x, Wd, Wu, kc, ub, bb, uf=None, bf=None, H=None, d=None):
@@ -105,6 +107,9 @@ class Oracle:
 
     def num_threads(self) -> int:
         return int(self._lib.oracle_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        self._lib.oracle_set_num_threads(int(n))
 
     def fwd_rows(self, q, k, v, w, beta, logf=None, scale=1.0, rows=None):
         """PaTH(-FoX) attention for selected rows of S slices, in fp64.
@@ -194,6 +199,10 @@ def default() -> Oracle:
 
 def num_threads() -> int:
     return default().num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    default().set_num_threads(n)
 
 
 def fwd_rows(*args, **kwargs):

@@ -250,6 +250,17 @@ int oracle_bwd(int S, int L, int d, int dv, const double *q, const double *k,
     return 0;
 }
 
+/* Threads the parallel regions of this library use from now on (n >= 1). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Number of OpenMP threads a parallel region of this library would use. */
 int oracle_num_threads(void)
 {
