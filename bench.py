@@ -62,15 +62,19 @@ def precond_flops(N, H, L, d, B=64):
 
 def bwd_flops(N, H, L, d, B=64):
     """Matrix-core flops the backward kernels execute, for B = d: per block
-    pair c < b, eight B x B x d products (the logits and dO V^T, each formed
-    by both the query-major and the key-major pass; dS Kr; P^T dO; dS^T Qw)
-    and three B x d x d ones (the carried queries' transition, the gradient
-    chain's, dE); per block, 32 products of B x B x d size (29 in the
-    backward of the preconditioning with its recomputed forward products,
-    three for the diagonal tile); plus the recomputed preconditioning."""
+    pair c < b, seven B x B x d products (key pass: the logits, dP, dV, dK;
+    query pass: the transposed logits, dP^T, and the dQ-chain update
+    Kr^T dS^T); per pair with c >= 1, three B x d x d ones (dE, the gradient
+    chain's E^T product, the carried queries' transition); per block, 33
+    products of B x B x d size (30 in the backward of the preconditioning with
+    its recomputed forward products, three for the diagonal tile); plus the
+    recomputed preconditioning, counted as in the forward.  rocprofv3's
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 matches this to 0.01 % once the
+    preconditioning's split-operand products are counted twice."""
     nb = (L + B - 1) // B
     pairs = nb * (nb - 1) // 2
-    per_slice = pairs * (8 * 2 * B * B * d + 3 * 2 * B * d * d) + nb * 32 * 2 * B * B * d
+    tpairs = max(nb - 1, 0) * max(nb - 2, 0) // 2
+    per_slice = pairs * 7 * 2 * B * B * d + tpairs * 3 * 2 * B * d * d + nb * 33 * 2 * B * B * d
     return N * H * per_slice + precond_flops(N, H, L, d, B)
 
 
@@ -133,6 +137,61 @@ def summarize_pmc(paths, workload):
     print(json.dumps(res))
 
 
+def causal_flops(N, H, L, d, B=64):
+    """GEMM flops of the plain causal kernel: Q.K^T and P.V for every block
+    pair c < b and for the (fully computed) diagonal tile."""
+    nb = (L + B - 1) // B
+    return N * H * (nb * (nb - 1) // 2 + nb) * 4 * B * B * d
+
+
+def summarize_mfma(path, workload):
+    """Matrix-core flops per dispatch from rocprofv3's SQ_INSTS_VALU_MFMA_MOPS_BF16
+    (bf16 MFMA operations / 512) beside the flops the bench counts for the same
+    launch: the long-context workload's scan, preconditioning and causal
+    baseline, and the backward at the LM-layer shape (its four pair/block
+    kernels plus the recomputed preconditioning against bwd_flops)."""
+    import csv
+
+    import workloads
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"]) * 512))
+
+    def mean(sub, grid=None):
+        v = [x for n, g, x in rows if sub in n and (grid is None or g == grid)]
+        return (sum(v) / len(v), len(v)) if v else (None, 0)
+
+    spec = WORKLOADS[workload]
+    wl = workloads.CONFIGS[spec["cfg"]]
+    N, H, L, d = wl.N, wl.H, spec.get("L", wl.L), wl.d
+    nb = (L + 63) // 64
+    lm = workloads.CONFIGS["lm"]
+    lnb = (lm.L + 63) // 64
+    res = {"workload": workload, "counter": "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512", "kernels": {}}
+    for key, sub, grid, counted in (
+            ("scan", "scan_mfma_kernel<64, true>", None, scan_flops(N, H, L, d)),
+            ("precond", "precond_mfma_kernel", N * H * nb * 512, precond_flops(N, H, L, d)),
+            ("causal_baseline", "causal_mfma_kernel", None, causal_flops(N, H, L, d))):
+        m, n = mean(sub, grid)
+        res["kernels"][key] = {"dispatches": n, "mfma_flops": m, "counted_flops": counted,
+                               "ratio": None if m is None else round(m / counted, 4)}
+    parts = {}
+    for sub in ("bwd_key_b16_kernel", "bwd_query_b16_kernel", "bwd_chain_b16_kernel",
+                "bwd_precond_b16_kernel"):
+        parts[sub] = mean(sub)[0]
+    parts["precond_mfma_kernel (recomputed)"] = mean("precond_mfma_kernel",
+                                                     lm.N * lm.H * lnb * 512)[0]
+    tot = sum(v for v in parts.values() if v is not None)
+    counted = bwd_flops(lm.N, lm.H, lm.L, lm.d)
+    res["kernels"]["backward_lm"] = {"parts": parts, "mfma_flops": tot, "counted_flops": counted,
+                                     "ratio": round(tot / counted, 4)}
+    out = os.path.join(ROOT, "profiles", f"mfma_{workload}.json")
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res))
+
+
 def measured_traffic(workload, key):
     """Counter-measured HBM bytes per launch, or None if not taken for this
     workload or if the kernel's source changed since."""
@@ -164,6 +223,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the decode steps one by one instead of replaying a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--summarize-mfma", metavar="MFMA_CSV",
+                    help="write profiles/mfma_<workload>.json from a rocprofv3 "
+                         "SQ_INSTS_VALU_MFMA_MOPS_BF16 counter CSV and exit")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a bench run "
                          "and of a --calibrate-copy run into profiles/traffic_<workload>.json")
@@ -171,6 +233,9 @@ def main():
                     help="only run a 1 GiB device-to-device copy three times (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, args.workload)
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc, args.workload)
         return
@@ -388,6 +453,7 @@ def cold_decode_rate(pa, pre, cache, tok, L, wl, ws, dws, ot, lt, kb, vb, steps=
     them); eager launches, mean over `steps` steps."""
     import torch
     N, H, d = cache.N, cache.H, cache.d
+    steps = min(steps, len(tok["q"]))
     scratch = torch.empty(scratch_bytes // 4, dtype=torch.float32, device=cache.device)
     scratch.fill_(1.0)
     acc = torch.empty((), dtype=torch.float32, device=cache.device)
