@@ -105,6 +105,13 @@ def test_bwd_bf16(fox):
     _run(wl, L=150)
 
 
+def test_bwd_bf16_ragged_slice_group():
+    # 20 slices: the pair kernels take slices 16 at a time, so one full group
+    # and one of 4; a ragged sequence tail as well
+    wl = workloads.CONFIGS["fox"].replace(N=2, H=10)
+    _run(wl, L=300, seed=3)
+
+
 def test_bwd_bf16_many_blocks():
     # 16 blocks: long transition chains through the scan's backward
     wl = workloads.CONFIGS["fox"].replace(N=1, H=2)
