@@ -136,6 +136,12 @@ def test_paged_fp32(gate):
     _run_and_check(b, False, torch.float32)
 
 
+def test_paged_bf16_head_dim_32_no_gate():
+    wl = workloads.CONFIGS["fox"].replace(H=2, d=32, fox=False, scale=32 ** -0.5)
+    b = Batch(wl, [3, 128, 300], steps=2, page_size=32, k_dtype=torch.bfloat16, seed=5)
+    _run_and_check(b, True, torch.bfloat16)
+
+
 def test_paged_bf16_fp32_keys_head_dim_16():
     wl = workloads.CONFIGS["fox"].replace(H=3, d=16, scale=0.25)
     b = Batch(wl, [33, 130], steps=2, page_size=16, k_dtype=torch.float32, seed=4)
