@@ -120,9 +120,10 @@ def test_bwd_bf16_many_blocks():
 
 def test_bwd_bf16_full_lm_shape_sampled_slices():
     """The LM-layer training shape the benchmark times (4 x 24 heads, L =
-    4096, d = 64, bf16), in its launch configuration (the slices split into
-    two groups over the pair buffers); the gradients of slices in both groups
-    and at the edges against the oracle, slice by slice."""
+    4096, d = 64, bf16), in its launch configuration (all 96 slices in one
+    pass over the pair buffers, which the pair kernels take 16 at a time); the
+    gradients of the first, a middle and the last slice against the oracle,
+    slice by slice."""
     pa = _pa()
     wl = workloads.CONFIGS["lm"]
     x = workloads.make_inputs(wl, device=DEV, variant=3)
