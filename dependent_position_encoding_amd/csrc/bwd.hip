@@ -31,6 +31,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "img.hpp"
 #include "kernels.hpp"
 #include "mfma.hpp"
 
@@ -926,14 +927,16 @@ __device__ inline void gemm_b_acc(int M, int N, const BV& A, const BV& Bv, f32x1
 // LDS load.  In each group of 16 lanes (16 consecutive columns i, one k0),
 // lane j names 4 consecutive elements of row k0 + j/4 starting at column
 // c0 + 4 (j mod 4), and lane i receives column c0 + i of those 4 rows; a
-// second load covers rows k0+4 .. k0+7.  Every lane of the wave must take part.
+// second load covers rows k0+gap .. k0+gap+3 (gap 4: the next four rows; gap 8
+// pairs with the column order of the tile images).  Every lane of the wave must
+// take part.
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
-__device__ inline bf16x8 frag_col(const __bf16* t, int ld, int i, int k0) {
+__device__ inline bf16x8 frag_col(const __bf16* t, int ld, int i, int k0, int gap = 4) {
     const int j = threadIdx.x & 15;
     const __bf16* p = t + (k0 + (j >> 2)) * ld + (i - j) + 4 * (j & 3);
     typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4;
     const bf16x4v a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
-    const bf16x4v b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * ld));
+    const bf16x4v b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + gap * ld));
     bf16x8 x;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1399,16 +1402,18 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
 // writes the tile to LDS once as bf16 Qw^T; from there the pair's X_bc rows
 // go to memory as 16-byte chunks (read down Qw^T's columns by the transposing
 // load) and the transition Qw <- Qw - Qw E_c^T takes its Qw operand the same
-// way, with -E_c (bf16) from LDS, accumulating into the registers.
+// way, accumulating into the registers.  -E_c comes from the block's tile
+// image (bf16, the values the forward's scan uses), read straight from memory
+// as the other operand; its columns sit in the image's swap23 order, so the Qw
+// fragment pairs rows k0+4h .. +3 with rows k0+8+4h .. +3 to match.
 template <int D>
 __global__ void __launch_bounds__(256)
 bwd_chain_b16_kernel(int nb, int nsc, int slice0, const float* __restrict__ ql,
-                     const float* __restrict__ em, float* __restrict__ X) {
+                     const char* __restrict__ img, float* __restrict__ X) {
+    using I = Img<D>;
     constexpr int TN = D / 32, NT = (kB / 32) * TN;        // Qw tiles
-    constexpr int LQ = kB + 8, LE = D + 8;                  // LDS row strides (bf16)
-    constexpr int EU = (D * D / 4 + 255) / 256;             // E float4 units per thread
+    constexpr int LQ = kB + 8;                              // LDS row stride (bf16)
     __shared__ __attribute__((aligned(16))) __bf16 sQt[D * LQ];   // Qw^T [d][q]
-    __shared__ __attribute__((aligned(16))) __bf16 sE[D * LE];    // -E_c [d_out][d_in]
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, h = lane >> 5;
     const int b = nb - 1 - (int)(blockIdx.x / nsc), sl = (int)(blockIdx.x % nsc);
     const size_t slice = (size_t)slice0 + sl, npairs = (size_t)nb * (nb - 1) / 2;
@@ -1423,16 +1428,16 @@ bwd_chain_b16_kernel(int nb, int nsc, int slice0, const float* __restrict__ ql,
 #pragma unroll
             for (int j = 0; j < 4; ++j) qw[4 * i + j] = qlb[(m0 + 8 * i + 4 * h + j) * D + n0 + r];
     }
-    f32x4 pe[EU];
+    // the lane's -E_c operand: row d = n0 + r of the image's -E, one 16-byte
+    // unit per 16 columns (the lane half's 8 columns)
+    bf16x8 ef[D / 16];
     auto loadE = [&](int c) {
-        const float* e = em + (slice * nb + c) * D * D;
+        const char* ie = img + (slice * nb + c) * I::BYTES + I::OFF_E + (n0 + r) * I::RB_E;
 #pragma unroll
-        for (int u = 0; u < EU; ++u) {
-            const int idx = tid + 256 * u;
-            if (idx < D * D / 4) pe[u] = *reinterpret_cast<const f32x4*>(e + 4 * idx);
-        }
+        for (int kc = 0; kc < D / 16; ++kc)
+            ef[kc] = *reinterpret_cast<const bf16x8*>(ie + swz_unit(n0 + r, 2 * kc + h, I::RB_E) * 16);
     };
-    if (b - 1 >= 1) loadE(b - 1);
+    if (owner && b - 1 >= 1) loadE(b - 1);
     // the X_bc chunk a lane stores: 16 consecutive q per group of 16 lanes, 8 d
     constexpr int XP = (kB * D / 8) / 256;                    // fragment passes per wave
     for (int c = b - 1; c >= 0; --c) {
@@ -1442,19 +1447,7 @@ bwd_chain_b16_kernel(int nb, int nsc, int slice0, const float* __restrict__ ql,
                 *reinterpret_cast<bf16x4_t*>(sQt + (n0 + r) * LQ + m0 + 8 * i + 4 * h) =
                     bf16x4_t{(__bf16)qw[4 * i], (__bf16)qw[4 * i + 1], (__bf16)qw[4 * i + 2],
                              (__bf16)qw[4 * i + 3]};
-        if (c > 0)
-#pragma unroll
-            for (int u = 0; u < EU; ++u) {
-                const int idx = tid + 256 * u;
-                if (idx < D * D / 4) {
-                    const int row = (4 * idx) / D, col = (4 * idx) % D;
-                    *reinterpret_cast<bf16x4_t*>(sE + row * LE + col) =
-                        bf16x4_t{(__bf16)-pe[u][0], (__bf16)-pe[u][1], (__bf16)-pe[u][2],
-                                 (__bf16)-pe[u][3]};
-                }
-            }
-        __syncthreads();   // Qw^T and -E_c in LDS
-        if (c - 1 >= 1) loadE(c - 1);
+        __syncthreads();   // Qw^T in LDS
         {   // X_bc = Qw as bf16 rows [q][d]
             __bf16* xo = Xs + pair_index(b, c) * kB * D;
 #pragma unroll
@@ -1468,11 +1461,11 @@ bwd_chain_b16_kernel(int nb, int nsc, int slice0, const float* __restrict__ ql,
         if (c > 0 && owner) {
             // Qw(q, d) += sum_k Qw(q, k) (-E_c(d, k))
 #pragma unroll
-            for (int k0 = 0; k0 < D; k0 += 16) {
-                const bf16x8 a = frag_col(sQt, LQ, m0 + r, k0 + 8 * h);
-                const bf16x8 e = *reinterpret_cast<const bf16x8*>(sE + (n0 + r) * LE + k0 + 8 * h);
-                qw = mfma32(a, e, qw);
+            for (int kc = 0; kc < D / 16; ++kc) {
+                const bf16x8 a = frag_col(sQt, LQ, m0 + r, 16 * kc + 4 * h, 8);
+                qw = mfma32(a, ef[kc], qw);
             }
+            if (c - 1 >= 1) loadE(c - 1);
         }
         __syncthreads();   // every read of this step's LDS done
     }
@@ -1787,7 +1780,7 @@ hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
         if (nb > 1) {
             if constexpr (sizeof(T) == 2 && D >= 32)
                 hipLaunchKernelGGL((bwd_chain_b16_kernel<D>), dim3(nsc * (nb - 1)), dim3(256), 0,
-                                   st, nb, nsc, s0, a.fw.ql, (const float*)a.fw.em, a.X);
+                                   st, nb, nsc, s0, a.fw.ql, (const char*)a.img, a.X);
             else
                 hipLaunchKernelGGL((bwd_chain_kernel<D, PARTS>), dim3(nsc * (nb - 1)),
                                    dim3(256), 0, st, nb, nsc, s0, a.fw.ql, (const float*)a.fw.em,
