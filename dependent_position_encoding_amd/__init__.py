@@ -144,6 +144,34 @@ def _need(t: torch.Tensor, name: str, dev, shape=None, dtype=None):
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
 
 
+def _workspace(workspace, nbytes: int, dev):
+    """The caller's workspace if it is a large enough uint8 tensor on dev, else a new one."""
+    if workspace is not None:
+        _need(workspace, "workspace", dev, None, torch.uint8)
+        if workspace.numel() >= nbytes:
+            return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+
+
+_OPTIONAL = ("lse", "lse_t")  # the C calls accept NULL for these outputs
+
+
+def _outs(out, dev, specs):
+    """Validate caller-provided output tensors against (name, shape, dtype)
+    specs; shape None means the output must be absent."""
+    if len(out) != len(specs):
+        raise ValueError(f"out must hold {len(specs)} tensors, got {len(out)}")
+    for t, (name, shape, dtype) in zip(out, specs):
+        if t is None:
+            if shape is not None and name not in _OPTIONAL:
+                raise ValueError(f"out: {name} is required")
+            continue
+        if shape is None:
+            raise ValueError(f"out: {name} must be None here")
+        _need(t, name, dev, shape, dtype)
+    return out
+
+
 def _desc(N, H, L, d, dtype, scale, block=0):
     return _Desc(N, H, L, d, _dtype_code(dtype), float(scale), int(block))
 
@@ -193,16 +221,21 @@ def fwd(q, k, v, w, beta, logf=None, scale=None, cache: Cache | None = None,
     _need(beta, "beta", dev, (N, H, L), torch.float32)
     if logf is not None:
         _need(logf, "logf", dev, (N, H, L), torch.float32)
+    if cache is not None:
+        if (cache.N, cache.H, cache.d) != (N, H, d) or cache.dtype != q.dtype:
+            raise ValueError(f"cache is [{cache.N},{cache.H},cap,{cache.d}] {cache.dtype}, "
+                             f"inputs are [{N},{H},{L},{d}] {q.dtype}")
+        if cache.device != dev:
+            raise ValueError(f"cache must be on {dev}")
     scale = d ** -0.5 if scale is None else scale
     desc = _desc(N, H, L, d, q.dtype, scale, block)
     nbytes = int(lib.path_attn_fwd_workspace(ctypes.byref(desc), int(cache is not None)))
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, nbytes, dev)
     if out is None:
         o = torch.empty_like(q)
         lse = torch.empty(N, H, L, dtype=torch.float32, device=dev)
     else:
-        o, lse = out
+        o, lse = _outs(out, dev, [("o", (N, H, L, d), q.dtype), ("lse", (N, H, L), torch.float32)])
     cc = cache._c() if cache is not None else None
     args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf),
             _ptr(o), _ptr(lse), ctypes.byref(cc) if cc is not None else None,
@@ -240,14 +273,17 @@ def bwd(q, k, v, w, beta, logf, o, lse, do, scale=None, workspace=None, out=None
     scale = d ** -0.5 if scale is None else scale
     desc = _desc(N, H, L, d, q.dtype, scale)
     nbytes = int(lib.path_attn_bwd_workspace(ctypes.byref(desc)))
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, nbytes, dev)
     if out is None:
         dq, dk, dv, dw = (torch.empty_like(q) for _ in range(4))
         dbeta = torch.empty(N, H, L, dtype=torch.float32, device=dev)
         dlogf = torch.empty(N, H, L, dtype=torch.float32, device=dev) if logf is not None else None
     else:
-        dq, dk, dv, dw, dbeta, dlogf = out
+        full, row = (N, H, L, d), (N, H, L)
+        dq, dk, dv, dw, dbeta, dlogf = _outs(out, dev, [
+            ("dq", full, q.dtype), ("dk", full, q.dtype), ("dv", full, q.dtype),
+            ("dw", full, q.dtype), ("dbeta", row, torch.float32),
+            ("dlogf", row if logf is not None else None, torch.float32)])
     _check(lib.path_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta),
                              _ptr(logf), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
                              _ptr(dv), _ptr(dw), _ptr(dbeta), _ptr(dlogf), _ptr(workspace),
@@ -261,6 +297,14 @@ def _init_events(events, dev):
         if e.cuda_event == 0:
             e.record(torch.cuda.current_stream(dev))
     return events
+
+
+def _token_outs(N, H, d, dtype, dev, q_t, out):
+    """(o_t, lse_t) for one decode position: new tensors, or the caller's, validated."""
+    if out is None:
+        return (torch.empty_like(q_t),
+                torch.empty(N, H, dtype=torch.float32, device=dev))
+    return _outs(out, dev, [("o_t", (N, H, d), dtype), ("lse_t", (N, H), torch.float32)])
 
 
 def _cache_desc(cache: Cache, scale):
@@ -303,13 +347,8 @@ def decode(cache: Cache, n_keys: int, q_t, scale=None, workspace=None, out=None)
     scale = cache.d ** -0.5 if scale is None else scale
     desc = _cache_desc(cache, scale)
     nbytes = decode_workspace_bytes(cache, n_keys)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=cache.device)
-    if out is None:
-        o = torch.empty_like(q_t)
-        lse = torch.empty(cache.N, cache.H, dtype=torch.float32, device=cache.device)
-    else:
-        o, lse = out
+    workspace = _workspace(workspace, nbytes, cache.device)
+    o, lse = _token_outs(cache.N, cache.H, cache.d, cache.dtype, cache.device, q_t, out)
     cc = cache._c()
     _check(lib.path_decode(ctypes.byref(desc), ctypes.byref(cc), int(n_keys), _ptr(q_t),
                            _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
@@ -329,13 +368,8 @@ def decode_step(cache: Cache, n: int, q_t, k_t, v_t, w_t, beta_t, logf_t=None,
     scale = cache.d ** -0.5 if scale is None else scale
     desc = _cache_desc(cache, scale)
     nbytes = decode_workspace_bytes(cache, n + 1)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=cache.device)
-    if out is None:
-        o = torch.empty_like(q_t)
-        lse = torch.empty(cache.N, cache.H, dtype=torch.float32, device=cache.device)
-    else:
-        o, lse = out
+    workspace = _workspace(workspace, nbytes, cache.device)
+    o, lse = _token_outs(cache.N, cache.H, cache.d, cache.dtype, cache.device, q_t, out)
     cc = cache._c()
     _check(lib.path_decode_step(ctypes.byref(desc), ctypes.byref(cc), int(n), _ptr(q_t),
                                 _ptr(k_t), _ptr(v_t), _ptr(w_t), _ptr(beta_t), _ptr(logf_t),
@@ -401,13 +435,8 @@ def paged_decode_step(cache: PagedCache, page_table, seq_lens, max_keys, q_t, k_
     scale = d ** -0.5 if scale is None else scale
     desc = _desc(S, H, 1, d, cache.dtype, scale)
     nbytes = paged_decode_workspace_bytes(S, H, d, cache.dtype, max_keys)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=cache.device)
-    if out is None:
-        o = torch.empty_like(q_t)
-        lse = torch.empty(S, H, dtype=torch.float32, device=cache.device)
-    else:
-        o, lse = out
+    workspace = _workspace(workspace, nbytes, cache.device)
+    o, lse = _token_outs(S, H, d, cache.dtype, cache.device, q_t, out)
     pc = cache._c()
     _check(lib.path_paged_decode_step(ctypes.byref(desc), ctypes.byref(pc), _ptr(page_table),
                                       int(stride), _ptr(seq_lens), int(max_keys), _ptr(q_t),
@@ -424,6 +453,13 @@ def paged_import(src: Cache, dst: PagedCache, page_table, seq_lens, max_keys):
     S, stride = _paged_tables(dst, page_table, seq_lens, max_keys)
     if src.N != S or src.H != dst.H or src.d != dst.d:
         raise ValueError("source cache and paged cache shapes differ")
+    if src.dtype != dst.dtype or src.k_dtype != dst.k_dtype:
+        raise ValueError(f"source cache ({src.dtype}, keys {src.k_dtype}) and paged cache "
+                         f"({dst.dtype}, keys {dst.k_dtype}) dtypes differ")
+    if (src.gcache is None) != (dst.gpages is None):
+        raise ValueError("source cache and paged cache must both have a gate prefix or neither")
+    if src.device != dst.device:
+        raise ValueError("source cache and paged cache are on different devices")
     desc = _desc(S, dst.H, 1, dst.d, dst.dtype, 1.0)
     sc, pc = src._c(), dst._c()
     _check(lib.path_paged_import(ctypes.byref(desc), ctypes.byref(sc), ctypes.byref(pc),
@@ -443,7 +479,8 @@ def causal_attn(q, k, v, scale=None, out=None):
         o = torch.empty_like(q)
         lse = torch.empty(N, H, L, dtype=torch.float32, device=q.device)
     else:
-        o, lse = out
+        o, lse = _outs(out, q.device, [("o", (N, H, L, d), q.dtype),
+                                       ("lse", (N, H, L), torch.float32)])
     _check(lib.path_causal_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                     _ptr(lse), _stream(q.device)))
     return o, lse
@@ -480,14 +517,15 @@ def param_fwd(x, Wd, Wu, kc, ub, bb, uf=None, bf=None, H=None, d=None, workspace
         _need(bf, "bf", dev, (H,), torch.float32)
     desc = _ParamDesc(N, L, Dm, R, H, d, _dtype_code(x.dtype))
     nbytes = int(lib.path_param_workspace(ctypes.byref(desc), 1 if gate else 0))
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, nbytes, dev)
     if out is None:
         w = torch.empty(N, H, L, d, dtype=x.dtype, device=dev)
         beta = torch.empty(N, H, L, dtype=torch.float32, device=dev)
         logf = torch.empty(N, H, L, dtype=torch.float32, device=dev) if gate else None
     else:
-        w, beta, logf = out
+        w, beta, logf = _outs(out, dev, [("w", (N, H, L, d), x.dtype),
+                                         ("beta", (N, H, L), torch.float32),
+                                         ("logf", (N, H, L) if gate else None, torch.float32)])
     _check(lib.path_param_fwd(ctypes.byref(desc), _ptr(x), _ptr(Wd), _ptr(Wu), _ptr(kc), _ptr(ub),
                               _ptr(bb), _ptr(uf), _ptr(bf), _ptr(w), _ptr(beta), _ptr(logf),
                               _ptr(workspace), workspace.numel(), _stream(dev)))

@@ -965,7 +965,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t st) {
                        (const __bf16*)a.w, a.beta, a.logf, a.L, nb, scale2, a.ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.ev) hipEventRecord(a.ev[1], st);
+    if (a.ev && (e = hipEventRecord(a.ev[1], st)) != hipSuccess) return e;
     const int ngrid = a.N * a.H * ((nb + 1) / 2);
     if (a.logf)
         hipLaunchKernelGGL((scan_mfma_kernel<D, true>), dim3(ngrid), dim3(256), 0, st, a.L, nb,

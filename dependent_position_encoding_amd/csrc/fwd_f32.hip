@@ -291,7 +291,7 @@ static hipError_t launch_fwd_f32_t(const FwdArgs& a, hipStream_t st) {
                        a.L, nb, a.ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.ev) hipEventRecord(a.ev[1], st);
+    if (a.ev && (e = hipEventRecord(a.ev[1], st)) != hipSuccess) return e;
     hipLaunchKernelGGL((scan_f32_kernel<T, B, D>), dim3(nblk), dim3(256), 0, st,
                        (const T*)a.v, a.L, nb, a.scale, a.logf ? 1 : 0, a.ws,
                        (T*)a.o, a.lse);

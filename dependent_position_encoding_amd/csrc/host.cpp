@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <string.h>
 #include <string>
 
 #include "kernels.hpp"
@@ -28,7 +29,19 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-bool valid_dtype(path_dtype t) { return t == PATH_F32 || t == PATH_BF16; }
+// A C caller may store any int in an enum field; in C++ loading a value outside
+// the enumerators' range as the enum type is undefined, so the field's bytes
+// are read as an int before anything compares them.
+int raw_enum(const void* field) {
+    int v;
+    memcpy(&v, field, sizeof v);
+    return v;
+}
+
+bool valid_dtype(const path_dtype* t) {
+    const int v = raw_enum(t);
+    return v == PATH_F32 || v == PATH_BF16;
+}
 
 size_t esize(path_dtype t) { return t == PATH_F32 ? 4 : 2; }
 
@@ -43,7 +56,7 @@ path_status check_desc(const path_fwd_desc* d, bool need_L) {
     if (!d) return fail(PATH_E_NULL, "desc is NULL");
     if (d->N < 1 || d->H < 1 || (need_L && d->L < 1))
         return fail(PATH_E_SHAPE, "N, H and L must be >= 1");
-    if (!valid_dtype(d->dtype)) return fail(PATH_E_DTYPE, "unknown dtype");
+    if (!valid_dtype(&d->dtype)) return fail(PATH_E_DTYPE, "unknown dtype");
     if (d->d != 16 && d->d != 32 && d->d != 64)
         return fail(PATH_E_UNSUPPORTED, "head dim must be 16, 32 or 64");
     const int B = block_of(d);
@@ -97,7 +110,7 @@ path_status check_cache(const path_fwd_desc* d, const path_cache* c) {
     if (!c) return fail(PATH_E_NULL, "cache is NULL");
     if (!c->kcache || !c->vcache) return fail(PATH_E_NULL, "kcache/vcache is NULL");
     if (c->cap < 1) return fail(PATH_E_SHAPE, "cache capacity must be >= 1");
-    if (!valid_dtype(c->k_dtype)) return fail(PATH_E_DTYPE, "unknown kcache dtype");
+    if (!valid_dtype(&c->k_dtype)) return fail(PATH_E_DTYPE, "unknown kcache dtype");
     if (!aligned(c->kcache, 16) || !aligned(c->vcache, 16) || !aligned(c->gcache, 4))
         return fail(PATH_E_ALIGN, "cache pointers must be 16-byte aligned (gcache 4)");
     (void)d;
@@ -172,7 +185,7 @@ path_status check_param(const path_param_desc* d) {
     if (!d) return fail(PATH_E_NULL, "desc is NULL");
     if (d->N < 1 || d->L < 1 || d->H < 1 || d->Dm < 1 || d->R < 1)
         return fail(PATH_E_SHAPE, "N, L, H, Dm and R must be >= 1");
-    if (!valid_dtype(d->dtype)) return fail(PATH_E_DTYPE, "unknown dtype");
+    if (!valid_dtype(&d->dtype)) return fail(PATH_E_DTYPE, "unknown dtype");
     if (d->d != 16 && d->d != 32 && d->d != 64)
         return fail(PATH_E_UNSUPPORTED, "head dim must be 16, 32 or 64");
     if (d->Dm % 16 != 0) return fail(PATH_E_UNSUPPORTED, "Dm must be a multiple of 16");
@@ -199,7 +212,7 @@ extern "C" {
 int path_abi_version(void) { return PATH_ATTN_ABI_VERSION; }
 
 const char* path_status_str(path_status s) {
-    switch (s) {
+    switch (raw_enum(&s)) {
         case PATH_OK: return "ok";
         case PATH_E_NULL: return "null pointer";
         case PATH_E_SHAPE: return "bad shape";
@@ -263,15 +276,19 @@ static path_status fwd_impl(const path_fwd_desc* desc, const void* q, const void
         a.ws.grp = reinterpret_cast<float*>(base + lay.grp);
     }
     a.ev = ev;
-    if (ev) hipEventRecord(ev[0], stream);
-    hipError_t e = use_mfma(desc) ? pa::launch_fwd_bf16(a, stream) : pa::launch_fwd_f32(a, stream);
+    hipError_t e = hipSuccess;
+    if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess)
+        return launched(e, "path_attn_fwd_timed (event 0)");
+    e = use_mfma(desc) ? pa::launch_fwd_bf16(a, stream) : pa::launch_fwd_f32(a, stream);
     if (e != hipSuccess) return launched(e, "path_attn_fwd");
-    if (ev) hipEventRecord(ev[2], stream);
+    if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess)
+        return launched(e, "path_attn_fwd_timed (event 2)");
     if (cache_out) {
         e = pa::launch_kv_align(a, cache_args(desc, cache_out), stream);
         if (e != hipSuccess) return launched(e, "path_attn_fwd (cache alignment)");
     }
-    if (ev) hipEventRecord(ev[3], stream);
+    if (ev && (e = hipEventRecord(ev[3], stream)) != hipSuccess)
+        return launched(e, "path_attn_fwd_timed (event 3)");
     return ok();
 }
 
@@ -386,7 +403,7 @@ static path_status check_paged(const path_fwd_desc* d, const path_paged_cache* c
     if (!c) return fail(PATH_E_NULL, "paged cache is NULL");
     if (!c->kpages || !c->vpages) return fail(PATH_E_NULL, "kpages/vpages is NULL");
     if (!table || !seq_lens) return fail(PATH_E_NULL, "page_table and seq_lens are required");
-    if (!valid_dtype(c->k_dtype)) return fail(PATH_E_DTYPE, "unknown kpages dtype");
+    if (!valid_dtype(&c->k_dtype)) return fail(PATH_E_DTYPE, "unknown kpages dtype");
     int l = 0;
     while (l < 8 && (1 << l) != c->page_size) ++l;
     if (l < 4 || l > 7) return fail(PATH_E_UNSUPPORTED, "page_size must be 16, 32, 64 or 128");

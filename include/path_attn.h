@@ -203,7 +203,10 @@ path_status path_decode(const path_fwd_desc *desc, const path_cache *cache,
                         int n_keys, const void *q_t, void *o_t, float *lse_t,
                         void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* One fused decode step at position t = n (n keys already cached, n < cap):
+/* One fused decode step at position t = n (n keys already cached, n < cap)
+ * [Notes s2.8, eq. (1) of the paper: every cached key is rewritten by the new
+ * transition, the new key enters unrewritten, and a plain softmax over the
+ * cache then gives the PaTH(-FoX) logits of query t; Explainer s3]:
  * path_kv_update(n, w_t, beta_t), path_kv_append(n, k_t, v_t, logf_t) and
  * path_decode(n + 1, q_t) in one pass over the cache.  Afterwards the cache
  * holds n + 1 keys.  logf_t may be NULL only if gcache is NULL.

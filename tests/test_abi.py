@@ -186,3 +186,77 @@ def test_paged_argument_errors():
     st = lib.path_paged_import(ctypes.byref(d), ctypes.byref(src), ctypes.byref(_paged(pa)),
                                None, 4, FAKE, 256, None)
     assert st == 1
+
+
+def _bwd_args(pa, lib, d, **kw):
+    """Arguments of path_attn_bwd: every tensor a fake aligned pointer unless overridden."""
+    names = ("q", "k", "v", "w", "beta", "logf", "o", "lse", "dout", "dq", "dk", "dv", "dw",
+             "dbeta", "dlogf", "ws")
+    ws_bytes = kw.pop("ws_bytes", 1 << 40)
+    return [ctypes.byref(d) if d is not None else None] + [kw.get(n, FAKE) for n in names] + [
+        ws_bytes, None]
+
+
+def test_bwd_argument_errors():
+    pa, lib = _lib()
+    d = _desc(pa, N=2, H=3, L=200)
+    need = lib.path_attn_bwd_workspace(ctypes.byref(d))
+    assert need > 0 and need % 256 == 0
+    # block must be 64 for the backward; invalid descriptions size to 0
+    for kw in (dict(block=32, dtype=pa.PATH_F32), dict(N=0), dict(d=48), dict(dtype=9)):
+        assert lib.path_attn_bwd_workspace(ctypes.byref(_desc(pa, **kw))) == 0, kw
+    assert lib.path_attn_bwd_workspace(None) == 0
+    assert lib.path_attn_bwd(*_bwd_args(pa, lib, None)) == 1
+    assert lib.path_attn_bwd(*_bwd_args(pa, lib, _desc(pa, block=32, dtype=pa.PATH_F32))) == 4
+    assert lib.path_attn_bwd(*_bwd_args(pa, lib, _desc(pa, d=128))) == 4
+    assert lib.path_attn_bwd(*_bwd_args(pa, lib, _desc(pa, L=0))) == 2
+    assert lib.path_attn_bwd(*_bwd_args(pa, lib, _desc(pa, dtype=9))) == 3
+    for n in ("q", "k", "v", "w", "beta", "o", "lse", "dout", "dq", "dk", "dv", "dw", "dbeta"):
+        assert lib.path_attn_bwd(*_bwd_args(pa, lib, d, **{n: None})) == 1, n
+    # the gate input and its gradient come together
+    assert lib.path_attn_bwd(*_bwd_args(pa, lib, d, logf=None)) == 1
+    assert lib.path_attn_bwd(*_bwd_args(pa, lib, d, dlogf=None)) == 1
+    odd16 = ctypes.c_void_p((1 << 20) + 8)
+    odd4 = ctypes.c_void_p((1 << 20) + 2)
+    for n in ("q", "k", "v", "w", "o", "dout", "dq", "dk", "dv", "dw"):
+        assert lib.path_attn_bwd(*_bwd_args(pa, lib, d, **{n: odd16})) == 5, n
+    for n in ("beta", "logf", "lse", "dbeta", "dlogf"):
+        assert lib.path_attn_bwd(*_bwd_args(pa, lib, d, **{n: odd4})) == 5, n
+    assert lib.path_attn_bwd(*_bwd_args(pa, lib, d, ws=None, ws_bytes=need)) == 6
+    assert lib.path_attn_bwd(*_bwd_args(pa, lib, d, ws_bytes=need - 1)) == 6
+    assert lib.path_attn_bwd(*_bwd_args(pa, lib, d, ws=ctypes.c_void_p((1 << 20) + 128),
+                                        ws_bytes=need)) == 5
+    assert lib.path_last_error()
+
+
+def test_causal_argument_errors():
+    pa, lib = _lib()
+    call = lambda d, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None: lib.path_causal_attn_fwd(
+        ctypes.byref(d) if d is not None else None, q, k, v, o, lse, None)
+    assert call(None) == 1
+    assert call(_desc(pa), q=None) == 1
+    assert call(_desc(pa), o=None) == 1
+    assert call(_desc(pa, N=0)) == 2
+    assert call(_desc(pa, dtype=9)) == 3
+    assert call(_desc(pa, dtype=pa.PATH_F32)) == 4      # baseline is bf16 only
+    assert call(_desc(pa, d=16)) == 4                   # head dim 32 or 64
+    assert call(_desc(pa), v=ctypes.c_void_p((1 << 20) + 8)) == 5
+    assert lib.path_last_error()
+
+
+def test_fwd_timed_argument_errors():
+    pa, lib = _lib()
+    d = _desc(pa)
+    need = lib.path_attn_fwd_workspace(ctypes.byref(d), 0)
+    args = [ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, need, None]
+    assert lib.path_attn_fwd_timed(*args, None) == 1
+    evs = (ctypes.c_void_p * 4)(1, 2, 0, 4)           # one event missing
+    assert lib.path_attn_fwd_timed(*args, evs) == 1
+    evs = (ctypes.c_void_p * 4)(1, 2, 3, 4)           # never recorded: validation fails first
+    bad = list(args)
+    bad[0] = ctypes.byref(_desc(pa, d=48))
+    assert lib.path_attn_fwd_timed(*bad, evs) == 4
+    bad = list(args)
+    bad[11] = need - 1
+    assert lib.path_attn_fwd_timed(*bad, evs) == 6
+    assert lib.path_last_error()

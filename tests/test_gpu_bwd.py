@@ -105,6 +105,26 @@ def test_bwd_bf16(fox):
     _run(wl, L=150)
 
 
+@pytest.mark.parametrize("fox", [False, True])
+def test_bwd_bf16_head_dim_32(fox):
+    """Head dim 32 (the flip-flop layer's) on the matrix-core backward kernels:
+    five blocks, the last one ragged, with and without the gate."""
+    wl = workloads.CONFIGS["flipflop"].replace(N=2, H=2, fox=fox)
+    _run(wl, L=300, seed=4)
+
+
+def test_bwd_bf16_flipflop_full_shape():
+    """The flip-flop layer's full shape (16 x 2 heads, L = 512, d = 32)."""
+    _run(workloads.CONFIGS["flipflop"], L=512, seed=5)
+
+
+@pytest.mark.parametrize("fox", [False, True])
+def test_bwd_bf16_head_dim_16(fox):
+    """Head dim 16 (generic kernels, bf16 data): four blocks, ragged."""
+    wl = workloads.CONFIGS["fox"].replace(N=1, H=2, d=16, qk_std=16 ** -0.25, fox=fox)
+    _run(wl, L=200, seed=6)
+
+
 def test_bwd_bf16_ragged_slice_group():
     # 20 slices: the pair kernels take slices 16 at a time, so one full group
     # and one of 4; a ragged sequence tail as well

@@ -186,7 +186,8 @@ def test_long_context_full_size():
 
 @pytest.mark.parametrize("k_dtype", [torch.bfloat16, torch.float32])
 def test_long_context_stress_full_size(k_dtype):
-    _long_case(workloads.stress(workloads.CONFIGS["long"]), k_dtype, head_stride=4)
+    """The near-reflection stress variant: all 32 heads x 256 decode steps."""
+    _long_case(workloads.stress(workloads.CONFIGS["long"]), k_dtype)
 
 
 def test_decode_steps_replayed_from_a_graph():

@@ -94,14 +94,52 @@ def _sample_rows(L, n, seed):
     return np.unique(np.concatenate([fixed, rng.integers(0, L, n - len(fixed))]))
 
 
-def test_lm_bf16_sampled():
+def _rows_per_head(L, heads, n, seed):
+    """[len(heads), n] query rows: 0, 63, 64 and L - 1 in every head, the rest
+    drawn per head (so the sampled rows of different heads hit different
+    query blocks)."""
+    rng = np.random.default_rng(seed)
+    fixed = np.array([0, 63, 64, L - 1])
+    out = np.empty((len(heads), n), dtype=np.int64)
+    for i in range(len(heads)):
+        rest = rng.choice(np.setdiff1d(np.arange(L), fixed), n - len(fixed), replace=False)
+        out[i] = np.sort(np.concatenate([fixed, rest]))
+    return out
+
+
+def _check_full_size(name, x, o, lse, scale, full_heads, sampled_heads, rows):
+    """Full heads (every row) and sampled rows of other heads against the oracle."""
+    f64 = {k: (workloads.as_slices_f64(v, full_heads) if v is not None else None)
+           for k, v in x.items()}
+    ro, rl = oracle.fwd_rows(f64["q"], f64["k"], f64["v"], f64["w"], f64["beta"], f64["logf"],
+                             scale)
+    check(f"{name} full heads {full_heads} o", workloads.as_slices_f64(o, full_heads), ro, bf16=True)
+    check(f"{name} full heads lse", workloads.as_slices_f64(lse, full_heads), rl, bf16=True)
+    f64 = {k: (workloads.as_slices_f64(v, sampled_heads) if v is not None else None)
+           for k, v in x.items()}
+    ro, rl = oracle.fwd_rows(f64["q"], f64["k"], f64["v"], f64["w"], f64["beta"], f64["logf"],
+                             scale, rows=rows)
+    idx = np.arange(len(sampled_heads))[:, None]
+    go = workloads.as_slices_f64(o, sampled_heads)[idx, rows]
+    gl = workloads.as_slices_f64(lse, sampled_heads)[idx, rows]
+    check(f"{name} {len(sampled_heads)} heads x {rows.shape[1]} rows o", go, ro, bf16=True)
+    check(f"{name} {len(sampled_heads)} heads x {rows.shape[1]} rows lse", gl, rl, bf16=True)
+
+
+def test_lm_bf16_full_size():
+    """The LM-layer workload at full size (4 x 24 heads, L = 4096, d = 64):
+    4 heads checked on every row, and 64 rows (0, 63, 64, L - 1 and 60 drawn
+    per head) of all 96 heads."""
+    pa = _pa()
     wl = workloads.CONFIGS["lm"]
+    x = workloads.make_inputs(wl, device=DEV)
+    print(f"case lm full {tuple(x['q'].shape)}", flush=True)
+    o, lse = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], logf=None, scale=wl.scale)
+    torch.cuda.synchronize()
     NH = wl.N * wl.H
-    heads = list(range(0, NH, 8))
-    rows = _sample_rows(wl.L, 48, 3)
-    go, gl, ro, rl = _run(wl, heads=heads, rows=rows)
-    check("lm o", go, ro, bf16=True)
-    check("lm lse", gl, rl, bf16=True)
+    heads = list(range(NH))
+    _check_full_size("lm", x, o, lse, wl.scale, [0, 37, 58, NH - 1], heads,
+                     _rows_per_head(wl.L, heads, 64, 3))
 
 
 def test_lm_bf16_scale_rsqrt_d():
@@ -111,16 +149,6 @@ def test_lm_bf16_scale_rsqrt_d():
     check("lm 1/sqrt(d) lse", gl, rl, bf16=True)
 
 
-@pytest.mark.parametrize("L", [2048])
-def test_fox_bf16_sampled(L):
-    wl = workloads.CONFIGS["fox"].replace(L=L)
-    heads = list(range(5, wl.N * wl.H, 64))
-    rows = _sample_rows(L, 48, 4)
-    go, gl, ro, rl = _run(wl, heads=heads, rows=rows)
-    check(f"fox L={L} o", go, ro, bf16=True)
-    check(f"fox L={L} lse", gl, rl, bf16=True)
-
-
 def test_bf16_ragged_and_stress():
     wl = workloads.stress(workloads.CONFIGS["fox"].replace(N=2, H=2, L=777))
     go, gl, ro, rl = _run(wl)
@@ -128,22 +156,22 @@ def test_bf16_ragged_and_stress():
     check("bf16 ragged stress lse", gl, rl, bf16=True)
 
 
-@pytest.mark.parametrize("L", [4096, 8192])
-def test_fox_bf16_full_size_sampled(L):
-    """The benchmark's FoX shapes (32 x 32 heads) with inputs drawn on the GPU."""
+@pytest.mark.parametrize("L", [2048, 4096, 8192])
+def test_fox_bf16_full_size(L):
+    """PaTH-FoX at the kernel-timing figure's shape (32 x 32 heads, d = 64)
+    at L = 2048, 4096 and 8192, inputs drawn on the GPU: 16 heads x 64 rows
+    (0, 63, 64, L - 1 and 60 drawn per head) and one head on every row."""
     pa = _pa()
     wl = workloads.CONFIGS["fox"].replace(L=L)
     x = workloads.make_inputs(wl, device=DEV)
     print(f"case fox full L={L}", flush=True)
     o, lse = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], logf=x["logf"], scale=wl.scale)
     torch.cuda.synchronize()
-    heads = list(range(7, wl.N * wl.H, 128))
-    rows = _sample_rows(L, 32, L)
-    f64 = {k: workloads.as_slices_f64(v, heads) for k, v in x.items()}
-    ro, rl = oracle.fwd_rows(f64["q"], f64["k"], f64["v"], f64["w"], f64["beta"], f64["logf"],
-                             wl.scale, rows=rows)
-    check(f"fox full L={L} o", workloads.as_slices_f64(o, heads)[:, rows], ro, bf16=True)
-    check(f"fox full L={L} lse", workloads.as_slices_f64(lse, heads)[:, rows], rl, bf16=True)
+    NH = wl.N * wl.H
+    heads = sorted(np.random.default_rng(L).choice(NH, 16, replace=False).tolist())
+    full = [int(np.random.default_rng(L + 1).integers(NH))]
+    _check_full_size(f"fox L={L}", x, o, lse, wl.scale, full, heads,
+                     _rows_per_head(L, heads, 64, L + 2))
 
 
 @pytest.mark.parametrize("name,L,d", [("flipflop", 512, 32), ("lm", 1000, 64), ("lm", 4096, 64)])
