@@ -623,7 +623,7 @@ enum { sU_, sX_, sM_, sY_, sP_, sR_, sdP_, sdR_, sdY_, sdM_, sdU_, sdX_, sTmp_, 
        sdT_, sAA_ };
 
 template <typename T, int D, int PARTS>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_precond_kernel(int L, int nb, int slice0, const T* __restrict__ q, const T* __restrict__ k,
                    const T* __restrict__ w, const float* __restrict__ beta,
                    const float* __restrict__ dQl, const float* __restrict__ dKr,
@@ -727,14 +727,20 @@ bwd_precond_kernel(int L, int nb, int slice0, const T* __restrict__ q, const T* 
                 [&](int m, int n, float val) { g(sdU_)[m * kB + n] += val; });
     // (the last term also takes U = T diag(beta) into dbeta: dbeta_j += sum_a T_aj dU_aj)
     gemm<F, F, kB>(kB, kB, gs(sX_), gs(sdP_), [&](int m, int n, float val) {
-        const float du = n <= m ? g(sdU_)[m * kB + n] + val : 0.f;
-        g(sdU_)[m * kB + n] = du;
-        if (n <= m) atomicAdd(&sdB[n], sT[m * kLdB + n] * du);
+        g(sdU_)[m * kB + n] = n <= m ? g(sdU_)[m * kB + n] + val : 0.f;
     });
     // dX = lower(dP U^T)
     gemm<F, F, kB>(kB, kB, gc(sdP_), gc(sU_),
                [&](int m, int n, float val) { g(sdX_)[m * kB + n] = n <= m ? val : 0.f; });
     __syncthreads();
+    // dbeta_n = sum_m T_mn dU_mn, one thread per n summing in row order (a
+    // fixed order, so the result does not depend on how waves are scheduled)
+    if (tid < kB) {
+        float acc = 0.f;
+#pragma unroll 1
+        for (int m = tid; m < kB; ++m) acc += sT[m * kLdB + tid] * g(sdU_)[m * kB + tid];
+        sdB[tid] = acc;
+    }
     // dT = dU diag(beta)
     for (int e = tid; e < kB * kB; e += 256) g(sdT_)[e] = g(sdU_)[e] * sBeta[e % kB];
     __syncthreads();
@@ -744,11 +750,16 @@ bwd_precond_kernel(int L, int nb, int slice0, const T* __restrict__ q, const T* 
     __syncthreads();
     // (G_ij = beta_i (w_i . w_j), i > j: dbeta_i += sum_j dG_ij (W W^T)_ij)
     gemm<F, F, kB>(kB, kB, strd(sT, kLdB), gs(sTmp_), [&](int m, int n, float val) {
-        const float dg = n < m ? -val : 0.f;
-        g(sdG_)[m * kB + n] = dg;
-        if (n < m) atomicAdd(&sdB[m], dg * g(sWW_)[m * kB + n]);
+        g(sdG_)[m * kB + n] = n < m ? -val : 0.f;
     });
     __syncthreads();
+    // dbeta_m += sum_{n<m} dG_mn (W W^T)_mn, one thread per m in column order
+    if (tid < kB) {
+        float acc = 0.f;
+#pragma unroll 1
+        for (int n = 0; n < tid; ++n) acc += g(sdG_)[tid * kB + n] * g(sWW_)[tid * kB + n];
+        sdB[tid] += acc;
+    }
     // the symmetric weight A + A^T, A = diag(beta) dG, for dW
     for (int e = tid; e < kB * kB; e += 256) {
         const int m = e / kB, n = e % kB;
@@ -1000,7 +1011,8 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sZ;     // A_{c-1} [query][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sdO;    // dO_b [query][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, kB, 1> sPT;   // P^T, then dS^T [key][query] (bf16)
-    __shared__ float sLse[kB], sDel[kB], sGb[kB], sGc[kB], sCol[kB];
+    __shared__ float sLse[kB], sDel[kB], sGb[kB], sGc[kB];
+    __shared__ float sColW[4][32];   // per (wave, lane) column sums of dS
     // log2-unit logit terms of the off-diagonal steps: per query row
     // (gate, shift, -lse; -inf past the sequence end) and per key (-gate)
     __shared__ __attribute__((aligned(16))) float sRow2[kB];
@@ -1036,7 +1048,6 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     if (tid < kB) {
         sGc[tid] = fox ? fw.gl[blk_c * kB + tid] : 0.f;
         sCol2[tid] = -sGc[tid] * kLog2e;
-        sCol[tid] = 0.f;
     }
     // prefetch of query block b's X_bc, Z_bc (4 x 4 bf16 blocks), dO and row terms
     bf16x4_t pX[4], pZ[4];
@@ -1158,12 +1169,15 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         if (c * kB + m < L) dv[(base + c * kB + m) * D + n] = from_f32<bf16>(val);
     });
     for_acc(D, D, accE, [&](int m, int n, float val) { dEm[blk_c * D * D + m * D + n] = -val; });
-    {   // the lane's key column of the (query x key) dS tiles
+    {   // the lane's key column of the (query x key) dS tiles: the column's
+        // two lane halves, then its two waves, are added pairwise (a + b =
+        // b + a), so the sum does not depend on the order the waves run in
         const int lane = tid & 63, wave = tid >> 6;
-        atomicAdd(&sCol[(wave % 2) * 32 + (lane & 31)], colAcc);
+        const float both = colAcc + __shfl_xor(colAcc, 32, 64);
+        if (lane < 32) sColW[wave][lane] = both;
     }
     __syncthreads();
-    if (tid < kB) colsum[blk_c * kB + tid] = sCol[tid];
+    if (tid < kB) colsum[blk_c * kB + tid] = sColW[tid / 32][tid % 32] + sColW[tid / 32 + 2][tid % 32];
 }
 
 // query, bf16: for query block b, left to right over the key blocks c < b.
@@ -1187,7 +1201,8 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     __shared__ __attribute__((aligned(16))) BTile<D, D, 1> sE;      // E_c [d][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sA;     // A_{c-1} [query][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, kB, 1> sS;    // P, then dS [query][key] (bf16)
-    __shared__ float sLse[kB], sDel[kB], sGb[kB], sGc[kB], sRow[kB];
+    __shared__ float sLse[kB], sDel[kB], sGb[kB], sGc[kB];
+    __shared__ float sRowW[4][32];   // per (wave, lane) row sums of dS
     // log2-unit logit terms of the off-diagonal steps: per query row (gate,
     // -lse; -inf past the sequence end) and per key of the current block (-gate)
     __shared__ float sRowB[kB];
@@ -1228,7 +1243,6 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         sLse[tid] = pos < L ? lse[base + pos] : 0.f;
         sGb[tid] = fox ? fw.gl[blk_b * kB + tid] : 0.f;
         sRowB[tid] = pos < L ? (sGb[tid] - sLse[tid]) * kLog2e : -INFINITY;
-        sRow[tid] = 0.f;
         delta[blk_b * kB + tid] = dl;
     }
     if (tid == 0) {
@@ -1390,9 +1404,13 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
             *reinterpret_cast<f32x4*>(qo + mA + 8 * i + 4 * h) =
                 f32x4{At[4 * i], At[4 * i + 1], At[4 * i + 2], At[4 * i + 3]};
     }
-    atomicAdd(&sRow[(wave % 2) * 32 + (lane & 31)], rowAcc);   // the lane's query column
+    {   // the lane's query column: lane halves, then the two waves of the
+        // column, added pairwise (order-independent, as for the key pass)
+        const float both = rowAcc + __shfl_xor(rowAcc, 32, 64);
+        if (lane < 32) sRowW[wave][lane] = both;
+    }
     __syncthreads();
-    if (tid < kB) rowsum[blk_b * kB + tid] = sRow[tid];
+    if (tid < kB) rowsum[blk_b * kB + tid] = sRowW[tid / 32][tid % 32] + sRowW[tid / 32 + 2][tid % 32];
 }
 
 // ---------------------------------------------------------------------------
@@ -1544,7 +1562,10 @@ bwd_precond_b16_kernel(int L, int nb, int slice0, const bf16* __restrict__ q,
                        float* __restrict__ dbeta) {
     static_assert(D == 32 || D == 64, "bf16 tiles");
     __shared__ __attribute__((aligned(16))) __bf16 sl[kSlots * kSlot];
-    __shared__ float sBeta[kB], sdB[kB];
+    __shared__ float sBeta[kB];
+    // dbeta partials: per (tile row, column) of the dU term and per (tile
+    // column, row) of the dG term, summed in a fixed order at the end
+    __shared__ float sDbU[2][kB], sDbG[2][kB];
     const int tid = threadIdx.x;
     const int c = (int)(blockIdx.x % nb), sli = (int)(blockIdx.x / nb);
     const size_t slice = (size_t)slice0 + sli, blk = slice * nb + c, base = slice * L;
@@ -1591,7 +1612,6 @@ bwd_precond_b16_kernel(int L, int nb, int slice0, const bf16* __restrict__ q,
     if (tid < kB) {
         const int pos = c * kB + tid;
         sBeta[tid] = pos < L ? beta[base + pos] : 0.f;
-        sdB[tid] = 0.f;
     }
     __syncthreads();
 
@@ -1691,11 +1711,17 @@ bwd_precond_b16_kernel(int L, int nb, int slice0, const bf16* __restrict__ q,
         f32x16 acc = tprod<true, true, kB>(sX, sDp, m0, n0, zero16());
         acc = tprod<false, false, kB>(sDr, sM, m0, n0, acc);
         acc = tprod<false, false, D>(sW, sDy, m0, n0, acc);
+        // dbeta_n: the lane sums its 16 rows of column n in a fixed order,
+        // the two lane halves of the column are added (a + b = b + a), and
+        // the tile's partial goes to its own slot: no order-dependent atomics
+        float part = 0.f;
         for_tile(t, kB, acc, [&](int m, int n, float v) {
             const float du = n <= m ? v : 0.f;
             put_bf(sDt, m, n, du * sBeta[n]);
-            if (n <= m) atomicAdd(&sdB[n], (float)sT[m * kLT + n] * du);
+            part += (float)sT[m * kLT + n] * du;
         });
+        part += __shfl_xor(part, 32, 64);
+        if ((threadIdx.x & 63) < 32) sDbU[t / 2][(t % 2) * 32 + (threadIdx.x & 31)] = part;
     }
     __syncthreads();
     // ---- 8. Tmp = dT T^T
@@ -1713,12 +1739,30 @@ bwd_precond_b16_kernel(int L, int nb, int slice0, const bf16* __restrict__ q,
 #pragma unroll
         for (int e = 0; e < 16; ++e) dgv[e] = -g[e];
         int e = 0;
+        f32x16 prod;
         for_tile(t, kB, dgv, [&](int m, int n, float v) {
             const float dg = n < m ? v : 0.f;
             fdG[m * kLdB + n] = dg;
-            if (n < m) atomicAdd(&sdB[m], dg * ww[e]);
+            prod[e] = dg * ww[e];
             ++e;
         });
+        // dbeta_m: each of the lane's 16 rows summed over the tile's 32 columns
+        // by an xor butterfly (every lane ends with the same, order-fixed sum)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float r = prod[i];
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) r += __shfl_xor(r, off, 64);
+            prod[i] = r;
+        }
+        const int lane = threadIdx.x & 63;
+        if ((lane & 31) == 0) {
+            const int m0 = (t / 2) * 32, h = lane >> 5;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sDbG[t % 2][m0 + 8 * i + 4 * h + j] = prod[4 * i + j];
+        }
     }
     if (qt >= 0) {
         aQ = tprod<false, true, kB>(sDx, sW, qm0, qn0, aQ);
@@ -1752,7 +1796,8 @@ bwd_precond_b16_kernel(int L, int nb, int slice0, const bf16* __restrict__ q,
         });
     }
     __syncthreads();
-    if (tid < kB && c * kB + tid < L) dbeta[base + c * kB + tid] = sdB[tid];
+    if (tid < kB && c * kB + tid < L)
+        dbeta[base + c * kB + tid] = (sDbU[0][tid] + sDbU[1][tid]) + (sDbG[0][tid] + sDbG[1][tid]);
 }
 
 template <typename T, int D, int PARTS>

@@ -10,7 +10,7 @@
   beta_0 never reach any output: changing them must leave o, lse and the
   aligned decode cache bit for bit unchanged.  log f_0 never reaches an
   output either, but the kernels add gate prefixes that include it and
-  subtract them again, so it changes results only by rounding.
+  subtract them again, so there the check is against the oracle's bar.
 """
 import numpy as np
 import pytest
@@ -65,13 +65,14 @@ def test_beta_zero_bf16_is_causal_attention(fox):
     x = _with_beta(workloads.make_inputs(wl, L=wl.L), 0.0)
     o, lse, g = _fwd_vs_oracle(f"beta=0 bf16 fox={fox}", wl, x)
     if not fox:
+        # The two kernels round the probabilities to bf16 against their own
+        # running maxima (and sum those rounded values into lse), so they
+        # agree to the bf16 bar, not bit for bit.
         co, cl = _pa().causal_attn(g["q"], g["k"], g["v"], scale=wl.scale)
         torch.cuda.synchronize()
-        d_o = (o.float() - co.float()).abs()
-        # at most one bf16 rounding step apart: an ulp of x is <= 2^-7 |x|
-        assert bool((d_o <= 2.0 ** -7 * co.float().abs() + 1e-30).all()), d_o.max().item()
-        assert d_o.sum().item() / co.float().abs().sum().item() < 1e-3
-        assert (lse - cl).abs().max().item() < 1e-4
+        check("beta=0 PaTH vs causal kernel o", o.float().cpu().numpy(), co.float().cpu().numpy(),
+              bf16=True)
+        check("beta=0 PaTH vs causal kernel lse", lse.cpu().numpy(), cl.cpu().numpy(), bf16=True)
 
 
 @pytest.mark.parametrize("d", [16, 64])
@@ -152,7 +153,7 @@ def _prefill_with_cache(x, wl):
 def test_first_transition_never_matters(cfg, dtype, d):
     """w_0 and beta_0 are on no path (H_j is excluded from key j's path and
     key 0 is the first), so changing them leaves o, lse and the aligned cache
-    bit-identical; the gate's log f_0 changes them by rounding only."""
+    bit-identical; the gate's log f_0 is checked against the oracle."""
     wl = workloads.CONFIGS[cfg].replace(N=2, H=2, L=300, d=d, dtype=dtype, fox=True)
     x = workloads.make_inputs(wl, L=wl.L)
     print(f"case first transition {cfg} {dtype} d={d}", flush=True)
@@ -169,13 +170,16 @@ def test_first_transition_never_matters(cfg, dtype, d):
         assert torch.equal(l0, l1), f"lse depends on w_0/beta_0 (beta_0 = {beta0})"
         assert torch.equal(c0.kcache, c1.kcache), "cached keys depend on w_0/beta_0"
         assert torch.equal(c0.vcache, c1.vcache) and torch.equal(c0.gcache, c1.gcache)
+    # log f_0 far outside its usual range: the kernels' block-relative gate
+    # sums carry it and cancel it, so the result must still meet the bar
+    # against the oracle (which never reads log f_0)
     y = dict(x)
     y["logf"] = x["logf"].clone()
     y["logf"][:, :, 0] = -7.5
     o2, l2, _ = _prefill_with_cache(y, wl)
-    d_o = (o2.float() - o0.float()).abs()
-    if dtype == torch.bfloat16:    # at most one bf16 rounding step: <= 2^-7 |x|
-        assert bool((d_o <= 2.0 ** -7 * o0.float().abs() + 1e-30).all()), d_o.max().item()
-    else:
-        assert d_o.max().item() <= 1e-5
-    assert (l2 - l0).abs().max().item() <= 1e-4
+    f64 = {k: workloads.as_slices_f64(v) for k, v in x.items()}
+    ro, rl = oracle.fwd_rows(f64["q"], f64["k"], f64["v"], f64["w"], f64["beta"], f64["logf"],
+                             wl.scale)
+    bf = dtype == torch.bfloat16
+    check("log f_0 = -7.5 o", workloads.as_slices_f64(o2), ro, bf16=bf)
+    check("log f_0 = -7.5 lse", workloads.as_slices_f64(l2), rl, bf16=bf)
