@@ -69,7 +69,7 @@ EXPORTS = ["path_abi_version", "path_status_str", "path_last_error",
            "path_decode_step", "path_causal_attn_fwd", "path_attn_fwd_timed",
            "path_param_workspace", "path_param_fwd", "path_attn_bwd_workspace",
            "path_attn_bwd", "path_paged_decode_workspace", "path_paged_decode_step",
-           "path_paged_import"]
+           "path_paged_import", "path_decode_step_noalloc", "path_decode_step_noalloc_limit"]
 
 
 def load_library(path: str = LIB_PATH):
@@ -103,6 +103,8 @@ def load_library(path: str = LIB_PATH):
         "path_paged_decode_step": ([DP, ctypes.POINTER(_PagedCache), P, I, P, I] + [P] * 9
                                    + [S, P], I),
         "path_paged_import": ([DP, CP, ctypes.POINTER(_PagedCache), P, I, P, I, P], I),
+        "path_decode_step_noalloc": ([DP, CP, I, P, P, P, P, P, P, P, P, P], I),
+        "path_decode_step_noalloc_limit": ([], S),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -375,6 +377,33 @@ def decode_step(cache: Cache, n: int, q_t, k_t, v_t, w_t, beta_t, logf_t=None,
                                 _ptr(k_t), _ptr(v_t), _ptr(w_t), _ptr(beta_t), _ptr(logf_t),
                                 _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
                                 _stream(cache.device)))
+    return o, lse
+
+
+def decode_step_noalloc_limit() -> int:
+    """Bytes of the library's device-resident scratch that decode_step_noalloc uses."""
+    return int(load_library().path_decode_step_noalloc_limit())
+
+
+def decode_step_noalloc(cache: Cache, n: int, q_t, k_t, v_t, w_t, beta_t, logf_t=None,
+                        scale=None, out=None):
+    """decode_step without a workspace: the split-K partial states go to a
+    scratch array the library keeps in device memory (one per GPU, shared by
+    every call on it, so overlapping calls on one GPU race).  For callers that
+    cannot allocate: pass `out` to make the call allocate nothing at all."""
+    lib = load_library()
+    for name, t in (("q_t", q_t), ("k_t", k_t), ("v_t", v_t), ("w_t", w_t)):
+        _need(t, name, cache.device, (cache.N, cache.H, cache.d), cache.dtype)
+    _need(beta_t, "beta_t", cache.device, (cache.N, cache.H), torch.float32)
+    if logf_t is not None:
+        _need(logf_t, "logf_t", cache.device, (cache.N, cache.H), torch.float32)
+    scale = cache.d ** -0.5 if scale is None else scale
+    desc = _cache_desc(cache, scale)
+    o, lse = _token_outs(cache.N, cache.H, cache.d, cache.dtype, cache.device, q_t, out)
+    cc = cache._c()
+    _check(lib.path_decode_step_noalloc(ctypes.byref(desc), ctypes.byref(cc), int(n), _ptr(q_t),
+                                        _ptr(k_t), _ptr(v_t), _ptr(w_t), _ptr(beta_t),
+                                        _ptr(logf_t), _ptr(o), _ptr(lse), _stream(cache.device)))
     return o, lse
 
 

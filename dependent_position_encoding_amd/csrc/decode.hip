@@ -7,6 +7,8 @@
 // Householder 变换编码位置" (cc.laoqi.cc), section 2.x; [Explainer s3] =
 // explainer page "PaTH Attention: Position Encoding via Accumulating
 // Householder Transformations" (gist.science), section 3.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma.hpp"
@@ -1002,6 +1004,54 @@ hipError_t launch_kv_align(const FwdArgs& a, const CacheArgs& c, hipStream_t st)
     if (c.k_bf16)
         return a.bf16 ? align_b<bf16, bf16>(a, c, st) : align_b<bf16, float>(a, c, st);
     return a.bf16 ? align_b<float, bf16>(a, c, st) : align_b<float, float>(a, c, st);
+}
+
+// ---------------------------------------------------------------------------
+// Device-resident scratch for the entry point that allocates nothing
+// (path_decode_step_noalloc): the split-K partial softmax states of a fused
+// decode step go here instead of into a caller workspace.  The array exists
+// once on every GPU the library's code object is loaded on and lives until
+// the process ends; all calls on one GPU share it and it keeps the last
+// call's contents (nothing in it needs to start at zero: every partial a
+// combine reads is written by the same call's chunk kernel).  Calls that
+// overlap on one GPU (different streams, or threads) race on it.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];     // device address of `scratch`, per device
+}  // namespace
+
+// The device address of `scratch` on the GPU that `stream` belongs to.  The
+// host-side name of the array is only a stand-in for the symbol, never a
+// device address: the address is looked up once per device (with that device
+// current) and kept.
+hipError_t static_scratch(hipStream_t stream, float** out) {
+    int dev = -1, cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (stream) {
+        if ((e = hipStreamGetDevice(stream, &dev)) != hipSuccess) return e;
+    } else {
+        dev = cur;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<float*>(g_scratch_ptr[dev]);
+    return hipSuccess;
 }
 
 }  // namespace pa

@@ -350,7 +350,8 @@ static path_status decode_common(const path_fwd_desc* desc, const path_cache* ca
                                  int n_keys, const void* q_t, void* o_t, float* lse_t,
                                  void* ws, size_t ws_bytes, bool fused, const void* k_t,
                                  const void* v_t, const void* w_t, const float* beta_t,
-                                 const float* logf_t, hipStream_t stream, const char* name) {
+                                 const float* logf_t, hipStream_t stream, const char* name,
+                                 bool validate_only = false) {
     path_status s = check_desc(desc, false);
     if (s != PATH_OK) return s;
     if ((s = check_cache(desc, cache)) != PATH_OK) return s;
@@ -361,6 +362,7 @@ static path_status decode_common(const path_fwd_desc* desc, const path_cache* ca
     if (n_keys > cache->cap) return fail(PATH_E_CAPACITY, "keys exceed cache capacity");
     if (n_keys > pa::decode_max_keys())
         return fail(PATH_E_UNSUPPORTED, "decode attends over at most 131072 keys per call");
+    if (validate_only) return PATH_OK;
     if (!ws) return fail(PATH_E_WORKSPACE, "workspace is NULL");
     if (!aligned(ws, 256)) return fail(PATH_E_ALIGN, "workspace must be 256-byte aligned");
     if (ws_bytes < path_decode_workspace(desc, n_keys))
@@ -379,11 +381,11 @@ path_status path_decode(const path_fwd_desc* desc, const path_cache* cache, int 
                          nullptr, nullptr, nullptr, nullptr, stream, "path_decode");
 }
 
-path_status path_decode_step(const path_fwd_desc* desc, const path_cache* cache, int n,
-                             const void* q_t, const void* k_t, const void* v_t,
-                             const void* w_t, const float* beta_t, const float* logf_t,
-                             void* o_t, float* lse_t, void* ws, size_t ws_bytes,
-                             hipStream_t stream) {
+// The token arguments of a fused step (shared by path_decode_step and
+// path_decode_step_noalloc).
+static path_status check_step_token(const path_cache* cache, int n, const void* k_t,
+                                    const void* v_t, const void* w_t, const float* beta_t,
+                                    const float* logf_t) {
     if (!k_t || !v_t || !w_t || !beta_t) return fail(PATH_E_NULL, "k_t, v_t, w_t and beta_t are required");
     if (!aligned(k_t, 16) || !aligned(v_t, 16) || !aligned(w_t, 16) || !aligned(beta_t, 4) ||
         !aligned(logf_t, 4))
@@ -391,8 +393,46 @@ path_status path_decode_step(const path_fwd_desc* desc, const path_cache* cache,
     if (cache && cache->gcache && !logf_t) return fail(PATH_E_NULL, "logf_t is required when gcache is set");
     if (n < 0) return fail(PATH_E_SHAPE, "n must be >= 0");
     if (cache && n >= cache->cap) return fail(PATH_E_CAPACITY, "slot n is beyond the cache capacity");
+    return PATH_OK;
+}
+
+path_status path_decode_step(const path_fwd_desc* desc, const path_cache* cache, int n,
+                             const void* q_t, const void* k_t, const void* v_t,
+                             const void* w_t, const float* beta_t, const float* logf_t,
+                             void* o_t, float* lse_t, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+    path_status s = check_step_token(cache, n, k_t, v_t, w_t, beta_t, logf_t);
+    if (s != PATH_OK) return s;
     return decode_common(desc, cache, n + 1, q_t, o_t, lse_t, ws, ws_bytes, true, k_t, v_t,
                          w_t, beta_t, logf_t, stream, "path_decode_step");
+}
+
+size_t path_decode_step_noalloc_limit(void) { return pa::kStaticScratchBytes; }
+
+path_status path_decode_step_noalloc(const path_fwd_desc* desc, const path_cache* cache, int n,
+                                     const void* q_t, const void* k_t, const void* v_t,
+                                     const void* w_t, const float* beta_t, const float* logf_t,
+                                     void* o_t, float* lse_t, hipStream_t stream) {
+    path_status s = check_step_token(cache, n, k_t, v_t, w_t, beta_t, logf_t);
+    if (s != PATH_OK) return s;
+    if ((s = check_desc(desc, false)) != PATH_OK) return s;
+    const size_t need = path_decode_workspace(desc, n + 1);
+    if (need > pa::kStaticScratchBytes)
+        return fail(PATH_E_WORKSPACE,
+                    "this step needs " + std::to_string(need) + " bytes of scratch; the "
+                    "library's static scratch holds " + std::to_string(pa::kStaticScratchBytes) +
+                    " (use path_decode_step with a workspace)");
+    // Everything else is checked (and reported) exactly as path_decode_step
+    // checks it before the scratch address is looked up.
+    if ((s = decode_common(desc, cache, n + 1, q_t, o_t, lse_t, nullptr, 0, true, k_t, v_t,
+                           w_t, beta_t, logf_t, stream, "path_decode_step_noalloc",
+                           /*validate_only=*/true)) != PATH_OK)
+        return s;
+    float* scratch = nullptr;
+    hipError_t e = pa::static_scratch(stream, &scratch);
+    if (e != hipSuccess) return launched(e, "path_decode_step_noalloc (scratch address)");
+    return decode_common(desc, cache, n + 1, q_t, o_t, lse_t, scratch, pa::kStaticScratchBytes,
+                         true, k_t, v_t, w_t, beta_t, logf_t, stream, "path_decode_step_noalloc");
 }
 
 // ---- paged cache

@@ -67,6 +67,11 @@ hipError_t launch_decode(const CacheArgs& c, int n_keys, float scale,
                          const float* logf_t, hipStream_t st);
 int decode_chunk(int n_keys);
 int decode_max_keys();   // longest cache one decode call can attend over
+// Bytes of the device-resident scratch array (one per GPU) that
+// path_decode_step_noalloc uses in place of a workspace, and its device
+// address on the GPU of `stream` (looked up once per device).
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+hipError_t static_scratch(hipStream_t stream, float** out);
 
 // paged cache [page][H][P][d] (P = 1 << lp) for a batch of S sequences
 struct PagedArgs {

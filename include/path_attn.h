@@ -22,6 +22,8 @@
  *   allocates nothing, frees nothing, keeps no per-call global state, and
  *   never synchronises the host with the device.  Work is enqueued on the
  *   caller's stream; results are visible after the caller synchronises it.
+ *   (path_decode_step_noalloc alone uses a fixed scratch array that the
+ *   library holds in device memory, one per GPU, instead of a workspace.)
  * - Layouts are dense and row-major:
  *     q, k, v, w, o          [N, H, L, d]  in desc->dtype
  *     beta, logf, lse        [N, H, L]     float32
@@ -52,7 +54,7 @@
 extern "C" {
 #endif
 
-#define PATH_ATTN_ABI_VERSION 4
+#define PATH_ATTN_ABI_VERSION 5
 
 typedef enum {
     PATH_OK = 0,
@@ -217,6 +219,31 @@ path_status path_decode_step(const path_fwd_desc *desc,
                              const void *w_t, const float *beta_t,
                              const float *logf_t, void *o_t, float *lse_t,
                              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* path_decode_step for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, semantics and results as path_decode_step
+ * (bit for bit: the same kernels), without the workspace arguments: the
+ * split-K partial states go to a scratch array that the library holds in
+ * device memory, one per GPU, for the life of the process
+ * (path_decode_step_noalloc_limit() bytes, 16 MiB).  Neither call allocates
+ * or frees anything.
+ *   - A step whose partial states need more than that (path_decode_workspace
+ *     (desc, n + 1) > the limit; at d = 64 about 63 500 chunks of 128 keys
+ *     over all N * H slices) returns PATH_E_WORKSPACE before any launch.
+ *   - The first call on a GPU looks the array's device address up (with that
+ *     GPU current; the GPU is the one `stream` belongs to) and keeps it.
+ *   - Every call on one GPU shares the array: calls that overlap on one GPU
+ *     (on different streams or from different threads) race and must be
+ *     ordered by the caller.  The array keeps the last call's contents;
+ *     nothing in it needs clearing. */
+size_t path_decode_step_noalloc_limit(void);
+path_status path_decode_step_noalloc(const path_fwd_desc *desc,
+                                     const path_cache *cache, int n,
+                                     const void *q_t, const void *k_t,
+                                     const void *v_t, const void *w_t,
+                                     const float *beta_t, const float *logf_t,
+                                     void *o_t, float *lse_t, hipStream_t stream);
 
 /* Paged decode cache for a batch of sequences of different lengths
  * [Notes s2.8; Explainer s3: the in-place key rewrite keeps decoding

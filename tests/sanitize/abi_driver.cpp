@@ -89,6 +89,15 @@ int main() {
     EXPECT(path_decode_step(&g, &small, 2, F, F, F, F, FF, nullptr, F, nullptr, F, 4, nullptr) ==
            PATH_E_WORKSPACE);
 
+    // the allocation-free step: validation, then the scratch size limit
+    EXPECT(path_decode_step_noalloc_limit() == ((size_t)16 << 20));
+    EXPECT(path_decode_step_noalloc(&g, &small, 8, F, F, F, F, FF, nullptr, F, nullptr,
+                                    nullptr) == PATH_E_CAPACITY);
+    path_fwd_desc huge = desc(64, 64, 1, 64, PATH_BF16, 0);
+    path_cache bigc{131072, PATH_BF16, F, F, nullptr};
+    EXPECT(path_decode_step_noalloc(&huge, &bigc, 131071, F, F, F, F, FF, nullptr, F, nullptr,
+                                    nullptr) == PATH_E_WORKSPACE);
+
     path_paged_cache pc{8, 64, PATH_BF16, F, F, nullptr};
     path_fwd_desc s3 = desc(3, 2, 1, 64, PATH_BF16, 0);
     size_t pws = path_paged_decode_workspace(&s3, 256);

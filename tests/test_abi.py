@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     pa, lib = _lib()
-    assert lib.path_abi_version() == 4
+    assert lib.path_abi_version() == 5
     for s in range(9):
         assert lib.path_status_str(s)
     assert lib.path_status_str(99) == b"unknown status"
@@ -260,3 +260,33 @@ def test_fwd_timed_argument_errors():
     bad[11] = need - 1
     assert lib.path_attn_fwd_timed(*bad, evs) == 6
     assert lib.path_last_error()
+
+
+def test_noalloc_step_argument_errors():
+    """The allocation-free decode step validates exactly as path_decode_step
+    does, and refuses a step whose partial states exceed its static scratch,
+    all before anything touches a device."""
+    pa, lib = _lib()
+    limit = lib.path_decode_step_noalloc_limit()
+    assert limit == 16 << 20
+    d = _desc(pa)
+    c = pa._Cache(8, pa.PATH_BF16, 1 << 20, 1 << 21, None)
+    call = lambda desc, cache, n, **kw: lib.path_decode_step_noalloc(
+        ctypes.byref(desc) if desc is not None else None, ctypes.byref(cache) if cache else None,
+        n, *[kw.get(x, FAKE) for x in ("q", "k", "v", "w", "beta")], kw.get("logf"),
+        kw.get("o", FAKE), None, None)
+    assert call(None, c, 2) == 1
+    assert call(d, None, 2) == 1
+    assert call(d, c, 8) == 7                  # slot 8 of a cache of 8
+    assert call(d, c, -1) == 2
+    assert call(d, c, 2, q=None) == 1
+    assert call(d, c, 2, k=ctypes.c_void_p((1 << 20) + 8)) == 5
+    assert call(_desc(pa, d=48), c, 2) == 4
+    g = pa._Cache(8, pa.PATH_BF16, 1 << 20, 1 << 21, 1 << 22)
+    assert call(d, g, 2) == 1                  # gate prefix without log f_t
+    # 4096 slices x 1024 chunks of partial states: far beyond the scratch
+    big = _desc(pa, N=64, H=64)
+    cb = pa._Cache(131072, pa.PATH_BF16, 1 << 20, 1 << 21, None)
+    assert lib.path_decode_workspace(ctypes.byref(big), 131072) > limit
+    assert call(big, cb, 131071) == 6
+    assert b"static scratch" in lib.path_last_error()
