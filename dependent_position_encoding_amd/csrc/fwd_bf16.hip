@@ -4,7 +4,8 @@
 // Householder 变换编码位置" (cc.laoqi.cc), section 2.x.
 //
 // Two kernels per call:
-//   precond (one 256-thread workgroup per 64-token block): UT solve
+//   precond (one 512-thread workgroup per 64-token block, operands staged in
+//   LDS once by direct HBM -> LDS loads): UT solve
 //     U = (I + strictLower(diag(beta) W W^T))^{-1} diag(beta)   [Notes s2.6]
 //     and the block products of [Notes s2.7]:
 //       P = lower(Q W^T) U,  Qleft = Q - P W,  M = strictLower(W K^T),
@@ -37,8 +38,6 @@ namespace pa {
 namespace {
 
 constexpr int kB = 64;       // block size
-constexpr int kSB = 72;      // LDS row stride of bf16 tiles with 64 columns
-constexpr int kSF = 68;      // LDS row stride of float tiles with 64 columns
 
 // Writes a C tile through f(row, col, value).
 template <typename F>
@@ -46,24 +45,6 @@ __device__ inline void for_tile(const f32x16& acc, int m0, int n0, int lane, F f
     const int h = lane >> 5, col = n0 + (lane & 31);
 #pragma unroll
     for (int r = 0; r < 16; ++r) f(m0 + crow(r, h), col, acc[r]);
-}
-
-// A float32 matrix held in LDS as two bf16 matrices, hi = bf16(x) and
-// lo = bf16(x - hi) (about 16 significant bits together), split once by its
-// producer so that every consumer reads matrix-core operands directly.
-struct Split {
-    __bf16* hi;
-    __bf16* lo;
-};
-constexpr int kSplitBytes = 2 * kB * kSB * 2;   // one 64 x 64 split matrix
-
-__device__ inline Split split_at(char* buf) {
-    return {reinterpret_cast<__bf16*>(buf), reinterpret_cast<__bf16*>(buf + kB * kSB * 2)};
-}
-__device__ inline void put(const Split& m, int r, int c, float v) {
-    const __bf16 hi = (__bf16)v;
-    m.hi[r * kSB + c] = hi;
-    m.lo[r * kSB + c] = (__bf16)(v - (float)hi);
 }
 
 // A C tile of a transposed product, read back row-wise: lane (tile column
@@ -78,69 +59,69 @@ __device__ inline void for_tile4(const f32x16& acc, int m0, int n0, int lane, F 
         f(row, m0 + 8 * i + 4 * h, f32x4{acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]});
 }
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-__device__ inline void put4(const Split& m, int r, int c, f32x4 v) {
-    bf16x4 hi, lo;
+
+// Wait for this wave's outstanding vector-memory loads (including direct
+// HBM -> LDS copies); the caller synchronises before reading the LDS.
+__device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ---------------------------------------------------------------------------
+// LDS layout of the preconditioning: no padding; every 16-byte unit of a row
+// sits at a row-dependent XOR position (swz_unit) so that a row fragment (32
+// rows, one unit each) and a transposed fragment (4 rows, 32 bytes each) hit
+// distinct banks.  Byte offsets of element (r, c):
+//   natural bf16 tiles [64][D] (rows of RB = 2 D bytes): pb<RB>(r, c);
+//   bf16 64 x 64 matrices (one part of a split matrix, 128-byte rows): pb<128>;
+//   float 64 x 64 matrices (256-byte rows): pf(r, c).
+template <int RB>
+__device__ __forceinline__ int pb(int r, int c) {
+    return r * RB + (swz_unit(r, c >> 3, RB) << 4) + ((c & 7) << 1);
+}
+__device__ __forceinline__ int pf(int r, int c) {
+    return r * 256 + (swz_unit(r, c >> 2, 256) << 4) + ((c & 3) << 2);
+}
+__device__ __forceinline__ float& fat(char* s, int r, int c) {
+    return *reinterpret_cast<float*>(s + pf(r, c));
+}
+constexpr int kSlot = 64 * 64 * 4;          // one float 64 x 64 matrix, or a split one
+constexpr int kPart = kSlot / 2;            // the lo part of a split matrix starts here
+
+// Row fragment of a bf16 LDS matrix with RB-byte rows: row r, columns k .. k+7.
+template <int RB>
+__device__ __forceinline__ bf16x8 frow(const char* t, int r, int k) {
+    return *reinterpret_cast<const bf16x8*>(t + pb<RB>(r, k));
+}
+// Column fragment: rows k .. k+7 of column c (the lane's column; the 16 lanes
+// of a group hold 16 consecutive columns), through gfx950's transposing LDS
+// load: in each group of 16 lanes, lane j names 4 consecutive elements of row
+// k + j/4 starting at column c0 + 4 (j mod 4) (c0 the group's first column),
+// and lane i receives column c0 + i of those 4 rows; a second load covers
+// rows k+4 .. k+7.  Every lane of the wave must take part.
+template <int RB>
+__device__ __forceinline__ bf16x8 fcol(const char* t, int c, int k) {
+    typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4;
+    const int j = threadIdx.x & 15, r = k + (j >> 2), c4 = c - j + 4 * (j & 3);
+    const bf16x4v a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + pb<RB>(r, c4)));
+    const bf16x4v b =
+        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + pb<RB>(r + 4, c4)));
+    bf16x8 x;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        hi[e] = (__bf16)v[e];
-        lo[e] = (__bf16)(v[e] - (float)hi[e]);
+        x[e] = a[e];
+        x[e + 4] = b[e];
     }
-    *reinterpret_cast<bf16x4*>(m.hi + r * kSB + c) = hi;
-    *reinterpret_cast<bf16x4*>(m.lo + r * kSB + c) = lo;
+    return x;
 }
-
-// acc += A[m0:+32, 0:K] * Bn[n0:+32, 0:K]^T over LDS bf16 operands; a split
-// operand contributes its lo part as well (lo * lo is dropped).
-template <int K, bool SA, bool SBL>
-__device__ inline void tile_mm_s(f32x16& acc, const __bf16* Ah, const __bf16* Al, const __bf16* Bh,
-                                 const __bf16* Bl, int m0, int n0, int lane) {
-    const int r = lane & 31, h = lane >> 5;
-#pragma unroll
-    for (int k0 = 0; k0 < K; k0 += 16) {
-        const int ao = (m0 + r) * kSB + k0 + 8 * h, bo = (n0 + r) * kSB + k0 + 8 * h;
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(Ah + ao);
-        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(Bh + bo);
-        if constexpr (SBL) acc = mfma32(ah, *reinterpret_cast<const bf16x8*>(Bl + bo), acc);
-        if constexpr (SA) acc = mfma32(*reinterpret_cast<const bf16x8*>(Al + ao), bh, acc);
-        acc = mfma32(ah, bh, acc);
-    }
-}
-
-// 32 rows [r0, r0 + 32) of a row-major bf16 block with D columns in global
-// memory, as the D/16 k-steps of an MFMA operand (lane: row r0 + l % 32,
-// columns 16 ks + 8h .. +7); rows at or beyond nvalid read as zero.
-template <int D>
-__device__ inline void ld_rows(bf16x8 (&o)[D / 16], const __bf16* base, int r0, int nvalid,
-                               int lane) {
-    const int r = r0 + (lane & 31), h = lane >> 5;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-        if (r < nvalid) {
-            o[ks] = *reinterpret_cast<const bf16x8*>(base + (size_t)r * D + 16 * ks + 8 * h);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[ks][e] = (__bf16)0.f;
-        }
-    }
-}
-
-template <int NK>
-__device__ inline void mm_regs(f32x16& acc, const bf16x8 (&a)[NK], const bf16x8 (&b)[NK]) {
-#pragma unroll
-    for (int ks = 0; ks < NK; ++ks) acc = mfma32(a[ks], b[ks], acc);
-}
-
-// Eight floats of LDS row r (row stride kSF) as a bf16 hi + lo operand pair:
+// Eight floats of row r of a float matrix as a bf16 hi + lo operand pair:
 // columns c0 + 8h .. +7, or with PERM the columns c0 + swap23(8h + e) that
 // match a C tile reused as the other operand; zero when !ok.
 template <bool PERM>
-__device__ inline void lds8_split(const float* base, int r, int c0, int h, bool ok, bf16x8& hi,
-                                  bf16x8& lo) {
+__device__ inline void fsplit8(const char* s, int r, int c0, int h, bool ok, bf16x8& hi,
+                               bf16x8& lo) {
     f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
     if (ok) {
-        const float* p = base + r * kSF + c0;
-        a = *reinterpret_cast<const f32x4*>(p + (PERM ? 4 * h : 8 * h));
-        b = *reinterpret_cast<const f32x4*>(p + (PERM ? 8 + 4 * h : 8 * h + 4));
+        a = *reinterpret_cast<const f32x4*>(s + pf(r, c0 + (PERM ? 4 * h : 8 * h)));
+        b = *reinterpret_cast<const f32x4*>(s + pf(r, c0 + (PERM ? 8 + 4 * h : 8 * h + 4)));
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -149,70 +130,113 @@ __device__ inline void lds8_split(const float* base, int r, int c0, int h, bool 
         lo[e] = (__bf16)(x - (float)hi[e]);
     }
 }
+// Four floats as bf16 hi and lo parts of a split 64 x 64 matrix in slot s.
+__device__ inline void sput4(char* s, int r, int c, f32x4 v) {
+    bf16x4 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        hi[e] = (__bf16)v[e];
+        lo[e] = (__bf16)(v[e] - (float)hi[e]);
+    }
+    *reinterpret_cast<bf16x4*>(s + pb<128>(r, c)) = hi;
+    *reinterpret_cast<bf16x4*>(s + kPart + pb<128>(r, c)) = lo;
+}
+// acc += A[m0:+32, 0:64] B[n0:+32, 0:64]^T for two split matrices in slots
+// (row fragments, hi and lo of both; lo * lo dropped).
+__device__ inline void mm_ss(f32x16& acc, const char* A, const char* Bn, int m0, int n0, int lane) {
+    const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int k0 = 0; k0 < kB; k0 += 16) {
+        const int k = k0 + 8 * h;
+        const bf16x8 ah = frow<128>(A, m0 + r, k), bh = frow<128>(Bn, n0 + r, k);
+        acc = mfma32(ah, frow<128>(Bn + kPart, n0 + r, k), acc);
+        acc = mfma32(frow<128>(A + kPart, m0 + r, k), bh, acc);
+        acc = mfma32(ah, bh, acc);
+    }
+}
+// acc += A[m0:+32, 0:64] B[0:64, n0:+32] for a split matrix A in a slot and
+// the natural [64][D] tile B read down its columns (exact bf16).
+template <int RB>
+__device__ inline void mm_sc(f32x16& acc, const char* A, const char* Bt, int m0, int n0, int lane) {
+    const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int k0 = 0; k0 < kB; k0 += 16) {
+        const int k = k0 + 8 * h;
+        const bf16x8 b = fcol<RB>(Bt, n0 + r, k);
+        acc = mfma32(frow<128>(A + kPart, m0 + r, k), b, acc);
+        acc = mfma32(frow<128>(A, m0 + r, k), b, acc);
+    }
+}
+// acc += A[m0:+32, 0:D] B[n0:+32, 0:D]^T for two natural [64][D] tiles
+// (row fragments, exact bf16).
+template <int D>
+__device__ inline void mm_nn(f32x16& acc, const char* A, const char* Bn, int m0, int n0, int lane) {
+    const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int k0 = 0; k0 < D; k0 += 16)
+        acc = mfma32(frow<2 * D>(A, m0 + r, k0 + 8 * h), frow<2 * D>(Bn, n0 + r, k0 + 8 * h), acc);
+}
 
-// One 512-thread workgroup (8 waves) per 64-token block, 64.8 KB of LDS so
-// that two workgroups share a CU and one's barriers and HBM waits overlap
-// the other's work.  Products over the head dimension read Q, K and W
-// straight from HBM as matrix-core operands; products over tokens read LDS.
+// Direct HBM -> LDS copy of the block's rows [row0, row0 + 64) of one [L][D]
+// bf16 slice into a natural swizzled tile.  A wave fills 1 KB of LDS
+// contiguously (16 bytes a lane); each lane fetches the unit that belongs at
+// its LDS position.  The buffer resource spans the slice, so rows past its end
+// (a ragged last block) read as zeros.
+template <int D>
+__device__ inline void stage_rows(const __bf16* slice_base, int L, int row0, char* dst, int tid) {
+    constexpr int RB = 2 * D, UPR = RB / 16, NU = 64 * UPR;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16*>(slice_base), 0, (uint32_t)L * RB, 0x00020000);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+#pragma unroll
+    for (int u0 = 0; u0 < NU; u0 += 512) {
+        if (u0 + wave * 64 < NU) {
+            const int U = u0 + wave * 64 + lane, r = U / UPR;
+            const uint32_t src = (uint32_t)(row0 + r) * RB + swz_unit(r, U % UPR, RB) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)(dst + (u0 + wave * 64) * 16), 16, src,
+                0, 0, 0);
+        }
+    }
+}
+
+// One 512-thread workgroup (8 waves) per 64-token block.  The block's Q, K,
+// W and V rows are copied into LDS once, at the start, with direct
+// HBM -> LDS loads; every product then reads its operands from LDS, so a
+// workgroup waits on HBM once.  72 KB of LDS (Q, K, W and three 64 x 64
+// slots, each a float matrix or a split one) and <= 128 VGPRs let two
+// workgroups share a CU and overlap each other's waits.
 template <int D>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
 precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                     const __bf16* __restrict__ v, const __bf16* __restrict__ w,
                     const float* __restrict__ beta, const float* __restrict__ logf,
                     int L, int nb, float kscale, FwdWs ws) {
-    constexpr int B = kB, SB = kSB, SF = kSF, UPR = D / 8, NTH = 512, NKS = D / 16;
-    constexpr int DT = D / 32;                 // 32-wide tiles along d
+    constexpr int B = kB, RB = 2 * D, NTH = 512, DT = D / 32;
     using I = Img<D>;
-    // W^T and three 64 x 64 slots, each holding a float matrix or a split one:
-    //   s0 : G (float)            -> X1 (split)    -> P (split)
-    //   s1 : T (float)            -> U^T (split)   -> Y^T (split)
-    //   s2 : V (float staging)    -> T^T (float)   -> M^T (split)
-    __shared__ __attribute__((aligned(16))) __bf16 sWt[D * SB];
-    __shared__ __attribute__((aligned(16))) char s0[kSplitBytes], s1[kSplitBytes], s2[kSplitBytes];
+    // Q, K, W rows (natural) and three slots, each a float or a split matrix:
+    //   s0 : G (float)        -> X1 (split)    -> P (split)
+    //   s1 : T (float)        -> U^T (split)   -> Y^T (split)
+    //   s2 : V (natural bf16) -> T^T (float)   -> M^T (split)
+    __shared__ __attribute__((aligned(16))) char sQ[B * RB], sK[B * RB], sW[B * RB];
+    __shared__ __attribute__((aligned(16))) char s0[kSlot], s1[kSlot], s2[kSlot];
     __shared__ float sBeta[B];
-    static_assert(kB * kSF * 4 <= kSplitBytes, "slot size");
-    float* fG = reinterpret_cast<float*>(s0);
-    float* fT = reinterpret_cast<float*>(s1);
-    float* fV = reinterpret_cast<float*>(s2);
-    float* fTt = reinterpret_cast<float*>(s2);
-    const Split X1 = split_at(s0), P = split_at(s0), Ut = split_at(s1), Yt = split_at(s1),
-                Mt = split_at(s2);
 
     const int blk = blockIdx.x, slice = blk / nb, c = blk % nb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const size_t base = (size_t)slice * L;
     const int row0 = c * B, nvalid = min(B, L - row0);
-    const size_t eoff = (base + row0) * D;       // the block's first element
-    const __bf16 *qb = q + eoff, *kb = k + eoff, *wb = w + eoff, *vb = v + eoff;
     char* img = static_cast<char*>(ws.img) + (size_t)blk * I::BYTES;
 
-    // ---- 1. W^T and V (as float) into LDS, beta, T = 0, gate cumsum; waves
-    //         0-2 fetch their W operand rows for G meanwhile
-    const int gmt = wave == 0 ? 0 : 1, gnt = wave == 2 ? 1 : 0;   // G's lower tiles
-    bf16x8 ga[NKS], gb[NKS];
-    if (wave < 3) {
-        ld_rows<D>(ga, wb, 32 * gmt, nvalid, lane);
-        ld_rows<D>(gb, wb, 32 * gnt, nvalid, lane);
-    }
-    for (int u = tid; u < B * UPR; u += NTH) {
-        const int r = u / UPR, x0 = (u % UPR) * 8;
-        bf16x8 wv, vv;
-        if (r < nvalid) {
-            wv = *reinterpret_cast<const bf16x8*>(wb + r * D + x0);
-            vv = *reinterpret_cast<const bf16x8*>(vb + r * D + x0);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) wv[e] = vv[e] = (__bf16)0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            sWt[(x0 + e) * SB + r] = wv[e];
-            fV[r * SF + x0 + e] = (float)vv[e];
-        }
-    }
-    for (int e = tid; e < B * B; e += NTH) fT[(e / B) * SF + e % B] = 0.f;
-    if (tid < B) sBeta[tid] = tid < nvalid ? beta[base + row0 + tid] : 0.f;
+    // ---- 0. Q, K, W, V rows into LDS (one wait); beta; T = 0; gate cumsum
+    stage_rows<D>(q + base * D, L, row0, sQ, tid);
+    stage_rows<D>(k + base * D, L, row0, sK, tid);
+    stage_rows<D>(w + base * D, L, row0, sW, tid);
+    stage_rows<D>(v + base * D, L, row0, s2, tid);
+    for (int e = tid; e < B * B / 4; e += NTH)
+        *reinterpret_cast<f32x4*>(s1 + 16 * e) = f32x4{0.f, 0.f, 0.f, 0.f};
     if (wave == 7) {
+        sBeta[lane] = lane < nvalid ? beta[base + row0 + lane] : 0.f;
         // in-block inclusive prefix sum of log f (one lane per token)
         float acc = (logf && lane < nvalid) ? logf[base + row0 + lane] : 0.f;
 #pragma unroll
@@ -224,30 +248,33 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         reinterpret_cast<float*>(img + I::OFF_G)[lane] = acc;
         if (lane == 63) ws.tot[blk] = acc;
     }
+    wait_loads();
     __syncthreads();
 
-    // ---- 2. V^T with keys in operand order; G = diag(beta) strictLower(WW^T)
+    // ---- 1. V^T with keys in operand order; G = diag(beta) strictLower(WW^T)
     for (int u = tid; u < D * 8; u += NTH) {
         const int x = u / 8, s0i = (u % 8) * 8;
         bf16x8 pk;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pk[e] = (__bf16)fV[swap23(s0i + e) * SF + x];
+        for (int e = 0; e < 8; ++e)
+            pk[e] = *reinterpret_cast<const __bf16*>(s2 + pb<RB>(swap23(s0i + e), x));
         *reinterpret_cast<bf16x8*>(img + I::OFF_V + img_off(x, s0i, I::RB_V)) = pk;
     }
     if (wave < 3) {
+        const int gmt = wave == 0 ? 0 : 1, gnt = wave == 2 ? 1 : 0;   // G's lower tiles
         f32x16 acc = zero16();
-        mm_regs(acc, gb, ga);   // (W W^T)^T tile: lane = row i of G
+        mm_nn<D>(acc, sW, sW, 32 * gnt, 32 * gmt, lane);   // (W W^T)^T tile: lane = row i of G
         for_tile4(acc, 32 * gnt, 32 * gmt, lane, [&](int i, int j0, f32x4 v) {
             const float bi = sBeta[i];
             f32x4 g;
 #pragma unroll
             for (int e = 0; e < 4; ++e) g[e] = i > j0 + e ? bi * v[e] : 0.f;
-            *reinterpret_cast<f32x4*>(fG + i * SF + j0) = g;
+            *reinterpret_cast<f32x4*>(s0 + pf(i, j0)) = g;
         });
     }
     __syncthreads();
 
-    // ---- 3. T = (I + G)^{-1}.  Diagonal 16 x 16 blocks by forward
+    // ---- 2. T = (I + G)^{-1}.  Diagonal 16 x 16 blocks by forward
     //         substitution (waves 0-3, one column per lane); then the
     //         off-diagonal blocks by doubling on the matrix cores: the inverse
     //         of a lower block-triangular [[A, 0], [C, B]] has off-diagonal
@@ -266,20 +293,19 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
             for (int kk = 0; kk < 15; ++kk)
 #pragma unroll
-                for (int i = kk + 1; i < 16; ++i) t[i] -= fG[(o + i) * SF + o + kk] * t[kk];
+                for (int i = kk + 1; i < 16; ++i) t[i] -= fat(s0, o + i, o + kk) * t[kk];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) fT[(o + i) * SF + o + lane] = t[i];
-            float* trow = fTt + (o + lane) * SF;
-            for (int c4 = 0; c4 < o; c4 += 4) *reinterpret_cast<f32x4*>(trow + c4) = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < 16; ++i) fat(s1, o + i, o + lane) = t[i];
+            const int tr = o + lane;
+            for (int c4 = 0; c4 < o; c4 += 4)
+                *reinterpret_cast<f32x4*>(s2 + pf(tr, c4)) = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c4 = 0; c4 < 16; c4 += 4)
-                *reinterpret_cast<f32x4*>(trow + o + c4) = f32x4{t[c4], t[c4 + 1], t[c4 + 2], t[c4 + 3]};
+                *reinterpret_cast<f32x4*>(s2 + pf(tr, o + c4)) =
+                    f32x4{t[c4], t[c4 + 1], t[c4 + 2], t[c4 + 3]};
         }
     } else if (!(xmt == 0 && xnt == 1)) {
-        bf16x8 a[NKS], b[NKS];
-        ld_rows<D>(a, qb, 32 * xmt, nvalid, lane);
-        ld_rows<D>(b, wb, 32 * xnt, nvalid, lane);
-        mm_regs(x1r, b, a);     // (Q W^T)^T tile: lane = row of X1
+        mm_nn<D>(x1r, sW, sQ, 32 * xnt, 32 * xmt, lane);     // (Q W^T)^T tile: lane = row of X1
     }
     __syncthreads();
     const int mrow = lane & 31, hh = lane >> 5;
@@ -288,8 +314,8 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const int o2 = 32 * wave;
         const bool ok = mrow < 16;
         bf16x8 ah, al, bh, bl;
-        lds8_split<false>(fG, o2 + 16 + mrow, o2, hh, ok, ah, al);
-        lds8_split<false>(fTt, o2 + mrow, o2, hh, ok, bh, bl);
+        fsplit8<false>(s0, o2 + 16 + mrow, o2, hh, ok, ah, al);
+        fsplit8<false>(s2, o2 + mrow, o2, hh, ok, bh, bl);
         const f32x16 x = mfma_split(ah, al, bh, bl, zero16());
         // X's C tile (rows 0-15 in registers 0-7) is the B operand of T_11 X
 #pragma unroll
@@ -297,22 +323,19 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             bh[e] = (__bf16)x[e];
             bl[e] = (__bf16)(x[e] - (float)bh[e]);
         }
-        lds8_split<true>(fT, o2 + 16 + mrow, o2 + 16, hh, ok, ah, al);
+        fsplit8<true>(s1, o2 + 16 + mrow, o2 + 16, hh, ok, ah, al);
         const f32x16 y = mfma_split(ah, al, bh, bl, zero16());
         if (ok) {
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 const int row = crow(r, hh);
-                fT[(o2 + 16 + row) * SF + o2 + mrow] = -y[r];
-                fTt[(o2 + mrow) * SF + o2 + 16 + row] = -y[r];
+                fat(s1, o2 + 16 + row, o2 + mrow) = -y[r];
+                fat(s2, o2 + mrow, o2 + 16 + row) = -y[r];
             }
         }
     } else if (wave >= 4 && !(xmt == 1 && xnt == 0)) {
         // M^T[j][b] = k_j . w_b for b > j (transposed tile: lane = row j)
-        bf16x8 a[NKS], b[NKS];
-        ld_rows<D>(a, kb, 32 * xmt, nvalid, lane);
-        ld_rows<D>(b, wb, 32 * xnt, nvalid, lane);
-        mm_regs(mtr, b, a);
+        mm_nn<D>(mtr, sW, sK, 32 * xnt, 32 * xmt, lane);
     }
     __syncthreads();
     if (wave == 0) {
@@ -321,8 +344,8 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             bf16x8 ah, al, bh, bl;
-            lds8_split<false>(fG, 32 + mrow, 16 * ks, hh, true, ah, al);
-            lds8_split<false>(fTt, mrow, 16 * ks, hh, true, bh, bl);
+            fsplit8<false>(s0, 32 + mrow, 16 * ks, hh, true, ah, al);
+            fsplit8<false>(s2, mrow, 16 * ks, hh, true, bh, bl);
             x = mfma_split(ah, al, bh, bl, x);
         }
         f32x16 y = zero16();
@@ -334,66 +357,65 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 bh[e] = (__bf16)x[8 * ks + e];
                 bl[e] = (__bf16)(x[8 * ks + e] - (float)bh[e]);
             }
-            lds8_split<true>(fT, 32 + mrow, 32 + 16 * ks, hh, true, ah, al);
+            fsplit8<true>(s1, 32 + mrow, 32 + 16 * ks, hh, true, ah, al);
             y = mfma_split(ah, al, bh, bl, y);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int row = crow(r, hh);
-            fT[(32 + row) * SF + mrow] = -y[r];
-            fTt[mrow * SF + 32 + row] = -y[r];
+            fat(s1, 32 + row, mrow) = -y[r];
+            fat(s2, mrow, 32 + row) = -y[r];
         }
     }
     __syncthreads();
 
-    // ---- 4. U^T = (T diag(beta))^T from T^T, row by row (over T); X1 to
+    // ---- 3. U^T = (T diag(beta))^T from T^T, row by row (over T); X1 to
     //         LDS over G (waves 4-7)
     {
         const int j = tid / 8, c0 = (tid % 8) * 8;
         const float bj = sBeta[j];
-        const f32x4 a = *reinterpret_cast<const f32x4*>(fTt + j * SF + c0);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(fTt + j * SF + c0 + 4);
-        put4(Ut, j, c0, a * bj);
-        put4(Ut, j, c0 + 4, b * bj);
+        const f32x4 a = *reinterpret_cast<const f32x4*>(s2 + pf(j, c0));
+        const f32x4 b = *reinterpret_cast<const f32x4*>(s2 + pf(j, c0 + 4));
+        sput4(s1, j, c0, a * bj);
+        sput4(s1, j, c0 + 4, b * bj);
     }
     if (wave >= 4)
         for_tile4(x1r, 32 * xnt, 32 * xmt, lane, [&](int i, int j0, f32x4 v) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = j0 + e <= i ? v[e] : 0.f;
-            put4(X1, i, j0, v);
+            sput4(s0, i, j0, v);
         });
     __syncthreads();
 
-    // ---- 5. M^T to LDS over T^T (waves 4-7); P = X1 U (waves 0-3) and
-    //         Y^T = W^T U (waves 4..), Y = U^T W, both as transposed products;
-    //         Kright = K - (U M)^T W = K - M^T Y and E = W^T Y below.
+    // ---- 4. M^T to LDS over T^T (waves 4-7); P = X1 U (waves 0-3) and
+    //         Y^T (Y = U^T W) on waves 4 .. 4 + 2 DT - 1, both as transposed
+    //         products; Kright = K - (U M)^T W = K - M^T Y and E = W^T Y below.
     {
         if (wave >= 4)
             for_tile4(mtr, 32 * xnt, 32 * xmt, lane, [&](int j, int b0, f32x4 v) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = b0 + e > j ? v[e] : 0.f;
-                put4(Mt, j, b0, v);
+                sput4(s2, j, b0, v);
             });
         f32x16 acc = zero16();
         const int mt = wave < 4 ? wave >> 1 : (wave - 4) / 2;
         const int nt = wave < 4 ? wave & 1 : (wave - 4) % 2;
         if (wave < 4) {
             // P^T[a][i] = sum_k U^T[a][k] X1[i][k]
-            if (!(mt == 0 && nt == 1))
-                tile_mm_s<B, true, true>(acc, Ut.hi, Ut.lo, X1.hi, X1.lo, 32 * nt, 32 * mt, lane);
+            if (!(mt == 0 && nt == 1)) mm_ss(acc, s1, s0, 32 * nt, 32 * mt, lane);
         } else if (wave < 4 + 2 * DT) {
-            // Y[cc][y] = sum_a U^T[cc][a] W^T[y][a]
-            tile_mm_s<B, true, false>(acc, Ut.hi, Ut.lo, sWt, nullptr, 32 * nt, 32 * mt, lane);
+            // Y[cc][y] = sum_a U^T[cc][a] W[a][y]
+            mm_sc<RB>(acc, s1, sW, 32 * nt, 32 * mt, lane);
         }
         __syncthreads();
         if (wave < 4)
-            for_tile4(acc, 32 * nt, 32 * mt, lane, [&](int i, int a0, f32x4 v) { put4(P, i, a0, v); });
+            for_tile4(acc, 32 * nt, 32 * mt, lane, [&](int i, int a0, f32x4 v) { sput4(s0, i, a0, v); });
         else if (wave < 4 + 2 * DT)
-            for_tile4(acc, 32 * nt, 32 * mt, lane, [&](int y, int c0, f32x4 v) { put4(Yt, y, c0, v); });
+            for_tile4(acc, 32 * nt, 32 * mt, lane, [&](int y, int c0, f32x4 v) { sput4(s1, y, c0, v); });
     }
     __syncthreads();
 
-    // ---- 6. outputs, stored straight to HBM, heaviest jobs first:
+    // ---- 5. outputs, stored straight to HBM, heaviest jobs first:
     //         Dg = lower(Q K^T) - P M (in-block logits), Kright = K - M^T Y
     //         (image, scaled, and its fp32 copy), Qleft = Q - P W,
     //         -E = -W^T Y (image, and E in fp32)
@@ -403,11 +425,8 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         if (j < ND) {
             const int mt = j == 0 ? 0 : 1, nt = j == 2 ? 1 : 0;
             f32x16 qk = zero16();
-            bf16x8 a[NKS], b[NKS];
-            ld_rows<D>(a, qb, 32 * mt, nvalid, lane);
-            ld_rows<D>(b, kb, 32 * nt, nvalid, lane);
-            mm_regs(qk, a, b);
-            tile_mm_s<B, true, true>(acc, P.hi, P.lo, Mt.hi, Mt.lo, 32 * mt, 32 * nt, lane);
+            mm_nn<D>(qk, sQ, sK, 32 * mt, 32 * nt, lane);
+            mm_ss(acc, s0, s2, 32 * mt, 32 * nt, lane);
             float* dg = ws.dg + (size_t)blk * B * B;
             const int h = lane >> 5, jj = 32 * nt + (lane & 31);
 #pragma unroll
@@ -416,19 +435,15 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 dg[i * B + jj] = jj <= i ? qk[r] - acc[r] : 0.f;
             }
         } else if (j < ND + NK) {
-            // (M^T Y)[r][x] = sum_a Mt[r][a] Y[a][x];  B^T row x = Y^T row x
             // transposed: (M^T Y)^T[x][r] = sum_a Y^T[x][a] M^T[r][a], lane = key r
             const int t = j - ND, mt = t / DT, nt = t % DT;
-            tile_mm_s<B, true, true>(acc, Yt.hi, Yt.lo, Mt.hi, Mt.lo, 32 * nt, 32 * mt, lane);
+            mm_ss(acc, s1, s2, 32 * nt, 32 * mt, lane);
             float* k32 = ws.k32 ? ws.k32 + (size_t)blk * B * D : nullptr;
             for_tile4(acc, 32 * nt, 32 * mt, lane, [&](int r, int x0, f32x4 a) {
-                f32x4 kv = {0.f, 0.f, 0.f, 0.f};
-                if (r < nvalid) {
-                    const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(kb + r * D + x0);
+                const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(sK + pb<RB>(r, x0));
+                f32x4 val;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) kv[e] = (float)k4[e];
-                }
-                const f32x4 val = kv - a;
+                for (int e = 0; e < 4; ++e) val[e] = (float)k4[e] - a[e];
                 bf16x4 ks;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ks[e] = (__bf16)(val[e] * kscale);
@@ -437,17 +452,17 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 if (k32) *reinterpret_cast<f32x4*>(k32 + r * D + x0) = val;
             });
         } else if (j < ND + NK + NQ) {
+            // (P W)[i][x] = sum_a P[i][a] W[a][x]
             const int t = j - ND - NK, mt = t / DT, nt = t % DT;
-            tile_mm_s<B, true, false>(acc, P.hi, P.lo, sWt, nullptr, 32 * mt, 32 * nt, lane);
+            mm_sc<RB>(acc, s0, sW, 32 * mt, 32 * nt, lane);
             float* ql = ws.ql + (size_t)blk * B * D;
             for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int x, float a) {
-                const float qv = i < nvalid ? (float)qb[i * D + x] : 0.f;
-                ql[i * D + x] = qv - a;
+                ql[i * D + x] = (float)*reinterpret_cast<const __bf16*>(sQ + pb<RB>(i, x)) - a;
             });
         } else {
-            // transposed: E^T[y][x] = sum_a Y^T[y][a] W^T[x][a], lane = row x of E
+            // transposed: E^T[y][x] = sum_a Y^T[y][a] W[a][x], lane = row x of E
             const int t = j - ND - NK - NQ, mt = t / DT, nt = t % DT;
-            tile_mm_s<B, true, false>(acc, Yt.hi, Yt.lo, sWt, nullptr, 32 * nt, 32 * mt, lane);
+            mm_sc<RB>(acc, s1, sW, 32 * nt, 32 * mt, lane);
             float* e32 = ws.e32 ? ws.e32 + (size_t)blk * D * D : nullptr;
             for_tile4(acc, 32 * nt, 32 * mt, lane, [&](int x, int y0, f32x4 a) {
                 bf16x4 es;
@@ -507,7 +522,6 @@ __device__ inline void load_image(__amdgpu_buffer_rsrc_t rsrc, uint32_t src_off,
     }
 }
 
-__device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int D, bool FOX>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
