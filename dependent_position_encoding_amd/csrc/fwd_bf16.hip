@@ -66,18 +66,32 @@ __device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "mem
 
 // ---------------------------------------------------------------------------
 // LDS layout of the preconditioning: no padding; every 16-byte unit of a row
-// sits at a row-dependent XOR position (swz_unit) so that a row fragment (32
-// rows, one unit each) and a transposed fragment (4 rows, 32 bytes each) hit
-// distinct banks.  Byte offsets of element (r, c):
+// sits at a row-dependent XOR position so that a row fragment (16 consecutive
+// rows, one unit each, per quarter-wave) and a transposed fragment (4 rows x
+// 2 adjacent units) both hit 16 distinct 16-byte bank groups.  For 128-byte
+// rows the pair index r / 2 is rotated by one bit first: rows r and r + 2
+// then differ in the upper unit bits, which a plain r / 2 would not give the
+// transposed read.  Byte offsets of element (r, c):
 //   natural bf16 tiles [64][D] (rows of RB = 2 D bytes): pb<RB>(r, c);
 //   bf16 64 x 64 matrices (one part of a split matrix, 128-byte rows): pb<128>;
 //   float 64 x 64 matrices (256-byte rows): pf(r, c).
 template <int RB>
+__device__ __forceinline__ int psw(int r, int u) {
+    if constexpr (RB == 128) {
+        const int s = (r >> 1) & 7;
+        return u ^ (((s & 1) << 2) | (s >> 1));
+    } else if constexpr (RB == 64) {
+        return u ^ ((r >> 2) & 3);
+    } else {
+        return u ^ (r & 15);
+    }
+}
+template <int RB>
 __device__ __forceinline__ int pb(int r, int c) {
-    return r * RB + (swz_unit(r, c >> 3, RB) << 4) + ((c & 7) << 1);
+    return r * RB + (psw<RB>(r, c >> 3) << 4) + ((c & 7) << 1);
 }
 __device__ __forceinline__ int pf(int r, int c) {
-    return r * 256 + (swz_unit(r, c >> 2, 256) << 4) + ((c & 3) << 2);
+    return r * 256 + (psw<256>(r, c >> 2) << 4) + ((c & 3) << 2);
 }
 __device__ __forceinline__ float& fat(char* s, int r, int c) {
     return *reinterpret_cast<float*>(s + pf(r, c));
@@ -90,20 +104,22 @@ template <int RB>
 __device__ __forceinline__ bf16x8 frow(const char* t, int r, int k) {
     return *reinterpret_cast<const bf16x8*>(t + pb<RB>(r, k));
 }
-// Column fragment: rows k .. k+7 of column c (the lane's column; the 16 lanes
-// of a group hold 16 consecutive columns), through gfx950's transposing LDS
-// load: in each group of 16 lanes, lane j names 4 consecutive elements of row
-// k + j/4 starting at column c0 + 4 (j mod 4) (c0 the group's first column),
-// and lane i receives column c0 + i of those 4 rows; a second load covers
-// rows k+4 .. k+7.  Every lane of the wave must take part.
-template <int RB>
+// Column fragment: rows k .. k+3 and k+GAP .. k+GAP+3 of column c (the lane's
+// column; the 16 lanes of a group hold 16 consecutive columns), through
+// gfx950's transposing LDS load: in each group of 16 lanes, lane j names 4
+// consecutive elements of row k + j/4 starting at column c0 + 4 (j mod 4) (c0
+// the group's first column), and lane i receives column c0 + i of those 4
+// rows.  GAP = 4 gives rows k .. k+7; GAP = 8 gives the key order of a C tile
+// reused as an operand (rows k .. k+3 then k+8 .. k+11).  Every lane of the
+// wave must take part.
+template <int RB, int GAP = 4>
 __device__ __forceinline__ bf16x8 fcol(const char* t, int c, int k) {
     typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4;
     const int j = threadIdx.x & 15, r = k + (j >> 2), c4 = c - j + 4 * (j & 3);
     const bf16x4v a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + pb<RB>(r, c4)));
     const bf16x4v b =
-        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + pb<RB>(r + 4, c4)));
+        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + pb<RB>(r + GAP, c4)));
     bf16x8 x;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -192,7 +208,7 @@ __device__ inline void stage_rows(const __bf16* slice_base, int L, int row0, cha
     for (int u0 = 0; u0 < NU; u0 += 512) {
         if (u0 + wave * 64 < NU) {
             const int U = u0 + wave * 64 + lane, r = U / UPR;
-            const uint32_t src = (uint32_t)(row0 + r) * RB + swz_unit(r, U % UPR, RB) * 16;
+            const uint32_t src = (uint32_t)(row0 + r) * RB + psw<RB>(r, U % UPR) * 16;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rs, (__attribute__((address_space(3))) void*)(dst + (u0 + wave * 64) * 16), 16, src,
                 0, 0, 0);
@@ -251,14 +267,14 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     wait_loads();
     __syncthreads();
 
-    // ---- 1. V^T with keys in operand order; G = diag(beta) strictLower(WW^T)
-    for (int u = tid; u < D * 8; u += NTH) {
-        const int x = u / 8, s0i = (u % 8) * 8;
-        bf16x8 pk;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            pk[e] = *reinterpret_cast<const __bf16*>(s2 + pb<RB>(swap23(s0i + e), x));
-        *reinterpret_cast<bf16x8*>(img + I::OFF_V + img_off(x, s0i, I::RB_V)) = pk;
+    // ---- 1. V^T with keys in operand order; G = diag(beta) strictLower(WW^T).
+    //         Image unit (x, 8 sg) holds keys swap23(8 sg + e): rows 16 (sg/2)
+    //         + 4 (sg%2) + {0..3} and those + 8, two transposing reads of V.
+    if (tid < D * 8) {
+        const int g = tid >> 4, cg = g % (D / 16), sg = g / (D / 16);
+        const int x = 16 * cg + (tid & 15);
+        const bf16x8 pk = fcol<RB, 8>(s2, x, 16 * (sg >> 1) + 4 * (sg & 1));
+        *reinterpret_cast<bf16x8*>(img + I::OFF_V + img_off(x, 8 * sg, I::RB_V)) = pk;
     }
     if (wave < 3) {
         const int gmt = wave == 0 ? 0 : 1, gnt = wave == 2 ? 1 : 0;   // G's lower tiles
