@@ -157,12 +157,16 @@ __device__ inline void sput4(char* s, int r, int c, f32x4 v) {
     *reinterpret_cast<bf16x4*>(s + pb<128>(r, c)) = hi;
     *reinterpret_cast<bf16x4*>(s + kPart + pb<128>(r, c)) = lo;
 }
-// acc += A[m0:+32, 0:64] B[n0:+32, 0:64]^T for two split matrices in slots
-// (row fragments, hi and lo of both; lo * lo dropped).
-__device__ inline void mm_ss(f32x16& acc, const char* A, const char* Bn, int m0, int n0, int lane) {
+// acc += A[m0:+32, kb:ke] B[n0:+32, kb:ke]^T for two split matrices in slots
+// (row fragments, hi and lo of both; lo * lo dropped).  [kb, ke) (multiples
+// of 16, uniform in the wave) is where both operands can be nonzero: the
+// block matrices here are triangular, so whole k-steps are exact zeros.
+__device__ inline void mm_ss(f32x16& acc, const char* A, const char* Bn, int m0, int n0, int lane,
+                             int kb = 0, int ke = kB) {
     const int r = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int k0 = 0; k0 < kB; k0 += 16) {
+        if (k0 < kb || k0 >= ke) continue;
         const int k = k0 + 8 * h;
         const bf16x8 ah = frow<128>(A, m0 + r, k), bh = frow<128>(Bn, n0 + r, k);
         acc = mfma32(ah, frow<128>(Bn + kPart, n0 + r, k), acc);
@@ -170,13 +174,16 @@ __device__ inline void mm_ss(f32x16& acc, const char* A, const char* Bn, int m0,
         acc = mfma32(ah, bh, acc);
     }
 }
-// acc += A[m0:+32, 0:64] B[0:64, n0:+32] for a split matrix A in a slot and
-// the natural [64][D] tile B read down its columns (exact bf16).
+// acc += A[m0:+32, kb:ke] B[kb:ke, n0:+32] for a split matrix A in a slot and
+// the natural [64][D] tile B read down its columns (exact bf16); [kb, ke) as
+// for mm_ss.
 template <int RB>
-__device__ inline void mm_sc(f32x16& acc, const char* A, const char* Bt, int m0, int n0, int lane) {
+__device__ inline void mm_sc(f32x16& acc, const char* A, const char* Bt, int m0, int n0, int lane,
+                             int kb = 0, int ke = kB) {
     const int r = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int k0 = 0; k0 < kB; k0 += 16) {
+        if (k0 < kb || k0 >= ke) continue;
         const int k = k0 + 8 * h;
         const bf16x8 b = fcol<RB>(Bt, n0 + r, k);
         acc = mfma32(frow<128>(A + kPart, m0 + r, k), b, acc);
@@ -291,28 +298,34 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     __syncthreads();
 
     // ---- 2. T = (I + G)^{-1}.  Diagonal 16 x 16 blocks by forward
-    //         substitution (waves 0-3, one column per lane); then the
-    //         off-diagonal blocks by doubling on the matrix cores: the inverse
-    //         of a lower block-triangular [[A, 0], [C, B]] has off-diagonal
-    //         block -B^{-1} C A^{-1} (16 -> 32 on waves 0-1, 32 -> 64 on wave
-    //         0).  T is kept in both layouts (T in s1, T^T in s2) so that every
-    //         operand is read along LDS rows.  Meanwhile waves 4-7 form
-    //         X1 = lower(Q W^T) and M^T (M = strictLower(W K^T)) in registers.
+    //         substitution (one column per lane), then the off-diagonal blocks
+    //         by doubling on the matrix cores: the inverse of a lower
+    //         block-triangular [[A, 0], [C, B]] has off-diagonal block
+    //         -B^{-1} C A^{-1}.  Wave w (w = 0, 1) solves diagonal blocks 2w and
+    //         2w + 1 (lanes 0-15 and 16-31) and then the 16 -> 32 step of rows
+    //         and columns [32 w, 32 w + 32), which needs nothing but its own
+    //         results; wave 0 then forms X = G[32:64, 0:32] T[0:32, 0:32] of the
+    //         32 -> 64 step.  After the barrier wave 0 finishes with
+    //         -T[32:64, 32:64] X.  T is kept in both layouts (T in s1, T^T in s2)
+    //         so that every operand is read along LDS rows.  Meanwhile waves 4-7
+    //         form X1 = lower(Q W^T) and M^T (M = strictLower(W K^T)) in
+    //         registers.
     const int xt = wave - 4, xmt = xt >> 1, xnt = xt & 1;
-    f32x16 x1r = zero16(), mtr = zero16();
-    if (wave < 4) {
-        if (lane < 16) {
-            const int o = 16 * wave;
+    const int mrow = lane & 31, hh = lane >> 5;
+    f32x16 x1r = zero16(), mtr = zero16(), x32 = zero16();
+    if (wave < 2) {
+        if (lane < 32) {
+            const int o = 16 * (2 * wave + (lane >> 4)), cl = lane & 15;
             float t[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) t[i] = i == lane ? 1.f : 0.f;
+            for (int i = 0; i < 16; ++i) t[i] = i == cl ? 1.f : 0.f;
 #pragma unroll
             for (int kk = 0; kk < 15; ++kk)
 #pragma unroll
                 for (int i = kk + 1; i < 16; ++i) t[i] -= fat(s0, o + i, o + kk) * t[kk];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) fat(s1, o + i, o + lane) = t[i];
-            const int tr = o + lane;
+            for (int i = 0; i < 16; ++i) fat(s1, o + i, o + cl) = t[i];
+            const int tr = o + cl;
             for (int c4 = 0; c4 < o; c4 += 4)
                 *reinterpret_cast<f32x4*>(s2 + pf(tr, c4)) = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -320,58 +333,64 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 *reinterpret_cast<f32x4*>(s2 + pf(tr, o + c4)) =
                     f32x4{t[c4], t[c4 + 1], t[c4 + 2], t[c4 + 3]};
         }
-    } else if (!(xmt == 0 && xnt == 1)) {
-        mm_nn<D>(x1r, sW, sQ, 32 * xnt, 32 * xmt, lane);     // (Q W^T)^T tile: lane = row of X1
-    }
-    __syncthreads();
-    const int mrow = lane & 31, hh = lane >> 5;
-    if (wave < 2) {
-        // 16 -> 32 inside rows/columns [o2, o2 + 32): X = G_10 T_00, Y = -T_11 X
-        const int o2 = 32 * wave;
-        const bool ok = mrow < 16;
-        bf16x8 ah, al, bh, bl;
-        fsplit8<false>(s0, o2 + 16 + mrow, o2, hh, ok, ah, al);
-        fsplit8<false>(s2, o2 + mrow, o2, hh, ok, bh, bl);
-        const f32x16 x = mfma_split(ah, al, bh, bl, zero16());
-        // X's C tile (rows 0-15 in registers 0-7) is the B operand of T_11 X
+        // the wave's own LDS writes above are read back below by other lanes:
+        // keep the compiler from moving those reads ahead of the writes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        {
+            // 16 -> 32 inside rows/columns [o2, o2 + 32): X = G_10 T_00, Y = -T_11 X
+            const int o2 = 32 * wave;
+            const bool ok = mrow < 16;
+            bf16x8 ah, al, bh, bl;
+            fsplit8<false>(s0, o2 + 16 + mrow, o2, hh, ok, ah, al);
+            fsplit8<false>(s2, o2 + mrow, o2, hh, ok, bh, bl);
+            const f32x16 x = mfma_split(ah, al, bh, bl, zero16());
+            // X's C tile (rows 0-15 in registers 0-7) is the B operand of T_11 X
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            bh[e] = (__bf16)x[e];
-            bl[e] = (__bf16)(x[e] - (float)bh[e]);
-        }
-        fsplit8<true>(s1, o2 + 16 + mrow, o2 + 16, hh, ok, ah, al);
-        const f32x16 y = mfma_split(ah, al, bh, bl, zero16());
-        if (ok) {
+            for (int e = 0; e < 8; ++e) {
+                bh[e] = (__bf16)x[e];
+                bl[e] = (__bf16)(x[e] - (float)bh[e]);
+            }
+            fsplit8<true>(s1, o2 + 16 + mrow, o2 + 16, hh, ok, ah, al);
+            const f32x16 y = mfma_split(ah, al, bh, bl, zero16());
+            if (ok) {
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int row = crow(r, hh);
-                fat(s1, o2 + 16 + row, o2 + mrow) = -y[r];
-                fat(s2, o2 + mrow, o2 + 16 + row) = -y[r];
+                for (int r = 0; r < 8; ++r) {
+                    const int row = crow(r, hh);
+                    fat(s1, o2 + 16 + row, o2 + mrow) = -y[r];
+                    fat(s2, o2 + mrow, o2 + 16 + row) = -y[r];
+                }
             }
         }
-    } else if (wave >= 4 && !(xmt == 1 && xnt == 0)) {
-        // M^T[j][b] = k_j . w_b for b > j (transposed tile: lane = row j)
-        mm_nn<D>(mtr, sW, sK, 32 * xnt, 32 * xmt, lane);
+        if (wave == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // 32 -> 64, first product: X = G[32:64, 0:32] T[0:32, 0:32]
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                bf16x8 ah, al, bh, bl;
+                fsplit8<false>(s0, 32 + mrow, 16 * ks, hh, true, ah, al);
+                fsplit8<false>(s2, mrow, 16 * ks, hh, true, bh, bl);
+                x32 = mfma_split(ah, al, bh, bl, x32);
+            }
+        }
+    } else if (wave >= 4) {
+        if (!(xmt == 0 && xnt == 1))
+            mm_nn<D>(x1r, sW, sQ, 32 * xnt, 32 * xmt, lane);     // (Q W^T)^T: lane = row of X1
+        if (!(xmt == 1 && xnt == 0))
+            mm_nn<D>(mtr, sW, sK, 32 * xnt, 32 * xmt, lane);     // M^T[j][b] = k_j . w_b, lane = j
     }
     __syncthreads();
     if (wave == 0) {
-        // 32 -> 64: X = G[32:64, 0:32] T[0:32, 0:32], Y = -T[32:64, 32:64] X
-        f32x16 x = zero16();
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 ah, al, bh, bl;
-            fsplit8<false>(s0, 32 + mrow, 16 * ks, hh, true, ah, al);
-            fsplit8<false>(s2, mrow, 16 * ks, hh, true, bh, bl);
-            x = mfma_split(ah, al, bh, bl, x);
-        }
+        // 32 -> 64, second product: Y = -T[32:64, 32:64] X
         f32x16 y = zero16();
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             bf16x8 ah, al, bh, bl;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                bh[e] = (__bf16)x[8 * ks + e];
-                bl[e] = (__bf16)(x[8 * ks + e] - (float)bh[e]);
+                bh[e] = (__bf16)x32[8 * ks + e];
+                bl[e] = (__bf16)(x32[8 * ks + e] - (float)bh[e]);
             }
             fsplit8<true>(s1, 32 + mrow, 32 + 16 * ks, hh, true, ah, al);
             y = mfma_split(ah, al, bh, bl, y);
@@ -418,10 +437,11 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const int nt = wave < 4 ? wave & 1 : (wave - 4) % 2;
         if (wave < 4) {
             // P^T[a][i] = sum_k U^T[a][k] X1[i][k]
-            if (!(mt == 0 && nt == 1)) mm_ss(acc, s1, s0, 32 * nt, 32 * mt, lane);
+            // X1 lower (c <= i) and U lower (c >= a): c in [32 nt, 32 (mt + 1))
+            if (!(mt == 0 && nt == 1)) mm_ss(acc, s1, s0, 32 * nt, 32 * mt, lane, 32 * nt, 32 * (mt + 1));
         } else if (wave < 4 + 2 * DT) {
-            // Y[cc][y] = sum_a U^T[cc][a] W[a][y]
-            mm_sc<RB>(acc, s1, sW, 32 * nt, 32 * mt, lane);
+            // Y[cc][y] = sum_a U^T[cc][a] W[a][y]  (U lower: a >= cc)
+            mm_sc<RB>(acc, s1, sW, 32 * nt, 32 * mt, lane, 32 * nt, kB);
         }
         __syncthreads();
         if (wave < 4)
@@ -442,7 +462,8 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const int mt = j == 0 ? 0 : 1, nt = j == 2 ? 1 : 0;
             f32x16 qk = zero16();
             mm_nn<D>(qk, sQ, sK, 32 * mt, 32 * nt, lane);
-            mm_ss(acc, s0, s2, 32 * mt, 32 * nt, lane);
+            // P lower (a <= i), M strictly lower (a > j): a in [32 nt, 32 (mt + 1))
+            mm_ss(acc, s0, s2, 32 * mt, 32 * nt, lane, 32 * nt, 32 * (mt + 1));
             float* dg = ws.dg + (size_t)blk * B * B;
             const int h = lane >> 5, jj = 32 * nt + (lane & 31);
 #pragma unroll
@@ -453,7 +474,7 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         } else if (j < ND + NK) {
             // transposed: (M^T Y)^T[x][r] = sum_a Y^T[x][a] M^T[r][a], lane = key r
             const int t = j - ND, mt = t / DT, nt = t % DT;
-            mm_ss(acc, s1, s2, 32 * nt, 32 * mt, lane);
+            mm_ss(acc, s1, s2, 32 * nt, 32 * mt, lane, 32 * mt, kB);   // M^T[r][a]: a > r
             float* k32 = ws.k32 ? ws.k32 + (size_t)blk * B * D : nullptr;
             for_tile4(acc, 32 * nt, 32 * mt, lane, [&](int r, int x0, f32x4 a) {
                 const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(sK + pb<RB>(r, x0));
@@ -470,7 +491,7 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         } else if (j < ND + NK + NQ) {
             // (P W)[i][x] = sum_a P[i][a] W[a][x]
             const int t = j - ND - NK, mt = t / DT, nt = t % DT;
-            mm_sc<RB>(acc, s0, sW, 32 * mt, 32 * nt, lane);
+            mm_sc<RB>(acc, s0, sW, 32 * mt, 32 * nt, lane, 0, 32 * (mt + 1));   // P lower: a <= i
             float* ql = ws.ql + (size_t)blk * B * D;
             for_tile(acc, 32 * mt, 32 * nt, lane, [&](int i, int x, float a) {
                 ql[i * D + x] = (float)*reinterpret_cast<const __bf16*>(sQ + pb<RB>(i, x)) - a;

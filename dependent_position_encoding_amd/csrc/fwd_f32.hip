@@ -67,20 +67,22 @@ precond_f32_kernel(const T* __restrict__ q, const T* __restrict__ k,
         sX[i][j] = s;
     }
     __syncthreads();
-    // T = (I + G)^{-1} by forward substitution, one column per thread:
-    //   T_jj = 1,  T_ij = -sum_{k=j}^{i-1} G_ik T_kj  (i > j).
+    // T = (I + G)^{-1} by forward substitution, one column per thread,
+    //   T_jj = 1,  T_ij = -sum_{k=j}^{i-1} G_ik T_kj  (i > j),
+    // with the column in registers: t = e_j, then for k = 0, 1, ... every
+    // t_i (i > k) takes its term -G_ik t_k (terms with k < j add exact zeros),
+    // so each entry sees the same operations in the same order as the sum.
     if (tid < B) {
         const int j = tid;
-        for (int i = 0; i < B; ++i) {
-            float t;
-            if (i < j) t = 0.f;
-            else if (i == j) t = 1.f;
-            else {
-                t = 0.f;
-                for (int kk = j; kk < i; ++kk) t -= sX[i][kk] * sU[kk][j];
-            }
-            sU[i][j] = t;
-        }
+        float t[B];
+#pragma unroll
+        for (int i = 0; i < B; ++i) t[i] = i == j ? 1.f : 0.f;
+#pragma unroll
+        for (int kk = 0; kk < B - 1; ++kk)
+#pragma unroll
+            for (int i = kk + 1; i < B; ++i) t[i] -= sX[i][kk] * t[kk];
+#pragma unroll
+        for (int i = 0; i < B; ++i) sU[i][j] = t[i];
     }
     __syncthreads();
     // U = T diag(beta)
