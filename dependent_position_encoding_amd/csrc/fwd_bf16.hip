@@ -586,6 +586,19 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
 
     f32x16 Qw[NT], Ot[NT], S[2];
     float m = 0.f, l = 0.f, gq = 0.f, grun = 0.f;
+    // the lane's row of the diagonal tile's in-block logits, fetched with the
+    // queries (before the first wait) so that the diagonal step does not wait
+    // on HBM a second time
+    f32x4 dgr[8];
+    if (myb >= 0) {
+        const size_t bq = blk0 + myb;
+        const float* dgp = ws.dg + (bq * B + qloc) * B;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dgr[4 * mt + i] = *reinterpret_cast<const f32x4*>(dgp + 32 * mt + 8 * i + 4 * h);
+    }
     if (myb >= 0) {
         const size_t bq = blk0 + myb;
         const float* qlp = ws.ql + (bq * B + qloc) * D;
@@ -631,8 +644,6 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
     };
 
     auto diag = [&](const char* im) {
-        const size_t bq = blk0 + myb;
-        const float* dgp = ws.dg + (bq * B + qloc) * B;
         const float* gimg = reinterpret_cast<const float*>(im + I::OFF_G);
         float mx = -INFINITY;
 #pragma unroll
@@ -640,7 +651,7 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int k0 = 32 * mt + 8 * i + 4 * h;
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(dgp + k0);
+                const f32x4 d4 = dgr[4 * mt + i];
                 f32x4 g4 = {0.f, 0.f, 0.f, 0.f};
                 if (FOX) g4 = *reinterpret_cast<const f32x4*>(gimg + k0);
 #pragma unroll
