@@ -243,7 +243,7 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     //   s2 : V (natural bf16) -> T^T (float)   -> M^T (split)
     __shared__ __attribute__((aligned(16))) char sQ[B * RB], sK[B * RB], sW[B * RB];
     __shared__ __attribute__((aligned(16))) char s0[kSlot], s1[kSlot], s2[kSlot];
-    __shared__ float sBeta[B];
+    __shared__ __attribute__((aligned(16))) float sBeta[B];
 
     const int blk = blockIdx.x, slice = blk / nb, c = blk % nb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -277,6 +277,10 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     // ---- 1. V^T with keys in operand order; G = diag(beta) strictLower(WW^T).
     //         Image unit (x, 8 sg) holds keys swap23(8 sg + e): rows 16 (sg/2)
     //         + 4 (sg%2) + {0..3} and those + 8, two transposing reads of V.
+    //         Inside each diagonal 16 x 16 block the upper triangle holds G
+    //         transposed (entry (k, i), k < i, is G[i][k] = beta_i (w_i . w_k),
+    //         WW^T being symmetric), so the forward substitution reads a column
+    //         of G as one row; nothing else reads that triangle.
     if (tid < D * 8) {
         const int g = tid >> 4, cg = g % (D / 16), sg = g / (D / 16);
         const int x = 16 * cg + (tid & 15);
@@ -289,9 +293,12 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         mm_nn<D>(acc, sW, sW, 32 * gnt, 32 * gmt, lane);   // (W W^T)^T tile: lane = row i of G
         for_tile4(acc, 32 * gnt, 32 * gmt, lane, [&](int i, int j0, f32x4 v) {
             const float bi = sBeta[i];
+            const bool dblk = (i >> 4) == (j0 >> 4);   // j0 .. j0 + 3 share a 16-block
+            const f32x4 bj = *reinterpret_cast<const f32x4*>(sBeta + j0);
             f32x4 g;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) g[e] = i > j0 + e ? bi * v[e] : 0.f;
+            for (int e = 0; e < 4; ++e)
+                g[e] = i > j0 + e ? bi * v[e] : (dblk && j0 + e > i ? bj[e] * v[e] : 0.f);
             *reinterpret_cast<f32x4*>(s0 + pf(i, j0)) = g;
         });
     }
@@ -319,10 +326,18 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             float t[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) t[i] = i == cl ? 1.f : 0.f;
+            // right-looking: once t[kk] is final, t[i] -= G[i][kk] t[kk] for
+            // i > kk, with G[o + i][o + kk] read as row kk of the block's upper
+            // triangle, 16 bytes (four i) at a time
 #pragma unroll
             for (int kk = 0; kk < 15; ++kk)
 #pragma unroll
-                for (int i = kk + 1; i < 16; ++i) t[i] -= fat(s0, o + i, o + kk) * t[kk];
+                for (int u = (kk + 1) >> 2; u < 4; ++u) {
+                    const f32x4 g4 = *reinterpret_cast<const f32x4*>(s0 + pf(o + kk, o + 4 * u));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * u + e > kk) t[4 * u + e] -= g4[e] * t[kk];
+                }
 #pragma unroll
             for (int i = 0; i < 16; ++i) fat(s1, o + i, o + cl) = t[i];
             const int tr = o + cl;
