@@ -477,8 +477,12 @@ decode_combine_kernel(const float* __restrict__ part, int nch, int pstride, int 
 // so that S_c = T_c Z_{g(c)} (align_apply_kernel).  All in fp32.
 constexpr int kSufGroup = 16;
 
-// The d x d products run on the matrix cores with fp32 operands split into
-// three bf16 parts (tile_mm_f32), on matrices padded to DP = max(d, 32).  The
+// The d x d products run on the matrix cores on matrices padded to
+// DP = max(d, 32), with fp32 operands split into bf16 parts: three parts and
+// six partial products (tile_mm_f32, fp32 accuracy) for an fp32 key cache;
+// two parts and three partial products (tile_mm, ~16 significant bits) for a
+// bf16 cache, whose own rounding (2^-9) is far coarser than what a chain of
+// at most kSufGroup + ceil(nb / kSufGroup) such products accumulates.  The
 // chain is kept transposed (S^T <- S^T - S^T E^T) so that every product reads
 // both operands row-major from LDS.  Stored: suf[c] = T_c^T, grp[g][0] = G_g,
 // grp[g][1] = Z_g^T.
@@ -518,7 +522,15 @@ struct MatRegs {
     }
 };
 
-template <int D>
+// acc += A B^T over a DP x DP tile pair at the chain's precision
+template <int DP, bool F32>
+__device__ inline void chain_mm(f32x16& acc, const float* A, const float* Bn, int m0, int n0,
+                                int lane) {
+    if constexpr (F32) tile_mm_f32<DP>(acc, A, kMS, Bn, kMS, m0, n0, lane);
+    else tile_mm<DP, float, float>(acc, A, kMS, Bn, kMS, m0, n0, lane);
+}
+
+template <int D, bool F32>
 __global__ void __launch_bounds__(256)
 suffix_local_kernel(int nb, int ngroups, FwdWs ws) {
     using P = Pad<D>;
@@ -540,7 +552,7 @@ suffix_local_kernel(int nb, int ngroups, FwdWs ws) {
         f32x16 acc = zero16();
         const int mt = wave / P::DT, nt = wave % P::DT;
         const bool mine = wave < P::DT * P::DT;
-        if (mine) tile_mm_f32<P::DP>(acc, sSt, kMS, sE, kMS, 32 * mt, 32 * nt, lane);
+        if (mine) chain_mm<P::DP, F32>(acc, sSt, sE, 32 * mt, 32 * nt, lane);
         const int h = lane >> 5, y = 32 * nt + (lane & 31);
         float nv[16];
         if (mine) {
@@ -564,7 +576,7 @@ suffix_local_kernel(int nb, int ngroups, FwdWs ws) {
     }
 }
 
-template <int D>
+template <int D, bool F32>
 __global__ void __launch_bounds__(256)
 suffix_groups_kernel(int nb, int ngroups, FwdWs ws) {
     using P = Pad<D>;
@@ -603,7 +615,7 @@ suffix_groups_kernel(int nb, int ngroups, FwdWs ws) {
         f32x16 acc = zero16();
         const int mt = wave / P::DT, nt = wave % P::DT;
         const bool mine = wave < P::DT * P::DT;
-        if (mine) tile_mm_f32<P::DP>(acc, sZt, kMS, sG, kMS, 32 * mt, 32 * nt, lane);
+        if (mine) chain_mm<P::DP, F32>(acc, sZt, sG, 32 * mt, 32 * nt, lane);
         __syncthreads();
         if (mine) {
             const int h = lane >> 5, y = 32 * nt + (lane & 31);
@@ -646,6 +658,15 @@ __device__ inline void ld8_split(const float* base, int ld, int row, int nr, int
 // stored), then kcache^T = Z_g^T X^T with X^T's C tiles reused directly as
 // the B operand.  Products use fp32 operands split into bf16 hi + lo (about
 // 16 significant bits), well below the bf16 or fp32 rounding of the cache.
+// Workgroups go to the 8 XCDs round-robin; the workgroups of one XCD take
+// consecutive block pairs, so that the blocks of a suffix group, which all
+// read that group's Z_g, run in one XCD and find it in its L2.
+__device__ inline int xcd_major(int b, int n) {
+    const int full = n & ~7;
+    if (b >= full) return b;
+    return (b & 7) * (full >> 3) + (b >> 3);
+}
+
 template <typename K, typename T, int B, int D>
 __global__ void __launch_bounds__(256)
 align_apply_kernel(int L, int nb, int ngroups, int nblk, FwdWs ws, const T* __restrict__ v,
@@ -655,7 +676,8 @@ align_apply_kernel(int L, int nb, int ngroups, int nblk, FwdWs ws, const T* __re
     constexpr int BP = B < 32 ? 32 : B, RT = BP / 32, BPW = 4 / RT;   // blocks per workgroup
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
     const int col = lane & 31;
-    const int blk = blockIdx.x * BPW + wave / RT, rt = wave % RT;
+    const int wg = xcd_major(blockIdx.x, gridDim.x);
+    const int blk = wg * BPW + wave / RT, rt = wave % RT;
     if (blk < nblk) {
         const int slice = blk / nb, c = blk % nb, g = c / kSufGroup;
         const float* Tt = ws.suf + (size_t)blk * D * D;
@@ -722,7 +744,7 @@ align_apply_kernel(int L, int nb, int ngroups, int nblk, FwdWs ws, const T* __re
     // values (16-byte units) and the gate prefix of this workgroup's blocks
     constexpr int UPR = D * (int)sizeof(T) / 16;
     for (int u = tid; u < BPW * B * UPR; u += 256) {
-        const int b2 = blockIdx.x * BPW + u / (B * UPR), rr = (u / UPR) % B, x = u % UPR;
+        const int b2 = wg * BPW + u / (B * UPR), rr = (u / UPR) % B, x = u % UPR;
         if (b2 >= nblk) continue;
         const int slice = b2 / nb, pos = (b2 % nb) * B + rr;
         if (pos < L)
@@ -731,7 +753,7 @@ align_apply_kernel(int L, int nb, int ngroups, int nblk, FwdWs ws, const T* __re
     }
     if (gc) {
         for (int u = tid; u < BPW * B; u += 256) {
-            const int b2 = blockIdx.x * BPW + u / B, rr = u % B;
+            const int b2 = wg * BPW + u / B, rr = u % B;
             if (b2 >= nblk) continue;
             const int slice = b2 / nb, pos = (b2 % nb) * B + rr;
             if (pos < L)
@@ -967,10 +989,11 @@ static hipError_t align_t(const FwdArgs& a, const CacheArgs& c, hipStream_t st) 
     const int nb = (a.L + B - 1) / B;
     const int ng = suffix_groups(nb);
     const int NH = a.N * a.H;
-    hipLaunchKernelGGL((suffix_local_kernel<D>), dim3(NH * ng), dim3(256), 0, st, nb, ng, a.ws);
+    constexpr bool F32 = sizeof(K) == 4;   // the chain at the key cache's precision
+    hipLaunchKernelGGL((suffix_local_kernel<D, F32>), dim3(NH * ng), dim3(256), 0, st, nb, ng, a.ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((suffix_groups_kernel<D>), dim3(NH), dim3(256), 0, st, nb, ng, a.ws);
+    hipLaunchKernelGGL((suffix_groups_kernel<D, F32>), dim3(NH), dim3(256), 0, st, nb, ng, a.ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     constexpr int BPW = 4 / ((B < 32 ? 32 : B) / 32);   // blocks per workgroup
     const int nblk = NH * nb;
