@@ -634,19 +634,28 @@ suffix_groups_kernel(int nb, int ngroups, FwdWs ws) {
 // hi + lo operand pair: columns c0 + 8h .. +7, or with PERM the columns
 // c0 + swap23(8h + e) that match a C tile reused as the other operand.  Rows
 // at or beyond nr and column groups at or beyond nc read as zero.
+// The load (ld8_raw) and the split (split8) are separate so that a product's
+// operand loads can all be in flight before its first matrix instruction.
+struct F8 {
+    f32x4 a, b;
+};
 template <bool PERM>
-__device__ inline void ld8_split(const float* base, int ld, int row, int nr, int c0, int nc,
-                                 int h, bf16x8& hi, bf16x8& lo) {
-    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
+__device__ inline F8 ld8_raw(const float* base, int ld, int row, int nr, int c0, int nc, int h) {
+    F8 v;
+    v.a = f32x4{0.f, 0.f, 0.f, 0.f};
+    v.b = v.a;
     if (row < nr && c0 < nc) {
         const float* p = base + (size_t)row * ld + c0;
         const int o0 = PERM ? 4 * h : 8 * h, o1 = PERM ? 8 + 4 * h : 8 * h + 4;
-        a = *reinterpret_cast<const f32x4*>(p + o0);
-        b = *reinterpret_cast<const f32x4*>(p + o1);
+        v.a = *reinterpret_cast<const f32x4*>(p + o0);
+        v.b = *reinterpret_cast<const f32x4*>(p + o1);
     }
+    return v;
+}
+__device__ inline void split8(const F8& v, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const float x = e < 4 ? a[e] : b[e - 4];
+        const float x = e < 4 ? v.a[e] : v.b[e - 4];
         hi[e] = (__bf16)x;
         lo[e] = (__bf16)(x - (float)hi[e]);
     }
@@ -656,7 +665,9 @@ __device__ inline void ld8_split(const float* base, int ld, int row, int nr, int
 // prefix + in-block cumsum.  Register-only: a wave owns 32 keys of one block
 // and forms X^T = T_c^T Kright_c^T (operands read from HBM as they are
 // stored), then kcache^T = Z_g^T X^T with X^T's C tiles reused directly as
-// the B operand.  Products use fp32 operands split into bf16 hi + lo (about
+// the B operand.  Each product's operand loads are all issued before its
+// first matrix instruction (two memory round trips per wave, not one per
+// k-step).  Products use fp32 operands split into bf16 hi + lo (about
 // 16 significant bits), well below the bf16 or fp32 rounding of the cache.
 // Workgroups go to the 8 XCDs round-robin; the workgroups of one XCD take
 // consecutive block pairs, so that the blocks of a suffix group, which all
@@ -678,15 +689,35 @@ align_apply_kernel(int L, int nb, int ngroups, int nblk, FwdWs ws, const T* __re
     const int col = lane & 31;
     const int wg = xcd_major(blockIdx.x, gridDim.x);
     const int blk = wg * BPW + wave / RT, rt = wave % RT;
+    // value unit i of this thread: (its slice, its position, its 16-byte unit x)
+    constexpr int UPR = D * (int)sizeof(T) / 16, NU = BPW * B * UPR, NVU = (NU + 255) / 256;
+    auto vunit = [&](int i, int& slice, int& pos, int& x) {
+        const int u = tid + 256 * i, b2 = wg * BPW + u / (B * UPR), rr = (u / UPR) % B;
+        x = u % UPR;
+        slice = b2 / nb;
+        pos = (b2 % nb) * B + rr;
+        return u < NU && b2 < nblk && pos < L;
+    };
+    const int slice = blk / nb, c = blk % nb, g = c / kSufGroup;
+    const int r = 32 * rt + col;                 // this lane's key (B-operand column)
+    // X^T's C tiles as the B operand of the second product: k-step ks holds
+    // rows 16 ks + swap23(slot)
+    bf16x8 bh[KS], bl[KS];
     if (blk < nblk) {
-        const int slice = blk / nb, c = blk % nb, g = c / kSufGroup;
         const float* Tt = ws.suf + (size_t)blk * D * D;
-        const float* Zt = ws.grp + (((size_t)slice * ngroups + g) * 2 + 1) * D * D;
         const float* kr = ws.k32 + (size_t)blk * B * D;
-        const int r = 32 * rt + col;                 // this lane's key (B-operand column)
+        F8 kv[KS], tv[XT][KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kv[ks] = ld8_raw<false>(kr, D, r, B, 16 * ks, D, h);
+#pragma unroll
+        for (int t = 0; t < XT; ++t)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                tv[t][ks] = ld8_raw<false>(Tt, D, 32 * t + col, D, 16 * ks, D, h);
+        __builtin_amdgcn_sched_barrier(0);   // every load above issued before the products
         bf16x8 kh[KS], kl[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) ld8_split<false>(kr, D, r, B, 16 * ks, D, h, kh[ks], kl[ks]);
+        for (int ks = 0; ks < KS; ++ks) split8(kv[ks], kh[ks], kl[ks]);
         f32x16 xt[XT];
 #pragma unroll
         for (int t = 0; t < XT; ++t) {
@@ -694,12 +725,10 @@ align_apply_kernel(int L, int nb, int ngroups, int nblk, FwdWs ws, const T* __re
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 bf16x8 ah, al;
-                ld8_split<false>(Tt, D, 32 * t + col, D, 16 * ks, D, h, ah, al);
+                split8(tv[t][ks], ah, al);
                 xt[t] = mfma_split(ah, al, kh[ks], kl[ks], xt[t]);
             }
         }
-        // X^T's C tiles as the B operand: k-step ks holds rows 16 ks + swap23(slot)
-        bf16x8 bh[KS], bl[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -708,15 +737,47 @@ align_apply_kernel(int L, int nb, int ngroups, int nblk, FwdWs ws, const T* __re
                 bh[ks][e] = (__bf16)x;
                 bl[ks][e] = (__bf16)(x - (float)bh[ks][e]);
             }
+    }
+    // values (16-byte units) and the gate prefix of this workgroup's blocks,
+    // loaded beside the second product's operands and stored at the end
+    u32x4 vv[NVU];
+#pragma unroll
+    for (int i = 0; i < NVU; ++i) {
+        int vs, vp, x;
+        vv[i] = vunit(i, vs, vp, x) ? reinterpret_cast<const u32x4*>(v + ((size_t)vs * L + vp) * D)[x]
+                                    : u32x4{0u, 0u, 0u, 0u};
+    }
+    float gpre = 0.f, gin = 0.f;     // added at the store, so nothing waits on them here
+    size_t gdst = ~(size_t)0;
+    if (gc && tid < BPW * B) {
+        const int b2 = wg * BPW + tid / B, rr = tid % B;
+        const int gs = b2 / nb, gp = (b2 % nb) * B + rr;
+        if (b2 < nblk && gp < L) {
+            gdst = (size_t)gs * cap + gp;
+            if (has_gate) {
+                gpre = ws.gpre[b2];
+                gin = ws.gl[(size_t)b2 * B + rr];
+            }
+        }
+    }
+    if (blk < nblk) {
+        const float* Zt = ws.grp + (((size_t)slice * ngroups + g) * 2 + 1) * D * D;
         const int pos = c * B + r;
         K* krow = kc + ((size_t)slice * cap + pos) * D;
+        F8 zv[XT][KS];
+#pragma unroll
+        for (int yt = 0; yt < XT; ++yt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                zv[yt][ks] = ld8_raw<true>(Zt, D, 32 * yt + col, D, 16 * ks, D, h);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int yt = 0; yt < XT; ++yt) {
             f32x16 acc = zero16();
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 bf16x8 ah, al;
-                ld8_split<true>(Zt, D, 32 * yt + col, D, 16 * ks, D, h, ah, al);
+                split8(zv[yt][ks], ah, al);
                 acc = mfma_split(ah, al, bh[ks], bl[ks], acc);
             }
             if (r < B && pos < L) {
@@ -741,26 +802,12 @@ align_apply_kernel(int L, int nb, int ngroups, int nblk, FwdWs ws, const T* __re
             }
         }
     }
-    // values (16-byte units) and the gate prefix of this workgroup's blocks
-    constexpr int UPR = D * (int)sizeof(T) / 16;
-    for (int u = tid; u < BPW * B * UPR; u += 256) {
-        const int b2 = wg * BPW + u / (B * UPR), rr = (u / UPR) % B, x = u % UPR;
-        if (b2 >= nblk) continue;
-        const int slice = b2 / nb, pos = (b2 % nb) * B + rr;
-        if (pos < L)
-            reinterpret_cast<u32x4*>(vc + ((size_t)slice * cap + pos) * D)[x] =
-                reinterpret_cast<const u32x4*>(v + ((size_t)slice * L + pos) * D)[x];
+#pragma unroll
+    for (int i = 0; i < NVU; ++i) {
+        int vs, vp, x;
+        if (vunit(i, vs, vp, x)) reinterpret_cast<u32x4*>(vc + ((size_t)vs * cap + vp) * D)[x] = vv[i];
     }
-    if (gc) {
-        for (int u = tid; u < BPW * B; u += 256) {
-            const int b2 = wg * BPW + u / B, rr = u % B;
-            if (b2 >= nblk) continue;
-            const int slice = b2 / nb, pos = (b2 % nb) * B + rr;
-            if (pos < L)
-                gc[(size_t)slice * cap + pos] =
-                    has_gate ? ws.gpre[b2] + ws.gl[(size_t)b2 * B + rr] : 0.f;
-        }
-    }
+    if (gdst != ~(size_t)0) gc[gdst] = gpre + gin;
 }
 
 // ---------------------------------------------------------------------------
