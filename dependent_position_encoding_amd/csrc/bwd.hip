@@ -1661,7 +1661,19 @@ bwd_precond_b16_kernel(int L, int nb, int slice0, const bf16* __restrict__ q,
     const int qt = half_tile(1, kB, D, 0);
     const int qm0 = qt >= 0 ? (qt / (D / 32)) * 32 : 0, qn0 = qt >= 0 ? (qt % (D / 32)) * 32 : 0;
     f32x16 aQ = zero16(), aK = zero16();
+    // the tile's dQl and dKr terms of the outputs, fetched now (in the tile's
+    // C layout) so that the final stores do not wait on them one by one
+    f32x16 dqv = zero16(), dkv = zero16();
     if (qt >= 0) {
+        const int r = threadIdx.x & 31, h = (threadIdx.x >> 5) & 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int m = qm0 + 8 * i + 4 * h + j, n = qn0 + r;
+                dqv[4 * i + j] = dql[m * D + n];
+                dkv[4 * i + j] = dkr[m * D + n];
+            }
         aQ = tprod<false, true, kB>(sDg, sK, qm0, qn0, aQ);
         aK = tprod<true, true, kB>(sDg, sQ, qm0, qn0, aK);
     }
@@ -1786,13 +1798,17 @@ bwd_precond_b16_kernel(int L, int nb, int slice0, const bf16* __restrict__ q,
         });
     }
     if (qt >= 0) {
+        int e = 0;
         for_tile(qt, D, aQ, [&](int m, int n, float v) {
             const int pos = c * kB + m;
-            if (pos < L) dq[(base + pos) * D + n] = from_f32<bf16>(v + dql[m * D + n]);
+            if (pos < L) dq[(base + pos) * D + n] = from_f32<bf16>(v + dqv[e]);
+            ++e;
         });
+        e = 0;
         for_tile(qt, D, aK, [&](int m, int n, float v) {
             const int pos = c * kB + m;
-            if (pos < L) dk[(base + pos) * D + n] = from_f32<bf16>(v + dkr[m * D + n]);
+            if (pos < L) dk[(base + pos) * D + n] = from_f32<bf16>(v + dkv[e]);
+            ++e;
         });
     }
     __syncthreads();
