@@ -1032,17 +1032,31 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     const int rb4 = tid / (D / 4), cb4 = tid % (D / 4);   // this thread's 4 x 4 block
     const int rb8 = tid / (D / 8), cb8 = tid % (D / 8);   // and 4 x 8 block
 
-    {   // resident: Kr_c, V_c
+    {   // resident: Kr_c, V_c (every load in flight before the first LDS write)
         const float* krc = static_cast<const float*>(fw.kr) + blk_c * kB * D;
-        for (int e = tid; e < kB * D / 4; e += 256) {
-            const int r = e / (D / 4), c0 = 4 * (e % (D / 4));
-            sK.put4(r, c0, *reinterpret_cast<const f32x4*>(krc + (size_t)r * D + c0));
+        constexpr int NK4 = kB * D / 4 / 256, NV8 = (kB * D / 8 + 255) / 256;
+        f32x4 kq[NK4];
+        u32x4 vq[NV8];
+#pragma unroll
+        for (int it = 0; it < NK4; ++it) {
+            const int e = tid + 256 * it, r = e / (D / 4), c0 = 4 * (e % (D / 4));
+            kq[it] = *reinterpret_cast<const f32x4*>(krc + (size_t)r * D + c0);
         }
-        for (int e = tid; e < kB * D / 8; e += 256) {
-            const int r = e / (D / 8), c0 = 8 * (e % (D / 8)), pos = c * kB + r;
-            u32x4 u = {0u, 0u, 0u, 0u};
-            if (pos < L) u = *reinterpret_cast<const u32x4*>(v + (base + pos) * D + c0);
-            *reinterpret_cast<u32x4*>(&sV.v[0][r * sV.LDE + c0]) = u;
+#pragma unroll
+        for (int it = 0; it < NV8; ++it) {
+            const int e = tid + 256 * it, r = e / (D / 8), c0 = 8 * (e % (D / 8)), pos = c * kB + r;
+            vq[it] = u32x4{0u, 0u, 0u, 0u};
+            if (e < kB * D / 8 && pos < L) vq[it] = *reinterpret_cast<const u32x4*>(v + (base + pos) * D + c0);
+        }
+#pragma unroll
+        for (int it = 0; it < NK4; ++it) {
+            const int e = tid + 256 * it, r = e / (D / 4), c0 = 4 * (e % (D / 4));
+            sK.put4(r, c0, kq[it]);
+        }
+#pragma unroll
+        for (int it = 0; it < NV8; ++it) {
+            const int e = tid + 256 * it, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            if (e < kB * D / 8) *reinterpret_cast<u32x4*>(&sV.v[0][r * sV.LDE + c0]) = vq[it];
         }
     }
     if (tid < kB) {
@@ -1052,9 +1066,10 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     // prefetch of query block b's X_bc, Z_bc (4 x 4 bf16 blocks), dO and row terms
     bf16x4_t pX[4], pZ[4];
     u32x4 pO[4];
-    float pLse = 0.f, pDel = 0.f, pGb = 0.f;
+    float pLse = 0.f, pDel = 0.f, pGb = 0.f, pTot = 0.f;   // pTot: the gate total of block b - 1
     auto prefetch = [&](int b) {
         const size_t blk_b = slice * nb + b;
+        pTot = fox && b >= 1 ? fw.tot[blk_b - 1] : 0.f;
         if (b > c && tid < NB4) {
             const __bf16* xb = Xs + pair_index(b, c) * kB * D + (size_t)(4 * rb4) * D + 4 * cb4;
             const __bf16* zb = Zs + pair_index(b, c) * kB * D + (size_t)(4 * rb4) * D + 4 * cb4;
@@ -1126,23 +1141,34 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     prefetch(c);
     commit(c);
     __syncthreads();
-    for (int e = tid; e < kB * kB / 4; e += 256) {
-        const int j = e / (kB / 4), i0 = 4 * (e % (kB / 4));   // key j, queries i0 .. i0+3
-        f32x4 p;
+    {
+        constexpr int NIT = kB * kB / 4 / 256;
+        float dgv[NIT][4];   // every load in flight before the first use
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int i = i0 + q;
-            p[q] = j <= i && c * kB + i < L
-                ? __expf(scale * fw.dg[blk_c * kB * kB + i * kB + j] + (sGc[i] - sGc[j]) - sLse[i])
-                : 0.f;
+        for (int it = 0; it < NIT; ++it) {
+            const int e = tid + 256 * it, j = e / (kB / 4), i0 = 4 * (e % (kB / 4));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dgv[it][q] = fw.dg[blk_c * kB * kB + (i0 + q) * kB + j];
         }
-        sPT.put4(j, i0, p);
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int e = tid + 256 * it, j = e / (kB / 4), i0 = 4 * (e % (kB / 4));   // key j, queries i0 .. i0+3
+            f32x4 p;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = i0 + q;
+                p[q] = j <= i && c * kB + i < L
+                    ? __expf(scale * dgv[it][q] + (sGc[i] - sGc[j]) - sLse[i])
+                    : 0.f;
+            }
+            sPT.put4(j, i0, p);
+        }
     }
     if (c + 1 < nb) prefetch(c + 1);
     backprop();
 
     for (int b = c + 1; b < nb; ++b) {
-        if (fox) shift += fw.tot[slice * nb + b - 1];
+        shift += pTot;   // block b - 1's total, fetched by prefetch(b)
         commit(b);
         __syncthreads();
         if (b + 1 < nb) prefetch(b + 1);
@@ -1208,7 +1234,7 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     __shared__ float sRowB[kB];
     __shared__ __attribute__((aligned(16))) float sCol2[kB];
     const float scale2 = scale * kLog2e;
-    __shared__ float sTb;
+    __shared__ float sTw[4];   // per-wave parts of the gate totals before block b
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int b, sl;
     pair_order(nb, nsc, b, sl);
@@ -1224,39 +1250,55 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     constexpr int NB4 = kB * D / 16, NE4 = D * D / 16;
     const int rb4 = tid / (D / 4), cb4 = tid % (D / 4);
 
-    // resident: dO_b; Delta = dO . o per row
+    // resident: dO_b; Delta = dO . o per row: each thread the dot of its
+    // 8-element piece of a row (loaded with the row), then the D / 8 threads
+    // of the row combined by an xor butterfly, in a fixed order
+    u32x4 uo[UB];
 #pragma unroll
     for (int i = 0; i < UB; ++i) {
         const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
         const int pos = b * kB + r;
         u32x4 u = {0u, 0u, 0u, 0u};
-        if (pos < L) u = *reinterpret_cast<const u32x4*>(dout + (base + pos) * D + c0);
+        uo[i] = u;
+        if (pos < L) {
+            u = *reinterpret_cast<const u32x4*>(dout + (base + pos) * D + c0);
+            uo[i] = *reinterpret_cast<const u32x4*>(o + (base + pos) * D + c0);
+        }
         *reinterpret_cast<u32x4*>(&sdO.v[0][r * sdO.LDE + c0]) = u;
+        float dl = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            dl += __uint_as_float(u[q] << 16) * __uint_as_float(uo[i][q] << 16);
+            dl += __uint_as_float(u[q] & 0xffff0000u) * __uint_as_float(uo[i][q] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int off = 1; off < D / 8; off <<= 1) dl += __shfl_xor(dl, off, 64);
+        if (e % (D / 8) == 0) {
+            sDel[r] = dl;
+            delta[blk_b * kB + r] = dl;
+        }
     }
     if (tid < kB) {
         const int pos = b * kB + tid;
-        float dl = 0.f;
-        if (pos < L)
-            for (int x = 0; x < D; ++x)
-                dl += to_f32(dout[(base + pos) * D + x]) * to_f32(o[(base + pos) * D + x]);
-        sDel[tid] = dl;
         sLse[tid] = pos < L ? lse[base + pos] : 0.f;
         sGb[tid] = fox ? fw.gl[blk_b * kB + tid] : 0.f;
         sRowB[tid] = pos < L ? (sGb[tid] - sLse[tid]) * kLog2e : -INFINITY;
-        delta[blk_b * kB + tid] = dl;
     }
-    if (tid == 0) {
-        float s = 0.f;
-        if (fox)
-            for (int c = 0; c < b; ++c) s += fw.tot[slice * nb + c];
-        sTb = s;
+    // the gate totals of blocks 0 .. b-1, summed by all threads (fixed order)
+    if (fox) {
+        float part = 0.f;
+        for (int cc = tid; cc < b; cc += 256) part += fw.tot[slice * nb + cc];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) part += __shfl_xor(part, off, 64);
+        if (lane == 0) sTw[wave] = part;
     }
     // prefetch of key block c's V, Kr (4 x 4 blocks), X_bc, E (4 x 4 blocks)
     u32x4 pV[UB], pX[UB];
     f32x4 pK[4], pE[4];
-    float pGc = 0.f;
+    float pGc = 0.f, pTot = 0.f;   // pTot: the gate total of block c - 1
     auto prefetch = [&](int c) {
         const size_t blk_c = slice * nb + c;
+        pTot = fox && c >= 1 ? fw.tot[blk_c - 1] : 0.f;
 #pragma unroll
         for (int i = 0; i < UB; ++i) {
             const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
@@ -1333,17 +1375,27 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     prefetch(b);   // V_b only is used here
     commit(b);
     __syncthreads();
-    for (int e = tid; e < kB * kB / 4; e += 256) {
-        const int i = e / (kB / 4), j0 = 4 * (e % (kB / 4));   // query i, keys j0 .. j0+3
-        f32x4 p;
+    {
+        constexpr int NIT = kB * kB / 4 / 256;
+        f32x4 dg4[NIT];   // every load in flight before the first use
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int j = j0 + q;
-            p[q] = j <= i && b * kB + i < L
-                ? __expf(scale * fw.dg[blk_b * kB * kB + i * kB + j] + (sGb[i] - sGb[j]) - sLse[i])
-                : 0.f;
+        for (int it = 0; it < NIT; ++it) {
+            const int e = tid + 256 * it, i = e / (kB / 4), j0 = 4 * (e % (kB / 4));
+            dg4[it] = *reinterpret_cast<const f32x4*>(fw.dg + blk_b * kB * kB + i * kB + j0);
         }
-        sS.put4(i, j0, p);
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int e = tid + 256 * it, i = e / (kB / 4), j0 = 4 * (e % (kB / 4));   // query i, keys j0 .. j0+3
+            f32x4 p;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int j = j0 + q;
+                p[q] = j <= i && b * kB + i < L
+                    ? __expf(scale * dg4[it][q] + (sGb[i] - sGb[j]) - sLse[i])
+                    : 0.f;
+            }
+            sS.put4(i, j0, p);
+        }
     }
     if (b > 0) prefetch(0);
     __syncthreads();
@@ -1360,7 +1412,7 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         commit(c);
         __syncthreads();
         if (c + 1 < b) prefetch(c + 1);
-        const float shift = fox ? sTb - Tc : 0.f;   // sum of the totals of blocks c .. b-1
+        const float shift = fox ? ((sTw[0] + sTw[1]) + (sTw[2] + sTw[3])) - Tc : 0.f;   // totals of blocks c .. b-1
         // S^T = Kr X^T: keys m .. m+3 of query n, written to the query-major P
         const float shift2 = shift * kLog2e;
         gemm_b4<1, 1, D>(kB, kB, bview(sK), bview(sX), [&](int n, int m, f32x4 sv) {
@@ -1395,7 +1447,7 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
             for (int i = 0; i < 4; ++i)
                 sA.put4(qcol, mA + 8 * i + 4 * h,
                         f32x4{At[4 * i], At[4 * i + 1], At[4 * i + 2], At[4 * i + 3]});
-        if (fox) Tc += fw.tot[blk_c];
+        Tc += pTot;   // block c's total, fetched by prefetch(c + 1) (unused after the last c)
     }
     if (owner) {
         float* qo = dQl + blk_b * kB * D + (size_t)qcol * D;
