@@ -1079,20 +1079,20 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
                 if (c >= 1) pZ[q] = *reinterpret_cast<const bf16x4_t*>(zb + (size_t)q * D);
             }
         }
+        // rows past the sequence end are loaded from its last row and masked
+        // at the commit: a register written before a load it may overlap
+        // would make the compiler wait for every load in flight
         if (tid < NB8) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int pos = b * kB + 4 * rb8 + q;
-                pO[q] = u32x4{0u, 0u, 0u, 0u};
-                if (pos < L)
-                    pO[q] = *reinterpret_cast<const u32x4*>(dout + (base + pos) * D + 8 * cb8);
+                const int pos = min(b * kB + 4 * rb8 + q, L - 1);
+                pO[q] = *reinterpret_cast<const u32x4*>(dout + (base + pos) * D + 8 * cb8);
             }
         }
         if (tid < kB) {
-            const int pos = b * kB + tid;
-            pLse = pos < L ? lse[base + pos] : 0.f;
+            pLse = lse[base + min(b * kB + tid, L - 1)];
             pDel = delta[blk_b * kB + tid];
-            pGb = fox ? fw.gl[blk_b * kB + tid] : 0.f;
+            pGb = fw.gl[blk_b * kB + tid];
         }
     };
     auto commit = [&](int b) {
@@ -1106,14 +1106,19 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         }
         if (tid < NB8) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<u32x4*>(&sdO.v[0][(4 * rb8 + q) * sdO.LDE + 8 * cb8]) = pO[q];
+            for (int q = 0; q < 4; ++q) {
+                const bool in = b * kB + 4 * rb8 + q < L;
+                *reinterpret_cast<u32x4*>(&sdO.v[0][(4 * rb8 + q) * sdO.LDE + 8 * cb8]) =
+                    in ? pO[q] : u32x4{0u, 0u, 0u, 0u};
+            }
         }
         if (tid < kB) {
-            sLse[tid] = pLse;
+            const bool in = b * kB + tid < L;
+            const float gb = fox ? pGb : 0.f;
+            sLse[tid] = in ? pLse : 0.f;
             sDel[tid] = pDel;
-            sGb[tid] = pGb;
-            sRow2[tid] = b * kB + tid < L ? (pGb + shift - pLse) * kLog2e : -INFINITY;
+            sGb[tid] = gb;
+            sRow2[tid] = in ? (gb + shift - pLse) * kLog2e : -INFINITY;
         }
     };
     f32x16 accV = zero16(), accK = zero16(), accE = zero16();
@@ -1301,10 +1306,12 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         pTot = fox && c >= 1 ? fw.tot[blk_c - 1] : 0.f;
 #pragma unroll
         for (int i = 0; i < UB; ++i) {
+            // rows past the sequence end: the last row, masked at the commit (a
+            // register written before a load it may overlap would make the
+            // compiler wait for every load in flight)
             const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
-            const int pos = c * kB + r;
-            pV[i] = u32x4{0u, 0u, 0u, 0u};
-            if (pos < L) pV[i] = *reinterpret_cast<const u32x4*>(v + (base + pos) * D + c0);
+            const int pos = min(c * kB + r, L - 1);
+            pV[i] = *reinterpret_cast<const u32x4*>(v + (base + pos) * D + c0);
         }
         if (tid < NB4)
 #pragma unroll
@@ -1323,13 +1330,14 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
             for (int q = 0; q < 4; ++q)
                 pE[q] = *reinterpret_cast<const f32x4*>(em + blk_c * D * D +
                                                          (size_t)(4 * rb4 + q) * D + 4 * cb4);
-        if (tid < kB) pGc = fox ? fw.gl[blk_c * kB + tid] : 0.f;
+        if (tid < kB) pGc = fw.gl[blk_c * kB + tid];
     };
     auto commit = [&](int c) {
 #pragma unroll
         for (int i = 0; i < UB; ++i) {
             const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
-            *reinterpret_cast<u32x4*>(&sV.v[0][r * sV.LDE + c0]) = pV[i];
+            *reinterpret_cast<u32x4*>(&sV.v[0][r * sV.LDE + c0]) =
+                c * kB + r < L ? pV[i] : u32x4{0u, 0u, 0u, 0u};
         }
         if (tid < NB4)
 #pragma unroll
@@ -1347,8 +1355,9 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
             for (int q = 0; q < 4; ++q)
                 sE.put4(4 * rb4 + q, 4 * cb4, pE[q]);
         if (tid < kB) {
-            sGc[tid] = pGc;
-            sCol2[tid] = -pGc * kLog2e;
+            const float gc = fox ? pGc : 0.f;
+            sGc[tid] = gc;
+            sCol2[tid] = -gc * kLog2e;
         }
     };
     float rowAcc = 0.f;   // the lane's query column (fixed by the tiling): dS summed over keys
