@@ -1034,7 +1034,9 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
 
     {   // resident: Kr_c, V_c (every load in flight before the first LDS write)
         const float* krc = static_cast<const float*>(fw.kr) + blk_c * kB * D;
-        constexpr int NK4 = kB * D / 4 / 256, NV8 = (kB * D / 8 + 255) / 256;
+        // (rows past the sequence end read its last row, zeroed at the write)
+        constexpr int NK4 = kB * D / 4 / 256, NV8 = kB * D / 8 / 256;
+        static_assert(NV8 * 256 == kB * D / 8, "whole V pieces per thread");
         f32x4 kq[NK4];
         u32x4 vq[NV8];
 #pragma unroll
@@ -1044,10 +1046,12 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         }
 #pragma unroll
         for (int it = 0; it < NV8; ++it) {
-            const int e = tid + 256 * it, r = e / (D / 8), c0 = 8 * (e % (D / 8)), pos = c * kB + r;
-            vq[it] = u32x4{0u, 0u, 0u, 0u};
-            if (e < kB * D / 8 && pos < L) vq[it] = *reinterpret_cast<const u32x4*>(v + (base + pos) * D + c0);
+            const int e = tid + 256 * it, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            const int pos = min(c * kB + r, L - 1);
+            vq[it] = *reinterpret_cast<const u32x4*>(v + (base + pos) * D + c0);
         }
+        const float gc = fw.gl[blk_c * kB + (tid % kB)];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int it = 0; it < NK4; ++it) {
             const int e = tid + 256 * it, r = e / (D / 4), c0 = 4 * (e % (D / 4));
@@ -1056,12 +1060,13 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
 #pragma unroll
         for (int it = 0; it < NV8; ++it) {
             const int e = tid + 256 * it, r = e / (D / 8), c0 = 8 * (e % (D / 8));
-            if (e < kB * D / 8) *reinterpret_cast<u32x4*>(&sV.v[0][r * sV.LDE + c0]) = vq[it];
+            *reinterpret_cast<u32x4*>(&sV.v[0][r * sV.LDE + c0]) =
+                c * kB + r < L ? vq[it] : u32x4{0u, 0u, 0u, 0u};
         }
-    }
-    if (tid < kB) {
-        sGc[tid] = fox ? fw.gl[blk_c * kB + tid] : 0.f;
-        sCol2[tid] = -sGc[tid] * kLog2e;
+        if (tid < kB) {
+            sGc[tid] = fox ? gc : 0.f;
+            sCol2[tid] = -(fox ? gc : 0.f) * kLog2e;
+        }
     }
     // prefetch of query block b's X_bc, Z_bc (4 x 4 bf16 blocks), dO and row terms
     bf16x4_t pX[4], pZ[4];
@@ -1162,9 +1167,10 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int i = i0 + q;
-                p[q] = j <= i && c * kB + i < L
-                    ? __expf(scale * dgv[it][q] + (sGc[i] - sGc[j]) - sLse[i])
-                    : 0.f;
+                // formed for every entry, then selected: a branch around it
+                // would pull the entry's load in and wait on it there
+                const float x = __expf(scale * dgv[it][q] + (sGc[i] - sGc[j]) - sLse[i]);
+                p[q] = j <= i && c * kB + i < L ? x : 0.f;
             }
             sPT.put4(j, i0, p);
         }
@@ -1257,24 +1263,34 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
 
     // resident: dO_b; Delta = dO . o per row: each thread the dot of its
     // 8-element piece of a row (loaded with the row), then the D / 8 threads
-    // of the row combined by an xor butterfly, in a fixed order
-    u32x4 uo[UB];
+    // of the row combined by an xor butterfly, in a fixed order. The setup's
+    // loads are all issued first, rows past the sequence end reading its last
+    // row (masked below), so that they overlap.
+    u32x4 ud[UB], uo[UB];
 #pragma unroll
     for (int i = 0; i < UB; ++i) {
         const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
-        const int pos = b * kB + r;
-        u32x4 u = {0u, 0u, 0u, 0u};
-        uo[i] = u;
-        if (pos < L) {
-            u = *reinterpret_cast<const u32x4*>(dout + (base + pos) * D + c0);
-            uo[i] = *reinterpret_cast<const u32x4*>(o + (base + pos) * D + c0);
-        }
+        const size_t gi = (base + min(b * kB + r, L - 1)) * D + c0;
+        ud[i] = *reinterpret_cast<const u32x4*>(dout + gi);
+        uo[i] = *reinterpret_cast<const u32x4*>(o + gi);
+    }
+    const float rLse = lse[base + min(b * kB + (tid % kB), L - 1)];
+    const float rGb = fw.gl[blk_b * kB + (tid % kB)];
+    // the gate totals of blocks 0 .. b-1 (the first 256 read here, any more
+    // in the loop below)
+    const float tot0 = fw.tot[slice * nb + min(tid, nb - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < UB; ++i) {
+        const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+        const bool in = b * kB + r < L;
+        const u32x4 u = in ? ud[i] : u32x4{0u, 0u, 0u, 0u}, w = in ? uo[i] : u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4*>(&sdO.v[0][r * sdO.LDE + c0]) = u;
         float dl = 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            dl += __uint_as_float(u[q] << 16) * __uint_as_float(uo[i][q] << 16);
-            dl += __uint_as_float(u[q] & 0xffff0000u) * __uint_as_float(uo[i][q] & 0xffff0000u);
+            dl += __uint_as_float(u[q] << 16) * __uint_as_float(w[q] << 16);
+            dl += __uint_as_float(u[q] & 0xffff0000u) * __uint_as_float(w[q] & 0xffff0000u);
         }
 #pragma unroll
         for (int off = 1; off < D / 8; off <<= 1) dl += __shfl_xor(dl, off, 64);
@@ -1284,15 +1300,16 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         }
     }
     if (tid < kB) {
-        const int pos = b * kB + tid;
-        sLse[tid] = pos < L ? lse[base + pos] : 0.f;
-        sGb[tid] = fox ? fw.gl[blk_b * kB + tid] : 0.f;
-        sRowB[tid] = pos < L ? (sGb[tid] - sLse[tid]) * kLog2e : -INFINITY;
+        const bool in = b * kB + tid < L;
+        const float gb = fox ? rGb : 0.f, ls = in ? rLse : 0.f;
+        sLse[tid] = ls;
+        sGb[tid] = gb;
+        sRowB[tid] = in ? (gb - ls) * kLog2e : -INFINITY;
     }
     // the gate totals of blocks 0 .. b-1, summed by all threads (fixed order)
     if (fox) {
-        float part = 0.f;
-        for (int cc = tid; cc < b; cc += 256) part += fw.tot[slice * nb + cc];
+        float part = tid < b ? tot0 : 0.f;
+        for (int cc = tid + 256; cc < b; cc += 256) part += fw.tot[slice * nb + cc];
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) part += __shfl_xor(part, off, 64);
         if (lane == 0) sTw[wave] = part;
@@ -1644,36 +1661,66 @@ bwd_precond_b16_kernel(int L, int nb, int slice0, const bf16* __restrict__ q,
     const float* dem = dEm + blk * D * D;
     const float* ddg = dDg + blk * kB * kB;
 
-    // ---- 0. inputs: q, k, w (exact), the incoming gradients rounded to bf16
-    for (int e = tid; e < kB * D / 8; e += 512) {
-        const int r = e / (D / 8), x0 = 8 * (e % (D / 8)), pos = c * kB + r;
-        u32x4 uq = {0u, 0u, 0u, 0u}, uk = uq, uw = uq;
-        if (pos < L) {
-            const size_t gi = (base + pos) * D + x0;
-            uq = *reinterpret_cast<const u32x4*>(q + gi);
-            uk = *reinterpret_cast<const u32x4*>(k + gi);
-            uw = *reinterpret_cast<const u32x4*>(w + gi);
-        }
-        *reinterpret_cast<u32x4*>(sQ + r * kLT + x0) = uq;
-        *reinterpret_cast<u32x4*>(sK + r * kLT + x0) = uk;
-        *reinterpret_cast<u32x4*>(sW + r * kLT + x0) = uw;
+    // ---- 0. inputs: q, k, w (exact), the incoming gradients rounded to bf16.
+    //         Every global load is issued before the first LDS write, rows past
+    //         the sequence end read its last row (masked at the write), so the
+    //         loads overlap instead of waiting one by one.
+    constexpr int nI = kB * D / 8, nA = kB * D / 4, nE = D * D / 4, nG = kB * kB / 4;
+    constexpr int RI = (nI + 511) / 512, RA = (nA + 511) / 512, RE = (nE + 511) / 512,
+                  RG = (nG + 511) / 512;
+    u32x4 uq[RI], uk[RI], uw[RI];
+    f32x4 fq[RA], fk[RA], fe[RE], fg[RG];
+#pragma unroll
+    for (int i = 0; i < RI; ++i) {
+        const int e = (tid + 512 * i) % nI, r = e / (D / 8), x0 = 8 * (e % (D / 8));
+        const size_t gi = (base + min(c * kB + r, L - 1)) * D + x0;
+        uq[i] = *reinterpret_cast<const u32x4*>(q + gi);
+        uk[i] = *reinterpret_cast<const u32x4*>(k + gi);
+        uw[i] = *reinterpret_cast<const u32x4*>(w + gi);
     }
-    auto stage = [&](__bf16* dst, const float* src, int rows, int cols) {
-        for (int e = tid; e < rows * cols / 4; e += 512) {
-            const int r = e / (cols / 4), x0 = 4 * (e % (cols / 4));
-            const f32x4 v = *reinterpret_cast<const f32x4*>(src + (size_t)r * cols + x0);
-            *reinterpret_cast<bf16x4_t*>(dst + r * kLT + x0) =
-                bf16x4_t{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+#pragma unroll
+    for (int i = 0; i < RA; ++i) {
+        const int e = (tid + 512 * i) % nA;
+        fq[i] = *reinterpret_cast<const f32x4*>(dql + 4 * e);
+        fk[i] = *reinterpret_cast<const f32x4*>(dkr + 4 * e);
+    }
+#pragma unroll
+    for (int i = 0; i < RE; ++i)
+        fe[i] = *reinterpret_cast<const f32x4*>(dem + 4 * ((tid + 512 * i) % nE));
+#pragma unroll
+    for (int i = 0; i < RG; ++i)
+        fg[i] = *reinterpret_cast<const f32x4*>(ddg + 4 * ((tid + 512 * i) % nG));
+    const float bt = beta[base + min(c * kB + (tid % kB), L - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < RI; ++i) {
+        const int e = tid + 512 * i, r = (e % nI) / (D / 8), x0 = 8 * (e % (D / 8));
+        if (e < nI) {
+            const bool in = c * kB + r < L;
+            *reinterpret_cast<u32x4*>(sQ + r * kLT + x0) = in ? uq[i] : u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(sK + r * kLT + x0) = in ? uk[i] : u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(sW + r * kLT + x0) = in ? uw[i] : u32x4{0u, 0u, 0u, 0u};
         }
+    }
+    // an fp32 piece e of a row-major rows x cols matrix, rounded into a slot
+    auto put4 = [&](__bf16* dst, int cols, int e, const f32x4& v) {
+        const int r = e / (cols / 4), x0 = 4 * (e % (cols / 4));
+        *reinterpret_cast<bf16x4_t*>(dst + r * kLT + x0) =
+            bf16x4_t{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
     };
-    stage(sDq, dql, kB, D);
-    stage(sDk, dkr, kB, D);
-    stage(sDe, dem, D, D);
-    stage(sDg, ddg, kB, kB);
-    if (tid < kB) {
-        const int pos = c * kB + tid;
-        sBeta[tid] = pos < L ? beta[base + pos] : 0.f;
-    }
+#pragma unroll
+    for (int i = 0; i < RA; ++i)
+        if (tid + 512 * i < nA) {
+            put4(sDq, D, tid + 512 * i, fq[i]);
+            put4(sDk, D, tid + 512 * i, fk[i]);
+        }
+#pragma unroll
+    for (int i = 0; i < RE; ++i)
+        if (tid + 512 * i < nE) put4(sDe, D, tid + 512 * i, fe[i]);
+#pragma unroll
+    for (int i = 0; i < RG; ++i)
+        if (tid + 512 * i < nG) put4(sDg, kB, tid + 512 * i, fg[i]);
+    if (tid < kB) sBeta[tid] = c * kB + tid < L ? bt : 0.f;
     __syncthreads();
 
     // ---- 1. G = diag(beta) strictLower(W W^T) (fp32, for the solve) | X = lower(Q W^T)
