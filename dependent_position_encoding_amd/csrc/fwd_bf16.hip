@@ -581,7 +581,8 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
                  float* __restrict__ lse) {
     using I = Img<D>;
     constexpr int B = kB, NT = D / 32, NKC = D / 16;
-    constexpr float kTau = 8.f;   // lazy rescale: keep a stale max while within 2^8
+    // lazy rescale: keep a stale max while every weight stays within 2^8
+    constexpr float kSumTau = 256.f;
     __shared__ __attribute__((aligned(16))) char sImg[2][I::BYTES];
 
     int pair, slice;
@@ -630,17 +631,14 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
         if (FOX) gq = ws.gl[bq * B + qloc] * kLog2e;
     }
 
-    // p = 2^S in place, with P as bf16 operands (keys in the k-slots);
+    // P = 2^S as bf16 operands (keys in the k-slots), S left as it is;
     // returns this lane's share of the row sum of that bf16 P
     auto probs = [&](bf16x8 (&Pb)[4]) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) S[mt][r] = __builtin_amdgcn_exp2f(S[mt][r]);
-#pragma unroll
         for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) Pb[kc][e] = (__bf16)S[kc >> 1][8 * (kc & 1) + e];
+            for (int e = 0; e < 8; ++e)
+                Pb[kc][e] = (__bf16)__builtin_amdgcn_exp2f(S[kc >> 1][8 * (kc & 1) + e]);
         return sum_bf16x32(Pb);
     };
     // O^T += V^T P^T from the V^T image
@@ -768,14 +766,20 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
             for (int kc = 0; kc < NKC; ++kc) Qw[t] = mfma32(ea[kc], Qb[kc], Qw[t]);
         }
         // online softmax with a lazily updated reference max: S' is already
-        // relative to m; rescale only when a row's max exceeds it by 2^kTau
-        float mx = -INFINITY;
+        // relative to m, and the weights are formed against it first.  Their
+        // bf16 sum over the lane's keys bounds every weight, so while it stays
+        // within kSumTau no weight exceeds it (an overflow shows as inf, and a
+        // NaN fails the test too); otherwise the row's max is taken and the
+        // reference moved up to it, as a max-first update would do.
+        bf16x8 Pb[4];
+        float ps = probs(Pb);
+        if (__any(!(ps <= kSumTau))) {
+            float mx = -INFINITY;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
-        mx = pair_max(mx);
-        if (__any(mx > kTau)) {
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
+            mx = pair_max(mx);
             const float up = fmaxf(mx, 0.f);
             const float alpha = __builtin_amdgcn_exp2f(-up);
             l *= alpha;
@@ -788,9 +792,9 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
 #pragma unroll
                 for (int r = 0; r < 16; ++r) S[mt][r] -= up;
             m += up;
+            ps = probs(Pb);
         }
-        bf16x8 Pb[4];
-        l += probs(Pb);
+        l += ps;
         pv(im, Pb);
     };
 
