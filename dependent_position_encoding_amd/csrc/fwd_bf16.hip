@@ -703,13 +703,13 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
         // contraction group adds the gate's per-key term -gl_c * log2(e)
         // (hi + lo against ones) and the per-query reference
         // -(m - rowb) (hi + mid + lo, exact to fp32, against ones on the key
-        // side), so the softmax needs no per-score subtraction.  Only the
-        // lower lane half carries that group (k-slots 0-7).  The last step
-        // (c = 0) also carries the queries across block 0, which is unused
-        // but cheaper than a branch.
-        const float nref = rowb - m;
-        const bool lo_half = h == 0;
-        const __bf16 zb = (__bf16)0.f, ob = (__bf16)1.f;
+        // side), so the softmax needs no per-score subtraction.  Both lane
+        // halves (k-slots 0-7 and 8-15) carry the same group with the query
+        // side halved (an exact scaling), so the lanes need no half select.
+        // The last step (c = 0) also carries the queries across block 0,
+        // which is unused but cheaper than a branch.
+        const float nref = 0.5f * (rowb - m);
+        const __bf16 zb = (__bf16)0.f, ob = (__bf16)1.f, hb = (__bf16)0.5f;
         bf16x8 qside;
         {
             const __bf16 r0 = (__bf16)nref;
@@ -718,11 +718,11 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
             const __bf16 r2 = (__bf16)(t1 - (float)r1);
 #pragma unroll
             for (int e = 0; e < 8; ++e) qside[e] = zb;
-            qside[0] = lo_half ? ob : zb;
-            qside[1] = lo_half ? ob : zb;
-            qside[2] = lo_half ? r0 : zb;
-            qside[3] = lo_half ? r1 : zb;
-            qside[4] = lo_half ? r2 : zb;
+            qside[0] = hb;
+            qside[1] = hb;
+            qside[2] = r0;
+            qside[3] = r1;
+            qside[4] = r2;
         }
         bf16x8 ka[2][NKC];
 #pragma unroll
@@ -744,11 +744,11 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
             bf16x8 a;
 #pragma unroll
             for (int e = 0; e < 8; ++e) a[e] = zb;
-            a[0] = lo_half ? ghi : zb;
-            a[1] = lo_half ? glo : zb;
-            a[2] = lo_half ? ob : zb;
-            a[3] = lo_half ? ob : zb;
-            a[4] = lo_half ? ob : zb;
+            a[0] = ghi;
+            a[1] = glo;
+            a[2] = ob;
+            a[3] = ob;
+            a[4] = ob;
             S[mt] = mfma32(a, qside, S[mt]);
         }
         // Qwork^T += (-E_c) Qwork^T: carry the queries across block c.  It
@@ -811,10 +811,17 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
         else diag(sImg[1]);
         wait_loads();
         __syncthreads();
-        for (int c = bB - 1; c >= 0; --c) {
-            const int buf = (bA - c) & 1;
-            if (c > 0) load_image<I::BYTES>(irs, (uint32_t)(c - 1) * I::BYTES, sImg[buf ^ 1], tid);
-            step(sImg[buf], c);
+        // two steps per trip, so that each names its buffer statically (the
+        // first, key block bA - 2, is in buffer 0) and the operand addresses
+        // are fixed offsets
+        for (int c = bB - 1; c >= 0; c -= 2) {
+            if (c > 0) load_image<I::BYTES>(irs, (uint32_t)(c - 1) * I::BYTES, sImg[1], tid);
+            step(sImg[0], c);
+            wait_loads();
+            __syncthreads();
+            if (c == 0) break;
+            if (c > 1) load_image<I::BYTES>(irs, (uint32_t)(c - 2) * I::BYTES, sImg[0], tid);
+            step(sImg[1], c - 1);
             wait_loads();
             __syncthreads();
         }
