@@ -85,10 +85,27 @@ def fa_eq_flops(N, H, L, d):
 
 TRACKED_SOURCES = {
     "scan": "dependent_position_encoding_amd/csrc/fwd_bf16.hip",
+    "precond": "dependent_position_encoding_amd/csrc/fwd_bf16.hip",
+    "causal_baseline": "dependent_position_encoding_amd/csrc/fwd_bf16.hip",
     "decode": "dependent_position_encoding_amd/csrc/decode.hip",
 }
-KERNEL_KEYS = {"scan": "scan_mfma_kernel<64, true>",
-               "decode": "decode_chunk_kernel<pa::bf16, pa::bf16, 64, true>"}
+
+
+def kernel_keys(workload):
+    """Kernel name and launch size (work-items, as rocprofv3 reports
+    Grid_Size) of each tracked kernel at a workload's shape."""
+    import workloads
+    spec = WORKLOADS[workload]
+    wl = workloads.CONFIGS[spec["cfg"]]
+    N, H, L, d = wl.N, wl.H, spec.get("L", wl.L), wl.d
+    nb = (L + 63) // 64
+    pairs = N * H * ((nb + 1) // 2) * 256
+    keys = {"scan": (f"scan_mfma_kernel<{d}, {'true' if wl.fox else 'false'}>", pairs),
+            "precond": (f"precond_mfma_kernel<{d}>", N * H * nb * 512),
+            "causal_baseline": (f"causal_mfma_kernel<{d}>", pairs)}
+    if wl.decode_steps:
+        keys["decode"] = (f"decode_chunk_kernel<pa::bf16, pa::bf16, {d}, true>", None)
+    return keys
 
 
 def _source_sha(rel):
@@ -97,38 +114,76 @@ def _source_sha(rel):
         return hashlib.sha256(f.read()).hexdigest()
 
 
+def _kname(raw):
+    """Short kernel name, e.g. precond_mfma_kernel<64>, from a demangled
+    signature or from a mangled one (whose template arguments are ints,
+    bools and the library's element types)."""
+    import re
+    raw = raw.replace("(anonymous namespace)::", "")
+    m = re.search(r"pa::(\w+(<[^()]*>)?)", raw)
+    if m:
+        return m.group(1)
+    m = re.match(r"_ZN2pa(?:12_GLOBAL__N_1)?(\d+)", raw)
+    if not m:
+        return raw[:70]
+    n = int(m.group(1))
+    name, rest = raw[m.end():m.end() + n], raw[m.end() + n:]
+    if not rest.startswith("I"):
+        return name
+    args, rest = [], rest[1:]
+    while rest and rest[0] != "E":
+        a = re.match(r"Li(-?\d+)E|Lb([01])E|NS_4bf16E|(f)", rest)
+        if not a:
+            break
+        args.append(a.group(1) if a.group(1) is not None else
+                    ("true" if a.group(2) == "1" else "false") if a.group(2) is not None else
+                    "float" if a.group(3) else "pa::bf16")
+        rest = rest[a.end():]
+    return f"{name}<{', '.join(args)}>"
+
+
 def _pmc_by_kernel(path):
+    """Counter values per (kernel name, Grid_Size) of a rocprofv3 counter CSV."""
     import csv
     import re
     out = {}
     with open(path) as f:
         for r in csv.DictReader(f):
-            m = re.search(r"pa::(?:\(anonymous namespace\)::)?(\w+)(<[^()]*>)?", r["Kernel_Name"])
-            name = (m.group(1) + (m.group(2) or "")) if m else r["Kernel_Name"][:40]
-            out.setdefault(name, []).append(float(r["Counter_Value"]))
+            name = _kname(r["Kernel_Name"])
+            out.setdefault((name, int(r.get("Grid_Size") or 0)), []).append(
+                float(r["Counter_Value"]))
     return out
 
 
+def _values(rec, name, grid):
+    return [v for (n, g), vs in rec.items() if n == name and (grid is None or g == grid)
+            for v in vs]
+
+
 def summarize_pmc(paths, workload):
-    """HBM bytes per launch of the scan and fused decode kernels from
-    rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by what
-    the same counter reports for a device copy of known size."""
+    """HBM bytes per launch of the scan, the preconditioning, the beta = 0
+    baseline and (with decode steps) the fused decode kernel at the workload's
+    shape, from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
+    scaled by what the same counter reports for a device copy of known size."""
     fetch, write, cfetch, cwrite = (_pmc_by_kernel(p) for p in paths)
     copy_bytes = float(1 << 30)
 
     def copy_kib(rec):
-        vals = [v for k, vs in rec.items() if "copy" in k.lower() for v in vs]
+        vals = [v for (k, _), vs in rec.items() if "copy" in k.lower() for v in vs]
         return sum(vals) / len(vals)
 
     f_scale = copy_bytes / (copy_kib(cfetch) * 1024)
     w_scale = copy_bytes / (copy_kib(cwrite) * 1024)
     res = {"workload": workload, "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
            "kernels": {}}
-    for key, kname in KERNEL_KEYS.items():
-        fv, wv = fetch[kname], write[kname]
+    for key, (kname, grid) in kernel_keys(workload).items():
+        fv, wv = _values(fetch, kname, grid), _values(write, kname, grid)
+        if not fv or not wv:
+            continue
         rb = sum(fv) / len(fv) * 1024 * f_scale
         wb = sum(wv) / len(wv) * 1024 * w_scale
-        res["kernels"][key] = {"name": kname, "dispatches": len(fv), "read_bytes": rb,
+        res["kernels"][key] = {"name": kname, "grid": grid, "dispatches": len(fv),
+                               "read_bytes": rb,
                                "write_bytes": wb, "bytes": rb + wb,
                                "source": TRACKED_SOURCES[key],
                                "source_sha256": _source_sha(TRACKED_SOURCES[key])}
@@ -136,6 +191,26 @@ def summarize_pmc(paths, workload):
     with open(out, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res))
+
+
+def summarize_trace(path, top=24):
+    """A markdown table of a rocprofv3 --kernel-trace --stats kernel_stats.csv:
+    per kernel the calls, average / minimum / maximum duration (us), total (ms)
+    and share of the traced kernel time."""
+    import csv
+    import re
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = _kname(r["Name"])
+            rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+                         float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
+    rows.sort(key=lambda x: -x[5])
+    print("| kernel | calls | avg us | min us | max us | total ms | % |")
+    print("|---|---|---|---|---|---|---|")
+    for n, c, a, lo, hi, t, pc in rows[:top]:
+        print(f"| `{n}` | {c} | {a:.2f} | {lo:.2f} | {hi:.2f} | {t:.3f} | {pc:.1f} |")
 
 
 def causal_flops(N, H, L, d, B=64):
@@ -232,6 +307,11 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a bench run "
                          "and of a --calibrate-copy run into profiles/traffic_<workload>.json")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
+                    help="print a markdown table of a rocprofv3 kernel_stats.csv and exit")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time the workload's prefill (and the beta = 0 baseline beside it) "
+                         "without the front-end, backward and paged-decode measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device-to-device copy three times (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -241,6 +321,9 @@ def main():
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc, args.workload)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
@@ -424,13 +507,15 @@ def main():
         out["unfused_decode"] = unfused_rates(pa, cache, tok, L, wl, dws, ot, lt, kb, vb)
         out["decode_cache_cold"] = cold_decode_rate(pa, pre, cache, tok, L, wl, ws, dws, ot, lt,
                                                     kb, vb)
-    out["prefill_reps"] = prefill_reps(pa, pre, wl, cache, ws, o, lse)
-    if args.workload == "long" and not args.no_configs:
+    if not args.prefill_only:
+        out["prefill_reps"] = prefill_reps(pa, pre, wl, cache, ws, o, lse)
+    if args.workload == "long" and not args.no_configs and not args.prefill_only:
         out["prefill_by_config"] = prefill_by_config(pa, dev)
     out["beta0_baseline"] = causal_baseline(pa, pre, wl, out["prefill"])
-    out["front_end"] = front_end_rate(pa, wl, dev)
-    out["backward"] = backward_rate(pa, dev)
-    out["paged_decode"] = paged_decode_rate(pa, dev)
+    if not args.prefill_only:
+        out["front_end"] = front_end_rate(pa, wl, dev)
+        out["backward"] = backward_rate(pa, dev)
+        out["paged_decode"] = paged_decode_rate(pa, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, N * (L + T) / (ms_step * 1e-3))
     print(json.dumps(out), flush=True)
