@@ -205,14 +205,14 @@ __device__ inline void mm_nn(f32x16& acc, const char* A, const char* Bn, int m0,
 // contiguously (16 bytes a lane); each lane fetches the unit that belongs at
 // its LDS position.  The buffer resource spans the slice, so rows past its end
 // (a ragged last block) read as zeros.
-template <int D>
+template <int D, int NTH = 512>
 __device__ inline void stage_rows(const __bf16* slice_base, int L, int row0, char* dst, int tid) {
     constexpr int RB = 2 * D, UPR = RB / 16, NU = 64 * UPR;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<__bf16*>(slice_base), 0, (uint32_t)L * RB, 0x00020000);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 #pragma unroll
-    for (int u0 = 0; u0 < NU; u0 += 512) {
+    for (int u0 = 0; u0 < NU; u0 += NTH) {
         if (u0 + wave * 64 < NU) {
             const int U = u0 + wave * 64 + lane, r = U / UPR;
             const uint32_t src = (uint32_t)(row0 + r) * RB + psw<RB>(r, U % UPR) * 16;
@@ -848,27 +848,22 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
 
 // ---------------------------------------------------------------------------
 // Plain causal softmax attention (every beta = 0, no gate): the baseline the
-// PaTH kernels are measured against.  Same workgroup shape, LDS layout,
+// PaTH kernels are measured against.  Same workgroup shape, launch order,
 // matrix-core formulation and online softmax as scan_mfma_kernel, minus the
-// preconditioning and the Qwork transition: key and value tiles come straight
-// from the inputs, converted to the operand layout while staged into LDS.
-template <int D>
-struct KVImg {
-    static constexpr int RB_K = 2 * D, RB_V = 2 * kB;
-    static constexpr int OFF_K = 0, OFF_V = kB * RB_K;
-    static constexpr int BYTES = OFF_V + D * RB_V;
-};
-
+// preconditioning and the Qwork transition.  A key block's K and V rows are
+// copied HBM -> LDS by direct buffer loads into natural tiles (rows
+// XOR-swizzled, double-buffered, 32 KB at d = 64); S^T = K Q^T reads K rows
+// along LDS rows against the lane's exact query row, and O^T += V^T P^T reads
+// V^T down the tile's columns with the transposing LDS load, in the key order
+// of the P operand.  The score scale enters the exponent's fma.
 template <int D>
 __global__ void __launch_bounds__(256)
 causal_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                    const __bf16* __restrict__ v, int L, int nb, float scale2,
                    __bf16* __restrict__ o, float* __restrict__ lse) {
-    using I = KVImg<D>;
-    constexpr int B = kB, NT = D / 32, NKC = D / 16, UPR = D / 8;
-    constexpr int UN = B * UPR / 256;           // 16-byte units per thread per tensor
-    constexpr float kTau = 8.f;
-    __shared__ __attribute__((aligned(16))) char sImg[2][I::BYTES];
+    constexpr int B = kB, NT = D / 32, NKC = D / 16, RB = 2 * D, TILE = B * RB;
+    constexpr float kSumTau = 256.f;   // lazy rescale, as in the scan
+    __shared__ __attribute__((aligned(16))) char sKV[2][2 * TILE];   // [buf][K tile | V tile]
 
     int pair, slice;
     pair_of(nb, pair, slice);
@@ -878,149 +873,120 @@ causal_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int myb = wave < 2 ? bA : bB;
     const int qloc = 32 * (wave & 1) + col;
     const size_t sbase = (size_t)slice * L;
-
-    u32x4 rk[UN], rv[UN];
-    auto fetch = [&](int c) {
-#pragma unroll
-        for (int i = 0; i < UN; ++i) {
-            const int u = tid + 256 * i, r = u / UPR, x0 = (u % UPR) * 8, pos = c * B + r;
-            const size_t g = (sbase + pos) * D + x0;
-            u32x4 z = {0u, 0u, 0u, 0u};
-            rk[i] = pos < L ? *reinterpret_cast<const u32x4*>(k + g) : z;
-            rv[i] = pos < L ? *reinterpret_cast<const u32x4*>(v + g) : z;
-        }
-    };
-    auto stage = [&](char* im) {
-#pragma unroll
-        for (int i = 0; i < UN; ++i) {
-            const int u = tid + 256 * i, r = u / UPR, x0 = (u % UPR) * 8;
-            bf16x8 kv = *reinterpret_cast<const bf16x8*>(&rk[i]);
-            bf16x8 vv = *reinterpret_cast<const bf16x8*>(&rv[i]);
-            typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-            bf16x4 lo4, hi4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                lo4[e] = (__bf16)((float)kv[e] * scale2);
-                hi4[e] = (__bf16)((float)kv[e + 4] * scale2);
-            }
-            const int g16 = x0 & ~15, off = x0 & 15;
-            *reinterpret_cast<bf16x4*>(im + I::OFF_K + img_off(r, g16 + swap23(off), I::RB_K)) = lo4;
-            *reinterpret_cast<bf16x4*>(im + I::OFF_K + img_off(r, g16 + swap23(off + 4), I::RB_K)) = hi4;
-            const int slot = swap23(r);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                *reinterpret_cast<__bf16*>(im + I::OFF_V + img_off(x0 + e, slot, I::RB_V)) = vv[e];
-        }
+    auto load_kv = [&](int c, char* dst) {
+        stage_rows<D, 256>(k + sbase * D, L, c * B, dst, tid);
+        stage_rows<D, 256>(v + sbase * D, L, c * B, dst + TILE, tid);
     };
 
+    load_kv(bA, sKV[0]);
+    if (bB >= 0) load_kv(bB, sKV[1]);
+
+    // the lane's query row, exact (k-slots 8h .. 8h+7 of group kc are
+    // elements 16 kc + 8h .. +7, the order the K row fragments take)
     f32x16 Ot[NT], S[2];
     bf16x8 Qb[NKC];
     float m = 0.f, l = 0.f;
-    if (myb >= 0) {
-        const int pos = myb * B + qloc;
-        const __bf16* qp = q + (sbase + (pos < L ? pos : L - 1)) * D;
-        typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+    {
+        const int pos = myb >= 0 ? min(myb * B + qloc, L - 1) : 0;
+        const __bf16* qp = q + (sbase + pos) * D;
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-            const bf16x4 a = *reinterpret_cast<const bf16x4*>(qp + 16 * kc + 4 * h);
-            const bf16x4 b = *reinterpret_cast<const bf16x4*>(qp + 16 * kc + 8 + 4 * h);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { Qb[kc][e] = a[e]; Qb[kc][4 + e] = b[e]; }
-        }
+        for (int kc = 0; kc < NKC; ++kc) Qb[kc] = *reinterpret_cast<const bf16x8*>(qp + 16 * kc + 8 * h);
 #pragma unroll
         for (int t = 0; t < NT; ++t) Ot[t] = zero16();
     }
 
-    auto scores = [&](const char* im) {
+    auto scores = [&](const char* t) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             S[mt] = zero16();
-            const int row = 32 * mt + col;
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    im + I::OFF_K + row * I::RB_K + swz_unit(row, 2 * kc + h, I::RB_K) * 16);
-                S[mt] = mfma32(a, Qb[kc], S[mt]);
-            }
+            for (int kc = 0; kc < NKC; ++kc)
+                S[mt] = mfma32(frow<RB>(t, 32 * mt + col, 16 * kc + 8 * h), Qb[kc], S[mt]);
         }
     };
-    auto pv = [&](const char* im) {
-        bf16x8 Pb[4];
+    // P = 2^(scale2 S - m) as bf16 operands, S left as it is; returns this
+    // lane's share of the row sum of that bf16 P
+    auto probs = [&](bf16x8 (&Pb)[4]) {
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) Pb[kc][e] = (__bf16)S[kc >> 1][8 * (kc & 1) + e];
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
-                const int row = 32 * t + col;
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    im + I::OFF_V + row * I::RB_V + swz_unit(row, 2 * kc + h, I::RB_V) * 16);
-                Ot[t] = mfma32(a, Pb[kc], Ot[t]);
-            }
+            for (int e = 0; e < 8; ++e)
+                Pb[kc][e] = (__bf16)__builtin_amdgcn_exp2f(
+                    __builtin_fmaf(S[kc >> 1][8 * (kc & 1) + e], scale2, -m));
         return sum_bf16x32(Pb);
     };
-    auto diag = [&](const char* im) {
-        scores(im);
-        float mx = -INFINITY;
+    // O^T += V^T P^T; the P operand's k-slots of group kc hold keys
+    // 16 kc + 4h .. +3 and 16 kc + 8 + 4h .. +3 (the C tile's row order)
+    auto pv = [&](const char* t, const bf16x8 (&Pb)[4]) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = 32 * mt + crow(r, h);
-                if (key > qloc) S[mt][r] = -INFINITY;
-                mx = fmaxf(mx, S[mt][r]);
-            }
-        m = pair_max(mx);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) S[mt][r] = __builtin_amdgcn_exp2f(S[mt][r] - m);
-        l = pv(im);   // this half's keys only; the halves are added at the end
+            for (int kc = 0; kc < 4; ++kc)
+                Ot[tt] = mfma32(fcol<RB, 8>(t + TILE, 32 * tt + col, 16 * kc + 4 * h), Pb[kc], Ot[tt]);
     };
-    auto step = [&](const char* im) {
-        scores(im);
+    auto row_max = [&]() {
         float mx = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
-        mx = pair_max(mx);
-        if (__any(mx > m + kTau)) {
-            const float mn = fmaxf(m, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m - mn);
-            l *= alpha;
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) Ot[t][r] *= alpha;
-            m = mn;
-        }
+        return pair_max(mx) * scale2;
+    };
+    auto diag = [&](const char* t) {
+        scores(t);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) S[mt][r] = __builtin_amdgcn_exp2f(S[mt][r] - m);
-        l += pv(im);
+            for (int r = 0; r < 16; ++r)
+                if (32 * mt + crow(r, h) > qloc) S[mt][r] = -INFINITY;
+        m = row_max();
+        bf16x8 Pb[4];
+        l = probs(Pb);   // this half's keys only; the halves are added at the end
+        pv(t, Pb);
+    };
+    // the weights against the stale reference first; the row's max is taken
+    // only when their bf16 sum over the lane's keys exceeds kSumTau (which
+    // bounds every weight; an overflow shows as inf)
+    auto step = [&](const char* t) {
+        scores(t);
+        bf16x8 Pb[4];
+        float ps = probs(Pb);
+        if (__any(!(ps <= kSumTau))) {
+            const float mn = fmaxf(m, row_max());
+            const float alpha = __builtin_amdgcn_exp2f(m - mn);
+            l *= alpha;
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Ot[tt][r] *= alpha;
+            m = mn;
+            ps = probs(Pb);
+        }
+        l += ps;
+        pv(t, Pb);
     };
 
-    fetch(bA);
-    stage(sImg[0]);
-    if (bB >= 0) fetch(bB);
+    wait_loads();
     __syncthreads();
-    if (wave < 2) diag(sImg[0]);
+    if (wave < 2) diag(sKV[0]);
+    __syncthreads();
     if (bB >= 0) {
-        stage(sImg[1]);
-        if (bB > 0) fetch(bB - 1);
+        if (bB > 0) load_kv(bB - 1, sKV[0]);
+        if (wave < 2) step(sKV[1]);
+        else diag(sKV[1]);
+        wait_loads();
         __syncthreads();
-        if (wave < 2) step(sImg[1]);
-        else diag(sImg[1]);
-        for (int c = bB - 1; c >= 0; --c) {
-            const int buf = (bA - c) & 1;
-            stage(sImg[buf]);
-            if (c > 0) fetch(c - 1);
+        // two steps per trip: the first, key block bA - 2, is in buffer 0
+        for (int c = bB - 1; c >= 0; c -= 2) {
+            if (c > 0) load_kv(c - 1, sKV[1]);
+            step(sKV[0]);
+            wait_loads();
             __syncthreads();
-            step(sImg[buf]);
+            if (c == 0) break;
+            if (c > 1) load_kv(c - 2, sKV[0]);
+            step(sKV[1]);
+            wait_loads();
+            __syncthreads();
         }
     }
 
@@ -1030,14 +996,14 @@ causal_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const float inv = 1.f / l;
         __bf16* op = o + (sbase + pos) * D;
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
                 bf16x4 pk;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) pk[j] = (__bf16)(Ot[t][4 * i + j] * inv);
-                *reinterpret_cast<bf16x4*>(op + 32 * t + 8 * i + 4 * h) = pk;
+                for (int j = 0; j < 4; ++j) pk[j] = (__bf16)(Ot[tt][4 * i + j] * inv);
+                *reinterpret_cast<bf16x4*>(op + 32 * tt + 8 * i + 4 * h) = pk;
             }
         if (lse && h == 0) lse[sbase + pos] = (m + __log2f(l)) * kLn2;
     }
