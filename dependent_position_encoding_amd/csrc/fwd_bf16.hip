@@ -531,22 +531,26 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 // ---------------------------------------------------------------------------
 // Work order of the scan-shaped kernels: one workgroup per (slice, pair of
 // query blocks), pair p covering blocks nb-1-2p and nb-2-2p, so lower p means
-// more key blocks.  Slices are taken kSliceGroup at a time and, inside a
-// group, pairs heaviest first with the group's slices interleaved:
+// more key blocks.  Slices are taken sg at a time and, inside a group, pairs
+// heaviest first with the group's slices interleaved:
 //  - the workgroups resident at once share a few slices, so a key block's
 //    tile image, streamed by every pair to its left, is read from HBM about
 //    once and then hit in cache;
-//  - workgroups go to the XCDs round-robin and kSliceGroup is a multiple of 8,
-//    so all workgroups of a slice sit on one XCD and share its L2;
+//  - workgroups go to the XCDs round-robin and sg is a multiple of 8, so all
+//    workgroups of a slice sit on one XCD and share its L2;
 //  - the long pairs start first and the short ones fill the tail.
+// Groups of 32 slices balance the short sequences best; from 128 pairs per
+// slice on, the scan does better with groups of 8 (fewer slices' images in
+// each L2 at a time; measured 3 % at L = 32768, 2-8 % slower below 16384).
 constexpr int kSliceGroup = 32;
+inline int scan_slice_group(int nb) { return (nb + 1) / 2 >= 128 ? 8 : kSliceGroup; }
 
-__device__ inline void pair_of(int nb, int& pair, int& slice) {
-    const int np = (nb + 1) / 2, nh = gridDim.x / np, span = kSliceGroup * np;
+__device__ inline void pair_of(int nb, int sg, int& pair, int& slice) {
+    const int np = (nb + 1) / 2, nh = gridDim.x / np, span = sg * np;
     const int g = blockIdx.x / span, r = blockIdx.x % span;
-    const int sz = min(kSliceGroup, nh - g * kSliceGroup);
+    const int sz = min(sg, nh - g * sg);
     pair = r / sz;
-    slice = g * kSliceGroup + r % sz;
+    slice = g * sg + r % sz;
 }
 
 // ---------------------------------------------------------------------------
@@ -577,7 +581,7 @@ __device__ inline void load_image(__amdgpu_buffer_rsrc_t rsrc, uint32_t src_off,
 
 template <int D, bool FOX>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
-scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
+scan_mfma_kernel(int L, int nb, int sg, float scale2, FwdWs ws, __bf16* __restrict__ o,
                  float* __restrict__ lse) {
     using I = Img<D>;
     constexpr int B = kB, NT = D / 32, NKC = D / 16;
@@ -586,7 +590,7 @@ scan_mfma_kernel(int L, int nb, float scale2, FwdWs ws, __bf16* __restrict__ o,
     __shared__ __attribute__((aligned(16))) char sImg[2][I::BYTES];
 
     int pair, slice;
-    pair_of(nb, pair, slice);
+    pair_of(nb, sg, pair, slice);
     const int bA = nb - 1 - 2 * pair, bB = bA - 1;          // bB may be -1
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
     const int col = lane & 31;
@@ -866,7 +870,7 @@ causal_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     __shared__ __attribute__((aligned(16))) char sKV[2][2 * TILE];   // [buf][K tile | V tile]
 
     int pair, slice;
-    pair_of(nb, pair, slice);
+    pair_of(nb, kSliceGroup, pair, slice);
     const int bA = nb - 1 - 2 * pair, bB = bA - 1;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
     const int col = lane & 31;
@@ -1023,9 +1027,11 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t st) {
     const int ngrid = a.N * a.H * ((nb + 1) / 2);
     if (a.logf)
         hipLaunchKernelGGL((scan_mfma_kernel<D, true>), dim3(ngrid), dim3(256), 0, st, a.L, nb,
+                           scan_slice_group(nb),
                            scale2, a.ws, (__bf16*)a.o, a.lse);
     else
         hipLaunchKernelGGL((scan_mfma_kernel<D, false>), dim3(ngrid), dim3(256), 0, st, a.L, nb,
+                           scan_slice_group(nb),
                            scale2, a.ws, (__bf16*)a.o, a.lse);
     return hipGetLastError();
 }
