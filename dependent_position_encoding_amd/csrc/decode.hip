@@ -8,6 +8,7 @@
 // explainer page "PaTH Attention: Position Encoding via Accumulating
 // Householder Transformations" (gist.science), section 3.
 #include <mutex>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -151,11 +152,15 @@ constexpr int kPagedChunk = 128;
 // one slice of a contiguous cache [slice][cap][D]
 template <typename K, typename T, int D>
 struct ContigRows {
+    static constexpr bool kSlotPointers = false;
     K* k0;            // the slice's slot 0
     T* v0;
     float* g0;        // its log-f prefix (NULL: no gate)
     __device__ size_t off(int j) const { return (size_t)j * D; }
     __device__ float* g(int j) const { return g0 + j; }
+    // the same for key j in key slot i of the chunk body (the slot is not needed here)
+    __device__ size_t off_i(int, int j) const { return off(j); }
+    __device__ float* g_i(int, int j) const { return g(j); }
     __device__ float prev_prefix(int t) const { return g0[t - 1]; }
     __device__ bool gate() const { return g0 != nullptr; }
 };
@@ -165,6 +170,7 @@ struct ContigRows {
 // staged in LDS) at position j & (P - 1)
 template <typename K, typename T, int D>
 struct PagedRows {
+    static constexpr bool kSlotPointers = false;
     K* k0;             // the page pool
     T* v0;
     float* gp;         // log-f pages [page][H][P] (NULL: no gate)
@@ -176,6 +182,39 @@ struct PagedRows {
     }
     __device__ size_t off(int j) const { return slab(j) * D; }
     __device__ float* g(int j) const { return gp + slab(j); }
+    __device__ size_t off_i(int, int j) const { return off(j); }
+    __device__ float* g_i(int, int j) const { return g(j); }
+    __device__ float prev_prefix(int) const { return *gprev; }
+    __device__ bool gate() const { return gp != nullptr; }
+};
+
+// A paged cache whose pages hold at least as many slots as the chunk body's
+// lane groups step over (GROUPS): then key slot i of the chunk (keys
+// j0 + i GROUPS .. j0 + (i + 1) GROUPS - 1, an aligned run no longer than a
+// page) lies in one page, and that page's slab start is the same for every
+// lane, so it is kept per slot in scalar registers and a key's offset is the
+// slab start plus its position in the page, as in a contiguous slice.
+template <typename K, typename T, int D, int NS>
+struct PagedSlotRows {
+    static constexpr bool kSlotPointers = true;
+    K* kb[NS];          // slot i's page slab: keys, values, log-f prefixes
+    T* vb[NS];
+    float* gb[NS];
+    const float* gprev;
+    float* gp;          // the log-f pool (NULL: no gate)
+    int mask;           // P - 1
+    // a row in its page: a 32-bit byte offset from the slot's base, so that
+    // the access takes the base from scalar registers and one offset VGPR
+    template <typename E>
+    __device__ static E* at(E* base, uint32_t bytes) {
+        return reinterpret_cast<E*>(reinterpret_cast<char*>(base) + bytes);
+    }
+    __device__ uint32_t row_bytes(int j, int e, uint32_t esize) const {
+        return ((uint32_t)(j & mask) * D + (uint32_t)e) * esize;
+    }
+    __device__ K* kp_i(int i, int j, int e) const { return at(kb[i], row_bytes(j, e, sizeof(K))); }
+    __device__ T* vp_i(int i, int j, int e) const { return at(vb[i], row_bytes(j, e, sizeof(T))); }
+    __device__ float* g_i(int i, int j) const { return at(gb[i], (uint32_t)(j & mask) * 4u); }
     __device__ float prev_prefix(int) const { return *gprev; }
     __device__ bool gate() const { return gp != nullptr; }
 };
@@ -202,7 +241,7 @@ __device__ inline void chunk_attend(const Rows& rows, int slice, int ch, int n_k
     const bool gate = rows.gate();
     float ct = 0.f;                               // C_t
     if (gate) {
-        if (FUSED) ct = (t > 0 ? rows.prev_prefix(t) : 0.f) + logf_t[slice];
+        if constexpr (FUSED) ct = (t > 0 ? rows.prev_prefix(t) : 0.f) + logf_t[slice];
         else ct = *rows.g(t);
     }
     const int j0 = ch * CH;
@@ -216,10 +255,15 @@ __device__ inline void chunk_attend(const Rows& rows, int slice, int ch, int n_k
         const int j = j0 + grp + GROUPS * i;
         const bool live = j < n_keys && !(FUSED && j == t);
         if (live) {
-            const size_t off = rows.off(j) + lane_in * VN;
-            kx[i].load(rows.k0 + off);
-            vr[i].load(rows.v0 + off);
-            gj[i] = gate ? *rows.g(j) : 0.f;
+            if constexpr (Rows::kSlotPointers) {
+                kx[i].load(rows.kp_i(i, j, lane_in * VN));
+                vr[i].load(rows.vp_i(i, j, lane_in * VN));
+            } else {
+                const size_t off = rows.off_i(i, j) + lane_in * VN;
+                kx[i].load(rows.k0 + off);
+                vr[i].load(rows.v0 + off);
+            }
+            gj[i] = gate ? *rows.g_i(i, j) : 0.f;
         } else {
             // keys past the end get weight 0; their values must be finite
 #pragma unroll
@@ -238,17 +282,25 @@ __device__ inline void chunk_attend(const Rows& rows, int slice, int ch, int n_k
             sc[i] = -INFINITY;
             continue;
         }
-        const size_t off = rows.off(j) + lane_in * VN;
+        // the key's and value's row (formed where used, as the loads formed them)
+        auto krow = [&]() -> K* {
+            if constexpr (Rows::kSlotPointers) return rows.kp_i(i, j, lane_in * VN);
+            else return rows.k0 + (rows.off_i(i, j) + lane_in * VN);
+        };
+        auto vrow = [&]() -> T* {
+            if constexpr (Rows::kSlotPointers) return rows.vp_i(i, j, lane_in * VN);
+            else return rows.v0 + (rows.off_i(i, j) + lane_in * VN);
+        };
         if (FUSED && j == t) {
             // the new token: stored as given, its own transition excluded
 #pragma unroll
             for (int e = 0; e < VN; ++e) {
                 kf[e] = to_f32(from_f32<K>(to_f32(k_t[sd + e])));
-                rows.k0[off + e] = from_f32<K>(kf[e]);
-                rows.v0[off + e] = v_t[sd + e];
+                krow()[e] = from_f32<K>(kf[e]);
+                vrow()[e] = v_t[sd + e];
             }
             vr[i].load(v_t + sd);
-            if (gate && lane_in == 0) *rows.g(t) = ct;
+            if (gate && lane_in == 0) *rows.g_i(i, t) = ct;
         } else {
             if (FUSED) {
                 float p = 0.f;
@@ -257,7 +309,7 @@ __device__ inline void chunk_attend(const Rows& rows, int slice, int ch, int n_k
                 const float cf = bt * group_sum<TPR>(p);
 #pragma unroll
                 for (int e = 0; e < VN; ++e) kx[i].set(e, kx[i].get(e) - cf * wv[e]);
-                kx[i].store(rows.k0 + off);
+                kx[i].store(krow());
             }
 #pragma unroll
             for (int e = 0; e < VN; ++e) kf[e] = kx[i].get(e);
@@ -330,15 +382,15 @@ decode_chunk_kernel(K* __restrict__ kc, T* __restrict__ vc, float* __restrict__ 
 // [0, num_pages) (its own pages, or with the gate the page of slot t - 1)
 // touches no cache memory and leaves m = +inf, which makes the combine's
 // result NaN for that (sequence, head).
-template <typename K, typename T, int D>
-__global__ void __launch_bounds__(256)
-paged_chunk_kernel(K* __restrict__ kp, T* __restrict__ vp, float* __restrict__ gp,
-                   int num_pages, int lp, int H, const int* __restrict__ tables,
-                   int table_stride, const int* __restrict__ seq_lens, int max_keys,
-                   float scale, const T* __restrict__ q_t, const T* __restrict__ k_t,
-                   const T* __restrict__ v_t, const T* __restrict__ w_t,
-                   const float* __restrict__ beta_t, const float* __restrict__ logf_t,
-                   float* __restrict__ part, int* __restrict__ nk) {
+template <typename K, typename T, int D, bool SLOTS>
+__device__ inline void paged_chunk(K* __restrict__ kp, T* __restrict__ vp, float* __restrict__ gp,
+                                   int num_pages, int lp, int H, const int* __restrict__ tables,
+                                   int table_stride, const int* __restrict__ seq_lens,
+                                   int max_keys, float scale, const T* __restrict__ q_t,
+                                   const T* __restrict__ k_t, const T* __restrict__ v_t,
+                                   const T* __restrict__ w_t, const float* __restrict__ beta_t,
+                                   const float* __restrict__ logf_t, float* __restrict__ part,
+                                   int* __restrict__ nk) {
     const int slice = blockIdx.y, ch = blockIdx.x, nch = gridDim.x;
     const int s = slice / H, h = slice % H;
     const int len = seq_lens[s];
@@ -376,10 +428,53 @@ paged_chunk_kernel(K* __restrict__ kp, T* __restrict__ vp, float* __restrict__ g
     }
     const float* gprev = gp && tp >= 0
         ? gp + ((((size_t)sPrev * H + h) << lp) | (size_t)(tp & ((1 << lp) - 1))) : nullptr;
-    const PagedRows<K, T, D> rows{kp, vp, gp, sPage, gprev, p0, lp, H, h};
-    chunk_attend<K, T, D, true, kPagedChunk>(rows, slice, ch, n_keys, scale, q_t, k_t, v_t,
-                                             w_t, beta_t, logf_t, out);
+    if constexpr (SLOTS) {
+        // pages of at least GROUPS slots (checked by the launch): one page per key slot
+        constexpr int GROUPS = 256 / (D / Vec<K>::n), NS = kPagedChunk / GROUPS;
+        static_assert(NS <= kPagedChunk / 16, "slot pages among the staged entries");
+        PagedSlotRows<K, T, D, NS> rows{{}, {}, {}, gprev, gp, (1 << lp) - 1};
+        const int j0 = ch * kPagedChunk;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            // slots past the sequence end may name an unstaged entry: their keys are never read
+            const int pg = __builtin_amdgcn_readfirstlane(sPage[((j0 + GROUPS * i) >> lp) - p0]);
+            const size_t slab = ((size_t)pg * H + h) << lp;
+            rows.kb[i] = kp + slab * D;
+            rows.vb[i] = vp + slab * D;
+            rows.gb[i] = gp ? gp + slab : nullptr;
+        }
+        chunk_attend<K, T, D, true, kPagedChunk>(rows, slice, ch, n_keys, scale, q_t, k_t, v_t,
+                                                 w_t, beta_t, logf_t, out);
+    } else {
+        const PagedRows<K, T, D> rows{kp, vp, gp, sPage, gprev, p0, lp, H, h};
+        chunk_attend<K, T, D, true, kPagedChunk>(rows, slice, ch, n_keys, scale, q_t, k_t, v_t,
+                                                 w_t, beta_t, logf_t, out);
+    }
 }
+#define PA_PAGED_PARAMS                                                                         \
+    K *__restrict__ kp, T *__restrict__ vp, float *__restrict__ gp, int num_pages, int lp,      \
+        int H, const int *__restrict__ tables, int table_stride,                                \
+        const int *__restrict__ seq_lens, int max_keys, float scale, const T *__restrict__ q_t, \
+        const T *__restrict__ k_t, const T *__restrict__ v_t, const T *__restrict__ w_t,        \
+        const float *__restrict__ beta_t, const float *__restrict__ logf_t,                     \
+        float *__restrict__ part, int *__restrict__ nk
+#define PA_PAGED_ARGS                                                                         \
+    kp, vp, gp, num_pages, lp, H, tables, table_stride, seq_lens, max_keys, scale, q_t, k_t, \
+        v_t, w_t, beta_t, logf_t, part, nk
+template <typename K, typename T, int D, bool SLOTS>
+__global__ void __launch_bounds__(256) paged_chunk_kernel(PA_PAGED_PARAMS) {
+    paged_chunk<K, T, D, SLOTS>(PA_PAGED_ARGS);
+}
+// The same at six waves per SIMD (registers capped at 80), for the cache
+// types whose step fits that without spilling: bf16 keys and values at d = 64
+// (measured 4-5 % faster than at the five waves its 84 registers would give).
+template <typename K, typename T, int D, bool SLOTS>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6)))
+paged_chunk6_kernel(PA_PAGED_PARAMS) {
+    paged_chunk<K, T, D, SLOTS>(PA_PAGED_ARGS);
+}
+#undef PA_PAGED_PARAMS
+#undef PA_PAGED_ARGS
 
 // Merge the chunk partials of one slice: o = sum acc_c e^{m_c - M} / l,
 // lse = M + log l.  One 1024-thread block per slice, one chunk per thread for
@@ -968,11 +1063,25 @@ static hipError_t paged_step_t(const PagedArgs& a, hipStream_t st) {
     const int S = a.S * a.H;
     float* part = a.ws;
     int* nk = reinterpret_cast<int*>(a.ws + (size_t)S * mch * (D + 2));
-    hipLaunchKernelGGL((paged_chunk_kernel<K, T, D>), dim3(mch, S), dim3(256), 0, st,
-                       (K*)a.kpages, (T*)a.vpages, a.gpages, a.num_pages, a.lp, a.H, a.tables,
-                       a.table_stride, (const int*)a.seq_lens, a.max_keys, a.scale,
-                       (const T*)a.q_t, (const T*)a.k_t, (const T*)a.v_t, (const T*)a.w_t,
-                       a.beta_t, a.logf_t, part, nk);
+    // pages of at least as many slots as the chunk body's lane groups step over
+    // take the scalar per-slot page bases
+    constexpr int GROUPS = 256 / (D / Vec<K>::n);
+    constexpr bool SIX = std::is_same_v<K, bf16> && std::is_same_v<T, bf16> && D == 64;
+    const bool slots = (1 << a.lp) >= GROUPS;
+    auto launch = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(mch, S), dim3(256), 0, st, (K*)a.kpages, (T*)a.vpages,
+                           a.gpages, a.num_pages, a.lp, a.H, a.tables, a.table_stride,
+                           (const int*)a.seq_lens, a.max_keys, a.scale, (const T*)a.q_t,
+                           (const T*)a.k_t, (const T*)a.v_t, (const T*)a.w_t, a.beta_t, a.logf_t,
+                           part, nk);
+    };
+    if constexpr (SIX) {
+        if (slots) launch(paged_chunk6_kernel<K, T, D, true>);
+        else launch(paged_chunk6_kernel<K, T, D, false>);
+    } else {
+        if (slots) launch(paged_chunk_kernel<K, T, D, true>);
+        else launch(paged_chunk_kernel<K, T, D, false>);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(S), dim3(kCombineThreads), 0, st,
