@@ -1509,7 +1509,11 @@ bwd_chain_b16_kernel(int nb, int nsc, int slice0, const float* __restrict__ ql,
     using I = Img<D>;
     constexpr int TN = D / 32, NT = (kB / 32) * TN;        // Qw tiles
     constexpr int LQ = kB + 8;                              // LDS row stride (bf16)
+    constexpr int LR = D + 8;
     __shared__ __attribute__((aligned(16))) __bf16 sQt[D * LQ];   // Qw^T [d][q]
+    // Qw [q][d] as well, for the stores: a lane then takes 16 bytes along a
+    // row and the lanes of a wave write whole rows, contiguous in memory
+    __shared__ __attribute__((aligned(16))) __bf16 sQr[kB * LR];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, h = lane >> 5;
     const int b = nb - 1 - (int)(blockIdx.x / nsc), sl = (int)(blockIdx.x % nsc);
     const size_t slice = (size_t)slice0 + sl, npairs = (size_t)nb * (nb - 1) / 2;
@@ -1539,19 +1543,22 @@ bwd_chain_b16_kernel(int nb, int nsc, int slice0, const float* __restrict__ ql,
     for (int c = b - 1; c >= 0; --c) {
         if (owner)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<bf16x4_t*>(sQt + (n0 + r) * LQ + m0 + 8 * i + 4 * h) =
-                    bf16x4_t{(__bf16)qw[4 * i], (__bf16)qw[4 * i + 1], (__bf16)qw[4 * i + 2],
-                             (__bf16)qw[4 * i + 3]};
-        __syncthreads();   // Qw^T in LDS
-        {   // X_bc = Qw as bf16 rows [q][d]
+            for (int i = 0; i < 4; ++i) {
+                const bf16x4_t x4{(__bf16)qw[4 * i], (__bf16)qw[4 * i + 1], (__bf16)qw[4 * i + 2],
+                                  (__bf16)qw[4 * i + 3]};
+                *reinterpret_cast<bf16x4_t*>(sQt + (n0 + r) * LQ + m0 + 8 * i + 4 * h) = x4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sQr[(m0 + 8 * i + 4 * h + j) * LR + n0 + r] = x4[j];
+            }
+        __syncthreads();   // Qw^T and Qw in LDS
+        {   // X_bc = Qw as bf16 rows [q][d]: D / 8 lanes per row
+            constexpr int CPR = D / 8, RPW = 64 / CPR;
             __bf16* xo = Xs + pair_index(b, c) * kB * D;
 #pragma unroll
             for (int u = 0; u < XP; ++u) {
-                const int G = (u * 4 + wave) * 4 + (lane >> 4);   // (16-q block, 8-d chunk)
-                const int q = 16 * (G % (kB / 16)) + (lane & 15), d0 = 8 * (G / (kB / 16));
-                const bf16x8 x = frag_col(sQt, LQ, q, d0);
-                *reinterpret_cast<bf16x8*>(xo + (size_t)q * D + d0) = x;
+                const int q = (u * 4 + wave) * RPW + lane / CPR, d0 = 8 * (lane % CPR);
+                *reinterpret_cast<bf16x8*>(xo + (size_t)q * D + d0) =
+                    *reinterpret_cast<const bf16x8*>(sQr + q * LR + d0);
             }
         }
         if (c > 0 && owner) {
