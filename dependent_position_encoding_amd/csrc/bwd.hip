@@ -1438,6 +1438,16 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         commit(c);
         __syncthreads();
         if (c + 1 < b) prefetch(c + 1);
+        if (c >= 1) {   // Z = A_{c-1}, bf16 rows [q][d], from its LDS copy: whole rows per wave
+            constexpr int CPR = D / 8, RPP = 256 / CPR;
+            __bf16* zo = Zs + pair_index(b, c) * kB * D;
+#pragma unroll
+            for (int u = 0; u < kB / RPP; ++u) {
+                const int q = u * RPP + tid / CPR, d0 = 8 * (tid % CPR);
+                *reinterpret_cast<bf16x8*>(zo + (size_t)q * D + d0) =
+                    *reinterpret_cast<const bf16x8*>(&sA.v[0][q * sA.LDE + d0]);
+            }
+        }
         const float shift = fox ? ((sTw[0] + sTw[1]) + (sTw[2] + sTw[3])) - Tc : 0.f;   // totals of blocks c .. b-1
         // S^T = Kr X^T: keys m .. m+3 of query n, written to the query-major P
         const float shift2 = shift * kLog2e;
@@ -1454,17 +1464,7 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         // G^T = Kr^T dS^T;  (A E)^T = E^T A^T;  A^T <- scale G^T + A^T - (A E)^T
         f32x16 gt = zero16(), ae = zero16();
         gemm_bc_acc<true, false, kB>(D, kB, bview(sK), bview(sS), gt);
-        if (c >= 1) {
-            gemm_bc_acc<true, false, D>(D, kB, bview(sE), bview(sA), ae);
-            if (owner) {   // Z = A_{c-1}: four consecutive d of the lane's query per group
-                __bf16* zo = Zs + pair_index(b, c) * kB * D + (size_t)qcol * D;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<bf16x4_t*>(zo + mA + 8 * i + 4 * h) =
-                        bf16x4_t{(__bf16)At[4 * i], (__bf16)At[4 * i + 1], (__bf16)At[4 * i + 2],
-                                 (__bf16)At[4 * i + 3]};
-            }
-        }
+        if (c >= 1) gemm_bc_acc<true, false, D>(D, kB, bview(sE), bview(sA), ae);
 #pragma unroll
         for (int q = 0; q < 16; ++q) At[q] = scale * gt[q] + (c >= 1 ? At[q] - ae[q] : 0.f);
         __syncthreads();   // every read of A_{c-1} and of the pair's tiles is done
