@@ -1244,7 +1244,6 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     // -lse; -inf past the sequence end) and per key of the current block (-gate)
     __shared__ float sRowB[kB];
     __shared__ __attribute__((aligned(16))) float sCol2[kB];
-    const float scale2 = scale * kLog2e;
     __shared__ float sTw[4];   // per-wave parts of the gate totals before block b
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int b, sl;
@@ -1356,10 +1355,13 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
             *reinterpret_cast<u32x4*>(&sV.v[0][r * sV.LDE + c0]) =
                 c * kB + r < L ? pV[i] : u32x4{0u, 0u, 0u, 0u};
         }
+        // Kr enters both of its products scaled (S^T = scale Kr X^T in the
+        // exponent, scale Kr^T dS^T in the chain), and E negated, so the chain
+        // accumulates straight into A^T
         if (tid < NB4)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                sK.put4(4 * rb4 + q, 4 * cb4, pK[q]);
+                sK.put4(4 * rb4 + q, 4 * cb4, pK[q] * scale);
             }
         if (c < b)
 #pragma unroll
@@ -1370,7 +1372,7 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         if (c >= 1 && tid < NE4)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                sE.put4(4 * rb4 + q, 4 * cb4, pE[q]);
+                sE.put4(4 * rb4 + q, 4 * cb4, -pE[q]);
         if (tid < kB) {
             const float gc = fox ? pGc : 0.f;
             sGc[tid] = gc;
@@ -1434,7 +1436,6 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     const bool owner = wave < (D / 32) * tq;
     const int qcol = nA + (lane & 31);   // the lane's query
     for (int c = 0; c < b; ++c) {
-        const size_t blk_c = slice * nb + c;
         commit(c);
         __syncthreads();
         if (c + 1 < b) prefetch(c + 1);
@@ -1449,7 +1450,7 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
             }
         }
         const float shift = fox ? ((sTw[0] + sTw[1]) + (sTw[2] + sTw[3])) - Tc : 0.f;   // totals of blocks c .. b-1
-        // S^T = Kr X^T: keys m .. m+3 of query n, written to the query-major P
+        // S^T = (scale Kr) X^T: keys m .. m+3 of query n, written to the query-major P
         const float shift2 = shift * kLog2e;
         gemm_b4<1, 1, D>(kB, kB, bview(sK), bview(sX), [&](int n, int m, f32x4 sv) {
             const float rw = sRowB[n] + shift2;
@@ -1457,16 +1458,13 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
             f32x4 p;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(scale2, sv[e], rw + cl[e]));
+                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(kLog2e, sv[e], rw + cl[e]));
             sS.put4(n, m, p);
         });
         backprop(false);
-        // G^T = Kr^T dS^T;  (A E)^T = E^T A^T;  A^T <- scale G^T + A^T - (A E)^T
-        f32x16 gt = zero16(), ae = zero16();
-        gemm_bc_acc<true, false, kB>(D, kB, bview(sK), bview(sS), gt);
-        if (c >= 1) gemm_bc_acc<true, false, D>(D, kB, bview(sE), bview(sA), ae);
-#pragma unroll
-        for (int q = 0; q < 16; ++q) At[q] = scale * gt[q] + (c >= 1 ? At[q] - ae[q] : 0.f);
+        // A^T <- A^T + (scale Kr)^T dS^T + (-E)^T A^T, accumulated in place
+        gemm_bc_acc<true, false, kB>(D, kB, bview(sK), bview(sS), At);
+        if (c >= 1) gemm_bc_acc<true, false, D>(D, kB, bview(sE), bview(sA), At);
         __syncthreads();   // every read of A_{c-1} and of the pair's tiles is done
         if (owner)
 #pragma unroll
