@@ -728,6 +728,10 @@ scan_mfma_kernel(int L, int nb, int sg, float scale2, FwdWs ws, __bf16* __restri
             qside[3] = r1;
             qside[4] = r2;
         }
+        // the step's matrix-core phases run at a raised wave priority and its
+        // softmax at the normal one, so that a SIMD's arbiter issues the
+        // products of one wave while the others do their vector work
+        __builtin_amdgcn_s_setprio(1);
         bf16x8 ka[2][NKC];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -769,6 +773,7 @@ scan_mfma_kernel(int L, int nb, int sg, float scale2, FwdWs ws, __bf16* __restri
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) Qw[t] = mfma32(ea[kc], Qb[kc], Qw[t]);
         }
+        __builtin_amdgcn_s_setprio(0);
         // online softmax with a lazily updated reference max: S' is already
         // relative to m, and the weights are formed against it first.  Their
         // bf16 sum over the lane's keys bounds every weight, so while it stays
@@ -799,7 +804,9 @@ scan_mfma_kernel(int L, int nb, int sg, float scale2, FwdWs ws, __bf16* __restri
             ps = probs(Pb);
         }
         l += ps;
+        __builtin_amdgcn_s_setprio(1);
         pv(im, Pb);
+        __builtin_amdgcn_s_setprio(0);
     };
 
     wait_loads();
