@@ -1017,7 +1017,6 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     // (gate, shift, -lse; -inf past the sequence end) and per key (-gate)
     __shared__ __attribute__((aligned(16))) float sRow2[kB];
     __shared__ float sCol2[kB];
-    const float scale2 = scale * kLog2e;
     float shift = 0.f;              // sum of the gate totals of blocks c .. b-1
     const int tid = threadIdx.x;
     int c, sl;
@@ -1032,17 +1031,18 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     const int rb4 = tid / (D / 4), cb4 = tid % (D / 4);   // this thread's 4 x 4 block
     const int rb8 = tid / (D / 8), cb8 = tid % (D / 8);   // and 4 x 8 block
 
-    {   // resident: Kr_c, V_c (every load in flight before the first LDS write)
-        const float* krc = static_cast<const float*>(fw.kr) + blk_c * kB * D;
+    {   // resident: scale * Kr_c (bf16 rows from the preconditioning), V_c
+        // (every load in flight before the first LDS write)
+        const __bf16* krc = static_cast<const __bf16*>(fw.kr) + blk_c * kB * D;
         // (rows past the sequence end read its last row, zeroed at the write)
-        constexpr int NK4 = kB * D / 4 / 256, NV8 = kB * D / 8 / 256;
+        constexpr int NV8 = kB * D / 8 / 256;
         static_assert(NV8 * 256 == kB * D / 8, "whole V pieces per thread");
-        f32x4 kq[NK4];
+        u32x4 kq[NV8];
         u32x4 vq[NV8];
 #pragma unroll
-        for (int it = 0; it < NK4; ++it) {
-            const int e = tid + 256 * it, r = e / (D / 4), c0 = 4 * (e % (D / 4));
-            kq[it] = *reinterpret_cast<const f32x4*>(krc + (size_t)r * D + c0);
+        for (int it = 0; it < NV8; ++it) {
+            const int e = tid + 256 * it, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            kq[it] = *reinterpret_cast<const u32x4*>(krc + (size_t)r * D + c0);
         }
 #pragma unroll
         for (int it = 0; it < NV8; ++it) {
@@ -1053,9 +1053,9 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         const float gc = fw.gl[blk_c * kB + (tid % kB)];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int it = 0; it < NK4; ++it) {
-            const int e = tid + 256 * it, r = e / (D / 4), c0 = 4 * (e % (D / 4));
-            sK.put4(r, c0, kq[it]);
+        for (int it = 0; it < NV8; ++it) {
+            const int e = tid + 256 * it, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            *reinterpret_cast<u32x4*>(&sK.v[0][r * sK.LDE + c0]) = kq[it];
         }
 #pragma unroll
         for (int it = 0; it < NV8; ++it) {
@@ -1183,14 +1183,14 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         commit(b);
         __syncthreads();
         if (b + 1 < nb) prefetch(b + 1);
-        // P = exp(scale X Kr^T + bias - lse), queries m .. m+3 of key n, into P^T
+        // P = exp(X (scale Kr)^T + bias - lse), queries m .. m+3 of key n, into P^T
         gemm_b4<1, 1, D>(kB, kB, bview(sX), bview(sK), [&](int n, int m, f32x4 sv) {
             const f32x4 rw = *reinterpret_cast<const f32x4*>(sRow2 + m);
             const float cl = sCol2[n];
             f32x4 p;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(scale2, sv[e], rw[e] + cl));
+                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(kLog2e, sv[e], rw[e] + cl));
             sPT.put4(n, m, p);
         });
         backprop();
@@ -1254,11 +1254,14 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     // the carried queries and the gradient chain, bf16 [pair][kB][D]
     const __bf16* Xs = reinterpret_cast<const __bf16*>(X) + (size_t)sl * npairs * kB * D;
     __bf16* Zs = reinterpret_cast<__bf16*>(Z) + (size_t)sl * npairs * kB * D;
-    const float* kr = static_cast<const float*>(fw.kr);
-    const float* em = static_cast<const float*>(fw.em);
+    // scale * Kr and -E as bf16 rows (from the preconditioning)
+    const __bf16* kr = static_cast<const __bf16*>(fw.kr);
+    const __bf16* em = static_cast<const __bf16*>(fw.em);
     constexpr int UB = kB * D / 8 / 256;
-    constexpr int NB4 = kB * D / 16, NE4 = D * D / 16;
-    const int rb4 = tid / (D / 4), cb4 = tid % (D / 4);
+    // 16-byte pieces of the D x D transition: D * D / 8 of them, at most one per thread
+    constexpr int NEU = D * D / 8;
+    static_assert(NEU <= 256 || NEU == 512, "E pieces per thread");
+    constexpr int UE = NEU > 256 ? 2 : 1;
 
     // resident: dO_b; Delta = dO . o per row: each thread the dot of its
     // 8-element piece of a row (loaded with the row), then the D / 8 threads
@@ -1313,9 +1316,8 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         for (int off = 1; off < 64; off <<= 1) part += __shfl_xor(part, off, 64);
         if (lane == 0) sTw[wave] = part;
     }
-    // prefetch of key block c's V, Kr (4 x 4 blocks), X_bc, E (4 x 4 blocks)
-    u32x4 pV[UB], pX[UB];
-    f32x4 pK[4], pE[4];
+    // prefetch of key block c's V, scale * Kr, X_bc, -E (16-byte pieces)
+    u32x4 pV[UB], pX[UB], pK[UB], pE[UE];
     float pGc = 0.f, pTot = 0.f;   // pTot: the gate total of block c - 1
     auto prefetch = [&](int c) {
         const size_t blk_c = slice * nb + c;
@@ -1329,11 +1331,11 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
             const int pos = min(c * kB + r, L - 1);
             pV[i] = *reinterpret_cast<const u32x4*>(v + (base + pos) * D + c0);
         }
-        if (tid < NB4)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                pK[q] = *reinterpret_cast<const f32x4*>(kr + blk_c * kB * D +
-                                                         (size_t)(4 * rb4 + q) * D + 4 * cb4);
+        for (int i = 0; i < UB; ++i) {
+            const int e = tid + 256 * i;
+            pK[i] = *reinterpret_cast<const u32x4*>(kr + blk_c * kB * D + (size_t)8 * e);
+        }
         if (c < b)
 #pragma unroll
             for (int i = 0; i < UB; ++i) {
@@ -1341,11 +1343,13 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
                 pX[i] = *reinterpret_cast<const u32x4*>(Xs + pair_index(b, c) * kB * D +
                                                          (size_t)r * D + c0);
             }
-        if (c >= 1 && tid < NE4)
+        if (c >= 1)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                pE[q] = *reinterpret_cast<const f32x4*>(em + blk_c * D * D +
-                                                         (size_t)(4 * rb4 + q) * D + 4 * cb4);
+            for (int i = 0; i < UE; ++i) {
+                const int e = tid + 256 * i;
+                if (e < NEU)
+                    pE[i] = *reinterpret_cast<const u32x4*>(em + blk_c * D * D + (size_t)8 * e);
+            }
         if (tid < kB) pGc = fw.gl[blk_c * kB + tid];
     };
     auto commit = [&](int c) {
@@ -1358,21 +1362,23 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         // Kr enters both of its products scaled (S^T = scale Kr X^T in the
         // exponent, scale Kr^T dS^T in the chain), and E negated, so the chain
         // accumulates straight into A^T
-        if (tid < NB4)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                sK.put4(4 * rb4 + q, 4 * cb4, pK[q] * scale);
-            }
+        for (int i = 0; i < UB; ++i) {
+            const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            *reinterpret_cast<u32x4*>(&sK.v[0][r * sK.LDE + c0]) = pK[i];
+        }
         if (c < b)
 #pragma unroll
             for (int i = 0; i < UB; ++i) {
                 const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
                 *reinterpret_cast<u32x4*>(&sX.v[0][r * sX.LDE + c0]) = pX[i];
             }
-        if (c >= 1 && tid < NE4)
+        if (c >= 1)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                sE.put4(4 * rb4 + q, 4 * cb4, -pE[q]);
+            for (int i = 0; i < UE; ++i) {
+                const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+                if (e < NEU) *reinterpret_cast<u32x4*>(&sE.v[0][r * sE.LDE + c0]) = pE[i];
+            }
         if (tid < kB) {
             const float gc = fox ? pGc : 0.f;
             sGc[tid] = gc;
@@ -1942,8 +1948,10 @@ hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
     hipError_t e;
     if (a.img) {   // bf16, d in {32, 64}: the matrix-core preconditioning
         f.ws.img = a.img;
-        f.ws.k32 = static_cast<float*>(a.fw.kr);
-        f.ws.e32 = static_cast<float*>(a.fw.em);
+        // the pair kernels take scale * Kright and -E as bf16 rows, in the
+        // (fp32-sized) kr and em areas
+        f.ws.kb16 = a.fw.kr;
+        f.ws.eb16 = a.fw.em;
         e = launch_precond_bf16(f, st);
     } else {
         e = launch_precond_f32(f, st);

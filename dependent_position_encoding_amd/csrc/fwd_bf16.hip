@@ -491,6 +491,8 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const int t = j - ND, mt = t / DT, nt = t % DT;
             mm_ss(acc, s1, s2, 32 * nt, 32 * mt, lane, 32 * mt, kB);   // M^T[r][a]: a > r
             float* k32 = ws.k32 ? ws.k32 + (size_t)blk * B * D : nullptr;
+            __bf16* kb16 = ws.kb16 ? static_cast<__bf16*>(ws.kb16) + (size_t)blk * B * D : nullptr;
+            const float qscale = kscale * kLn2;   // the score scale itself
             for_tile4(acc, 32 * nt, 32 * mt, lane, [&](int r, int x0, f32x4 a) {
                 const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(sK + pb<RB>(r, x0));
                 f32x4 val;
@@ -502,6 +504,12 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 // four consecutive columns stay consecutive under swap23
                 *reinterpret_cast<bf16x4*>(img + I::OFF_K + img_off(r, swap23(x0), I::RB_K)) = ks;
                 if (k32) *reinterpret_cast<f32x4*>(k32 + r * D + x0) = val;
+                if (kb16) {
+                    bf16x4 kq;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) kq[e] = (__bf16)(val[e] * qscale);
+                    *reinterpret_cast<bf16x4*>(kb16 + r * D + x0) = kq;
+                }
             });
         } else if (j < ND + NK + NQ) {
             // (P W)[i][x] = sum_a P[i][a] W[a][x]
@@ -516,12 +524,14 @@ precond_mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const int t = j - ND - NK - NQ, mt = t / DT, nt = t % DT;
             mm_sc<RB>(acc, s1, sW, 32 * nt, 32 * mt, lane);
             float* e32 = ws.e32 ? ws.e32 + (size_t)blk * D * D : nullptr;
+            __bf16* eb16 = ws.eb16 ? static_cast<__bf16*>(ws.eb16) + (size_t)blk * D * D : nullptr;
             for_tile4(acc, 32 * nt, 32 * mt, lane, [&](int x, int y0, f32x4 a) {
                 bf16x4 es;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) es[e] = (__bf16)(-a[e]);
                 *reinterpret_cast<bf16x4*>(img + I::OFF_E + img_off(x, swap23(y0), I::RB_E)) = es;
                 if (e32) *reinterpret_cast<f32x4*>(e32 + x * D + y0) = a;
+                if (eb16) *reinterpret_cast<bf16x4*>(eb16 + x * D + y0) = es;
             });
         }
     };

@@ -23,6 +23,10 @@ struct FwdWs {
     float* suf;   // suffix transitions S_c [blk][d][d]
     float* gpre;  // log f sum of all blocks before c [blk]
     float* grp;   // per group of blocks: whole transition and suffix [slice][g][2][d][d]
+    // backward (bf16 pair kernels) only (NULL otherwise): bf16 copies of
+    // scale * Kright [blk][B][d] and of -E [blk][d][d], row-major
+    void* kb16;
+    void* eb16;
 };
 
 struct FwdArgs {
