@@ -995,8 +995,9 @@ __device__ inline void pair_order(int nb, int nsc, int& rank, int& sl) {
 // key, bf16: for key block c, over the query blocks b >= c.  The logits are
 // formed query-major (S = X Kr^T) and written transposed, four queries of a
 // key at a time, so P^T and dS^T are key-major operands of dV = P^T dO and
-// dKr = dS^T X; X, Z and dO are staged in 4 x 4 (4 x 8) register blocks and
-// written both ways, for the products that contract over the queries.
+// dKr = dS^T X; X, Z and dO come in as 16-byte pieces of their rows, and the
+// products that contract over the queries read them down their columns with
+// the transposing LDS load.
 template <int D>
 __global__ void __launch_bounds__(256)
 bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
@@ -1026,10 +1027,6 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     // the carried queries and the gradient chain, bf16 [pair][kB][D]
     const __bf16* Xs = reinterpret_cast<const __bf16*>(X) + (size_t)sl * npairs * kB * D;
     const __bf16* Zs = reinterpret_cast<const __bf16*>(Z) + (size_t)sl * npairs * kB * D;
-    constexpr int NB4 = kB * D / 16;   // 4 x 4 blocks of a [kB][D] tile
-    constexpr int NB8 = kB * D / 32;   // 4 x 8 blocks of a [kB][D] bf16 tile
-    const int rb4 = tid / (D / 4), cb4 = tid % (D / 4);   // this thread's 4 x 4 block
-    const int rb8 = tid / (D / 8), cb8 = tid % (D / 8);   // and 4 x 8 block
 
     {   // resident: scale * Kr_c (bf16 rows from the preconditioning), V_c
         // (every load in flight before the first LDS write)
@@ -1068,31 +1065,32 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
             sCol2[tid] = -(fox ? gc : 0.f) * kLog2e;
         }
     }
-    // prefetch of query block b's X_bc, Z_bc (4 x 4 bf16 blocks), dO and row terms
-    bf16x4_t pX[4], pZ[4];
-    u32x4 pO[4];
+    // prefetch of query block b's X_bc, Z_bc, dO (16-byte pieces of their
+    // rows) and row terms
+    constexpr int UB = kB * D / 8 / 256;
+    u32x4 pX[UB], pZ[UB], pO[UB];
     float pLse = 0.f, pDel = 0.f, pGb = 0.f, pTot = 0.f;   // pTot: the gate total of block b - 1
     auto prefetch = [&](int b) {
         const size_t blk_b = slice * nb + b;
         pTot = fox && b >= 1 ? fw.tot[blk_b - 1] : 0.f;
-        if (b > c && tid < NB4) {
-            const __bf16* xb = Xs + pair_index(b, c) * kB * D + (size_t)(4 * rb4) * D + 4 * cb4;
-            const __bf16* zb = Zs + pair_index(b, c) * kB * D + (size_t)(4 * rb4) * D + 4 * cb4;
+        if (b > c) {
+            const __bf16* xb = Xs + pair_index(b, c) * kB * D;
+            const __bf16* zb = Zs + pair_index(b, c) * kB * D;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                pX[q] = *reinterpret_cast<const bf16x4_t*>(xb + (size_t)q * D);
-                if (c >= 1) pZ[q] = *reinterpret_cast<const bf16x4_t*>(zb + (size_t)q * D);
+            for (int i = 0; i < UB; ++i) {
+                const int e = tid + 256 * i;
+                pX[i] = *reinterpret_cast<const u32x4*>(xb + (size_t)8 * e);
+                if (c >= 1) pZ[i] = *reinterpret_cast<const u32x4*>(zb + (size_t)8 * e);
             }
         }
         // rows past the sequence end are loaded from its last row and masked
         // at the commit: a register written before a load it may overlap
         // would make the compiler wait for every load in flight
-        if (tid < NB8) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int pos = min(b * kB + 4 * rb8 + q, L - 1);
-                pO[q] = *reinterpret_cast<const u32x4*>(dout + (base + pos) * D + 8 * cb8);
-            }
+        for (int i = 0; i < UB; ++i) {
+            const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            const int pos = min(b * kB + r, L - 1);
+            pO[i] = *reinterpret_cast<const u32x4*>(dout + (base + pos) * D + c0);
         }
         if (tid < kB) {
             pLse = lse[base + min(b * kB + tid, L - 1)];
@@ -1101,21 +1099,15 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         }
     };
     auto commit = [&](int b) {
-        if (b > c && tid < NB4) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                *reinterpret_cast<bf16x4_t*>(&sX.v[0][(4 * rb4 + q) * sX.LDE + 4 * cb4]) = pX[q];
-                if (c >= 1)
-                    *reinterpret_cast<bf16x4_t*>(&sZ.v[0][(4 * rb4 + q) * sZ.LDE + 4 * cb4]) = pZ[q];
+        for (int i = 0; i < UB; ++i) {
+            const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            if (b > c) {
+                *reinterpret_cast<u32x4*>(&sX.v[0][r * sX.LDE + c0]) = pX[i];
+                if (c >= 1) *reinterpret_cast<u32x4*>(&sZ.v[0][r * sZ.LDE + c0]) = pZ[i];
             }
-        }
-        if (tid < NB8) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const bool in = b * kB + 4 * rb8 + q < L;
-                *reinterpret_cast<u32x4*>(&sdO.v[0][(4 * rb8 + q) * sdO.LDE + 8 * cb8]) =
-                    in ? pO[q] : u32x4{0u, 0u, 0u, 0u};
-            }
+            *reinterpret_cast<u32x4*>(&sdO.v[0][r * sdO.LDE + c0]) =
+                b * kB + r < L ? pO[i] : u32x4{0u, 0u, 0u, 0u};
         }
         if (tid < kB) {
             const bool in = b * kB + tid < L;
