@@ -10,7 +10,9 @@ namespace pa {
 // workspace by the host layer.  "blk" = slice * nb + c with slice = n*H + h.
 struct FwdWs {
     void* kr;     // f32 path: keys moved to their block's right edge [blk][B][d]
+                  //   (the bf16 backward keeps scale * Kright here as bf16, see kb16)
     void* em;     // f32 path: block transition I - E, E as [blk][d][d]
+                  //   (the bf16 backward keeps -E here as bf16, see eb16)
     void* img;    // bf16 path: per-block tile images (Kright, V^T, -E, gate
                   //   cumsum) in the scan's LDS layout [blk][image bytes]
     float* ql;    // queries moved to their block's left edge [blk][B][d]
@@ -114,7 +116,8 @@ struct BwdArgs {
     const float *beta, *logf, *lse;
     void *dq, *dk, *dv, *dw;
     float *dbeta, *dlogf;
-    FwdWs fw;            // recomputed preconditioning (ql, kr, em, dg, gl, tot; fp32)
+    FwdWs fw;            // recomputed preconditioning (ql, kr, em, dg, gl, tot; fp32,
+                         // kr and em as bf16 rows on the bf16 matrix-core path)
     float *X, *Z;        // per block pair of a chunk of slices [slice][pair][B][d] (bf16
                          // elements for bf16 inputs at d >= 32)
     float *dQl, *dKr, *dEm, *dDg;   // per block: gradients of the preconditioned products
