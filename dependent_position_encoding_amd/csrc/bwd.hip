@@ -1216,20 +1216,29 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
 // consecutive d values per register group, so the operand copy of A in LDS
 // and the stores of A go out as vectors.
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
                      const bf16* __restrict__ v, const bf16* __restrict__ o,
                      const bf16* __restrict__ dout, const float* __restrict__ lse, FwdWs fw,
                      const float* __restrict__ X, float* __restrict__ Z,
                      float* __restrict__ dQl, float* __restrict__ dDg,
                      float* __restrict__ rowsum, float* __restrict__ delta) {
+    // Five tiles, so that three workgroups share a CU: X's tile takes P (then
+    // dS) once the logits are formed, and V's takes -E once dP is formed.
+    using TX = BTile<kB, D, 1>;
+    using TS = BTile<kB, kB, 1>;
+    using TE = BTile<D, D, 1>;
+    constexpr int XS_BYTES = sizeof(TX) > sizeof(TS) ? sizeof(TX) : sizeof(TS);
+    constexpr int VE_BYTES = sizeof(TX) > sizeof(TE) ? sizeof(TX) : sizeof(TE);
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sdO;    // dO_b [query][d]
-    __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sV;     // V_c [key][d]
-    __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sX;     // X_bc [query][d]
-    __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sK;     // Kr_c [key][d]
-    __shared__ __attribute__((aligned(16))) BTile<D, D, 1> sE;      // E_c [d][d]
+    __shared__ __attribute__((aligned(16))) char sVE[VE_BYTES];     // V_c [key][d], then -E_c [d][d]
+    __shared__ __attribute__((aligned(16))) char sXS[XS_BYTES];     // X_bc [query][d], then P, dS [query][key]
+    __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sK;     // scale Kr_c [key][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sA;     // A_{c-1} [query][d]
-    __shared__ __attribute__((aligned(16))) BTile<kB, kB, 1> sS;    // P, then dS [query][key] (bf16)
+    TX& sV = *reinterpret_cast<TX*>(sVE);
+    TE& sE = *reinterpret_cast<TE*>(sVE);
+    TX& sX = *reinterpret_cast<TX*>(sXS);
+    TS& sS = *reinterpret_cast<TS*>(sXS);
     __shared__ float sLse[kB], sDel[kB], sGb[kB], sGc[kB];
     __shared__ float sRowW[4][32];   // per (wave, lane) row sums of dS
     // log2-unit logit terms of the off-diagonal steps: per query row (gate,
@@ -1335,14 +1344,24 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
                 pX[i] = *reinterpret_cast<const u32x4*>(Xs + pair_index(b, c) * kB * D +
                                                          (size_t)r * D + c0);
             }
-        if (c >= 1)
-#pragma unroll
-            for (int i = 0; i < UE; ++i) {
-                const int e = tid + 256 * i;
-                if (e < NEU)
-                    pE[i] = *reinterpret_cast<const u32x4*>(em + blk_c * D * D + (size_t)8 * e);
-            }
         if (tid < kB) pGc = fw.gl[blk_c * kB + tid];
+    };
+    // -E_c is fetched a pair ahead, once the previous pair has written its
+    // copy, and written over V's tile after dP is formed
+    auto load_e = [&](int c) {
+        const size_t blk_c = slice * nb + c;
+#pragma unroll
+        for (int i = 0; i < UE; ++i) {
+            const int e = tid + 256 * i;
+            if (e < NEU) pE[i] = *reinterpret_cast<const u32x4*>(em + blk_c * D * D + (size_t)8 * e);
+        }
+    };
+    auto commit_e = [&] {
+#pragma unroll
+        for (int i = 0; i < UE; ++i) {
+            const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            if (e < NEU) *reinterpret_cast<u32x4*>(&sE.v[0][r * sE.LDE + c0]) = pE[i];
+        }
     };
     auto commit = [&](int c) {
 #pragma unroll
@@ -1364,12 +1383,6 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
             for (int i = 0; i < UB; ++i) {
                 const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
                 *reinterpret_cast<u32x4*>(&sX.v[0][r * sX.LDE + c0]) = pX[i];
-            }
-        if (c >= 1)
-#pragma unroll
-            for (int i = 0; i < UE; ++i) {
-                const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
-                if (e < NEU) *reinterpret_cast<u32x4*>(&sE.v[0][r * sE.LDE + c0]) = pE[i];
             }
         if (tid < kB) {
             const float gc = fox ? pGc : 0.f;
@@ -1448,21 +1461,36 @@ bwd_query_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
             }
         }
         const float shift = fox ? ((sTw[0] + sTw[1]) + (sTw[2] + sTw[3])) - Tc : 0.f;   // totals of blocks c .. b-1
-        // S^T = (scale Kr) X^T: keys m .. m+3 of query n, written to the query-major P
+        // S^T = (scale Kr) X^T, a 32 x 32 tile per wave: keys m .. m+3 of query
+        // n, written to the query-major P over X's tile once every wave has
+        // read X
         const float shift2 = shift * kLog2e;
-        gemm_b4<1, 1, D>(kB, kB, bview(sK), bview(sX), [&](int n, int m, f32x4 sv) {
+        {
+            const int r = lane & 31, hh = lane >> 5, m0 = (wave >> 1) * 32, n0 = (wave & 1) * 32;
+            const f32x16 sv = tile_b<1, 1, D>(bview(sK), bview(sX), m0, n0, r, hh);
+            __syncthreads();   // X's tile is free
+            const int n = n0 + r;
             const float rw = sRowB[n] + shift2;
-            const f32x4 cl = *reinterpret_cast<const f32x4*>(sCol2 + m);
-            f32x4 p;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(kLog2e, sv[e], rw + cl[e]));
-            sS.put4(n, m, p);
-        });
+            for (int i = 0; i < 4; ++i) {
+                const int m = m0 + 8 * i + 4 * hh;
+                const f32x4 cl = *reinterpret_cast<const f32x4*>(sCol2 + m);
+                f32x4 p;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(kLog2e, sv[4 * i + e], rw + cl[e]));
+                sS.put4(n, m, p);
+            }
+        }
         backprop(false);
+        if (c >= 1) {       // V's tile is free (dS complete): -E_c over it
+            commit_e();
+            __syncthreads();
+        }
         // A^T <- A^T + (scale Kr)^T dS^T + (-E)^T A^T, accumulated in place
         gemm_bc_acc<true, false, kB>(D, kB, bview(sK), bview(sS), At);
         if (c >= 1) gemm_bc_acc<true, false, D>(D, kB, bview(sE), bview(sA), At);
+        if (c + 1 < b && c + 1 >= 1) load_e(c + 1);
         __syncthreads();   // every read of A_{c-1} and of the pair's tiles is done
         if (owner)
 #pragma unroll
