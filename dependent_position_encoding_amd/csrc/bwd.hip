@@ -999,7 +999,7 @@ __device__ inline void pair_order(int nb, int nsc, int& rank, int& sl) {
 // products that contract over the queries read them down their columns with
 // the transposing LDS load.
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
                    const bf16* __restrict__ v, const bf16* __restrict__ dout,
                    const float* __restrict__ lse, const float* __restrict__ delta, FwdWs fw,
@@ -1009,8 +1009,10 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sK;     // Kr_c [key][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sV;     // V_c [key][d]
     __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sX;     // X_bc [query][d]
-    __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sZ;     // A_{c-1} [query][d]
-    __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sdO;    // dO_b [query][d]
+    // dO_b [query][d], then A_{c-1} [query][d] once dP is formed (five tiles,
+    // so that three workgroups share a CU)
+    __shared__ __attribute__((aligned(16))) BTile<kB, D, 1> sdO;
+    BTile<kB, D, 1>& sZ = sdO;
     __shared__ __attribute__((aligned(16))) BTile<kB, kB, 1> sPT;   // P^T, then dS^T [key][query] (bf16)
     __shared__ float sLse[kB], sDel[kB], sGb[kB], sGc[kB];
     __shared__ float sColW[4][32];   // per (wave, lane) column sums of dS
@@ -1075,12 +1077,10 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         pTot = fox && b >= 1 ? fw.tot[blk_b - 1] : 0.f;
         if (b > c) {
             const __bf16* xb = Xs + pair_index(b, c) * kB * D;
-            const __bf16* zb = Zs + pair_index(b, c) * kB * D;
 #pragma unroll
             for (int i = 0; i < UB; ++i) {
                 const int e = tid + 256 * i;
                 pX[i] = *reinterpret_cast<const u32x4*>(xb + (size_t)8 * e);
-                if (c >= 1) pZ[i] = *reinterpret_cast<const u32x4*>(zb + (size_t)8 * e);
             }
         }
         // rows past the sequence end are loaded from its last row and masked
@@ -1102,10 +1102,7 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
 #pragma unroll
         for (int i = 0; i < UB; ++i) {
             const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
-            if (b > c) {
-                *reinterpret_cast<u32x4*>(&sX.v[0][r * sX.LDE + c0]) = pX[i];
-                if (c >= 1) *reinterpret_cast<u32x4*>(&sZ.v[0][r * sZ.LDE + c0]) = pZ[i];
-            }
+            if (b > c) *reinterpret_cast<u32x4*>(&sX.v[0][r * sX.LDE + c0]) = pX[i];
             *reinterpret_cast<u32x4*>(&sdO.v[0][r * sdO.LDE + c0]) =
                 b * kB + r < L ? pO[i] : u32x4{0u, 0u, 0u, 0u};
         }
@@ -1116,6 +1113,20 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
             sDel[tid] = pDel;
             sGb[tid] = gb;
             sRow2[tid] = in ? (gb + shift - pLse) * kLog2e : -INFINITY;
+        }
+    };
+    // A_{c-1} of pair (b, c) is fetched a pair ahead, once the previous pair
+    // has written its copy, and written over dO's tile after dP is formed
+    auto load_z = [&](int b) {
+        const __bf16* zb = Zs + pair_index(b, c) * kB * D;
+#pragma unroll
+        for (int i = 0; i < UB; ++i) pZ[i] = *reinterpret_cast<const u32x4*>(zb + (size_t)8 * (tid + 256 * i));
+    };
+    auto commit_z = [&] {
+#pragma unroll
+        for (int i = 0; i < UB; ++i) {
+            const int e = tid + 256 * i, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            *reinterpret_cast<u32x4*>(&sZ.v[0][r * sZ.LDE + c0]) = pZ[i];
         }
     };
     f32x16 accV = zero16(), accK = zero16(), accE = zero16();
@@ -1168,6 +1179,7 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
         }
     }
     if (c + 1 < nb) prefetch(c + 1);
+    if (c >= 1 && c + 1 < nb) load_z(c + 1);
     backprop();
 
     for (int b = c + 1; b < nb; ++b) {
@@ -1186,6 +1198,11 @@ bwd_key_b16_kernel(int L, int nb, int nsc, int slice0, float scale, int fox,
             sPT.put4(n, m, p);
         });
         backprop();
+        if (c >= 1) {       // dO's tile is free (dS^T complete): A_{c-1} over it
+            commit_z();
+            __syncthreads();
+            if (b + 1 < nb) load_z(b + 1);
+        }
         // dKr += dS^T X (scaled at the end);  dE -= A_{c-1}^T X
         gemm_bc_acc<false, true, kB>(kB, D, bview(sPT), bview(sX), accK);
         if (c >= 1) gemm_bc_acc<true, true, kB>(D, D, bview(sZ), bview(sX), accE);
