@@ -391,7 +391,10 @@ __device__ inline void paged_chunk(K* __restrict__ kp, T* __restrict__ vp, float
                                    const T* __restrict__ w_t, const float* __restrict__ beta_t,
                                    const float* __restrict__ logf_t, float* __restrict__ part,
                                    int* __restrict__ nk) {
-    const int slice = blockIdx.y, ch = blockIdx.x, nch = gridDim.x;
+    // chunk-major grid: every slice's chunk 0, then every slice's chunk 1, ...,
+    // so the chunks past the shorter sequences' ends, which exit at once,
+    // come at the end of the dispatch instead of between working ones
+    const int slice = blockIdx.x, ch = blockIdx.y, nch = gridDim.y;
     const int s = slice / H, h = slice % H;
     const int len = seq_lens[s];
     const bool ok = len >= 0 && len < max_keys;
@@ -1069,7 +1072,7 @@ static hipError_t paged_step_t(const PagedArgs& a, hipStream_t st) {
     constexpr bool SIX = std::is_same_v<K, bf16> && std::is_same_v<T, bf16> && D == 64;
     const bool slots = (1 << a.lp) >= GROUPS;
     auto launch = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3(mch, S), dim3(256), 0, st, (K*)a.kpages, (T*)a.vpages,
+        hipLaunchKernelGGL(kernel, dim3(S, mch), dim3(256), 0, st, (K*)a.kpages, (T*)a.vpages,
                            a.gpages, a.num_pages, a.lp, a.H, a.tables, a.table_stride,
                            (const int*)a.seq_lens, a.max_keys, a.scale, (const T*)a.q_t,
                            (const T*)a.k_t, (const T*)a.v_t, (const T*)a.w_t, a.beta_t, a.logf_t,
