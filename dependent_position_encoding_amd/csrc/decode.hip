@@ -403,29 +403,28 @@ __device__ inline void paged_chunk(K* __restrict__ kp, T* __restrict__ vp, float
     if (!ok || ch * kPagedChunk >= n_keys) return;
     const int* table = tables + (size_t)s * table_stride;
     float* out = part + ((size_t)slice * nch + ch) * (D + 2);
-    // The chunk's page-table entries into LDS, each checked against the pool
-    // (one lane per page); the key rows then read their page from LDS.  With
-    // the gate, every chunk also reads the log-f prefix of slot t - 1 (the
-    // new token's prefix continues it), whose page is loaded and checked on
-    // its own: it need not be one of this chunk's pages.
+    // The chunk's page-table entries into LDS (one lane per page) and, on the
+    // last lane, with the gate, the entry of slot t - 1's page (the new
+    // token's log-f prefix continues that slot's, which need not be on one of
+    // this chunk's pages), loaded together and each checked against the pool;
+    // the key rows then read their page from LDS.
     __shared__ int sPage[kPagedChunk / 16];
-    __shared__ int sBad, sPrev;
+    __shared__ int sPrev;
     const int p0 = (ch * kPagedChunk) >> lp, p1 = (min(n_keys, (ch + 1) * kPagedChunk) - 1) >> lp;
     const int tp = n_keys - 2;                    // slot t - 1
-    if (threadIdx.x == 0) {
+    bool bad = false;
+    if (threadIdx.x <= p1 - p0) {                 // at most kPagedChunk / 16 lanes
+        const int pg = table[p0 + threadIdx.x];
+        sPage[threadIdx.x] = pg;
+        bad = (unsigned)pg >= (unsigned)num_pages;
+    }
+    if (threadIdx.x == blockDim.x - 1) {
         int prev = 0;
         if (gp && tp >= 0) prev = table[tp >> lp];
         sPrev = prev;
-        sBad = (unsigned)prev >= (unsigned)num_pages;
+        bad = bad || (unsigned)prev >= (unsigned)num_pages;
     }
-    __syncthreads();
-    if (threadIdx.x <= p1 - p0) {
-        const int pg = table[p0 + threadIdx.x];
-        sPage[threadIdx.x] = pg;
-        if ((unsigned)pg >= (unsigned)num_pages) sBad = 1;
-    }
-    __syncthreads();
-    if (sBad) {
+    if (__syncthreads_or(bad)) {
         if (threadIdx.x < D + 2) out[threadIdx.x] = threadIdx.x == 0 ? INFINITY : 0.f;
         return;
     }
