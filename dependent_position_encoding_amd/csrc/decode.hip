@@ -572,7 +572,7 @@ decode_combine_kernel(const float* __restrict__ part, int nch, int pstride, int 
 // and the group's whole transition G_g = F_first T_first; across groups
 //   Z_{ng-1} = I,  Z_g = G_{g+1} Z_{g+1}         (suffix_groups_kernel)
 // so that S_c = T_c Z_{g(c)} (align_apply_kernel).  All in fp32.
-constexpr int kSufGroup = 16;
+constexpr int kSufGroup = 32;
 
 // The d x d products run on the matrix cores on matrices padded to
 // DP = max(d, 32), with fp32 operands split into bf16 parts: three parts and
