@@ -740,7 +740,9 @@ scan_mfma_kernel(int L, int nb, int sg, float scale2, FwdWs ws, __bf16* __restri
         }
         // the step's matrix-core phases run at a raised wave priority and its
         // softmax at the normal one, so that a SIMD's arbiter issues the
-        // products of one wave while the others do their vector work
+        // products of one wave while the others do their vector work; P.V,
+        // which ends the step, one level above the scores, so that a wave
+        // finishing its step goes before one starting the next
         __builtin_amdgcn_s_setprio(1);
         bf16x8 ka[2][NKC];
 #pragma unroll
@@ -814,7 +816,7 @@ scan_mfma_kernel(int L, int nb, int sg, float scale2, FwdWs ws, __bf16* __restri
             ps = probs(Pb);
         }
         l += ps;
-        __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_s_setprio(2);
         pv(im, Pb);
         __builtin_amdgcn_s_setprio(0);
     };
